@@ -1,0 +1,246 @@
+"""CPU oracle for the fused AdamW-family optimizer step (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark may import this package; the product path never does.
+It wraps ``oracle.c`` (plain scalar C, fp64, built with gcc) through ctypes and
+adds thin numpy drivers that hold per-parameter state.  It shares no code with
+the HIP library.
+
+Each function cites the web page (title, section) whose definition it follows;
+see the header of ``oracle.c`` for the page list.  Conversions between bit
+patterns and numbers here are exact (bf16/fp32 -> float64 widening).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O2, no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.check_call([
+            "gcc", "-O2", "-std=c11", "-D_DEFAULT_SOURCE", "-fPIC", "-shared",
+            "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+            "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+_d = ctypes.c_double
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+_p = ctypes.c_void_p
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        L = ctypes.CDLL(_LIB_PATH)
+        sigs = {
+            "oracle_adamw_step": [_i64, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64],
+            "mutant_adamw_decay_after_step": [_i64, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64],
+            "oracle_ademamix_step": [_i64, _p, _p, _p, _p, _p, _d, _d, _d, _d, _d, _d, _d, _i64],
+            "oracle_adam_mini_step": [_i64, _i64, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64],
+            "oracle_any_nonfinite": [_i64, _p],
+            "oracle_cosine_lr": [_i64, _i64, _d, _d],
+            "oracle_remainder_split": [_i64, _p, _p, _p],
+            "oracle_remainder_reconstruct": [_i64, _p, _p, _p],
+            "oracle_remainder_exhaustive": [],
+            "oracle_dynamic_map": [_i32, _p],
+            "oracle_thresholds": [_i32, _p, _p],
+            "oracle_quantize": [_i64, _i64, _i32, _i32, _p, _p, _p, _p],
+            "oracle_dequantize": [_i64, _i64, _i32, _i32, _p, _p, _p, _p],
+            "oracle_pack_nibbles": [_i64, _p, _p],
+            "oracle_unpack_nibbles": [_i64, _p, _p],
+            "oracle_blockwise_step": [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p,
+                                      _d, _d, _d, _d, _d, _i64, _p, _p],
+        }
+        restypes = {"oracle_any_nonfinite": _i32, "oracle_cosine_lr": ctypes.c_float,
+                    "oracle_remainder_exhaustive": _i64, "oracle_dynamic_map": _i32}
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = restypes.get(name, None)
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# exact widening of stored formats
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64 (exact)."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def f32_bits(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+
+
+# --------------------------------------------------------------------------
+# per-step functions (in place on float64 state arrays)
+def adamw_step(p, m, v, g, lr, beta1, beta2, eps, wd, t):
+    """AdamW, Algorithm 2 decay order (bitsandbytes PR #2040, description)."""
+    lib().oracle_adamw_step(p.size, _ptr(p), _ptr(m), _ptr(v), _ptr(_f64(g)),
+                            lr, beta1, beta2, eps, wd, t)
+
+
+def mutant_adamw_decay_after_step(p, m, v, g, lr, beta1, beta2, eps, wd, t):
+    """TEST MUTANT: the decay-after ordering the bitsandbytes PR removes."""
+    lib().mutant_adamw_decay_after_step(p.size, _ptr(p), _ptr(m), _ptr(v),
+                                        _ptr(_f64(g)), lr, beta1, beta2, eps, wd, t)
+
+
+def ademamix_step(p, m1, m2, nu, g, lr, beta1, beta2, beta3, alpha, eps, wd, t):
+    """AdEMAMix with constant alpha/beta3, m2 not bias-corrected."""
+    lib().oracle_ademamix_step(p.size, _ptr(p), _ptr(m1), _ptr(m2), _ptr(nu),
+                               _ptr(_f64(g)), lr, beta1, beta2, beta3, alpha,
+                               eps, wd, t)
+
+
+def adam_mini_step(p, m, V, g, block, lr, beta1, beta2, eps, wd, t):
+    """Adam-mini shared-v step for one tensor (block = head_numel or numel)."""
+    assert p.size % block == 0 and V.size == p.size // block
+    lib().oracle_adam_mini_step(p.size, block, _ptr(p), _ptr(m), _ptr(V),
+                                _ptr(_f64(g)), lr, beta1, beta2, eps, wd, t)
+
+
+def any_nonfinite(x) -> bool:
+    x = _f64(x)
+    return bool(lib().oracle_any_nonfinite(x.size, _ptr(x)))
+
+
+def cosine_lr(k: int, K: int, lr_max: float, lr_min: float = 0.0) -> np.float32:
+    return np.float32(lib().oracle_cosine_lr(k, K, lr_max, lr_min))
+
+
+# --------------------------------------------------------------------------
+# bf16 + int16 remainder (TransformerEngine PR #1408, description)
+def remainder_split(x_f32: np.ndarray):
+    u = np.ascontiguousarray(f32_bits(x_f32).ravel())
+    b = np.empty(u.size, np.uint16)
+    r = np.empty(u.size, np.int16)
+    lib().oracle_remainder_split(u.size, _ptr(u), _ptr(b), _ptr(r))
+    return b, r
+
+
+def remainder_reconstruct(b: np.ndarray, r: np.ndarray) -> np.ndarray:
+    b = np.ascontiguousarray(b, dtype=np.uint16).ravel()
+    r = np.ascontiguousarray(r, dtype=np.int16).ravel()
+    u = np.empty(b.size, np.uint32)
+    lib().oracle_remainder_reconstruct(b.size, _ptr(b), _ptr(r), _ptr(u))
+    return u.view(np.float32)
+
+
+def remainder_exhaustive_failures() -> int:
+    return int(lib().oracle_remainder_exhaustive())
+
+
+# --------------------------------------------------------------------------
+# blockwise quantized states
+def dynamic_map(mag_bits: int) -> np.ndarray:
+    M = np.zeros(1 << mag_bits, np.float32)
+    cnt = lib().oracle_dynamic_map(mag_bits, _ptr(M))
+    assert cnt == M.size
+    return M
+
+
+def thresholds(M: np.ndarray) -> np.ndarray:
+    T = np.zeros(M.size, np.float32)
+    lib().oracle_thresholds(M.size, _ptr(np.ascontiguousarray(M, np.float32)), _ptr(T))
+    return T
+
+
+def quantize(x: np.ndarray, block: int, mag_bits: int, signed: bool):
+    x = np.ascontiguousarray(x, np.float32).ravel()
+    T = thresholds(dynamic_map(mag_bits))
+    codes = np.empty(x.size, np.uint8)
+    absmax = np.empty((x.size + block - 1) // block, np.float32)
+    lib().oracle_quantize(x.size, block, mag_bits, int(signed), _ptr(x), _ptr(T),
+                          _ptr(codes), _ptr(absmax))
+    return codes, absmax
+
+
+def dequantize(codes: np.ndarray, absmax: np.ndarray, block: int, mag_bits: int,
+               signed: bool) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8).ravel()
+    absmax = np.ascontiguousarray(absmax, np.float32)
+    M = dynamic_map(mag_bits)
+    x = np.empty(codes.size, np.float32)
+    lib().oracle_dequantize(codes.size, block, mag_bits, int(signed), _ptr(codes),
+                            _ptr(M), _ptr(absmax), _ptr(x))
+    return x
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8).ravel()
+    out = np.empty((codes.size + 1) // 2, np.uint8)
+    lib().oracle_pack_nibbles(codes.size, _ptr(codes), _ptr(out))
+    return out
+
+
+def unpack_nibbles(packed: np.ndarray, n: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, np.uint8).ravel()
+    out = np.empty(n, np.uint8)
+    lib().oracle_unpack_nibbles(n, _ptr(packed), _ptr(out))
+    return out
+
+
+def blockwise_step(p, g_f32, qm, qv, am, av, bits, block, lr, beta1, beta2, eps,
+                   wd, t):
+    """Blockwise 8-bit/4-bit 2-state AdamW step; codes unpacked, in place."""
+    n = p.size
+    g = np.ascontiguousarray(g_f32, np.float32).ravel()
+    sm = np.empty(n, np.float32)
+    sv = np.empty(n, np.float32)
+    lib().oracle_blockwise_step(n, block, bits, _ptr(p), _ptr(g), _ptr(qm), _ptr(qv),
+                                _ptr(am), _ptr(av), lr, beta1, beta2, eps, wd, t,
+                                _ptr(sm), _ptr(sv))
+    return sm, sv  # the fp32 states before requantization
+
+
+# --------------------------------------------------------------------------
+# Adam-mini partition by parameter name ("Adam-mini <> DTensor", AdamWMini)
+MINI_FULL_V, MINI_HEAD, MINI_SCALAR = 0, 1, 2
+
+
+def adam_mini_kind(name: str) -> int:
+    if any(s in name for s in ("embed", "embd", "wte", "lm_head.weight", "output.weight")):
+        return MINI_FULL_V
+    if any(s in name for s in ("q_proj.weight", "k_proj.weight", "wq.weight", "wk.weight")):
+        return MINI_HEAD
+    return MINI_SCALAR
+
+
+def adam_mini_weight_decay(name: str, wd: float) -> float:
+    return 0.0 if ("norm" in name or "ln_f" in name) else wd
+
+
+# --------------------------------------------------------------------------
+# error metric: |x - ref| / max(|ref|, tau)
+def relerr_tau(x, ref, tau: float) -> np.ndarray:
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return np.abs(x - ref) / np.maximum(np.abs(ref), tau)
