@@ -1,0 +1,251 @@
+/*
+ * optim_step.h -- C ABI of the fused, multi-tensor AdamW-family optimizer
+ * step for AMD Instinct MI355X (gfx950).
+ *
+ * Sources for the operations (web pages, cited by title and section):
+ *  [BNB]  "Fix decoupled weight decay ordering in the CUDA Adam/AdEMAMix
+ *         kernels" (bitsandbytes PR #2040)
+ *  [AO]   "4 bit Adam should support non constant lr" (pytorch/ao #730)
+ *  [MINI] "Adam-mini <> DTensor" (Adam-mini issue #14)
+ *  [LTN]  "FusedAdam & PyTorch Lightning AMP" (Lightning issue #15501)
+ *  [TE]   "Support store_param_remainders feature from Apex in TE Fused
+ *         Adam" (TransformerEngine PR #1408)
+ *
+ * Conventions for every entry point:
+ *  - Returns OPTIM_OK (0) or a positive OPTIM_E* code; optim_last_error()
+ *    then holds a message for the calling thread.  Nothing aborts, throws or
+ *    blocks the host; a failed call has launched nothing.
+ *  - "dev" pointers are device (HBM) pointers owned by the caller; "host"
+ *    pointers are host memory owned by the caller.  The library allocates no
+ *    device memory: plan metadata, per-step scalars and reduction partials
+ *    live in a caller-owned workspace.  The only host allocation is the plan
+ *    object itself.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *    device-side effect is enqueued on it, in order; nothing reads device
+ *    memory back to the host, so a whole step can be captured in a HIP graph.
+ *  - Updates are in place.  Gradients are read only and must not alias any
+ *    buffer the step writes.
+ */
+#ifndef OPTIM_STEP_H
+#define OPTIM_STEP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define OPTIM_OK 0
+#define OPTIM_EINVAL 1       /* bad argument or hyperparameter             */
+#define OPTIM_EALIGN 2       /* pointer not aligned to its element size    */
+#define OPTIM_EDTYPE 3       /* dtype combination not supported            */
+#define OPTIM_EWORKSPACE 4   /* workspace missing, misaligned or too small */
+#define OPTIM_EUNSUPPORTED 5 /* valid request this library does not do    */
+#define OPTIM_EHIP 6         /* a HIP runtime call failed                  */
+
+/* ---- enumerations ------------------------------------------------------ */
+enum { OPTIM_F32 = 0, OPTIM_BF16 = 1 };
+enum {
+    OPTIM_ALGO_ADAMW = 0,
+    OPTIM_ALGO_ADEMAMIX = 1,
+    OPTIM_ALGO_ADAM_MINI = 2,
+    OPTIM_ALGO_BLOCKWISE = 3
+};
+/* Adam-mini partition of a tensor ([MINI], AdamWMini constructor/step). */
+enum { OPTIM_MINI_FULL_V = 0, OPTIM_MINI_HEAD = 1, OPTIM_MINI_SCALAR = 2 };
+enum { OPTIM_SCHED_NONE = 0, OPTIM_SCHED_COSINE = 1 };
+
+/* ---- tensor list -------------------------------------------------------
+ * n tensors; every array below is a host array of length n (or NULL where
+ * the algorithm does not use it) whose entries are device pointers.
+ *
+ *  numel        elements per tensor (> 0)
+ *  param        F32: float[numel]; BF16: uint16 bf16 patterns[numel]
+ *  grad         F32 float[numel] or BF16 uint16[numel] (grad_dtype)
+ *  m, v         float[numel] first / second moment (AdamW, AdEMAMix,
+ *               Adam-mini FULL_V).  Adam-mini HEAD/SCALAR: m float[numel]
+ *               and v float[numel/head_numel] (one shared v per block).
+ *  m2           float[numel] AdEMAMix slow EMA; NULL otherwise
+ *  remainder    int16[numel] low halves of the fp32 master ([TE]); required
+ *               when param_dtype is BF16, NULL otherwise
+ *  qm, qv       blockwise codes: 8-bit one byte per element; 4-bit two per
+ *               byte (element 2i in the low nibble); m signed, v unsigned
+ *  absmax_m/_v  float[ceil(numel/block)] per-block scale of qm / qv
+ *  weight_decay per-tensor decoupled decay (>= 0)
+ *  mini_kind    Adam-mini only: OPTIM_MINI_*
+ *  head_numel   Adam-mini only: block length for HEAD (must divide numel);
+ *               ignored otherwise
+ * All device arrays must be aligned to their element size; 16-byte aligned
+ * tensors take the vector path, others a per-element path.                */
+typedef struct optim_tensor_list {
+    int32_t n;
+    const int64_t *numel;
+    void *const *param;
+    const void *const *grad;
+    void *const *m;
+    void *const *v;
+    void *const *m2;
+    void *const *remainder;
+    void *const *qm;
+    void *const *qv;
+    float *const *absmax_m;
+    float *const *absmax_v;
+    const double *weight_decay;
+    const int32_t *mini_kind;
+    const int64_t *head_numel;
+    int32_t param_dtype;
+    int32_t grad_dtype;
+} optim_tensor_list;
+
+/* Plan options.  bits/block: blockwise algorithms only (8-bit: block 64,
+ * 128 or 256; 4-bit: block 128, 256 or 512).  grid: persistent workgroup
+ * count, 0 = chosen from the device's compute-unit count.                */
+typedef struct optim_plan_opts {
+    int32_t bits;
+    int32_t block;
+    int32_t grid;
+} optim_plan_opts;
+
+/* Hyperparameters, validated as in [MINI] AdamWMini's constructor:
+ * 0 <= beta < 1, eps >= 0.  The learning rate is a device scalar.        */
+typedef struct optim_adamw_hp {
+    double beta1, beta2, eps;
+} optim_adamw_hp;
+
+typedef struct optim_ademamix_hp {
+    double beta1, beta2, beta3, alpha, eps;
+} optim_ademamix_hp;
+
+typedef struct optim_plan optim_plan;
+
+/* Message for the last failed call on this thread ("" if none).          */
+const char *optim_last_error(void);
+
+/* ---- plans --------------------------------------------------------------
+ * A plan fixes a tensor list and algorithm: it validates them, splits every
+ * tensor into work units and lays out the device-side tables (tensor
+ * descriptors, unit spans, weight-decay groups, quantization tables) in the
+ * workspace.  This size query is host-only and touches no device.        */
+int optim_plan_workspace_size(const optim_tensor_list *list, int32_t algo,
+                              const optim_plan_opts *opts, size_t *bytes);
+
+/* Builds the plan, copies its tables into `workspace` (device, >= the size
+ * above, 256-byte aligned) on `stream` and waits for that one copy (plan
+ * creation is set-up, not part of a step).  The workspace must stay
+ * allocated and untouched while the plan lives; steps of one plan must not
+ * overlap each other (they share its workspace).  The host arrays of `list`
+ * may be freed after return.  Queries the current device's compute-unit
+ * count to size the persistent grid.                                      */
+int optim_plan_create(const optim_tensor_list *list, int32_t algo,
+                      const optim_plan_opts *opts, void *workspace,
+                      size_t workspace_bytes, void *stream, optim_plan **out);
+
+/* Frees the host plan object.  Work already enqueued is unaffected.      */
+int optim_plan_destroy(optim_plan *plan);
+
+/* Device learning-rate schedule ([AO]: the lr changes every step and must
+ * stay a device scalar updated in place, with no per-step allocation).
+ * OPTIM_SCHED_COSINE: at each step call the library reads k = *iter_dev,
+ * writes *lr_dev = fl32(lr_min + (lr_max - lr_min)*(1 + cos(pi*min(k,K)/K))/2)
+ * (evaluated in fp64) and stores k + 1 into *iter_dev -- also on a skipped
+ * step, since k counts loop iterations.  OPTIM_SCHED_NONE: *lr_dev is read
+ * as given.  iter_dev: device int32, caller-owned.                        */
+int optim_plan_set_schedule(optim_plan *plan, int32_t kind, double lr_max,
+                            double lr_min, int32_t K, int32_t *iter_dev);
+
+/* ---- steps --------------------------------------------------------------
+ * Common arguments:
+ *  lr_dev        device float learning rate (read; written when a schedule
+ *                is set)
+ *  inv_scale_dev device float; gradients are multiplied by it exactly once
+ *                ([LTN] analysis: the fused step does the unscale, so the
+ *                caller must not unscale first).  NULL = 1.
+ *  found_inf_dev device float; non-zero means skip: no parameter, state,
+ *                remainder, code or absmax byte is written and *step_dev is
+ *                not advanced.  NULL = never skip.
+ *  step_dev      device int32 count of applied steps; the step uses
+ *                t = *step_dev + 1 for bias correction and stores t.
+ * Per element (t-th applied step, g = grad * inv_scale):
+ *  m <- beta1 m + (1-beta1) g;  v <- beta2 v + (1-beta2) g^2
+ *  p <- p (1 - lr wd) - (lr / (1-beta1^t)) m / (sqrt(v)/sqrt(1-beta2^t) + eps)
+ * the decay taken from the previous p, in Loshchilov & Hutter Algorithm 2
+ * order ([BNB] PR description; [MINI] AdamWMini for bias correction and
+ * eps placement).  Bias corrections are evaluated in fp64 on the device and
+ * rounded once to fp32; the element math is fp32.  With BF16 params the
+ * fp32 master is rebuilt from (param, remainder), updated, and split back
+ * ([TE] description).                                                     */
+int optim_step_adamw(optim_plan *plan, const optim_adamw_hp *hp, float *lr_dev,
+                     const float *inv_scale_dev, const float *found_inf_dev,
+                     int32_t *step_dev, void *stream);
+
+/* AdEMAMix ([BNB] PR description and PR body): adds the slow EMA
+ *  m2 <- beta3 m2 + (1-beta3) g (no bias correction) and uses
+ *  p <- p (1 - lr wd) - lr (m/(1-beta1^t) + alpha m2) / (sqrt(v)/sqrt(1-beta2^t) + eps).
+ * alpha and beta3 are constants.                                          */
+int optim_step_ademamix(optim_plan *plan, const optim_ademamix_hp *hp,
+                        float *lr_dev, const float *inv_scale_dev,
+                        const float *found_inf_dev, int32_t *step_dev,
+                        void *stream);
+
+/* Adam-mini ([MINI] AdamWMini.step): FULL_V tensors take the AdamW step;
+ * HEAD tensors share one v per block of head_numel consecutive elements and
+ * SCALAR tensors one v for the whole tensor:
+ *  V_b <- beta2 V_b + (1-beta2) mean_{i in b}(g_i^2)
+ *  p <- p (1 - lr wd) - lr (m/(1-beta1^t)) / (sqrt(V_b)/sqrt(1-beta2^t) + eps).
+ * Block sums are reduced in a fixed order (deterministic).                */
+int optim_step_adam_mini(optim_plan *plan, const optim_adamw_hp *hp,
+                         float *lr_dev, const float *inv_scale_dev,
+                         const float *found_inf_dev, int32_t *step_dev,
+                         void *stream);
+
+/* Blockwise-quantized 2-state AdamW ([BNB]: the 2-state branch of the
+ * blockwise 8-bit kernel, same decay ordering; [AO]: 4-bit states).
+ * bits/block must equal the plan's.  Per block: dequantize m, v
+ * (x = fl32(+-M[idx] * absmax)), update them in fp32 without contraction
+ *  m = fl32(fl32(b1 m) + fl32(c1 g)), v = fl32(fl32(b2 v) + fl32(c2 fl32(g g)))
+ * with b1 = fl32(beta1), c1 = fl32(1-beta1) (likewise beta2), update p as
+ * in optim_step_adamw, then requantize: absmax A = max|x| over the block,
+ * a = fl32(|x| * fl32(1/A)), code = largest j with T[j] <= a (sign in the
+ * top bit for m; 0 if A = 0).  M and T are the tables optim_quant_codebook
+ * returns.                                                                */
+int optim_step_8bit_blockwise(optim_plan *plan, const optim_adamw_hp *hp,
+                              int32_t bits, int32_t block, float *lr_dev,
+                              const float *inv_scale_dev,
+                              const float *found_inf_dev, int32_t *step_dev,
+                              void *stream);
+
+/* ---- helpers ------------------------------------------------------------ */
+
+/* Sets *found_inf_dev = 1.0f if any gradient element of the plan is NaN or
+ * +-Inf ([LTN] analysis: the fused step consumes found_inf); otherwise
+ * leaves it unchanged, so the caller zeroes it first.                     */
+int optim_check_finite(optim_plan *plan, float *found_inf_dev, void *stream);
+
+/* [TE] description: fp32 master <-> (bf16 param, int16 remainder).  For the
+ * 32-bit pattern u of x: r = low 16 bits of u as int16, b = (high 16 bits of
+ * u) + (r < 0) mod 2^16, i.e. x rounded to bf16, nearest, ties away from
+ * zero.  reconstruct(split(x)) == x for every pattern.  n >= 0 elements;
+ * device arrays.                                                          */
+int optim_remainder_split(const float *master_dev, uint16_t *bf16_dev,
+                          int16_t *rem_dev, int64_t n, void *stream);
+int optim_remainder_reconstruct(const uint16_t *bf16_dev,
+                                const int16_t *rem_dev, float *master_dev,
+                                int64_t n, void *stream);
+
+/* Host: the dynamic quantization map the blockwise step uses.  bits 8 or
+ * 4; is_signed selects the map for m (sign bit + bits-1 magnitude bits) or
+ * for v (bits magnitude bits).  Writes the 2^mb sorted magnitudes
+ *  {0} U {10^-e (0.1 + 0.9 (k+1)/2^(mb-1-e)) : e < mb, k < 2^(mb-1-e)}
+ * (each evaluated in fp64, rounded to fp32) to values[2^mb] and the decision
+ * thresholds T[j] = fl32((M[j-1]+M[j])/2), T[0] = 0, to thresholds[2^mb].
+ * The map follows the dynamic (exponent + linear fraction) quantization of
+ * Dettmers et al., arXiv:2110.02861; the pages give no values.           */
+int optim_quant_codebook(int32_t bits, int32_t is_signed, float *values,
+                         float *thresholds);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OPTIM_STEP_H */

@@ -1,0 +1,543 @@
+// api.cpp -- C ABI of the fused AdamW-family optimizer step: validation,
+// plan tables (tensor descriptors, unit spans, weight-decay groups,
+// quantization tables), workspace layout and launches.  Declared in
+// include/optim_step.h, which documents each entry point and its sources.
+#include "optim_step.h"
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+using namespace optim;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string &msg) {
+    g_err = msg;
+    return code;
+}
+
+#define HIP_OK(expr)                                                                 \
+    do {                                                                             \
+        hipError_t e_ = (expr);                                                      \
+        if (e_ != hipSuccess)                                                        \
+            return fail(OPTIM_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+    } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------- codebook
+// Dynamic map with mb magnitude bits (see optim_quant_codebook).
+void dynamic_map(int mb, float *vals, float *thr) {
+    std::vector<float> M;
+    M.reserve(size_t(1) << mb);
+    M.push_back(0.0f);
+    for (int e = 0; e < mb; ++e) {
+        const int nk = 1 << (mb - 1 - e);
+        const double dec = std::pow(10.0, -(double)e);
+        for (int k = 0; k < nk; ++k)
+            M.push_back((float)(dec * (0.1 + 0.9 * (double)(k + 1) / (double)nk)));
+    }
+    std::sort(M.begin(), M.end());
+    for (size_t j = 0; j < M.size(); ++j) {
+        vals[j] = M[j];
+        thr[j] = j == 0 ? 0.0f : (float)(((double)M[j - 1] + (double)M[j]) * 0.5);
+    }
+}
+
+// ---------------------------------------------------------------- plan build
+struct Built {
+    std::vector<TensorDesc> tensors;
+    std::vector<SpanDesc> spans;  // with sentinel
+    std::vector<int32_t> blockspan;
+    std::vector<double> group_wd;
+    int64_t nunits = 0;
+    int32_t nblocks = 0;
+    Layout L{};
+};
+
+struct Range {
+    uintptr_t lo, hi;
+    bool written;
+    int tensor;
+    const char *what;
+};
+
+int check_hp_beta(double b, const char *name) {
+    if (!(b >= 0.0 && b < 1.0))
+        return fail(OPTIM_EINVAL, std::string("invalid ") + name + " (need 0 <= beta < 1)");
+    return OPTIM_OK;
+}
+
+int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *opts, Built &B) {
+    if (!list) return fail(OPTIM_EINVAL, "tensor list is NULL");
+    if (algo < OPTIM_ALGO_ADAMW || algo > OPTIM_ALGO_BLOCKWISE)
+        return fail(OPTIM_EINVAL, "unknown algorithm");
+    const int n = list->n;
+    if (n < 0) return fail(OPTIM_EINVAL, "negative tensor count");
+    if (list->param_dtype != OPTIM_F32 && list->param_dtype != OPTIM_BF16)
+        return fail(OPTIM_EDTYPE, "param_dtype must be OPTIM_F32 or OPTIM_BF16");
+    if (list->grad_dtype != OPTIM_F32 && list->grad_dtype != OPTIM_BF16)
+        return fail(OPTIM_EDTYPE, "grad_dtype must be OPTIM_F32 or OPTIM_BF16");
+    const bool bf16p = list->param_dtype == OPTIM_BF16;
+    if (bf16p && algo == OPTIM_ALGO_BLOCKWISE)
+        return fail(OPTIM_EUNSUPPORTED, "blockwise states take fp32 params only");
+    int bits = 0, block = 0;
+    if (algo == OPTIM_ALGO_BLOCKWISE) {
+        if (!opts) return fail(OPTIM_EINVAL, "blockwise plans need opts (bits, block)");
+        bits = opts->bits;
+        block = opts->block;
+        // a block is L = block/E lanes of one wavefront (E = 4 codes per lane
+        // for 8-bit, 8 for 4-bit), L a power of two in [16, 64]
+        if (bits != 8 && bits != 4) return fail(OPTIM_EINVAL, "bits must be 8 or 4");
+        const bool ok = bits == 8 ? (block == 64 || block == 128 || block == 256)
+                                  : (block == 128 || block == 256 || block == 512);
+        if (!ok)
+            return fail(OPTIM_EINVAL, bits == 8 ? "8-bit block must be 64, 128 or 256"
+                                                : "4-bit block must be 128, 256 or 512");
+    }
+    if (opts && opts->grid < 0) return fail(OPTIM_EINVAL, "negative grid");
+    if (n > 0 && (!list->numel || !list->param || !list->grad || !list->weight_decay))
+        return fail(OPTIM_EINVAL, "numel, param, grad and weight_decay arrays are required");
+    const bool need_mv = algo != OPTIM_ALGO_BLOCKWISE;
+    if (n > 0 && need_mv && (!list->m || !list->v)) return fail(OPTIM_EINVAL, "m and v arrays are required");
+    if (n > 0 && algo == OPTIM_ALGO_ADEMAMIX && !list->m2)
+        return fail(OPTIM_EINVAL, "AdEMAMix needs the m2 array");
+    if (n > 0 && algo == OPTIM_ALGO_BLOCKWISE &&
+        (!list->qm || !list->qv || !list->absmax_m || !list->absmax_v))
+        return fail(OPTIM_EINVAL, "blockwise plans need qm, qv, absmax_m and absmax_v");
+    if (n > 0 && algo == OPTIM_ALGO_ADAM_MINI && (!list->mini_kind || !list->head_numel))
+        return fail(OPTIM_EINVAL, "Adam-mini needs mini_kind and head_numel arrays");
+    if (n > 0 && bf16p && !list->remainder)
+        return fail(OPTIM_EUNSUPPORTED, "bf16 params need int16 remainders (fp32 master)");
+
+    const size_t psz = bf16p ? 2 : 4, gsz = list->grad_dtype == OPTIM_BF16 ? 2 : 4;
+    std::vector<Range> ranges;
+    B.tensors.assign(n, TensorDesc{});
+    B.spans.clear();
+    B.blockspan.clear();
+    B.group_wd.clear();
+    B.nunits = 0;
+    B.nblocks = 0;
+    for (int i = 0; i < n; ++i) {
+        const std::string ti = "tensor " + std::to_string(i) + ": ";
+        TensorDesc &T = B.tensors[i];
+        const int64_t numel = list->numel[i];
+        if (numel < 0) return fail(OPTIM_EINVAL, ti + "negative numel");
+        const double wd = list->weight_decay[i];
+        if (!(wd >= 0.0) || !std::isfinite(wd)) return fail(OPTIM_EINVAL, ti + "invalid weight_decay");
+        auto git = std::find(B.group_wd.begin(), B.group_wd.end(), wd);
+        if (git == B.group_wd.end()) {
+            if ((int)B.group_wd.size() >= kMaxGroups)
+                return fail(OPTIM_EUNSUPPORTED, "more than 64 distinct weight_decay values");
+            B.group_wd.push_back(wd);
+            git = B.group_wd.end() - 1;
+        }
+        T.group = (int32_t)(git - B.group_wd.begin());
+        T.numel = numel;
+        T.p = list->param[i];
+        T.g = list->grad[i];
+        if (numel > 0 && (!T.p || !T.g)) return fail(OPTIM_EINVAL, ti + "NULL param or grad");
+        if (!aligned(T.p, psz) || !aligned(T.g, gsz)) return fail(OPTIM_EALIGN, ti + "param/grad misaligned");
+        bool vec = aligned(T.p, 16) && aligned(T.g, 16);
+        auto add = [&](const void *ptr, size_t bytes, bool written, const char *what) {
+            if (ptr && bytes) ranges.push_back({(uintptr_t)ptr, (uintptr_t)ptr + bytes, written, i, what});
+        };
+        add(T.p, numel * psz, true, "param");
+        add(T.g, numel * gsz, false, "grad");
+        if (bf16p) {
+            T.rem = static_cast<uint16_t *>(list->remainder[i]);
+            if (numel > 0 && !T.rem) return fail(OPTIM_EINVAL, ti + "NULL remainder");
+            if (!aligned(T.rem, 2)) return fail(OPTIM_EALIGN, ti + "remainder misaligned");
+            vec = vec && aligned(T.rem, 16);
+            add(T.rem, numel * 2, true, "remainder");
+        } else if (list->remainder && list->remainder[i]) {
+            return fail(OPTIM_EINVAL, ti + "remainder given for fp32 params");
+        }
+        int32_t kind = OPTIM_MINI_FULL_V;
+        int64_t vlen = numel;
+        if (algo == OPTIM_ALGO_ADAM_MINI) {
+            kind = list->mini_kind[i];
+            if (kind == OPTIM_MINI_HEAD) {
+                const int64_t h = list->head_numel[i];
+                if (h <= 0 || numel % h != 0)
+                    return fail(OPTIM_EINVAL, ti + "head_numel must be > 0 and divide numel");
+                T.block_len = h;
+                vlen = numel / h;
+            } else if (kind == OPTIM_MINI_SCALAR) {
+                T.block_len = numel;
+                vlen = numel > 0 ? 1 : 0;
+            } else if (kind == OPTIM_MINI_FULL_V) {
+                T.block_len = 0;
+            } else {
+                return fail(OPTIM_EINVAL, ti + "unknown mini_kind");
+            }
+        }
+        T.kind = kind;
+        if (need_mv) {
+            T.m = static_cast<float *>(list->m[i]);
+            T.v = static_cast<float *>(list->v[i]);
+            if (numel > 0 && (!T.m || !T.v)) return fail(OPTIM_EINVAL, ti + "NULL m or v");
+            if (!aligned(T.m, 4) || !aligned(T.v, 4)) return fail(OPTIM_EALIGN, ti + "m/v misaligned");
+            vec = vec && aligned(T.m, 16) && (kind != OPTIM_MINI_FULL_V || aligned(T.v, 16));
+            add(T.m, numel * 4, true, "m");
+            add(T.v, vlen * 4, true, "v");
+        }
+        if (algo == OPTIM_ALGO_ADEMAMIX) {
+            T.m2 = static_cast<float *>(list->m2[i]);
+            if (numel > 0 && !T.m2) return fail(OPTIM_EINVAL, ti + "NULL m2");
+            if (!aligned(T.m2, 4)) return fail(OPTIM_EALIGN, ti + "m2 misaligned");
+            vec = vec && aligned(T.m2, 16);
+            add(T.m2, numel * 4, true, "m2");
+        }
+        if (algo == OPTIM_ALGO_BLOCKWISE) {
+            T.qm = static_cast<uint8_t *>(list->qm[i]);
+            T.qv = static_cast<uint8_t *>(list->qv[i]);
+            T.am = list->absmax_m[i];
+            T.av = list->absmax_v[i];
+            if (numel > 0 && (!T.qm || !T.qv || !T.am || !T.av))
+                return fail(OPTIM_EINVAL, ti + "NULL code or absmax buffer");
+            if (!aligned(T.am, 4) || !aligned(T.av, 4)) return fail(OPTIM_EALIGN, ti + "absmax misaligned");
+            vec = vec && aligned(T.qm, 16) && aligned(T.qv, 16);
+            const int64_t cbytes = (numel * bits + 7) / 8;
+            const int64_t nblk = (numel + block - 1) / block;
+            add(T.qm, cbytes, true, "qm");
+            add(T.qv, cbytes, true, "qv");
+            add(T.am, nblk * 4, true, "absmax_m");
+            add(T.av, nblk * 4, true, "absmax_v");
+        }
+        T.vec_ok = vec ? 1 : 0;
+        if (numel == 0) continue;
+        // spans
+        if (algo == OPTIM_ALGO_ADAM_MINI && kind != OPTIM_MINI_FULL_V) {
+            for (int64_t s = 0; s < numel; s += T.block_len) {
+                SpanDesc sp{B.nunits, s, T.block_len, i, B.nblocks};
+                B.blockspan.push_back((int32_t)B.spans.size());
+                B.spans.push_back(sp);
+                B.nunits += (T.block_len + kTile - 1) / kTile;
+                if (B.nblocks == INT32_MAX) return fail(OPTIM_EUNSUPPORTED, "too many blocks");
+                ++B.nblocks;
+            }
+        } else {
+            B.spans.push_back(SpanDesc{B.nunits, 0, numel, i, -1});
+            B.nunits += (numel + kTile - 1) / kTile;
+        }
+    }
+    if (B.spans.size() >= (size_t)INT32_MAX) return fail(OPTIM_EUNSUPPORTED, "too many spans");
+    B.spans.push_back(SpanDesc{B.nunits, 0, 0, -1, -1});  // sentinel
+
+    // no written buffer may overlap any other buffer of the plan
+    std::sort(ranges.begin(), ranges.end(), [](const Range &a, const Range &b) { return a.lo < b.lo; });
+    uintptr_t end_all = 0, end_w = 0;
+    const Range *cov_all = nullptr, *cov_w = nullptr;
+    for (const Range &r : ranges) {
+        const Range *hit = nullptr;
+        if (r.written && r.lo < end_all) hit = cov_all;
+        else if (!r.written && r.lo < end_w) hit = cov_w;
+        if (hit)
+            return fail(OPTIM_EINVAL, "buffers overlap: tensor " + std::to_string(hit->tensor) + " " +
+                                          hit->what + " and tensor " + std::to_string(r.tensor) + " " +
+                                          r.what);
+        if (r.hi > end_all) { end_all = r.hi; cov_all = &r; }
+        if (r.written && r.hi > end_w) { end_w = r.hi; cov_w = &r; }
+    }
+
+    Layout &L = B.L;
+    size_t off = 0;
+    L.scalars = off; off += align256(sizeof(Scalars));
+    L.group_wd = off; off += align256(kMaxGroups * sizeof(double));
+    L.tensors = off; off += align256(std::max<size_t>(1, B.tensors.size()) * sizeof(TensorDesc));
+    L.spans = off; off += align256(B.spans.size() * sizeof(SpanDesc));
+    L.codebook = off; off += algo == OPTIM_ALGO_BLOCKWISE ? align256(kCbFloats * sizeof(float)) : 0;
+    L.blockspan = off; off += align256(std::max<size_t>(1, B.blockspan.size()) * sizeof(int32_t));
+    L.partials = off;
+    off += algo == OPTIM_ALGO_ADAM_MINI ? align256(std::max<int64_t>(1, B.nunits) * sizeof(double)) : 0;
+    L.blockfac = off; off += align256(std::max<int32_t>(1, B.nblocks) * sizeof(float));
+    L.total = off;
+    return OPTIM_OK;
+}
+
+}  // namespace
+
+struct optim_plan {
+    int32_t algo;
+    int32_t pk, gk;
+    int32_t bits, block;
+    int32_t grid;  // requested persistent workgroups (0 = from occupancy)
+    int32_t cus;
+    int32_t nspans, nblocks, ngroups;
+    int64_t nunits;
+    char *ws;
+    Layout L;
+    int32_t sched;
+    double lr_max, lr_min;
+    int32_t K;
+    int32_t *iter_dev;
+};
+
+extern "C" {
+
+const char *optim_last_error(void) { return g_err.c_str(); }
+
+int optim_quant_codebook(int32_t bits, int32_t is_signed, float *values, float *thresholds) {
+    if (bits != 8 && bits != 4) return fail(OPTIM_EINVAL, "bits must be 8 or 4");
+    if (!values || !thresholds) return fail(OPTIM_EINVAL, "NULL output");
+    dynamic_map(is_signed ? bits - 1 : bits, values, thresholds);
+    return OPTIM_OK;
+}
+
+int optim_plan_workspace_size(const optim_tensor_list *list, int32_t algo,
+                              const optim_plan_opts *opts, size_t *bytes) {
+    if (!bytes) return fail(OPTIM_EINVAL, "bytes is NULL");
+    Built B;
+    const int rc = build(list, algo, opts, B);
+    if (rc) return rc;
+    *bytes = B.L.total;
+    return OPTIM_OK;
+}
+
+int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *opts,
+                      void *workspace, size_t workspace_bytes, void *stream, optim_plan **out) {
+    if (!out) return fail(OPTIM_EINVAL, "out is NULL");
+    *out = nullptr;
+    Built B;
+    int rc = build(list, algo, opts, B);
+    if (rc) return rc;
+    if (!workspace || !aligned(workspace, 256))
+        return fail(OPTIM_EWORKSPACE, "workspace must be a 256-byte aligned device pointer");
+    if (workspace_bytes < B.L.total)
+        return fail(OPTIM_EWORKSPACE, "workspace too small: need " + std::to_string(B.L.total) +
+                                          " bytes, got " + std::to_string(workspace_bytes));
+    // host image of the table region [0, partials)
+    std::vector<char> img(B.L.partials, 0);
+    std::memcpy(img.data() + B.L.group_wd, B.group_wd.data(), B.group_wd.size() * sizeof(double));
+    std::memcpy(img.data() + B.L.tensors, B.tensors.data(), B.tensors.size() * sizeof(TensorDesc));
+    std::memcpy(img.data() + B.L.spans, B.spans.data(), B.spans.size() * sizeof(SpanDesc));
+    std::memcpy(img.data() + B.L.blockspan, B.blockspan.data(), B.blockspan.size() * sizeof(int32_t));
+    if (algo == OPTIM_ALGO_BLOCKWISE) {
+        float *cb = reinterpret_cast<float *>(img.data() + B.L.codebook);
+        dynamic_map(7, cb + kCb8SignedVals, cb + kCb8SignedThr);
+        dynamic_map(8, cb + kCb8UnsVals, cb + kCb8UnsThr);
+        dynamic_map(3, cb + kCb4SignedVals, cb + kCb4SignedThr);
+        dynamic_map(4, cb + kCb4UnsVals, cb + kCb4UnsThr);
+    }
+    int dev = 0, cus = 0;
+    HIP_OK(hipGetDevice(&dev));
+    HIP_OK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    HIP_OK(hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice, s));
+    HIP_OK(hipStreamSynchronize(s));
+
+    optim_plan *P = new (std::nothrow) optim_plan{};
+    if (!P) return fail(OPTIM_EINVAL, "out of host memory");
+    P->algo = algo;
+    P->pk = list->param_dtype == OPTIM_BF16 ? P_BF16R : P_F32;
+    P->gk = list->grad_dtype == OPTIM_BF16 ? G_BF16 : G_F32;
+    P->bits = opts ? opts->bits : 0;
+    P->block = opts ? opts->block : 0;
+    P->grid = opts ? opts->grid : 0;
+    P->cus = cus;
+    P->nspans = (int32_t)B.spans.size() - 1;
+    P->nblocks = B.nblocks;
+    P->ngroups = (int32_t)B.group_wd.size();
+    P->nunits = B.nunits;
+    P->ws = static_cast<char *>(workspace);
+    P->L = B.L;
+    P->sched = OPTIM_SCHED_NONE;
+    *out = P;
+    return OPTIM_OK;
+}
+
+int optim_plan_destroy(optim_plan *plan) {
+    delete plan;
+    return OPTIM_OK;
+}
+
+int optim_plan_set_schedule(optim_plan *plan, int32_t kind, double lr_max, double lr_min, int32_t K,
+                            int32_t *iter_dev) {
+    if (!plan) return fail(OPTIM_EINVAL, "plan is NULL");
+    if (kind == OPTIM_SCHED_NONE) {
+        plan->sched = OPTIM_SCHED_NONE;
+        plan->iter_dev = nullptr;
+        return OPTIM_OK;
+    }
+    if (kind != OPTIM_SCHED_COSINE) return fail(OPTIM_EINVAL, "unknown schedule kind");
+    if (!(lr_max >= 0.0) || !(lr_min >= 0.0) || !std::isfinite(lr_max) || !std::isfinite(lr_min))
+        return fail(OPTIM_EINVAL, "invalid learning rate (need 0 <= lr, finite)");
+    if (K <= 0) return fail(OPTIM_EINVAL, "schedule length K must be > 0");
+    if (!iter_dev || !aligned(iter_dev, 4)) return fail(OPTIM_EINVAL, "iter_dev must be an aligned device int32");
+    plan->sched = kind;
+    plan->lr_max = lr_max;
+    plan->lr_min = lr_min;
+    plan->K = K;
+    plan->iter_dev = iter_dev;
+    return OPTIM_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+StepArgs step_args(optim_plan *P) {
+    StepArgs a{};
+    a.tensors = reinterpret_cast<const TensorDesc *>(P->ws + P->L.tensors);
+    a.spans = reinterpret_cast<const SpanDesc *>(P->ws + P->L.spans);
+    a.nspans = P->nspans;
+    a.nunits = P->nunits;
+    a.sc = reinterpret_cast<const Scalars *>(P->ws + P->L.scalars);
+    a.partials = reinterpret_cast<double *>(P->ws + P->L.partials);
+    a.blockfac = reinterpret_cast<float *>(P->ws + P->L.blockfac);
+    a.blockspan = reinterpret_cast<const int32_t *>(P->ws + P->L.blockspan);
+    a.nblocks = P->nblocks;
+    a.codebook = reinterpret_cast<const float *>(P->ws + P->L.codebook);
+    a.bits = P->bits;
+    a.block = P->block;
+    a.cus = P->cus;
+    a.grid_request = P->grid;
+    return a;
+}
+
+int prep(optim_plan *P, double b1, double b2, double b3, double alpha, double eps, float *lr_dev,
+         const float *inv_scale, const float *found_inf, int32_t *step_dev, hipStream_t s) {
+    if (!lr_dev || !aligned(lr_dev, 4)) return fail(OPTIM_EINVAL, "lr_dev must be an aligned device float");
+    if (!step_dev || !aligned(step_dev, 4)) return fail(OPTIM_EINVAL, "step_dev must be an aligned device int32");
+    if (!aligned(inv_scale, 4) || !aligned(found_inf, 4)) return fail(OPTIM_EALIGN, "scalar pointer misaligned");
+    if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(OPTIM_EINVAL, "invalid eps (need finite eps >= 0)");
+    PrepArgs a{};
+    a.sc = reinterpret_cast<Scalars *>(P->ws + P->L.scalars);
+    a.group_wd = reinterpret_cast<const double *>(P->ws + P->L.group_wd);
+    a.ngroups = P->ngroups;
+    a.sched = P->sched;
+    a.lr_dev = lr_dev;
+    a.inv_scale = inv_scale;
+    a.found_inf = found_inf;
+    a.step_dev = step_dev;
+    a.iter_dev = P->iter_dev;
+    a.lr_max = P->lr_max;
+    a.lr_min = P->lr_min;
+    a.K = P->K;
+    a.beta1 = b1;
+    a.beta2 = b2;
+    a.beta3 = b3;
+    a.alpha = alpha;
+    a.eps = eps;
+    HIP_OK(launch_prep(a, s));
+    return OPTIM_OK;
+}
+
+int check_plan(optim_plan *P, int32_t algo, const char *fn) {
+    if (!P) return fail(OPTIM_EINVAL, std::string(fn) + ": plan is NULL");
+    if (P->algo != algo) return fail(OPTIM_EINVAL, std::string(fn) + ": plan was built for another algorithm");
+    return OPTIM_OK;
+}
+
+int check_adamw_hp(const optim_adamw_hp *hp) {
+    if (!hp) return fail(OPTIM_EINVAL, "hyperparameters are NULL");
+    int rc = check_hp_beta(hp->beta1, "beta1");
+    if (rc) return rc;
+    return check_hp_beta(hp->beta2, "beta2");
+}
+
+}  // namespace
+
+extern "C" {
+
+int optim_step_adamw(optim_plan *plan, const optim_adamw_hp *hp, float *lr_dev, const float *inv_scale_dev,
+                     const float *found_inf_dev, int32_t *step_dev, void *stream) {
+    int rc = check_plan(plan, OPTIM_ALGO_ADAMW, "optim_step_adamw");
+    if (!rc) rc = check_adamw_hp(hp);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = prep(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev, step_dev, s);
+    if (rc) return rc;
+    if (plan->nunits > 0) HIP_OK(launch_adamw(step_args(plan), plan->pk, plan->gk, s));
+    return OPTIM_OK;
+}
+
+int optim_step_ademamix(optim_plan *plan, const optim_ademamix_hp *hp, float *lr_dev,
+                        const float *inv_scale_dev, const float *found_inf_dev, int32_t *step_dev,
+                        void *stream) {
+    int rc = check_plan(plan, OPTIM_ALGO_ADEMAMIX, "optim_step_ademamix");
+    if (rc) return rc;
+    if (!hp) return fail(OPTIM_EINVAL, "hyperparameters are NULL");
+    if ((rc = check_hp_beta(hp->beta1, "beta1")) || (rc = check_hp_beta(hp->beta2, "beta2")) ||
+        (rc = check_hp_beta(hp->beta3, "beta3")))
+        return rc;
+    if (!std::isfinite(hp->alpha) || hp->alpha < 0.0) return fail(OPTIM_EINVAL, "invalid alpha (need finite alpha >= 0)");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = prep(plan, hp->beta1, hp->beta2, hp->beta3, hp->alpha, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
+              step_dev, s);
+    if (rc) return rc;
+    if (plan->nunits > 0) HIP_OK(launch_ademamix(step_args(plan), plan->pk, plan->gk, s));
+    return OPTIM_OK;
+}
+
+int optim_step_adam_mini(optim_plan *plan, const optim_adamw_hp *hp, float *lr_dev, const float *inv_scale_dev,
+                         const float *found_inf_dev, int32_t *step_dev, void *stream) {
+    int rc = check_plan(plan, OPTIM_ALGO_ADAM_MINI, "optim_step_adam_mini");
+    if (!rc) rc = check_adamw_hp(hp);
+    if (rc) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = prep(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev, step_dev, s);
+    if (rc) return rc;
+    if (plan->nunits > 0) HIP_OK(launch_adam_mini(step_args(plan), plan->pk, plan->gk, s));
+    return OPTIM_OK;
+}
+
+int optim_step_8bit_blockwise(optim_plan *plan, const optim_adamw_hp *hp, int32_t bits, int32_t block,
+                              float *lr_dev, const float *inv_scale_dev, const float *found_inf_dev,
+                              int32_t *step_dev, void *stream) {
+    int rc = check_plan(plan, OPTIM_ALGO_BLOCKWISE, "optim_step_8bit_blockwise");
+    if (!rc) rc = check_adamw_hp(hp);
+    if (rc) return rc;
+    if (bits != plan->bits || block != plan->block)
+        return fail(OPTIM_EINVAL, "bits/block differ from the plan's");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = prep(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev, step_dev, s);
+    if (rc) return rc;
+    if (plan->nunits > 0) HIP_OK(launch_blockwise(step_args(plan), plan->gk, s));
+    return OPTIM_OK;
+}
+
+int optim_check_finite(optim_plan *plan, float *found_inf_dev, void *stream) {
+    if (!plan) return fail(OPTIM_EINVAL, "plan is NULL");
+    if (!found_inf_dev || !aligned(found_inf_dev, 4))
+        return fail(OPTIM_EINVAL, "found_inf_dev must be an aligned device float");
+    if (plan->nunits == 0) return OPTIM_OK;
+    StepArgs a = step_args(plan);
+    a.found_inf = found_inf_dev;
+    HIP_OK(launch_check_finite(a, plan->gk, static_cast<hipStream_t>(stream)));
+    return OPTIM_OK;
+}
+
+int optim_remainder_split(const float *master_dev, uint16_t *bf16_dev, int16_t *rem_dev, int64_t n,
+                          void *stream) {
+    if (n < 0) return fail(OPTIM_EINVAL, "negative n");
+    if (n == 0) return OPTIM_OK;
+    if (!master_dev || !bf16_dev || !rem_dev) return fail(OPTIM_EINVAL, "NULL buffer");
+    if (!aligned(master_dev, 4) || !aligned(bf16_dev, 2) || !aligned(rem_dev, 2))
+        return fail(OPTIM_EALIGN, "buffer misaligned");
+    HIP_OK(launch_remainder_split(master_dev, bf16_dev, rem_dev, n, static_cast<hipStream_t>(stream)));
+    return OPTIM_OK;
+}
+
+int optim_remainder_reconstruct(const uint16_t *bf16_dev, const int16_t *rem_dev, float *master_dev, int64_t n,
+                                void *stream) {
+    if (n < 0) return fail(OPTIM_EINVAL, "negative n");
+    if (n == 0) return OPTIM_OK;
+    if (!master_dev || !bf16_dev || !rem_dev) return fail(OPTIM_EINVAL, "NULL buffer");
+    if (!aligned(master_dev, 4) || !aligned(bf16_dev, 2) || !aligned(rem_dev, 2))
+        return fail(OPTIM_EALIGN, "buffer misaligned");
+    HIP_OK(launch_remainder_reconstruct(bf16_dev, rem_dev, master_dev, n, static_cast<hipStream_t>(stream)));
+    return OPTIM_OK;
+}
+
+}  // extern "C"

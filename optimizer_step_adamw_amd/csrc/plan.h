@@ -1,0 +1,124 @@
+// plan.h -- device-visible plan tables shared by the C-ABI host layer
+// (api.cpp) and the gfx950 kernels (kernels.hip).  Internal; not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace optim {
+
+// Work decomposition: every tensor (Adam-mini: every shared-v block) is a
+// "span"; a span is cut into units of kTile consecutive elements (the last
+// one ragged).  Units are numbered globally; a persistent workgroup owns a
+// contiguous range of unit numbers.
+constexpr int kThreads = 256;     // workgroup size (4 wavefronts of 64)
+constexpr int64_t kTile = 4096;   // elements per unit
+constexpr int kMaxGroups = 64;    // distinct weight-decay values per plan
+
+enum ParamKind { P_F32 = 0, P_BF16R = 1 };  // fp32, or bf16 + int16 remainder
+enum GradKind { G_F32 = 0, G_BF16 = 1 };
+
+struct TensorDesc {       // 128 bytes
+    void *p;              // param (fp32 or bf16 patterns)
+    const void *g;        // gradient
+    float *m;             // first moment
+    float *v;             // second moment (Adam-mini HEAD/SCALAR: per block)
+    float *m2;            // AdEMAMix slow EMA
+    uint16_t *rem;        // int16 remainder (as raw 16-bit patterns)
+    uint8_t *qm, *qv;     // blockwise codes
+    float *am, *av;       // blockwise absmax
+    int64_t numel;
+    int64_t block_len;    // Adam-mini shared-v block length (0 = full v)
+    int32_t group;        // weight-decay group
+    int32_t kind;         // Adam-mini partition
+    int32_t vec_ok;       // every pointer 16-byte aligned
+    int32_t pad_[5];
+};
+static_assert(sizeof(TensorDesc) == 128, "TensorDesc layout");
+
+struct SpanDesc {         // 32 bytes
+    int64_t unit_begin;   // first global unit number of this span
+    int64_t elem_begin;   // first element, relative to the tensor
+    int64_t len;          // elements in the span
+    int32_t tensor;       // index into the tensor table
+    int32_t block;        // Adam-mini global block number, -1 for full v
+};
+static_assert(sizeof(SpanDesc) == 32, "SpanDesc layout");
+
+// Per-step scalars, written by the prep kernel at the start of every step
+// and read (uniformly) by the step kernels of that step.
+struct Scalars {
+    int32_t skip;         // non-zero: found_inf was set, write nothing
+    int32_t t;            // applied-step count including this step
+    float lr;
+    float step_size;      // fl32(lr / (1 - beta1^t))
+    float inv_sqrt_bc2;   // fl32(1 / sqrt(1 - beta2^t))
+    float inv_bc1;        // fl32(1 / (1 - beta1^t))
+    float b1, c1;         // fl32(beta1), fl32(1 - beta1)
+    float b2, c2;
+    float b3, c3;         // AdEMAMix
+    float alpha;
+    float eps;
+    float inv_scale;      // gradient multiplier (AMP unscale), 1 if none
+    float pad0_;
+    double lr64, step_size64, inv_sqrt_bc2_64, eps64, beta2_64, c2_64;
+    float decay[kMaxGroups];  // fl32(1 - lr * wd_group)
+};
+
+// Workspace layout (byte offsets from the workspace base, 256-aligned).
+struct Layout {
+    size_t scalars, group_wd, tensors, spans, codebook, partials, blockfac,
+        blockspan, total;
+};
+
+// Codebook region: signed map for m then unsigned map for v, values then
+// thresholds, for 8-bit followed by 4-bit.
+constexpr int kCb8SignedVals = 0, kCb8SignedThr = 128, kCb8UnsVals = 256,
+              kCb8UnsThr = 512, kCb4SignedVals = 768, kCb4SignedThr = 776,
+              kCb4UnsVals = 784, kCb4UnsThr = 800, kCbFloats = 816;
+
+struct PrepArgs {
+    Scalars *sc;
+    const double *group_wd;
+    int32_t ngroups;
+    int32_t sched;        // OPTIM_SCHED_*
+    float *lr_dev;
+    const float *inv_scale;
+    const float *found_inf;
+    int32_t *step_dev;
+    int32_t *iter_dev;
+    double lr_max, lr_min;
+    int32_t K;
+    double beta1, beta2, beta3, alpha, eps;
+};
+
+struct StepArgs {
+    const TensorDesc *tensors;
+    const SpanDesc *spans;    // nspans + 1 entries (sentinel at the end)
+    int32_t nspans;
+    int64_t nunits;
+    const Scalars *sc;
+    double *partials;         // Adam-mini: one per unit
+    float *blockfac;          // Adam-mini: per block lr/bc1/h
+    const int32_t *blockspan; // Adam-mini: span index of each block
+    int32_t nblocks;
+    const float *codebook;
+    int32_t bits, block;
+    float *found_inf;         // finite check output
+    int32_t cus;              // compute units of the device
+    int32_t grid_request;     // persistent workgroups requested (0 = auto)
+};
+
+// Launchers (kernels.hip).  Return the hipError_t of the launch.
+hipError_t launch_prep(const PrepArgs &a, hipStream_t s);
+hipError_t launch_adamw(const StepArgs &a, int pk, int gk, hipStream_t s);
+hipError_t launch_ademamix(const StepArgs &a, int pk, int gk, hipStream_t s);
+hipError_t launch_adam_mini(const StepArgs &a, int pk, int gk, hipStream_t s);
+hipError_t launch_blockwise(const StepArgs &a, int gk, hipStream_t s);
+hipError_t launch_check_finite(const StepArgs &a, int gk, hipStream_t s);
+hipError_t launch_remainder_split(const float *x, uint16_t *b, int16_t *r, int64_t n,
+                                  hipStream_t s);
+hipError_t launch_remainder_reconstruct(const uint16_t *b, const int16_t *r, float *x,
+                                        int64_t n, hipStream_t s);
+
+}  // namespace optim

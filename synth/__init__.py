@@ -9,9 +9,10 @@ stream 0 = initial parameters, 1 = gradients, 2 = inf-injection site.
 "N(0, s)" means a normal with standard deviation s: float64 normals are scaled
 by s and rounded once to float32.
 
-Host draws use numpy PCG64 keyed by a SeedSequence.  Device draws (for the
-billion-element lists, where host RNG is too slow) use torch's generator on
-the device seeded from the same key; which one a test used is stated there.
+Host draws use numpy PCG64 keyed by a SeedSequence (float64 normal * std,
+rounded to float32).  Device draws (for the billion-element lists, where host
+RNG is too slow) use torch's float32 generator on the device seeded from the
+same key; which one a test used is stated there.
 """
 from __future__ import annotations
 
@@ -39,17 +40,14 @@ def host_normal(n: int, std: float, *key: int) -> np.ndarray:
 
 
 def device_normal(n: int, std: float, device, *key: int):
-    """Same distribution drawn on a torch device (float64 normal * std -> fp32)."""
+    """N(0, std) drawn on a torch device: float32 normals from torch's
+    generator seeded with the key, times std in float32 (used for the
+    billion-element lists, where host generation is too slow)."""
     import torch
     gen = torch.Generator(device=device)
     gen.manual_seed(key_seed(*key))
-    out = torch.empty(n, dtype=torch.float32, device=device)
-    # draw in slices so the float64 temporary stays bounded
-    CH = 1 << 26
-    for s in range(0, n, CH):
-        e = min(n, s + CH)
-        out[s:e] = (torch.randn(e - s, dtype=torch.float64, device=device, generator=gen)
-                    * std).to(torch.float32)
+    out = torch.randn(n, dtype=torch.float32, device=device, generator=gen)
+    out.mul_(std)
     return out
 
 

@@ -1,0 +1,151 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and its host-only entry points (codebook, plan sizing
+and validation) behave.  Device pointers here are fake integers: the
+size query validates and lays out a plan without touching the device."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import optimizer_step_adamw_amd as osa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(osa.LIB_PATH):
+        osa.build_library()
+    return osa.lib()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "optim_step.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(optim_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_function(L):
+    declared = header_functions()
+    assert len(declared) == 13, declared
+    assert sorted(osa.EXPORTED) == declared
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+@pytest.mark.parametrize("bits,signed", [(8, True), (8, False), (4, True), (4, False)])
+def test_codebook_matches_oracle(L, orc, bits, signed):
+    """Two independent implementations of the same map definition."""
+    vals, thr = osa.optim_quant_codebook(bits, signed)
+    mb = bits - 1 if signed else bits
+    M = orc.dynamic_map(mb)
+    assert np.array_equal(vals.view(np.uint32), M.view(np.uint32))
+    assert np.array_equal(thr[1:].view(np.uint32), orc.thresholds(M)[1:].view(np.uint32))
+
+
+class Fake:
+    """Non-overlapping fake device addresses."""
+
+    def __init__(self):
+        self.next = 1 << 40
+
+    def __call__(self, nbytes, misalign=0):
+        a = self.next + misalign
+        self.next += ((nbytes + 4095) // 4096 + 1) * 4096
+        return a
+
+
+def fake_list(sizes, algo=osa.OPTIM_ALGO_ADAMW, fake=None, **kw):
+    fake = fake or Fake()
+    n = len(sizes)
+    args = dict(params=[fake(4 * s) for s in sizes], grads=[fake(4 * s) for s in sizes],
+                m=[fake(4 * s) for s in sizes], v=[fake(4 * s) for s in sizes],
+                weight_decay=[0.01] * n, numel=sizes)
+    if algo == osa.OPTIM_ALGO_ADEMAMIX:
+        args["m2"] = [fake(4 * s) for s in sizes]
+    args.update(kw)
+    return osa.TensorList(**args)
+
+
+def ws(tl, algo, opts=None):
+    return osa.optim_plan_workspace_size(tl, algo, opts)
+
+
+def expect_error(code, fn):
+    with pytest.raises(osa.OptimError) as ei:
+        fn()
+    assert ei.value.code == code, str(ei.value)
+    assert len(str(ei.value)) > 20
+
+
+def test_workspace_size_grows_with_units(L):
+    a = ws(fake_list([4096]), osa.OPTIM_ALGO_ADAMW)
+    b = ws(fake_list([4096] * 300), osa.OPTIM_ALGO_ADAMW)
+    assert 0 < a < b
+    assert ws(osa.TensorList([], [], weight_decay=[], numel=[]), osa.OPTIM_ALGO_ADAMW) > 0
+
+
+def test_validation_codes(L):
+    f = Fake()
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([-1]), osa.OPTIM_ALGO_ADAMW))
+    expect_error(osa.OPTIM_EALIGN, lambda: ws(
+        fake_list([8], params=[f(32, misalign=2)]), osa.OPTIM_ALGO_ADAMW))
+    # a gradient that aliases another tensor's moment buffer
+    fk = Fake()
+    tl = fake_list([1024, 1024], fake=fk)
+    m0 = tl.struct.m[0]
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(
+        fake_list([1024, 1024], grads=[f(4096), m0 + 64]), osa.OPTIM_ALGO_ADAMW))
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([8], weight_decay=[-0.1]), osa.OPTIM_ALGO_ADAMW))
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([8]), osa.OPTIM_ALGO_ADEMAMIX))  # no m2
+    expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(
+        fake_list([8] * 65, weight_decay=[i * 1e-3 for i in range(65)]), osa.OPTIM_ALGO_ADAMW))
+    expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(
+        fake_list([8], param_dtype=osa.OPTIM_BF16), osa.OPTIM_ALGO_ADAMW))  # no remainder
+    expect_error(osa.OPTIM_EDTYPE, lambda: ws(fake_list([8], grad_dtype=7), osa.OPTIM_ALGO_ADAMW))
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([8]), 9))
+
+
+def test_adam_mini_validation(L):
+    kinds = [osa.OPTIM_MINI_HEAD]
+    ok = fake_list([4096], mini_kind=kinds, head_numel=[512])
+    assert ws(ok, osa.OPTIM_ALGO_ADAM_MINI) > 0
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(
+        fake_list([4096], mini_kind=kinds, head_numel=[500]), osa.OPTIM_ALGO_ADAM_MINI))
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(
+        fake_list([4096], mini_kind=[7], head_numel=[0]), osa.OPTIM_ALGO_ADAM_MINI))
+
+
+def test_blockwise_validation(L):
+    f = Fake()
+    n = 1000
+    kw = dict(m=None, v=None, qm=[f(n)], qv=[f(n)], absmax_m=[f(64)], absmax_v=[f(64)])
+    for bits, block in ((8, 256), (8, 64), (4, 128), (4, 512)):
+        assert ws(fake_list([n], fake=f, **kw), osa.OPTIM_ALGO_BLOCKWISE,
+                  osa.optim_plan_opts(bits, block, 0)) > 0
+    for bits, block in ((8, 512), (4, 64), (6, 256), (8, 100)):
+        expect_error(osa.OPTIM_EINVAL, lambda: ws(
+            fake_list([n], fake=f, **kw), osa.OPTIM_ALGO_BLOCKWISE, osa.optim_plan_opts(bits, block, 0)))
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, **kw), osa.OPTIM_ALGO_BLOCKWISE, None))
+    # the codes of one tensor overlapping its own parameter
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(
+        fake_list([n], **kw), osa.OPTIM_ALGO_BLOCKWISE, osa.optim_plan_opts(8, 256, 0)))
+
+
+def test_null_plan_is_rejected_without_device(L):
+    expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_step_adamw(
+        None, osa.optim_adamw_hp(0.9, 0.999, 1e-8), 1 << 40, None, None, 1 << 41, 0))
+    expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_plan_set_schedule(None, 1, 1e-3, 0.0, 10, 1 << 40))
+    expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_remainder_split(0, 0, 0, -1, 0))
+
+
+def test_product_partition_by_name():
+    names = ["tok_embeddings.weight", "layers.0.attention.wq.weight", "layers.0.attention.wk.weight",
+             "layers.0.attention.wv.weight", "layers.0.attention_norm.weight", "output.weight"]
+    numels = [32 * 64, 64 * 64, 64 * 64, 64 * 64, 64, 32 * 64]
+    kinds, heads, wds = osa.adam_mini_partition(names, numels, dim=64, n_heads=4, weight_decay=0.1)
+    assert kinds == [0, 1, 1, 2, 2, 0]
+    assert heads[1] == heads[2] == 1024 and heads[3] == 4096 and heads[4] == 64
+    assert wds == [0.1, 0.1, 0.1, 0.1, 0.0, 0.1]
+    with pytest.raises(ValueError):
+        osa.adam_mini_partition(names, numels, dim=10, n_heads=3, weight_decay=0.1)

@@ -1,0 +1,304 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration
+the benchmark times.  The HIP path runs the whole list; the oracle follows a
+seeded sample of elements (every algorithm here is elementwise or blockwise,
+so a sampled element or block is computed exactly as in the full run):
+individual elements for the elementwise paths, whole quantization blocks for
+the blockwise states, whole shared-v blocks / tensors for Adam-mini.
+Gradients are drawn on the device (torch's seeded generator) and the sampled
+values copied to the host for the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+import optimizer_step_adamw_amd as osa
+import synth
+from gpu_support import (DEV, TOL_RUN, TOL_STEP1, AdamState, DevScalars, QuantState, all_equal,
+                         relerr_tau, say, snapshot, to_np_u16)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(n, k, *key):
+    rng = synth.host_rng(*key)
+    idx = np.unique(np.concatenate([rng.integers(0, n, k), [0, n - 1]]))
+    return torch.from_numpy(idx).to(DEV), idx
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ C1
+def test_c1_single_tensor_full_oracle():
+    wl = synth.c1_single_tensor()
+    n = wl.numel
+    p0 = synth.initial_param_host(wl.tensors[0], wl.p_std, wl.index, 0)
+    st = AdamState([torch.from_numpy(p0).to(DEV)])
+    plan = osa.Plan(st.tensor_list([wl.hp.wd]), osa.OPTIM_ALGO_ADAMW)
+    sc = DevScalars(wl.hp.lr)
+    hp = osa.optim_adamw_hp(wl.hp.beta1, wl.hp.beta2, wl.hp.eps)
+    lr32 = float(np.float32(wl.hp.lr))
+    p, m, v = p0.astype(np.float64), np.zeros(n), np.zeros(n)
+    for t in range(1, wl.steps + 1):
+        g = synth.host_normal(n, wl.g_std, wl.index, 0, t, synth.GRAD)
+        st.g[0].copy_(torch.from_numpy(g).to(DEV))
+        osa.optim_step_adamw(plan.handle, hp, sc.lr, None, None, sc.step)
+        orc.adamw_step(p, m, v, g, lr32, wl.hp.beta1, wl.hp.beta2, wl.hp.eps, wl.hp.wd, t)
+        err = relerr_tau(st.p[0].cpu().numpy(), p, lr32)
+        assert err <= (TOL_STEP1 if t == 1 else TOL_RUN), (t, err)
+        if t == 1:
+            gd = g.astype(np.float64)
+            closed = p0 * (1 - lr32 * wl.hp.wd) - lr32 * gd / (np.abs(gd) + wl.hp.eps)
+            assert relerr_tau(st.p[0].cpu().numpy(), closed, lr32) <= TOL_STEP1
+    say(f"C1 ok: {wl.steps} steps, final relerr_tau {err:.3e}")
+
+
+# ------------------------------------------------------------------ C2
+@pytest.mark.parametrize("algo", ["adamw", "ademamix"])
+def test_c2_decay_stress_sampled(algo):
+    wl = synth.c2_decay_stress()
+    n, hpw = wl.numel, wl.hp
+    b3, alpha = wl.extra["beta3"], wl.extra["alpha"]
+    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, DEV)
+    ade = algo == "ademamix"
+    st = AdamState([p0], ademamix=ade)
+    plan = osa.Plan(st.tensor_list([hpw.wd]), osa.OPTIM_ALGO_ADEMAMIX if ade else osa.OPTIM_ALGO_ADAMW)
+    sc = DevScalars(hpw.lr)
+    lr32 = float(np.float32(hpw.lr))
+    di, _ = _sample(n, 1 << 18, wl.index, 0, 0, 7)
+    p = p0[di].double().cpu().numpy()
+    p_init = p.copy()
+    del p0
+    k = p.size
+    m, v, m2 = np.zeros(k), np.zeros(k), np.zeros(k)
+    p_mut, m_mut, v_mut = p.copy(), np.zeros(k), np.zeros(k)
+    for t in range(1, wl.steps + 1):
+        st.g[0].copy_(synth.device_normal(n, wl.g_std, DEV, wl.index, 0, t, synth.GRAD))
+        g = st.g[0][di].double().cpu().numpy()
+        if ade:
+            osa.optim_step_ademamix(plan.handle, osa.optim_ademamix_hp(hpw.beta1, hpw.beta2, b3, alpha, hpw.eps),
+                                    sc.lr, None, None, sc.step)
+            orc.ademamix_step(p, m, m2, v, g, lr32, hpw.beta1, hpw.beta2, b3, alpha, hpw.eps, hpw.wd, t)
+        else:
+            osa.optim_step_adamw(plan.handle, osa.optim_adamw_hp(hpw.beta1, hpw.beta2, hpw.eps), sc.lr, None,
+                                 None, sc.step)
+            orc.adamw_step(p, m, v, g, lr32, hpw.beta1, hpw.beta2, hpw.eps, hpw.wd, t)
+            if t == 1:
+                orc.mutant_adamw_decay_after_step(p_mut, m_mut, v_mut, g, lr32, hpw.beta1, hpw.beta2, hpw.eps,
+                                                  hpw.wd, t)
+        if t in (1, 10, 50, wl.steps):
+            got = st.p[0][di].cpu().numpy()
+            err = relerr_tau(got, p, lr32)
+            say(f"C2 {algo} step {t}: relerr_tau {err:.3e}")
+            assert err <= (TOL_STEP1 if t == 1 else TOL_RUN), (t, err)
+            if t == 1 and not ade:
+                # the decay-after ordering is ~lr^2*wd = 1e-3 away: far outside the bound
+                assert relerr_tau(got, p_mut, lr32) > 100 * TOL_STEP1
+            if t == 1 and ade:
+                closed = p_init * (1 - lr32 * hpw.wd) - lr32 * (1 + alpha * (1 - b3)) * g / (np.abs(g) + hpw.eps)
+                assert relerr_tau(got, closed, lr32) <= TOL_STEP1
+    del st, plan
+    _free()
+
+
+# ------------------------------------------------------------------ C3
+def test_c3_llama1b_bf16_remainder_amp_cosine():
+    """Llama-shaped 1.1B list: bf16 params + int16 remainders, bf16 grads x
+    65536 with inv_scale 2^-16 on the device, +Inf injected at iterations 49
+    and 99, cosine lr written by the step.  Skips are bit-exact no-ops; the
+    sampled fp32 masters follow the oracle; the lr values are equal."""
+    wl = synth.c3_llama_1b()
+    hpw, K = wl.hp, wl.steps
+    scale = wl.extra["loss_scale"]
+    specs = wl.tensors
+    assert len(specs) == 146 and wl.numel == 1_139_345_408
+    wd = [0.0 if s.is_norm else hpw.wd for s in specs]
+    p0 = []
+    for i, s in enumerate(specs):
+        p0.append(synth.initial_param_device(s, wl.p_std, wl.index, i, DEV))
+    st = AdamState(p0, grad_bf16=True, param_bf16=True)
+    # sample: 64 elements per tensor (+ ends) and the injection sites
+    inject = {}
+    for k in range(wl.extra["inf_every"] - 1, K, wl.extra["inf_every"]):
+        rng = synth.host_rng(wl.index, 0, k, synth.INF)
+        ti = int(rng.integers(0, len(specs)))
+        inject[k] = (ti, int(rng.integers(0, specs[ti].numel)))
+    samp = []
+    for i, s in enumerate(specs):
+        extra = [e for (ti, e) in inject.values() if ti == i]
+        rng = synth.host_rng(wl.index, i, 0, 9)
+        idx = np.unique(np.concatenate([rng.integers(0, s.numel, 64), [0, s.numel - 1], extra]))
+        samp.append((torch.from_numpy(idx).to(DEV), idx))
+    op = [p0[i][d].double().cpu().numpy() for i, (d, _) in enumerate(samp)]
+    del p0
+    _free()
+    om = [np.zeros(x.size) for x in op]
+    ov = [np.zeros(x.size) for x in op]
+    plan = osa.Plan(st.tensor_list(wd), osa.OPTIM_ALGO_ADAMW)
+    sc = DevScalars(0.0, inv_scale=1.0 / scale)
+    osa.optim_plan_set_schedule(plan.handle, osa.OPTIM_SCHED_COSINE, hpw.lr, wl.extra["lr_min"], K, sc.iter)
+    hp = osa.optim_adamw_hp(hpw.beta1, hpw.beta2, hpw.eps)
+    t_or = 0
+    for k in range(K):
+        for i, s in enumerate(specs):
+            g = synth.device_normal(s.numel, wl.g_std, DEV, wl.index, i, k, synth.GRAD)
+            st.g[i].copy_(g.mul_(scale).to(torch.bfloat16).view(torch.int16))
+        if k in inject:
+            ti, e = inject[k]
+            st.g[ti][e] = torch.tensor(float("inf")).to(torch.bfloat16).view(torch.int16)
+        gs = [orc.bf16_bits_to_f64(to_np_u16(st.g[i][d])) / scale for i, (d, _) in enumerate(samp)]
+        sc.found_inf.zero_()
+        osa.optim_check_finite(plan.handle, sc.found_inf)
+        before = snapshot(st.buffers()) if k in inject else None
+        osa.optim_step_adamw(plan.handle, hp, sc.lr, sc.inv_scale, sc.found_inf, sc.step)
+        lr_k = orc.cosine_lr(k, K, hpw.lr, wl.extra["lr_min"])
+        assert sc.lr.item() == float(lr_k), k
+        skip = any(orc.any_nonfinite(g) for g in gs)
+        assert (sc.found_inf.item() != 0.0) == skip, k
+        if skip:
+            assert all_equal(before, st.buffers()), k
+            del before
+            _free()
+            say(f"C3 iteration {k}: skipped, all buffers unchanged")
+        else:
+            t_or += 1
+            for i in range(len(specs)):
+                orc.adamw_step(op[i], om[i], ov[i], gs[i], float(lr_k), hpw.beta1, hpw.beta2, hpw.eps, wd[i],
+                               t_or)
+        assert int(sc.step.item()) == t_or
+        if k in (0, 9, 48, K - 2):
+            err = max(relerr_tau(st.master(i)[d].cpu().numpy(), op[i], hpw.lr)
+                      for i, (d, _) in enumerate(samp))
+            say(f"C3 iteration {k}: applied {t_or}, sampled master relerr_tau {err:.3e}")
+            assert err <= (TOL_STEP1 if t_or == 1 else TOL_RUN), (k, err)
+    # stored bf16 == split(stored master), on the samples
+    for i, (d, _) in enumerate(samp):
+        b, _r = orc.remainder_split(st.master(i)[d].cpu().numpy())
+        assert np.array_equal(b, to_np_u16(st.p[i][d]))
+    assert t_or == K - len(inject)
+    del st, plan
+    _free()
+
+
+# ------------------------------------------------------------------ C4
+@pytest.mark.parametrize("bits", [8, 4])
+def test_c4_blockwise_268M(bits):
+    """Fresh step: codes and absmax bit-exact on sampled blocks, p at the closed
+    form; then 10 steps with codes still bit-exact; plus the discriminating
+    fresh step at lr=0.1, wd=0.1."""
+    wl = synth.c4_blockwise()
+    n, hpw = wl.numel, wl.hp
+    block = wl.extra["block8"] if bits == 8 else wl.extra["block4"]
+    nblk = n // block
+    rng = synth.host_rng(wl.index, bits, 0, 7)
+    blocks = np.unique(np.concatenate([rng.integers(0, nblk, 2048), [0, nblk - 1]]))
+    eidx = (blocks[:, None] * block + np.arange(block)[None, :]).ravel()
+    di = torch.from_numpy(eidx).to(DEV)
+    for lr, wd, steps in ((hpw.lr, hpw.wd, wl.steps), (0.1, 0.1, 1)):
+        p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, DEV)
+        qs = QuantState([p0], bits, block)
+        plan = osa.Plan(qs.tensor_list([wd]), osa.OPTIM_ALGO_BLOCKWISE, bits=bits, block=block)
+        sc = DevScalars(lr)
+        lr32 = float(np.float32(lr))
+        p = p0[di].double().cpu().numpy()
+        p_init = p.copy()
+        del p0
+        k = eidx.size
+        qm, qv = np.zeros(k, np.uint8), np.zeros(k, np.uint8)
+        am, av = np.zeros(blocks.size, np.float32), np.zeros(blocks.size, np.float32)
+        hp = osa.optim_adamw_hp(hpw.beta1, hpw.beta2, hpw.eps)
+        for t in range(1, steps + 1):
+            qs.g[0].copy_(synth.device_normal(n, wl.g_std, DEV, wl.index, 0, t, synth.GRAD))
+            g = qs.g[0][di].cpu().numpy()
+            osa.optim_step_8bit_blockwise(plan.handle, hp, bits, block, sc.lr, None, None, sc.step)
+            orc.blockwise_step(p, g, qm, qv, am, av, bits, block, lr32, hpw.beta1, hpw.beta2, hpw.eps, wd, t)
+            bi = torch.from_numpy(blocks).to(DEV)
+            assert np.array_equal(qs.am[0][bi].cpu().numpy().view(np.uint32), am.view(np.uint32)), t
+            assert np.array_equal(qs.av[0][bi].cpu().numpy().view(np.uint32), av.view(np.uint32)), t
+            if bits == 8:
+                gm, gv = qs.qm[0][di].cpu().numpy(), qs.qv[0][di].cpu().numpy()
+            else:
+                bytes_idx = torch.from_numpy(np.unique(eidx // 2)).to(DEV)
+                gm = orc.unpack_nibbles(qs.qm[0][bytes_idx].cpu().numpy(), k)
+                gv = orc.unpack_nibbles(qs.qv[0][bytes_idx].cpu().numpy(), k)
+            assert np.array_equal(gm, qm), (t, int(np.sum(gm != qm)))
+            assert np.array_equal(gv, qv), (t, int(np.sum(gv != qv)))
+            got = qs.p[0][di].cpu().numpy()
+            err = relerr_tau(got, p, lr32)
+            assert err <= (TOL_STEP1 if t == 1 else TOL_RUN), (t, err)
+            if t == 1:
+                gd = g.astype(np.float64)
+                closed = p_init * (1 - lr32 * wd) - lr32 * gd / (np.abs(gd) + hpw.eps)
+                assert relerr_tau(got, closed, lr32) <= TOL_STEP1
+                if lr == 0.1:
+                    mutant = (p_init - lr32 * gd / (np.abs(gd) + hpw.eps)) * (1 - lr32 * wd)
+                    assert np.max(np.abs(got - mutant)) > 0.9e-3
+        say(f"C4 {bits}-bit block {block} lr={lr}: {steps} steps, codes bit-exact, relerr_tau {err:.3e}")
+        del qs, plan
+        _free()
+
+
+# ------------------------------------------------------------------ C5
+def test_c5_adam_mini_llama7b_sampled():
+    """Adam-mini over the 7B list (6.7e9 fp32 params).  The oracle follows
+    whole blocks: two q/k tensors' first and last head blocks, a whole
+    value projection and two norms (one shared v each), and samples of the
+    embedding and output (full v)."""
+    wl = synth.c5_adam_mini_7b()
+    hpw = wl.hp
+    specs = wl.tensors
+    assert len(specs) == 291 and wl.numel == 6_738_415_616
+    names = [s.name for s in specs]
+    sizes = [s.numel for s in specs]
+    dim, heads = wl.extra["dim"], wl.extra["n_heads"]
+    kinds, hn, wds = osa.adam_mini_partition(names, sizes, dim=dim, n_heads=heads, weight_decay=hpw.wd)
+    vlen = [s if k == osa.OPTIM_MINI_FULL_V else s // h for k, s, h in zip(kinds, sizes, hn)]
+    p0 = [synth.initial_param_device(s, wl.p_std, wl.index, i, DEV) for i, s in enumerate(specs)]
+    st = AdamState(p0, v_len=vlen)
+    del p0
+    plan = osa.Plan(st.tensor_list(wds, mini_kind=kinds, head_numel=hn), osa.OPTIM_ALGO_ADAM_MINI)
+    sc = DevScalars(hpw.lr)
+    lr32 = float(np.float32(hpw.lr))
+    H = dim * dim // heads
+    # tracked pieces: (tensor, element index array on host, oracle block length)
+    track = []
+    name_to_i = {n: i for i, n in enumerate(names)}
+    for nm in ("layers.0.attention.wq.weight", "layers.31.attention.wk.weight"):
+        i = name_to_i[nm]
+        for blk in (0, sizes[i] // H - 1):
+            track.append((i, np.arange(blk * H, (blk + 1) * H), H))
+    for nm in ("layers.3.attention.wv.weight", "layers.5.attention_norm.weight", "norm.weight"):
+        i = name_to_i[nm]
+        track.append((i, np.arange(sizes[i]), sizes[i]))
+    for nm in ("tok_embeddings.weight", "output.weight"):
+        i = name_to_i[nm]
+        idx = np.unique(synth.host_rng(wl.index, i, 0, 9).integers(0, sizes[i], 4096))
+        track.append((i, idx, 1))  # full v: elementwise AdamW
+    for i, idx, b in track:  # the oracle partitions by name on its own
+        kind = orc.adam_mini_kind(names[i])
+        assert (kind == orc.MINI_FULL_V) == (b == 1)
+    dev_idx = [torch.from_numpy(idx).to(DEV) for _, idx, _ in track]
+    op = [st.p[i][d].double().cpu().numpy() for (i, _, _), d in zip(track, dev_idx)]
+    om = [np.zeros(x.size) for x in op]
+    ov = [np.zeros(x.size if b == 1 else x.size // b) for x, (_, _, b) in zip(op, track)]
+    owd = [orc.adam_mini_weight_decay(names[i], hpw.wd) for i, _, _ in track]
+    hp = osa.optim_adamw_hp(hpw.beta1, hpw.beta2, hpw.eps)
+    for t in range(1, wl.steps + 1):
+        for i, s in enumerate(specs):
+            st.g[i].copy_(synth.device_normal(s.numel, wl.g_std, DEV, wl.index, i, t, synth.GRAD))
+        osa.optim_step_adam_mini(plan.handle, hp, sc.lr, None, None, sc.step)
+        for j, ((i, idx, b), d) in enumerate(zip(track, dev_idx)):
+            g = st.g[i][d].double().cpu().numpy()
+            if b == 1:
+                orc.adamw_step(op[j], om[j], ov[j], g, lr32, hpw.beta1, hpw.beta2, hpw.eps, owd[j], t)
+            else:
+                orc.adam_mini_step(op[j], om[j], ov[j], g, b, lr32, hpw.beta1, hpw.beta2, hpw.eps, owd[j], t)
+        if t in (1, wl.steps):
+            err = max(relerr_tau(st.p[i][d].cpu().numpy(), op[j], lr32)
+                      for j, ((i, _, _), d) in enumerate(zip(track, dev_idx)))
+            say(f"C5 step {t}: tracked relerr_tau {err:.3e}")
+            assert err <= (TOL_STEP1 if t == 1 else TOL_RUN), (t, err)
+    del st, plan
+    _free()
