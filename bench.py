@@ -1,0 +1,384 @@
+"""Benchmark of the fused AdamW-family optimizer step on one MI355X.
+
+Headline workload: one fp32 tensor of 4096 x 4096 elements stepped by AdamW
+(lr 0.1, wd 0.1) and by AdEMAMix (beta3 0.9999, alpha 5) on the same
+gradients, each optimizer with its own state.  One benchmark step = one
+AdamW step + one AdEMAMix step through the C ABI (every kernel of the path:
+per-step scalars, moments, bias correction, decay, update).  `value` is
+optimizer element-updates per second with all inputs resident in HBM.
+
+Secondary workloads (same JSON line, "secondary"): the 1M-element tensor,
+the Llama-shaped 1.1B bf16+remainder AMP list with device cosine lr, the
+268M-element blockwise 8-bit and 4-bit states, and Adam-mini over the 7B
+list.  Gradients are drawn once per workload, outside the timed region.
+
+Timing: HIP events on the stream the library launches on (torch's current
+stream), one pair around every optimizer call inside the timed region; the
+region itself is bracketed by device synchronisation.  Achieved bandwidth
+counts algorithmic bytes (what the method must read and write once).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "optimizer-step elements/s and achieved HBM GB/s (% of peak), fp32 and 8-bit"
+
+# algorithmic bytes per element (read + write once)
+B_ADAMW_F32 = 28.0            # R p g m v (16) + W p m v (12)
+B_ADEMAMIX_F32 = 36.0         # + m2 read and write
+B_BF16R_AMP = 26.0 + 2.0      # R bf16 p, int16 r, bf16 g, m, v (14) + W (12); + finite check g
+B_8BIT = 4 + 4 + 1 + 1 + 8 / 256 + 4 + 1 + 1 + 8 / 256
+B_4BIT = 4 + 4 + 0.5 + 0.5 + 8 / 128 + 4 + 0.5 + 0.5 + 8 / 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--secondary", default="c1,c3,c4,c5",
+                    help="comma list of secondary workloads (c1,c3,c4,c5) or 'none'")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    return ap.parse_args()
+
+
+class Timer:
+    """Events around each call on the current stream; total from first to last."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.marks.append(e)
+
+    def durations_ms(self):
+        self.torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in zip(self.marks[:-1], self.marks[1:])]
+
+
+def run_timed(torch, calls, steps, warmup):
+    """calls: list of zero-arg functions forming one step.  Returns total ms
+    per step and the mean ms of each call."""
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    tm = Timer(torch)
+    t0 = time.perf_counter()
+    tm.mark()
+    for _ in range(steps):
+        for c in calls:
+            c()
+            tm.mark()
+    d = tm.durations_ms()
+    wall = (time.perf_counter() - t0) * 1e3
+    per_call = [sum(d[i::len(calls)]) / steps for i in range(len(calls))]
+    return sum(d) / steps, per_call, wall / steps
+
+
+def gbs(bytes_per_step, ms):
+    return bytes_per_step / (ms * 1e-3) / 1e9
+
+
+# --------------------------------------------------------------------------
+def adam_buffers(torch, p0_list, grad_dtype, param_bf16=False, ademamix=False, v_len=None):
+    dev = "cuda"
+    import optimizer_step_adamw_amd as osa
+    bufs = {}
+    if param_bf16:
+        bufs["p"] = [torch.empty(x.numel(), dtype=torch.int16, device=dev) for x in p0_list]
+        bufs["r"] = [torch.empty(x.numel(), dtype=torch.int16, device=dev) for x in p0_list]
+        for x, b, r in zip(p0_list, bufs["p"], bufs["r"]):
+            osa.optim_remainder_split(x, b, r, x.numel())
+    else:
+        bufs["p"] = [x.clone() for x in p0_list]
+        bufs["r"] = None
+    bufs["m"] = [torch.zeros(x.numel(), dtype=torch.float32, device=dev) for x in p0_list]
+    vl = v_len or [x.numel() for x in p0_list]
+    bufs["v"] = [torch.zeros(k, dtype=torch.float32, device=dev) for k in vl]
+    bufs["m2"] = ([torch.zeros(x.numel(), dtype=torch.float32, device=dev) for x in p0_list]
+                  if ademamix else None)
+    return bufs
+
+
+def scalars(torch, lr, inv_scale=None):
+    dev = "cuda"
+    return dict(lr=torch.tensor([lr], dtype=torch.float32, device=dev),
+                step=torch.zeros(1, dtype=torch.int32, device=dev),
+                found_inf=torch.zeros(1, dtype=torch.float32, device=dev),
+                iter=torch.zeros(1, dtype=torch.int32, device=dev),
+                inv_scale=None if inv_scale is None else
+                torch.tensor([inv_scale], dtype=torch.float32, device=dev))
+
+
+def bench_headline(torch, osa, synth, steps, warmup):
+    wl = synth.c2_decay_stress()
+    n, hp = wl.numel, wl.hp
+    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
+    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
+    A = adam_buffers(torch, [p0], osa.OPTIM_F32)
+    B = adam_buffers(torch, [p0], osa.OPTIM_F32, ademamix=True)
+    del p0
+    tla = osa.TensorList(A["p"], [g], m=A["m"], v=A["v"], weight_decay=[hp.wd])
+    tlb = osa.TensorList(B["p"], [g], m=B["m"], v=B["v"], m2=B["m2"], weight_decay=[hp.wd])
+    pa = osa.Plan(tla, osa.OPTIM_ALGO_ADAMW)
+    pb = osa.Plan(tlb, osa.OPTIM_ALGO_ADEMAMIX)
+    sa, sb = scalars(torch, hp.lr), scalars(torch, hp.lr)
+    hpa = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
+    hpb = osa.optim_ademamix_hp(hp.beta1, hp.beta2, wl.extra["beta3"], wl.extra["alpha"], hp.eps)
+
+    def call_a():
+        osa.optim_step_adamw(pa.handle, hpa, sa["lr"], None, None, sa["step"])
+
+    def call_b():
+        osa.optim_step_ademamix(pb.handle, hpb, sb["lr"], None, None, sb["step"])
+
+    ms, per_call, wall = run_timed(torch, [call_a, call_b], steps, warmup)
+    res = dict(workload=wl.name, elements=n, ms_per_step=ms, wall_ms_per_step=wall,
+               elements_per_s=2 * n / (ms * 1e-3),
+               kernels={
+                   "adamw_fp32": dict(ms=per_call[0], bytes=B_ADAMW_F32 * n,
+                                      gbs=gbs(B_ADAMW_F32 * n, per_call[0])),
+                   "ademamix_fp32": dict(ms=per_call[1], bytes=B_ADEMAMIX_F32 * n,
+                                         gbs=gbs(B_ADEMAMIX_F32 * n, per_call[1])),
+               })
+    for k in res["kernels"].values():
+        k["frac"] = k["gbs"] / PEAK_HBM_GBS
+    pa.close()
+    pb.close()
+    return res
+
+
+def bench_c1(torch, osa, synth, steps, warmup):
+    wl = synth.c1_single_tensor()
+    n, hp = wl.numel, wl.hp
+    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
+    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
+    A = adam_buffers(torch, [p0], osa.OPTIM_F32)
+    plan = osa.Plan(osa.TensorList(A["p"], [g], m=A["m"], v=A["v"], weight_decay=[hp.wd]),
+                    osa.OPTIM_ALGO_ADAMW)
+    s = scalars(torch, hp.lr)
+    h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
+    ms, _, _ = run_timed(torch, [lambda: osa.optim_step_adamw(plan.handle, h, s["lr"], None, None,
+                                                               s["step"])], steps, warmup)
+    plan.close()
+    return dict(workload=wl.name, elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
+                gbs=gbs(B_ADAMW_F32 * n, ms), frac=gbs(B_ADAMW_F32 * n, ms) / PEAK_HBM_GBS,
+                note="29 MB of state: cache-resident and launch-bound")
+
+
+def bench_c3(torch, osa, synth, steps, warmup):
+    wl = synth.c3_llama_1b()
+    hp, scale = wl.hp, wl.extra["loss_scale"]
+    specs = wl.tensors
+    n = wl.numel
+    p0 = [synth.initial_param_device(s, wl.p_std, wl.index, i, "cuda") for i, s in enumerate(specs)]
+    A = adam_buffers(torch, p0, osa.OPTIM_BF16, param_bf16=True)
+    del p0
+    torch.cuda.empty_cache()
+    G = []
+    for i, s in enumerate(specs):
+        x = synth.device_normal(s.numel, wl.g_std, "cuda", wl.index, i, 0, synth.GRAD)
+        G.append(x.mul_(scale).to(torch.bfloat16).view(torch.int16))
+        del x
+    wd = [0.0 if s.is_norm else hp.wd for s in specs]
+    tl = osa.TensorList(A["p"], G, m=A["m"], v=A["v"], remainders=A["r"], weight_decay=wd,
+                        param_dtype=osa.OPTIM_BF16, grad_dtype=osa.OPTIM_BF16)
+    plan = osa.Plan(tl, osa.OPTIM_ALGO_ADAMW)
+    s = scalars(torch, 0.0, inv_scale=1.0 / scale)
+    osa.optim_plan_set_schedule(plan.handle, osa.OPTIM_SCHED_COSINE, hp.lr, 0.0, wl.steps, s["iter"])
+    h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
+
+    def finite():
+        s["found_inf"].zero_()
+        osa.optim_check_finite(plan.handle, s["found_inf"])
+
+    def step():
+        osa.optim_step_adamw(plan.handle, h, s["lr"], s["inv_scale"], s["found_inf"], s["step"])
+
+    ms, per_call, _ = run_timed(torch, [finite, step], steps, warmup)
+    plan.close()
+    del A, G
+    torch.cuda.empty_cache()
+    b = B_BF16R_AMP * n
+    return dict(workload=wl.name, elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
+                gbs=gbs(b, ms), frac=gbs(b, ms) / PEAK_HBM_GBS,
+                kernels={"check_finite_bf16": dict(ms=per_call[0], gbs=gbs(2.0 * n, per_call[0])),
+                         "adamw_bf16_remainder": dict(ms=per_call[1], gbs=gbs(26.0 * n, per_call[1]))})
+
+
+def bench_c4(torch, osa, synth, steps, warmup):
+    wl = synth.c4_blockwise()
+    n, hp = wl.numel, wl.hp
+    out = {}
+    for bits, block, bpe in ((8, wl.extra["block8"], B_8BIT), (4, wl.extra["block4"], B_4BIT)):
+        p = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
+        g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
+        nb = (n * bits + 7) // 8
+        qm = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+        qv = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+        am = torch.zeros(n // block, dtype=torch.float32, device="cuda")
+        av = torch.zeros(n // block, dtype=torch.float32, device="cuda")
+        tl = osa.TensorList([p], [g], qm=[qm], qv=[qv], absmax_m=[am], absmax_v=[av], weight_decay=[hp.wd])
+        plan = osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE, bits=bits, block=block)
+        s = scalars(torch, hp.lr)
+        h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
+        ms, _, _ = run_timed(torch, [lambda: osa.optim_step_8bit_blockwise(
+            plan.handle, h, bits, block, s["lr"], None, None, s["step"])], steps, warmup)
+        plan.close()
+        out[f"blockwise_{bits}bit_block{block}"] = dict(
+            elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3), bytes_per_element=bpe,
+            gbs=gbs(bpe * n, ms), frac=gbs(bpe * n, ms) / PEAK_HBM_GBS)
+        del p, g, qm, qv, am, av
+        torch.cuda.empty_cache()
+    return dict(workload=wl.name, **out)
+
+
+def bench_c5(torch, osa, synth, steps, warmup):
+    wl = synth.c5_adam_mini_7b()
+    hp = wl.hp
+    specs = wl.tensors
+    names = [s.name for s in specs]
+    sizes = [s.numel for s in specs]
+    kinds, hn, wds = osa.adam_mini_partition(names, sizes, dim=wl.extra["dim"], n_heads=wl.extra["n_heads"],
+                                             weight_decay=hp.wd)
+    vlen = [s if k == osa.OPTIM_MINI_FULL_V else s // h for k, s, h in zip(kinds, sizes, hn)]
+    P = [synth.initial_param_device(s, wl.p_std, wl.index, i, "cuda") for i, s in enumerate(specs)]
+    G = [synth.device_normal(s.numel, wl.g_std, "cuda", wl.index, i, 1, synth.GRAD) for i, s in enumerate(specs)]
+    M = [torch.zeros(k, dtype=torch.float32, device="cuda") for k in sizes]
+    V = [torch.zeros(k, dtype=torch.float32, device="cuda") for k in vlen]
+    tl = osa.TensorList(P, G, m=M, v=V, weight_decay=wds, mini_kind=kinds, head_numel=hn)
+    plan = osa.Plan(tl, osa.OPTIM_ALGO_ADAM_MINI)
+    s = scalars(torch, hp.lr)
+    h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
+    ms, _, _ = run_timed(torch, [lambda: osa.optim_step_adam_mini(plan.handle, h, s["lr"], None, None,
+                                                                   s["step"])], max(3, steps // 2), 2)
+    plan.close()
+    n = wl.numel
+    full = sum(sz for sz, k in zip(sizes, kinds) if k == osa.OPTIM_MINI_FULL_V)
+    alg = 28.0 * full + 20.0 * (n - full)
+    del P, G, M, V
+    torch.cuda.empty_cache()
+    return dict(workload=wl.name, elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
+                gbs=gbs(alg, ms), frac=gbs(alg, ms) / PEAK_HBM_GBS,
+                note="algorithmic bytes 28 B/elem for full-v tensors, 20 B/elem for shared-v tensors; "
+                     "the kernels read g twice (block sums, then update)")
+
+
+# --------------------------------------------------------------------------
+def cpu_baseline(synth, target_s):
+    """The CPU oracle (single-threaded scalar C, fp64) on a row slice of the
+    headline tensor: AdamW + AdEMAMix, same hyperparameters."""
+    import numpy as np
+    import oracle
+    wl = synth.c2_decay_stress()
+    hp = wl.hp
+    rows = 256
+    n = rows * 4096
+    p0 = synth.host_normal(n, wl.p_std, wl.index, 0, 0, synth.P0).astype(np.float64)
+    g = synth.host_normal(n, wl.g_std, wl.index, 0, 1, synth.GRAD).astype(np.float64)
+    pa, ma, va = p0.copy(), np.zeros(n), np.zeros(n)
+    pb, m1, m2, nu = p0.copy(), np.zeros(n), np.zeros(n), np.zeros(n)
+    steps, spent = 0, 0.0
+    while spent < target_s and steps < 1000:
+        t0 = time.perf_counter()
+        oracle.adamw_step(pa, ma, va, g, hp.lr, hp.beta1, hp.beta2, hp.eps, hp.wd, steps + 1)
+        oracle.ademamix_step(pb, m1, m2, nu, g, hp.lr, hp.beta1, hp.beta2, wl.extra["beta3"],
+                             wl.extra["alpha"], hp.eps, hp.wd, steps + 1)
+        spent += time.perf_counter() - t0
+        steps += 1
+    return dict(value=2 * n * steps / spent, unit="elements/s", cores=1, kind="oracle",
+                sample=f"{rows}x4096 rows of the 4096x4096 tensor, AdamW + AdEMAMix, {steps} steps, "
+                       f"{spent:.1f} s, single thread ({os.cpu_count()} host cores visible)")
+
+
+def traffic_from_profile(kernel_key):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    valid only while the kernel source is the one the counters were taken on."""
+    src = os.path.join(ROOT, "optimizer_step_adamw_amd", "csrc", "kernels.hip")
+    path = os.path.join(ROOT, "profiles", f"counters_{kernel_key}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    m = re.search(r"kernels_hip_sha256:\s*([0-9a-f]{64})", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != sha:
+        return None
+    return float(t.group(1))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the optimizer step needs no cross-GPU exchange; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import optimizer_step_adamw_amd as osa
+    import synth
+    osa.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    log(f"device: {torch.cuda.get_device_name(0)}")
+    head = bench_headline(torch, osa, synth, args.steps, args.warmup)
+    log(f"headline: {head['ms_per_step']:.4f} ms/step, {head['elements_per_s']:.4e} elem/s, "
+        f"{json.dumps(head['kernels'])}")
+    secondary = {}
+    todo = [] if args.secondary == "none" else args.secondary.split(",")
+    fns = dict(c1=bench_c1, c3=bench_c3, c4=bench_c4, c5=bench_c5)
+    for key in todo:
+        t0 = time.perf_counter()
+        secondary[key] = fns[key](torch, osa, synth, args.steps, args.warmup)
+        log(f"{key}: {json.dumps(secondary[key])} ({time.perf_counter() - t0:.1f} s)")
+    dom_name = max(head["kernels"], key=lambda k: head["kernels"][k]["ms"])
+    dom = head["kernels"][dom_name]
+    roof = dict(bound="hbm", kernel=dom_name, achieved=dom["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=dom["gbs"] / PEAK_HBM_GBS, traffic=traffic_from_profile(dom_name),
+                bytes_per_launch=dom["bytes"], launch_ms=dom["ms"])
+    cpu = cpu_baseline(synth, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    out = {
+        "metric": METRIC,
+        "value": head["elements_per_s"],
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "elements": head["elements"],
+                   "optimizers": ["adamw", "ademamix"], "lr": 0.1, "weight_decay": 0.1,
+                   "betas": [0.9, 0.999], "beta3": 0.9999, "alpha": 5.0},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": head["kernels"],
+        "secondary": secondary,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

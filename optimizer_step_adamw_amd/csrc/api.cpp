@@ -252,7 +252,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
 
     Layout &L = B.L;
     size_t off = 0;
-    L.scalars = off; off += align256(sizeof(Scalars));
+    L.counters = off; off += align256(kCounterBytes);
     L.group_wd = off; off += align256(kMaxGroups * sizeof(double));
     L.tensors = off; off += align256(std::max<size_t>(1, B.tensors.size()) * sizeof(TensorDesc));
     L.spans = off; off += align256(B.spans.size() * sizeof(SpanDesc));
@@ -388,11 +388,12 @@ namespace {
 
 StepArgs step_args(optim_plan *P) {
     StepArgs a{};
+    a.done = reinterpret_cast<uint32_t *>(P->ws + P->L.counters);
+    a.commit = 1;
     a.tensors = reinterpret_cast<const TensorDesc *>(P->ws + P->L.tensors);
     a.spans = reinterpret_cast<const SpanDesc *>(P->ws + P->L.spans);
     a.nspans = P->nspans;
     a.nunits = P->nunits;
-    a.sc = reinterpret_cast<const Scalars *>(P->ws + P->L.scalars);
     a.partials = reinterpret_cast<double *>(P->ws + P->L.partials);
     a.blockfac = reinterpret_cast<float *>(P->ws + P->L.blockfac);
     a.blockspan = reinterpret_cast<const int32_t *>(P->ws + P->L.blockspan);
@@ -405,31 +406,32 @@ StepArgs step_args(optim_plan *P) {
     return a;
 }
 
-int prep(optim_plan *P, double b1, double b2, double b3, double alpha, double eps, float *lr_dev,
-         const float *inv_scale, const float *found_inf, int32_t *step_dev, hipStream_t s) {
+// Validates the per-step device scalars and fills the inputs every step
+// kernel derives its scalars from.
+int step_inputs(optim_plan *P, double b1, double b2, double b3, double alpha, double eps, float *lr_dev,
+                const float *inv_scale, const float *found_inf, int32_t *step_dev, StepArgs &a) {
     if (!lr_dev || !aligned(lr_dev, 4)) return fail(OPTIM_EINVAL, "lr_dev must be an aligned device float");
     if (!step_dev || !aligned(step_dev, 4)) return fail(OPTIM_EINVAL, "step_dev must be an aligned device int32");
     if (!aligned(inv_scale, 4) || !aligned(found_inf, 4)) return fail(OPTIM_EALIGN, "scalar pointer misaligned");
     if (!(eps >= 0.0) || !std::isfinite(eps)) return fail(OPTIM_EINVAL, "invalid eps (need finite eps >= 0)");
-    PrepArgs a{};
-    a.sc = reinterpret_cast<Scalars *>(P->ws + P->L.scalars);
-    a.group_wd = reinterpret_cast<const double *>(P->ws + P->L.group_wd);
-    a.ngroups = P->ngroups;
-    a.sched = P->sched;
-    a.lr_dev = lr_dev;
-    a.inv_scale = inv_scale;
-    a.found_inf = found_inf;
-    a.step_dev = step_dev;
-    a.iter_dev = P->iter_dev;
-    a.lr_max = P->lr_max;
-    a.lr_min = P->lr_min;
-    a.K = P->K;
-    a.beta1 = b1;
-    a.beta2 = b2;
-    a.beta3 = b3;
-    a.alpha = alpha;
-    a.eps = eps;
-    HIP_OK(launch_prep(a, s));
+    a = step_args(P);
+    PrepArgs &p = a.prep;
+    p.group_wd = reinterpret_cast<const double *>(P->ws + P->L.group_wd);
+    p.ngroups = P->ngroups;
+    p.sched = P->sched;
+    p.lr_dev = lr_dev;
+    p.inv_scale = inv_scale;
+    p.found_inf = found_inf;
+    p.step_dev = step_dev;
+    p.iter_dev = P->iter_dev;
+    p.lr_max = P->lr_max;
+    p.lr_min = P->lr_min;
+    p.K = P->K;
+    p.beta1 = b1;
+    p.beta2 = b2;
+    p.beta3 = b3;
+    p.alpha = alpha;
+    p.eps = eps;
     return OPTIM_OK;
 }
 
@@ -455,10 +457,11 @@ int optim_step_adamw(optim_plan *plan, const optim_adamw_hp *hp, float *lr_dev, 
     int rc = check_plan(plan, OPTIM_ALGO_ADAMW, "optim_step_adamw");
     if (!rc) rc = check_adamw_hp(hp);
     if (rc) return rc;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    rc = prep(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev, step_dev, s);
+    StepArgs a;
+    rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
+                     step_dev, a);
     if (rc) return rc;
-    if (plan->nunits > 0) HIP_OK(launch_adamw(step_args(plan), plan->pk, plan->gk, s));
+    HIP_OK(launch_adamw(a, plan->pk, plan->gk, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
 
@@ -472,11 +475,11 @@ int optim_step_ademamix(optim_plan *plan, const optim_ademamix_hp *hp, float *lr
         (rc = check_hp_beta(hp->beta3, "beta3")))
         return rc;
     if (!std::isfinite(hp->alpha) || hp->alpha < 0.0) return fail(OPTIM_EINVAL, "invalid alpha (need finite alpha >= 0)");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    rc = prep(plan, hp->beta1, hp->beta2, hp->beta3, hp->alpha, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
-              step_dev, s);
+    StepArgs a;
+    rc = step_inputs(plan, hp->beta1, hp->beta2, hp->beta3, hp->alpha, hp->eps, lr_dev, inv_scale_dev,
+                     found_inf_dev, step_dev, a);
     if (rc) return rc;
-    if (plan->nunits > 0) HIP_OK(launch_ademamix(step_args(plan), plan->pk, plan->gk, s));
+    HIP_OK(launch_ademamix(a, plan->pk, plan->gk, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
 
@@ -485,10 +488,11 @@ int optim_step_adam_mini(optim_plan *plan, const optim_adamw_hp *hp, float *lr_d
     int rc = check_plan(plan, OPTIM_ALGO_ADAM_MINI, "optim_step_adam_mini");
     if (!rc) rc = check_adamw_hp(hp);
     if (rc) return rc;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    rc = prep(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev, step_dev, s);
+    StepArgs a;
+    rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
+                     step_dev, a);
     if (rc) return rc;
-    if (plan->nunits > 0) HIP_OK(launch_adam_mini(step_args(plan), plan->pk, plan->gk, s));
+    HIP_OK(launch_adam_mini(a, plan->pk, plan->gk, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
 
@@ -500,10 +504,11 @@ int optim_step_8bit_blockwise(optim_plan *plan, const optim_adamw_hp *hp, int32_
     if (rc) return rc;
     if (bits != plan->bits || block != plan->block)
         return fail(OPTIM_EINVAL, "bits/block differ from the plan's");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    rc = prep(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev, step_dev, s);
+    StepArgs a;
+    rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
+                     step_dev, a);
     if (rc) return rc;
-    if (plan->nunits > 0) HIP_OK(launch_blockwise(step_args(plan), plan->gk, s));
+    HIP_OK(launch_blockwise(a, plan->gk, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
 
@@ -513,6 +518,7 @@ int optim_check_finite(optim_plan *plan, float *found_inf_dev, void *stream) {
         return fail(OPTIM_EINVAL, "found_inf_dev must be an aligned device float");
     if (plan->nunits == 0) return OPTIM_OK;
     StepArgs a = step_args(plan);
+    a.commit = 0;
     a.found_inf = found_inf_dev;
     HIP_OK(launch_check_finite(a, plan->gk, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;

@@ -50,69 +50,99 @@ __device__ __forceinline__ void rem_split(float x, uint32_t &b, uint32_t &r) {
 }
 
 // ---------------------------------------------------------------- loads
+// Every tensor lives in HBM: accesses go through global-address-space
+// pointers so they compile to global_load/store (not flat) instructions.
 // N = 8: two 128-bit accesses (fp32) or one (16-bit); N = 1: one element.
+#define GMEM __attribute__((address_space(1)))
+typedef float __attribute__((ext_vector_type(4))) f32x4;
+typedef uint32_t __attribute__((ext_vector_type(4))) u32x4;
+typedef uint32_t __attribute__((ext_vector_type(2))) u32x2;
+
+template <class T>
+__device__ __forceinline__ GMEM T *gp(T *p) { return (GMEM T *)p; }
+template <class T>
+__device__ __forceinline__ const GMEM T *gp(const T *p) { return (const GMEM T *)p; }
+
+#ifndef OPTIM_NT
+#define OPTIM_NT 0  // 1: nontemporal 128-bit loads and stores
+#endif
+template <class V>
+__device__ __forceinline__ V vload(const GMEM V *q) {
+#if OPTIM_NT
+    return __builtin_nontemporal_load(q);
+#else
+    return *q;
+#endif
+}
+template <class V>
+__device__ __forceinline__ void vstore(GMEM V *q, V x) {
+#if OPTIM_NT
+    __builtin_nontemporal_store(x, q);
+#else
+    *q = x;
+#endif
+}
+
 template <int N>
 __device__ __forceinline__ void ldf(const float *a, int64_t e, float (&x)[N]) {
     if constexpr (N == 8) {
-        const float4 *q = reinterpret_cast<const float4 *>(a + e);
-        const float4 u = q[0], w = q[1];
+        const GMEM f32x4 *q = (const GMEM f32x4 *)gp(a + e);
+        const f32x4 u = vload(q), w = vload(q + 1);
         x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
         x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
     } else if constexpr (N == 4) {
-        const float4 u = *reinterpret_cast<const float4 *>(a + e);
+        const f32x4 u = *(const GMEM f32x4 *)gp(a + e);
         x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
     } else {
+        const GMEM float *q = gp(a);
 #pragma unroll
-        for (int k = 0; k < N; ++k) x[k] = a[e + k];
+        for (int k = 0; k < N; ++k) x[k] = q[e + k];
     }
 }
 
 template <int N>
 __device__ __forceinline__ void stf(float *a, int64_t e, const float (&x)[N]) {
     if constexpr (N == 8) {
-        float4 *q = reinterpret_cast<float4 *>(a + e);
-        q[0] = make_float4(x[0], x[1], x[2], x[3]);
-        q[1] = make_float4(x[4], x[5], x[6], x[7]);
+        GMEM f32x4 *q = (GMEM f32x4 *)gp(a + e);
+        vstore(q, f32x4{x[0], x[1], x[2], x[3]});
+        vstore(q + 1, f32x4{x[4], x[5], x[6], x[7]});
     } else if constexpr (N == 4) {
-        *reinterpret_cast<float4 *>(a + e) = make_float4(x[0], x[1], x[2], x[3]);
+        *(GMEM f32x4 *)gp(a + e) = f32x4{x[0], x[1], x[2], x[3]};
     } else {
+        GMEM float *q = gp(a);
 #pragma unroll
-        for (int k = 0; k < N; ++k) a[e + k] = x[k];
+        for (int k = 0; k < N; ++k) q[e + k] = x[k];
     }
 }
 
 template <int N>
 __device__ __forceinline__ void ldh(const uint16_t *a, int64_t e, uint32_t (&x)[N]) {
     if constexpr (N == 8) {
-        const uint4 u = *reinterpret_cast<const uint4 *>(a + e);
+        const u32x4 u = vload((const GMEM u32x4 *)gp(a + e));
         x[0] = u.x & 0xFFFFu; x[1] = u.x >> 16; x[2] = u.y & 0xFFFFu; x[3] = u.y >> 16;
         x[4] = u.z & 0xFFFFu; x[5] = u.z >> 16; x[6] = u.w & 0xFFFFu; x[7] = u.w >> 16;
     } else if constexpr (N == 4) {
-        const uint2 u = *reinterpret_cast<const uint2 *>(a + e);
+        const u32x2 u = *(const GMEM u32x2 *)gp(a + e);
         x[0] = u.x & 0xFFFFu; x[1] = u.x >> 16; x[2] = u.y & 0xFFFFu; x[3] = u.y >> 16;
     } else {
+        const GMEM uint16_t *q = gp(a);
 #pragma unroll
-        for (int k = 0; k < N; ++k) x[k] = a[e + k];
+        for (int k = 0; k < N; ++k) x[k] = q[e + k];
     }
 }
 
 template <int N>
 __device__ __forceinline__ void sth(uint16_t *a, int64_t e, const uint32_t (&x)[N]) {
     if constexpr (N == 8) {
-        uint4 u;
-        u.x = (x[0] & 0xFFFFu) | (x[1] << 16);
-        u.y = (x[2] & 0xFFFFu) | (x[3] << 16);
-        u.z = (x[4] & 0xFFFFu) | (x[5] << 16);
-        u.w = (x[6] & 0xFFFFu) | (x[7] << 16);
-        *reinterpret_cast<uint4 *>(a + e) = u;
+        vstore((GMEM u32x4 *)gp(a + e),
+               u32x4{(x[0] & 0xFFFFu) | (x[1] << 16), (x[2] & 0xFFFFu) | (x[3] << 16),
+                     (x[4] & 0xFFFFu) | (x[5] << 16), (x[6] & 0xFFFFu) | (x[7] << 16)});
     } else if constexpr (N == 4) {
-        uint2 u;
-        u.x = (x[0] & 0xFFFFu) | (x[1] << 16);
-        u.y = (x[2] & 0xFFFFu) | (x[3] << 16);
-        *reinterpret_cast<uint2 *>(a + e) = u;
+        *(GMEM u32x2 *)gp(a + e) = u32x2{(x[0] & 0xFFFFu) | (x[1] << 16), (x[2] & 0xFFFFu) | (x[3] << 16)};
     } else {
+        GMEM uint16_t *q = gp(a);
 #pragma unroll
-        for (int k = 0; k < N; ++k) a[e + k] = (uint16_t)x[k];
+        for (int k = 0; k < N; ++k) q[e + k] = (uint16_t)x[k];
     }
 }
 
@@ -160,25 +190,153 @@ __device__ __forceinline__ void load_g(const void *g, int64_t e, float s, float 
 // ---------------------------------------------------------------- traversal
 // Calls body(u, span, first element, element count) for every unit u this
 // workgroup owns.  All arguments are uniform across the workgroup.
-template <class Body>
-__device__ __forceinline__ void for_units(const StepArgs &a, Body &&body) {
-    const int64_t G = gridDim.x, b = blockIdx.x;
-    int64_t u = a.nunits * b / G;
-    const int64_t u1 = a.nunits * (b + 1) / G;
-    if (u >= u1) return;
+// OPTIM_TRAVERSAL 1 (default): grid-stride -- workgroup b takes units b,
+// b+G, b+2G, ..., so the resident workgroups sweep one contiguous window of
+// each array at a time (DRAM pages stay local).  0: one contiguous range of
+// units per workgroup.
+#ifndef OPTIM_TRAVERSAL
+#define OPTIM_TRAVERSAL 1
+#endif
+__device__ __forceinline__ int span_of(const StepArgs &a, int64_t u) {
     int lo = 0, hi = a.nspans;  // spans[nspans].unit_begin == nunits > u
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (a.spans[mid].unit_begin <= u) lo = mid; else hi = mid;
     }
-    int s = lo;
-    for (; u < u1; ++u) {
+    return lo;
+}
+
+template <class Body>
+__device__ __forceinline__ void for_units(const StepArgs &a, Body &&body) {
+    const int64_t G = gridDim.x, b = blockIdx.x;
+#if OPTIM_TRAVERSAL == 0
+    int64_t u = a.nunits * b / G;
+    const int64_t u1 = a.nunits * (b + 1) / G, stride = 1;
+#else
+    int64_t u = b;
+    const int64_t u1 = a.nunits, stride = G;
+#endif
+    if (u >= u1) return;
+    int s = span_of(a, u);
+    for (; u < u1; u += stride) {
         while (a.spans[s + 1].unit_begin <= u) ++s;
         const SpanDesc sp = a.spans[s];
         const int64_t off = (u - sp.unit_begin) * kTile;
         const int64_t len = sp.len - off < kTile ? sp.len - off : kTile;
         body(u, sp, sp.elem_begin + off, len);
     }
+}
+
+// ---------------------------------------------------------------- per-step scalars
+// Bias corrections and step sizes in fp64, rounded once to fp32: in fp32,
+// 1 - beta2^t cancels badly at small t, and fast power/divide intrinsics put
+// a kernel micro-units off the closed form ([BNB] PR body).  beta^t is taken
+// by repeated squaring (t is an integer; a few ulp of fp64 at most).  The lr
+// is read from a device scalar (or computed from the device iteration
+// counter for the cosine schedule), never passed from the host per step
+// ([AO]).
+__device__ __forceinline__ double ipow(double b, int32_t t) {
+    double r = 1.0;
+    for (; t > 0; t >>= 1) {
+        if (t & 1) r *= b;
+        b *= b;
+    }
+    return r;
+}
+
+// Thread 0 derives the step's scalars into LDS; the caller then reads them
+// back as wave-uniform values.
+__device__ __forceinline__ void step_begin(const StepArgs &a, Scalars &S) {
+    const PrepArgs &p = a.prep;
+    if (threadIdx.x == 0) {
+        float lr;
+        int32_t k = 0;
+        if (p.sched == 1) {
+            k = *p.iter_dev;
+            const int32_t kk = k < 0 ? 0 : (k < p.K ? k : p.K);
+            const double x = (double)kk / (double)p.K;
+            lr = (float)(p.lr_min + (p.lr_max - p.lr_min) * 0.5 * (1.0 + cos(kPi * x)));
+        } else {
+            lr = *p.lr_dev;
+        }
+        const int skip = (p.found_inf != nullptr) && (*p.found_inf != 0.0f);
+        const int32_t t = *p.step_dev + 1;
+        const double bc1 = 1.0 - ipow(p.beta1, t);
+        const double bc2 = 1.0 - ipow(p.beta2, t);
+        const double lr64 = (double)lr;
+        const double rs2 = 1.0 / sqrt(bc2);
+        S.skip = skip;
+        S.t = t;
+        S.k = k;
+        S.lr = lr;
+        S.step_size = (float)(lr64 / bc1);
+        S.inv_sqrt_bc2 = (float)rs2;
+        S.inv_bc1 = (float)(1.0 / bc1);
+        S.b1 = (float)p.beta1;
+        S.c1 = (float)(1.0 - p.beta1);
+        S.b2 = (float)p.beta2;
+        S.c2 = (float)(1.0 - p.beta2);
+        S.b3 = (float)p.beta3;
+        S.c3 = (float)(1.0 - p.beta3);
+        S.alpha = (float)p.alpha;
+        S.eps = (float)p.eps;
+        S.inv_scale = p.inv_scale ? *p.inv_scale : 1.0f;
+        S.lr64 = lr64;
+        S.step_size64 = lr64 / bc1;
+        S.inv_sqrt_bc2_64 = rs2;
+        S.eps64 = p.eps;
+        S.beta2_64 = p.beta2;
+        S.c2_64 = 1.0 - p.beta2;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < p.ngroups)
+        S.decay[threadIdx.x] = (float)(1.0 - S.lr64 * p.group_wd[threadIdx.x]);
+    __syncthreads();
+}
+
+// Commit: every workgroup read the step counter, lr and iteration in its
+// prologue, before it arrives here; the last workgroup to arrive publishes
+// t (unless the step was skipped), the scheduled lr and k + 1, and rearms the
+// counters.  Arrivals go through kSubCounters counters on separate lines and
+// then one top counter, so no single address takes every workgroup's atomic.
+// Ordering: the only requirement is that every prologue load has returned
+// before its workgroup arrives, so a workgroup-scope fence (a wait on
+// outstanding memory operations) precedes a relaxed device-scope RMW.  An
+// acquire/release RMW at device scope would instead write back and
+// invalidate the XCD's L2 in every workgroup.
+__device__ __forceinline__ uint32_t arrive(uint32_t *c) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void step_end(const StepArgs &a, const Scalars &S) {
+    if (!a.commit || threadIdx.x != 0) return;
+    const uint32_t G = gridDim.x, b = blockIdx.x;
+    const uint32_t nsub = G < (uint32_t)kSubCounters ? G : (uint32_t)kSubCounters;
+    const uint32_t j = b % nsub;
+    const uint32_t members = G / nsub + (j < G % nsub ? 1u : 0u);
+    uint32_t *sub = a.done + (1 + j) * kCounterStride;
+    if (arrive(sub) != members - 1) return;
+    __hip_atomic_store(sub, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (arrive(a.done) != nsub - 1) return;
+    __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const PrepArgs &p = a.prep;
+    if (p.sched == 1) {
+        *p.lr_dev = S.lr;
+        *p.iter_dev = S.k + 1;
+    }
+    if (!S.skip) *p.step_dev = S.t;
+}
+
+// Runs the commit on every exit path of a step kernel (skipped steps too).
+struct StepCommit {
+    const StepArgs &a;
+    const Scalars &S;
+    __device__ ~StepCommit() { step_end(a, S); }
+};
+
+__device__ __forceinline__ float uniform(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
 // ---------------------------------------------------------------- AdamW / AdEMAMix
@@ -188,9 +346,10 @@ struct AdamK {
 
 __device__ __forceinline__ AdamK adam_consts(const Scalars &S) {
     AdamK k;
-    k.b1 = S.b1; k.c1 = S.c1; k.b2 = S.b2; k.c2 = S.c2; k.b3 = S.b3; k.c3 = S.c3;
-    k.alpha = S.alpha; k.eps = S.eps; k.ss = S.step_size; k.isb2 = S.inv_sqrt_bc2;
-    k.ibc1 = S.inv_bc1; k.lr = S.lr; k.inv_scale = S.inv_scale;
+    k.b1 = uniform(S.b1); k.c1 = uniform(S.c1); k.b2 = uniform(S.b2); k.c2 = uniform(S.c2);
+    k.b3 = uniform(S.b3); k.c3 = uniform(S.c3); k.alpha = uniform(S.alpha);
+    k.eps = uniform(S.eps); k.ss = uniform(S.step_size); k.isb2 = uniform(S.inv_sqrt_bc2);
+    k.ibc1 = uniform(S.inv_bc1); k.lr = uniform(S.lr); k.inv_scale = uniform(S.inv_scale);
     return k;
 }
 
@@ -242,12 +401,14 @@ __device__ __forceinline__ void adam_unit(const TensorDesc &T, int64_t start, in
 
 template <int PK, int GK, bool ADE>
 __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
-    const Scalars &S = *a.sc;
+    __shared__ Scalars S;
+    step_begin(a, S);
+    const StepCommit commit{a, S};
     if (S.skip) return;
     const AdamK k = adam_consts(S);
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
         const TensorDesc &T = a.tensors[sp.tensor];
-        adam_unit<PK, GK, ADE>(T, start, len, k, S.decay[T.group]);
+        adam_unit<PK, GK, ADE>(T, start, len, k, uniform(S.decay[T.group]));
     });
 }
 
@@ -264,7 +425,9 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 template <int GK>
 __global__ __launch_bounds__(kThreads) void mini_sumsq_kernel(StepArgs a) {
-    const Scalars &S = *a.sc;
+    __shared__ Scalars S;
+    step_begin(a, S);
+    const StepCommit commit{a, S};
     if (S.skip) return;
     const float s = S.inv_scale;
     __shared__ double red[kThreads / 64];
@@ -303,7 +466,9 @@ __global__ __launch_bounds__(kThreads) void mini_sumsq_kernel(StepArgs a) {
 }
 
 __global__ __launch_bounds__(kThreads) void mini_finalize_kernel(StepArgs a) {
-    const Scalars &S = *a.sc;
+    __shared__ Scalars S;
+    step_begin(a, S);
+    const StepCommit commit{a, S};
     if (S.skip) return;
     __shared__ double red[kThreads];
     for (int b = blockIdx.x; b < a.nblocks; b += gridDim.x) {
@@ -349,12 +514,14 @@ __device__ __forceinline__ void mini_elems(const TensorDesc &T, int64_t e, const
 
 template <int PK, int GK>
 __global__ __launch_bounds__(kThreads) void mini_update_kernel(StepArgs a) {
-    const Scalars &S = *a.sc;
+    __shared__ Scalars S;
+    step_begin(a, S);
+    const StepCommit commit{a, S};
     if (S.skip) return;
     const AdamK k = adam_consts(S);
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
         const TensorDesc &T = a.tensors[sp.tensor];
-        const float decay = S.decay[T.group];
+        const float decay = uniform(S.decay[T.group]);
         if (sp.block < 0) {
             adam_unit<PK, GK, false>(T, start, len, k, decay);
             return;
@@ -405,14 +572,16 @@ __global__ __launch_bounds__(kThreads) void blockwise_kernel(StepArgs a) {
         for (int i = threadIdx.x; i < CV; i += kThreads) { sMv[i] = cb[ov + i]; sTv[i] = cb[otv + i]; }
     }
     __syncthreads();
-    const Scalars &S = *a.sc;
+    __shared__ Scalars S;
+    step_begin(a, S);
+    const StepCommit commit{a, S};
     if (S.skip) return;
     const AdamK k = adam_consts(S);
     const int L = a.block / E;  // lanes per quantization block (power of 2, <= 64)
     const int lane = threadIdx.x & 63;
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
         const TensorDesc &T = a.tensors[sp.tensor];
-        const float decay = S.decay[T.group];
+        const float decay = uniform(S.decay[T.group]);
         float *P = static_cast<float *>(T.p);
         const int rows = (int)((len + kThreads * E - 1) / (kThreads * E));
         for (int row = 0; row < rows; ++row) {
@@ -545,64 +714,6 @@ __global__ __launch_bounds__(kThreads) void finite_kernel(StepArgs a) {
     });
 }
 
-// ---------------------------------------------------------------- prep
-// Per-step scalars in fp64, rounded once to fp32.  Bias corrections are not
-// evaluated in fp32: 1 - beta2^t cancels badly there at small t, and fast
-// power/divide intrinsics put a kernel microns off the closed form ([BNB] PR
-// body).  The lr is read from (or, with a schedule, written to) a device
-// scalar, never passed from the host per step ([AO]).
-__global__ void prep_kernel(PrepArgs a) {
-    __shared__ float s_lr;
-    if (threadIdx.x == 0) {
-        float lr;
-        int32_t k = 0;
-        if (a.sched == 1) {
-            k = *a.iter_dev;
-            const int32_t kk = k < 0 ? 0 : (k < a.K ? k : a.K);
-            const double x = (double)kk / (double)a.K;
-            lr = (float)(a.lr_min + (a.lr_max - a.lr_min) * 0.5 * (1.0 + cos(kPi * x)));
-        } else {
-            lr = *a.lr_dev;
-        }
-        const int skip = (a.found_inf != nullptr) && (*a.found_inf != 0.0f);
-        const int32_t t = *a.step_dev + 1;
-        const double bc1 = 1.0 - pow(a.beta1, (double)t);
-        const double bc2 = 1.0 - pow(a.beta2, (double)t);
-        const double lr64 = (double)lr;
-        Scalars *sc = a.sc;
-        sc->skip = skip;
-        sc->t = t;
-        sc->lr = lr;
-        sc->step_size = (float)(lr64 / bc1);
-        sc->inv_sqrt_bc2 = (float)(1.0 / sqrt(bc2));
-        sc->inv_bc1 = (float)(1.0 / bc1);
-        sc->b1 = (float)a.beta1;
-        sc->c1 = (float)(1.0 - a.beta1);
-        sc->b2 = (float)a.beta2;
-        sc->c2 = (float)(1.0 - a.beta2);
-        sc->b3 = (float)a.beta3;
-        sc->c3 = (float)(1.0 - a.beta3);
-        sc->alpha = (float)a.alpha;
-        sc->eps = (float)a.eps;
-        sc->inv_scale = a.inv_scale ? *a.inv_scale : 1.0f;
-        sc->lr64 = lr64;
-        sc->step_size64 = lr64 / bc1;
-        sc->inv_sqrt_bc2_64 = 1.0 / sqrt(bc2);
-        sc->eps64 = a.eps;
-        sc->beta2_64 = a.beta2;
-        sc->c2_64 = 1.0 - a.beta2;
-        s_lr = lr;
-        if (a.sched == 1) {
-            *a.lr_dev = lr;
-            *a.iter_dev = k + 1;
-        }
-        if (!skip) *a.step_dev = t;
-    }
-    __syncthreads();
-    if ((int)threadIdx.x < a.ngroups)
-        a.sc->decay[threadIdx.x] = (float)(1.0 - (double)s_lr * a.group_wd[threadIdx.x]);
-}
-
 // ---------------------------------------------------------------- remainder utils
 __global__ __launch_bounds__(kThreads) void split_kernel(const float *x, uint16_t *b, int16_t *r,
                                                          int64_t n) {
@@ -633,23 +744,19 @@ int flat_grid(int64_t n) {
 // A positive request overrides the occupancy query.
 template <class K>
 int persistent_grid(K kernel, const StepArgs &a) {
-    if (a.grid_request > 0) return a.grid_request < a.nunits ? a.grid_request : (int)a.nunits;
+    const int64_t units = a.nunits > 0 ? a.nunits : 1;
+    if (a.grid_request > 0) return (int)(a.grid_request < units ? a.grid_request : units);
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess ||
         per_cu < 1)
         per_cu = 1;
     const int64_t g = (int64_t)per_cu * (a.cus > 0 ? a.cus : 1);
-    return (int)(g < a.nunits ? g : (a.nunits > 0 ? a.nunits : 1));
+    return (int)(g < units ? g : units);
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_prep(const PrepArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(prep_kernel, dim3(1), dim3(kMaxGroups), 0, s, a);
-    return hipGetLastError();
-}
-
 #define LAUNCH_PERSISTENT(K, a, s)                                                     \
     hipLaunchKernelGGL(K, dim3(persistent_grid(K, a)), dim3(kThreads), 0, s, a)
 
@@ -674,7 +781,10 @@ hipError_t launch_ademamix(const StepArgs &a, int pk, int gk, hipStream_t s) {
     return launch_adam_t<true>(a, pk, gk, s);
 }
 
-hipError_t launch_adam_mini(const StepArgs &a, int pk, int gk, hipStream_t s) {
+hipError_t launch_adam_mini(const StepArgs &args, int pk, int gk, hipStream_t s) {
+    // block sums and finalize read the step's inputs; the update publishes it
+    StepArgs a = args;
+    a.commit = 0;
     if (gk == G_F32)
         LAUNCH_PERSISTENT((mini_sumsq_kernel<G_F32>), a, s);
     else
@@ -687,6 +797,7 @@ hipError_t launch_adam_mini(const StepArgs &a, int pk, int gk, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    a.commit = 1;
     if (pk == P_F32 && gk == G_F32)
         LAUNCH_PERSISTENT((mini_update_kernel<P_F32, G_F32>), a, s);
     else if (pk == P_F32 && gk == G_BF16)

@@ -45,8 +45,9 @@ struct SpanDesc {         // 32 bytes
 };
 static_assert(sizeof(SpanDesc) == 32, "SpanDesc layout");
 
-// Per-step scalars, written by the prep kernel at the start of every step
-// and read (uniformly) by the step kernels of that step.
+// Per-step scalars.  Every workgroup of a step kernel derives them in its
+// prologue (fp64, rounded once to fp32) into LDS from the device lr, step
+// counter, found_inf and inv_scale.
 struct Scalars {
     int32_t skip;         // non-zero: found_inf was set, write nothing
     int32_t t;            // applied-step count including this step
@@ -60,14 +61,21 @@ struct Scalars {
     float alpha;
     float eps;
     float inv_scale;      // gradient multiplier (AMP unscale), 1 if none
-    float pad0_;
+    int32_t k;            // schedule iteration read by this step
     double lr64, step_size64, inv_sqrt_bc2_64, eps64, beta2_64, c2_64;
     float decay[kMaxGroups];  // fl32(1 - lr * wd_group)
 };
 
+// Commit counters: one top counter and kSubCounters sub-counters, each on its
+// own 128-byte line, so arrivals of different workgroups spread over lines.
+constexpr int kSubCounters = 32;
+constexpr int kCounterStride = 32;  // uint32 words between counters
+constexpr size_t kCounterBytes = (1 + kSubCounters) * kCounterStride * sizeof(uint32_t);
+
 // Workspace layout (byte offsets from the workspace base, 256-aligned).
+// `counters` holds the arrival counters of the step kernels' commit.
 struct Layout {
-    size_t scalars, group_wd, tensors, spans, codebook, partials, blockfac,
+    size_t counters, group_wd, tensors, spans, codebook, partials, blockfac,
         blockspan, total;
 };
 
@@ -78,7 +86,6 @@ constexpr int kCb8SignedVals = 0, kCb8SignedThr = 128, kCb8UnsVals = 256,
               kCb4UnsVals = 784, kCb4UnsThr = 800, kCbFloats = 816;
 
 struct PrepArgs {
-    Scalars *sc;
     const double *group_wd;
     int32_t ngroups;
     int32_t sched;        // OPTIM_SCHED_*
@@ -93,11 +100,13 @@ struct PrepArgs {
 };
 
 struct StepArgs {
+    PrepArgs prep;            // inputs of the per-step scalars
+    uint32_t *done;           // arrival counters (workspace), 0 between steps
+    int32_t commit;           // this kernel publishes step / lr / iteration
     const TensorDesc *tensors;
     const SpanDesc *spans;    // nspans + 1 entries (sentinel at the end)
     int32_t nspans;
     int64_t nunits;
-    const Scalars *sc;
     double *partials;         // Adam-mini: one per unit
     float *blockfac;          // Adam-mini: per block lr/bc1/h
     const int32_t *blockspan; // Adam-mini: span index of each block
@@ -109,8 +118,9 @@ struct StepArgs {
     int32_t grid_request;     // persistent workgroups requested (0 = auto)
 };
 
-// Launchers (kernels.hip).  Return the hipError_t of the launch.
-hipError_t launch_prep(const PrepArgs &a, hipStream_t s);
+// Launchers (kernels.hip).  Return the hipError_t of the launch.  Step
+// launchers always start at least one workgroup (the commit must run even
+// for an empty plan).
 hipError_t launch_adamw(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_ademamix(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_adam_mini(const StepArgs &a, int pk, int gk, hipStream_t s);

@@ -129,7 +129,8 @@ def test_c3_llama1b_bf16_remainder_amp_cosine():
     for i, s in enumerate(specs):
         extra = [e for (ti, e) in inject.values() if ti == i]
         rng = synth.host_rng(wl.index, i, 0, 9)
-        idx = np.unique(np.concatenate([rng.integers(0, s.numel, 64), [0, s.numel - 1], extra]))
+        idx = np.unique(np.concatenate([rng.integers(0, s.numel, 64), [0, s.numel - 1],
+                                         np.array(extra, dtype=np.int64)]))
         samp.append((torch.from_numpy(idx).to(DEV), idx))
     op = [p0[i][d].double().cpu().numpy() for i, (d, _) in enumerate(samp)]
     del p0
