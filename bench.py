@@ -310,20 +310,52 @@ def cpu_baseline(synth, target_s):
                        f"{spent:.1f} s, single thread ({os.cpu_count()} host cores visible)")
 
 
+KERNEL_SOURCES = {  # kernel -> sources its device code comes from
+    "adamw_fp32": ("device_common.h", "kernels_adam.hip"),
+    "ademamix_fp32": ("device_common.h", "kernels_adam.hip"),
+}
+
+
+def kernel_sources_sha256(kernel_key):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel_key]:
+        with open(os.path.join(ROOT, "optimizer_step_adamw_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(kernel_key):
-    """HBM traffic per launch from the committed rocprofv3 counter summary,
-    valid only while the kernel source is the one the counters were taken on."""
-    src = os.path.join(ROOT, "optimizer_step_adamw_amd", "csrc", "kernels.hip")
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size), valid
+    only while the kernel's sources are the ones the counters were taken on."""
     path = os.path.join(ROOT, "profiles", f"counters_{kernel_key}.txt")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or kernel_key not in KERNEL_SOURCES:
         return None
     text = open(path).read()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    m = re.search(r"kernels_hip_sha256:\s*([0-9a-f]{64})", text)
+    m = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != sha:
+    if not m or not t or m.group(1) != kernel_sources_sha256(kernel_key):
         return None
     return float(t.group(1))
+
+
+def copy_probe(torch, nbytes=256 << 20, reps=5):
+    """Plain device-to-device copy of a known size: the streaming ceiling for
+    context, and the known-size kernel that scales the traffic counters."""
+    x = torch.randn(nbytes // 4, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        y.copy_(x)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del x, y
+    return dict(bytes=2 * nbytes, ms=ms, gbs=2 * nbytes / (ms * 1e-3) / 1e9)
 
 
 def main():
@@ -340,6 +372,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     log(f"device: {torch.cuda.get_device_name(0)}")
+    copy = copy_probe(torch)
+    log(f"copy probe: {json.dumps(copy)}")
     head = bench_headline(torch, osa, synth, args.steps, args.warmup)
     log(f"headline: {head['ms_per_step']:.4f} ms/step, {head['elements_per_s']:.4e} elem/s, "
         f"{json.dumps(head['kernels'])}")
@@ -375,6 +409,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": head["kernels"],
+        "copy_ceiling": copy,
         "secondary": secondary,
     }
     print(json.dumps(out), flush=True)

@@ -99,13 +99,18 @@ typedef struct optim_tensor_list {
     int32_t grad_dtype;
 } optim_tensor_list;
 
-/* Plan options.  bits/block: blockwise algorithms only (8-bit: block 64,
- * 128 or 256; 4-bit: block 128, 256 or 512).  grid: persistent workgroup
- * count, 0 = chosen from the device's compute-unit count.                */
+/* Plan options (NULL = all defaults).
+ *  bits/block  blockwise algorithms only (8-bit: block 64, 128 or 256;
+ *              4-bit: block 128, 256 or 512)
+ *  grid        0 (default): one workgroup per work unit; > 0: a persistent
+ *              grid of that many workgroups walking the units grid-stride
+ *  tile        elements per work unit, a power of two in [2048, 2^24];
+ *              0 = 2048 (16384 for blockwise plans)                       */
 typedef struct optim_plan_opts {
     int32_t bits;
     int32_t block;
     int32_t grid;
+    int32_t tile;
 } optim_plan_opts;
 
 /* Hyperparameters, validated as in [MINI] AdamWMini's constructor:
@@ -137,7 +142,7 @@ int optim_plan_workspace_size(const optim_tensor_list *list, int32_t algo,
  * allocated and untouched while the plan lives; steps of one plan must not
  * overlap each other (they share its workspace).  The host arrays of `list`
  * may be freed after return.  Queries the current device's compute-unit
- * count to size the persistent grid.                                      */
+ * count.                                                                  */
 int optim_plan_create(const optim_tensor_list *list, int32_t algo,
                       const optim_plan_opts *opts, void *workspace,
                       size_t workspace_bytes, void *stream, optim_plan **out);
@@ -222,6 +227,23 @@ int optim_step_8bit_blockwise(optim_plan *plan, const optim_adamw_hp *hp,
  * +-Inf ([LTN] analysis: the fused step consumes found_inf); otherwise
  * leaves it unchanged, so the caller zeroes it first.                     */
 int optim_check_finite(optim_plan *plan, float *found_inf_dev, void *stream);
+
+/* Blockwise quantize / dequantize of a plain fp32 device array with the
+ * codebook, bits and block of a blockwise `plan`, by the same device code as
+ * optim_step_8bit_blockwise: for importing fp32 optimizer state into codes
+ * and exporting it back (checkpoints).  is_signed: the signed map (used for
+ * m) or the unsigned map (for v).  codes: (n*bits+7)/8 bytes (4-bit: element
+ * 2i in the low nibble); absmax: ceil(n/block) floats; blocks start at
+ * element 0.  Quantize: A = max|x| per block, a = fl32(|x| * fl32(1/A)),
+ * code = largest j with T[j] <= a (sign above the magnitude bits for the
+ * signed map, 0 if A = 0).  Dequantize: x = fl32(+-M[idx] * A).          */
+int optim_quantize_blockwise(optim_plan *plan, int32_t is_signed,
+                             const float *x_dev, int64_t n, uint8_t *codes_dev,
+                             float *absmax_dev, void *stream);
+int optim_dequantize_blockwise(optim_plan *plan, int32_t is_signed,
+                               const uint8_t *codes_dev,
+                               const float *absmax_dev, int64_t n,
+                               float *x_dev, void *stream);
 
 /* [TE] description: fp32 master <-> (bf16 param, int16 remainder).  For the
  * 32-bit pattern u of x: r = low 16 bits of u as int16, b = (high 16 bits of

@@ -26,7 +26,8 @@ EXPORTED = (
     "optim_last_error", "optim_plan_workspace_size", "optim_plan_create", "optim_plan_destroy",
     "optim_plan_set_schedule", "optim_step_adamw", "optim_step_ademamix", "optim_step_adam_mini",
     "optim_step_8bit_blockwise", "optim_check_finite", "optim_remainder_split",
-    "optim_remainder_reconstruct", "optim_quant_codebook",
+    "optim_remainder_reconstruct", "optim_quant_codebook", "optim_quantize_blockwise",
+    "optim_dequantize_blockwise",
 )
 
 
@@ -55,7 +56,8 @@ class optim_tensor_list(ctypes.Structure):
 
 
 class optim_plan_opts(ctypes.Structure):
-    _fields_ = [("bits", ctypes.c_int32), ("block", ctypes.c_int32), ("grid", ctypes.c_int32)]
+    _fields_ = [("bits", ctypes.c_int32), ("block", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("tile", ctypes.c_int32)]
 
 
 class optim_adamw_hp(ctypes.Structure):
@@ -97,6 +99,8 @@ def lib() -> ctypes.CDLL:
             "optim_remainder_split": ([_P, _P, _P, i64, _P], i32),
             "optim_remainder_reconstruct": ([_P, _P, _P, i64, _P], i32),
             "optim_quant_codebook": ([i32, i32, _P, _P], i32),
+            "optim_quantize_blockwise": ([_P, i32, _P, i64, _P, _P, _P], i32),
+            "optim_dequantize_blockwise": ([_P, i32, _P, _P, i64, _P, _P], i32),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -236,6 +240,16 @@ def optim_remainder_reconstruct(bf16, rem, master, n: int, stream=None) -> None:
            "optim_remainder_reconstruct")
 
 
+def optim_quantize_blockwise(plan, is_signed: bool, x, n: int, codes, absmax, stream=None) -> None:
+    _check(lib().optim_quantize_blockwise(plan, int(is_signed), _ptr(x), n, _ptr(codes), _ptr(absmax),
+                                          _stream(stream)), "optim_quantize_blockwise")
+
+
+def optim_dequantize_blockwise(plan, is_signed: bool, codes, absmax, n: int, x, stream=None) -> None:
+    _check(lib().optim_dequantize_blockwise(plan, int(is_signed), _ptr(codes), _ptr(absmax), n, _ptr(x),
+                                            _stream(stream)), "optim_dequantize_blockwise")
+
+
 def optim_quant_codebook(bits: int, is_signed: bool):
     import numpy as np
     mb = bits - 1 if is_signed else bits
@@ -252,11 +266,11 @@ class Plan:
     """Plan + workspace.  ``tl`` must hold device tensors that outlive it."""
 
     def __init__(self, tl: TensorList, algo: int, *, bits: int = 0, block: int = 0, grid: int = 0,
-                 device=None, stream=None):
+                 tile: int = 0, device=None, stream=None):
         import torch
         self.algo = algo
         self.tl = tl
-        self.opts = optim_plan_opts(bits, block, grid)
+        self.opts = optim_plan_opts(bits, block, grid, tile)
         nbytes = optim_plan_workspace_size(tl, algo, self.opts)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
         self.handle = optim_plan_create(tl, algo, self.opts, self.workspace, nbytes, stream)

@@ -53,6 +53,39 @@ void dynamic_map(int mb, float *vals, float *thr) {
     }
 }
 
+float bits_to_float(uint32_t u) {
+    float f;
+    std::memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+// Largest j >= 1 with thr[j] <= a, else 0 (the threshold rule itself).
+int threshold_index(const float *thr, int count, float a) {
+    int idx = 0;
+    for (int j = 1; j < count; ++j)
+        if (thr[j] <= a) idx = j;
+    return idx;
+}
+
+// Values, thresholds and the bucket table of one map.  Returns false if a
+// bucket would hold two thresholds or a threshold lies below the table.
+bool build_map(int mb, QuantMap &q) {
+    std::memset(&q, 0, sizeof q);
+    dynamic_map(mb, q.vals, q.thr);
+    const int count = 1 << mb;
+    const uint32_t shift = 23 - kLutMantBits;
+    if (threshold_index(q.thr, count, bits_to_float(((uint32_t)kLutBaseExp << 23) - 1)) != 0) return false;
+    for (int b = 0; b < kLutBuckets; ++b) {
+        const uint32_t lo = (uint32_t)(b + (kLutBaseExp << kLutMantBits)) << shift;
+        const uint32_t hi = lo + (1u << shift) - 1u;
+        const int ilo = threshold_index(q.thr, count, bits_to_float(lo));
+        const int ihi = threshold_index(q.thr, count, bits_to_float(hi));
+        if (ihi - ilo > 1) return false;
+        q.lut[b] = (uint8_t)ilo;
+    }
+    return true;
+}
+
 // ---------------------------------------------------------------- plan build
 struct Built {
     std::vector<TensorDesc> tensors;
@@ -60,6 +93,7 @@ struct Built {
     std::vector<int32_t> blockspan;
     std::vector<double> group_wd;
     int64_t nunits = 0;
+    int64_t tile = 0;
     int32_t nblocks = 0;
     Layout L{};
 };
@@ -105,6 +139,14 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
                                                 : "4-bit block must be 128, 256 or 512");
     }
     if (opts && opts->grid < 0) return fail(OPTIM_EINVAL, "negative grid");
+    // measured on MI355X: one 2048-element row per workgroup streams best for
+    // the elementwise steps; the blockwise step amortises its LDS tables and
+    // prologue over larger units
+    const int64_t tile = (opts && opts->tile > 0) ? opts->tile
+                         : (algo == OPTIM_ALGO_BLOCKWISE ? kBlockwiseTile : kDefaultTile);
+    if (tile < kMinTile || tile > (1 << 24) || (tile & (tile - 1)))
+        return fail(OPTIM_EINVAL, "tile must be a power of two in [2048, 2^24]");
+    B.tile = tile;
     if (n > 0 && (!list->numel || !list->param || !list->grad || !list->weight_decay))
         return fail(OPTIM_EINVAL, "numel, param, grad and weight_decay arrays are required");
     const bool need_mv = algo != OPTIM_ALGO_BLOCKWISE;
@@ -222,13 +264,13 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
                 SpanDesc sp{B.nunits, s, T.block_len, i, B.nblocks};
                 B.blockspan.push_back((int32_t)B.spans.size());
                 B.spans.push_back(sp);
-                B.nunits += (T.block_len + kTile - 1) / kTile;
+                B.nunits += (T.block_len + tile - 1) / tile;
                 if (B.nblocks == INT32_MAX) return fail(OPTIM_EUNSUPPORTED, "too many blocks");
                 ++B.nblocks;
             }
         } else {
             B.spans.push_back(SpanDesc{B.nunits, 0, numel, i, -1});
-            B.nunits += (numel + kTile - 1) / kTile;
+            B.nunits += (numel + tile - 1) / tile;
         }
     }
     if (B.spans.size() >= (size_t)INT32_MAX) return fail(OPTIM_EUNSUPPORTED, "too many spans");
@@ -256,7 +298,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     L.group_wd = off; off += align256(kMaxGroups * sizeof(double));
     L.tensors = off; off += align256(std::max<size_t>(1, B.tensors.size()) * sizeof(TensorDesc));
     L.spans = off; off += align256(B.spans.size() * sizeof(SpanDesc));
-    L.codebook = off; off += algo == OPTIM_ALGO_BLOCKWISE ? align256(kCbFloats * sizeof(float)) : 0;
+    L.codebook = off; off += algo == OPTIM_ALGO_BLOCKWISE ? align256(sizeof(Codebook)) : 0;
     L.blockspan = off; off += align256(std::max<size_t>(1, B.blockspan.size()) * sizeof(int32_t));
     L.partials = off;
     off += algo == OPTIM_ALGO_ADAM_MINI ? align256(std::max<int64_t>(1, B.nunits) * sizeof(double)) : 0;
@@ -271,10 +313,11 @@ struct optim_plan {
     int32_t algo;
     int32_t pk, gk;
     int32_t bits, block;
-    int32_t grid;  // requested persistent workgroups (0 = from occupancy)
+    int32_t grid;  // requested persistent workgroups (0 = one per unit)
     int32_t cus;
     int32_t nspans, nblocks, ngroups;
     int64_t nunits;
+    int64_t tile;
     char *ws;
     Layout L;
     int32_t sched;
@@ -323,11 +366,9 @@ int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_p
     std::memcpy(img.data() + B.L.spans, B.spans.data(), B.spans.size() * sizeof(SpanDesc));
     std::memcpy(img.data() + B.L.blockspan, B.blockspan.data(), B.blockspan.size() * sizeof(int32_t));
     if (algo == OPTIM_ALGO_BLOCKWISE) {
-        float *cb = reinterpret_cast<float *>(img.data() + B.L.codebook);
-        dynamic_map(7, cb + kCb8SignedVals, cb + kCb8SignedThr);
-        dynamic_map(8, cb + kCb8UnsVals, cb + kCb8UnsThr);
-        dynamic_map(3, cb + kCb4SignedVals, cb + kCb4SignedThr);
-        dynamic_map(4, cb + kCb4UnsVals, cb + kCb4UnsThr);
+        Codebook *cb = reinterpret_cast<Codebook *>(img.data() + B.L.codebook);
+        if (!build_map(7, cb->m8) || !build_map(8, cb->v8) || !build_map(3, cb->m4) || !build_map(4, cb->v4))
+            return fail(OPTIM_EUNSUPPORTED, "quantization map does not fit the bucket table");
     }
     int dev = 0, cus = 0;
     HIP_OK(hipGetDevice(&dev));
@@ -349,6 +390,7 @@ int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_p
     P->nblocks = B.nblocks;
     P->ngroups = (int32_t)B.group_wd.size();
     P->nunits = B.nunits;
+    P->tile = B.tile;
     P->ws = static_cast<char *>(workspace);
     P->L = B.L;
     P->sched = OPTIM_SCHED_NONE;
@@ -394,11 +436,12 @@ StepArgs step_args(optim_plan *P) {
     a.spans = reinterpret_cast<const SpanDesc *>(P->ws + P->L.spans);
     a.nspans = P->nspans;
     a.nunits = P->nunits;
+    a.tile = P->tile;
     a.partials = reinterpret_cast<double *>(P->ws + P->L.partials);
     a.blockfac = reinterpret_cast<float *>(P->ws + P->L.blockfac);
     a.blockspan = reinterpret_cast<const int32_t *>(P->ws + P->L.blockspan);
     a.nblocks = P->nblocks;
-    a.codebook = reinterpret_cast<const float *>(P->ws + P->L.codebook);
+    a.codebook = reinterpret_cast<const Codebook *>(P->ws + P->L.codebook);
     a.bits = P->bits;
     a.block = P->block;
     a.cus = P->cus;
@@ -521,6 +564,34 @@ int optim_check_finite(optim_plan *plan, float *found_inf_dev, void *stream) {
     a.commit = 0;
     a.found_inf = found_inf_dev;
     HIP_OK(launch_check_finite(a, plan->gk, static_cast<hipStream_t>(stream)));
+    return OPTIM_OK;
+}
+
+int optim_quantize_blockwise(optim_plan *plan, int32_t is_signed, const float *x_dev, int64_t n,
+                             uint8_t *codes_dev, float *absmax_dev, void *stream) {
+    int rc = check_plan(plan, OPTIM_ALGO_BLOCKWISE, "optim_quantize_blockwise");
+    if (rc) return rc;
+    if (n < 0) return fail(OPTIM_EINVAL, "negative n");
+    if (n == 0) return OPTIM_OK;
+    if (!x_dev || !codes_dev || !absmax_dev) return fail(OPTIM_EINVAL, "NULL buffer");
+    if (!aligned(x_dev, 4) || !aligned(absmax_dev, 4)) return fail(OPTIM_EALIGN, "buffer misaligned");
+    HIP_OK(launch_quantize(reinterpret_cast<const Codebook *>(plan->ws + plan->L.codebook), plan->bits,
+                           plan->block, is_signed ? 1 : 0, x_dev, n, codes_dev, absmax_dev,
+                           static_cast<hipStream_t>(stream)));
+    return OPTIM_OK;
+}
+
+int optim_dequantize_blockwise(optim_plan *plan, int32_t is_signed, const uint8_t *codes_dev,
+                               const float *absmax_dev, int64_t n, float *x_dev, void *stream) {
+    int rc = check_plan(plan, OPTIM_ALGO_BLOCKWISE, "optim_dequantize_blockwise");
+    if (rc) return rc;
+    if (n < 0) return fail(OPTIM_EINVAL, "negative n");
+    if (n == 0) return OPTIM_OK;
+    if (!x_dev || !codes_dev || !absmax_dev) return fail(OPTIM_EINVAL, "NULL buffer");
+    if (!aligned(x_dev, 4) || !aligned(absmax_dev, 4)) return fail(OPTIM_EALIGN, "buffer misaligned");
+    HIP_OK(launch_dequantize(reinterpret_cast<const Codebook *>(plan->ws + plan->L.codebook), plan->bits,
+                             plan->block, is_signed ? 1 : 0, codes_dev, absmax_dev, n, x_dev,
+                             static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
 

@@ -1,0 +1,400 @@
+// device_common.h -- device-side building blocks shared by the gfx950
+// kernels of the fused, multi-tensor AdamW-family optimizer step: storage
+// formats, global-memory accesses, unit traversal, the per-step scalar
+// prologue and commit, and the AdamW/AdEMAMix element update.
+//
+// The step is elementwise and HBM-bound (a few flops per byte), so there is
+// no matrix-core work.  A step kernel processes work units (`tile`
+// consecutive elements of one span) with 128-bit loads and stores, 8
+// consecutive elements per lane; by default one workgroup per unit.  Every
+// workgroup derives the step's scalars in its prologue and the last one to
+// finish publishes the new step counter.
+//
+// Sources (web pages, by title and section):
+//  [BNB]  "Fix decoupled weight decay ordering in the CUDA Adam/AdEMAMix
+//         kernels" (bitsandbytes PR #2040): decay before the update
+//         (Loshchilov & Hutter Algorithm 2 order); AdEMAMix; blockwise 8-bit.
+//  [AO]   "4 bit Adam should support non constant lr" (pytorch/ao #730):
+//         device-resident lr, cosine schedule, 4-bit states.
+//  [MINI] "Adam-mini <> DTensor" (Adam-mini #14): AdamWMini.step.
+//  [LTN]  "FusedAdam & PyTorch Lightning AMP" (Lightning #15501): in-step
+//         unscale and found_inf skip.
+//  [TE]   "Support store_param_remainders feature from Apex in TE Fused
+//         Adam" (TransformerEngine PR #1408): bf16 + int16 remainder.
+//
+// Build flags: -ffp-contract=off (every multiply and add rounds on its own,
+// as written), IEEE division and sqrt, fp32 denormals kept.
+#pragma once
+
+#include "plan.h"
+
+#include <math.h>
+
+namespace optim {
+namespace {
+
+constexpr double kPi = 3.141592653589793;
+
+// ---------------------------------------------------------------- formats
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// [TE] description: the fp32 master is rebuilt from the bf16 param b and the
+// int16 remainder r.  Encoding: r = low half of the master's bits; b = high
+// half + carry (bit 15 of r), so the carry is undone before concatenating.
+__device__ __forceinline__ float rem_reconstruct(uint32_t b, uint32_t r) {
+    const uint32_t c = (r >> 15) & 1u;
+    return __uint_as_float((((b - c) & 0xFFFFu) << 16) | (r & 0xFFFFu));
+}
+
+__device__ __forceinline__ void rem_split(float x, uint32_t &b, uint32_t &r) {
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t lo = u & 0xFFFFu;
+    b = ((u >> 16) + (lo >> 15)) & 0xFFFFu;
+    r = lo;
+}
+
+// ---------------------------------------------------------------- loads
+// Every tensor lives in HBM: accesses go through global-address-space
+// pointers so they compile to global_load/store (not flat) instructions.
+// N = 8: two 128-bit accesses (fp32) or one (16-bit); N = 1: one element.
+#define GMEM __attribute__((address_space(1)))
+typedef float __attribute__((ext_vector_type(4))) f32x4;
+typedef uint32_t __attribute__((ext_vector_type(4))) u32x4;
+typedef uint32_t __attribute__((ext_vector_type(2))) u32x2;
+
+template <class T>
+__device__ __forceinline__ GMEM T *gp(T *p) { return (GMEM T *)p; }
+template <class T>
+__device__ __forceinline__ const GMEM T *gp(const T *p) { return (const GMEM T *)p; }
+
+template <class V>
+__device__ __forceinline__ V vload(const GMEM V *q) {
+    return *q;
+}
+template <class V>
+__device__ __forceinline__ void vstore(GMEM V *q, V x) {
+    *q = x;
+}
+
+template <int N>
+__device__ __forceinline__ void ldf(const float *a, int64_t e, float (&x)[N]) {
+    if constexpr (N == 8) {
+        const GMEM f32x4 *q = (const GMEM f32x4 *)gp(a + e);
+        const f32x4 u = vload(q), w = vload(q + 1);
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+        x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
+    } else if constexpr (N == 4) {
+        const f32x4 u = *(const GMEM f32x4 *)gp(a + e);
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    } else {
+        const GMEM float *q = gp(a);
+#pragma unroll
+        for (int k = 0; k < N; ++k) x[k] = q[e + k];
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void stf(float *a, int64_t e, const float (&x)[N]) {
+    if constexpr (N == 8) {
+        GMEM f32x4 *q = (GMEM f32x4 *)gp(a + e);
+        vstore(q, f32x4{x[0], x[1], x[2], x[3]});
+        vstore(q + 1, f32x4{x[4], x[5], x[6], x[7]});
+    } else if constexpr (N == 4) {
+        *(GMEM f32x4 *)gp(a + e) = f32x4{x[0], x[1], x[2], x[3]};
+    } else {
+        GMEM float *q = gp(a);
+#pragma unroll
+        for (int k = 0; k < N; ++k) q[e + k] = x[k];
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void ldh(const uint16_t *a, int64_t e, uint32_t (&x)[N]) {
+    if constexpr (N == 8) {
+        const u32x4 u = vload((const GMEM u32x4 *)gp(a + e));
+        x[0] = u.x & 0xFFFFu; x[1] = u.x >> 16; x[2] = u.y & 0xFFFFu; x[3] = u.y >> 16;
+        x[4] = u.z & 0xFFFFu; x[5] = u.z >> 16; x[6] = u.w & 0xFFFFu; x[7] = u.w >> 16;
+    } else if constexpr (N == 4) {
+        const u32x2 u = *(const GMEM u32x2 *)gp(a + e);
+        x[0] = u.x & 0xFFFFu; x[1] = u.x >> 16; x[2] = u.y & 0xFFFFu; x[3] = u.y >> 16;
+    } else {
+        const GMEM uint16_t *q = gp(a);
+#pragma unroll
+        for (int k = 0; k < N; ++k) x[k] = q[e + k];
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void sth(uint16_t *a, int64_t e, const uint32_t (&x)[N]) {
+    if constexpr (N == 8) {
+        vstore((GMEM u32x4 *)gp(a + e),
+               u32x4{(x[0] & 0xFFFFu) | (x[1] << 16), (x[2] & 0xFFFFu) | (x[3] << 16),
+                     (x[4] & 0xFFFFu) | (x[5] << 16), (x[6] & 0xFFFFu) | (x[7] << 16)});
+    } else if constexpr (N == 4) {
+        *(GMEM u32x2 *)gp(a + e) = u32x2{(x[0] & 0xFFFFu) | (x[1] << 16), (x[2] & 0xFFFFu) | (x[3] << 16)};
+    } else {
+        GMEM uint16_t *q = gp(a);
+#pragma unroll
+        for (int k = 0; k < N; ++k) q[e + k] = (uint16_t)x[k];
+    }
+}
+
+template <int PK, int N>
+__device__ __forceinline__ void load_p(const TensorDesc &T, int64_t e, float (&p)[N]) {
+    if constexpr (PK == P_F32) {
+        ldf<N>(static_cast<const float *>(T.p), e, p);
+    } else {
+        uint32_t b[N], r[N];
+        ldh<N>(static_cast<const uint16_t *>(T.p), e, b);
+        ldh<N>(T.rem, e, r);
+#pragma unroll
+        for (int k = 0; k < N; ++k) p[k] = rem_reconstruct(b[k], r[k]);
+    }
+}
+
+template <int PK, int N>
+__device__ __forceinline__ void store_p(const TensorDesc &T, int64_t e, const float (&p)[N]) {
+    if constexpr (PK == P_F32) {
+        stf<N>(static_cast<float *>(T.p), e, p);
+    } else {
+        uint32_t b[N], r[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) rem_split(p[k], b[k], r[k]);
+        sth<N>(static_cast<uint16_t *>(T.p), e, b);
+        sth<N>(T.rem, e, r);
+    }
+}
+
+// Gradient load with the AMP unscale applied exactly once ([LTN] analysis).
+template <int GK, int N>
+__device__ __forceinline__ void load_g(const void *g, int64_t e, float s, float (&x)[N]) {
+    if constexpr (GK == G_F32) {
+        ldf<N>(static_cast<const float *>(g), e, x);
+    } else {
+        uint32_t b[N];
+        ldh<N>(static_cast<const uint16_t *>(g), e, b);
+#pragma unroll
+        for (int k = 0; k < N; ++k) x[k] = bf16_to_f32(b[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) x[k] = x[k] * s;
+}
+
+// ---------------------------------------------------------------- traversal
+// Calls body(u, span, first element, element count) for every unit u this
+// workgroup owns: u = b, b + G, b + 2G, ... (with the default grid of one
+// workgroup per unit, just u = b).  All arguments are uniform across the
+// workgroup.  A persistent grid walks grid-stride so its resident
+// workgroups sweep one window of each array at a time (measured faster on
+// MI355X than one contiguous range per workgroup, whose ~1500 separate
+// streams lose DRAM page locality).
+__device__ __forceinline__ int span_of(const StepArgs &a, int64_t u) {
+    int lo = 0, hi = a.nspans;  // spans[nspans].unit_begin == nunits > u
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.spans[mid].unit_begin <= u) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+template <class Body>
+__device__ __forceinline__ void for_units(const StepArgs &a, Body &&body) {
+    const int64_t G = gridDim.x;
+    int64_t u = blockIdx.x;
+    if (u >= a.nunits) return;
+    int s = span_of(a, u);
+    for (; u < a.nunits; u += G) {
+        while (a.spans[s + 1].unit_begin <= u) ++s;
+        const SpanDesc sp = a.spans[s];
+        const int64_t off = (u - sp.unit_begin) * a.tile;
+        const int64_t len = sp.len - off < a.tile ? sp.len - off : a.tile;
+        body(u, sp, sp.elem_begin + off, len);
+    }
+}
+
+// ---------------------------------------------------------------- per-step scalars
+// Bias corrections and step sizes in fp64, rounded once to fp32: in fp32,
+// 1 - beta2^t cancels badly at small t, and fast power/divide intrinsics put
+// a kernel micro-units off the closed form ([BNB] PR body).  beta^t is taken
+// by repeated squaring (t is an integer; a few ulp of fp64 at most).  The lr
+// is read from a device scalar (or computed from the device iteration
+// counter for the cosine schedule), never passed from the host per step
+// ([AO]).
+__device__ __forceinline__ double ipow(double b, int32_t t) {
+    double r = 1.0;
+    for (; t > 0; t >>= 1) {
+        if (t & 1) r *= b;
+        b *= b;
+    }
+    return r;
+}
+
+// Thread 0 derives the step's scalars into LDS; the caller then reads them
+// back as wave-uniform values.
+__device__ __forceinline__ void step_begin(const StepArgs &a, Scalars &S) {
+    const PrepArgs &p = a.prep;
+    if (threadIdx.x == 0) {
+        float lr;
+        int32_t k = 0;
+        if (p.sched == 1) {
+            k = *p.iter_dev;
+            const int32_t kk = k < 0 ? 0 : (k < p.K ? k : p.K);
+            const double x = (double)kk / (double)p.K;
+            lr = (float)(p.lr_min + (p.lr_max - p.lr_min) * 0.5 * (1.0 + cos(kPi * x)));
+        } else {
+            lr = *p.lr_dev;
+        }
+        const int skip = (p.found_inf != nullptr) && (*p.found_inf != 0.0f);
+        const int32_t t = *p.step_dev + 1;
+        const double bc1 = 1.0 - ipow(p.beta1, t);
+        const double bc2 = 1.0 - ipow(p.beta2, t);
+        const double lr64 = (double)lr;
+        const double rs2 = 1.0 / sqrt(bc2);
+        S.skip = skip;
+        S.t = t;
+        S.k = k;
+        S.lr = lr;
+        S.step_size = (float)(lr64 / bc1);
+        S.inv_sqrt_bc2 = (float)rs2;
+        S.inv_bc1 = (float)(1.0 / bc1);
+        S.b1 = (float)p.beta1;
+        S.c1 = (float)(1.0 - p.beta1);
+        S.b2 = (float)p.beta2;
+        S.c2 = (float)(1.0 - p.beta2);
+        S.b3 = (float)p.beta3;
+        S.c3 = (float)(1.0 - p.beta3);
+        S.alpha = (float)p.alpha;
+        S.eps = (float)p.eps;
+        S.inv_scale = p.inv_scale ? *p.inv_scale : 1.0f;
+        S.lr64 = lr64;
+        S.step_size64 = lr64 / bc1;
+        S.inv_sqrt_bc2_64 = rs2;
+        S.eps64 = p.eps;
+        S.beta2_64 = p.beta2;
+        S.c2_64 = 1.0 - p.beta2;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < p.ngroups)
+        S.decay[threadIdx.x] = (float)(1.0 - S.lr64 * p.group_wd[threadIdx.x]);
+    __syncthreads();
+}
+
+// Commit: every workgroup read the step counter, lr and iteration in its
+// prologue, before it arrives here; the last workgroup to arrive publishes
+// t (unless the step was skipped), the scheduled lr and k + 1, and rearms the
+// counters.  Arrivals go through kSubCounters counters on separate lines and
+// then one top counter, so no single address takes every workgroup's atomic.
+// Ordering: the only requirement is that every prologue load has returned
+// before its workgroup arrives, so a workgroup-scope fence (a wait on
+// outstanding memory operations) precedes a relaxed device-scope RMW.  An
+// acquire/release RMW at device scope would instead write back and
+// invalidate the XCD's L2 in every workgroup.
+__device__ __forceinline__ uint32_t arrive(uint32_t *c) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void step_end(const StepArgs &a, const Scalars &S) {
+    if (!a.commit || threadIdx.x != 0) return;
+    const uint32_t G = gridDim.x, b = blockIdx.x;
+    const uint32_t nsub = G < (uint32_t)kSubCounters ? G : (uint32_t)kSubCounters;
+    const uint32_t j = b % nsub;
+    const uint32_t members = G / nsub + (j < G % nsub ? 1u : 0u);
+    uint32_t *sub = a.done + (1 + j) * kCounterStride;
+    if (arrive(sub) != members - 1) return;
+    __hip_atomic_store(sub, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (arrive(a.done) != nsub - 1) return;
+    __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const PrepArgs &p = a.prep;
+    if (p.sched == 1) {
+        *p.lr_dev = S.lr;
+        *p.iter_dev = S.k + 1;
+    }
+    if (!S.skip) *p.step_dev = S.t;
+}
+
+// Runs the commit on every exit path of a step kernel (skipped steps too).
+struct StepCommit {
+    const StepArgs &a;
+    const Scalars &S;
+    __device__ ~StepCommit() { step_end(a, S); }
+};
+
+__device__ __forceinline__ float uniform(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
+// ---------------------------------------------------------------- AdamW / AdEMAMix
+struct AdamK {
+    float b1, c1, b2, c2, b3, c3, alpha, eps, ss, isb2, ibc1, lr, inv_scale;
+};
+
+__device__ __forceinline__ AdamK adam_consts(const Scalars &S) {
+    AdamK k;
+    k.b1 = uniform(S.b1); k.c1 = uniform(S.c1); k.b2 = uniform(S.b2); k.c2 = uniform(S.c2);
+    k.b3 = uniform(S.b3); k.c3 = uniform(S.c3); k.alpha = uniform(S.alpha);
+    k.eps = uniform(S.eps); k.ss = uniform(S.step_size); k.isb2 = uniform(S.inv_sqrt_bc2);
+    k.ibc1 = uniform(S.inv_bc1); k.lr = uniform(S.lr); k.inv_scale = uniform(S.inv_scale);
+    return k;
+}
+
+// [BNB] PR description / [MINI] AdamWMini full-v branch, per element:
+//   m <- b1 m + c1 g;  v <- b2 v + c2 g^2;  h = sqrt(v)/sqrt(bc2) + eps
+//   p <- p (1 - lr wd) - (lr/bc1) m / h          (decay from the old p)
+// AdEMAMix adds m2 <- b3 m2 + c3 g and uses lr (m/bc1 + alpha m2) / h.
+template <int PK, int GK, bool ADE, int N>
+__device__ __forceinline__ void adam_elems(const TensorDesc &T, int64_t e, const AdamK &k,
+                                           float decay) {
+    float p[N], g[N], m[N], v[N], m2[N];
+    load_p<PK, N>(T, e, p);
+    load_g<GK, N>(T.g, e, k.inv_scale, g);
+    ldf<N>(T.m, e, m);
+    ldf<N>(T.v, e, v);
+    if constexpr (ADE) ldf<N>(T.m2, e, m2);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        m[i] = k.b1 * m[i] + k.c1 * g[i];
+        v[i] = k.b2 * v[i] + k.c2 * (g[i] * g[i]);
+        const float h = sqrtf(v[i]) * k.isb2 + k.eps;
+        if constexpr (ADE) {
+            m2[i] = k.b3 * m2[i] + k.c3 * g[i];
+            p[i] = p[i] * decay - k.lr * ((m[i] * k.ibc1 + k.alpha * m2[i]) / h);
+        } else {
+            p[i] = p[i] * decay - k.ss * (m[i] / h);
+        }
+    }
+    store_p<PK, N>(T, e, p);
+    stf<N>(T.m, e, m);
+    stf<N>(T.v, e, v);
+    if constexpr (ADE) stf<N>(T.m2, e, m2);
+}
+
+template <int PK, int GK, bool ADE>
+__device__ __forceinline__ void adam_unit(const TensorDesc &T, int64_t start, int64_t len,
+                                          const AdamK &k, float decay) {
+    const bool vec = T.vec_ok && (start % 8 == 0);
+    for (int64_t rel = threadIdx.x * 8; rel < len; rel += kThreads * 8) {
+        const int64_t e = start + rel;
+        if (vec && rel + 8 <= len) {
+            adam_elems<PK, GK, ADE, 8>(T, e, k, decay);
+        } else {
+            const int64_t n = len - rel < 8 ? len - rel : 8;
+            for (int64_t j = 0; j < n; ++j) adam_elems<PK, GK, ADE, 1>(T, e + j, k, decay);
+        }
+    }
+}
+
+// Grid: one workgroup per unit unless the plan asked for a persistent grid
+// of grid_request workgroups (then never more than there are units).
+template <class K>
+int persistent_grid(K, const StepArgs &a) {
+    const int64_t units = a.nunits > 0 ? a.nunits : 1;
+    const int64_t g = a.grid_request > 0 && a.grid_request < units ? a.grid_request : units;
+    return (int)(g < INT32_MAX ? g : INT32_MAX);
+}
+
+#define LAUNCH_PERSISTENT(K, a, s)                                                     \
+    hipLaunchKernelGGL(K, dim3(persistent_grid(K, a)), dim3(kThreads), 0, s, a)
+
+}  // namespace
+}  // namespace optim

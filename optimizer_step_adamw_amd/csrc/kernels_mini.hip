@@ -1,0 +1,166 @@
+// kernels_mini.hip -- Adam-mini step kernels: per-unit block sums of g^2,
+// per-block finalize, elementwise update.
+#include "device_common.h"
+
+namespace optim {
+namespace {
+
+// ---------------------------------------------------------------- Adam-mini
+// [MINI] AdamWMini.step, q/k and "other" branches: one v per block of the
+// flattened gradient, updated with the block mean of g^2.  Three kernels:
+// per-unit partial sums of g^2 -> per-block finalize (fixed-order fp64 sum,
+// v update, step factor) -> elementwise m/p update.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+template <int GK>
+__global__ __launch_bounds__(kThreads) void mini_sumsq_kernel(StepArgs a) {
+    __shared__ Scalars S;
+    step_begin(a, S);
+    const StepCommit commit{a, S};
+    if (S.skip) return;
+    const float s = S.inv_scale;
+    __shared__ double red[kThreads / 64];
+    for_units(a, [&](int64_t u, const SpanDesc &sp, int64_t start, int64_t len) {
+        if (sp.block < 0) return;  // full-v tensor: no shared block
+        const TensorDesc &T = a.tensors[sp.tensor];
+        const bool vec = T.vec_ok && (start % 8 == 0);
+        float acc = 0.0f;
+        for (int64_t rel = threadIdx.x * 8; rel < len; rel += kThreads * 8) {
+            const int64_t e = start + rel;
+            if (vec && rel + 8 <= len) {
+                float g[8];
+                load_g<GK, 8>(T.g, e, s, g);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc += g[i] * g[i];
+            } else {
+                const int64_t n = len - rel < 8 ? len - rel : 8;
+                for (int64_t j = 0; j < n; ++j) {
+                    float g[1];
+                    load_g<GK, 1>(T.g, e + j, s, g);
+                    acc += g[0] * g[0];
+                }
+            }
+        }
+        acc = wave_sum(acc);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = (double)acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double t = 0.0;
+#pragma unroll
+            for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+            a.partials[u] = t;
+        }
+        __syncthreads();
+    });
+}
+
+__global__ __launch_bounds__(kThreads) void mini_finalize_kernel(StepArgs a) {
+    __shared__ Scalars S;
+    step_begin(a, S);
+    const StepCommit commit{a, S};
+    if (S.skip) return;
+    __shared__ double red[kThreads];
+    for (int b = blockIdx.x; b < a.nblocks; b += gridDim.x) {
+        const int si = a.blockspan[b];
+        const SpanDesc sp = a.spans[si];
+        const int64_t u0 = sp.unit_begin, u1 = a.spans[si + 1].unit_begin;
+        double acc = 0.0;
+        for (int64_t u = u0 + threadIdx.x; u < u1; u += kThreads) acc += a.partials[u];
+        red[threadIdx.x] = acc;
+        __syncthreads();
+        for (int st = kThreads / 2; st > 0; st >>= 1) {
+            if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) {
+            const TensorDesc &T = a.tensors[sp.tensor];
+            const int64_t j = sp.elem_begin / T.block_len;
+            const double mean = red[0] / (double)sp.len;
+            const double V = S.beta2_64 * (double)T.v[j] + S.c2_64 * mean;
+            T.v[j] = (float)V;
+            const double h = sqrt(V) * S.inv_sqrt_bc2_64 + S.eps64;
+            a.blockfac[b] = (float)(S.step_size64 / h);
+        }
+        __syncthreads();
+    }
+}
+
+template <int PK, int GK, int N>
+__device__ __forceinline__ void mini_elems(const TensorDesc &T, int64_t e, const AdamK &k,
+                                           float decay, float f) {
+    float p[N], g[N], m[N];
+    load_p<PK, N>(T, e, p);
+    load_g<GK, N>(T.g, e, k.inv_scale, g);
+    ldf<N>(T.m, e, m);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        m[i] = k.b1 * m[i] + k.c1 * g[i];
+        p[i] = p[i] * decay - f * m[i];
+    }
+    store_p<PK, N>(T, e, p);
+    stf<N>(T.m, e, m);
+}
+
+template <int PK, int GK>
+__global__ __launch_bounds__(kThreads) void mini_update_kernel(StepArgs a) {
+    __shared__ Scalars S;
+    step_begin(a, S);
+    const StepCommit commit{a, S};
+    if (S.skip) return;
+    const AdamK k = adam_consts(S);
+    for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
+        const TensorDesc &T = a.tensors[sp.tensor];
+        const float decay = uniform(S.decay[T.group]);
+        if (sp.block < 0) {
+            adam_unit<PK, GK, false>(T, start, len, k, decay);
+            return;
+        }
+        const float f = a.blockfac[sp.block];
+        const bool vec = T.vec_ok && (start % 8 == 0);
+        for (int64_t rel = threadIdx.x * 8; rel < len; rel += kThreads * 8) {
+            const int64_t e = start + rel;
+            if (vec && rel + 8 <= len) {
+                mini_elems<PK, GK, 8>(T, e, k, decay, f);
+            } else {
+                const int64_t n = len - rel < 8 ? len - rel : 8;
+                for (int64_t j = 0; j < n; ++j) mini_elems<PK, GK, 1>(T, e + j, k, decay, f);
+            }
+        }
+    });
+}
+
+}  // namespace
+
+hipError_t launch_adam_mini(const StepArgs &args, int pk, int gk, hipStream_t s) {
+    // block sums and finalize read the step's inputs; the update publishes it
+    StepArgs a = args;
+    a.commit = 0;
+    if (gk == G_F32)
+        LAUNCH_PERSISTENT((mini_sumsq_kernel<G_F32>), a, s);
+    else
+        LAUNCH_PERSISTENT((mini_sumsq_kernel<G_BF16>), a, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.nblocks > 0) {
+        const int fg = a.nblocks < 2048 ? a.nblocks : 2048;
+        hipLaunchKernelGGL(mini_finalize_kernel, dim3(fg), dim3(kThreads), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    a.commit = 1;
+    if (pk == P_F32 && gk == G_F32)
+        LAUNCH_PERSISTENT((mini_update_kernel<P_F32, G_F32>), a, s);
+    else if (pk == P_F32 && gk == G_BF16)
+        LAUNCH_PERSISTENT((mini_update_kernel<P_F32, G_BF16>), a, s);
+    else if (pk == P_BF16R && gk == G_F32)
+        LAUNCH_PERSISTENT((mini_update_kernel<P_BF16R, G_F32>), a, s);
+    else
+        LAUNCH_PERSISTENT((mini_update_kernel<P_BF16R, G_BF16>), a, s);
+    return hipGetLastError();
+}
+
+}  // namespace optim

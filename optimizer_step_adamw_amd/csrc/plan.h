@@ -8,11 +8,15 @@
 namespace optim {
 
 // Work decomposition: every tensor (Adam-mini: every shared-v block) is a
-// "span"; a span is cut into units of kTile consecutive elements (the last
-// one ragged).  Units are numbered globally; a persistent workgroup owns a
-// contiguous range of unit numbers.
-constexpr int kThreads = 256;     // workgroup size (4 wavefronts of 64)
-constexpr int64_t kTile = 4096;   // elements per unit
+// "span"; a span is cut into units of `tile` consecutive elements (the last
+// one ragged).  Units are numbered globally.  By default one workgroup runs
+// per unit, so the hardware dispatcher keeps the resident workgroups on one
+// narrow, advancing window of every array; a plan may instead ask for a
+// persistent grid whose workgroups walk the units grid-stride.
+constexpr int kThreads = 256;        // workgroup size (4 wavefronts of 64)
+constexpr int64_t kDefaultTile = 2048;
+constexpr int64_t kBlockwiseTile = 16384;
+constexpr int64_t kMinTile = 2048;   // one row: 256 lanes x 8 elements
 constexpr int kMaxGroups = 64;    // distinct weight-decay values per plan
 
 enum ParamKind { P_F32 = 0, P_BF16R = 1 };  // fp32, or bf16 + int16 remainder
@@ -79,11 +83,26 @@ struct Layout {
         blockspan, total;
 };
 
-// Codebook region: signed map for m then unsigned map for v, values then
-// thresholds, for 8-bit followed by 4-bit.
-constexpr int kCb8SignedVals = 0, kCb8SignedThr = 128, kCb8UnsVals = 256,
-              kCb8UnsThr = 512, kCb4SignedVals = 768, kCb4SignedThr = 776,
-              kCb4UnsVals = 784, kCb4UnsThr = 800, kCbFloats = 816;
+// Quantization maps.  A normalised magnitude a in [0, 1] maps to the largest
+// j with thr[j] <= a.  The search starts from a bucket table indexed by a's
+// exponent and top kLutMantBits mantissa bits over [2^-26, 2): lut[bucket]
+// is the index of the bucket's smallest value, and table construction
+// checks that no bucket holds more than one threshold, so one comparison
+// finishes the search.  Every threshold of every map is above 2^-26.
+constexpr int kLutMantBits = 8;
+constexpr int kLutBaseExp = 127 - 26;  // biased exponent of 2^-26
+constexpr int kLutBinades = 27;        // 2^-26 ... [1, 2)
+constexpr int kLutBuckets = kLutBinades << kLutMantBits;
+
+struct QuantMap {
+    float vals[256];       // sorted magnitudes (first 2^mb used)
+    float thr[256];        // thr[j] = fl32((vals[j-1] + vals[j]) / 2), thr[0] = 0
+    uint8_t lut[kLutBuckets];
+};
+
+struct Codebook {          // signed map for m, unsigned map for v
+    QuantMap m8, v8, m4, v4;
+};
 
 struct PrepArgs {
     const double *group_wd;
@@ -107,15 +126,16 @@ struct StepArgs {
     const SpanDesc *spans;    // nspans + 1 entries (sentinel at the end)
     int32_t nspans;
     int64_t nunits;
+    int64_t tile;             // elements per unit
     double *partials;         // Adam-mini: one per unit
     float *blockfac;          // Adam-mini: per block lr/bc1/h
     const int32_t *blockspan; // Adam-mini: span index of each block
     int32_t nblocks;
-    const float *codebook;
+    const Codebook *codebook;
     int32_t bits, block;
     float *found_inf;         // finite check output
     int32_t cus;              // compute units of the device
-    int32_t grid_request;     // persistent workgroups requested (0 = auto)
+    int32_t grid_request;     // persistent workgroups (0 = one per unit)
 };
 
 // Launchers (kernels.hip).  Return the hipError_t of the launch.  Step
@@ -126,6 +146,10 @@ hipError_t launch_ademamix(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_adam_mini(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_blockwise(const StepArgs &a, int gk, hipStream_t s);
 hipError_t launch_check_finite(const StepArgs &a, int gk, hipStream_t s);
+hipError_t launch_quantize(const Codebook *cb, int bits, int block, int is_signed, const float *x,
+                           int64_t n, uint8_t *codes, float *absmax, hipStream_t s);
+hipError_t launch_dequantize(const Codebook *cb, int bits, int block, int is_signed, const uint8_t *codes,
+                             const float *absmax, int64_t n, float *x, hipStream_t s);
 hipError_t launch_remainder_split(const float *x, uint16_t *b, int16_t *r, int64_t n,
                                   hipStream_t s);
 hipError_t launch_remainder_reconstruct(const uint16_t *b, const int16_t *r, float *x,

@@ -27,7 +27,7 @@ def header_functions():
 
 def test_exports_every_declared_function(L):
     declared = header_functions()
-    assert len(declared) == 13, declared
+    assert len(declared) == 15, declared
     assert sorted(osa.EXPORTED) == declared
     for name in declared:
         assert hasattr(L, name), name
@@ -122,14 +122,14 @@ def test_blockwise_validation(L):
     kw = dict(m=None, v=None, qm=[f(n)], qv=[f(n)], absmax_m=[f(64)], absmax_v=[f(64)])
     for bits, block in ((8, 256), (8, 64), (4, 128), (4, 512)):
         assert ws(fake_list([n], fake=f, **kw), osa.OPTIM_ALGO_BLOCKWISE,
-                  osa.optim_plan_opts(bits, block, 0)) > 0
+                  osa.optim_plan_opts(bits, block, 0, 0)) > 0
     for bits, block in ((8, 512), (4, 64), (6, 256), (8, 100)):
         expect_error(osa.OPTIM_EINVAL, lambda: ws(
-            fake_list([n], fake=f, **kw), osa.OPTIM_ALGO_BLOCKWISE, osa.optim_plan_opts(bits, block, 0)))
+            fake_list([n], fake=f, **kw), osa.OPTIM_ALGO_BLOCKWISE, osa.optim_plan_opts(bits, block, 0, 0)))
     expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, **kw), osa.OPTIM_ALGO_BLOCKWISE, None))
     # the codes of one tensor overlapping its own parameter
     expect_error(osa.OPTIM_EINVAL, lambda: ws(
-        fake_list([n], **kw), osa.OPTIM_ALGO_BLOCKWISE, osa.optim_plan_opts(8, 256, 0)))
+        fake_list([n], **kw), osa.OPTIM_ALGO_BLOCKWISE, osa.optim_plan_opts(8, 256, 0, 0)))
 
 
 def test_null_plan_is_rejected_without_device(L):
