@@ -313,6 +313,8 @@ def cpu_baseline(synth, target_s):
 KERNEL_SOURCES = {  # kernel -> sources its device code comes from
     "adamw_fp32": ("device_common.h", "kernels_adam.hip"),
     "ademamix_fp32": ("device_common.h", "kernels_adam.hip"),
+    "blockwise_8bit": ("device_common.h", "kernels_blockwise.hip"),
+    "blockwise_4bit": ("device_common.h", "kernels_blockwise.hip"),
 }
 
 

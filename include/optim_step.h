@@ -105,7 +105,7 @@ typedef struct optim_tensor_list {
  *  grid        0 (default): one workgroup per work unit; > 0: a persistent
  *              grid of that many workgroups walking the units grid-stride
  *  tile        elements per work unit, a power of two in [2048, 2^24];
- *              0 = 2048 (16384 for blockwise plans)                       */
+ *              0 = 2048 (Adam-mini 4096, blockwise 65536)                 */
 typedef struct optim_plan_opts {
     int32_t bits;
     int32_t block;

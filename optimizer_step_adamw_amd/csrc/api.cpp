@@ -73,6 +73,7 @@ bool build_map(int mb, QuantMap &q) {
     std::memset(&q, 0, sizeof q);
     dynamic_map(mb, q.vals, q.thr);
     const int count = 1 << mb;
+    for (int j = count; j < (int)(sizeof q.thr / sizeof q.thr[0]); ++j) q.thr[j] = INFINITY;
     const uint32_t shift = 23 - kLutMantBits;
     if (threshold_index(q.thr, count, bits_to_float(((uint32_t)kLutBaseExp << 23) - 1)) != 0) return false;
     for (int b = 0; b < kLutBuckets; ++b) {
@@ -129,8 +130,8 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
         if (!opts) return fail(OPTIM_EINVAL, "blockwise plans need opts (bits, block)");
         bits = opts->bits;
         block = opts->block;
-        // a block is L = block/E lanes of one wavefront (E = 4 codes per lane
-        // for 8-bit, 8 for 4-bit), L a power of two in [16, 64]
+        // a block is L = block/8 lanes of one wavefront (8 codes per lane), L a
+        // power of two in [8, 64]
         if (bits != 8 && bits != 4) return fail(OPTIM_EINVAL, "bits must be 8 or 4");
         const bool ok = bits == 8 ? (block == 64 || block == 128 || block == 256)
                                   : (block == 128 || block == 256 || block == 512);
@@ -140,10 +141,12 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     }
     if (opts && opts->grid < 0) return fail(OPTIM_EINVAL, "negative grid");
     // measured on MI355X: one 2048-element row per workgroup streams best for
-    // the elementwise steps; the blockwise step amortises its LDS tables and
-    // prologue over larger units
+    // AdamW / AdEMAMix, Adam-mini prefers 4096, and the blockwise step
+    // amortises its LDS tables and prologue over larger units
     const int64_t tile = (opts && opts->tile > 0) ? opts->tile
-                         : (algo == OPTIM_ALGO_BLOCKWISE ? kBlockwiseTile : kDefaultTile);
+                         : algo == OPTIM_ALGO_BLOCKWISE ? kBlockwiseTile
+                         : algo == OPTIM_ALGO_ADAM_MINI ? kAdamMiniTile
+                                                        : kDefaultTile;
     if (tile < kMinTile || tile > (1 << 24) || (tile & (tile - 1)))
         return fail(OPTIM_EINVAL, "tile must be a power of two in [2048, 2^24]");
     B.tile = tile;
@@ -446,6 +449,7 @@ StepArgs step_args(optim_plan *P) {
     a.block = P->block;
     a.cus = P->cus;
     a.grid_request = P->grid;
+    a.units_per_wg = 1;
     return a;
 }
 

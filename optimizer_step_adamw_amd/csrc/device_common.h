@@ -182,12 +182,13 @@ __device__ __forceinline__ void load_g(const void *g, int64_t e, float s, float 
 
 // ---------------------------------------------------------------- traversal
 // Calls body(u, span, first element, element count) for every unit u this
-// workgroup owns: u = b, b + G, b + 2G, ... (with the default grid of one
-// workgroup per unit, just u = b).  All arguments are uniform across the
-// workgroup.  A persistent grid walks grid-stride so its resident
-// workgroups sweep one window of each array at a time (measured faster on
-// MI355X than one contiguous range per workgroup, whose ~1500 separate
-// streams lose DRAM page locality).
+// workgroup owns.  All arguments are uniform across the workgroup.
+// Default grid: workgroup b owns units_per_wg consecutive units (usually
+// one), and the hardware dispatcher keeps the resident workgroups on one
+// narrow, advancing window of every array.  Persistent grid: workgroup b
+// takes units b, b + G, b + 2G, ..., so its resident workgroups also sweep
+// one window at a time (measured faster on MI355X than one contiguous range
+// per workgroup, whose ~1500 separate streams lose DRAM page locality).
 __device__ __forceinline__ int span_of(const StepArgs &a, int64_t u) {
     int lo = 0, hi = a.nspans;  // spans[nspans].unit_begin == nunits > u
     while (hi - lo > 1) {
@@ -199,11 +200,19 @@ __device__ __forceinline__ int span_of(const StepArgs &a, int64_t u) {
 
 template <class Body>
 __device__ __forceinline__ void for_units(const StepArgs &a, Body &&body) {
-    const int64_t G = gridDim.x;
-    int64_t u = blockIdx.x;
-    if (u >= a.nunits) return;
+    int64_t u, u1, stride;
+    if (a.grid_request > 0) {
+        u = blockIdx.x;
+        u1 = a.nunits;
+        stride = gridDim.x;
+    } else {
+        u = (int64_t)blockIdx.x * a.units_per_wg;
+        u1 = u + a.units_per_wg < a.nunits ? u + a.units_per_wg : a.nunits;
+        stride = 1;
+    }
+    if (u >= u1) return;
     int s = span_of(a, u);
-    for (; u < a.nunits; u += G) {
+    for (; u < u1; u += stride) {
         while (a.spans[s + 1].unit_begin <= u) ++s;
         const SpanDesc sp = a.spans[s];
         const int64_t off = (u - sp.unit_begin) * a.tile;
@@ -384,12 +393,17 @@ __device__ __forceinline__ void adam_unit(const TensorDesc &T, int64_t start, in
     }
 }
 
-// Grid: one workgroup per unit unless the plan asked for a persistent grid
-// of grid_request workgroups (then never more than there are units).
+// Grid: ceil(units / units_per_wg) workgroups, unless the plan asked for a
+// persistent grid of grid_request workgroups (never more than there are
+// units).  At least one workgroup: the commit must run for an empty plan.
 template <class K>
 int persistent_grid(K, const StepArgs &a) {
     const int64_t units = a.nunits > 0 ? a.nunits : 1;
-    const int64_t g = a.grid_request > 0 && a.grid_request < units ? a.grid_request : units;
+    int64_t g;
+    if (a.grid_request > 0)
+        g = a.grid_request < units ? a.grid_request : units;
+    else
+        g = (units + a.units_per_wg - 1) / a.units_per_wg;
     return (int)(g < INT32_MAX ? g : INT32_MAX);
 }
 

@@ -71,7 +71,10 @@ int flat_grid(int64_t n) {
 
 }  // namespace
 
-hipError_t launch_check_finite(const StepArgs &a, int gk, hipStream_t s) {
+hipError_t launch_check_finite(const StepArgs &args, int gk, hipStream_t s) {
+    // a read-only scan streams best with ~8192 elements per workgroup
+    StepArgs a = args;
+    a.units_per_wg = (int32_t)(a.tile >= kFiniteCheckElems ? 1 : kFiniteCheckElems / a.tile);
     if (gk == G_F32)
         LAUNCH_PERSISTENT((finite_kernel<G_F32>), a, s);
     else

@@ -15,7 +15,9 @@ namespace optim {
 // persistent grid whose workgroups walk the units grid-stride.
 constexpr int kThreads = 256;        // workgroup size (4 wavefronts of 64)
 constexpr int64_t kDefaultTile = 2048;
-constexpr int64_t kBlockwiseTile = 16384;
+constexpr int64_t kAdamMiniTile = 4096;
+constexpr int64_t kBlockwiseTile = 65536;
+constexpr int64_t kFiniteCheckElems = 8192;  // read-only scan: elements per workgroup
 constexpr int64_t kMinTile = 2048;   // one row: 256 lanes x 8 elements
 constexpr int kMaxGroups = 64;    // distinct weight-decay values per plan
 
@@ -96,7 +98,8 @@ constexpr int kLutBuckets = kLutBinades << kLutMantBits;
 
 struct QuantMap {
     float vals[256];       // sorted magnitudes (first 2^mb used)
-    float thr[256];        // thr[j] = fl32((vals[j-1] + vals[j]) / 2), thr[0] = 0
+    float thr[260];        // thr[j] = fl32((vals[j-1] + vals[j]) / 2), thr[0] = 0,
+                           // thr[2^mb...] = +inf (ends the search)
     uint8_t lut[kLutBuckets];
 };
 
@@ -135,7 +138,9 @@ struct StepArgs {
     int32_t bits, block;
     float *found_inf;         // finite check output
     int32_t cus;              // compute units of the device
-    int32_t grid_request;     // persistent workgroups (0 = one per unit)
+    int32_t grid_request;     // persistent workgroups (0 = see units_per_wg)
+    int32_t units_per_wg;     // without a persistent grid: consecutive units
+                              // per workgroup (set by the launcher)
 };
 
 // Launchers (kernels.hip).  Return the hipError_t of the launch.  Step
