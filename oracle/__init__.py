@@ -43,39 +43,75 @@ _i32 = ctypes.c_int
 _p = ctypes.c_void_p
 
 
+_SIGS = {
+    "oracle_adamw_step": [_i64, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64],
+    "mutant_adamw_decay_after_step": [_i64, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64],
+    "oracle_ademamix_step": [_i64, _p, _p, _p, _p, _p, _d, _d, _d, _d, _d, _d, _d, _i64],
+    "oracle_adam_mini_step": [_i64, _i64, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64],
+    "oracle_any_nonfinite": [_i64, _p],
+    "oracle_cosine_lr": [_i64, _i64, _d, _d],
+    "oracle_remainder_split": [_i64, _p, _p, _p],
+    "oracle_remainder_reconstruct": [_i64, _p, _p, _p],
+    "oracle_remainder_exhaustive": [],
+    "oracle_dynamic_map": [_i32, _p],
+    "oracle_thresholds": [_i32, _p, _p],
+    "oracle_quantize": [_i64, _i64, _i32, _i32, _p, _p, _p, _p],
+    "oracle_dequantize": [_i64, _i64, _i32, _i32, _p, _p, _p, _p],
+    "oracle_pack_nibbles": [_i64, _p, _p],
+    "oracle_unpack_nibbles": [_i64, _p, _p],
+    "oracle_blockwise_step": [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p,
+                              _d, _d, _d, _d, _d, _i64, _p, _p],
+}
+_RESTYPES = {"oracle_any_nonfinite": _i32, "oracle_cosine_lr": ctypes.c_float,
+             "oracle_remainder_exhaustive": _i64, "oracle_dynamic_map": _i32}
+
+
+def load(path: str) -> ctypes.CDLL:
+    """A configured handle on a build of oracle.c at `path`."""
+    L = ctypes.CDLL(path)
+    for name, args in _SIGS.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = _RESTYPES.get(name, None)
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             build(force=False)
-        L = ctypes.CDLL(_LIB_PATH)
-        sigs = {
-            "oracle_adamw_step": [_i64, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64],
-            "mutant_adamw_decay_after_step": [_i64, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64],
-            "oracle_ademamix_step": [_i64, _p, _p, _p, _p, _p, _d, _d, _d, _d, _d, _d, _d, _i64],
-            "oracle_adam_mini_step": [_i64, _i64, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64],
-            "oracle_any_nonfinite": [_i64, _p],
-            "oracle_cosine_lr": [_i64, _i64, _d, _d],
-            "oracle_remainder_split": [_i64, _p, _p, _p],
-            "oracle_remainder_reconstruct": [_i64, _p, _p, _p],
-            "oracle_remainder_exhaustive": [],
-            "oracle_dynamic_map": [_i32, _p],
-            "oracle_thresholds": [_i32, _p, _p],
-            "oracle_quantize": [_i64, _i64, _i32, _i32, _p, _p, _p, _p],
-            "oracle_dequantize": [_i64, _i64, _i32, _i32, _p, _p, _p, _p],
-            "oracle_pack_nibbles": [_i64, _p, _p],
-            "oracle_unpack_nibbles": [_i64, _p, _p],
-            "oracle_blockwise_step": [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p,
-                                      _d, _d, _d, _d, _d, _i64, _p, _p],
-        }
-        restypes = {"oracle_any_nonfinite": _i32, "oracle_cosine_lr": ctypes.c_float,
-                    "oracle_remainder_exhaustive": _i64, "oracle_dynamic_map": _i32}
-        for name, args in sigs.items():
-            fn = getattr(L, name)
-            fn.argtypes = args
-            fn.restype = restypes.get(name, None)
-        _lib = L
+        _lib = load(_LIB_PATH)
     return _lib
+
+
+class use_build:
+    """Context manager: route every oracle call to another build of
+    oracle.c (the mutation test plants mistakes in copies of it)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = lib()
+        _lib = load(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def compile_source(src: str, out_path: str) -> None:
+    """gcc a variant of the oracle source with the flags build() uses."""
+    c_path = out_path[:-3] + ".c"
+    with open(c_path, "w") as f:
+        f.write(src)
+    subprocess.check_call([
+        "gcc", "-O2", "-std=c11", "-D_DEFAULT_SOURCE", "-fPIC", "-shared",
+        "-ffp-contract=off", "-fno-fast-math", "-w", "-o", out_path, c_path, "-lm"])
 
 
 def _ptr(a: np.ndarray):
