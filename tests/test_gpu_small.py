@@ -424,3 +424,51 @@ def test_remainder_exhaustive_against_oracle():
         assert np.array_equal(to_np_u16(b), ob), c
         assert np.array_equal(r.cpu().numpy(), orr), c
         say(f"remainder chunk {c} ok")
+
+
+def test_step_replays_in_a_hip_graph():
+    """Every step-varying value lives on the device and no memset is
+    recorded, so a whole AMP step (finite check + bf16/remainder AdamW +
+    cosine lr) can be captured once and replayed; each replay, with eager
+    work in between, equals the same step run eagerly, bit for bit."""
+    sizes = [5000, 4097, 33]
+    p0 = _p0(sizes, 22)
+    eager = AdamState(_to_dev(p0), grad_bf16=True, param_bf16=True)
+    graph = AdamState(_to_dev(p0), grad_bf16=True, param_bf16=True)
+    pe = osa.Plan(eager.tensor_list([0.1, 0.0, 0.1]), osa.OPTIM_ALGO_ADAMW)
+    pg = osa.Plan(graph.tensor_list([0.1, 0.0, 0.1]), osa.OPTIM_ALGO_ADAMW)
+    se, sg = DevScalars(0.0, inv_scale=2.0 ** -16), DevScalars(0.0, inv_scale=2.0 ** -16)
+    for plan, sc in ((pe, se), (pg, sg)):
+        osa.optim_plan_set_schedule(plan.handle, osa.OPTIM_SCHED_COSINE, 3e-4, 0.0, 10, sc.iter)
+    hp = osa.optim_adamw_hp(0.9, 0.95, 1e-8)
+
+    def step(plan, sc):
+        sc.found_inf.zero_()
+        osa.optim_check_finite(plan.handle, sc.found_inf)
+        osa.optim_step_adamw(plan.handle, hp, sc.lr, sc.inv_scale, sc.found_inf, sc.step)
+
+    torch.cuda.synchronize()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cs):
+        with torch.cuda.graph(g, stream=cs):
+            step(pg, sg)
+    torch.cuda.current_stream().wait_stream(cs)
+    torch.cuda.synchronize()
+    # capture recorded the work without running it: nothing has moved yet
+    assert int(sg.step.item()) == 0 and int(sg.iter.item()) == 0
+    for t in range(6):
+        gs = _grads(sizes, 22, t, 1e-3)
+        _load_grads(eager, gs, scale=65536.0)
+        _load_grads(graph, gs, scale=65536.0)
+        if t == 3:  # one skipped step: the replay must skip too
+            for st in (eager, graph):
+                st.g[1][17] = torch.tensor(float("inf")).to(torch.bfloat16).view(torch.int16)
+        step(pe, se)
+        g.replay()
+        torch.cuda.synchronize()
+        assert all_equal(eager.buffers(), graph.buffers()), t
+        for a, b in ((se.step, sg.step), (se.iter, sg.iter), (se.lr, sg.lr), (se.found_inf, sg.found_inf)):
+            assert torch.equal(a, b), t
+    assert int(sg.step.item()) == 5 and int(sg.iter.item()) == 6
