@@ -104,8 +104,9 @@ typedef struct optim_tensor_list {
  *              4-bit: block 128, 256 or 512)
  *  grid        0 (default): one workgroup per work unit; > 0: a persistent
  *              grid of that many workgroups walking the units grid-stride
- *  tile        elements per work unit, a power of two in [2048, 2^24];
- *              0 = 2048 (Adam-mini 4096, blockwise 65536)                 */
+ *  tile        elements per work unit, a power of two in [1024, 2^24]
+ *              (blockwise: at least 2048); 0 = 2048 (Adam-mini 4096,
+ *              blockwise 65536)                                            */
 typedef struct optim_plan_opts {
     int32_t bits;
     int32_t block;

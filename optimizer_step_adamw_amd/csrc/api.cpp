@@ -140,15 +140,19 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
                                                 : "4-bit block must be 128, 256 or 512");
     }
     if (opts && opts->grid < 0) return fail(OPTIM_EINVAL, "negative grid");
-    // measured on MI355X: one 2048-element row per workgroup streams best for
-    // AdamW / AdEMAMix, Adam-mini prefers 4096, and the blockwise step
-    // amortises its LDS tables and prologue over larger units
+    if (opts && opts->tile < 0) return fail(OPTIM_EINVAL, "negative tile");
+    // measured on MI355X: 2048 elements per workgroup (two groups of 4 per
+    // lane, loaded at once) stream best for AdamW / AdEMAMix, Adam-mini
+    // prefers 4096, and the blockwise step amortises its LDS tables and
+    // prologue over larger units
     const int64_t tile = (opts && opts->tile > 0) ? opts->tile
                          : algo == OPTIM_ALGO_BLOCKWISE ? kBlockwiseTile
                          : algo == OPTIM_ALGO_ADAM_MINI ? kAdamMiniTile
                                                         : kDefaultTile;
     if (tile < kMinTile || tile > (1 << 24) || (tile & (tile - 1)))
-        return fail(OPTIM_EINVAL, "tile must be a power of two in [2048, 2^24]");
+        return fail(OPTIM_EINVAL, "tile must be a power of two in [1024, 2^24]");
+    if (algo == OPTIM_ALGO_BLOCKWISE && tile < kMinBlockwiseTile)
+        return fail(OPTIM_EINVAL, "blockwise tile must be at least 2048");
     B.tile = tile;
     if (n > 0 && (!list->numel || !list->param || !list->grad || !list->weight_decay))
         return fail(OPTIM_EINVAL, "numel, param, grad and weight_decay arrays are required");

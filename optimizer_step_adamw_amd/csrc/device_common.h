@@ -5,10 +5,11 @@
 //
 // The step is elementwise and HBM-bound (a few flops per byte), so there is
 // no matrix-core work.  A step kernel processes work units (`tile`
-// consecutive elements of one span) with 128-bit loads and stores, 8
-// consecutive elements per lane; by default one workgroup per unit.  Every
-// workgroup derives the step's scalars in its prologue and the last one to
-// finish publishes the new step counter.
+// consecutive elements of one span) with non-temporal 128-bit (fp32) or
+// 64-bit (16-bit) loads and stores, each instruction of a wave covering one
+// contiguous run; by default one workgroup per unit.  Every workgroup
+// derives the step's scalars in its prologue and the last one to finish
+// publishes the new step counter.
 //
 // Sources (web pages, by title and section):
 //  [BNB]  "Fix decoupled weight decay ordering in the CUDA Adam/AdEMAMix
@@ -56,86 +57,113 @@ __device__ __forceinline__ void rem_split(float x, uint32_t &b, uint32_t &r) {
 // ---------------------------------------------------------------- loads
 // Every tensor lives in HBM: accesses go through global-address-space
 // pointers so they compile to global_load/store (not flat) instructions.
-// N = 8: two 128-bit accesses (fp32) or one (16-bit); N = 1: one element.
+//
+// Two register layouts for a lane's N elements:
+//  kStrided (step kernels): N = 4V elements in V groups of 4 consecutive
+//    elements, group j at e + j*kSub, with lane t's e = unit start + 4t.
+//    One instruction of a wave then covers one contiguous 1 KiB (fp32) or
+//    512 B (16-bit) run, and the accesses are non-temporal: streamed data is
+//    touched once per step, and on MI355X non-temporal loads plus stores of
+//    whole contiguous runs sustain ~13% more bandwidth on the AdamW access
+//    pattern than ordinary ones (measured 5.99 vs 5.29 TB/s for 4 reads and
+//    3 writes per element), while non-temporal stores of half-filled lines
+//    (8 adjacent fp32 per lane) lose write combining and fall far below.
+//  kRun (blockwise quantizer rows): N consecutive elements from e, ordinary
+//    loads and stores; the per-block DPP reductions want each lane's
+//    elements adjacent.
+// N = 1 is one element, ordinary access, in either layout.
 #define GMEM __attribute__((address_space(1)))
 typedef float __attribute__((ext_vector_type(4))) f32x4;
 typedef uint32_t __attribute__((ext_vector_type(4))) u32x4;
 typedef uint32_t __attribute__((ext_vector_type(2))) u32x2;
+
+constexpr int kVec = 4;                             // elements per lane per group
+constexpr int64_t kSub = (int64_t)kVec * kThreads;  // elements per workgroup per group
+enum Layout { kStrided = 0, kRun = 1 };
+// groups of 4 elements per lane the AdamW / AdEMAMix / Adam-mini update
+// loads before computing (one 1 KiB run per array per wave and group)
+constexpr int kAdamGroups = 2;
 
 template <class T>
 __device__ __forceinline__ GMEM T *gp(T *p) { return (GMEM T *)p; }
 template <class T>
 __device__ __forceinline__ const GMEM T *gp(const T *p) { return (const GMEM T *)p; }
 
-template <class V>
+template <int LAY, class V>
 __device__ __forceinline__ V vload(const GMEM V *q) {
-    return *q;
+    if constexpr (LAY == kStrided) return __builtin_nontemporal_load(q);
+    else return *q;
 }
-template <class V>
+template <int LAY, class V>
 __device__ __forceinline__ void vstore(GMEM V *q, V x) {
-    *q = x;
+    if constexpr (LAY == kStrided) __builtin_nontemporal_store(x, q);
+    else *q = x;
+}
+// element offset of group j of a lane's elements
+template <int LAY>
+__device__ __forceinline__ constexpr int64_t group_off(int j) {
+    return LAY == kStrided ? j * kSub : (int64_t)j * kVec;
 }
 
-template <int N>
+template <int N, int LAY = kStrided>
 __device__ __forceinline__ void ldf(const float *a, int64_t e, float (&x)[N]) {
-    if constexpr (N == 8) {
-        const GMEM f32x4 *q = (const GMEM f32x4 *)gp(a + e);
-        const f32x4 u = vload(q), w = vload(q + 1);
-        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-        x[4] = w.x; x[5] = w.y; x[6] = w.z; x[7] = w.w;
-    } else if constexpr (N == 4) {
-        const f32x4 u = *(const GMEM f32x4 *)gp(a + e);
-        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+    if constexpr (N == 1) {
+        x[0] = gp(a)[e];
     } else {
-        const GMEM float *q = gp(a);
+        static_assert(N % kVec == 0, "groups of 4");
 #pragma unroll
-        for (int k = 0; k < N; ++k) x[k] = q[e + k];
+        for (int j = 0; j < N / kVec; ++j) {
+            const f32x4 u = vload<LAY>((const GMEM f32x4 *)gp(a + e + group_off<LAY>(j)));
+            x[4 * j] = u.x; x[4 * j + 1] = u.y; x[4 * j + 2] = u.z; x[4 * j + 3] = u.w;
+        }
     }
 }
 
-template <int N>
+template <int N, int LAY = kStrided>
 __device__ __forceinline__ void stf(float *a, int64_t e, const float (&x)[N]) {
-    if constexpr (N == 8) {
-        GMEM f32x4 *q = (GMEM f32x4 *)gp(a + e);
-        vstore(q, f32x4{x[0], x[1], x[2], x[3]});
-        vstore(q + 1, f32x4{x[4], x[5], x[6], x[7]});
-    } else if constexpr (N == 4) {
-        *(GMEM f32x4 *)gp(a + e) = f32x4{x[0], x[1], x[2], x[3]};
+    if constexpr (N == 1) {
+        gp(a)[e] = x[0];
     } else {
-        GMEM float *q = gp(a);
+        static_assert(N % kVec == 0, "groups of 4");
 #pragma unroll
-        for (int k = 0; k < N; ++k) q[e + k] = x[k];
+        for (int j = 0; j < N / kVec; ++j)
+            vstore<LAY>((GMEM f32x4 *)gp(a + e + group_off<LAY>(j)),
+                        f32x4{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]});
     }
 }
 
-template <int N>
+// 16-bit arrays (bf16 params and grads, int16 remainders): values are
+// returned zero-extended in 32-bit registers.
+template <int N, int LAY = kStrided>
 __device__ __forceinline__ void ldh(const uint16_t *a, int64_t e, uint32_t (&x)[N]) {
-    if constexpr (N == 8) {
-        const u32x4 u = vload((const GMEM u32x4 *)gp(a + e));
+    if constexpr (N == 1) {
+        x[0] = gp(a)[e];
+    } else if constexpr (LAY == kRun && N == 8) {
+        const u32x4 u = vload<LAY>((const GMEM u32x4 *)gp(a + e));
         x[0] = u.x & 0xFFFFu; x[1] = u.x >> 16; x[2] = u.y & 0xFFFFu; x[3] = u.y >> 16;
         x[4] = u.z & 0xFFFFu; x[5] = u.z >> 16; x[6] = u.w & 0xFFFFu; x[7] = u.w >> 16;
-    } else if constexpr (N == 4) {
-        const u32x2 u = *(const GMEM u32x2 *)gp(a + e);
-        x[0] = u.x & 0xFFFFu; x[1] = u.x >> 16; x[2] = u.y & 0xFFFFu; x[3] = u.y >> 16;
     } else {
-        const GMEM uint16_t *q = gp(a);
+        static_assert(N % kVec == 0, "groups of 4");
 #pragma unroll
-        for (int k = 0; k < N; ++k) x[k] = q[e + k];
+        for (int j = 0; j < N / kVec; ++j) {
+            const u32x2 u = vload<LAY>((const GMEM u32x2 *)gp(a + e + group_off<LAY>(j)));
+            x[4 * j] = u.x & 0xFFFFu; x[4 * j + 1] = u.x >> 16;
+            x[4 * j + 2] = u.y & 0xFFFFu; x[4 * j + 3] = u.y >> 16;
+        }
     }
 }
 
-template <int N>
+template <int N, int LAY = kStrided>
 __device__ __forceinline__ void sth(uint16_t *a, int64_t e, const uint32_t (&x)[N]) {
-    if constexpr (N == 8) {
-        vstore((GMEM u32x4 *)gp(a + e),
-               u32x4{(x[0] & 0xFFFFu) | (x[1] << 16), (x[2] & 0xFFFFu) | (x[3] << 16),
-                     (x[4] & 0xFFFFu) | (x[5] << 16), (x[6] & 0xFFFFu) | (x[7] << 16)});
-    } else if constexpr (N == 4) {
-        *(GMEM u32x2 *)gp(a + e) = u32x2{(x[0] & 0xFFFFu) | (x[1] << 16), (x[2] & 0xFFFFu) | (x[3] << 16)};
+    if constexpr (N == 1) {
+        gp(a)[e] = (uint16_t)x[0];
     } else {
-        GMEM uint16_t *q = gp(a);
+        static_assert(N % kVec == 0, "groups of 4");
 #pragma unroll
-        for (int k = 0; k < N; ++k) q[e + k] = (uint16_t)x[k];
+        for (int j = 0; j < N / kVec; ++j)
+            vstore<LAY>((GMEM u32x2 *)gp(a + e + group_off<LAY>(j)),
+                        u32x2{(x[4 * j] & 0xFFFFu) | (x[4 * j + 1] << 16),
+                              (x[4 * j + 2] & 0xFFFFu) | (x[4 * j + 3] << 16)});
     }
 }
 
@@ -166,13 +194,13 @@ __device__ __forceinline__ void store_p(const TensorDesc &T, int64_t e, const fl
 }
 
 // Gradient load with the AMP unscale applied exactly once ([LTN] analysis).
-template <int GK, int N>
+template <int GK, int N, int LAY = kStrided>
 __device__ __forceinline__ void load_g(const void *g, int64_t e, float s, float (&x)[N]) {
     if constexpr (GK == G_F32) {
-        ldf<N>(static_cast<const float *>(g), e, x);
+        ldf<N, LAY>(static_cast<const float *>(g), e, x);
     } else {
         uint32_t b[N];
-        ldh<N>(static_cast<const uint16_t *>(g), e, b);
+        ldh<N, LAY>(static_cast<const uint16_t *>(g), e, b);
 #pragma unroll
         for (int k = 0; k < N; ++k) x[k] = bf16_to_f32(b[k]);
     }
@@ -218,6 +246,30 @@ __device__ __forceinline__ void for_units(const StepArgs &a, Body &&body) {
         const int64_t off = (u - sp.unit_begin) * a.tile;
         const int64_t len = sp.len - off < a.tile ? sp.len - off : a.tile;
         body(u, sp, sp.elem_begin + off, len);
+    }
+}
+
+// Visits this lane's elements of the unit [start, start + len) in the
+// kStrided layout: lane t owns the groups of 4 at start + 4t + q*kSub.
+// body(Int<N>{}, e) handles N elements from e; full groups go G at a time
+// (all their loads issue before any use), then one at a time, and a ragged
+// end (or a unit whose pointers are not 16-byte aligned) element by element.
+template <int N>
+struct Int {
+    static constexpr int value = N;
+};
+
+template <int G, class Body>
+__device__ __forceinline__ void lane_walk(int64_t start, int64_t len, bool vec_ok, Body &&body) {
+    int64_t rel = threadIdx.x * kVec;
+    if (vec_ok && start % kVec == 0) {
+        if constexpr (G > 1)
+            for (; rel + (G - 1) * kSub + kVec <= len; rel += G * kSub) body(Int<kVec * G>{}, start + rel);
+        for (; rel + kVec <= len; rel += kSub) body(Int<kVec>{}, start + rel);
+    }
+    for (; rel < len; rel += kSub) {
+        const int64_t n = len - rel < kVec ? len - rel : kVec;
+        for (int64_t j = 0; j < n; ++j) body(Int<1>{}, start + rel + j);
     }
 }
 
@@ -381,16 +433,9 @@ __device__ __forceinline__ void adam_elems(const TensorDesc &T, int64_t e, const
 template <int PK, int GK, bool ADE>
 __device__ __forceinline__ void adam_unit(const TensorDesc &T, int64_t start, int64_t len,
                                           const AdamK &k, float decay) {
-    const bool vec = T.vec_ok && (start % 8 == 0);
-    for (int64_t rel = threadIdx.x * 8; rel < len; rel += kThreads * 8) {
-        const int64_t e = start + rel;
-        if (vec && rel + 8 <= len) {
-            adam_elems<PK, GK, ADE, 8>(T, e, k, decay);
-        } else {
-            const int64_t n = len - rel < 8 ? len - rel : 8;
-            for (int64_t j = 0; j < n; ++j) adam_elems<PK, GK, ADE, 1>(T, e + j, k, decay);
-        }
-    }
+    lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+        adam_elems<PK, GK, ADE, decltype(n)::value>(T, e, k, decay);
+    });
 }
 
 // Grid: ceil(units / units_per_wg) workgroups, unless the plan asked for a

@@ -166,8 +166,8 @@ __device__ __forceinline__ void blockwise_row(const BlockCtx &c, const AdamK &k,
         av = gp(T.av)[blk];
     }
     if (FULL) {
-        ldf<kQE>(P, e, p);
-        load_g<GK, kQE>(T.g, e, k.inv_scale, g);
+        ldf<kQE, kRun>(P, e, p);
+        load_g<GK, kQE, kRun>(T.g, e, k.inv_scale, g);
         cm = load_codes_full<BITS>(T.qm, e);
         cv = load_codes_full<BITS>(T.qv, e);
     } else {
@@ -204,7 +204,7 @@ __device__ __forceinline__ void blockwise_row(const BlockCtx &c, const AdamK &k,
     const uint64_t om = quantize_lane<BITS, true>(mn, c.L, Mm, am2);
     const uint64_t ov = quantize_lane<BITS, false>(vn, c.L, Mv, av2);
     if (FULL) {
-        stf<kQE>(P, e, p);
+        stf<kQE, kRun>(P, e, p);
         store_codes_full<BITS>(T.qm, e, om);
         store_codes_full<BITS>(T.qv, e, ov);
     } else if (nv > 0) {
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const Codebook *cb, 
         const bool full = vec && nv == kQE;
         float v[kQE];
         if (full) {
-            ldf<kQE>(x, e, v);
+            ldf<kQE, kRun>(x, e, v);
         } else {
 #pragma unroll
             for (int j = 0; j < kQE; ++j) {
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(const Codebook *cb
         const uint64_t c = full ? load_codes_full<BITS>(codes, e) : load_codes_part<BITS>(codes, e, nv);
         dequantize_lane<BITS, SIGNED>(c, gp(absmax)[e / block], M, v);
         if (full) {
-            stf<kQE>(x, e, v);
+            stf<kQE, kRun>(x, e, v);
         } else {
             for (int j = 0; j < nv; ++j) {
                 const float vj[1] = {v[j]};

@@ -27,24 +27,14 @@ __global__ __launch_bounds__(kThreads) void mini_sumsq_kernel(StepArgs a) {
     for_units(a, [&](int64_t u, const SpanDesc &sp, int64_t start, int64_t len) {
         if (sp.block < 0) return;  // full-v tensor: no shared block
         const TensorDesc &T = a.tensors[sp.tensor];
-        const bool vec = T.vec_ok && (start % 8 == 0);
         float acc = 0.0f;
-        for (int64_t rel = threadIdx.x * 8; rel < len; rel += kThreads * 8) {
-            const int64_t e = start + rel;
-            if (vec && rel + 8 <= len) {
-                float g[8];
-                load_g<GK, 8>(T.g, e, s, g);
+        lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+            constexpr int N = decltype(n)::value;
+            float g[N];
+            load_g<GK, N>(T.g, e, s, g);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc += g[i] * g[i];
-            } else {
-                const int64_t n = len - rel < 8 ? len - rel : 8;
-                for (int64_t j = 0; j < n; ++j) {
-                    float g[1];
-                    load_g<GK, 1>(T.g, e + j, s, g);
-                    acc += g[0] * g[0];
-                }
-            }
-        }
+            for (int i = 0; i < N; ++i) acc += g[i] * g[i];
+        });
         acc = wave_sum(acc);
         if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = (double)acc;
         __syncthreads();
@@ -120,16 +110,9 @@ __global__ __launch_bounds__(kThreads) void mini_update_kernel(StepArgs a) {
             return;
         }
         const float f = a.blockfac[sp.block];
-        const bool vec = T.vec_ok && (start % 8 == 0);
-        for (int64_t rel = threadIdx.x * 8; rel < len; rel += kThreads * 8) {
-            const int64_t e = start + rel;
-            if (vec && rel + 8 <= len) {
-                mini_elems<PK, GK, 8>(T, e, k, decay, f);
-            } else {
-                const int64_t n = len - rel < 8 ? len - rel : 8;
-                for (int64_t j = 0; j < n; ++j) mini_elems<PK, GK, 1>(T, e + j, k, decay, f);
-            }
-        }
+        lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+            mini_elems<PK, GK, decltype(n)::value>(T, e, k, decay, f);
+        });
     });
 }
 

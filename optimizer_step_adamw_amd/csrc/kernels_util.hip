@@ -7,41 +7,48 @@ namespace {
 
 // ---------------------------------------------------------------- finite check
 // [LTN] analysis: found_inf marks a NaN or +-Inf anywhere in the gradients.
+// A read-only scan: each workgroup takes kFiniteCheckElems elements (several
+// consecutive units, merged into one walk where they are contiguous).
+// Measured on MI355X: bf16 gradients stream best with 8 groups of 4 per lane
+// in flight (7.4 TB/s), fp32 with one group at a time (7.0 TB/s).
+template <int GK>
+__device__ __forceinline__ bool any_nonfinite(const TensorDesc &T, int64_t start, int64_t len) {
+    constexpr int G = GK == G_F32 ? 1 : 8;
+    bool bad = false;
+    lane_walk<G>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+        constexpr int N = decltype(n)::value;
+        if constexpr (GK == G_F32) {
+            float x[N];
+            ldf<N>(static_cast<const float *>(T.g), e, x);
+#pragma unroll
+            for (int i = 0; i < N; ++i) bad |= (__float_as_uint(x[i]) & 0x7F800000u) == 0x7F800000u;
+        } else {
+            uint32_t w[N];
+            ldh<N>(static_cast<const uint16_t *>(T.g), e, w);
+#pragma unroll
+            for (int i = 0; i < N; ++i) bad |= (w[i] & 0x7F80u) == 0x7F80u;
+        }
+    });
+    return bad;
+}
+
 template <int GK>
 __global__ __launch_bounds__(kThreads) void finite_kernel(StepArgs a) {
-    for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
-        const TensorDesc &T = a.tensors[sp.tensor];
-        const bool vec = T.vec_ok && (start % 8 == 0);
-        bool bad = false;
-        for (int64_t rel = threadIdx.x * 8; rel < len; rel += kThreads * 8) {
-            const int64_t e = start + rel;
-            if constexpr (GK == G_F32) {
-                const uint32_t *g = static_cast<const uint32_t *>(T.g);
-                if (vec && rel + 8 <= len) {
-                    const uint4 *q = reinterpret_cast<const uint4 *>(g + e);
-                    const uint4 x = q[0], y = q[1];
-                    const uint32_t w[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) bad |= (w[i] & 0x7F800000u) == 0x7F800000u;
-                } else {
-                    const int64_t n = len - rel < 8 ? len - rel : 8;
-                    for (int64_t j = 0; j < n; ++j) bad |= (g[e + j] & 0x7F800000u) == 0x7F800000u;
-                }
-            } else {
-                const uint16_t *g = static_cast<const uint16_t *>(T.g);
-                if (vec && rel + 8 <= len) {
-                    uint32_t w[8];
-                    ldh<8>(g, e, w);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) bad |= (w[i] & 0x7F80u) == 0x7F80u;
-                } else {
-                    const int64_t n = len - rel < 8 ? len - rel : 8;
-                    for (int64_t j = 0; j < n; ++j) bad |= (g[e + j] & 0x7F80u) == 0x7F80u;
-                }
-            }
+    bool bad = false;
+    int tensor = -1;
+    int64_t start = 0, len = 0;
+    for_units(a, [&](int64_t, const SpanDesc &sp, int64_t s, int64_t l) {
+        if (sp.tensor == tensor && s == start + len) {
+            len += l;
+            return;
         }
-        if (bad) *a.found_inf = 1.0f;
+        if (len > 0) bad |= any_nonfinite<GK>(a.tensors[tensor], start, len);
+        tensor = sp.tensor;
+        start = s;
+        len = l;
     });
+    if (len > 0) bad |= any_nonfinite<GK>(a.tensors[tensor], start, len);
+    if (bad) *a.found_inf = 1.0f;
 }
 
 // ---------------------------------------------------------------- remainder utils

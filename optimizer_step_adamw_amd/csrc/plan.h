@@ -18,7 +18,8 @@ constexpr int64_t kDefaultTile = 2048;
 constexpr int64_t kAdamMiniTile = 4096;
 constexpr int64_t kBlockwiseTile = 65536;
 constexpr int64_t kFiniteCheckElems = 8192;  // read-only scan: elements per workgroup
-constexpr int64_t kMinTile = 2048;   // one row: 256 lanes x 8 elements
+constexpr int64_t kMinTile = 1024;   // one group of 4 elements per lane
+constexpr int64_t kMinBlockwiseTile = 2048;  // one quantizer row: 256 lanes x 8 elements
 constexpr int kMaxGroups = 64;    // distinct weight-decay values per plan
 
 enum ParamKind { P_F32 = 0, P_BF16R = 1 };  // fp32, or bf16 + int16 remainder

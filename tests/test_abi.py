@@ -132,6 +132,22 @@ def test_blockwise_validation(L):
         fake_list([n], **kw), osa.OPTIM_ALGO_BLOCKWISE, osa.optim_plan_opts(8, 256, 0, 0)))
 
 
+def test_tile_bounds(L):
+    """Work units are a power of two of at least one group of 4 elements per
+    lane (1024); blockwise rows need 2048."""
+    f = Fake()
+    for tile in (1024, 2048, 1 << 24):
+        assert ws(fake_list([5000]), osa.OPTIM_ALGO_ADAMW, osa.optim_plan_opts(0, 0, 0, tile)) > 0
+    for tile in (512, 3072, 1 << 25, -4):
+        expect_error(osa.OPTIM_EINVAL, lambda: ws(
+            fake_list([5000]), osa.OPTIM_ALGO_ADAMW, osa.optim_plan_opts(0, 0, 0, tile)))
+    n = 1000
+    kw = dict(m=None, v=None, qm=[f(n)], qv=[f(n)], absmax_m=[f(64)], absmax_v=[f(64)])
+    assert ws(fake_list([n], fake=f, **kw), osa.OPTIM_ALGO_BLOCKWISE, osa.optim_plan_opts(8, 256, 0, 2048)) > 0
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(
+        fake_list([n], fake=f, **kw), osa.OPTIM_ALGO_BLOCKWISE, osa.optim_plan_opts(8, 256, 0, 1024)))
+
+
 def test_null_plan_is_rejected_without_device(L):
     expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_step_adamw(
         None, osa.optim_adamw_hp(0.9, 0.999, 1e-8), 1 << 40, None, None, 1 << 41, 0))

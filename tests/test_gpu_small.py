@@ -53,7 +53,8 @@ def _load_grads(state, gs, scale=1.0):
 
 
 def _run_adam(algo, sizes, steps, *, lr, betas=(0.9, 0.999), eps=1e-8, wd_of=None, grad_bf16=False,
-              param_bf16=False, unaligned=(), beta3=0.9999, alpha=5.0, g_std=1e-2, key=0):
+              param_bf16=False, unaligned=(), beta3=0.9999, alpha=5.0, g_std=1e-2, key=0, tile=0,
+              grid=0):
     wd = [wd_of(i) if wd_of else 0.01 * (i % 3) for i in range(len(sizes))]
     p0 = _p0(sizes, key)
     st = AdamState(_to_dev(p0, unaligned), grad_bf16=grad_bf16, param_bf16=param_bf16,
@@ -63,7 +64,7 @@ def _run_adam(algo, sizes, steps, *, lr, betas=(0.9, 0.999), eps=1e-8, wd_of=Non
             for lst in (st.m, st.v):
                 buf = torch.zeros(sizes[i] + 1, dtype=torch.float32, device=DEV)
                 lst[i] = buf[1:]
-    plan = osa.Plan(st.tensor_list(wd), algo)
+    plan = osa.Plan(st.tensor_list(wd), algo, tile=tile, grid=grid)
     sc = DevScalars(lr)
     op = [x.astype(np.float64) for x in p0]
     om = [np.zeros(n) for n in sizes]
@@ -112,6 +113,17 @@ def test_adamw_bf16_params_with_remainders():
         assert np.array_equal(r, st.r[i].cpu().numpy())
 
 
+@pytest.mark.parametrize("algo,tile,grid", [(osa.OPTIM_ALGO_ADAMW, 1024, 0), (osa.OPTIM_ALGO_ADAMW, 8192, 0),
+                                            (osa.OPTIM_ALGO_ADAMW, 2048, 7), (osa.OPTIM_ALGO_ADEMAMIX, 1024, 0)])
+def test_launch_shapes(algo, tile, grid):
+    """Smallest and larger work units and a persistent grid of 7 workgroups
+    cover the same elements (full groups, single groups, ragged ends): bf16
+    params with remainders and bf16 grads exercise the 16-bit accesses."""
+    bf16 = algo == osa.OPTIM_ALGO_ADAMW
+    _run_adam(algo, RAGGED, 4, lr=3e-4, betas=(0.9, 0.95), grad_bf16=bf16, param_bf16=bf16, g_std=1e-3,
+              key=5, tile=tile, grid=grid)
+
+
 def test_ademamix_fp32_ragged():
     _run_adam(osa.OPTIM_ALGO_ADEMAMIX, RAGGED, 12, lr=0.1, wd_of=lambda i: 0.1, key=3)
 
@@ -140,14 +152,14 @@ MINI_LIST = [("tok_embeddings.weight", 37 * 64), ("layers.0.attention.wq.weight"
              ("norm.weight", 64), ("output.weight", 37 * 64)]
 
 
-def _mini_run(steps, key, grad_bf16=False, lr=3e-4, wd=0.1, dim=64, heads=4, items=MINI_LIST):
+def _mini_run(steps, key, grad_bf16=False, lr=3e-4, wd=0.1, dim=64, heads=4, items=MINI_LIST, tile=0):
     names = [n for n, _ in items]
     sizes = [s for _, s in items]
     kinds, hn, wds = osa.adam_mini_partition(names, sizes, dim=dim, n_heads=heads, weight_decay=wd)
     vlen = [s if k == osa.OPTIM_MINI_FULL_V else s // h for k, s, h in zip(kinds, sizes, hn)]
     p0 = _p0(sizes, key)
     st = AdamState(_to_dev(p0), grad_bf16=grad_bf16, v_len=vlen)
-    plan = osa.Plan(st.tensor_list(wds, mini_kind=kinds, head_numel=hn), osa.OPTIM_ALGO_ADAM_MINI)
+    plan = osa.Plan(st.tensor_list(wds, mini_kind=kinds, head_numel=hn), osa.OPTIM_ALGO_ADAM_MINI, tile=tile)
     sc = DevScalars(lr)
     lr32 = float(np.float32(lr))
     # oracle side: its own partition by name
@@ -179,6 +191,15 @@ def test_adam_mini_bf16_grads_and_unaligned_blocks():
     items = [("layers.0.attention.wq.weight", 100), ("layers.0.attention.wk.weight", 100),
              ("layers.0.attention.wo.weight", 100), ("embed.weight", 30)]
     _mini_run(6, 6, grad_bf16=True, dim=10, heads=4, items=items)
+
+
+def test_adam_mini_small_units():
+    """1024-element units: a head block of 8192 (dim 128, 2 heads) spans 8
+    units whose partial sums the finalize adds; ragged other tensors."""
+    items = [("layers.0.attention.wq.weight", 128 * 128), ("layers.0.attention.wk.weight", 128 * 128),
+             ("layers.0.feed_forward.w1.weight", 128 * 300 + 7), ("layers.0.attention_norm.weight", 128),
+             ("output.weight", 5003)]
+    _mini_run(5, 9, dim=128, heads=2, items=items, tile=1024)
 
 
 def test_adam_mini_deterministic():
