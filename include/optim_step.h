@@ -106,7 +106,7 @@ typedef struct optim_tensor_list {
  *              grid of that many workgroups walking the units grid-stride
  *  tile        elements per work unit, a power of two in [1024, 2^24]
  *              (blockwise: at least 2048); 0 = 2048 (Adam-mini 4096,
- *              blockwise 65536)                                            */
+ *              blockwise 16384)                                            */
 typedef struct optim_plan_opts {
     int32_t bits;
     int32_t block;

@@ -2,31 +2,42 @@
 // quantize / dequantize helpers that share its device code.
 //
 // [BNB]: the 2-state branch of the blockwise 8-bit kernel, with the
-// Algorithm 2 decay order; [AO]: 4-bit optimizer states.  Each lane owns 8
-// consecutive elements per row of 2048; one quantization block is L = block/8
-// consecutive lanes of one wavefront, so the block absmax is a max over an
-// aligned lane group (DPP row operations, then one swizzle / readlane step).
-// The maps -- values, thresholds and the bucket table of the code search --
-// live in LDS.  This step issues far more VALU and LDS work per byte than the
-// elementwise steps, so every per-element instruction counts here.
+// Algorithm 2 decay order; [AO]: 4-bit optimizer states.  Each lane owns E
+// consecutive elements per row of 256*E; one quantization block is
+// L = block/E consecutive lanes of one wavefront, so the block absmax is a
+// max over an aligned lane group (DPP row operations, then one swizzle /
+// readlane step).  E = 4 wherever a block fits in one wave (block <= 256):
+// a wave instruction then covers one contiguous run and the accesses are
+// non-temporal, as in the elementwise steps.  E = 8 (ordinary accesses) for
+// 4-bit blocks of 512.  The maps -- values, thresholds and the bucket table
+// of the code search -- live in LDS.  This step issues far more VALU and LDS
+// work per byte than the elementwise steps, so every per-element
+// instruction counts here.
 #include "device_common.h"
+
+#include <type_traits>
 
 namespace optim {
 namespace {
 
-constexpr int kQE = 8;  // elements per lane per row
-constexpr int64_t kQRow = (int64_t)kThreads * kQE;
+// lanes per block <= 64 (one wave): E = 4 up to block 256, else 8
+__host__ __device__ constexpr int lane_elems(int block) { return block <= 256 ? 4 : 8; }
+template <int E>
+constexpr int row_layout() { return E == 4 ? kStrided : kRun; }
 
+// vals: the 2^MB magnitudes, then their negations, so a signed code (sign
+// bit above the MB magnitude bits) indexes its signed value directly.
 template <int MB>
 struct LdsMap {
-    float vals[1 << MB];
+    float vals[2 << MB];
     float thr[(1 << MB) + 4];  // thr[2^MB] = +inf ends the search
     uint8_t lut[kLutBuckets];
 };
 
 template <int MB>
 __device__ __forceinline__ void load_map(LdsMap<MB> &dst, const QuantMap &src) {
-    for (int i = threadIdx.x; i < (1 << MB); i += kThreads) dst.vals[i] = src.vals[i];
+    for (int i = threadIdx.x; i < (2 << MB); i += kThreads)
+        dst.vals[i] = i < (1 << MB) ? src.vals[i] : -src.vals[i - (1 << MB)];
     for (int i = threadIdx.x; i <= (1 << MB); i += kThreads) dst.thr[i] = src.thr[i];
     const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src.lut);
     u32x4 *d4 = reinterpret_cast<u32x4 *>(dst.lut);
@@ -40,51 +51,65 @@ __device__ __forceinline__ void load_map(LdsMap<MB> &dst, const QuantMap &src) {
 // thr[1] > 2^-26).
 template <int MB>
 __device__ __forceinline__ uint32_t code_index(const LdsMap<MB> &M, float a) {
-    int32_t b = (int32_t)(__float_as_uint(a) >> (23 - kLutMantBits)) - (kLutBaseExp << kLutMantBits);
-    b = b < 0 ? 0 : (b < kLutBuckets ? b : kLutBuckets - 1);
+    const int32_t b = __builtin_elementwise_min(
+        __builtin_elementwise_max((int32_t)(__float_as_uint(a) >> (23 - kLutMantBits)) -
+                                      (kLutBaseExp << kLutMantBits), 0),
+        kLutBuckets - 1);
     const uint32_t c = M.lut[b];
     return c + (M.thr[c + 1] <= a ? 1u : 0u);
 }
 
+// Lane-group max on the bit patterns of non-negative, NaN-free floats,
+// whose unsigned order is their numeric order (no canonicalisation of
+// exchanged values, and the exchange folds into the max instruction).
 template <int CTRL>
-__device__ __forceinline__ float max_dpp(float x) {
-    const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false);
-    return fmaxf(x, __int_as_float(y));
+__device__ __forceinline__ uint32_t max_dpp(uint32_t x) {
+    const uint32_t y = __builtin_amdgcn_update_dpp(0u, x, CTRL, 0xF, 0xF, false);
+    return x > y ? x : y;
 }
 
 // Max over each aligned group of L lanes (L a power of two, <= 64); every
 // lane of a group receives its group's max.  Needs all 64 lanes active.
-__device__ __forceinline__ float group_max(float x, int L) {
-    if (L >= 2) x = max_dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-    if (L >= 4) x = max_dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-    if (L >= 8) x = max_dpp<0x141>(x);  // row_half_mirror
-    if (L >= 16) x = max_dpp<0x140>(x); // row_mirror
-    if (L >= 32)                        // lanes i <-> i ^ 16 within 32
-        x = fmaxf(x, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F)));
-    if (L >= 64)
-        x = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)),
-                  __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)));
+template <int L>
+__device__ __forceinline__ uint32_t group_max(uint32_t x) {
+    static_assert(L >= 1 && L <= 64 && (L & (L - 1)) == 0, "lane group");
+    if constexpr (L >= 2) x = max_dpp<0xB1>(x);   // quad_perm [1,0,3,2]
+    if constexpr (L >= 4) x = max_dpp<0x4E>(x);   // quad_perm [2,3,0,1]
+    if constexpr (L >= 8) x = max_dpp<0x141>(x);  // row_half_mirror
+    if constexpr (L >= 16) x = max_dpp<0x140>(x); // row_mirror
+    // Swapping a register with itself across rows: permlane16_swap pairs lane
+    // i with i ^ 16, permlane32_swap pairs i with i ^ 32 (VALU, no LDS).
+    if constexpr (L >= 32) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        x = r[0] > r[1] ? r[0] : r[1];
+    }
+    if constexpr (L >= 64) {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        x = r[0] > r[1] ? r[0] : r[1];
+    }
     return x;
 }
 
-// Codes of this lane's 8 elements (element j in bits [j*BITS, (j+1)*BITS));
+// Codes of this lane's E elements (element j in bits [j*BITS, (j+1)*BITS));
 // the block is this lane's group of L lanes.  A = max|x| over the block,
 // r = fl32(1/A) (IEEE division), a = fl32(|x| r); signed maps put the sign
 // above the magnitude bits, sign 0 for index 0; A = 0 gives all-zero codes.
 // Elements outside the tensor must hold 0.
-template <int BITS, bool SIGNED>
-__device__ __forceinline__ uint64_t quantize_lane(const float (&x)[kQE], int L,
+template <int BITS, bool SIGNED, int E, int L>
+__device__ __forceinline__ uint64_t quantize_lane(const float (&x)[E],
                                                   const LdsMap<SIGNED ? BITS - 1 : BITS> &M, float &A) {
     constexpr int MB = SIGNED ? BITS - 1 : BITS;
-    float mx = fabsf(x[0]);
+    // max|x| of the lane, NaN ignored as the threshold rule ignores it (an
+    // all-NaN lane counts as 0), then of the block
+    float lm = fabsf(x[0]);
 #pragma unroll
-    for (int j = 1; j < kQE; ++j) mx = fmaxf(mx, fabsf(x[j]));
-    mx = group_max(mx, L);
+    for (int j = 1; j < E; ++j) lm = fmaxf(lm, fabsf(x[j]));
+    const float mx = __uint_as_float(group_max<L>(lm == lm ? __float_as_uint(lm) : 0u));
     A = mx;
     const float r = mx > 0.0f ? 1.0f / mx : 0.0f;
     uint64_t out = 0;
 #pragma unroll
-    for (int j = 0; j < kQE; ++j) {
+    for (int j = 0; j < E; ++j) {
         uint32_t c = code_index<MB>(M, fabsf(x[j]) * r);
         if (SIGNED) c |= (x[j] < 0.0f && c > 0) ? (1u << MB) : 0u;
         out |= (uint64_t)c << (j * BITS);
@@ -92,42 +117,48 @@ __device__ __forceinline__ uint64_t quantize_lane(const float (&x)[kQE], int L,
     return out;
 }
 
-// x = fl32(+-vals[idx] * A)
-template <int BITS, bool SIGNED>
+// x = fl32(+-vals[idx] * A): the table holds the signed value of a signed
+// code, and (-v) * A = -(v * A) exactly.
+template <int BITS, bool SIGNED, int E>
 __device__ __forceinline__ void dequantize_lane(uint64_t codes, float A,
-                                                const LdsMap<SIGNED ? BITS - 1 : BITS> &M, float (&x)[kQE]) {
-    constexpr int MB = SIGNED ? BITS - 1 : BITS;
+                                                const LdsMap<SIGNED ? BITS - 1 : BITS> &M, float (&x)[E]) {
 #pragma unroll
-    for (int j = 0; j < kQE; ++j) {
+    for (int j = 0; j < E; ++j) {
         const uint32_t c = (uint32_t)(codes >> (j * BITS)) & ((1u << BITS) - 1u);
-        const float mag = M.vals[c & ((1u << MB) - 1u)] * A;
-        x[j] = (SIGNED && ((c >> MB) & 1u)) ? -mag : mag;
+        x[j] = M.vals[c] * A;
     }
 }
 
-// Packed codes of elements [e, e + 8) (e a multiple of 8, so this lane owns
-// whole bytes).  Full: one 8-byte (8-bit) or 4-byte (4-bit) access.
-template <int BITS>
+// Packed codes of elements [e, e + E) (e a multiple of E, so this lane owns
+// whole bytes).  Full: one access of E*BITS bits (64, 32 or 16).
+template <int BITS, int E>
 __device__ __forceinline__ uint64_t load_codes_full(const uint8_t *q, int64_t e) {
+    constexpr int LAY = row_layout<E>();
     const int64_t byte0 = e * BITS / 8;
-    if constexpr (BITS == 8) {
-        const u32x2 w = *(const GMEM u32x2 *)gp(q + byte0);
+    if constexpr (E * BITS == 64) {
+        const u32x2 w = vload<LAY>((const GMEM u32x2 *)gp(q + byte0));
         return (uint64_t)w.x | ((uint64_t)w.y << 32);
+    } else if constexpr (E * BITS == 32) {
+        return vload<LAY>((const GMEM uint32_t *)gp(q + byte0));
     } else {
-        return *(const GMEM uint32_t *)gp(q + byte0);
+        static_assert(E * BITS == 16, "code run");
+        return vload<LAY>((const GMEM uint16_t *)gp(q + byte0));
     }
 }
 
-template <int BITS>
+template <int BITS, int E>
 __device__ __forceinline__ void store_codes_full(uint8_t *q, int64_t e, uint64_t c) {
+    constexpr int LAY = row_layout<E>();
     const int64_t byte0 = e * BITS / 8;
-    if constexpr (BITS == 8)
-        *(GMEM u32x2 *)gp(q + byte0) = u32x2{(uint32_t)c, (uint32_t)(c >> 32)};
+    if constexpr (E * BITS == 64)
+        vstore<LAY>((GMEM u32x2 *)gp(q + byte0), u32x2{(uint32_t)c, (uint32_t)(c >> 32)});
+    else if constexpr (E * BITS == 32)
+        vstore<LAY>((GMEM uint32_t *)gp(q + byte0), (uint32_t)c);
     else
-        *(GMEM uint32_t *)gp(q + byte0) = (uint32_t)c;
+        vstore<LAY>((GMEM uint16_t *)gp(q + byte0), (uint16_t)c);
 }
 
-// Tail: nv < 8 valid elements, byte by byte; a half byte beyond the tensor
+// Tail: nv < E valid elements, byte by byte; a half byte beyond the tensor
 // reads as 0 and is written as 0.
 template <int BITS>
 __device__ __forceinline__ uint64_t load_codes_part(const uint8_t *q, int64_t e, int nv) {
@@ -145,84 +176,138 @@ __device__ __forceinline__ void store_codes_part(uint8_t *q, int64_t e, int nv, 
     for (int b = 0; b < nbytes; ++b) gp(q)[byte0 + b] = (uint8_t)(c >> (8 * b));
 }
 
-struct BlockCtx {
-    const TensorDesc *T;
-    int L, lane, block;
+// A 64-bit pointer that is the same in every lane, moved to scalar registers.
+// readfirstlane returns int: each half goes back through uint32_t, so a low
+// half with bit 31 set is not sign-extended into the high half.
+template <class T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (T *)((hi << 32) | lo);
+}
+
+// One unit's arrays, offset to the unit's first element (a multiple of the
+// tile, hence of the quantization block and of 8 elements) and kept in scalar
+// registers: the tensor descriptor is read once per unit, not once per row.
+struct UnitPtrs {
+    float *p;
+    const void *g;
+    uint8_t *qm, *qv;
+    float *am, *av;
     float decay;
+    int lane;
 };
 
-// One row of 2048 elements: this lane's 8 elements start at element e.
-// FULL: the whole row is inside the tensor and every pointer is aligned.
-template <int GK, int BITS, bool FULL>
-__device__ __forceinline__ void blockwise_row(const BlockCtx &c, const AdamK &k, int64_t e, int nv,
-                                              const LdsMap<BITS - 1> &Mm, const LdsMap<BITS> &Mv) {
-    const TensorDesc &T = *c.T;
-    float *P = static_cast<float *>(T.p);
-    const int64_t blk = e / c.block;
-    float p[kQE], g[kQE], am = 0.0f, av = 0.0f;
-    uint64_t cm = 0, cv = 0;
+template <int GK, int BITS, int BLOCK>
+__device__ __forceinline__ UnitPtrs unit_ptrs(const TensorDesc &T, int64_t start, float decay) {
+    UnitPtrs u;
+    u.p = uniform_ptr(static_cast<float *>(T.p) + start);
+    u.g = uniform_ptr(static_cast<const char *>(T.g) + start * (GK == G_F32 ? 4 : 2));
+    u.qm = uniform_ptr(T.qm + start * BITS / 8);
+    u.qv = uniform_ptr(T.qv + start * BITS / 8);
+    u.am = uniform_ptr(T.am + start / BLOCK);
+    u.av = uniform_ptr(T.av + start / BLOCK);
+    u.decay = decay;
+    u.lane = threadIdx.x & 63;
+    return u;
+}
+
+// One row of 256*E elements, this lane's E elements from element e of the
+// unit: its inputs, loaded ahead of the row's arithmetic.
+template <int E>
+struct RowIn {
+    float p[E], g[E];
+    uint64_t cm, cv;
+    float am, av;
+};
+
+// FULL: the whole row is inside the tensor and every pointer is aligned;
+// otherwise nv (0..E) of the lane's elements are valid and the rest read 0.
+template <int GK, int BITS, int BLOCK, bool FULL>
+__device__ __forceinline__ void load_row(const UnitPtrs &u, const AdamK &k, uint32_t e, int nv,
+                                         RowIn<lane_elems(BLOCK)> &in) {
+    constexpr int E = lane_elems(BLOCK);
+    constexpr int LAY = row_layout<E>();
+    const uint32_t blk = e / BLOCK;
+    in.am = in.av = 0.0f;
+    in.cm = in.cv = 0;
     if (FULL || nv > 0) {
-        am = gp(T.am)[blk];
-        av = gp(T.av)[blk];
+        in.am = gp(u.am)[blk];
+        in.av = gp(u.av)[blk];
     }
     if (FULL) {
-        ldf<kQE, kRun>(P, e, p);
-        load_g<GK, kQE, kRun>(T.g, e, k.inv_scale, g);
-        cm = load_codes_full<BITS>(T.qm, e);
-        cv = load_codes_full<BITS>(T.qv, e);
+        ldf<E, LAY>(u.p, e, in.p);
+        load_g<GK, E, LAY>(u.g, e, k.inv_scale, in.g);
+        in.cm = load_codes_full<BITS, E>(u.qm, e);
+        in.cv = load_codes_full<BITS, E>(u.qv, e);
     } else {
 #pragma unroll
-        for (int j = 0; j < kQE; ++j) {
+        for (int j = 0; j < E; ++j) {
             float pj[1] = {0.0f}, gj[1] = {0.0f};
             if (j < nv) {
-                ldf<1>(P, e + j, pj);
-                load_g<GK, 1>(T.g, e + j, k.inv_scale, gj);
+                ldf<1>(u.p, e + j, pj);
+                load_g<GK, 1>(u.g, e + j, k.inv_scale, gj);
             }
-            p[j] = pj[0];
-            g[j] = gj[0];
+            in.p[j] = pj[0];
+            in.g[j] = gj[0];
         }
         if (nv > 0) {
-            cm = load_codes_part<BITS>(T.qm, e, nv);
-            cv = load_codes_part<BITS>(T.qv, e, nv);
+            in.cm = load_codes_part<BITS>(u.qm, e, nv);
+            in.cv = load_codes_part<BITS>(u.qv, e, nv);
         }
-    }
-    float mt[kQE], vt[kQE];
-    dequantize_lane<BITS, true>(cm, am, Mm, mt);
-    dequantize_lane<BITS, false>(cv, av, Mv, vt);
-    // fp32 state recipe, every product and sum rounded on its own; outside
-    // the tensor g = 0 and the codes are 0, so the new states are 0 there
-    float mn[kQE], vn[kQE];
-#pragma unroll
-    for (int j = 0; j < kQE; ++j) {
-        mn[j] = k.b1 * mt[j] + k.c1 * g[j];
-        vn[j] = k.b2 * vt[j] + k.c2 * (g[j] * g[j]);
-        // parameter update: hardware sqrt / reciprocal (1 ulp each)
-        const float h = __builtin_amdgcn_sqrtf(vn[j]) * k.isb2 + k.eps;
-        p[j] = p[j] * c.decay - k.ss * (mn[j] * __builtin_amdgcn_rcpf(h));
-    }
-    float am2, av2;
-    const uint64_t om = quantize_lane<BITS, true>(mn, c.L, Mm, am2);
-    const uint64_t ov = quantize_lane<BITS, false>(vn, c.L, Mv, av2);
-    if (FULL) {
-        stf<kQE, kRun>(P, e, p);
-        store_codes_full<BITS>(T.qm, e, om);
-        store_codes_full<BITS>(T.qv, e, ov);
-    } else if (nv > 0) {
-        for (int j = 0; j < nv; ++j) {
-            const float pj[1] = {p[j]};
-            stf<1>(P, e + j, pj);
-        }
-        store_codes_part<BITS>(T.qm, e, nv, om);
-        store_codes_part<BITS>(T.qv, e, nv, ov);
-    }
-    if ((FULL || nv > 0) && (c.lane & (c.L - 1)) == 0) {
-        gp(T.am)[blk] = am2;
-        gp(T.av)[blk] = av2;
     }
 }
 
-template <int GK, int BITS>
+template <int GK, int BITS, int BLOCK, bool FULL>
+__device__ __forceinline__ void step_row(const UnitPtrs &u, const AdamK &k, uint32_t e, int nv,
+                                         RowIn<lane_elems(BLOCK)> &in, const LdsMap<BITS - 1> &Mm,
+                                         const LdsMap<BITS> &Mv) {
+    constexpr int E = lane_elems(BLOCK), L = BLOCK / E;
+    constexpr int LAY = row_layout<E>();
+    float mt[E], vt[E];
+    dequantize_lane<BITS, true, E>(in.cm, in.am, Mm, mt);
+    dequantize_lane<BITS, false, E>(in.cv, in.av, Mv, vt);
+    // fp32 state recipe, every product and sum rounded on its own; outside
+    // the tensor g = 0 and the codes are 0, so the new states are 0 there
+    float mn[E], vn[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        mn[j] = k.b1 * mt[j] + k.c1 * in.g[j];
+        vn[j] = k.b2 * vt[j] + k.c2 * (in.g[j] * in.g[j]);
+        // parameter update: hardware sqrt / reciprocal (1 ulp each)
+        const float h = __builtin_amdgcn_sqrtf(vn[j]) * k.isb2 + k.eps;
+        in.p[j] = in.p[j] * u.decay - k.ss * (mn[j] * __builtin_amdgcn_rcpf(h));
+    }
+    float am2, av2;
+    const uint64_t om = quantize_lane<BITS, true, E, L>(mn, Mm, am2);
+    const uint64_t ov = quantize_lane<BITS, false, E, L>(vn, Mv, av2);
+    if (FULL) {
+        stf<E, LAY>(u.p, e, in.p);
+        store_codes_full<BITS, E>(u.qm, e, om);
+        store_codes_full<BITS, E>(u.qv, e, ov);
+    } else if (nv > 0) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const float pj[1] = {in.p[j]};
+            if (j < nv) stf<1>(u.p, e + j, pj);
+        }
+        store_codes_part<BITS>(u.qm, e, nv, om);
+        store_codes_part<BITS>(u.qv, e, nv, ov);
+    }
+    // every lane of a block holds the block's absmax: all of them store it
+    // (one line per wave instruction, no branch around the store)
+    if (FULL || nv > 0) {
+        const uint32_t blk = e / BLOCK;
+        gp(u.am)[blk] = am2;
+        gp(u.av)[blk] = av2;
+    }
+}
+
+template <int GK, int BITS, int BLOCK>
 __global__ __launch_bounds__(kThreads) void blockwise_kernel(StepArgs a) {
+    constexpr int E = lane_elems(BLOCK);
+    constexpr uint32_t kRow = (uint32_t)kThreads * E;
     __shared__ LdsMap<BITS - 1> Mm;
     __shared__ LdsMap<BITS> Mv;
     load_map(Mm, BITS == 8 ? a.codebook->m8 : a.codebook->m4);
@@ -232,135 +317,166 @@ __global__ __launch_bounds__(kThreads) void blockwise_kernel(StepArgs a) {
     const StepCommit commit{a, S};
     if (S.skip) return;
     const AdamK k = adam_consts(S);
-    for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
-        BlockCtx c;
-        c.T = &a.tensors[sp.tensor];
-        c.L = a.block / kQE;
-        c.lane = threadIdx.x & 63;
-        c.block = a.block;
-        c.decay = uniform(S.decay[c.T->group]);
-        const bool aligned = c.T->vec_ok;
-        for (int64_t r0 = 0; r0 < len; r0 += kQRow) {
-            const int64_t rel = r0 + threadIdx.x * kQE;
-            const int64_t e = start + rel;  // a multiple of 8
-            if (aligned && r0 + kQRow <= len) {
-                blockwise_row<GK, BITS, true>(c, k, e, kQE, Mm, Mv);
-            } else {
-                const int nv = len - rel >= kQE ? kQE : (len - rel > 0 ? (int)(len - rel) : 0);
-                blockwise_row<GK, BITS, false>(c, k, e, nv, Mm, Mv);
+    for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len64) {
+        const TensorDesc &T = a.tensors[sp.tensor];
+        const UnitPtrs u = unit_ptrs<GK, BITS, BLOCK>(T, start, uniform(S.decay[T.group]));
+        const uint32_t len = (uint32_t)len64;  // <= tile <= 2^24
+        const uint32_t lane0 = threadIdx.x * E;
+        // full rows, software-pipelined: the next row's loads are in flight
+        // while this row computes
+        const uint32_t nfull = T.vec_ok ? len / kRow : 0;
+        if (nfull > 0) {
+            RowIn<E> cur;
+            load_row<GK, BITS, BLOCK, true>(u, k, lane0, E, cur);
+            uint32_t r = 0;
+            for (; r + 1 < nfull; ++r) {
+                RowIn<E> nxt;
+                load_row<GK, BITS, BLOCK, true>(u, k, lane0 + (r + 1) * kRow, E, nxt);
+                step_row<GK, BITS, BLOCK, true>(u, k, lane0 + r * kRow, E, cur, Mm, Mv);
+                cur = nxt;
             }
+            step_row<GK, BITS, BLOCK, true>(u, k, lane0 + r * kRow, E, cur, Mm, Mv);
+        }
+        for (uint32_t r0 = nfull * kRow; r0 < len; r0 += kRow) {
+            const uint32_t rel = r0 + lane0;
+            const int nv = rel + E <= len ? E : (rel < len ? (int)(len - rel) : 0);
+            RowIn<E> in;
+            load_row<GK, BITS, BLOCK, false>(u, k, rel, nv, in);
+            step_row<GK, BITS, BLOCK, false>(u, k, rel, nv, in, Mm, Mv);
         }
     });
 }
 
 // Blockwise quantize / dequantize of a plain fp32 array with the same code
-// path as the step (state import and export).  Rows of 2048 elements,
+// path as the step (state import and export).  Rows of 256*E elements,
 // grid-stride; the loop trip count is uniform per workgroup.
-template <int BITS, bool SIGNED>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(const Codebook *cb, int block, const float *x,
-                                                           int64_t n, bool vec, uint8_t *codes, float *absmax) {
+template <int BITS, bool SIGNED, int BLOCK>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const Codebook *cb, const float *x, int64_t n, bool vec,
+                                                           uint8_t *codes, float *absmax) {
     constexpr int MB = SIGNED ? BITS - 1 : BITS;
+    constexpr int E = lane_elems(BLOCK), L = BLOCK / E;
+    constexpr int LAY = row_layout<E>();
+    constexpr int64_t kRow = (int64_t)kThreads * E;
     __shared__ LdsMap<MB> M;
     load_map(M, BITS == 8 ? (SIGNED ? cb->m8 : cb->v8) : (SIGNED ? cb->m4 : cb->v4));
     __syncthreads();
-    const int L = block / kQE;
-    const int64_t nrows = (n + kQRow - 1) / kQRow;
+    const int64_t nrows = (n + kRow - 1) / kRow;
     for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
-        const int64_t e = row * kQRow + threadIdx.x * kQE;
-        const int nv = n - e >= kQE ? kQE : (n - e > 0 ? (int)(n - e) : 0);
-        const bool full = vec && nv == kQE;
-        float v[kQE];
+        const int64_t e = row * kRow + threadIdx.x * E;
+        const int nv = n - e >= E ? E : (n - e > 0 ? (int)(n - e) : 0);
+        const bool full = vec && nv == E;
+        float v[E];
         if (full) {
-            ldf<kQE, kRun>(x, e, v);
+            ldf<E, LAY>(x, e, v);
         } else {
 #pragma unroll
-            for (int j = 0; j < kQE; ++j) {
+            for (int j = 0; j < E; ++j) {
                 float vj[1] = {0.0f};
                 if (j < nv) ldf<1>(x, e + j, vj);
                 v[j] = vj[0];
             }
         }
         float A;
-        const uint64_t c = quantize_lane<BITS, SIGNED>(v, L, M, A);
+        const uint64_t c = quantize_lane<BITS, SIGNED, E, L>(v, M, A);
         if (full)
-            store_codes_full<BITS>(codes, e, c);
+            store_codes_full<BITS, E>(codes, e, c);
         else if (nv > 0)
             store_codes_part<BITS>(codes, e, nv, c);
-        if (nv > 0 && (threadIdx.x & (L - 1)) == 0) gp(absmax)[e / block] = A;
+        if (nv > 0 && (threadIdx.x & (L - 1)) == 0) gp(absmax)[e / BLOCK] = A;
     }
 }
 
-template <int BITS, bool SIGNED>
-__global__ __launch_bounds__(kThreads) void dequantize_kernel(const Codebook *cb, int block, const uint8_t *codes,
+template <int BITS, bool SIGNED, int BLOCK>
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(const Codebook *cb, const uint8_t *codes,
                                                              const float *absmax, int64_t n, bool vec, float *x) {
     constexpr int MB = SIGNED ? BITS - 1 : BITS;
+    constexpr int E = lane_elems(BLOCK);
+    constexpr int LAY = row_layout<E>();
+    constexpr int64_t kRow = (int64_t)kThreads * E;
     __shared__ LdsMap<MB> M;
     load_map(M, BITS == 8 ? (SIGNED ? cb->m8 : cb->v8) : (SIGNED ? cb->m4 : cb->v4));
     __syncthreads();
-    const int64_t nrows = (n + kQRow - 1) / kQRow;
+    const int64_t nrows = (n + kRow - 1) / kRow;
     for (int64_t row = blockIdx.x; row < nrows; row += gridDim.x) {
-        const int64_t e = row * kQRow + threadIdx.x * kQE;
-        const int nv = n - e >= kQE ? kQE : (n - e > 0 ? (int)(n - e) : 0);
+        const int64_t e = row * kRow + threadIdx.x * E;
+        const int nv = n - e >= E ? E : (n - e > 0 ? (int)(n - e) : 0);
         if (nv == 0) continue;
-        const bool full = vec && nv == kQE;
-        float v[kQE];
-        const uint64_t c = full ? load_codes_full<BITS>(codes, e) : load_codes_part<BITS>(codes, e, nv);
-        dequantize_lane<BITS, SIGNED>(c, gp(absmax)[e / block], M, v);
+        const bool full = vec && nv == E;
+        float v[E];
+        const uint64_t c = full ? load_codes_full<BITS, E>(codes, e) : load_codes_part<BITS>(codes, e, nv);
+        dequantize_lane<BITS, SIGNED, E>(c, gp(absmax)[e / BLOCK], M, v);
         if (full) {
-            stf<kQE, kRun>(x, e, v);
+            stf<E, LAY>(x, e, v);
         } else {
-            for (int j = 0; j < nv; ++j) {
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
                 const float vj[1] = {v[j]};
-                stf<1>(x, e + j, vj);
+                if (j < nv) stf<1>(x, e + j, vj);
             }
         }
     }
 }
 
+// (bits, block) -> compile-time block size; the plan admits 8-bit blocks of
+// 64, 128, 256 and 4-bit blocks of 128, 256, 512.
+template <class F>
+hipError_t with_block(int bits, int block, F &&f) {
+    if (bits == 8) {
+        if (block == 64) return f(std::integral_constant<int, 8>{}, std::integral_constant<int, 64>{});
+        if (block == 128) return f(std::integral_constant<int, 8>{}, std::integral_constant<int, 128>{});
+        if (block == 256) return f(std::integral_constant<int, 8>{}, std::integral_constant<int, 256>{});
+    } else if (bits == 4) {
+        if (block == 128) return f(std::integral_constant<int, 4>{}, std::integral_constant<int, 128>{});
+        if (block == 256) return f(std::integral_constant<int, 4>{}, std::integral_constant<int, 256>{});
+        if (block == 512) return f(std::integral_constant<int, 4>{}, std::integral_constant<int, 512>{});
+    }
+    return hipErrorInvalidValue;
+}
+
+int quant_grid(int64_t n, int E) {
+    const int64_t rows = (n + (int64_t)kThreads * E - 1) / ((int64_t)kThreads * E);
+    return (int)(rows < 16384 ? (rows > 0 ? rows : 1) : 16384);
+}
+
 }  // namespace
 
 hipError_t launch_blockwise(const StepArgs &a, int gk, hipStream_t s) {
-    if (a.bits == 8 && gk == G_F32)
-        LAUNCH_PERSISTENT((blockwise_kernel<G_F32, 8>), a, s);
-    else if (a.bits == 8)
-        LAUNCH_PERSISTENT((blockwise_kernel<G_BF16, 8>), a, s);
-    else if (gk == G_F32)
-        LAUNCH_PERSISTENT((blockwise_kernel<G_F32, 4>), a, s);
-    else
-        LAUNCH_PERSISTENT((blockwise_kernel<G_BF16, 4>), a, s);
-    return hipGetLastError();
+    return with_block(a.bits, a.block, [&](auto bits, auto block) {
+        constexpr int B = decltype(bits)::value, K = decltype(block)::value;
+        if (gk == G_F32)
+            LAUNCH_PERSISTENT((blockwise_kernel<G_F32, B, K>), a, s);
+        else
+            LAUNCH_PERSISTENT((blockwise_kernel<G_BF16, B, K>), a, s);
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_quantize(const Codebook *cb, int bits, int block, int is_signed, const float *x,
                            int64_t n, uint8_t *codes, float *absmax, hipStream_t s) {
-    const int64_t rows = (n + kQRow - 1) / kQRow;
-    const int grid = (int)(rows < 16384 ? (rows > 0 ? rows : 1) : 16384);
     const bool vec = ((uintptr_t)x % 16 == 0) && ((uintptr_t)codes % 8 == 0);
-    if (bits == 8 && is_signed)
-        hipLaunchKernelGGL((quantize_kernel<8, true>), dim3(grid), dim3(kThreads), 0, s, cb, block, x, n, vec, codes, absmax);
-    else if (bits == 8)
-        hipLaunchKernelGGL((quantize_kernel<8, false>), dim3(grid), dim3(kThreads), 0, s, cb, block, x, n, vec, codes, absmax);
-    else if (is_signed)
-        hipLaunchKernelGGL((quantize_kernel<4, true>), dim3(grid), dim3(kThreads), 0, s, cb, block, x, n, vec, codes, absmax);
-    else
-        hipLaunchKernelGGL((quantize_kernel<4, false>), dim3(grid), dim3(kThreads), 0, s, cb, block, x, n, vec, codes, absmax);
-    return hipGetLastError();
+    return with_block(bits, block, [&](auto b, auto k) {
+        constexpr int B = decltype(b)::value, K = decltype(k)::value;
+        const dim3 grid(quant_grid(n, lane_elems(K)));
+        if (is_signed)
+            hipLaunchKernelGGL((quantize_kernel<B, true, K>), grid, dim3(kThreads), 0, s, cb, x, n, vec, codes, absmax);
+        else
+            hipLaunchKernelGGL((quantize_kernel<B, false, K>), grid, dim3(kThreads), 0, s, cb, x, n, vec, codes, absmax);
+        return hipGetLastError();
+    });
 }
 
 hipError_t launch_dequantize(const Codebook *cb, int bits, int block, int is_signed, const uint8_t *codes,
                              const float *absmax, int64_t n, float *x, hipStream_t s) {
-    const int64_t rows = (n + kQRow - 1) / kQRow;
-    const int grid = (int)(rows < 16384 ? (rows > 0 ? rows : 1) : 16384);
     const bool vec = ((uintptr_t)x % 16 == 0) && ((uintptr_t)codes % 8 == 0);
-    if (bits == 8 && is_signed)
-        hipLaunchKernelGGL((dequantize_kernel<8, true>), dim3(grid), dim3(kThreads), 0, s, cb, block, codes, absmax, n, vec, x);
-    else if (bits == 8)
-        hipLaunchKernelGGL((dequantize_kernel<8, false>), dim3(grid), dim3(kThreads), 0, s, cb, block, codes, absmax, n, vec, x);
-    else if (is_signed)
-        hipLaunchKernelGGL((dequantize_kernel<4, true>), dim3(grid), dim3(kThreads), 0, s, cb, block, codes, absmax, n, vec, x);
-    else
-        hipLaunchKernelGGL((dequantize_kernel<4, false>), dim3(grid), dim3(kThreads), 0, s, cb, block, codes, absmax, n, vec, x);
-    return hipGetLastError();
+    return with_block(bits, block, [&](auto b, auto k) {
+        constexpr int B = decltype(b)::value, K = decltype(k)::value;
+        const dim3 grid(quant_grid(n, lane_elems(K)));
+        if (is_signed)
+            hipLaunchKernelGGL((dequantize_kernel<B, true, K>), grid, dim3(kThreads), 0, s, cb, codes, absmax, n, vec, x);
+        else
+            hipLaunchKernelGGL((dequantize_kernel<B, false, K>), grid, dim3(kThreads), 0, s, cb, codes, absmax, n, vec, x);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace optim

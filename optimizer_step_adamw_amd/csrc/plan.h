@@ -16,7 +16,7 @@ namespace optim {
 constexpr int kThreads = 256;        // workgroup size (4 wavefronts of 64)
 constexpr int64_t kDefaultTile = 2048;
 constexpr int64_t kAdamMiniTile = 4096;
-constexpr int64_t kBlockwiseTile = 65536;
+constexpr int64_t kBlockwiseTile = 16384;
 constexpr int64_t kFiniteCheckElems = 8192;  // read-only scan: elements per workgroup
 constexpr int64_t kMinTile = 1024;   // one group of 4 elements per lane
 constexpr int64_t kMinBlockwiseTile = 2048;  // one quantizer row: 256 lanes x 8 elements

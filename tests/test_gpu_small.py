@@ -247,6 +247,51 @@ def test_blockwise_codes_bit_exact(bits, block):
             assert err <= (TOL_STEP1 if t == 1 else TOL_RUN), (t, i, err)
 
 
+@pytest.mark.parametrize("bits,block,tile", [(8, 256, 16384), (4, 128, 0)])
+def test_blockwise_arrays_across_a_2gib_address_boundary(bits, block, tile):
+    """Every array of the tensor sits in one 4 GiB allocation, placed so that
+    the low 32 bits of its addresses run through 0x80000000 (the step keeps
+    per-unit pointers in scalar registers; each half of a pointer must be
+    moved without sign extension)."""
+    n = 3 * 16384 + 2 * 256 + 13
+    nb, nblk = (n * bits + 7) // 8, (n + block - 1) // block
+    sizes = [4 * n, 4 * n, nb, nb, 4 * nblk, 4 * nblk]
+    span = sum((x + 255) // 256 * 256 for x in sizes)
+    buf = torch.zeros((1 << 32) + span, dtype=torch.uint8, device=DEV)
+    off = (0x7FFFC000 - buf.data_ptr()) % (1 << 32)
+    views, o = [], off
+    for x in sizes:
+        views.append(buf[o:o + x])
+        o += (x + 255) // 256 * 256
+    assert views[0].data_ptr() % (1 << 32) < 0x80000000 < (views[0].data_ptr() + 4 * n) % (1 << 32)
+    p, g = views[0].view(torch.float32), views[1].view(torch.float32)
+    qm, qv, am, av = views[2], views[3], views[4].view(torch.float32), views[5].view(torch.float32)
+    p0 = _p0([n], 30 + bits)[0]
+    p.copy_(torch.from_numpy(p0).to(DEV))
+    tl = osa.TensorList([p], [g], qm=[qm], qv=[qv], absmax_m=[am], absmax_v=[av], weight_decay=[0.01])
+    plan = osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE, bits=bits, block=block, tile=tile)
+    sc = DevScalars(1e-3)
+    lr32 = float(np.float32(1e-3))
+    op = p0.astype(np.float64)
+    oqm, oqv = np.zeros(n, np.uint8), np.zeros(n, np.uint8)
+    oam, oav = np.zeros(nblk, np.float32), np.zeros(nblk, np.float32)
+    for t in range(1, 4):
+        gh = _grads([n], 31, t, 1e-3)[0]
+        g.copy_(torch.from_numpy(gh).to(DEV))
+        osa.optim_step_8bit_blockwise(plan.handle, osa.optim_adamw_hp(0.9, 0.999, 1e-8), bits, block, sc.lr,
+                                      None, None, sc.step)
+        orc.blockwise_step(op, gh, oqm, oqv, oam, oav, bits, block, lr32, 0.9, 0.999, 1e-8, 0.01, t)
+        em = orc.pack_nibbles(oqm) if bits == 4 else oqm
+        ev = orc.pack_nibbles(oqv) if bits == 4 else oqv
+        assert np.array_equal(qm.cpu().numpy(), em), t
+        assert np.array_equal(qv.cpu().numpy(), ev), t
+        assert np.array_equal(am.cpu().numpy().view(np.uint32), oam.view(np.uint32)), t
+        assert np.array_equal(av.cpu().numpy().view(np.uint32), oav.view(np.uint32)), t
+        assert relerr_tau(p.cpu().numpy(), op, lr32) <= (TOL_STEP1 if t == 1 else TOL_RUN), t
+    del buf, views, p, g, qm, qv, am, av, tl, plan
+    torch.cuda.empty_cache()
+
+
 def test_blockwise_fresh_step_discriminates_ordering():
     """bitsandbytes PR #2040 body: one fresh 8-bit step at lr=0.1, wd=0.1 has
     the closed form -lr*g/(|g|+eps) after decay; decay-after is 1e-3 away."""
