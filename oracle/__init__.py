@@ -61,9 +61,13 @@ _SIGS = {
     "oracle_unpack_nibbles": [_i64, _p, _p],
     "oracle_blockwise_step": [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p,
                               _d, _d, _d, _d, _d, _i64, _p, _p],
+    "oracle_sumsq": [_i64, _p],
+    "oracle_clip_coef": [_d, _d],
+    "oracle_scaler_update": [_p, _p, _i32, _d, _d, _i32],
 }
 _RESTYPES = {"oracle_any_nonfinite": _i32, "oracle_cosine_lr": ctypes.c_float,
-             "oracle_remainder_exhaustive": _i64, "oracle_dynamic_map": _i32}
+             "oracle_remainder_exhaustive": _i64, "oracle_dynamic_map": _i32,
+             "oracle_sumsq": _d, "oracle_clip_coef": _d}
 
 
 def load(path: str) -> ctypes.CDLL:
@@ -166,6 +170,32 @@ def adam_mini_step(p, m, V, g, block, lr, beta1, beta2, eps, wd, t):
 def any_nonfinite(x) -> bool:
     x = _f64(x)
     return bool(lib().oracle_any_nonfinite(x.size, _ptr(x)))
+
+
+def grad_norm(grads, inv_scale: float = 1.0) -> float:
+    """Global L2 norm of the unscaled gradients G*s over the whole list
+    (FusedAdam & PyTorch Lightning AMP: clipping folded into the step)."""
+    total = 0.0
+    for G in grads:
+        x = _f64(np.asarray(G, np.float64).ravel() * inv_scale)
+        total += lib().oracle_sumsq(x.size, _ptr(x))
+    return float(np.sqrt(total))
+
+
+def clip_coef(norm: float, max_norm: float) -> float:
+    return float(lib().oracle_clip_coef(norm, max_norm))
+
+
+class ScalerState:
+    """Dynamic loss scale (fp32) and count of clean steps."""
+
+    def __init__(self, scale: float, tracker: int = 0):
+        self.scale = np.array([scale], np.float32)
+        self.tracker = np.array([tracker], np.int32)
+
+    def update(self, found_inf: bool, growth: float, backoff: float, interval: int):
+        lib().oracle_scaler_update(_ptr(self.scale), _ptr(self.tracker), int(bool(found_inf)),
+                                   growth, backoff, interval)
 
 
 def cosine_lr(k: int, K: int, lr_max: float, lr_min: float = 0.0) -> np.float32:

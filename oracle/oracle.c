@@ -24,6 +24,8 @@
  *  [LTN]  "FusedAdam & PyTorch Lightning AMP" (Lightning issue #15501).
  *  [TE]   "Support store_param_remainders feature from Apex in TE Fused
  *         Adam" (TransformerEngine PR #1408): description.
+ *  [LTN]  also for the loop around the step: scale, backward, the optional
+ *         unscale_ that exists for gradient clipping, step, update.
  *
  * Parity pins: every function below is pinned by a CPU test against a closed
  * form, an invariant, a library routine (torch.optim.AdamW in float64) or an
@@ -143,6 +145,59 @@ int oracle_any_nonfinite(int64_t n, const double *x)
         if (!isfinite(x[i]))
             return 1;
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gradient clipping inside the fused step.  [LTN] analysis: unscale_ runs
+ * before step only so that gradients can be clipped, and with a fused
+ * optimizer that unscales inside its step an explicit unscale_ is applied a
+ * second time.  Reading used here: clipping is folded into the step's
+ * unscale factor.  The global L2 norm is taken over every gradient of the
+ * step after unscaling, norm = sqrt(sum (G s)^2), summed in index order; the
+ * clip coefficient is min(1, max_norm / (norm + 1e-6)) (the form of
+ * torch.nn.utils.clip_grad_norm_), and 1 when max_norm <= 0 or is +inf, or
+ * when the norm is not finite (the step is skipped then).                  */
+double oracle_sumsq(int64_t n, const double *x)
+{
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        s += x[i] * x[i];
+    return s;
+}
+
+double oracle_clip_coef(double norm, double max_norm)
+{
+    if (!(max_norm > 0.0) || isinf(max_norm) || !isfinite(norm))
+        return 1.0;
+    double c = max_norm / (norm + 1e-6);
+    return c < 1.0 ? c : 1.0;
+}
+
+/* Dynamic loss scale, updated once per loop iteration after the step.
+ * [LTN] shows scaler.update() closing the loop; the pages give no rule.
+ * Reading used here (GradScaler's documented behaviour): a step with a
+ * non-finite gradient multiplies the scale by backoff and resets the count
+ * of clean steps; otherwise the count grows, and when it reaches interval
+ * the scale is multiplied by growth (kept only if the product is finite)
+ * and the count restarts.  The scale is stored as a float: each product is
+ * taken in double and rounded once.                                         */
+void oracle_scaler_update(float *scale, int32_t *tracker, int found_inf, double growth,
+                          double backoff, int32_t interval)
+{
+    if (found_inf) {
+        *scale = (float)((double)*scale * backoff);
+        *tracker = 0;
+        return;
+    }
+    int32_t k = *tracker + 1;
+    if (k >= interval) {
+        float grown = (float)((double)*scale * growth);
+        if (isfinite(grown))
+            *scale = grown;
+        *tracker = 0;
+    } else {
+        *tracker = k;
+    }
 }
 
 /* ------------------------------------------------------------------------ */

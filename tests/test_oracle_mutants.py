@@ -137,6 +137,21 @@ MUTANTS = [
      ["test_absmax_element_roundtrips"]),
     ("nibble_order_swapped", "packed[i] = (uint8_t)(lo | (hi << 4));",
      "packed[i] = (uint8_t)(hi | (lo << 4));", ["test_nibble_packing_layout"]),
+    # ---- gradient clipping and loss scale
+    ("sumsq_of_magnitudes", "        s += x[i] * x[i];\n    return s;", "        s += fabs(x[i]);\n    return s;",
+     ["test_grad_norm_library_and_closed_form", "test_clip_matches_torch_clip_grad_norm"]),
+    ("clip_not_clamped_to_one", "    return c < 1.0 ? c : 1.0;", "    return c;",
+     ["test_clip_matches_torch_clip_grad_norm", "test_clip_coef_special_cases"]),
+    ("clip_without_eps_guard", "double c = max_norm / (norm + 1e-6);", "double c = max_norm / norm;",
+     ["test_clip_matches_torch_clip_grad_norm", "test_clip_coef_special_cases"]),
+    ("scaler_keeps_count_on_overflow",
+     "        *scale = (float)((double)*scale * backoff);\n        *tracker = 0;",
+     "        *scale = (float)((double)*scale * backoff);",
+     ["test_scaler_update_matches_torch", "test_scaler_update_closed_form"]),
+    ("scaler_grows_one_step_late", "    if (k >= interval) {", "    if (k > interval) {",
+     ["test_scaler_update_matches_torch", "test_scaler_update_closed_form"]),
+    ("scaler_grows_to_infinity", "        if (isfinite(grown))\n            *scale = grown;",
+     "        *scale = grown;", ["test_scaler_update_matches_torch"]),
     # ---- blockwise-quantized step
     ("blockwise_decay_after_update",
      "        p[i] = p[i] * (1.0 - lr * wd);\n        double h = sqrt(vi) / sqrt(bc2) + eps;\n"

@@ -446,3 +446,75 @@ def test_blockwise_fresh_step(orc, bits, block):
     c_m, a_m = orc.quantize(sm, block, bits - 1, True)
     assert np.array_equal(c_m, qm) and np.array_equal(a_m, am)
     assert np.array_equal(am, np.max(np.abs(sm).reshape(-1, block), axis=1))
+
+
+# ------------------------------------------------------------------ clipping and loss scale
+def test_grad_norm_library_and_closed_form(orc):
+    """FusedAdam & PyTorch Lightning AMP: clipping is folded into the fused
+    step, so the norm is that of the unscaled gradients G*s over the whole
+    list.  Referee: torch.linalg.vector_norm in float64; closed form: a
+    constant list of N entries c has norm |c| sqrt(N)."""
+    gs = [host_normal(n, 1.0, 903, 0, i, 1).astype(np.float64) * 65536.0 for i, n in enumerate((5, 4097, 300))]
+    s = 2.0 ** -16
+    ref = torch.linalg.vector_norm(torch.cat([torch.from_numpy(g * s) for g in gs])).item()
+    assert abs(orc.grad_norm(gs, s) - ref) <= 1e-14 * ref
+    assert orc.grad_norm([np.full(7, -3.0), np.full(9, -3.0)], 0.25) == 0.75 * 4.0
+    assert orc.grad_norm([np.zeros(5)], 1.0) == 0.0
+
+
+@pytest.mark.parametrize("max_norm", [0.05, 1.0, 1e6])
+def test_clip_matches_torch_clip_grad_norm(orc, max_norm):
+    """Referee: torch.nn.utils.clip_grad_norm_ (float64) on the unscaled
+    gradients; the oracle's coefficient times G*s gives the same gradients,
+    and its returned total norm is the oracle's norm."""
+    gs = [host_normal(n, 1e-2, 904, 1, i, 1).astype(np.float64) * 1024.0 for i, n in enumerate((100, 33, 2048))]
+    s = 1.0 / 1024.0
+    params = [torch.nn.Parameter(torch.zeros(g.size, dtype=torch.float64)) for g in gs]
+    for p, g in zip(params, gs):
+        p.grad = torch.from_numpy(g * s)
+    total = torch.nn.utils.clip_grad_norm_(params, max_norm).item()
+    norm = orc.grad_norm(gs, s)
+    assert abs(norm - total) <= 1e-14 * total
+    c = orc.clip_coef(norm, max_norm)
+    assert (c == 1.0) == (max_norm >= norm)
+    for p, g in zip(params, gs):
+        assert np.allclose(g * s * c, p.grad.numpy(), rtol=1e-14, atol=0)  # torch: norm of per-tensor norms
+
+
+def test_clip_coef_special_cases(orc):
+    assert orc.clip_coef(5.0, 0.0) == 1.0          # no clipping requested
+    assert orc.clip_coef(5.0, float("inf")) == 1.0
+    assert orc.clip_coef(float("inf"), 1.0) == 1.0  # step skipped anyway
+    assert orc.clip_coef(float("nan"), 1.0) == 1.0
+    assert orc.clip_coef(0.0, 1.0) == 1.0
+    assert orc.clip_coef(4.0, 2.0) == 2.0 / (4.0 + 1e-6)
+
+
+def test_scaler_update_matches_torch(orc):
+    """Referee: torch._amp_update_scale_ on CPU float32 (GradScaler's update)
+    over a fixed pattern of clean and overflowing steps, including growth to
+    +inf (not applied) and backoff from a large scale: scale and count equal
+    after every iteration, bit for bit."""
+    pattern = [0, 0, 0, 1, 0, 0, 0, 0, 0, 0, 1, 1, 0, 0, 0, 0, 0, 0, 0, 0]
+    for scale0, growth, backoff, interval in ((65536.0, 2.0, 0.5, 3), (2.0 ** 126, 2.0, 0.5, 2),
+                                               (3.0, 1.7, 0.3, 1)):
+        st = orc.ScalerState(scale0)
+        ts = torch.tensor([scale0], dtype=torch.float32)
+        tg = torch.tensor([0], dtype=torch.int32)
+        for f in pattern:
+            st.update(bool(f), growth, backoff, interval)
+            torch._amp_update_scale_(ts, tg, torch.tensor([float(f)]), growth, backoff, interval)
+            assert st.scale.view(np.uint32)[0] == ts.numpy().view(np.uint32)[0], (scale0, f)
+            assert st.tracker[0] == tg.item()
+
+
+def test_scaler_update_closed_form(orc):
+    """k clean steps from scale S0 with interval N and growth 2 give
+    S0 * 2^floor(k/N) and count k mod N; one overflow halves the scale and
+    resets the count."""
+    st = orc.ScalerState(1024.0)
+    for k in range(1, 26):
+        st.update(False, 2.0, 0.5, 4)
+        assert st.scale[0] == 1024.0 * 2 ** (k // 4) and st.tracker[0] == k % 4
+    st.update(True, 2.0, 0.5, 4)
+    assert st.scale[0] == 1024.0 * 2 ** 6 / 2 and st.tracker[0] == 0
