@@ -8,7 +8,9 @@ per-step scalars, moments, bias correction, decay, update).  `value` is
 optimizer element-updates per second with all inputs resident in HBM.
 
 Secondary workloads (same JSON line, "secondary"): the 1M-element tensor,
-the Llama-shaped 1.1B bf16+remainder AMP list with device cosine lr, the
+the Llama-shaped 1.1B bf16+remainder AMP list with device cosine lr (also
+timed as the full AMP loop with global-norm clipping folded into the step
+and the dynamic loss-scale update), the
 268M-element blockwise 8-bit and 4-bit states, and Adam-mini over the 7B
 list.  Gradients are drawn once per workload, outside the timed region.
 
@@ -39,6 +41,7 @@ B_ADEMAMIX_F32 = 36.0         # + m2 read and write
 B_BF16R_AMP = 26.0 + 2.0      # R bf16 p, int16 r, bf16 g, m, v (14) + W (12); + finite check g
 B_8BIT = 4 + 4 + 1 + 1 + 8 / 256 + 4 + 1 + 1 + 8 / 256
 B_4BIT = 4 + 4 + 0.5 + 0.5 + 8 / 128 + 4 + 0.5 + 0.5 + 8 / 128
+CLIP_MAX_NORM = 1.0           # global-norm clip of the Llama 1.1B AMP loop
 
 
 def log(*a):
@@ -215,6 +218,25 @@ def bench_c3(torch, osa, synth, steps, warmup):
         osa.optim_step_adamw(plan.handle, h, s["lr"], s["inv_scale"], s["found_inf"], s["step"])
 
     ms, per_call, _ = run_timed(torch, [finite, step], steps, warmup)
+
+    # the same list in the full AMP loop with clipping folded into the step:
+    # check + global norm (one read of the grads), clipped step, scale update
+    scale_dev = torch.tensor([scale], dtype=torch.float32, device="cuda")
+    tracker = torch.zeros(1, dtype=torch.int32, device="cuda")
+    norm = torch.zeros(1, dtype=torch.float32, device="cuda")
+    clip = torch.zeros(1, dtype=torch.float32, device="cuda")
+
+    def check_norm():
+        s["found_inf"].zero_()
+        osa.optim_grad_norm(plan.handle, s["inv_scale"], CLIP_MAX_NORM, s["found_inf"], norm, clip)
+
+    def clipped_step():
+        osa.optim_step_adamw(plan.handle, h, s["lr"], clip, s["found_inf"], s["step"])
+
+    def scaler():
+        osa.optim_scaler_update(scale_dev, s["inv_scale"], tracker, s["found_inf"], 2.0, 0.5, 2000)
+
+    ms_c, per_c, _ = run_timed(torch, [check_norm, clipped_step, scaler], steps, warmup)
     plan.close()
     del A, G
     torch.cuda.empty_cache()
@@ -222,7 +244,13 @@ def bench_c3(torch, osa, synth, steps, warmup):
     return dict(workload=wl.name, elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
                 gbs=gbs(b, ms), frac=gbs(b, ms) / PEAK_HBM_GBS,
                 kernels={"check_finite_bf16": dict(ms=per_call[0], gbs=gbs(2.0 * n, per_call[0])),
-                         "adamw_bf16_remainder": dict(ms=per_call[1], gbs=gbs(26.0 * n, per_call[1]))})
+                         "adamw_bf16_remainder": dict(ms=per_call[1], gbs=gbs(26.0 * n, per_call[1]))},
+                amp_clip_loop=dict(
+                    ms_per_step=ms_c, elements_per_s=n / (ms_c * 1e-3), gbs=gbs(b, ms_c),
+                    frac=gbs(b, ms_c) / PEAK_HBM_GBS, max_norm=CLIP_MAX_NORM,
+                    kernels={"check_and_norm_bf16": dict(ms=per_c[0], gbs=gbs(2.0 * n, per_c[0])),
+                             "adamw_bf16_remainder_clipped": dict(ms=per_c[1], gbs=gbs(26.0 * n, per_c[1])),
+                             "scaler_update": dict(ms=per_c[2])}))
 
 
 def bench_c4(torch, osa, synth, steps, warmup):

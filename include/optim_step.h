@@ -229,6 +229,40 @@ int optim_step_8bit_blockwise(optim_plan *plan, const optim_adamw_hp *hp,
  * leaves it unchanged, so the caller zeroes it first.                     */
 int optim_check_finite(optim_plan *plan, float *found_inf_dev, void *stream);
 
+/* Gradient clipping folded into the fused step ([LTN] analysis: unscale_
+ * before step exists so that gradients can be clipped, and a fused step
+ * that unscales inside must not receive already-unscaled gradients).  One
+ * read of every gradient of the plan: as optim_check_finite it ORs 1.0f
+ * into *found_inf_dev on a NaN / +-Inf, and it sums G^2 (the stored, scaled
+ * gradients; fp32 per lane, fp64 per workgroup and across workgroups in a
+ * fixed order).  Then, with s = *inv_scale_dev (NULL: 1):
+ *   *norm_dev           = sqrt(sum G^2) * s, the global L2 norm of the
+ *                         unscaled gradients (norm_dev may be NULL);
+ *   *clip_inv_scale_dev = s * min(1, max_norm / (norm + 1e-6)),
+ * to be passed as the inv_scale of the step that follows.  max_norm <= 0
+ * or +inf means no clipping (clip = s); NaN is EINVAL.  When the norm is
+ * not finite, clip = s (found_inf is set and the step skips).  Uses the
+ * plan's workspace (partial sums): do not overlap it with a step of the
+ * same plan on another stream.                                             */
+int optim_grad_norm(optim_plan *plan, const float *inv_scale_dev,
+                    double max_norm, float *found_inf_dev, float *norm_dev,
+                    float *clip_inv_scale_dev, void *stream);
+
+/* Dynamic loss scale, once per loop iteration after the step ([LTN]: the
+ * loop ends with the scaler's update; rule as GradScaler documents it).
+ * If *found_inf_dev != 0: scale *= backoff_factor, tracker = 0.  Else
+ * tracker += 1, and when it reaches growth_interval: scale *= growth_factor
+ * (kept only if finite) and tracker = 0.  Products in double, rounded once
+ * to the stored float.  If inv_scale_dev is not NULL it receives
+ * fl32(1/scale) (exact for power-of-two scales), ready for the next step.
+ * growth_factor > 1 (finite), 0 < backoff_factor < 1, growth_interval >= 1,
+ * else EINVAL.                                                              */
+int optim_scaler_update(float *scale_dev, float *inv_scale_dev,
+                        int32_t *growth_tracker_dev,
+                        const float *found_inf_dev, double growth_factor,
+                        double backoff_factor, int32_t growth_interval,
+                        void *stream);
+
 /* Blockwise quantize / dequantize of a plain fp32 device array with the
  * codebook, bits and block of a blockwise `plan`, by the same device code as
  * optim_step_8bit_blockwise: for importing fp32 optimizer state into codes

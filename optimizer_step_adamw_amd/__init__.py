@@ -27,7 +27,7 @@ EXPORTED = (
     "optim_plan_set_schedule", "optim_step_adamw", "optim_step_ademamix", "optim_step_adam_mini",
     "optim_step_8bit_blockwise", "optim_check_finite", "optim_remainder_split",
     "optim_remainder_reconstruct", "optim_quant_codebook", "optim_quantize_blockwise",
-    "optim_dequantize_blockwise",
+    "optim_dequantize_blockwise", "optim_grad_norm", "optim_scaler_update",
 )
 
 
@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
             "optim_quant_codebook": ([i32, i32, _P, _P], i32),
             "optim_quantize_blockwise": ([_P, i32, _P, i64, _P, _P, _P], i32),
             "optim_dequantize_blockwise": ([_P, i32, _P, _P, i64, _P, _P], i32),
+            "optim_grad_norm": ([_P, _P, f64, _P, _P, _P, _P], i32),
+            "optim_scaler_update": ([_P, _P, _P, _P, f64, f64, i32, _P], i32),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -228,6 +230,19 @@ def optim_step_8bit_blockwise(plan, hp: optim_adamw_hp, bits: int, block: int, l
 
 def optim_check_finite(plan, found_inf_dev, stream=None) -> None:
     _check(lib().optim_check_finite(plan, _ptr(found_inf_dev), _stream(stream)), "optim_check_finite")
+
+
+def optim_grad_norm(plan, inv_scale_dev, max_norm: float, found_inf_dev, norm_dev, clip_inv_scale_dev,
+                    stream=None) -> None:
+    _check(lib().optim_grad_norm(plan, _ptr(inv_scale_dev), float(max_norm), _ptr(found_inf_dev),
+                                 _ptr(norm_dev), _ptr(clip_inv_scale_dev), _stream(stream)), "optim_grad_norm")
+
+
+def optim_scaler_update(scale_dev, inv_scale_dev, growth_tracker_dev, found_inf_dev, growth_factor: float,
+                        backoff_factor: float, growth_interval: int, stream=None) -> None:
+    _check(lib().optim_scaler_update(_ptr(scale_dev), _ptr(inv_scale_dev), _ptr(growth_tracker_dev),
+                                     _ptr(found_inf_dev), float(growth_factor), float(backoff_factor),
+                                     int(growth_interval), _stream(stream)), "optim_scaler_update")
 
 
 def optim_remainder_split(master, bf16, rem, n: int, stream=None) -> None:

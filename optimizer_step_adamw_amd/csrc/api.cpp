@@ -95,6 +95,8 @@ struct Built {
     std::vector<double> group_wd;
     int64_t nunits = 0;
     int64_t tile = 0;
+    int32_t grid = 0;        // requested persistent workgroups
+    int64_t npartials = 0;   // capacity of the partials region
     int32_t nblocks = 0;
     Layout L{};
 };
@@ -140,6 +142,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
                                                 : "4-bit block must be 128, 256 or 512");
     }
     if (opts && opts->grid < 0) return fail(OPTIM_EINVAL, "negative grid");
+    B.grid = opts ? opts->grid : 0;
     if (opts && opts->tile < 0) return fail(OPTIM_EINVAL, "negative tile");
     // measured on MI355X: 2048 elements per workgroup (two groups of 4 per
     // lane, loaded at once) stream best for AdamW / AdEMAMix, Adam-mini
@@ -307,8 +310,13 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     L.spans = off; off += align256(B.spans.size() * sizeof(SpanDesc));
     L.codebook = off; off += algo == OPTIM_ALGO_BLOCKWISE ? align256(sizeof(Codebook)) : 0;
     L.blockspan = off; off += align256(std::max<size_t>(1, B.blockspan.size()) * sizeof(int32_t));
+    // partial sums: Adam-mini's block sums (one per unit) and the gradient
+    // norm pass (one per workgroup) share the region; they never overlap in
+    // stream order
     L.partials = off;
-    off += algo == OPTIM_ALGO_ADAM_MINI ? align256(std::max<int64_t>(1, B.nunits) * sizeof(double)) : 0;
+    B.npartials = std::max<int64_t>(algo == OPTIM_ALGO_ADAM_MINI ? B.nunits : 0,
+                                    norm_partials(B.nunits, B.tile, B.grid));
+    off += align256(std::max<int64_t>(1, B.npartials) * sizeof(double));
     L.blockfac = off; off += align256(std::max<int32_t>(1, B.nblocks) * sizeof(float));
     L.total = off;
     return OPTIM_OK;
@@ -325,6 +333,7 @@ struct optim_plan {
     int32_t nspans, nblocks, ngroups;
     int64_t nunits;
     int64_t tile;
+    int64_t npartials;
     char *ws;
     Layout L;
     int32_t sched;
@@ -398,6 +407,7 @@ int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_p
     P->ngroups = (int32_t)B.group_wd.size();
     P->nunits = B.nunits;
     P->tile = B.tile;
+    P->npartials = B.npartials;
     P->ws = static_cast<char *>(workspace);
     P->L = B.L;
     P->sched = OPTIM_SCHED_NONE;
@@ -445,6 +455,7 @@ StepArgs step_args(optim_plan *P) {
     a.nunits = P->nunits;
     a.tile = P->tile;
     a.partials = reinterpret_cast<double *>(P->ws + P->L.partials);
+    a.npartials = P->npartials;
     a.blockfac = reinterpret_cast<float *>(P->ws + P->L.blockfac);
     a.blockspan = reinterpret_cast<const int32_t *>(P->ws + P->L.blockspan);
     a.nblocks = P->nblocks;
@@ -572,6 +583,40 @@ int optim_check_finite(optim_plan *plan, float *found_inf_dev, void *stream) {
     a.commit = 0;
     a.found_inf = found_inf_dev;
     HIP_OK(launch_check_finite(a, plan->gk, static_cast<hipStream_t>(stream)));
+    return OPTIM_OK;
+}
+
+int optim_grad_norm(optim_plan *plan, const float *inv_scale_dev, double max_norm, float *found_inf_dev,
+                    float *norm_dev, float *clip_inv_scale_dev, void *stream) {
+    if (!plan) return fail(OPTIM_EINVAL, "plan is NULL");
+    if (!found_inf_dev || !aligned(found_inf_dev, 4))
+        return fail(OPTIM_EINVAL, "found_inf_dev must be an aligned device float");
+    if (!clip_inv_scale_dev || !aligned(clip_inv_scale_dev, 4))
+        return fail(OPTIM_EINVAL, "clip_inv_scale_dev must be an aligned device float");
+    if (!aligned(inv_scale_dev, 4) || !aligned(norm_dev, 4)) return fail(OPTIM_EALIGN, "scalar pointer misaligned");
+    if (std::isnan(max_norm)) return fail(OPTIM_EINVAL, "max_norm is NaN");
+    StepArgs a = step_args(plan);
+    a.commit = 0;
+    a.found_inf = found_inf_dev;
+    HIP_OK(launch_grad_norm(a, plan->gk, inv_scale_dev, max_norm, norm_dev, clip_inv_scale_dev,
+                            static_cast<hipStream_t>(stream)));
+    return OPTIM_OK;
+}
+
+int optim_scaler_update(float *scale_dev, float *inv_scale_dev, int32_t *growth_tracker_dev,
+                        const float *found_inf_dev, double growth_factor, double backoff_factor,
+                        int32_t growth_interval, void *stream) {
+    if (!scale_dev || !growth_tracker_dev || !found_inf_dev)
+        return fail(OPTIM_EINVAL, "scale, growth tracker and found_inf are required");
+    if (!aligned(scale_dev, 4) || !aligned(inv_scale_dev, 4) || !aligned(growth_tracker_dev, 4) ||
+        !aligned(found_inf_dev, 4))
+        return fail(OPTIM_EALIGN, "scalar pointer misaligned");
+    if (!(growth_factor > 1.0) || !std::isfinite(growth_factor))
+        return fail(OPTIM_EINVAL, "growth_factor must be finite and > 1");
+    if (!(backoff_factor > 0.0 && backoff_factor < 1.0)) return fail(OPTIM_EINVAL, "backoff_factor must be in (0, 1)");
+    if (growth_interval < 1) return fail(OPTIM_EINVAL, "growth_interval must be >= 1");
+    HIP_OK(launch_scaler_update(scale_dev, inv_scale_dev, growth_tracker_dev, found_inf_dev, growth_factor,
+                                backoff_factor, growth_interval, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
 

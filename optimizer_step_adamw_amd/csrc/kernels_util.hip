@@ -11,14 +11,16 @@ namespace {
 // consecutive units, merged into one walk where they are contiguous).
 // Measured on MI355X: bf16 gradients stream best with 8 groups of 4 per lane
 // in flight (7.4 TB/s), fp32 with one group at a time (7.0 TB/s).
-template <int GK>
-__device__ __forceinline__ bool any_nonfinite(const TensorDesc &T, int64_t start, int64_t len) {
+// NORM: the same pass also sums the squares of the (scaled) gradients, per
+// lane in fp32 and per workgroup in fp64, into partials[workgroup].
+template <int GK, bool NORM>
+__device__ __forceinline__ bool scan_grads(const TensorDesc &T, int64_t start, int64_t len, float &acc) {
     constexpr int G = GK == G_F32 ? 1 : 8;
     bool bad = false;
     lane_walk<G>(start, len, T.vec_ok, [&](auto n, int64_t e) {
         constexpr int N = decltype(n)::value;
+        float x[N];
         if constexpr (GK == G_F32) {
-            float x[N];
             ldf<N>(static_cast<const float *>(T.g), e, x);
 #pragma unroll
             for (int i = 0; i < N; ++i) bad |= (__float_as_uint(x[i]) & 0x7F800000u) == 0x7F800000u;
@@ -26,15 +28,23 @@ __device__ __forceinline__ bool any_nonfinite(const TensorDesc &T, int64_t start
             uint32_t w[N];
             ldh<N>(static_cast<const uint16_t *>(T.g), e, w);
 #pragma unroll
-            for (int i = 0; i < N; ++i) bad |= (w[i] & 0x7F80u) == 0x7F80u;
+            for (int i = 0; i < N; ++i) {
+                bad |= (w[i] & 0x7F80u) == 0x7F80u;
+                x[i] = bf16_to_f32(w[i]);
+            }
+        }
+        if constexpr (NORM) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) acc += x[i] * x[i];
         }
     });
     return bad;
 }
 
-template <int GK>
+template <int GK, bool NORM>
 __global__ __launch_bounds__(kThreads) void finite_kernel(StepArgs a) {
     bool bad = false;
+    float acc = 0.0f;
     int tensor = -1;
     int64_t start = 0, len = 0;
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t s, int64_t l) {
@@ -42,13 +52,106 @@ __global__ __launch_bounds__(kThreads) void finite_kernel(StepArgs a) {
             len += l;
             return;
         }
-        if (len > 0) bad |= any_nonfinite<GK>(a.tensors[tensor], start, len);
+        if (len > 0) bad |= scan_grads<GK, NORM>(a.tensors[tensor], start, len, acc);
         tensor = sp.tensor;
         start = s;
         len = l;
     });
-    if (len > 0) bad |= any_nonfinite<GK>(a.tensors[tensor], start, len);
+    if (len > 0) bad |= scan_grads<GK, NORM>(a.tensors[tensor], start, len, acc);
     if (bad) *a.found_inf = 1.0f;
+    if constexpr (NORM) {
+        __shared__ double red[kThreads / 64];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = (double)acc;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double t = 0.0;
+#pragma unroll
+            for (int w = 0; w < kThreads / 64; ++w) t += red[w];
+            a.partials[blockIdx.x] = t;
+        }
+    }
+}
+
+// The partial sums are added in a fixed order in two stages: workgroup w of
+// stage 1 sums partials [w*kNormChunk, (w+1)*kNormChunk) (16 independent
+// loads per lane) into partials2[w]; one workgroup then sums partials2 and
+// derives
+//   norm = sqrt(sum G^2) * s                 (the norm of the unscaled G s)
+//   clip = s * min(1, max_norm / (norm + 1e-6))
+// with s = *inv_scale (1 if absent).  No clipping when max_norm <= 0 or is
+// +inf, or when the norm is not finite (found_inf is set and the step that
+// reads clip is skipped).
+constexpr int kNormPerLane = 16;
+constexpr int64_t kNormChunk = (int64_t)kThreads * kNormPerLane;
+
+__device__ __forceinline__ double block_sum(double x, double *red) {
+    red[threadIdx.x] = x;
+    __syncthreads();
+    for (int st = kThreads / 2; st > 0; st >>= 1) {
+        if ((int)threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
+        __syncthreads();
+    }
+    return red[0];
+}
+
+__global__ __launch_bounds__(kThreads) void norm_stage1_kernel(const double *partials, int64_t n,
+                                                                double *partials2) {
+    __shared__ double red[kThreads];
+    const int64_t base = (int64_t)blockIdx.x * kNormChunk + threadIdx.x;
+    double v[kNormPerLane];
+#pragma unroll
+    for (int j = 0; j < kNormPerLane; ++j) {
+        const int64_t i = base + (int64_t)j * kThreads;
+        v[j] = i < n ? partials[i] : 0.0;
+    }
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < kNormPerLane; ++j) acc += v[j];
+    const double t = block_sum(acc, red);
+    if (threadIdx.x == 0) partials2[blockIdx.x] = t;
+}
+
+__global__ __launch_bounds__(kThreads) void norm_finalize_kernel(const double *partials2, int64_t n2,
+                                                                  const float *inv_scale, double max_norm,
+                                                                  float *norm_out, float *clip_out) {
+    __shared__ double red[kThreads];
+    double acc = 0.0;
+    for (int64_t i = threadIdx.x; i < n2; i += kThreads) acc += partials2[i];
+    const double total = block_sum(acc, red);
+    if (threadIdx.x == 0) {
+        const double s = inv_scale ? (double)*inv_scale : 1.0;
+        const double norm = sqrt(total) * fabs(s);
+        double coef = 1.0;
+        if (max_norm > 0.0 && isfinite(max_norm) && isfinite(norm)) {
+            const double c = max_norm / (norm + 1e-6);
+            coef = c < 1.0 ? c : 1.0;
+        }
+        if (norm_out) *norm_out = (float)norm;
+        *clip_out = (float)(s * coef);
+    }
+}
+
+// Dynamic loss scale: backoff on a non-finite step (count reset), growth
+// after `interval` clean steps (kept only if finite); each product in double,
+// rounded once to the stored float.  inv_scale, if given, becomes 1/scale.
+__global__ void scaler_kernel(float *scale, float *inv_scale, int32_t *tracker, const float *found_inf,
+                              double growth, double backoff, int32_t interval) {
+    if (threadIdx.x != 0) return;
+    float S = *scale;
+    int32_t k = *tracker;
+    if (*found_inf != 0.0f) {
+        S = (float)((double)S * backoff);
+        k = 0;
+    } else if (++k >= interval) {
+        const float grown = (float)((double)S * growth);
+        if (isfinite(grown)) S = grown;
+        k = 0;
+    }
+    *scale = S;
+    *tracker = k;
+    if (inv_scale) *inv_scale = (float)(1.0 / (double)S);
 }
 
 // ---------------------------------------------------------------- remainder utils
@@ -78,17 +181,62 @@ int flat_grid(int64_t n) {
 
 }  // namespace
 
+// Without a persistent grid, a finite-check / norm workgroup takes
+// kFiniteCheckElems consecutive elements (that many / tile units).
+static int32_t finite_units_per_wg(int64_t tile) {
+    return (int32_t)(tile >= kFiniteCheckElems ? 1 : kFiniteCheckElems / tile);
+}
+
+int64_t finite_pass_grid(int64_t nunits, int64_t tile, int32_t grid_request) {
+    const int64_t units = nunits > 0 ? nunits : 1;
+    if (grid_request > 0) return grid_request < units ? grid_request : units;
+    const int64_t upw = finite_units_per_wg(tile);
+    return (units + upw - 1) / upw;
+}
+
+int64_t norm_partials(int64_t nunits, int64_t tile, int32_t grid_request) {
+    const int64_t g = finite_pass_grid(nunits, tile, grid_request);
+    return g + (g + kNormChunk - 1) / kNormChunk;
+}
+
 hipError_t launch_check_finite(const StepArgs &args, int gk, hipStream_t s) {
-    // a read-only scan streams best with ~8192 elements per workgroup
     StepArgs a = args;
-    a.units_per_wg = (int32_t)(a.tile >= kFiniteCheckElems ? 1 : kFiniteCheckElems / a.tile);
+    a.units_per_wg = finite_units_per_wg(a.tile);
     if (gk == G_F32)
-        LAUNCH_PERSISTENT((finite_kernel<G_F32>), a, s);
+        LAUNCH_PERSISTENT((finite_kernel<G_F32, false>), a, s);
     else
-        LAUNCH_PERSISTENT((finite_kernel<G_BF16>), a, s);
+        LAUNCH_PERSISTENT((finite_kernel<G_BF16, false>), a, s);
     return hipGetLastError();
 }
 
+hipError_t launch_grad_norm(const StepArgs &args, int gk, const float *inv_scale, double max_norm,
+                            float *norm_out, float *clip_out, hipStream_t s) {
+    StepArgs a = args;
+    a.units_per_wg = finite_units_per_wg(a.tile);
+    const int64_t grid = finite_pass_grid(a.nunits, a.tile, a.grid_request);
+    const int64_t grid1 = (grid + kNormChunk - 1) / kNormChunk;
+    if (grid + grid1 > a.npartials || grid != persistent_grid(0, a)) return hipErrorInvalidValue;
+    if (gk == G_F32)
+        LAUNCH_PERSISTENT((finite_kernel<G_F32, true>), a, s);
+    else
+        LAUNCH_PERSISTENT((finite_kernel<G_BF16, true>), a, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    double *partials2 = a.partials + grid;
+    hipLaunchKernelGGL(norm_stage1_kernel, dim3((unsigned)grid1), dim3(kThreads), 0, s, a.partials, grid, partials2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(kThreads), 0, s, partials2, grid1, inv_scale, max_norm,
+                       norm_out, clip_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_scaler_update(float *scale, float *inv_scale, int32_t *tracker, const float *found_inf,
+                                double growth, double backoff, int32_t interval, hipStream_t s) {
+    hipLaunchKernelGGL(scaler_kernel, dim3(1), dim3(64), 0, s, scale, inv_scale, tracker, found_inf, growth,
+                       backoff, interval);
+    return hipGetLastError();
+}
 
 hipError_t launch_remainder_split(const float *x, uint16_t *b, int16_t *r, int64_t n,
                                   hipStream_t s) {

@@ -131,7 +131,9 @@ struct StepArgs {
     int32_t nspans;
     int64_t nunits;
     int64_t tile;             // elements per unit
-    double *partials;         // Adam-mini: one per unit
+    double *partials;         // Adam-mini: one per unit; gradient norm:
+                              // one per workgroup
+    int64_t npartials;        // capacity of partials
     float *blockfac;          // Adam-mini: per block lr/bc1/h
     const int32_t *blockspan; // Adam-mini: span index of each block
     int32_t nblocks;
@@ -152,6 +154,14 @@ hipError_t launch_ademamix(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_adam_mini(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_blockwise(const StepArgs &a, int gk, hipStream_t s);
 hipError_t launch_check_finite(const StepArgs &a, int gk, hipStream_t s);
+// Workgroups of the finite check / gradient norm pass for a plan.
+int64_t finite_pass_grid(int64_t nunits, int64_t tile, int32_t grid_request);
+// Partial sums the gradient norm pass needs (both reduction stages).
+int64_t norm_partials(int64_t nunits, int64_t tile, int32_t grid_request);
+hipError_t launch_grad_norm(const StepArgs &a, int gk, const float *inv_scale, double max_norm,
+                            float *norm_out, float *clip_out, hipStream_t s);
+hipError_t launch_scaler_update(float *scale, float *inv_scale, int32_t *tracker, const float *found_inf,
+                                double growth, double backoff, int32_t interval, hipStream_t s);
 hipError_t launch_quantize(const Codebook *cb, int bits, int block, int is_signed, const float *x,
                            int64_t n, uint8_t *codes, float *absmax, hipStream_t s);
 hipError_t launch_dequantize(const Codebook *cb, int bits, int block, int is_signed, const uint8_t *codes,

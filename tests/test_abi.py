@@ -27,7 +27,7 @@ def header_functions():
 
 def test_exports_every_declared_function(L):
     declared = header_functions()
-    assert len(declared) == 15, declared
+    assert len(declared) == 17, declared
     assert sorted(osa.EXPORTED) == declared
     for name in declared:
         assert hasattr(L, name), name
@@ -146,6 +146,17 @@ def test_tile_bounds(L):
     assert ws(fake_list([n], fake=f, **kw), osa.OPTIM_ALGO_BLOCKWISE, osa.optim_plan_opts(8, 256, 0, 2048)) > 0
     expect_error(osa.OPTIM_EINVAL, lambda: ws(
         fake_list([n], fake=f, **kw), osa.OPTIM_ALGO_BLOCKWISE, osa.optim_plan_opts(8, 256, 0, 1024)))
+
+
+def test_scaler_and_norm_validation_without_device(L):
+    """Argument errors come back before any device work."""
+    a = 1 << 40
+    expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_scaler_update(None, None, a, a, 2.0, 0.5, 10, 0))
+    expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_scaler_update(a, None, a, a, 1.0, 0.5, 10, 0))
+    expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_scaler_update(a, None, a, a, 2.0, 1.0, 10, 0))
+    expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_scaler_update(a, None, a, a, 2.0, 0.5, 0, 0))
+    expect_error(osa.OPTIM_EALIGN, lambda: osa.optim_scaler_update(a + 2, None, a, a, 2.0, 0.5, 10, 0))
+    expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_grad_norm(None, None, 1.0, a, None, a, 0))
 
 
 def test_null_plan_is_rejected_without_device(L):
