@@ -61,6 +61,8 @@ _SIGS = {
     "oracle_unpack_nibbles": [_i64, _p, _p],
     "oracle_blockwise_step": [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p,
                               _d, _d, _d, _d, _d, _i64, _p, _p],
+    "oracle_blockwise_ademamix_step": [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
+                                       _d, _d, _d, _d, _d, _d, _d, _i64, _p, _p, _p],
     "oracle_sumsq": [_i64, _p],
     "oracle_clip_coef": [_d, _d],
     "oracle_scaler_update": [_p, _p, _i32, _d, _d, _i32],
@@ -285,6 +287,20 @@ def blockwise_step(p, g_f32, qm, qv, am, av, bits, block, lr, beta1, beta2, eps,
                                 _ptr(am), _ptr(av), lr, beta1, beta2, eps, wd, t,
                                 _ptr(sm), _ptr(sv))
     return sm, sv  # the fp32 states before requantization
+
+
+def blockwise_ademamix_step(p, g_f32, qm, qm2, qv, am, am2, av, bits, block, lr, beta1, beta2,
+                            beta3, alpha, eps, wd, t):
+    """Blockwise 8-bit/4-bit AdEMAMix step (m1, m2 signed, nu unsigned); codes
+    unpacked, in place.  Returns the fp32 states before requantization."""
+    n = p.size
+    g = np.ascontiguousarray(g_f32, np.float32).ravel()
+    sm, sm2, sv = (np.empty(n, np.float32) for _ in range(3))
+    lib().oracle_blockwise_ademamix_step(n, block, bits, _ptr(p), _ptr(g), _ptr(qm), _ptr(qm2),
+                                         _ptr(qv), _ptr(am), _ptr(am2), _ptr(av), lr, beta1,
+                                         beta2, beta3, alpha, eps, wd, t, _ptr(sm), _ptr(sm2),
+                                         _ptr(sv))
+    return sm, sm2, sv
 
 
 # --------------------------------------------------------------------------

@@ -429,3 +429,54 @@ void oracle_blockwise_step(int64_t n, int64_t block, int bits, double *p,
     oracle_quantize(n, block, bm, 1, scratch_m, Tm, qm, am);
     oracle_quantize(n, block, bv, 0, scratch_v, Tv, qv, av);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Blockwise-quantized AdEMAMix (three states).  [BNB] PR description and the
+ * review's confirmation of the 8-bit blockwise site: the 2-state blockwise
+ * kernel has an AdEMAMix branch, which takes the same Algorithm 2 decay
+ * order; PR body: on a fresh step AdEMAMix mixes in alpha*(1-beta3)*g.
+ * States: m1 and m2 with the signed map, nu with the unsigned map, each with
+ * its own absmax per block.  fp32-faithful state recipe as in
+ * oracle_blockwise_step, with m2 = fl32(fl32(b3*m2~) + fl32(c3*g)),
+ * b3 = fl32(beta3), c3 = fl32(1-beta3).  The parameter update uses the fp32
+ * states in double: p <- p(1-lr wd) - lr (m1/bc1 + alpha m2)/h, m2 not
+ * bias-corrected, as oracle_ademamix_step.  Then all three requantize.      */
+void oracle_blockwise_ademamix_step(int64_t n, int64_t block, int bits, double *p,
+                                    const float *g, uint8_t *qm, uint8_t *qm2, uint8_t *qv,
+                                    float *am, float *am2, float *av, double lr, double beta1,
+                                    double beta2, double beta3, double alpha, double eps,
+                                    double wd, int64_t t, float *scratch_m, float *scratch_m2,
+                                    float *scratch_v)
+{
+    int bm = bits - 1, bv = bits;
+    float Mm[256], Tm[256], Mv[256], Tv[256];
+    oracle_dynamic_map(bm, Mm);
+    oracle_thresholds(1 << bm, Mm, Tm);
+    oracle_dynamic_map(bv, Mv);
+    oracle_thresholds(1 << bv, Mv, Tv);
+
+    double b1 = F32(beta1), c1 = F32(1.0 - beta1);
+    double b2 = F32(beta2), c2 = F32(1.0 - beta2);
+    double b3 = F32(beta3), c3 = F32(1.0 - beta3);
+    double bc1 = 1.0 - pow(beta1, (double)t);
+    double bc2 = 1.0 - pow(beta2, (double)t);
+
+    oracle_dequantize(n, block, bm, 1, qm, Mm, am, scratch_m);
+    oracle_dequantize(n, block, bm, 1, qm2, Mm, am2, scratch_m2);
+    oracle_dequantize(n, block, bv, 0, qv, Mv, av, scratch_v);
+    for (int64_t i = 0; i < n; ++i) {
+        double gi = (double)g[i];
+        double mi = F32(F32(b1 * (double)scratch_m[i]) + F32(c1 * gi));
+        double m2i = F32(F32(b3 * (double)scratch_m2[i]) + F32(c3 * gi));
+        double vi = F32(F32(b2 * (double)scratch_v[i]) + F32(c2 * F32(gi * gi)));
+        scratch_m[i] = (float)mi;
+        scratch_m2[i] = (float)m2i;
+        scratch_v[i] = (float)vi;
+        p[i] = p[i] * (1.0 - lr * wd);
+        double h = sqrt(vi) / sqrt(bc2) + eps;
+        p[i] = p[i] - lr * (mi / bc1 + alpha * m2i) / h;
+    }
+    oracle_quantize(n, block, bm, 1, scratch_m, Tm, qm, am);
+    oracle_quantize(n, block, bm, 1, scratch_m2, Tm, qm2, am2);
+    oracle_quantize(n, block, bv, 0, scratch_v, Tv, qv, av);
+}

@@ -137,6 +137,22 @@ MUTANTS = [
      ["test_absmax_element_roundtrips"]),
     ("nibble_order_swapped", "packed[i] = (uint8_t)(lo | (hi << 4));",
      "packed[i] = (uint8_t)(hi | (lo << 4));", ["test_nibble_packing_layout"]),
+    # ---- blockwise AdEMAMix
+    ("blockwise_ademamix_decay_after_update",
+     "        p[i] = p[i] * (1.0 - lr * wd);\n        double h = sqrt(vi) / sqrt(bc2) + eps;\n"
+     "        p[i] = p[i] - lr * (mi / bc1 + alpha * m2i) / h;",
+     "        double h = sqrt(vi) / sqrt(bc2) + eps;\n"
+     "        p[i] = (p[i] - lr * (mi / bc1 + alpha * m2i) / h) * (1.0 - lr * wd);",
+     ["test_blockwise_ademamix_fresh_step"]),
+    ("blockwise_ademamix_m2_with_beta1",
+     "double m2i = F32(F32(b3 * (double)scratch_m2[i]) + F32(c3 * gi));",
+     "double m2i = F32(F32(b1 * (double)scratch_m2[i]) + F32(c1 * gi));",
+     ["test_blockwise_ademamix_fresh_step"]),
+    ("blockwise_ademamix_m2_unsigned_map", "oracle_quantize(n, block, bm, 1, scratch_m2, Tm, qm2, am2);",
+     "oracle_quantize(n, block, bv, 0, scratch_m2, Tv, qm2, am2);", ["test_blockwise_ademamix_fresh_step"]),
+    ("blockwise_ademamix_m1_bias_uncorrected", "p[i] = p[i] - lr * (mi / bc1 + alpha * m2i) / h;",
+     "p[i] = p[i] - lr * (mi + alpha * m2i) / h;",
+     ["test_blockwise_ademamix_fresh_step", "test_blockwise_ademamix_alpha_zero_is_blockwise_adamw"]),
     # ---- gradient clipping and loss scale
     ("sumsq_of_magnitudes", "        s += x[i] * x[i];\n    return s;", "        s += fabs(x[i]);\n    return s;",
      ["test_grad_norm_library_and_closed_form", "test_clip_matches_torch_clip_grad_norm"]),
@@ -159,12 +175,15 @@ MUTANTS = [
      "        double h = sqrt(vi) / sqrt(bc2) + eps;\n"
      "        p[i] = (p[i] - (lr / bc1) * mi / h) * (1.0 - lr * wd);",
      ["test_blockwise_fresh_step"]),
-    ("blockwise_v_of_g_not_g_squared", "F32(c2 * F32(gi * gi))", "F32(c2 * fabs(gi))",
+    ("blockwise_v_of_g_not_g_squared", "F32(c2 * F32(gi * gi)));\n        scratch_m[i] = (float)mi;\n        scratch_v",
+     "F32(c2 * fabs(gi)));\n        scratch_m[i] = (float)mi;\n        scratch_v", ["test_blockwise_fresh_step"]),
+    ("blockwise_m_with_unsigned_map", "oracle_quantize(n, block, bm, 1, scratch_m, Tm, qm, am);\n    oracle_quantize(n, block, bv",
+     "oracle_quantize(n, block, bm, 0, scratch_m, Tm, qm, am);\n    oracle_quantize(n, block, bv",
      ["test_blockwise_fresh_step"]),
-    ("blockwise_m_with_unsigned_map", "oracle_quantize(n, block, bm, 1, scratch_m",
-     "oracle_quantize(n, block, bm, 0, scratch_m", ["test_blockwise_fresh_step"]),
-    ("blockwise_beta_weights_swapped", "double b1 = F32(beta1), c1 = F32(1.0 - beta1);",
-     "double c1 = F32(beta1), b1 = F32(1.0 - beta1);", ["test_blockwise_fresh_step"]),
+    ("blockwise_beta_weights_swapped",
+     "double b1 = F32(beta1), c1 = F32(1.0 - beta1);\n    double b2 = F32(beta2), c2 = F32(1.0 - beta2);\n    double bc1",
+     "double c1 = F32(beta1), b1 = F32(1.0 - beta1);\n    double b2 = F32(beta2), c2 = F32(1.0 - beta2);\n    double bc1",
+     ["test_blockwise_fresh_step"]),
 ]
 
 

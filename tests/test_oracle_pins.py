@@ -518,3 +518,53 @@ def test_scaler_update_closed_form(orc):
         assert st.scale[0] == 1024.0 * 2 ** (k // 4) and st.tracker[0] == k % 4
     st.update(True, 2.0, 0.5, 4)
     assert st.scale[0] == 1024.0 * 2 ** 6 / 2 and st.tracker[0] == 0
+
+
+# ------------------------------------------------------------------ blockwise AdEMAMix
+@pytest.mark.parametrize("bits,block", [(8, 256), (4, 128)])
+def test_blockwise_ademamix_fresh_step(orc, bits, block):
+    """bitsandbytes PR #2040 body: a fresh 8-bit AdEMAMix step has AdamW's
+    closed form plus alpha*(1-beta3)*g; zero states quantize exactly; the
+    three fresh states are the fp32 products of g; the decay-after ordering
+    sits 1e-3 away at lr = 0.1, wd = 0.1."""
+    n, lr, wd, a, b3 = block * 40, 0.1, 0.1, 5.0, 0.9999
+    p = host_normal(n, 0.02, 905, bits, 0, 0).astype(np.float64)
+    p0 = p.copy()
+    g = host_normal(n, 1e-3, 905, bits, 1, 1)
+    q = [np.zeros(n, np.uint8) for _ in range(3)]
+    ab = [np.zeros(n // block, np.float32) for _ in range(3)]
+    sm, sm2, sv = orc.blockwise_ademamix_step(p, g, q[0], q[1], q[2], ab[0], ab[1], ab[2], bits, block,
+                                              lr, 0.9, 0.999, b3, a, 1e-8, wd, 1)
+    assert np.array_equal(sm, np.float32(np.float32(0.1) * g))
+    assert np.array_equal(sm2, np.float32(np.float32(1.0 - b3) * g))
+    assert np.array_equal(sv, np.float32(np.float32(1.0 - 0.999) * np.float32(g * g)))
+    gd = g.astype(np.float64)
+    k = 1 + a * (1 - b3)
+    expect = p0 * (1 - lr * wd) - lr * k * gd / (np.abs(gd) + 1e-8)
+    assert rel_tau(p, expect, lr) < 2e-6
+    mutant = (p0 - lr * k * gd / (np.abs(gd) + 1e-8)) * (1 - lr * wd)
+    assert np.max(np.abs(p - mutant)) > 0.9e-3
+    for st, code, am, signed in ((sm, q[0], ab[0], True), (sm2, q[1], ab[1], True), (sv, q[2], ab[2], False)):
+        c, A = orc.quantize(st, block, bits - 1 if signed else bits, signed)
+        assert np.array_equal(c, code) and np.array_equal(A, am)
+
+
+def test_blockwise_ademamix_alpha_zero_is_blockwise_adamw(orc):
+    """alpha = 0 takes m2 out of the update: the m and nu codes and absmax
+    equal the 2-state blockwise AdamW step's bit for bit over several steps,
+    and p agrees to fp64 rounding (lr (m/bc1)/h against (lr/bc1) m/h)."""
+    n, block, bits = 256 * 12 + 77, 256, 8
+    p = host_normal(n, 0.02, 906, 0, 0, 0).astype(np.float64)
+    pa = p.copy()
+    q = [np.zeros(n, np.uint8) for _ in range(3)]
+    ab = [np.zeros((n + block - 1) // block, np.float32) for _ in range(3)]
+    qa = [np.zeros(n, np.uint8) for _ in range(2)]
+    aa = [np.zeros((n + block - 1) // block, np.float32) for _ in range(2)]
+    for t in range(1, 8):
+        g = host_normal(n, 1e-3, 906, 0, t, 1)
+        orc.blockwise_ademamix_step(p, g, q[0], q[1], q[2], ab[0], ab[1], ab[2], bits, block,
+                                    1e-3, 0.9, 0.999, 0.9999, 0.0, 1e-8, 0.01, t)
+        orc.blockwise_step(pa, g, qa[0], qa[1], aa[0], aa[1], bits, block, 1e-3, 0.9, 0.999, 1e-8, 0.01, t)
+        assert rel_tau(p, pa, 1e-3) < 1e-13
+        assert np.array_equal(q[0], qa[0]) and np.array_equal(q[2], qa[1])
+        assert np.array_equal(ab[0], aa[0]) and np.array_equal(ab[2], aa[1])
