@@ -10,9 +10,9 @@ optimizer element-updates per second with all inputs resident in HBM.
 Secondary workloads (same JSON line, "secondary"): the 1M-element tensor,
 the Llama-shaped 1.1B bf16+remainder AMP list with device cosine lr (also
 timed as the full AMP loop with global-norm clipping folded into the step
-and the dynamic loss-scale update), the
-268M-element blockwise 8-bit and 4-bit states, and Adam-mini over the 7B
-list.  Gradients are drawn once per workload, outside the timed region.
+and the dynamic loss-scale update), the 268M-element blockwise 8-bit and
+4-bit states (2-state AdamW and 3-state AdEMAMix), and Adam-mini over the
+7B list.  Gradients are drawn once per workload, outside the timed region.
 
 Timing: HIP events on the stream the library launches on (torch's current
 stream), one pair around every optimizer call inside the timed region; the
@@ -42,6 +42,7 @@ B_BF16R_AMP = 26.0 + 2.0      # R bf16 p, int16 r, bf16 g, m, v (14) + W (12); +
 B_8BIT = 4 + 4 + 1 + 1 + 8 / 256 + 4 + 1 + 1 + 8 / 256
 B_4BIT = 4 + 4 + 0.5 + 0.5 + 8 / 128 + 4 + 0.5 + 0.5 + 8 / 128
 CLIP_MAX_NORM = 1.0           # global-norm clip of the Llama 1.1B AMP loop
+C4_BETA3, C4_ALPHA = 0.9999, 5.0   # AdEMAMix on the blockwise list: the 4096^2 run's values
 
 
 def log(*a):
@@ -275,7 +276,22 @@ def bench_c4(torch, osa, synth, steps, warmup):
         out[f"blockwise_{bits}bit_block{block}"] = dict(
             elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3), bytes_per_element=bpe,
             gbs=gbs(bpe * n, ms), frac=gbs(bpe * n, ms) / PEAK_HBM_GBS)
-        del p, g, qm, qv, am, av
+        # the same list with AdEMAMix's third state (slow EMA m2, signed codes)
+        qm2 = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+        am2 = torch.zeros(n // block, dtype=torch.float32, device="cuda")
+        tl = osa.TensorList([p], [g], qm=[qm], qv=[qv], absmax_m=[am], absmax_v=[av], qm2=[qm2],
+                            absmax_m2=[am2], weight_decay=[hp.wd])
+        plan = osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX, bits=bits, block=block)
+        s = scalars(torch, hp.lr)
+        he = osa.optim_ademamix_hp(hp.beta1, hp.beta2, C4_BETA3, C4_ALPHA, hp.eps)
+        ms, _, _ = run_timed(torch, [lambda: osa.optim_step_8bit_blockwise_ademamix(
+            plan.handle, he, bits, block, s["lr"], None, None, s["step"])], steps, warmup)
+        plan.close()
+        bpe3 = bpe + bits / 4 + 8 / block  # + m2 codes and absmax, read and written
+        out[f"blockwise_ademamix_{bits}bit_block{block}"] = dict(
+            elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3), bytes_per_element=bpe3,
+            gbs=gbs(bpe3 * n, ms), frac=gbs(bpe3 * n, ms) / PEAK_HBM_GBS, beta3=C4_BETA3, alpha=C4_ALPHA)
+        del p, g, qm, qv, am, av, qm2, am2
         torch.cuda.empty_cache()
     return dict(workload=wl.name, **out)
 
@@ -343,6 +359,8 @@ KERNEL_SOURCES = {  # kernel -> sources its device code comes from
     "ademamix_fp32": ("device_common.h", "kernels_adam.hip"),
     "blockwise_8bit": ("device_common.h", "kernels_blockwise.hip"),
     "blockwise_4bit": ("device_common.h", "kernels_blockwise.hip"),
+    "blockwise_ademamix_8bit": ("device_common.h", "kernels_blockwise.hip"),
+    "blockwise_ademamix_4bit": ("device_common.h", "kernels_blockwise.hip"),
 }
 
 

@@ -51,7 +51,8 @@ enum {
     OPTIM_ALGO_ADAMW = 0,
     OPTIM_ALGO_ADEMAMIX = 1,
     OPTIM_ALGO_ADAM_MINI = 2,
-    OPTIM_ALGO_BLOCKWISE = 3
+    OPTIM_ALGO_BLOCKWISE = 3,
+    OPTIM_ALGO_BLOCKWISE_ADEMAMIX = 4
 };
 /* Adam-mini partition of a tensor ([MINI], AdamWMini constructor/step). */
 enum { OPTIM_MINI_FULL_V = 0, OPTIM_MINI_HEAD = 1, OPTIM_MINI_SCALAR = 2 };
@@ -73,6 +74,8 @@ enum { OPTIM_SCHED_NONE = 0, OPTIM_SCHED_COSINE = 1 };
  *  qm, qv       blockwise codes: 8-bit one byte per element; 4-bit two per
  *               byte (element 2i in the low nibble); m signed, v unsigned
  *  absmax_m/_v  float[ceil(numel/block)] per-block scale of qm / qv
+ *  qm2,         blockwise AdEMAMix only: codes of the slow EMA m2 (signed,
+ *  absmax_m2    layout as qm) and their per-block scale; NULL otherwise
  *  weight_decay per-tensor decoupled decay (>= 0)
  *  mini_kind    Adam-mini only: OPTIM_MINI_*
  *  head_numel   Adam-mini only: block length for HEAD (must divide numel);
@@ -97,6 +100,8 @@ typedef struct optim_tensor_list {
     const int64_t *head_numel;
     int32_t param_dtype;
     int32_t grad_dtype;
+    void *const *qm2;
+    float *const *absmax_m2;
 } optim_tensor_list;
 
 /* Plan options (NULL = all defaults).
@@ -221,6 +226,21 @@ int optim_step_8bit_blockwise(optim_plan *plan, const optim_adamw_hp *hp,
                               const float *inv_scale_dev,
                               const float *found_inf_dev, int32_t *step_dev,
                               void *stream);
+
+/* Blockwise-quantized AdEMAMix ([BNB]: the blockwise 8-bit kernel's
+ * AdEMAMix branch, same decay ordering; the fresh step mixes in
+ * alpha*(1-beta3)*g).  Plan algorithm OPTIM_ALGO_BLOCKWISE_ADEMAMIX, with
+ * qm, qm2, qv and their absmax in the tensor list.  As
+ * optim_step_8bit_blockwise with a third state: m2 uses the signed map and
+ *  m2 = fl32(fl32(b3 m2) + fl32(c3 g)), b3 = fl32(beta3), c3 = fl32(1-beta3),
+ * and the update is p <- p (1 - lr wd) - lr (m/bc1 + alpha m2) / h (m2 not
+ * bias-corrected), as optim_step_ademamix.                                  */
+int optim_step_8bit_blockwise_ademamix(optim_plan *plan,
+                                       const optim_ademamix_hp *hp,
+                                       int32_t bits, int32_t block,
+                                       float *lr_dev, const float *inv_scale_dev,
+                                       const float *found_inf_dev,
+                                       int32_t *step_dev, void *stream);
 
 /* ---- helpers ------------------------------------------------------------ */
 

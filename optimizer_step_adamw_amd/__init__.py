@@ -18,7 +18,8 @@ from .build import LIB_PATH, build as build_library
 OPTIM_OK = 0
 OPTIM_EINVAL, OPTIM_EALIGN, OPTIM_EDTYPE, OPTIM_EWORKSPACE, OPTIM_EUNSUPPORTED, OPTIM_EHIP = range(1, 7)
 OPTIM_F32, OPTIM_BF16 = 0, 1
-OPTIM_ALGO_ADAMW, OPTIM_ALGO_ADEMAMIX, OPTIM_ALGO_ADAM_MINI, OPTIM_ALGO_BLOCKWISE = range(4)
+(OPTIM_ALGO_ADAMW, OPTIM_ALGO_ADEMAMIX, OPTIM_ALGO_ADAM_MINI, OPTIM_ALGO_BLOCKWISE,
+ OPTIM_ALGO_BLOCKWISE_ADEMAMIX) = range(5)
 OPTIM_MINI_FULL_V, OPTIM_MINI_HEAD, OPTIM_MINI_SCALAR = range(3)
 OPTIM_SCHED_NONE, OPTIM_SCHED_COSINE = 0, 1
 
@@ -28,6 +29,7 @@ EXPORTED = (
     "optim_step_8bit_blockwise", "optim_check_finite", "optim_remainder_split",
     "optim_remainder_reconstruct", "optim_quant_codebook", "optim_quantize_blockwise",
     "optim_dequantize_blockwise", "optim_grad_norm", "optim_scaler_update",
+    "optim_step_8bit_blockwise_ademamix",
 )
 
 
@@ -52,6 +54,7 @@ class optim_tensor_list(ctypes.Structure):
         ("head_numel", ctypes.POINTER(ctypes.c_int64)),
         ("param_dtype", ctypes.c_int32),
         ("grad_dtype", ctypes.c_int32),
+        ("qm2", _PP), ("absmax_m2", _PP),
     ]
 
 
@@ -103,6 +106,8 @@ def lib() -> ctypes.CDLL:
             "optim_dequantize_blockwise": ([_P, i32, _P, _P, i64, _P, _P], i32),
             "optim_grad_norm": ([_P, _P, f64, _P, _P, _P, _P], i32),
             "optim_scaler_update": ([_P, _P, _P, _P, f64, f64, i32, _P], i32),
+            "optim_step_8bit_blockwise_ademamix": ([_P, ctypes.POINTER(optim_ademamix_hp), i32, i32, _P, _P,
+                                                    _P, _P, _P], i32),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -139,6 +144,7 @@ class TensorList:
 
     def __init__(self, params: Sequence, grads: Sequence, *, m=None, v=None, m2=None,
                  remainders=None, qm=None, qv=None, absmax_m=None, absmax_v=None,
+                 qm2=None, absmax_m2=None,
                  weight_decay: Sequence[float], mini_kind=None, head_numel=None,
                  param_dtype: int = OPTIM_F32, grad_dtype: int = OPTIM_F32,
                  numel: Optional[Sequence[int]] = None):
@@ -162,6 +168,7 @@ class TensorList:
         s.param, s.grad = parr(params), parr(grads)
         s.m, s.v, s.m2, s.remainder = parr(m), parr(v), parr(m2), parr(remainders)
         s.qm, s.qv, s.absmax_m, s.absmax_v = parr(qm), parr(qv), parr(absmax_m), parr(absmax_v)
+        s.qm2, s.absmax_m2 = parr(qm2), parr(absmax_m2)
         s.weight_decay = ctypes.cast(self._wd, ctypes.POINTER(ctypes.c_double))
         if mini_kind is not None:
             self._kind = (ctypes.c_int32 * max(n, 1))(*mini_kind)
@@ -226,6 +233,14 @@ def optim_step_8bit_blockwise(plan, hp: optim_adamw_hp, bits: int, block: int, l
                                            _ptr(inv_scale_dev), _ptr(found_inf_dev), _ptr(step_dev),
                                            _stream(stream)),
            "optim_step_8bit_blockwise")
+
+
+def optim_step_8bit_blockwise_ademamix(plan, hp: optim_ademamix_hp, bits: int, block: int, lr_dev,
+                                       inv_scale_dev, found_inf_dev, step_dev, stream=None) -> None:
+    _check(lib().optim_step_8bit_blockwise_ademamix(plan, ctypes.byref(hp), bits, block, _ptr(lr_dev),
+                                                    _ptr(inv_scale_dev), _ptr(found_inf_dev), _ptr(step_dev),
+                                                    _stream(stream)),
+           "optim_step_8bit_blockwise_ademamix")
 
 
 def optim_check_finite(plan, found_inf_dev, stream=None) -> None:

@@ -114,9 +114,11 @@ int check_hp_beta(double b, const char *name) {
     return OPTIM_OK;
 }
 
+bool is_blockwise(int32_t algo) { return algo == OPTIM_ALGO_BLOCKWISE || algo == OPTIM_ALGO_BLOCKWISE_ADEMAMIX; }
+
 int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *opts, Built &B) {
     if (!list) return fail(OPTIM_EINVAL, "tensor list is NULL");
-    if (algo < OPTIM_ALGO_ADAMW || algo > OPTIM_ALGO_BLOCKWISE)
+    if (algo < OPTIM_ALGO_ADAMW || algo > OPTIM_ALGO_BLOCKWISE_ADEMAMIX)
         return fail(OPTIM_EINVAL, "unknown algorithm");
     const int n = list->n;
     if (n < 0) return fail(OPTIM_EINVAL, "negative tensor count");
@@ -125,15 +127,15 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     if (list->grad_dtype != OPTIM_F32 && list->grad_dtype != OPTIM_BF16)
         return fail(OPTIM_EDTYPE, "grad_dtype must be OPTIM_F32 or OPTIM_BF16");
     const bool bf16p = list->param_dtype == OPTIM_BF16;
-    if (bf16p && algo == OPTIM_ALGO_BLOCKWISE)
+    if (bf16p && is_blockwise(algo))
         return fail(OPTIM_EUNSUPPORTED, "blockwise states take fp32 params only");
     int bits = 0, block = 0;
-    if (algo == OPTIM_ALGO_BLOCKWISE) {
+    if (is_blockwise(algo)) {
         if (!opts) return fail(OPTIM_EINVAL, "blockwise plans need opts (bits, block)");
         bits = opts->bits;
         block = opts->block;
-        // a block is L = block/8 lanes of one wavefront (8 codes per lane), L a
-        // power of two in [8, 64]
+        // a block is L = block/E lanes of one wavefront (E = 4 codes per lane
+        // up to block 256, else 8), L a power of two in [16, 64]
         if (bits != 8 && bits != 4) return fail(OPTIM_EINVAL, "bits must be 8 or 4");
         const bool ok = bits == 8 ? (block == 64 || block == 128 || block == 256)
                                   : (block == 128 || block == 256 || block == 512);
@@ -149,23 +151,24 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     // prefers 4096, and the blockwise step amortises its LDS tables and
     // prologue over larger units
     const int64_t tile = (opts && opts->tile > 0) ? opts->tile
-                         : algo == OPTIM_ALGO_BLOCKWISE ? kBlockwiseTile
+                         : is_blockwise(algo) ? kBlockwiseTile
                          : algo == OPTIM_ALGO_ADAM_MINI ? kAdamMiniTile
                                                         : kDefaultTile;
     if (tile < kMinTile || tile > (1 << 24) || (tile & (tile - 1)))
         return fail(OPTIM_EINVAL, "tile must be a power of two in [1024, 2^24]");
-    if (algo == OPTIM_ALGO_BLOCKWISE && tile < kMinBlockwiseTile)
+    if (is_blockwise(algo) && tile < kMinBlockwiseTile)
         return fail(OPTIM_EINVAL, "blockwise tile must be at least 2048");
     B.tile = tile;
     if (n > 0 && (!list->numel || !list->param || !list->grad || !list->weight_decay))
         return fail(OPTIM_EINVAL, "numel, param, grad and weight_decay arrays are required");
-    const bool need_mv = algo != OPTIM_ALGO_BLOCKWISE;
+    const bool need_mv = !is_blockwise(algo);
     if (n > 0 && need_mv && (!list->m || !list->v)) return fail(OPTIM_EINVAL, "m and v arrays are required");
     if (n > 0 && algo == OPTIM_ALGO_ADEMAMIX && !list->m2)
         return fail(OPTIM_EINVAL, "AdEMAMix needs the m2 array");
-    if (n > 0 && algo == OPTIM_ALGO_BLOCKWISE &&
-        (!list->qm || !list->qv || !list->absmax_m || !list->absmax_v))
+    if (n > 0 && is_blockwise(algo) && (!list->qm || !list->qv || !list->absmax_m || !list->absmax_v))
         return fail(OPTIM_EINVAL, "blockwise plans need qm, qv, absmax_m and absmax_v");
+    if (n > 0 && algo == OPTIM_ALGO_BLOCKWISE_ADEMAMIX && (!list->qm2 || !list->absmax_m2))
+        return fail(OPTIM_EINVAL, "blockwise AdEMAMix plans need qm2 and absmax_m2");
     if (n > 0 && algo == OPTIM_ALGO_ADAM_MINI && (!list->mini_kind || !list->head_numel))
         return fail(OPTIM_EINVAL, "Adam-mini needs mini_kind and head_numel arrays");
     if (n > 0 && bf16p && !list->remainder)
@@ -250,7 +253,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
             vec = vec && aligned(T.m2, 16);
             add(T.m2, numel * 4, true, "m2");
         }
-        if (algo == OPTIM_ALGO_BLOCKWISE) {
+        if (is_blockwise(algo)) {
             T.qm = static_cast<uint8_t *>(list->qm[i]);
             T.qv = static_cast<uint8_t *>(list->qv[i]);
             T.am = list->absmax_m[i];
@@ -265,6 +268,15 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
             add(T.qv, cbytes, true, "qv");
             add(T.am, nblk * 4, true, "absmax_m");
             add(T.av, nblk * 4, true, "absmax_v");
+            if (algo == OPTIM_ALGO_BLOCKWISE_ADEMAMIX) {
+                T.qm2 = static_cast<uint8_t *>(list->qm2[i]);
+                T.am2 = list->absmax_m2[i];
+                if (numel > 0 && (!T.qm2 || !T.am2)) return fail(OPTIM_EINVAL, ti + "NULL qm2 or absmax_m2");
+                if (!aligned(T.am2, 4)) return fail(OPTIM_EALIGN, ti + "absmax_m2 misaligned");
+                vec = vec && aligned(T.qm2, 16);
+                add(T.qm2, cbytes, true, "qm2");
+                add(T.am2, nblk * 4, true, "absmax_m2");
+            }
         }
         T.vec_ok = vec ? 1 : 0;
         if (numel == 0) continue;
@@ -308,7 +320,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     L.group_wd = off; off += align256(kMaxGroups * sizeof(double));
     L.tensors = off; off += align256(std::max<size_t>(1, B.tensors.size()) * sizeof(TensorDesc));
     L.spans = off; off += align256(B.spans.size() * sizeof(SpanDesc));
-    L.codebook = off; off += algo == OPTIM_ALGO_BLOCKWISE ? align256(sizeof(Codebook)) : 0;
+    L.codebook = off; off += is_blockwise(algo) ? align256(sizeof(Codebook)) : 0;
     L.blockspan = off; off += align256(std::max<size_t>(1, B.blockspan.size()) * sizeof(int32_t));
     // partial sums: Adam-mini's block sums (one per unit) and the gradient
     // norm pass (one per workgroup) share the region; they never overlap in
@@ -381,7 +393,7 @@ int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_p
     std::memcpy(img.data() + B.L.tensors, B.tensors.data(), B.tensors.size() * sizeof(TensorDesc));
     std::memcpy(img.data() + B.L.spans, B.spans.data(), B.spans.size() * sizeof(SpanDesc));
     std::memcpy(img.data() + B.L.blockspan, B.blockspan.data(), B.blockspan.size() * sizeof(int32_t));
-    if (algo == OPTIM_ALGO_BLOCKWISE) {
+    if (is_blockwise(algo)) {
         Codebook *cb = reinterpret_cast<Codebook *>(img.data() + B.L.codebook);
         if (!build_map(7, cb->m8) || !build_map(8, cb->v8) || !build_map(3, cb->m4) || !build_map(4, cb->v4))
             return fail(OPTIM_EUNSUPPORTED, "quantization map does not fit the bucket table");
@@ -503,6 +515,23 @@ int check_plan(optim_plan *P, int32_t algo, const char *fn) {
     return OPTIM_OK;
 }
 
+// the quantize / dequantize helpers take either blockwise plan
+int check_blockwise_plan(optim_plan *P, const char *fn) {
+    if (!P) return fail(OPTIM_EINVAL, std::string(fn) + ": plan is NULL");
+    if (!is_blockwise(P->algo)) return fail(OPTIM_EINVAL, std::string(fn) + ": plan is not blockwise");
+    return OPTIM_OK;
+}
+
+int check_ademamix_hp(const optim_ademamix_hp *hp) {
+    if (!hp) return fail(OPTIM_EINVAL, "hyperparameters are NULL");
+    int rc;
+    if ((rc = check_hp_beta(hp->beta1, "beta1")) || (rc = check_hp_beta(hp->beta2, "beta2")) ||
+        (rc = check_hp_beta(hp->beta3, "beta3")))
+        return rc;
+    if (!std::isfinite(hp->alpha) || hp->alpha < 0.0) return fail(OPTIM_EINVAL, "invalid alpha (need finite alpha >= 0)");
+    return OPTIM_OK;
+}
+
 int check_adamw_hp(const optim_adamw_hp *hp) {
     if (!hp) return fail(OPTIM_EINVAL, "hyperparameters are NULL");
     int rc = check_hp_beta(hp->beta1, "beta1");
@@ -531,12 +560,8 @@ int optim_step_ademamix(optim_plan *plan, const optim_ademamix_hp *hp, float *lr
                         const float *inv_scale_dev, const float *found_inf_dev, int32_t *step_dev,
                         void *stream) {
     int rc = check_plan(plan, OPTIM_ALGO_ADEMAMIX, "optim_step_ademamix");
+    if (!rc) rc = check_ademamix_hp(hp);
     if (rc) return rc;
-    if (!hp) return fail(OPTIM_EINVAL, "hyperparameters are NULL");
-    if ((rc = check_hp_beta(hp->beta1, "beta1")) || (rc = check_hp_beta(hp->beta2, "beta2")) ||
-        (rc = check_hp_beta(hp->beta3, "beta3")))
-        return rc;
-    if (!std::isfinite(hp->alpha) || hp->alpha < 0.0) return fail(OPTIM_EINVAL, "invalid alpha (need finite alpha >= 0)");
     StepArgs a;
     rc = step_inputs(plan, hp->beta1, hp->beta2, hp->beta3, hp->alpha, hp->eps, lr_dev, inv_scale_dev,
                      found_inf_dev, step_dev, a);
@@ -570,7 +595,23 @@ int optim_step_8bit_blockwise(optim_plan *plan, const optim_adamw_hp *hp, int32_
     rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
                      step_dev, a);
     if (rc) return rc;
-    HIP_OK(launch_blockwise(a, plan->gk, static_cast<hipStream_t>(stream)));
+    HIP_OK(launch_blockwise(a, plan->gk, false, static_cast<hipStream_t>(stream)));
+    return OPTIM_OK;
+}
+
+int optim_step_8bit_blockwise_ademamix(optim_plan *plan, const optim_ademamix_hp *hp, int32_t bits, int32_t block,
+                                       float *lr_dev, const float *inv_scale_dev, const float *found_inf_dev,
+                                       int32_t *step_dev, void *stream) {
+    int rc = check_plan(plan, OPTIM_ALGO_BLOCKWISE_ADEMAMIX, "optim_step_8bit_blockwise_ademamix");
+    if (!rc) rc = check_ademamix_hp(hp);
+    if (rc) return rc;
+    if (bits != plan->bits || block != plan->block)
+        return fail(OPTIM_EINVAL, "bits/block differ from the plan's");
+    StepArgs a;
+    rc = step_inputs(plan, hp->beta1, hp->beta2, hp->beta3, hp->alpha, hp->eps, lr_dev, inv_scale_dev,
+                     found_inf_dev, step_dev, a);
+    if (rc) return rc;
+    HIP_OK(launch_blockwise(a, plan->gk, true, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
 
@@ -622,7 +663,7 @@ int optim_scaler_update(float *scale_dev, float *inv_scale_dev, int32_t *growth_
 
 int optim_quantize_blockwise(optim_plan *plan, int32_t is_signed, const float *x_dev, int64_t n,
                              uint8_t *codes_dev, float *absmax_dev, void *stream) {
-    int rc = check_plan(plan, OPTIM_ALGO_BLOCKWISE, "optim_quantize_blockwise");
+    int rc = check_blockwise_plan(plan, "optim_quantize_blockwise");
     if (rc) return rc;
     if (n < 0) return fail(OPTIM_EINVAL, "negative n");
     if (n == 0) return OPTIM_OK;
@@ -636,7 +677,7 @@ int optim_quantize_blockwise(optim_plan *plan, int32_t is_signed, const float *x
 
 int optim_dequantize_blockwise(optim_plan *plan, int32_t is_signed, const uint8_t *codes_dev,
                                const float *absmax_dev, int64_t n, float *x_dev, void *stream) {
-    int rc = check_plan(plan, OPTIM_ALGO_BLOCKWISE, "optim_dequantize_blockwise");
+    int rc = check_blockwise_plan(plan, "optim_dequantize_blockwise");
     if (rc) return rc;
     if (n < 0) return fail(OPTIM_EINVAL, "negative n");
     if (n == 0) return OPTIM_OK;

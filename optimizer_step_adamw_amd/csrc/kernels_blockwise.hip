@@ -193,13 +193,13 @@ __device__ __forceinline__ T *uniform_ptr(T *p) {
 struct UnitPtrs {
     float *p;
     const void *g;
-    uint8_t *qm, *qv;
-    float *am, *av;
+    uint8_t *qm, *qv, *qm2;
+    float *am, *av, *am2;
     float decay;
     int lane;
 };
 
-template <int GK, int BITS, int BLOCK>
+template <int GK, int BITS, int BLOCK, bool ADE>
 __device__ __forceinline__ UnitPtrs unit_ptrs(const TensorDesc &T, int64_t start, float decay) {
     UnitPtrs u;
     u.p = uniform_ptr(static_cast<float *>(T.p) + start);
@@ -208,6 +208,10 @@ __device__ __forceinline__ UnitPtrs unit_ptrs(const TensorDesc &T, int64_t start
     u.qv = uniform_ptr(T.qv + start * BITS / 8);
     u.am = uniform_ptr(T.am + start / BLOCK);
     u.av = uniform_ptr(T.av + start / BLOCK);
+    if (ADE) {
+        u.qm2 = uniform_ptr(T.qm2 + start * BITS / 8);
+        u.am2 = uniform_ptr(T.am2 + start / BLOCK);
+    }
     u.decay = decay;
     u.lane = threadIdx.x & 63;
     return u;
@@ -218,29 +222,31 @@ __device__ __forceinline__ UnitPtrs unit_ptrs(const TensorDesc &T, int64_t start
 template <int E>
 struct RowIn {
     float p[E], g[E];
-    uint64_t cm, cv;
-    float am, av;
+    uint64_t cm, cv, cm2;
+    float am, av, am2;
 };
 
 // FULL: the whole row is inside the tensor and every pointer is aligned;
 // otherwise nv (0..E) of the lane's elements are valid and the rest read 0.
-template <int GK, int BITS, int BLOCK, bool FULL>
+template <int GK, int BITS, int BLOCK, bool ADE, bool FULL>
 __device__ __forceinline__ void load_row(const UnitPtrs &u, const AdamK &k, uint32_t e, int nv,
                                          RowIn<lane_elems(BLOCK)> &in) {
     constexpr int E = lane_elems(BLOCK);
     constexpr int LAY = row_layout<E>();
     const uint32_t blk = e / BLOCK;
-    in.am = in.av = 0.0f;
-    in.cm = in.cv = 0;
+    in.am = in.av = in.am2 = 0.0f;
+    in.cm = in.cv = in.cm2 = 0;
     if (FULL || nv > 0) {
         in.am = gp(u.am)[blk];
         in.av = gp(u.av)[blk];
+        if (ADE) in.am2 = gp(u.am2)[blk];
     }
     if (FULL) {
         ldf<E, LAY>(u.p, e, in.p);
         load_g<GK, E, LAY>(u.g, e, k.inv_scale, in.g);
         in.cm = load_codes_full<BITS, E>(u.qm, e);
         in.cv = load_codes_full<BITS, E>(u.qv, e);
+        if (ADE) in.cm2 = load_codes_full<BITS, E>(u.qm2, e);
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j) {
@@ -255,37 +261,49 @@ __device__ __forceinline__ void load_row(const UnitPtrs &u, const AdamK &k, uint
         if (nv > 0) {
             in.cm = load_codes_part<BITS>(u.qm, e, nv);
             in.cv = load_codes_part<BITS>(u.qv, e, nv);
+            if (ADE) in.cm2 = load_codes_part<BITS>(u.qm2, e, nv);
         }
     }
 }
 
-template <int GK, int BITS, int BLOCK, bool FULL>
+// ADE: AdEMAMix's third state m2 (signed map) and update
+// p <- p decay - lr (m/bc1 + alpha m2) / h.
+template <int GK, int BITS, int BLOCK, bool ADE, bool FULL>
 __device__ __forceinline__ void step_row(const UnitPtrs &u, const AdamK &k, uint32_t e, int nv,
                                          RowIn<lane_elems(BLOCK)> &in, const LdsMap<BITS - 1> &Mm,
                                          const LdsMap<BITS> &Mv) {
     constexpr int E = lane_elems(BLOCK), L = BLOCK / E;
     constexpr int LAY = row_layout<E>();
-    float mt[E], vt[E];
+    float mt[E], vt[E], m2t[E];
     dequantize_lane<BITS, true, E>(in.cm, in.am, Mm, mt);
     dequantize_lane<BITS, false, E>(in.cv, in.av, Mv, vt);
+    if (ADE) dequantize_lane<BITS, true, E>(in.cm2, in.am2, Mm, m2t);
     // fp32 state recipe, every product and sum rounded on its own; outside
     // the tensor g = 0 and the codes are 0, so the new states are 0 there
-    float mn[E], vn[E];
+    float mn[E], vn[E], m2n[E];
 #pragma unroll
     for (int j = 0; j < E; ++j) {
         mn[j] = k.b1 * mt[j] + k.c1 * in.g[j];
         vn[j] = k.b2 * vt[j] + k.c2 * (in.g[j] * in.g[j]);
         // parameter update: hardware sqrt / reciprocal (1 ulp each)
         const float h = __builtin_amdgcn_sqrtf(vn[j]) * k.isb2 + k.eps;
-        in.p[j] = in.p[j] * u.decay - k.ss * (mn[j] * __builtin_amdgcn_rcpf(h));
+        if (ADE) {
+            m2n[j] = k.b3 * m2t[j] + k.c3 * in.g[j];
+            in.p[j] = in.p[j] * u.decay - k.lr * ((mn[j] * k.ibc1 + k.alpha * m2n[j]) * __builtin_amdgcn_rcpf(h));
+        } else {
+            in.p[j] = in.p[j] * u.decay - k.ss * (mn[j] * __builtin_amdgcn_rcpf(h));
+        }
     }
-    float am2, av2;
+    float am2, av2, am22 = 0.0f;
     const uint64_t om = quantize_lane<BITS, true, E, L>(mn, Mm, am2);
     const uint64_t ov = quantize_lane<BITS, false, E, L>(vn, Mv, av2);
+    uint64_t om2 = 0;
+    if (ADE) om2 = quantize_lane<BITS, true, E, L>(m2n, Mm, am22);
     if (FULL) {
         stf<E, LAY>(u.p, e, in.p);
         store_codes_full<BITS, E>(u.qm, e, om);
         store_codes_full<BITS, E>(u.qv, e, ov);
+        if (ADE) store_codes_full<BITS, E>(u.qm2, e, om2);
     } else if (nv > 0) {
 #pragma unroll
         for (int j = 0; j < E; ++j) {
@@ -294,6 +312,7 @@ __device__ __forceinline__ void step_row(const UnitPtrs &u, const AdamK &k, uint
         }
         store_codes_part<BITS>(u.qm, e, nv, om);
         store_codes_part<BITS>(u.qv, e, nv, ov);
+        if (ADE) store_codes_part<BITS>(u.qm2, e, nv, om2);
     }
     // every lane of a block holds the block's absmax: all of them store it
     // (one line per wave instruction, no branch around the store)
@@ -301,10 +320,11 @@ __device__ __forceinline__ void step_row(const UnitPtrs &u, const AdamK &k, uint
         const uint32_t blk = e / BLOCK;
         gp(u.am)[blk] = am2;
         gp(u.av)[blk] = av2;
+        if (ADE) gp(u.am2)[blk] = am22;
     }
 }
 
-template <int GK, int BITS, int BLOCK>
+template <int GK, int BITS, int BLOCK, bool ADE>
 __global__ __launch_bounds__(kThreads) void blockwise_kernel(StepArgs a) {
     constexpr int E = lane_elems(BLOCK);
     constexpr uint32_t kRow = (uint32_t)kThreads * E;
@@ -319,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void blockwise_kernel(StepArgs a) {
     const AdamK k = adam_consts(S);
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len64) {
         const TensorDesc &T = a.tensors[sp.tensor];
-        const UnitPtrs u = unit_ptrs<GK, BITS, BLOCK>(T, start, uniform(S.decay[T.group]));
+        const UnitPtrs u = unit_ptrs<GK, BITS, BLOCK, ADE>(T, start, uniform(S.decay[T.group]));
         const uint32_t len = (uint32_t)len64;  // <= tile <= 2^24
         const uint32_t lane0 = threadIdx.x * E;
         // full rows, software-pipelined: the next row's loads are in flight
@@ -327,22 +347,22 @@ __global__ __launch_bounds__(kThreads) void blockwise_kernel(StepArgs a) {
         const uint32_t nfull = T.vec_ok ? len / kRow : 0;
         if (nfull > 0) {
             RowIn<E> cur;
-            load_row<GK, BITS, BLOCK, true>(u, k, lane0, E, cur);
+            load_row<GK, BITS, BLOCK, ADE, true>(u, k, lane0, E, cur);
             uint32_t r = 0;
             for (; r + 1 < nfull; ++r) {
                 RowIn<E> nxt;
-                load_row<GK, BITS, BLOCK, true>(u, k, lane0 + (r + 1) * kRow, E, nxt);
-                step_row<GK, BITS, BLOCK, true>(u, k, lane0 + r * kRow, E, cur, Mm, Mv);
+                load_row<GK, BITS, BLOCK, ADE, true>(u, k, lane0 + (r + 1) * kRow, E, nxt);
+                step_row<GK, BITS, BLOCK, ADE, true>(u, k, lane0 + r * kRow, E, cur, Mm, Mv);
                 cur = nxt;
             }
-            step_row<GK, BITS, BLOCK, true>(u, k, lane0 + r * kRow, E, cur, Mm, Mv);
+            step_row<GK, BITS, BLOCK, ADE, true>(u, k, lane0 + r * kRow, E, cur, Mm, Mv);
         }
         for (uint32_t r0 = nfull * kRow; r0 < len; r0 += kRow) {
             const uint32_t rel = r0 + lane0;
             const int nv = rel + E <= len ? E : (rel < len ? (int)(len - rel) : 0);
             RowIn<E> in;
-            load_row<GK, BITS, BLOCK, false>(u, k, rel, nv, in);
-            step_row<GK, BITS, BLOCK, false>(u, k, rel, nv, in, Mm, Mv);
+            load_row<GK, BITS, BLOCK, ADE, false>(u, k, rel, nv, in);
+            step_row<GK, BITS, BLOCK, ADE, false>(u, k, rel, nv, in, Mm, Mv);
         }
     });
 }
@@ -440,13 +460,17 @@ int quant_grid(int64_t n, int E) {
 
 }  // namespace
 
-hipError_t launch_blockwise(const StepArgs &a, int gk, hipStream_t s) {
+hipError_t launch_blockwise(const StepArgs &a, int gk, bool ademamix, hipStream_t s) {
     return with_block(a.bits, a.block, [&](auto bits, auto block) {
         constexpr int B = decltype(bits)::value, K = decltype(block)::value;
-        if (gk == G_F32)
-            LAUNCH_PERSISTENT((blockwise_kernel<G_F32, B, K>), a, s);
+        if (gk == G_F32 && !ademamix)
+            LAUNCH_PERSISTENT((blockwise_kernel<G_F32, B, K, false>), a, s);
+        else if (!ademamix)
+            LAUNCH_PERSISTENT((blockwise_kernel<G_BF16, B, K, false>), a, s);
+        else if (gk == G_F32)
+            LAUNCH_PERSISTENT((blockwise_kernel<G_F32, B, K, true>), a, s);
         else
-            LAUNCH_PERSISTENT((blockwise_kernel<G_BF16, B, K>), a, s);
+            LAUNCH_PERSISTENT((blockwise_kernel<G_BF16, B, K, true>), a, s);
         return hipGetLastError();
     });
 }

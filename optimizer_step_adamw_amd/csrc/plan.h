@@ -39,7 +39,9 @@ struct TensorDesc {       // 128 bytes
     int32_t group;        // weight-decay group
     int32_t kind;         // Adam-mini partition
     int32_t vec_ok;       // every pointer 16-byte aligned
-    int32_t pad_[5];
+    int32_t pad_;
+    uint8_t *qm2;         // blockwise AdEMAMix: codes of m2
+    float *am2;           // blockwise AdEMAMix: absmax of m2
 };
 static_assert(sizeof(TensorDesc) == 128, "TensorDesc layout");
 
@@ -152,7 +154,7 @@ struct StepArgs {
 hipError_t launch_adamw(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_ademamix(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_adam_mini(const StepArgs &a, int pk, int gk, hipStream_t s);
-hipError_t launch_blockwise(const StepArgs &a, int gk, hipStream_t s);
+hipError_t launch_blockwise(const StepArgs &a, int gk, bool ademamix, hipStream_t s);
 hipError_t launch_check_finite(const StepArgs &a, int gk, hipStream_t s);
 // Workgroups of the finite check / gradient norm pass for a plan.
 int64_t finite_pass_grid(int64_t nunits, int64_t tile, int32_t grid_request);

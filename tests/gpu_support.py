@@ -100,7 +100,7 @@ class AdamState:
 class QuantState:
     """Device buffers for the blockwise 8-bit / 4-bit step."""
 
-    def __init__(self, p0: list, bits: int, block: int):
+    def __init__(self, p0: list, bits: int, block: int, ademamix: bool = False):
         self.bits, self.block = bits, block
         self.p = [x.clone() for x in p0]
         self.g = [torch.zeros_like(x) for x in p0]
@@ -110,13 +110,18 @@ class QuantState:
         self.qv = [torch.zeros(k, dtype=torch.uint8, device=DEV) for k in nbytes]
         self.am = [torch.zeros(k, dtype=torch.float32, device=DEV) for k in nblk]
         self.av = [torch.zeros(k, dtype=torch.float32, device=DEV) for k in nblk]
+        self.qm2 = [torch.zeros(k, dtype=torch.uint8, device=DEV) for k in nbytes] if ademamix else None
+        self.am2 = [torch.zeros(k, dtype=torch.float32, device=DEV) for k in nblk] if ademamix else None
 
     def tensor_list(self, wd):
         return osa.TensorList(self.p, self.g, qm=self.qm, qv=self.qv, absmax_m=self.am,
-                              absmax_v=self.av, weight_decay=wd)
+                              absmax_v=self.av, qm2=self.qm2, absmax_m2=self.am2, weight_decay=wd)
 
     def buffers(self):
-        return list(self.p) + list(self.qm) + list(self.qv) + list(self.am) + list(self.av)
+        out = list(self.p) + list(self.qm) + list(self.qv) + list(self.am) + list(self.av)
+        if self.qm2:
+            out += list(self.qm2) + list(self.am2)
+        return out
 
 
 def snapshot(bufs):

@@ -27,7 +27,7 @@ def header_functions():
 
 def test_exports_every_declared_function(L):
     declared = header_functions()
-    assert len(declared) == 17, declared
+    assert len(declared) == 18, declared
     assert sorted(osa.EXPORTED) == declared
     for name in declared:
         assert hasattr(L, name), name
@@ -157,6 +157,20 @@ def test_scaler_and_norm_validation_without_device(L):
     expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_scaler_update(a, None, a, a, 2.0, 0.5, 0, 0))
     expect_error(osa.OPTIM_EALIGN, lambda: osa.optim_scaler_update(a + 2, None, a, a, 2.0, 0.5, 10, 0))
     expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_grad_norm(None, None, 1.0, a, None, a, 0))
+
+
+def test_blockwise_ademamix_validation(L):
+    f = Fake()
+    n = 1000
+    kw = dict(m=None, v=None, qm=[f(n)], qv=[f(n)], absmax_m=[f(64)], absmax_v=[f(64)])
+    opts = osa.optim_plan_opts(8, 256, 0, 0)
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, **kw), osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX, opts))
+    full = dict(kw, qm2=[f(n)], absmax_m2=[f(64)])
+    assert ws(fake_list([n], fake=f, **full), osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX, opts) > 0
+    # m2's codes overlapping m's
+    bad = dict(kw, qm2=[kw["qm"][0] + 8], absmax_m2=[f(64)])
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, **bad), osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX, opts))
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, **full), 5, opts))
 
 
 def test_null_plan_is_rejected_without_device(L):

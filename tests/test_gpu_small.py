@@ -292,6 +292,64 @@ def test_blockwise_arrays_across_a_2gib_address_boundary(bits, block, tile):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("bits,block", [(8, 256), (4, 128), (8, 64), (4, 512)])
+def test_blockwise_ademamix_codes_bit_exact(bits, block):
+    """Blockwise AdEMAMix: the three code arrays and absmax equal the
+    oracle's bit for bit at every step of ten; p within the step bounds;
+    ragged tensors, several units, a persistent-grid-free default launch."""
+    sizes = [77, 1000, 4096, 5000, 3 * 4096 + 2 * 256 + 13, 16384 + 512]
+    lr, wd, b3, alpha = 1e-3, 0.01, 0.999, 5.0
+    p0 = _p0(sizes, 40 + bits)
+    qs = QuantState(_to_dev(p0), bits, block, ademamix=True)
+    plan = osa.Plan(qs.tensor_list([wd] * len(sizes)), osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX, bits=bits, block=block,
+                    tile=4096)
+    hp = osa.optim_ademamix_hp(0.9, 0.999, b3, alpha, 1e-8)
+    sc = DevScalars(lr)
+    lr32 = float(np.float32(lr))
+    op = [x.astype(np.float64) for x in p0]
+    oq = [[np.zeros(n, np.uint8) for n in sizes] for _ in range(3)]
+    oa = [[np.zeros((n + block - 1) // block, np.float32) for n in sizes] for _ in range(3)]
+    pack = (lambda c: orc.pack_nibbles(c)) if bits == 4 else (lambda c: c)
+    for t in range(1, 11):
+        gs = _grads(sizes, 41, t, 1e-3)
+        for dst, g in zip(qs.g, gs):
+            dst.copy_(torch.from_numpy(g).to(DEV))
+        osa.optim_step_8bit_blockwise_ademamix(plan.handle, hp, bits, block, sc.lr, None, None, sc.step)
+        for i, n in enumerate(sizes):
+            orc.blockwise_ademamix_step(op[i], gs[i], oq[0][i], oq[1][i], oq[2][i], oa[0][i], oa[1][i], oa[2][i],
+                                        bits, block, lr32, 0.9, 0.999, b3, alpha, 1e-8, wd, t)
+            for dev, want in ((qs.qm[i], oq[0][i]), (qs.qm2[i], oq[1][i]), (qs.qv[i], oq[2][i])):
+                got = dev.cpu().numpy()
+                assert np.array_equal(got, pack(want)), (t, i, np.flatnonzero(got != pack(want))[:10])
+            for dev, want in ((qs.am[i], oa[0][i]), (qs.am2[i], oa[1][i]), (qs.av[i], oa[2][i])):
+                assert np.array_equal(dev.cpu().numpy().view(np.uint32), want.view(np.uint32)), (t, i)
+            err = relerr_tau(qs.p[i].cpu().numpy(), op[i], lr32)
+            assert err <= (TOL_STEP1 if t == 1 else TOL_RUN), (t, i, err)
+    assert int(sc.step.item()) == 10
+
+
+def test_blockwise_ademamix_fresh_step_closed_form():
+    """bitsandbytes PR #2040 body: one fresh 8-bit AdEMAMix step at lr = 0.1,
+    wd = 0.1 is the AdamW closed form with the extra alpha*(1-beta3)*g;
+    decay-after sits 1e-3 away."""
+    n, lr, wd, a, b3 = 256 * 300, 0.1, 0.1, 5.0, 0.9999
+    p0 = _p0([n], 42)
+    qs = QuantState(_to_dev(p0), 8, 256, ademamix=True)
+    plan = osa.Plan(qs.tensor_list([wd]), osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX, bits=8, block=256)
+    sc = DevScalars(lr)
+    g = _grads([n], 42, 1, 1e-3)[0]
+    qs.g[0].copy_(torch.from_numpy(g).to(DEV))
+    osa.optim_step_8bit_blockwise_ademamix(plan.handle, osa.optim_ademamix_hp(0.9, 0.999, b3, a, 1e-8), 8, 256,
+                                           sc.lr, None, None, sc.step)
+    lr32 = float(np.float32(lr))
+    gd = g.astype(np.float64)
+    k = 1 + a * (1 - b3)
+    got = qs.p[0].cpu().numpy()
+    assert relerr_tau(got, p0[0] * (1 - lr32 * wd) - lr32 * k * gd / (np.abs(gd) + 1e-8), lr32) <= TOL_STEP1
+    mutant = (p0[0] - lr32 * k * gd / (np.abs(gd) + 1e-8)) * (1 - lr32 * wd)
+    assert np.max(np.abs(got - mutant)) > 0.9e-3
+
+
 def test_blockwise_fresh_step_discriminates_ordering():
     """bitsandbytes PR #2040 body: one fresh 8-bit step at lr=0.1, wd=0.1 has
     the closed form -lr*g/(|g|+eps) after decay; decay-after is 1e-3 away."""
