@@ -63,6 +63,8 @@ _SIGS = {
                               _d, _d, _d, _d, _d, _i64, _p, _p],
     "oracle_blockwise_ademamix_step": [_i64, _i64, _i32, _p, _p, _p, _p, _p, _p, _p, _p,
                                        _d, _d, _d, _d, _d, _d, _d, _i64, _p, _p, _p],
+    "oracle_lion_step": [_i64, _p, _p, _p, _d, _d, _d, _d],
+    "oracle_lamb_step": [_i64, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64, _p],
     "oracle_sumsq": [_i64, _p],
     "oracle_clip_coef": [_d, _d],
     "oracle_scaler_update": [_p, _p, _i32, _d, _d, _i32],
@@ -172,6 +174,21 @@ def adam_mini_step(p, m, V, g, block, lr, beta1, beta2, eps, wd, t):
 def any_nonfinite(x) -> bool:
     x = _f64(x)
     return bool(lib().oracle_any_nonfinite(x.size, _ptr(x)))
+
+
+def lion_step(p, m_f32, g_f32, lr, beta1, beta2, wd):
+    """Lion (decay before the sign update); m float32 state, in place."""
+    assert m_f32.dtype == np.float32 and m_f32.flags["C_CONTIGUOUS"]
+    g = np.ascontiguousarray(g_f32, np.float32).ravel()
+    lib().oracle_lion_step(p.size, _ptr(p), _ptr(m_f32), _ptr(g), lr, beta1, beta2, wd)
+
+
+def lamb_step(p, m, v, g, lr, beta1, beta2, eps, wd, t):
+    """LAMB on one tensor (per-tensor trust ratio), in place; returns u."""
+    u = np.empty(p.size)
+    lib().oracle_lamb_step(p.size, _ptr(p), _ptr(m), _ptr(v), _ptr(_f64(g)), lr, beta1, beta2,
+                           eps, wd, t, _ptr(u))
+    return u
 
 
 def grad_norm(grads, inv_scale: float = 1.0) -> float:

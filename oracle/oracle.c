@@ -480,3 +480,58 @@ void oracle_blockwise_ademamix_step(int64_t n, int64_t block, int bits, double *
     oracle_quantize(n, block, bm, 1, scratch_m2, Tm, qm2, am2);
     oracle_quantize(n, block, bv, 0, scratch_v, Tv, qv, av);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Lion.  [BNB] PR review on the 1-state kernels: Lion applies decoupled
+ * decay to the parameter before its sign update (the ordering the PR
+ * establishes for the 2-state kernels).  The pages give no formula; the
+ * update is Lion's published one (Chen et al., arXiv:2302.06675):
+ *   c = b1 m + c1 g;  p <- p (1 - lr wd) - lr sign(c);  m <- b2 m + c2 g
+ * sign(0) = 0.  The sign is an integer decision taken from c, so c and the
+ * state m follow the fp32 recipe of the kernel (fp32-faithful):
+ *   c = fl32(fl32(b1 m) + fl32(c1 g)),  m = fl32(fl32(b2 m) + fl32(c2 g)),
+ * with b1 = fl32(beta1), c1 = fl32(1 - beta1) (likewise beta2) and g the
+ * float gradient; the parameter update is taken in double.                  */
+void oracle_lion_step(int64_t n, double *p, float *m, const float *g, double lr, double beta1,
+                      double beta2, double wd)
+{
+    double b1 = F32(beta1), c1 = F32(1.0 - beta1);
+    double b2 = F32(beta2), c2 = F32(1.0 - beta2);
+    for (int64_t i = 0; i < n; ++i) {
+        double gi = (double)g[i];
+        double c = F32(F32(b1 * (double)m[i]) + F32(c1 * gi));
+        double sg = c > 0.0 ? 1.0 : (c < 0.0 ? -1.0 : 0.0);
+        p[i] = p[i] * (1.0 - lr * wd);
+        p[i] = p[i] - lr * sg;
+        m[i] = (float)F32(F32(b2 * (double)m[i]) + F32(c2 * gi));
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* LAMB, one tensor (the trust ratio is per tensor).  [BNB] PR description:
+ * LAMB shares the Adam kernels and their decay ordering.  The pages give no
+ * formula; the update is LAMB's published one (You et al., arXiv:1904.00962,
+ * Algorithm 2), with Adam's direction in the form used above:
+ *   m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2
+ *   r = (m/bc1) / (sqrt(v)/sqrt(bc2) + eps);  u = r + wd p
+ *   p <- p - lr (|p| / |u|) u        (L2 norms over the tensor, previous p)
+ * with the trust ratio |p|/|u| taken as 1 when either norm is 0.  Norms are
+ * summed in index order.                                                     */
+void oracle_lamb_step(int64_t n, double *p, double *m, double *v, const double *g, double lr,
+                      double beta1, double beta2, double eps, double wd, int64_t t, double *u)
+{
+    double bc1 = 1.0 - pow(beta1, (double)t);
+    double bc2 = 1.0 - pow(beta2, (double)t);
+    double pn = 0.0, un = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        m[i] = beta1 * m[i] + (1.0 - beta1) * g[i];
+        v[i] = beta2 * v[i] + (1.0 - beta2) * g[i] * g[i];
+        double r = (m[i] / bc1) / (sqrt(v[i]) / sqrt(bc2) + eps);
+        u[i] = r + wd * p[i];
+        pn += p[i] * p[i];
+        un += u[i] * u[i];
+    }
+    double trust = (pn > 0.0 && un > 0.0) ? sqrt(pn) / sqrt(un) : 1.0;
+    for (int64_t i = 0; i < n; ++i)
+        p[i] = p[i] - lr * trust * u[i];
+}

@@ -153,6 +153,29 @@ MUTANTS = [
     ("blockwise_ademamix_m1_bias_uncorrected", "p[i] = p[i] - lr * (mi / bc1 + alpha * m2i) / h;",
      "p[i] = p[i] - lr * (mi + alpha * m2i) / h;",
      ["test_blockwise_ademamix_fresh_step", "test_blockwise_ademamix_alpha_zero_is_blockwise_adamw"]),
+    # ---- Lion
+    ("lion_decay_after_update", "        p[i] = p[i] * (1.0 - lr * wd);\n        p[i] = p[i] - lr * sg;",
+     "        p[i] = p[i] - lr * sg;\n        p[i] = p[i] * (1.0 - lr * wd);",
+     ["test_lion_constant_gradient_closed_form"]),
+    ("lion_sign_of_gradient", "double sg = c > 0.0 ? 1.0 : (c < 0.0 ? -1.0 : 0.0);",
+     "double sg = gi > 0.0 ? 1.0 : (gi < 0.0 ? -1.0 : 0.0);", ["test_lion_reversal_follows_the_interpolation"]),
+    ("lion_interpolates_with_beta2", "double c = F32(F32(b1 * (double)m[i]) + F32(c1 * gi));",
+     "double c = F32(F32(b2 * (double)m[i]) + F32(c2 * gi));", ["test_lion_reversal_follows_the_interpolation"]),
+    ("lion_momentum_before_sign",
+     "        double c = F32(F32(b1 * (double)m[i]) + F32(c1 * gi));\n",
+     "        m[i] = (float)F32(F32(b2 * (double)m[i]) + F32(c2 * gi));\n"
+     "        double c = F32(F32(b1 * (double)m[i]) + F32(c1 * gi));\n",
+     ["test_lion_reversal_follows_the_interpolation"]),
+    # ---- LAMB
+    ("lamb_trust_without_sqrt", "double trust = (pn > 0.0 && un > 0.0) ? sqrt(pn) / sqrt(un) : 1.0;",
+     "double trust = (pn > 0.0 && un > 0.0) ? pn / un : 1.0;", ["test_lamb_step_norm_is_lr_times_param_norm"]),
+    ("lamb_trust_inverted", "double trust = (pn > 0.0 && un > 0.0) ? sqrt(pn) / sqrt(un) : 1.0;",
+     "double trust = (pn > 0.0 && un > 0.0) ? sqrt(un) / sqrt(pn) : 1.0;",
+     ["test_lamb_step_norm_is_lr_times_param_norm", "test_lamb_scale_equivariance"]),
+    ("lamb_no_decay_term", "        u[i] = r + wd * p[i];", "        u[i] = r;",
+     ["test_lamb_fresh_step_direction"]),
+    ("lamb_uncorrected_moments", "double r = (m[i] / bc1) / (sqrt(v[i]) / sqrt(bc2) + eps);",
+     "double r = m[i] / (sqrt(v[i]) + eps);", ["test_lamb_fresh_step_direction"]),
     # ---- gradient clipping and loss scale
     ("sumsq_of_magnitudes", "        s += x[i] * x[i];\n    return s;", "        s += fabs(x[i]);\n    return s;",
      ["test_grad_norm_library_and_closed_form", "test_clip_matches_torch_clip_grad_norm"]),

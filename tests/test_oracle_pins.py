@@ -568,3 +568,90 @@ def test_blockwise_ademamix_alpha_zero_is_blockwise_adamw(orc):
         assert rel_tau(p, pa, 1e-3) < 1e-13
         assert np.array_equal(q[0], qa[0]) and np.array_equal(q[2], qa[1])
         assert np.array_equal(ab[0], aa[0]) and np.array_equal(ab[2], aa[1])
+
+
+# ------------------------------------------------------------------ Lion
+def test_lion_constant_gradient_closed_form(orc):
+    """With a constant gradient the interpolation c keeps the gradient's sign,
+    so each step moves p by exactly lr against it after the decay:
+    p_T = (1-a)^T p0 - lr sign(g) (1-(1-a)^T)/a, a = lr wd (decay first, as
+    the bitsandbytes PR review describes Lion); sign(0) = 0 leaves pure decay."""
+    n, lr, wd, T = 1000, 1e-3, 0.1, 25
+    p = host_normal(n, 0.02, 907, 0, 0, 0).astype(np.float64)
+    p0 = p.copy()
+    g = host_normal(n, 1e-3, 907, 0, 0, 1)
+    g[::10] = 0.0
+    m = np.zeros(n, np.float32)
+    for _ in range(T):
+        orc.lion_step(p, m, g, lr, 0.9, 0.99, wd)
+    a = lr * wd
+    s = np.sign(g).astype(np.float64)  # not float32: lr would round to fp32
+    expect = (1 - a) ** T * p0 - lr * s * (1 - (1 - a) ** T) / a
+    assert rel_tau(p, expect, lr) < 1e-11
+    assert np.all(m[::10] == 0.0)
+
+
+def test_lion_reversal_follows_the_interpolation(orc):
+    """Hand-worked two steps (lr 0.1, wd 0, beta1 0.9, beta2 0.99): g = +1
+    moves p to -0.1 and leaves m = fl32(0.01); then g = -0.085 gives
+    c = 0.9 m + 0.1 g = +0.0005 > 0, so p moves on to -0.2 although the
+    gradient turned (updating m first, or using beta2 for c, or the sign of
+    g, would move it back to 0); m = 0.99 m + 0.01 g = 0.00905."""
+    p = np.zeros(1)
+    m = np.zeros(1, np.float32)
+    orc.lion_step(p, m, np.array([1.0], np.float32), 0.1, 0.9, 0.99, 0.0)
+    assert p[0] == -0.1 and m[0] == np.float32(0.01)
+    orc.lion_step(p, m, np.array([-0.085], np.float32), 0.1, 0.9, 0.99, 0.0)
+    assert p[0] == -0.2
+    assert abs(m[0] - 0.00905) < 1e-9
+    # a larger reversal, g = -0.2: c = 0.009 - 0.02 < 0 turns p back to 0
+    # (beta2 in the interpolation, 0.0099 - 0.002 > 0, would not)
+    p, m = np.zeros(1), np.zeros(1, np.float32)
+    for g in (1.0, -0.2):
+        orc.lion_step(p, m, np.array([g], np.float32), 0.1, 0.9, 0.99, 0.0)
+    assert abs(p[0]) < 1e-17 and abs(m[0] - 0.0079) < 1e-9
+
+
+# ------------------------------------------------------------------ LAMB
+@pytest.mark.parametrize("wd", [0.0, 0.1])
+def test_lamb_step_norm_is_lr_times_param_norm(orc, wd):
+    """LAMB's layer-wise normalisation: ||p_new - p|| = lr ||p|| on every step
+    (trust ratio ||p||/||u|| times the update u), here over 6 steps."""
+    n, lr = 3000, 1e-2
+    p = host_normal(n, 0.02, 908, 0, 0, 0).astype(np.float64)
+    m, v = np.zeros(n), np.zeros(n)
+    for t in range(1, 7):
+        prev = p.copy()
+        orc.lamb_step(p, m, v, grads(n, 1e-3, 8, t), lr, 0.9, 0.999, 1e-6, wd, t)
+        assert abs(np.linalg.norm(p - prev) - lr * np.linalg.norm(prev)) <= 1e-12 * lr * np.linalg.norm(prev)
+
+
+def test_lamb_fresh_step_direction(orc):
+    """From zero moments the bias-corrected direction is g/(|g|+eps), so the
+    first step is parallel to g/(|g|+eps) + wd p0 (cosine 1); a zero
+    parameter has trust ratio 1 and takes Adam's fresh step -lr g/(|g|+eps)."""
+    n, lr, wd, eps = 2048, 1e-2, 0.1, 1e-6
+    p = host_normal(n, 0.02, 909, 0, 0, 0).astype(np.float64)
+    p0 = p.copy()
+    g = grads(n, 1e-3, 9, 1)
+    orc.lamb_step(p, np.zeros(n), np.zeros(n), g, lr, 0.9, 0.999, eps, wd, 1)
+    u = g / (np.abs(g) + eps) + wd * p0
+    d = p0 - p
+    assert abs(d @ u / (np.linalg.norm(d) * np.linalg.norm(u)) - 1.0) < 1e-12
+    z = np.zeros(n)
+    orc.lamb_step(z, np.zeros(n), np.zeros(n), g, lr, 0.9, 0.999, eps, wd, 1)
+    assert np.allclose(z, -lr * g / (np.abs(g) + eps), rtol=1e-13, atol=0)
+
+
+def test_lamb_scale_equivariance(orc):
+    """Without decay the update scales with the parameter: stepping c*p0
+    gives c times the step of p0 (the trust ratio carries ||p||)."""
+    n, lr = 1500, 1e-2
+    p = host_normal(n, 0.02, 910, 0, 0, 0).astype(np.float64)
+    q = 8.0 * p
+    ma, va, mb, vb = np.zeros(n), np.zeros(n), np.zeros(n), np.zeros(n)
+    for t in range(1, 5):
+        g = grads(n, 1e-3, 10, t)
+        orc.lamb_step(p, ma, va, g, lr, 0.9, 0.999, 1e-6, 0.0, t)
+        orc.lamb_step(q, mb, vb, g, lr, 0.9, 0.999, 1e-6, 0.0, t)
+    assert rel_tau(q, 8.0 * p, 1e-3) < 1e-13
