@@ -11,8 +11,8 @@ Secondary workloads (same JSON line, "secondary"): the 1M-element tensor,
 the Llama-shaped 1.1B bf16+remainder AMP list with device cosine lr (also
 timed as the full AMP loop with global-norm clipping folded into the step
 and the dynamic loss-scale update), the 268M-element blockwise 8-bit and
-4-bit states (2-state AdamW and 3-state AdEMAMix), and Adam-mini over the
-7B list.  Gradients are drawn once per workload, outside the timed region.
+4-bit states (2-state AdamW and 3-state AdEMAMix), Adam-mini over the 7B
+list, and Lion and LAMB on the 4096 x 4096 tensor.  Gradients are drawn once per workload, outside the timed region.
 
 Timing: HIP events on the stream the library launches on (torch's current
 stream), one pair around every optimizer call inside the timed region; the
@@ -38,6 +38,7 @@ METRIC = "optimizer-step elements/s and achieved HBM GB/s (% of peak), fp32 and 
 # algorithmic bytes per element (read + write once)
 B_ADAMW_F32 = 28.0            # R p g m v (16) + W p m v (12)
 B_ADEMAMIX_F32 = 36.0         # + m2 read and write
+B_LION_F32 = 20.0             # R p g m (12) + W p m (8)
 B_BF16R_AMP = 26.0 + 2.0      # R bf16 p, int16 r, bf16 g, m, v (14) + W (12); + finite check g
 B_8BIT = 4 + 4 + 1 + 1 + 8 / 256 + 4 + 1 + 1 + 8 / 256
 B_4BIT = 4 + 4 + 0.5 + 0.5 + 8 / 128 + 4 + 0.5 + 0.5 + 8 / 128
@@ -54,8 +55,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--secondary", default="c1,c3,c4,c5",
-                    help="comma list of secondary workloads (c1,c3,c4,c5) or 'none'")
+    ap.add_argument("--secondary", default="c1,c3,c4,c5,lion_lamb",
+                    help="comma list of secondary workloads (c1,c3,c4,c5,lion_lamb) or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
@@ -169,6 +170,39 @@ def bench_headline(torch, osa, synth, steps, warmup):
     pa.close()
     pb.close()
     return res
+
+
+def bench_lion_lamb(torch, osa, synth, steps, warmup):
+    """Lion and LAMB on the 4096 x 4096 tensor and gradients of the headline,
+    each with its own state (beta (0.9, 0.99) for Lion; LAMB eps 1e-6)."""
+    wl = synth.c2_decay_stress()
+    n, hp = wl.numel, wl.hp
+    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
+    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
+    A = adam_buffers(torch, [p0], osa.OPTIM_F32)
+    B = adam_buffers(torch, [p0], osa.OPTIM_F32)
+    del p0
+    pl = osa.Plan(osa.TensorList(A["p"], [g], m=A["m"], weight_decay=[hp.wd]), osa.OPTIM_ALGO_LION)
+    pm = osa.Plan(osa.TensorList(B["p"], [g], m=B["m"], v=B["v"], weight_decay=[hp.wd]), osa.OPTIM_ALGO_LAMB)
+    sl, sm = scalars(torch, 1e-4), scalars(torch, 1e-3)
+    hl = osa.optim_lion_hp(0.9, 0.99)
+    hm = osa.optim_adamw_hp(hp.beta1, hp.beta2, 1e-6)
+    ms, per_call, _ = run_timed(torch, [
+        lambda: osa.optim_step_lion(pl.handle, hl, sl["lr"], None, None, sl["step"]),
+        lambda: osa.optim_step_lamb(pm.handle, hm, sm["lr"], None, None, sm["step"])], steps, warmup)
+    pl.close()
+    pm.close()
+    del A, B, g
+    torch.cuda.empty_cache()
+    return dict(workload="lion_lamb_fp32_4096x4096", elements=n, ms_per_step=ms,
+                kernels={"lion_fp32": dict(ms=per_call[0], bytes_per_element=B_LION_F32,
+                                           gbs=gbs(B_LION_F32 * n, per_call[0]),
+                                           frac=gbs(B_LION_F32 * n, per_call[0]) / PEAK_HBM_GBS),
+                         "lamb_fp32": dict(ms=per_call[1], bytes_per_element=B_ADAMW_F32,
+                                           gbs=gbs(B_ADAMW_F32 * n, per_call[1]),
+                                           frac=gbs(B_ADAMW_F32 * n, per_call[1]) / PEAK_HBM_GBS,
+                                           note="algorithmic 28 B/elem; the two passes move 40 B/elem "
+                                                "(p, m, v read again for the per-tensor trust ratio)")})
 
 
 def bench_c1(torch, osa, synth, steps, warmup):
@@ -427,7 +461,7 @@ def main():
         f"{json.dumps(head['kernels'])}")
     secondary = {}
     todo = [] if args.secondary == "none" else args.secondary.split(",")
-    fns = dict(c1=bench_c1, c3=bench_c3, c4=bench_c4, c5=bench_c5)
+    fns = dict(c1=bench_c1, c3=bench_c3, c4=bench_c4, c5=bench_c5, lion_lamb=bench_lion_lamb)
     for key in todo:
         t0 = time.perf_counter()
         secondary[key] = fns[key](torch, osa, synth, args.steps, args.warmup)

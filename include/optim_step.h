@@ -52,7 +52,9 @@ enum {
     OPTIM_ALGO_ADEMAMIX = 1,
     OPTIM_ALGO_ADAM_MINI = 2,
     OPTIM_ALGO_BLOCKWISE = 3,
-    OPTIM_ALGO_BLOCKWISE_ADEMAMIX = 4
+    OPTIM_ALGO_BLOCKWISE_ADEMAMIX = 4,
+    OPTIM_ALGO_LION = 5,
+    OPTIM_ALGO_LAMB = 6
 };
 /* Adam-mini partition of a tensor ([MINI], AdamWMini constructor/step). */
 enum { OPTIM_MINI_FULL_V = 0, OPTIM_MINI_HEAD = 1, OPTIM_MINI_SCALAR = 2 };
@@ -65,9 +67,10 @@ enum { OPTIM_SCHED_NONE = 0, OPTIM_SCHED_COSINE = 1 };
  *  numel        elements per tensor (> 0)
  *  param        F32: float[numel]; BF16: uint16 bf16 patterns[numel]
  *  grad         F32 float[numel] or BF16 uint16[numel] (grad_dtype)
- *  m, v         float[numel] first / second moment (AdamW, AdEMAMix,
+ *  m, v         float[numel] first / second moment (AdamW, AdEMAMix, LAMB,
  *               Adam-mini FULL_V).  Adam-mini HEAD/SCALAR: m float[numel]
  *               and v float[numel/head_numel] (one shared v per block).
+ *               Lion: m only (v NULL).
  *  m2           float[numel] AdEMAMix slow EMA; NULL otherwise
  *  remainder    int16[numel] low halves of the fp32 master ([TE]); required
  *               when param_dtype is BF16, NULL otherwise
@@ -128,6 +131,11 @@ typedef struct optim_adamw_hp {
 typedef struct optim_ademamix_hp {
     double beta1, beta2, beta3, alpha, eps;
 } optim_ademamix_hp;
+
+/* Lion: beta1 interpolates the sign argument, beta2 the momentum.        */
+typedef struct optim_lion_hp {
+    double beta1, beta2;
+} optim_lion_hp;
 
 typedef struct optim_plan optim_plan;
 
@@ -226,6 +234,30 @@ int optim_step_8bit_blockwise(optim_plan *plan, const optim_adamw_hp *hp,
                               const float *inv_scale_dev,
                               const float *found_inf_dev, int32_t *step_dev,
                               void *stream);
+
+/* Lion ([BNB] PR review: Lion applies decoupled decay to the parameter
+ * before its sign update; update rule of Chen et al., arXiv:2302.06675).
+ * Per element, in fp32 without contraction:
+ *   c = fl32(fl32(b1 m) + fl32(c1 g)),  p <- p (1 - lr wd) - lr sign(c),
+ *   m <- fl32(fl32(b2 m) + fl32(c2 g)),  sign(0) = 0,
+ * b1 = fl32(beta1), c1 = fl32(1-beta1) (likewise beta2), g = G * inv_scale.
+ * Plan algorithm OPTIM_ALGO_LION (param, grad, m).  The step counter
+ * advances as for the other steps.                                          */
+int optim_step_lion(optim_plan *plan, const optim_lion_hp *hp, float *lr_dev,
+                    const float *inv_scale_dev, const float *found_inf_dev,
+                    int32_t *step_dev, void *stream);
+
+/* LAMB, trust ratio per tensor ([BNB] PR description: LAMB shares the Adam
+ * kernels' decay ordering; update of You et al., arXiv:1904.00962, Alg. 2):
+ *   m, v as optim_step_adamw;  r = (m/bc1) / (sqrt(v)/sqrt(bc2) + eps)
+ *   u = r + wd p;  p <- p - lr (|p| / |u|) u   (norms over each tensor,
+ *   from the previous p; the ratio is 1 when either norm is 0).
+ * Plan algorithm OPTIM_ALGO_LAMB (param, grad, m, v).  Three kernels: moments
+ * and per-unit sums of p^2 and u^2, per-tensor ratios (fixed-order fp64
+ * sums), update.                                                             */
+int optim_step_lamb(optim_plan *plan, const optim_adamw_hp *hp, float *lr_dev,
+                    const float *inv_scale_dev, const float *found_inf_dev,
+                    int32_t *step_dev, void *stream);
 
 /* Blockwise-quantized AdEMAMix ([BNB]: the blockwise 8-bit kernel's
  * AdEMAMix branch, same decay ordering; the fresh step mixes in

@@ -19,7 +19,7 @@ OPTIM_OK = 0
 OPTIM_EINVAL, OPTIM_EALIGN, OPTIM_EDTYPE, OPTIM_EWORKSPACE, OPTIM_EUNSUPPORTED, OPTIM_EHIP = range(1, 7)
 OPTIM_F32, OPTIM_BF16 = 0, 1
 (OPTIM_ALGO_ADAMW, OPTIM_ALGO_ADEMAMIX, OPTIM_ALGO_ADAM_MINI, OPTIM_ALGO_BLOCKWISE,
- OPTIM_ALGO_BLOCKWISE_ADEMAMIX) = range(5)
+ OPTIM_ALGO_BLOCKWISE_ADEMAMIX, OPTIM_ALGO_LION, OPTIM_ALGO_LAMB) = range(7)
 OPTIM_MINI_FULL_V, OPTIM_MINI_HEAD, OPTIM_MINI_SCALAR = range(3)
 OPTIM_SCHED_NONE, OPTIM_SCHED_COSINE = 0, 1
 
@@ -29,7 +29,7 @@ EXPORTED = (
     "optim_step_8bit_blockwise", "optim_check_finite", "optim_remainder_split",
     "optim_remainder_reconstruct", "optim_quant_codebook", "optim_quantize_blockwise",
     "optim_dequantize_blockwise", "optim_grad_norm", "optim_scaler_update",
-    "optim_step_8bit_blockwise_ademamix",
+    "optim_step_8bit_blockwise_ademamix", "optim_step_lion", "optim_step_lamb",
 )
 
 
@@ -65,6 +65,10 @@ class optim_plan_opts(ctypes.Structure):
 
 class optim_adamw_hp(ctypes.Structure):
     _fields_ = [("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("eps", ctypes.c_double)]
+
+
+class optim_lion_hp(ctypes.Structure):
+    _fields_ = [("beta1", ctypes.c_double), ("beta2", ctypes.c_double)]
 
 
 class optim_ademamix_hp(ctypes.Structure):
@@ -108,6 +112,8 @@ def lib() -> ctypes.CDLL:
             "optim_scaler_update": ([_P, _P, _P, _P, f64, f64, i32, _P], i32),
             "optim_step_8bit_blockwise_ademamix": ([_P, ctypes.POINTER(optim_ademamix_hp), i32, i32, _P, _P,
                                                     _P, _P, _P], i32),
+            "optim_step_lion": ([_P, ctypes.POINTER(optim_lion_hp), _P, _P, _P, _P, _P], i32),
+            "optim_step_lamb": ([_P, ctypes.POINTER(optim_adamw_hp), _P, _P, _P, _P, _P], i32),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -233,6 +239,18 @@ def optim_step_8bit_blockwise(plan, hp: optim_adamw_hp, bits: int, block: int, l
                                            _ptr(inv_scale_dev), _ptr(found_inf_dev), _ptr(step_dev),
                                            _stream(stream)),
            "optim_step_8bit_blockwise")
+
+
+def optim_step_lion(plan, hp: optim_lion_hp, lr_dev, inv_scale_dev, found_inf_dev, step_dev,
+                    stream=None) -> None:
+    _check(lib().optim_step_lion(plan, ctypes.byref(hp), _ptr(lr_dev), _ptr(inv_scale_dev), _ptr(found_inf_dev),
+                                 _ptr(step_dev), _stream(stream)), "optim_step_lion")
+
+
+def optim_step_lamb(plan, hp: optim_adamw_hp, lr_dev, inv_scale_dev, found_inf_dev, step_dev,
+                    stream=None) -> None:
+    _check(lib().optim_step_lamb(plan, ctypes.byref(hp), _ptr(lr_dev), _ptr(inv_scale_dev), _ptr(found_inf_dev),
+                                 _ptr(step_dev), _stream(stream)), "optim_step_lamb")
 
 
 def optim_step_8bit_blockwise_ademamix(plan, hp: optim_ademamix_hp, bits: int, block: int, lr_dev,

@@ -118,7 +118,7 @@ bool is_blockwise(int32_t algo) { return algo == OPTIM_ALGO_BLOCKWISE || algo ==
 
 int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *opts, Built &B) {
     if (!list) return fail(OPTIM_EINVAL, "tensor list is NULL");
-    if (algo < OPTIM_ALGO_ADAMW || algo > OPTIM_ALGO_BLOCKWISE_ADEMAMIX)
+    if (algo < OPTIM_ALGO_ADAMW || algo > OPTIM_ALGO_LAMB)
         return fail(OPTIM_EINVAL, "unknown algorithm");
     const int n = list->n;
     if (n < 0) return fail(OPTIM_EINVAL, "negative tensor count");
@@ -161,8 +161,9 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     B.tile = tile;
     if (n > 0 && (!list->numel || !list->param || !list->grad || !list->weight_decay))
         return fail(OPTIM_EINVAL, "numel, param, grad and weight_decay arrays are required");
-    const bool need_mv = !is_blockwise(algo);
+    const bool need_mv = !is_blockwise(algo) && algo != OPTIM_ALGO_LION;
     if (n > 0 && need_mv && (!list->m || !list->v)) return fail(OPTIM_EINVAL, "m and v arrays are required");
+    if (n > 0 && algo == OPTIM_ALGO_LION && !list->m) return fail(OPTIM_EINVAL, "Lion needs the m array");
     if (n > 0 && algo == OPTIM_ALGO_ADEMAMIX && !list->m2)
         return fail(OPTIM_EINVAL, "AdEMAMix needs the m2 array");
     if (n > 0 && is_blockwise(algo) && (!list->qm || !list->qv || !list->absmax_m || !list->absmax_v))
@@ -246,6 +247,13 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
             add(T.m, numel * 4, true, "m");
             add(T.v, vlen * 4, true, "v");
         }
+        if (algo == OPTIM_ALGO_LION) {
+            T.m = static_cast<float *>(list->m[i]);
+            if (numel > 0 && !T.m) return fail(OPTIM_EINVAL, ti + "NULL m");
+            if (!aligned(T.m, 4)) return fail(OPTIM_EALIGN, ti + "m misaligned");
+            vec = vec && aligned(T.m, 16);
+            add(T.m, numel * 4, true, "m");
+        }
         if (algo == OPTIM_ALGO_ADEMAMIX) {
             T.m2 = static_cast<float *>(list->m2[i]);
             if (numel > 0 && !T.m2) return fail(OPTIM_EINVAL, ti + "NULL m2");
@@ -290,6 +298,12 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
                 if (B.nblocks == INT32_MAX) return fail(OPTIM_EUNSUPPORTED, "too many blocks");
                 ++B.nblocks;
             }
+        } else if (algo == OPTIM_ALGO_LAMB) {
+            // one block per tensor: its trust ratio
+            B.blockspan.push_back((int32_t)B.spans.size());
+            B.spans.push_back(SpanDesc{B.nunits, 0, numel, i, B.nblocks});
+            B.nunits += (numel + tile - 1) / tile;
+            ++B.nblocks;
         } else {
             B.spans.push_back(SpanDesc{B.nunits, 0, numel, i, -1});
             B.nunits += (numel + tile - 1) / tile;
@@ -326,7 +340,10 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     // norm pass (one per workgroup) share the region; they never overlap in
     // stream order
     L.partials = off;
-    B.npartials = std::max<int64_t>(algo == OPTIM_ALGO_ADAM_MINI ? B.nunits : 0,
+    // (LAMB: two per unit, sums of p^2 and u^2)
+    B.npartials = std::max<int64_t>(algo == OPTIM_ALGO_ADAM_MINI ? B.nunits
+                                    : algo == OPTIM_ALGO_LAMB    ? 2 * B.nunits
+                                                                 : 0,
                                     norm_partials(B.nunits, B.tile, B.grid));
     off += align256(std::max<int64_t>(1, B.npartials) * sizeof(double));
     L.blockfac = off; off += align256(std::max<int32_t>(1, B.nblocks) * sizeof(float));
@@ -580,6 +597,32 @@ int optim_step_adam_mini(optim_plan *plan, const optim_adamw_hp *hp, float *lr_d
                      step_dev, a);
     if (rc) return rc;
     HIP_OK(launch_adam_mini(a, plan->pk, plan->gk, static_cast<hipStream_t>(stream)));
+    return OPTIM_OK;
+}
+
+int optim_step_lion(optim_plan *plan, const optim_lion_hp *hp, float *lr_dev, const float *inv_scale_dev,
+                    const float *found_inf_dev, int32_t *step_dev, void *stream) {
+    int rc = check_plan(plan, OPTIM_ALGO_LION, "optim_step_lion");
+    if (rc) return rc;
+    if (!hp) return fail(OPTIM_EINVAL, "hyperparameters are NULL");
+    if ((rc = check_hp_beta(hp->beta1, "beta1")) || (rc = check_hp_beta(hp->beta2, "beta2"))) return rc;
+    StepArgs a;
+    rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, 0.0, lr_dev, inv_scale_dev, found_inf_dev, step_dev, a);
+    if (rc) return rc;
+    HIP_OK(launch_lion(a, plan->pk, plan->gk, static_cast<hipStream_t>(stream)));
+    return OPTIM_OK;
+}
+
+int optim_step_lamb(optim_plan *plan, const optim_adamw_hp *hp, float *lr_dev, const float *inv_scale_dev,
+                    const float *found_inf_dev, int32_t *step_dev, void *stream) {
+    int rc = check_plan(plan, OPTIM_ALGO_LAMB, "optim_step_lamb");
+    if (!rc) rc = check_adamw_hp(hp);
+    if (rc) return rc;
+    StepArgs a;
+    rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
+                     step_dev, a);
+    if (rc) return rc;
+    HIP_OK(launch_lamb(a, plan->pk, plan->gk, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
 

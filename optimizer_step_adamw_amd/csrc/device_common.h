@@ -385,6 +385,21 @@ __device__ __forceinline__ float uniform(float x) {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
+// ---------------------------------------------------------------- partial sums
+// Sum of x[i * stride] over i in [i0, i1), this lane taking i0 + lane,
+// i0 + lane + kThreads, ...: eight independent accumulators (loads in
+// flight together), combined in a fixed order -- deterministic.
+__device__ __forceinline__ double lane_sum(const double *x, int64_t stride, int64_t i0, int64_t i1) {
+    double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    int64_t i = i0 + threadIdx.x;
+    for (; i + 7 * kThreads < i1; i += 8 * kThreads) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] += x[(i + j * kThreads) * stride];
+    }
+    for (; i < i1; i += kThreads) acc[0] += x[i * stride];
+    return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
 // ---------------------------------------------------------------- AdamW / AdEMAMix
 struct AdamK {
     float b1, c1, b2, c2, b3, c3, alpha, eps, ss, isb2, ibc1, lr, inv_scale;

@@ -1,0 +1,215 @@
+// kernels_lion_lamb.hip -- Lion and LAMB step kernels (fp32 or bf16+remainder
+// params, fp32 or bf16 grads), in the streaming layout of the AdamW kernels.
+#include "device_common.h"
+
+namespace optim {
+namespace {
+
+// ---------------------------------------------------------------- Lion
+// [BNB] PR review: Lion applies decoupled decay to the parameter before its
+// sign update.  Per element (Chen et al., arXiv:2302.06675), fp32, no
+// contraction:
+//   c = b1 m + c1 g;  p <- p (1 - lr wd) - lr sign(c);  m <- b2 m + c2 g
+template <int PK, int GK, int N>
+__device__ __forceinline__ void lion_elems(const TensorDesc &T, int64_t e, const AdamK &k, float decay) {
+    float p[N], g[N], m[N];
+    load_p<PK, N>(T, e, p);
+    load_g<GK, N>(T.g, e, k.inv_scale, g);
+    ldf<N>(T.m, e, m);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        const float c = k.b1 * m[i] + k.c1 * g[i];
+        const float s = c > 0.0f ? 1.0f : (c < 0.0f ? -1.0f : 0.0f);
+        p[i] = p[i] * decay - k.lr * s;
+        m[i] = k.b2 * m[i] + k.c2 * g[i];
+    }
+    store_p<PK, N>(T, e, p);
+    stf<N>(T.m, e, m);
+}
+
+template <int PK, int GK>
+__global__ __launch_bounds__(kThreads) void lion_kernel(StepArgs a) {
+    __shared__ Scalars S;
+    step_begin(a, S);
+    const StepCommit commit{a, S};
+    if (S.skip) return;
+    const AdamK k = adam_consts(S);
+    for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
+        const TensorDesc &T = a.tensors[sp.tensor];
+        const float decay = uniform(S.decay[T.group]);
+        lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+            lion_elems<PK, GK, decltype(n)::value>(T, e, k, decay);
+        });
+    });
+}
+
+// ---------------------------------------------------------------- LAMB
+// You et al., arXiv:1904.00962, Algorithm 2, with Adam's direction as in the
+// AdamW kernel ([BNB] PR description: LAMB shares the Adam kernels):
+//   r = (m/bc1) / (sqrt(v)/sqrt(bc2) + eps),  u = r + wd p,
+//   p <- p - lr (|p|/|u|) u   per tensor.
+// Three kernels: moments + per-unit sums of p^2 and u^2 (from the previous
+// p) -> per-tensor factor lr |p|/|u| (fixed-order fp64 sums) -> update,
+// which recomputes u from the stored m, v and the untouched p with the same
+// fp32 operations.
+__device__ __forceinline__ float lamb_u(float p, float m, float v, const AdamK &k, float wd) {
+    const float h = sqrtf(v) * k.isb2 + k.eps;
+    return (m * k.ibc1) / h + wd * p;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+template <int PK, int GK>
+__global__ __launch_bounds__(kThreads) void lamb_moments_kernel(StepArgs a) {
+    __shared__ Scalars S;
+    step_begin(a, S);
+    const StepCommit commit{a, S};
+    if (S.skip) return;
+    const AdamK k = adam_consts(S);
+    __shared__ double red[2][kThreads / 64];
+    for_units(a, [&](int64_t u, const SpanDesc &sp, int64_t start, int64_t len) {
+        const TensorDesc &T = a.tensors[sp.tensor];
+        const float wd = uniform((float)a.prep.group_wd[T.group]);
+        float sp2 = 0.0f, su2 = 0.0f;
+        lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+            constexpr int N = decltype(n)::value;
+            float p[N], g[N], m[N], v[N];
+            load_p<PK, N>(T, e, p);
+            load_g<GK, N>(T.g, e, k.inv_scale, g);
+            ldf<N>(T.m, e, m);
+            ldf<N>(T.v, e, v);
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                m[i] = k.b1 * m[i] + k.c1 * g[i];
+                v[i] = k.b2 * v[i] + k.c2 * (g[i] * g[i]);
+                const float uu = lamb_u(p[i], m[i], v[i], k, wd);
+                sp2 += p[i] * p[i];
+                su2 += uu * uu;
+            }
+            stf<N>(T.m, e, m);
+            stf<N>(T.v, e, v);
+        });
+        sp2 = wave_sum(sp2);
+        su2 = wave_sum(su2);
+        if ((threadIdx.x & 63) == 0) {
+            red[0][threadIdx.x >> 6] = (double)sp2;
+            red[1][threadIdx.x >> 6] = (double)su2;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            double tp = 0.0, tu = 0.0;
+#pragma unroll
+            for (int w = 0; w < kThreads / 64; ++w) {
+                tp += red[0][w];
+                tu += red[1][w];
+            }
+            a.partials[2 * u] = tp;
+            a.partials[2 * u + 1] = tu;
+        }
+        __syncthreads();
+    });
+}
+
+__global__ __launch_bounds__(kThreads) void lamb_trust_kernel(StepArgs a) {
+    __shared__ Scalars S;
+    step_begin(a, S);
+    const StepCommit commit{a, S};
+    if (S.skip) return;
+    __shared__ double red[2][kThreads];
+    for (int b = blockIdx.x; b < a.nblocks; b += gridDim.x) {
+        const int si = a.blockspan[b];
+        const int64_t u0 = a.spans[si].unit_begin, u1 = a.spans[si + 1].unit_begin;
+        red[0][threadIdx.x] = lane_sum(a.partials, 2, u0, u1);
+        red[1][threadIdx.x] = lane_sum(a.partials + 1, 2, u0, u1);
+        __syncthreads();
+        for (int st = kThreads / 2; st > 0; st >>= 1) {
+            if ((int)threadIdx.x < st) {
+                red[0][threadIdx.x] += red[0][threadIdx.x + st];
+                red[1][threadIdx.x] += red[1][threadIdx.x + st];
+            }
+            __syncthreads();
+        }
+        if (threadIdx.x == 0) {
+            const double pn = red[0][0], un = red[1][0];
+            const double trust = (pn > 0.0 && un > 0.0) ? sqrt(pn) / sqrt(un) : 1.0;
+            a.blockfac[b] = (float)(S.lr64 * trust);
+        }
+        __syncthreads();
+    }
+}
+
+template <int PK, int GK>
+__global__ __launch_bounds__(kThreads) void lamb_update_kernel(StepArgs a) {
+    __shared__ Scalars S;
+    step_begin(a, S);
+    const StepCommit commit{a, S};
+    if (S.skip) return;
+    const AdamK k = adam_consts(S);
+    for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
+        const TensorDesc &T = a.tensors[sp.tensor];
+        const float wd = uniform((float)a.prep.group_wd[T.group]);
+        const float f = a.blockfac[sp.block];
+        lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+            constexpr int N = decltype(n)::value;
+            float p[N], m[N], v[N];
+            load_p<PK, N>(T, e, p);
+            ldf<N>(T.m, e, m);
+            ldf<N>(T.v, e, v);
+#pragma unroll
+            for (int i = 0; i < N; ++i) p[i] = p[i] - f * lamb_u(p[i], m[i], v[i], k, wd);
+            store_p<PK, N>(T, e, p);
+        });
+    });
+}
+
+}  // namespace
+
+hipError_t launch_lion(const StepArgs &a, int pk, int gk, hipStream_t s) {
+    if (pk == P_F32 && gk == G_F32)
+        LAUNCH_PERSISTENT((lion_kernel<P_F32, G_F32>), a, s);
+    else if (pk == P_F32 && gk == G_BF16)
+        LAUNCH_PERSISTENT((lion_kernel<P_F32, G_BF16>), a, s);
+    else if (pk == P_BF16R && gk == G_F32)
+        LAUNCH_PERSISTENT((lion_kernel<P_BF16R, G_F32>), a, s);
+    else
+        LAUNCH_PERSISTENT((lion_kernel<P_BF16R, G_BF16>), a, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_lamb(const StepArgs &args, int pk, int gk, hipStream_t s) {
+    // the moments and ratios read the step's inputs; the update publishes it
+    StepArgs a = args;
+    a.commit = 0;
+    if (pk == P_F32 && gk == G_F32)
+        LAUNCH_PERSISTENT((lamb_moments_kernel<P_F32, G_F32>), a, s);
+    else if (pk == P_F32 && gk == G_BF16)
+        LAUNCH_PERSISTENT((lamb_moments_kernel<P_F32, G_BF16>), a, s);
+    else if (pk == P_BF16R && gk == G_F32)
+        LAUNCH_PERSISTENT((lamb_moments_kernel<P_BF16R, G_F32>), a, s);
+    else
+        LAUNCH_PERSISTENT((lamb_moments_kernel<P_BF16R, G_BF16>), a, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (a.nblocks > 0) {
+        const int fg = a.nblocks < 2048 ? a.nblocks : 2048;
+        hipLaunchKernelGGL(lamb_trust_kernel, dim3(fg), dim3(kThreads), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    a.commit = 1;
+    if (pk == P_F32 && gk == G_F32)
+        LAUNCH_PERSISTENT((lamb_update_kernel<P_F32, G_F32>), a, s);
+    else if (pk == P_F32 && gk == G_BF16)
+        LAUNCH_PERSISTENT((lamb_update_kernel<P_F32, G_BF16>), a, s);
+    else if (pk == P_BF16R && gk == G_F32)
+        LAUNCH_PERSISTENT((lamb_update_kernel<P_BF16R, G_F32>), a, s);
+    else
+        LAUNCH_PERSISTENT((lamb_update_kernel<P_BF16R, G_BF16>), a, s);
+    return hipGetLastError();
+}
+
+}  // namespace optim

@@ -58,9 +58,7 @@ __global__ __launch_bounds__(kThreads) void mini_finalize_kernel(StepArgs a) {
         const int si = a.blockspan[b];
         const SpanDesc sp = a.spans[si];
         const int64_t u0 = sp.unit_begin, u1 = a.spans[si + 1].unit_begin;
-        double acc = 0.0;
-        for (int64_t u = u0 + threadIdx.x; u < u1; u += kThreads) acc += a.partials[u];
-        red[threadIdx.x] = acc;
+        red[threadIdx.x] = lane_sum(a.partials, 1, u0, u1);
         __syncthreads();
         for (int st = kThreads / 2; st > 0; st >>= 1) {
             if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];

@@ -154,6 +154,8 @@ struct StepArgs {
 hipError_t launch_adamw(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_ademamix(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_adam_mini(const StepArgs &a, int pk, int gk, hipStream_t s);
+hipError_t launch_lion(const StepArgs &a, int pk, int gk, hipStream_t s);
+hipError_t launch_lamb(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_blockwise(const StepArgs &a, int gk, bool ademamix, hipStream_t s);
 hipError_t launch_check_finite(const StepArgs &a, int gk, hipStream_t s);
 // Workgroups of the finite check / gradient norm pass for a plan.

@@ -27,7 +27,7 @@ def header_functions():
 
 def test_exports_every_declared_function(L):
     declared = header_functions()
-    assert len(declared) == 18, declared
+    assert len(declared) == 20, declared
     assert sorted(osa.EXPORTED) == declared
     for name in declared:
         assert hasattr(L, name), name
@@ -171,6 +171,20 @@ def test_blockwise_ademamix_validation(L):
     bad = dict(kw, qm2=[kw["qm"][0] + 8], absmax_m2=[f(64)])
     expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, **bad), osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX, opts))
     expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, **full), 5, opts))
+
+
+def test_lion_and_lamb_validation(L):
+    f = Fake()
+    n = 1000
+    lion = dict(m=[f(4 * n)], v=None)
+    assert ws(fake_list([n], fake=f, **lion), osa.OPTIM_ALGO_LION) > 0
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, m=None, v=None), osa.OPTIM_ALGO_LION))
+    assert ws(fake_list([n], fake=f), osa.OPTIM_ALGO_LAMB) > 0
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, v=None), osa.OPTIM_ALGO_LAMB))
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f), 7))
+    # LAMB keeps two partial sums per unit: its workspace exceeds AdamW's
+    assert ws(fake_list([1 << 20], fake=f), osa.OPTIM_ALGO_LAMB) > ws(fake_list([1 << 20], fake=f),
+                                                                         osa.OPTIM_ALGO_ADAMW)
 
 
 def test_null_plan_is_rejected_without_device(L):
