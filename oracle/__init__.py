@@ -65,6 +65,7 @@ _SIGS = {
                                        _d, _d, _d, _d, _d, _d, _d, _i64, _p, _p, _p],
     "oracle_lion_step": [_i64, _p, _p, _p, _d, _d, _d, _d],
     "oracle_lamb_step": [_i64, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64, _p],
+    "oracle_round_model_copy": [_i64, _i32, _p, _p],
     "oracle_sumsq": [_i64, _p],
     "oracle_clip_coef": [_d, _d],
     "oracle_scaler_update": [_p, _p, _i32, _d, _d, _i32],
@@ -174,6 +175,14 @@ def adam_mini_step(p, m, V, g, block, lr, beta1, beta2, eps, wd, t):
 def any_nonfinite(x) -> bool:
     x = _f64(x)
     return bool(lib().oracle_any_nonfinite(x.size, _ptr(x)))
+
+
+def round_model_copy(master_f32: np.ndarray, half: bool) -> np.ndarray:
+    """fp32 master -> bf16 or fp16 bit patterns, round to nearest even."""
+    u = np.ascontiguousarray(f32_bits(master_f32).ravel())
+    out = np.empty(u.size, np.uint16)
+    lib().oracle_round_model_copy(u.size, int(bool(half)), _ptr(u), _ptr(out))
+    return out
 
 
 def lion_step(p, m_f32, g_f32, lr, beta1, beta2, wd):

@@ -535,3 +535,67 @@ void oracle_lamb_step(int64_t n, double *p, double *m, double *v, const double *
     for (int64_t i = 0; i < n; ++i)
         p[i] = p[i] - lr * trust * u[i];
 }
+
+/* ------------------------------------------------------------------------ */
+/* Low-precision model copy of an fp32 master.  [TE] page, review thread:
+ * with master weights the model parameter is BF16 or FP16 and the FP32
+ * master is kept beside it (the remainder feature applies to BF16 only);
+ * after the step the model copy is the master rounded to the model dtype.
+ * Rounding is to nearest, ties to even (the IEEE default), written here from
+ * the bit patterns:
+ *   bf16: keep the top 16 bits of the fp32 pattern, rounded on the low 16;
+ *   fp16: 1 sign, 5 exponent (bias 15), 10 fraction bits; overflow to +-inf,
+ *         gradual underflow to subnormals and zero.
+ * NaN inputs map to a quiet NaN of the same sign.                          */
+uint16_t oracle_f32_to_bf16_rne(uint32_t u)
+{
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu))
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lo = u & 0xFFFFu, hi = u >> 16;
+    if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u)))
+        hi += 1u; /* a carry into the exponent is the correct rounding */
+    return (uint16_t)hi;
+}
+
+uint16_t oracle_f32_to_f16_rne(uint32_t u)
+{
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    uint32_t ex = (u >> 23) & 0xFFu, fr = u & 0x007FFFFFu;
+    if (ex == 0xFFu)
+        return (uint16_t)(sign | 0x7C00u | (fr ? 0x0200u : 0u));
+    /* value = 1.fr * 2^(ex-127) for normal fp32; fp32 subnormals are far
+     * below the fp16 range and round to zero */
+    if (ex == 0)
+        return sign;
+    int e = (int)ex - 127 + 15; /* fp16 biased exponent */
+    uint32_t mant = fr | 0x00800000u; /* 24-bit significand */
+    if (e >= 31)
+        return (uint16_t)(sign | 0x7C00u);
+    int shift; /* bits to drop from the 24-bit significand */
+    uint32_t out_exp;
+    if (e >= 1) {
+        shift = 13;
+        out_exp = (uint32_t)e;
+    } else {
+        shift = 14 - e; /* subnormal: the significand shifts further right */
+        out_exp = 0;
+        if (shift > 24)
+            return sign;
+    }
+    uint32_t kept = mant >> shift;
+    uint32_t rem = mant & ((1u << shift) - 1u), half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (kept & 1u)))
+        kept += 1u;
+    /* normal: kept holds the implicit bit at 2^10; subnormal: no implicit bit.
+     * A carry out of the fraction moves into the exponent field naturally. */
+    uint32_t bits = (out_exp ? ((out_exp << 10) + (kept - 0x400u)) : kept);
+    if (bits >= 0x7C00u)
+        return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | bits);
+}
+
+void oracle_round_model_copy(int64_t n, int to_half, const uint32_t *master, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = to_half ? oracle_f32_to_f16_rne(master[i]) : oracle_f32_to_bf16_rne(master[i]);
+}

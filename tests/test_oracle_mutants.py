@@ -176,6 +176,17 @@ MUTANTS = [
      ["test_lamb_fresh_step_direction"]),
     ("lamb_uncorrected_moments", "double r = (m[i] / bc1) / (sqrt(v[i]) / sqrt(bc2) + eps);",
      "double r = m[i] / (sqrt(v[i]) + eps);", ["test_lamb_fresh_step_direction"]),
+    # ---- low-precision model copy
+    ("bf16_copy_ties_away", "if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u)))", "if (lo >= 0x8000u)",
+     ["test_model_copy_bf16_is_torch_rne"]),
+    ("bf16_copy_truncates", "        hi += 1u; /* a carry into the exponent is the correct rounding */",
+     "        hi += 0u;", ["test_model_copy_bf16_is_torch_rne"]),
+    ("f16_copy_ties_up", "if (rem > half || (rem == half && (kept & 1u)))", "if (rem >= half)",
+     ["test_model_copy_f16_is_numpy_rne"]),
+    ("f16_copy_subnormal_shift", "shift = 14 - e; /* subnormal", "shift = 13 - e; /* subnormal",
+     ["test_model_copy_f16_is_numpy_rne"]),
+    ("f16_copy_exponent_bias", "int e = (int)ex - 127 + 15; /* fp16 biased exponent */",
+     "int e = (int)ex - 127 + 14; /* fp16 biased exponent */", ["test_model_copy_f16_is_numpy_rne"]),
     # ---- gradient clipping and loss scale
     ("sumsq_of_magnitudes", "        s += x[i] * x[i];\n    return s;", "        s += fabs(x[i]);\n    return s;",
      ["test_grad_norm_library_and_closed_form", "test_clip_matches_torch_clip_grad_norm"]),

@@ -655,3 +655,46 @@ def test_lamb_scale_equivariance(orc):
         orc.lamb_step(p, ma, va, g, lr, 0.9, 0.999, 1e-6, 0.0, t)
         orc.lamb_step(q, mb, vb, g, lr, 0.9, 0.999, 1e-6, 0.0, t)
     assert rel_tau(q, 8.0 * p, 1e-3) < 1e-13
+
+
+# ------------------------------------------------------------------ low-precision model copy
+def _patterns():
+    """Every high half of the fp32 pattern with the low halves that decide
+    rounding (exact, below / at / above the bf16 and the fp16 halfway
+    points, odd and even kept bits), plus random patterns."""
+    hi = np.arange(1 << 16, dtype=np.uint32) << np.uint32(16)
+    lows = np.array([0x0000, 0x0001, 0x0FFF, 0x1000, 0x1001, 0x2000, 0x3000, 0x7FFF, 0x8000, 0x8001,
+                     0xA000, 0xFFFF], np.uint32)
+    grid = (hi[:, None] | lows[None, :]).ravel()
+    rnd = np.random.default_rng(911).integers(0, 1 << 32, 1 << 20, dtype=np.uint64).astype(np.uint32)
+    return np.concatenate([grid, rnd])
+
+
+def test_model_copy_bf16_is_torch_rne(orc):
+    """Transformer Engine remainder page, review thread: with master weights
+    the model copy is the fp32 master rounded to the model dtype.  Referee:
+    torch's float32 -> bfloat16 cast (round to nearest even); NaNs stay NaN."""
+    u = _patterns()
+    x = u.view(np.float32)
+    got = orc.round_model_copy(x, half=False)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all((got[nan] & 0x7F80) == 0x7F80) and np.all(got[nan] & 0x007F)
+
+
+def test_model_copy_f16_is_numpy_rne(orc):
+    """Referee: numpy's float32 -> float16 cast (IEEE round to nearest even,
+    overflow to inf, gradual underflow), on the same patterns."""
+    u = _patterns()
+    x = u.view(np.float32)
+    got = orc.round_model_copy(x, half=True)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(got[nan].view(np.float16)))
+    # hand-worked: 65520 is the halfway point to 2^16 (rounds to inf), the
+    # smallest subnormal 2^-24 and half of it (a tie to even: zero)
+    assert orc.round_model_copy(np.float32([65504.0, 65519.0, 65520.0]), True).tolist() == [0x7BFF, 0x7BFF, 0x7C00]
+    assert orc.round_model_copy(np.float32([2.0 ** -24, 2.0 ** -25, 1.5 * 2.0 ** -25]), True).tolist() == [1, 0, 1]
