@@ -12,7 +12,8 @@ the Llama-shaped 1.1B bf16+remainder AMP list with device cosine lr (also
 timed as the full AMP loop with global-norm clipping folded into the step
 and the dynamic loss-scale update), the 268M-element blockwise 8-bit and
 4-bit states (2-state AdamW and 3-state AdEMAMix), Adam-mini over the 7B
-list, and Lion and LAMB on the 4096 x 4096 tensor.  Gradients are drawn once per workload, outside the timed region.
+list, and Lion, LAMB and AdamW with an fp32 master and a bf16 / fp16 model
+copy on the 4096 x 4096 tensor.  Gradients are drawn once per workload, outside the timed region.
 
 Timing: HIP events on the stream the library launches on (torch's current
 stream), one pair around every optimizer call inside the timed region; the
@@ -39,6 +40,7 @@ METRIC = "optimizer-step elements/s and achieved HBM GB/s (% of peak), fp32 and 
 B_ADAMW_F32 = 28.0            # R p g m v (16) + W p m v (12)
 B_ADEMAMIX_F32 = 36.0         # + m2 read and write
 B_LION_F32 = 20.0             # R p g m (12) + W p m (8)
+B_ADAMW_MASTER = 30.0         # R master g m v (16) + W master, 16-bit copy, m, v (14)
 B_BF16R_AMP = 26.0 + 2.0      # R bf16 p, int16 r, bf16 g, m, v (14) + W (12); + finite check g
 B_8BIT = 4 + 4 + 1 + 1 + 8 / 256 + 4 + 1 + 1 + 8 / 256
 B_4BIT = 4 + 4 + 0.5 + 0.5 + 8 / 128 + 4 + 0.5 + 0.5 + 8 / 128
@@ -55,8 +57,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--secondary", default="c1,c3,c4,c5,lion_lamb",
-                    help="comma list of secondary workloads (c1,c3,c4,c5,lion_lamb) or 'none'")
+    ap.add_argument("--secondary", default="c1,c3,c4,c5,lion_lamb,master",
+                    help="comma list of secondary workloads (c1,c3,c4,c5,lion_lamb,master) or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
@@ -203,6 +205,34 @@ def bench_lion_lamb(torch, osa, synth, steps, warmup):
                                            frac=gbs(B_ADAMW_F32 * n, per_call[1]) / PEAK_HBM_GBS,
                                            note="algorithmic 28 B/elem; the two passes move 40 B/elem "
                                                 "(p, m, v read again for the per-tensor trust ratio)")})
+
+
+def bench_master(torch, osa, synth, steps, warmup):
+    """AdamW with an fp32 master and a bf16 or fp16 model copy on the
+    4096 x 4096 tensor and gradients of the headline."""
+    wl = synth.c2_decay_stress()
+    n, hp = wl.numel, wl.hp
+    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
+    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
+    out = {}
+    for name, dt in (("adamw_master_bf16", osa.OPTIM_BF16), ("adamw_master_f16", osa.OPTIM_F16)):
+        master = p0.clone()
+        model = torch.zeros(n, dtype=torch.int16, device="cuda")
+        m = torch.zeros(n, device="cuda")
+        v = torch.zeros(n, device="cuda")
+        plan = osa.Plan(osa.TensorList([model], [g], m=[m], v=[v], master=[master], weight_decay=[hp.wd],
+                                       param_dtype=dt), osa.OPTIM_ALGO_ADAMW)
+        sc = scalars(torch, hp.lr)
+        h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
+        ms, _, _ = run_timed(torch, [lambda: osa.optim_step_adamw(plan.handle, h, sc["lr"], None, None,
+                                                                  sc["step"])], steps, warmup)
+        plan.close()
+        out[name] = dict(ms=ms, bytes_per_element=B_ADAMW_MASTER, gbs=gbs(B_ADAMW_MASTER * n, ms),
+                         frac=gbs(B_ADAMW_MASTER * n, ms) / PEAK_HBM_GBS)
+        del master, model, m, v
+    del p0, g
+    torch.cuda.empty_cache()
+    return dict(workload="adamw_master_copy_4096x4096", elements=n, kernels=out)
 
 
 def bench_c1(torch, osa, synth, steps, warmup):
@@ -461,7 +491,8 @@ def main():
         f"{json.dumps(head['kernels'])}")
     secondary = {}
     todo = [] if args.secondary == "none" else args.secondary.split(",")
-    fns = dict(c1=bench_c1, c3=bench_c3, c4=bench_c4, c5=bench_c5, lion_lamb=bench_lion_lamb)
+    fns = dict(c1=bench_c1, c3=bench_c3, c4=bench_c4, c5=bench_c5, lion_lamb=bench_lion_lamb,
+               master=bench_master)
     for key in todo:
         t0 = time.perf_counter()
         secondary[key] = fns[key](torch, osa, synth, args.steps, args.warmup)

@@ -46,7 +46,7 @@ extern "C" {
 #define OPTIM_EHIP 6         /* a HIP runtime call failed                  */
 
 /* ---- enumerations ------------------------------------------------------ */
-enum { OPTIM_F32 = 0, OPTIM_BF16 = 1 };
+enum { OPTIM_F32 = 0, OPTIM_BF16 = 1, OPTIM_F16 = 2 };
 enum {
     OPTIM_ALGO_ADAMW = 0,
     OPTIM_ALGO_ADEMAMIX = 1,
@@ -65,7 +65,8 @@ enum { OPTIM_SCHED_NONE = 0, OPTIM_SCHED_COSINE = 1 };
  * the algorithm does not use it) whose entries are device pointers.
  *
  *  numel        elements per tensor (> 0)
- *  param        F32: float[numel]; BF16: uint16 bf16 patterns[numel]
+ *  param        F32: float[numel]; BF16: uint16 bf16 patterns[numel];
+ *               F16 (with master only): uint16 fp16 patterns[numel]
  *  grad         F32 float[numel] or BF16 uint16[numel] (grad_dtype)
  *  m, v         float[numel] first / second moment (AdamW, AdEMAMix, LAMB,
  *               Adam-mini FULL_V).  Adam-mini HEAD/SCALAR: m float[numel]
@@ -79,6 +80,11 @@ enum { OPTIM_SCHED_NONE = 0, OPTIM_SCHED_COSINE = 1 };
  *  absmax_m/_v  float[ceil(numel/block)] per-block scale of qm / qv
  *  qm2,         blockwise AdEMAMix only: codes of the slow EMA m2 (signed,
  *  absmax_m2    layout as qm) and their per-block scale; NULL otherwise
+ *  master       float[numel] fp32 master weights of a BF16 or F16 model
+ *               param ([TE] review: master weights beside a low-precision
+ *               model param), AdamW and AdEMAMix only: the step updates the
+ *               master and rewrites param as the master rounded to nearest
+ *               even.  remainder must be NULL then.  NULL otherwise.
  *  weight_decay per-tensor decoupled decay (>= 0)
  *  mini_kind    Adam-mini only: OPTIM_MINI_*
  *  head_numel   Adam-mini only: block length for HEAD (must divide numel);
@@ -105,6 +111,7 @@ typedef struct optim_tensor_list {
     int32_t grad_dtype;
     void *const *qm2;
     float *const *absmax_m2;
+    float *const *master;
 } optim_tensor_list;
 
 /* Plan options (NULL = all defaults).

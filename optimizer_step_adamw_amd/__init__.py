@@ -17,7 +17,7 @@ from .build import LIB_PATH, build as build_library
 
 OPTIM_OK = 0
 OPTIM_EINVAL, OPTIM_EALIGN, OPTIM_EDTYPE, OPTIM_EWORKSPACE, OPTIM_EUNSUPPORTED, OPTIM_EHIP = range(1, 7)
-OPTIM_F32, OPTIM_BF16 = 0, 1
+OPTIM_F32, OPTIM_BF16, OPTIM_F16 = 0, 1, 2
 (OPTIM_ALGO_ADAMW, OPTIM_ALGO_ADEMAMIX, OPTIM_ALGO_ADAM_MINI, OPTIM_ALGO_BLOCKWISE,
  OPTIM_ALGO_BLOCKWISE_ADEMAMIX, OPTIM_ALGO_LION, OPTIM_ALGO_LAMB) = range(7)
 OPTIM_MINI_FULL_V, OPTIM_MINI_HEAD, OPTIM_MINI_SCALAR = range(3)
@@ -54,7 +54,7 @@ class optim_tensor_list(ctypes.Structure):
         ("head_numel", ctypes.POINTER(ctypes.c_int64)),
         ("param_dtype", ctypes.c_int32),
         ("grad_dtype", ctypes.c_int32),
-        ("qm2", _PP), ("absmax_m2", _PP),
+        ("qm2", _PP), ("absmax_m2", _PP), ("master", _PP),
     ]
 
 
@@ -150,7 +150,7 @@ class TensorList:
 
     def __init__(self, params: Sequence, grads: Sequence, *, m=None, v=None, m2=None,
                  remainders=None, qm=None, qv=None, absmax_m=None, absmax_v=None,
-                 qm2=None, absmax_m2=None,
+                 qm2=None, absmax_m2=None, master=None,
                  weight_decay: Sequence[float], mini_kind=None, head_numel=None,
                  param_dtype: int = OPTIM_F32, grad_dtype: int = OPTIM_F32,
                  numel: Optional[Sequence[int]] = None):
@@ -174,7 +174,7 @@ class TensorList:
         s.param, s.grad = parr(params), parr(grads)
         s.m, s.v, s.m2, s.remainder = parr(m), parr(v), parr(m2), parr(remainders)
         s.qm, s.qv, s.absmax_m, s.absmax_v = parr(qm), parr(qv), parr(absmax_m), parr(absmax_v)
-        s.qm2, s.absmax_m2 = parr(qm2), parr(absmax_m2)
+        s.qm2, s.absmax_m2, s.master = parr(qm2), parr(absmax_m2), parr(master)
         s.weight_decay = ctypes.cast(self._wd, ctypes.POINTER(ctypes.c_double))
         if mini_kind is not None:
             self._kind = (ctypes.c_int32 * max(n, 1))(*mini_kind)

@@ -122,12 +122,18 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
         return fail(OPTIM_EINVAL, "unknown algorithm");
     const int n = list->n;
     if (n < 0) return fail(OPTIM_EINVAL, "negative tensor count");
-    if (list->param_dtype != OPTIM_F32 && list->param_dtype != OPTIM_BF16)
-        return fail(OPTIM_EDTYPE, "param_dtype must be OPTIM_F32 or OPTIM_BF16");
+    const int32_t pdt = list->param_dtype;
+    if (pdt != OPTIM_F32 && pdt != OPTIM_BF16 && pdt != OPTIM_F16)
+        return fail(OPTIM_EDTYPE, "param_dtype must be OPTIM_F32, OPTIM_BF16 or OPTIM_F16");
     if (list->grad_dtype != OPTIM_F32 && list->grad_dtype != OPTIM_BF16)
         return fail(OPTIM_EDTYPE, "grad_dtype must be OPTIM_F32 or OPTIM_BF16");
-    const bool bf16p = list->param_dtype == OPTIM_BF16;
-    if (bf16p && is_blockwise(algo))
+    const bool masterw = list->master != nullptr;
+    if (masterw && pdt == OPTIM_F32) return fail(OPTIM_EINVAL, "master weights need a BF16 or F16 model param");
+    if (pdt == OPTIM_F16 && !masterw) return fail(OPTIM_EUNSUPPORTED, "F16 params need fp32 master weights");
+    if (masterw && algo != OPTIM_ALGO_ADAMW && algo != OPTIM_ALGO_ADEMAMIX)
+        return fail(OPTIM_EUNSUPPORTED, "master weights are supported for AdamW and AdEMAMix");
+    const bool bf16p = pdt == OPTIM_BF16 && !masterw;  // bf16 + remainder
+    if (pdt != OPTIM_F32 && is_blockwise(algo))
         return fail(OPTIM_EUNSUPPORTED, "blockwise states take fp32 params only");
     int bits = 0, block = 0;
     if (is_blockwise(algo)) {
@@ -175,7 +181,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     if (n > 0 && bf16p && !list->remainder)
         return fail(OPTIM_EUNSUPPORTED, "bf16 params need int16 remainders (fp32 master)");
 
-    const size_t psz = bf16p ? 2 : 4, gsz = list->grad_dtype == OPTIM_BF16 ? 2 : 4;
+    const size_t psz = pdt == OPTIM_F32 ? 4 : 2, gsz = list->grad_dtype == OPTIM_BF16 ? 2 : 4;
     std::vector<Range> ranges;
     B.tensors.assign(n, TensorDesc{});
     B.spans.clear();
@@ -216,7 +222,15 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
             vec = vec && aligned(T.rem, 16);
             add(T.rem, numel * 2, true, "remainder");
         } else if (list->remainder && list->remainder[i]) {
-            return fail(OPTIM_EINVAL, ti + "remainder given for fp32 params");
+            return fail(OPTIM_EINVAL, ti + (masterw ? "remainder given with master weights"
+                                                    : "remainder given for fp32 params"));
+        }
+        if (masterw) {
+            T.master = list->master[i];
+            if (numel > 0 && !T.master) return fail(OPTIM_EINVAL, ti + "NULL master");
+            if (!aligned(T.master, 4)) return fail(OPTIM_EALIGN, ti + "master misaligned");
+            vec = vec && aligned(T.master, 16);
+            add(T.master, numel * 4, true, "master");
         }
         int32_t kind = OPTIM_MINI_FULL_V;
         int64_t vlen = numel;
@@ -425,7 +439,10 @@ int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_p
     optim_plan *P = new (std::nothrow) optim_plan{};
     if (!P) return fail(OPTIM_EINVAL, "out of host memory");
     P->algo = algo;
-    P->pk = list->param_dtype == OPTIM_BF16 ? P_BF16R : P_F32;
+    P->pk = list->param_dtype == OPTIM_F32 ? P_F32
+            : !list->master                 ? P_BF16R
+            : list->param_dtype == OPTIM_BF16 ? P_MBF16
+                                              : P_MF16;
     P->gk = list->grad_dtype == OPTIM_BF16 ? G_BF16 : G_F32;
     P->bits = opts ? opts->bits : 0;
     P->block = opts ? opts->block : 0;

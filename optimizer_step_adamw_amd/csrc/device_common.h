@@ -29,6 +29,7 @@
 
 #include "plan.h"
 
+#include <hip/hip_fp16.h>
 #include <math.h>
 
 namespace optim {
@@ -167,16 +168,36 @@ __device__ __forceinline__ void sth(uint16_t *a, int64_t e, const uint32_t (&x)[
     }
 }
 
+// fp32 -> bf16 pattern, round to nearest even ([TE] review: the model copy
+// of an fp32 master is the master rounded to the model dtype); NaN stays a
+// quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// fp32 -> fp16 pattern: the hardware conversion, round to nearest even
+// (the default mode), fp16 denormals kept.
+__device__ __forceinline__ uint32_t f32_to_f16_rne(float x) {
+    return (uint32_t)__half_as_ushort(__float2half_rn(x));
+}
+
+// Parameters: fp32 (P_F32); bf16 + int16 remainder rebuilding the fp32
+// master (P_BF16R); or an fp32 master with a bf16 / fp16 model copy in p
+// (P_MBF16 / P_MF16), rewritten from the updated master.
 template <int PK, int N>
 __device__ __forceinline__ void load_p(const TensorDesc &T, int64_t e, float (&p)[N]) {
     if constexpr (PK == P_F32) {
         ldf<N>(static_cast<const float *>(T.p), e, p);
-    } else {
+    } else if constexpr (PK == P_BF16R) {
         uint32_t b[N], r[N];
         ldh<N>(static_cast<const uint16_t *>(T.p), e, b);
         ldh<N>(T.rem, e, r);
 #pragma unroll
         for (int k = 0; k < N; ++k) p[k] = rem_reconstruct(b[k], r[k]);
+    } else {
+        ldf<N>(T.master, e, p);
     }
 }
 
@@ -184,12 +205,18 @@ template <int PK, int N>
 __device__ __forceinline__ void store_p(const TensorDesc &T, int64_t e, const float (&p)[N]) {
     if constexpr (PK == P_F32) {
         stf<N>(static_cast<float *>(T.p), e, p);
-    } else {
+    } else if constexpr (PK == P_BF16R) {
         uint32_t b[N], r[N];
 #pragma unroll
         for (int k = 0; k < N; ++k) rem_split(p[k], b[k], r[k]);
         sth<N>(static_cast<uint16_t *>(T.p), e, b);
         sth<N>(T.rem, e, r);
+    } else {
+        stf<N>(T.master, e, p);
+        uint32_t c[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) c[k] = PK == P_MBF16 ? f32_to_bf16_rne(p[k]) : f32_to_f16_rne(p[k]);
+        sth<N>(static_cast<uint16_t *>(T.p), e, c);
     }
 }
 

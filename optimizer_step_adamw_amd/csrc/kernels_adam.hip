@@ -20,16 +20,22 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
 
 }  // namespace
 
+template <bool ADE, int PK>
+static void launch_adam_pk(const StepArgs &a, int gk, hipStream_t s) {
+    if (gk == G_F32)
+        LAUNCH_PERSISTENT((adam_kernel<PK, G_F32, ADE>), a, s);
+    else
+        LAUNCH_PERSISTENT((adam_kernel<PK, G_BF16, ADE>), a, s);
+}
+
 template <bool ADE>
 static hipError_t launch_adam_t(const StepArgs &a, int pk, int gk, hipStream_t s) {
-    if (pk == P_F32 && gk == G_F32)
-        LAUNCH_PERSISTENT((adam_kernel<P_F32, G_F32, ADE>), a, s);
-    else if (pk == P_F32 && gk == G_BF16)
-        LAUNCH_PERSISTENT((adam_kernel<P_F32, G_BF16, ADE>), a, s);
-    else if (pk == P_BF16R && gk == G_F32)
-        LAUNCH_PERSISTENT((adam_kernel<P_BF16R, G_F32, ADE>), a, s);
-    else
-        LAUNCH_PERSISTENT((adam_kernel<P_BF16R, G_BF16, ADE>), a, s);
+    switch (pk) {
+    case P_F32: launch_adam_pk<ADE, P_F32>(a, gk, s); break;
+    case P_BF16R: launch_adam_pk<ADE, P_BF16R>(a, gk, s); break;
+    case P_MBF16: launch_adam_pk<ADE, P_MBF16>(a, gk, s); break;
+    default: launch_adam_pk<ADE, P_MF16>(a, gk, s); break;
+    }
     return hipGetLastError();
 }
 

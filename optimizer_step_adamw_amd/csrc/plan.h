@@ -22,10 +22,11 @@ constexpr int64_t kMinTile = 1024;   // one group of 4 elements per lane
 constexpr int64_t kMinBlockwiseTile = 2048;  // one quantizer row: 256 lanes x 8 elements
 constexpr int kMaxGroups = 64;    // distinct weight-decay values per plan
 
-enum ParamKind { P_F32 = 0, P_BF16R = 1 };  // fp32, or bf16 + int16 remainder
+// fp32; bf16 + int16 remainder; fp32 master + bf16 or fp16 model copy
+enum ParamKind { P_F32 = 0, P_BF16R = 1, P_MBF16 = 2, P_MF16 = 3 };
 enum GradKind { G_F32 = 0, G_BF16 = 1 };
 
-struct TensorDesc {       // 128 bytes
+struct TensorDesc {       // 136 bytes
     void *p;              // param (fp32 or bf16 patterns)
     const void *g;        // gradient
     float *m;             // first moment
@@ -42,8 +43,9 @@ struct TensorDesc {       // 128 bytes
     int32_t pad_;
     uint8_t *qm2;         // blockwise AdEMAMix: codes of m2
     float *am2;           // blockwise AdEMAMix: absmax of m2
+    float *master;        // fp32 master of a bf16 / fp16 model param (p)
 };
-static_assert(sizeof(TensorDesc) == 128, "TensorDesc layout");
+static_assert(sizeof(TensorDesc) == 136, "TensorDesc layout");
 
 struct SpanDesc {         // 32 bytes
     int64_t unit_begin;   // first global unit number of this span

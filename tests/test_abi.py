@@ -187,6 +187,27 @@ def test_lion_and_lamb_validation(L):
                                                                          osa.OPTIM_ALGO_ADAMW)
 
 
+def test_master_weight_validation(L):
+    f = Fake()
+    n = 1000
+    mw = dict(params=[f(2 * n)], master=[f(4 * n)])
+    for dt in (osa.OPTIM_BF16, osa.OPTIM_F16):
+        for algo in (osa.OPTIM_ALGO_ADAMW, osa.OPTIM_ALGO_ADEMAMIX):
+            extra = dict(m2=[f(4 * n)]) if algo == osa.OPTIM_ALGO_ADEMAMIX else {}
+            assert ws(fake_list([n], fake=f, param_dtype=dt, **mw, **extra), algo) > 0
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, master=[f(4 * n)]), osa.OPTIM_ALGO_ADAMW))
+    expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(
+        fake_list([n], fake=f, params=[f(2 * n)], param_dtype=osa.OPTIM_F16), osa.OPTIM_ALGO_ADAMW))
+    expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(
+        fake_list([n], fake=f, param_dtype=osa.OPTIM_BF16, v=None, **mw), osa.OPTIM_ALGO_LION))
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(
+        fake_list([n], fake=f, param_dtype=osa.OPTIM_BF16, remainders=[f(2 * n)], **mw), osa.OPTIM_ALGO_ADAMW))
+    p = f(4 * n)
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(  # master overlapping the model copy
+        fake_list([n], fake=f, params=[p], master=[p + 16], param_dtype=osa.OPTIM_BF16), osa.OPTIM_ALGO_ADAMW))
+    expect_error(osa.OPTIM_EDTYPE, lambda: ws(fake_list([n], fake=f, param_dtype=3), osa.OPTIM_ALGO_ADAMW))
+
+
 def test_null_plan_is_rejected_without_device(L):
     expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_step_adamw(
         None, osa.optim_adamw_hp(0.9, 0.999, 1e-8), 1 << 40, None, None, 1 << 41, 0))
