@@ -66,6 +66,7 @@ _SIGS = {
     "oracle_lion_step": [_i64, _p, _p, _p, _d, _d, _d, _d],
     "oracle_lamb_step": [_i64, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64, _p],
     "oracle_round_model_copy": [_i64, _i32, _p, _p],
+    "oracle_adamw_scaled_step": [_i64, _i32, _p, _p, _p, _p, _p, _p, _d, _d, _d, _d, _d, _i64, _p, _p],
     "oracle_sumsq": [_i64, _p],
     "oracle_clip_coef": [_d, _d],
     "oracle_scaler_update": [_p, _p, _i32, _d, _d, _i32],
@@ -183,6 +184,22 @@ def round_model_copy(master_f32: np.ndarray, half: bool) -> np.ndarray:
     out = np.empty(u.size, np.uint16)
     lib().oracle_round_model_copy(u.size, int(bool(half)), _ptr(u), _ptr(out))
     return out
+
+
+def adamw_scaled_step(p, qm, qv, sm, sv, g_f32, half, lr, beta1, beta2, eps, wd, t):
+    """AdamW with per-tensor scaled 16-bit moments (fp16 if half, else bf16):
+    qm, qv uint16 patterns and sm, sv float32[1] scales, all in place.
+    Returns the fp32 moments before rescaling."""
+    for a in (qm, qv):
+        assert a.dtype == np.uint16 and a.flags["C_CONTIGUOUS"]
+    for a in (sm, sv):
+        assert a.dtype == np.float32 and a.size == 1
+    g = np.ascontiguousarray(g_f32, np.float32).ravel()
+    m32, v32 = np.empty(p.size, np.float32), np.empty(p.size, np.float32)
+    lib().oracle_adamw_scaled_step(p.size, int(bool(half)), _ptr(p), _ptr(qm), _ptr(qv), _ptr(sm),
+                                   _ptr(sv), _ptr(g), lr, beta1, beta2, eps, wd, t, _ptr(m32),
+                                   _ptr(v32))
+    return m32, v32
 
 
 def lion_step(p, m_f32, g_f32, lr, beta1, beta2, wd):

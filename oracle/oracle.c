@@ -35,6 +35,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <string.h>
 
 #define F32(x) ((double)(float)(x)) /* one rounding to float, kept as double */
 
@@ -598,4 +599,83 @@ void oracle_round_model_copy(int64_t n, int to_half, const uint32_t *master, uin
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = to_half ? oracle_f32_to_f16_rne(master[i]) : oracle_f32_to_bf16_rne(master[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* AdamW with per-tensor scaled 16-bit moments.  [TE] review thread shows the
+ * state scaling of the fused optimizer: a state kept in a low-precision
+ * dtype with a per-tensor scale, the fp32 value being stored * scale, and a
+ * new state written as (fp32 value * rscale) copied into the low-precision
+ * tensor.  The page shows no rule for the scale; reading used here: fp16
+ * states take scale = fl32(amax / 65504) over the tensor's new state (1 if
+ * the state is all zero) and rscale = fl32(1 / scale), so the largest
+ * magnitude lands on the top of the fp16 range; bf16 states keep scale 1
+ * (bf16 has the range of fp32).  One tensor, fp32-faithful state recipe:
+ *   m~ = fl32(h(qm) * sm), v~ = fl32(h(qv) * sv)      (h = 16-bit value)
+ *   m = fl32(fl32(b1 m~) + fl32(c1 g)),  v = fl32(fl32(b2 v~) + fl32(c2 fl32(g g)))
+ *   p <- p (1 - lr wd) - (lr/bc1) m / (sqrt(v)/sqrt(bc2) + eps)   (double)
+ *   sm' = scale(max |m|), qm = rne16(fl32(m * fl32(1/sm'))), likewise v.
+ * half = 1: fp16 states; 0: bf16 states.  qm, qv hold 16-bit patterns.    */
+static double h16_to_double(uint16_t b, int half)
+{
+    if (!half) {
+        uint32_t u = (uint32_t)b << 16;
+        float f;
+        memcpy(&f, &u, 4);
+        return (double)f;
+    }
+    int s = (b >> 15) & 1, e = (b >> 10) & 31, f = b & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(f | 1024), e - 25);
+    return s ? -v : v;
+}
+
+static uint16_t f32_to_16(float x, int half)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    return half ? oracle_f32_to_f16_rne(u) : oracle_f32_to_bf16_rne(u);
+}
+
+void oracle_adamw_scaled_step(int64_t n, int half, double *p, uint16_t *qm, uint16_t *qv,
+                              float *sm, float *sv, const float *g, double lr, double beta1,
+                              double beta2, double eps, double wd, int64_t t, float *scratch_m,
+                              float *scratch_v)
+{
+    double b1 = F32(beta1), c1 = F32(1.0 - beta1);
+    double b2 = F32(beta2), c2 = F32(1.0 - beta2);
+    double bc1 = 1.0 - pow(beta1, (double)t);
+    double bc2 = 1.0 - pow(beta2, (double)t);
+    double am = 0.0, av = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        double gi = (double)g[i];
+        double mt = F32(h16_to_double(qm[i], half) * (double)*sm);
+        double vt = F32(h16_to_double(qv[i], half) * (double)*sv);
+        double mi = F32(F32(b1 * mt) + F32(c1 * gi));
+        double vi = F32(F32(b2 * vt) + F32(c2 * F32(gi * gi)));
+        scratch_m[i] = (float)mi;
+        scratch_v[i] = (float)vi;
+        if (fabs(mi) > am) am = fabs(mi);
+        if (fabs(vi) > av) av = fabs(vi);
+        p[i] = p[i] * (1.0 - lr * wd);
+        double h = sqrt(vi) / sqrt(bc2) + eps;
+        p[i] = p[i] - (lr / bc1) * mi / h;
+    }
+    float nsm = 1.0f, nsv = 1.0f;
+    if (half) {
+        if (am > 0.0) nsm = (float)(am / 65504.0);
+        if (av > 0.0) nsv = (float)(av / 65504.0);
+    }
+    float rm = (float)(1.0 / (double)nsm), rv = (float)(1.0 / (double)nsv);
+    for (int64_t i = 0; i < n; ++i) {
+        qm[i] = f32_to_16((float)((double)scratch_m[i] * (double)rm), half);
+        qv[i] = f32_to_16((float)((double)scratch_v[i] * (double)rv), half);
+    }
+    *sm = nsm;
+    *sv = nsv;
 }

@@ -187,6 +187,18 @@ MUTANTS = [
      ["test_model_copy_f16_is_numpy_rne"]),
     ("f16_copy_exponent_bias", "int e = (int)ex - 127 + 15; /* fp16 biased exponent */",
      "int e = (int)ex - 127 + 14; /* fp16 biased exponent */", ["test_model_copy_f16_is_numpy_rne"]),
+    # ---- scaled 16-bit moments
+    ("scaled_state_not_unscaled", "double mt = F32(h16_to_double(qm[i], half) * (double)*sm);",
+     "double mt = F32(h16_to_double(qm[i], half));", ["test_scaled_fp16_states_track_fp32_adamw"]),
+    ("scaled_state_scale_without_range", "if (am > 0.0) nsm = (float)(am / 65504.0);",
+     "if (am > 0.0) nsm = (float)am;", ["test_scaled_states_fresh_step"]),
+    ("scaled_state_not_rescaled", "qm[i] = f32_to_16((float)((double)scratch_m[i] * (double)rm), half);",
+     "qm[i] = f32_to_16(scratch_m[i], half);", ["test_scaled_states_fresh_step", "test_scaled_states_round_trip_precision"]),
+    ("scaled_state_decay_after", "        p[i] = p[i] * (1.0 - lr * wd);\n        double h = sqrt(vi) / sqrt(bc2) + eps;\n"
+     "        p[i] = p[i] - (lr / bc1) * mi / h;\n    }\n    float nsm",
+     "        double h = sqrt(vi) / sqrt(bc2) + eps;\n"
+     "        p[i] = (p[i] - (lr / bc1) * mi / h) * (1.0 - lr * wd);\n    }\n    float nsm",
+     ["test_scaled_states_fresh_step"]),
     # ---- gradient clipping and loss scale
     ("sumsq_of_magnitudes", "        s += x[i] * x[i];\n    return s;", "        s += fabs(x[i]);\n    return s;",
      ["test_grad_norm_library_and_closed_form", "test_clip_matches_torch_clip_grad_norm"]),
@@ -205,18 +217,20 @@ MUTANTS = [
     # ---- blockwise-quantized step
     ("blockwise_decay_after_update",
      "        p[i] = p[i] * (1.0 - lr * wd);\n        double h = sqrt(vi) / sqrt(bc2) + eps;\n"
-     "        p[i] = p[i] - (lr / bc1) * mi / h;",
+     "        p[i] = p[i] - (lr / bc1) * mi / h;\n    }\n    oracle_quantize",
      "        double h = sqrt(vi) / sqrt(bc2) + eps;\n"
-     "        p[i] = (p[i] - (lr / bc1) * mi / h) * (1.0 - lr * wd);",
+     "        p[i] = (p[i] - (lr / bc1) * mi / h) * (1.0 - lr * wd);\n    }\n    oracle_quantize",
      ["test_blockwise_fresh_step"]),
-    ("blockwise_v_of_g_not_g_squared", "F32(c2 * F32(gi * gi)));\n        scratch_m[i] = (float)mi;\n        scratch_v",
-     "F32(c2 * fabs(gi)));\n        scratch_m[i] = (float)mi;\n        scratch_v", ["test_blockwise_fresh_step"]),
+    ("blockwise_v_of_g_not_g_squared",
+     "double vi = F32(F32(b2 * (double)scratch_v[i]) + F32(c2 * F32(gi * gi)));\n        scratch_m[i] = (float)mi;\n        scratch_v",
+     "double vi = F32(F32(b2 * (double)scratch_v[i]) + F32(c2 * fabs(gi)));\n        scratch_m[i] = (float)mi;\n        scratch_v",
+     ["test_blockwise_fresh_step"]),
     ("blockwise_m_with_unsigned_map", "oracle_quantize(n, block, bm, 1, scratch_m, Tm, qm, am);\n    oracle_quantize(n, block, bv",
      "oracle_quantize(n, block, bm, 0, scratch_m, Tm, qm, am);\n    oracle_quantize(n, block, bv",
      ["test_blockwise_fresh_step"]),
     ("blockwise_beta_weights_swapped",
-     "double b1 = F32(beta1), c1 = F32(1.0 - beta1);\n    double b2 = F32(beta2), c2 = F32(1.0 - beta2);\n    double bc1",
-     "double c1 = F32(beta1), b1 = F32(1.0 - beta1);\n    double b2 = F32(beta2), c2 = F32(1.0 - beta2);\n    double bc1",
+     "oracle_thresholds(1 << bv, Mv, Tv);\n\n    double b1 = F32(beta1), c1 = F32(1.0 - beta1);\n    double b2 = F32(beta2), c2 = F32(1.0 - beta2);\n    double bc1",
+     "oracle_thresholds(1 << bv, Mv, Tv);\n\n    double c1 = F32(beta1), b1 = F32(1.0 - beta1);\n    double b2 = F32(beta2), c2 = F32(1.0 - beta2);\n    double bc1",
      ["test_blockwise_fresh_step"]),
 ]
 

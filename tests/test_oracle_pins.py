@@ -698,3 +698,71 @@ def test_model_copy_f16_is_numpy_rne(orc):
     # smallest subnormal 2^-24 and half of it (a tie to even: zero)
     assert orc.round_model_copy(np.float32([65504.0, 65519.0, 65520.0]), True).tolist() == [0x7BFF, 0x7BFF, 0x7C00]
     assert orc.round_model_copy(np.float32([2.0 ** -24, 2.0 ** -25, 1.5 * 2.0 ** -25]), True).tolist() == [1, 0, 1]
+
+
+# ------------------------------------------------------------------ scaled 16-bit moments
+def _scaled_run(orc, half, steps, n=3000, key=0):
+    p = host_normal(n, 0.02, 912, key, 0, 0).astype(np.float64)
+    q = p.copy()
+    qm, qv = np.zeros(n, np.uint16), np.zeros(n, np.uint16)
+    sm, sv = np.ones(1, np.float32), np.ones(1, np.float32)
+    m, v = np.zeros(n), np.zeros(n)
+    out = []
+    for t in range(1, steps + 1):
+        g = host_normal(n, 1e-3, 912, key, t, 1)
+        m32, v32 = orc.adamw_scaled_step(p, qm, qv, sm, sv, g, half, 1e-3, 0.9, 0.999, 1e-8, 0.1, t)
+        orc.adamw_step(q, m, v, g.astype(np.float64), 1e-3, 0.9, 0.999, 1e-8, 0.1, t)
+        out.append((m32, v32))
+    return p, q, qm, qv, sm, sv, out
+
+
+def _h(bits, half):
+    return bits.view(np.float16).astype(np.float64) if half else orc_bf16(bits)
+
+
+def orc_bf16(bits):
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("half", [True, False])
+def test_scaled_states_fresh_step(orc, half):
+    """Transformer Engine page, review thread (state scaling: stored * scale
+    is the fp32 state; the new state is value * rscale copied into the
+    low-precision tensor).  From zero states the fp32 moments are the fresh
+    products of g and the update is AdamW's (the states used are fp32); fp16
+    states put the tensor's largest |m| on 65504 with scale = amax/65504,
+    bf16 states keep scale 1 and are the moments rounded to nearest even."""
+    p, q, qm, qv, sm, sv, out = _scaled_run(orc, half, 1)
+    m32, v32 = out[0]
+    assert rel_tau(p, q, 1e-3) < 2e-6
+    for bits, s, st in ((qm, sm, m32), (qv, sv, v32)):
+        if half:
+            assert np.max(np.abs(bits.view(np.float16).astype(np.float64))) == 65504.0
+            assert s[0] == np.float32(np.float64(np.max(np.abs(st))) / 65504.0)
+        else:
+            assert s[0] == 1.0 and np.array_equal(bits, orc.round_model_copy(st, False))
+
+
+@pytest.mark.parametrize("half", [True, False])
+def test_scaled_states_round_trip_precision(orc, half):
+    """stored * scale reproduces every moment that is not tiny against the
+    tensor's largest to the 16-bit format's half-ulp (2^-11 fp16, 2^-8 bf16)."""
+    _, _, qm, qv, sm, sv, out = _scaled_run(orc, half, 3)
+    m32, v32 = out[-1]
+    tol = 2.0 ** -11 if half else 2.0 ** -8
+    for bits, s, st in ((qm, sm, m32), (qv, sv, v32)):
+        back = np.float32(_h(bits, half) * np.float64(s[0]))
+        big = np.abs(st) >= np.max(np.abs(st)) * 2.0 ** -12
+        rel = np.abs(back[big].astype(np.float64) - st[big]) / np.abs(st[big])
+        assert np.max(rel) <= tol * (1 + 1e-6)
+
+
+def test_scaled_fp16_states_track_fp32_adamw(orc):
+    """Over 20 steps the fp16-state trajectory stays close to fp32-state
+    AdamW (relerr_tau 5.3e-3: the smallest second moments sit in fp16's
+    subnormal range after scaling); bf16 states, with 8 significant bits,
+    drift several times further."""
+    p16, q, *_ = _scaled_run(orc, True, 20)
+    pb, qb, *_ = _scaled_run(orc, False, 20)
+    e16, eb = rel_tau(p16, q, 1e-3), rel_tau(pb, qb, 1e-3)
+    assert e16 < 1e-2 and e16 < eb / 4
