@@ -41,6 +41,8 @@ B_ADAMW_F32 = 28.0            # R p g m v (16) + W p m v (12)
 B_ADEMAMIX_F32 = 36.0         # + m2 read and write
 B_LION_F32 = 20.0             # R p g m (12) + W p m (8)
 B_ADAMW_MASTER = 30.0         # R master g m v (16) + W master, 16-bit copy, m, v (14)
+B_ADAMW_STATES16 = 20.0       # R p g (8) + 16-bit m v (4); W p (4) + 16-bit m v (4)
+T_ADAMW_STATES16 = 28.0       # fp16: two passes, the second re-reads g, m, v (8)
 B_BF16R_AMP = 26.0 + 2.0      # R bf16 p, int16 r, bf16 g, m, v (14) + W (12); + finite check g
 B_8BIT = 4 + 4 + 1 + 1 + 8 / 256 + 4 + 1 + 1 + 8 / 256
 B_4BIT = 4 + 4 + 0.5 + 0.5 + 8 / 128 + 4 + 0.5 + 0.5 + 8 / 128
@@ -57,8 +59,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--secondary", default="c1,c3,c4,c5,lion_lamb,master",
-                    help="comma list of secondary workloads (c1,c3,c4,c5,lion_lamb,master) or 'none'")
+    ap.add_argument("--secondary", default="c1,c3,c4,c5,lion_lamb,master,states16",
+                    help="comma list of secondary workloads (c1,c3,c4,c5,lion_lamb,master,states16) or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
@@ -233,6 +235,36 @@ def bench_master(torch, osa, synth, steps, warmup):
     del p0, g
     torch.cuda.empty_cache()
     return dict(workload="adamw_master_copy_4096x4096", elements=n, kernels=out)
+
+
+def bench_states16(torch, osa, synth, steps, warmup):
+    """AdamW with fp16 or bf16 moments and per-tensor scales on the
+    4096 x 4096 fp32 tensor and gradients of the headline.  frac is priced on
+    the algorithmic 20 B/element; the two-pass fp16 step moves 28."""
+    wl = synth.c2_decay_stress()
+    n, hp = wl.numel, wl.hp
+    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
+    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
+    out = {}
+    for name, sdt in (("adamw_states_f16", osa.OPTIM_F16), ("adamw_states_bf16", osa.OPTIM_BF16)):
+        p = p0.clone()
+        m = torch.zeros(n, dtype=torch.int16, device="cuda")
+        v = torch.zeros(n, dtype=torch.int16, device="cuda")
+        sm, sv = torch.ones(1, device="cuda"), torch.ones(1, device="cuda")
+        plan = osa.Plan(osa.TensorList([p], [g], m=[m], v=[v], scale_m=[sm], scale_v=[sv], weight_decay=[hp.wd]),
+                        osa.OPTIM_ALGO_ADAMW, state_dtype=sdt)
+        sc = scalars(torch, hp.lr)
+        h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
+        ms, _, _ = run_timed(torch, [lambda: osa.optim_step_adamw(plan.handle, h, sc["lr"], None, None,
+                                                                  sc["step"])], steps, warmup)
+        plan.close()
+        moved = T_ADAMW_STATES16 if sdt == osa.OPTIM_F16 else B_ADAMW_STATES16  # bf16: one pass
+        out[name] = dict(ms=ms, bytes_per_element=B_ADAMW_STATES16, moved_per_element=moved,
+                         gbs=gbs(B_ADAMW_STATES16 * n, ms), frac=gbs(B_ADAMW_STATES16 * n, ms) / PEAK_HBM_GBS)
+        del p, m, v
+    del p0, g
+    torch.cuda.empty_cache()
+    return dict(workload="adamw_scaled_states_fp32_4096x4096", elements=n, kernels=out)
 
 
 def bench_c1(torch, osa, synth, steps, warmup):
@@ -492,7 +524,7 @@ def main():
     secondary = {}
     todo = [] if args.secondary == "none" else args.secondary.split(",")
     fns = dict(c1=bench_c1, c3=bench_c3, c4=bench_c4, c5=bench_c5, lion_lamb=bench_lion_lamb,
-               master=bench_master)
+               master=bench_master, states16=bench_states16)
     for key in todo:
         t0 = time.perf_counter()
         secondary[key] = fns[key](torch, osa, synth, args.steps, args.warmup)

@@ -80,6 +80,9 @@ enum { OPTIM_SCHED_NONE = 0, OPTIM_SCHED_COSINE = 1 };
  *  absmax_m/_v  float[ceil(numel/block)] per-block scale of qm / qv
  *  qm2,         blockwise AdEMAMix only: codes of the slow EMA m2 (signed,
  *  absmax_m2    layout as qm) and their per-block scale; NULL otherwise
+ *  scale_m,     AdamW plans with 16-bit states (opts->state_dtype): one
+ *  scale_v      device float per tensor, the scale of its stored m / v
+ *               (1.0 for a fresh state); m and v are then uint16 patterns
  *  master       float[numel] fp32 master weights of a BF16 or F16 model
  *               param ([TE] review: master weights beside a low-precision
  *               model param), AdamW and AdEMAMix only: the step updates the
@@ -112,6 +115,8 @@ typedef struct optim_tensor_list {
     void *const *qm2;
     float *const *absmax_m2;
     float *const *master;
+    float *const *scale_m;
+    float *const *scale_v;
 } optim_tensor_list;
 
 /* Plan options (NULL = all defaults).
@@ -120,13 +125,17 @@ typedef struct optim_tensor_list {
  *  grid        0 (default): one workgroup per work unit; > 0: a persistent
  *              grid of that many workgroups walking the units grid-stride
  *  tile        elements per work unit, a power of two in [1024, 2^24]
- *              (blockwise: at least 2048); 0 = 2048 (Adam-mini 4096,
- *              blockwise 16384)                                            */
+ *              (blockwise: at least 2048); 0 = 2048 (Adam-mini and fp16
+ *              states 4096, blockwise 16384)
+ *  state_dtype AdamW only: OPTIM_F32 (0, default) fp32 moments; OPTIM_F16
+ *              or OPTIM_BF16 16-bit moments with a per-tensor scale
+ *              ([TE] review: state scaling), see optim_step_adamw         */
 typedef struct optim_plan_opts {
     int32_t bits;
     int32_t block;
     int32_t grid;
     int32_t tile;
+    int32_t state_dtype;
 } optim_plan_opts;
 
 /* Hyperparameters, validated as in [MINI] AdamWMini's constructor:
@@ -201,7 +210,19 @@ int optim_plan_set_schedule(optim_plan *plan, int32_t kind, double lr_max,
  * eps placement).  Bias corrections are evaluated in fp64 on the device and
  * rounded once to fp32; the element math is fp32.  With BF16 params the
  * fp32 master is rebuilt from (param, remainder), updated, and split back
- * ([TE] description).                                                     */
+ * ([TE] description).
+ *
+ * With 16-bit states (plan opts state_dtype OPTIM_F16 / OPTIM_BF16; [TE]
+ * review: a scaled low-precision state, its fp32 value being stored * scale,
+ * a new state being value * rscale copied into the 16-bit tensor): per
+ * tensor m~ = fl32(h(m) * scale_m) (likewise v), the moments follow the
+ * fp32 recipe m = fl32(fl32(b1 m~) + fl32(c1 g)), v = fl32(fl32(b2 v~) +
+ * fl32(c2 fl32(g g))), p is updated from these fp32 moments, and the stored
+ * moments become rne16(fl32(m * fl32(1/scale'))) with, for fp16, scale' =
+ * fl32(max|m| / 65504) over the tensor (1 if zero) and, for bf16, 1.  bf16
+ * states take one kernel; fp16 states two (p and the new maxima, then the
+ * stored moments recomputed from the old stored ones), and the new scales
+ * are written at the end of the step.  A skipped step changes no scale.    */
 int optim_step_adamw(optim_plan *plan, const optim_adamw_hp *hp, float *lr_dev,
                      const float *inv_scale_dev, const float *found_inf_dev,
                      int32_t *step_dev, void *stream);

@@ -54,13 +54,13 @@ class optim_tensor_list(ctypes.Structure):
         ("head_numel", ctypes.POINTER(ctypes.c_int64)),
         ("param_dtype", ctypes.c_int32),
         ("grad_dtype", ctypes.c_int32),
-        ("qm2", _PP), ("absmax_m2", _PP), ("master", _PP),
+        ("qm2", _PP), ("absmax_m2", _PP), ("master", _PP), ("scale_m", _PP), ("scale_v", _PP),
     ]
 
 
 class optim_plan_opts(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("block", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("tile", ctypes.c_int32)]
+                ("tile", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
 
 
 class optim_adamw_hp(ctypes.Structure):
@@ -150,7 +150,7 @@ class TensorList:
 
     def __init__(self, params: Sequence, grads: Sequence, *, m=None, v=None, m2=None,
                  remainders=None, qm=None, qv=None, absmax_m=None, absmax_v=None,
-                 qm2=None, absmax_m2=None, master=None,
+                 qm2=None, absmax_m2=None, master=None, scale_m=None, scale_v=None,
                  weight_decay: Sequence[float], mini_kind=None, head_numel=None,
                  param_dtype: int = OPTIM_F32, grad_dtype: int = OPTIM_F32,
                  numel: Optional[Sequence[int]] = None):
@@ -175,6 +175,7 @@ class TensorList:
         s.m, s.v, s.m2, s.remainder = parr(m), parr(v), parr(m2), parr(remainders)
         s.qm, s.qv, s.absmax_m, s.absmax_v = parr(qm), parr(qv), parr(absmax_m), parr(absmax_v)
         s.qm2, s.absmax_m2, s.master = parr(qm2), parr(absmax_m2), parr(master)
+        s.scale_m, s.scale_v = parr(scale_m), parr(scale_v)
         s.weight_decay = ctypes.cast(self._wd, ctypes.POINTER(ctypes.c_double))
         if mini_kind is not None:
             self._kind = (ctypes.c_int32 * max(n, 1))(*mini_kind)
@@ -314,11 +315,11 @@ class Plan:
     """Plan + workspace.  ``tl`` must hold device tensors that outlive it."""
 
     def __init__(self, tl: TensorList, algo: int, *, bits: int = 0, block: int = 0, grid: int = 0,
-                 tile: int = 0, device=None, stream=None):
+                 tile: int = 0, state_dtype: int = OPTIM_F32, device=None, stream=None):
         import torch
         self.algo = algo
         self.tl = tl
-        self.opts = optim_plan_opts(bits, block, grid, tile)
+        self.opts = optim_plan_opts(bits, block, grid, tile, state_dtype)
         nbytes = optim_plan_workspace_size(tl, algo, self.opts)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
         self.handle = optim_plan_create(tl, algo, self.opts, self.workspace, nbytes, stream)

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "liboptim_step.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("kernels_adam.hip", "kernels_mini.hip", "kernels_blockwise.hip",
-                                           "kernels_util.hip", "kernels_lion_lamb.hip", "api.cpp")]
+                                           "kernels_util.hip", "kernels_lion_lamb.hip", "kernels_scaled.hip", "api.cpp")]
 ARCH = os.environ.get("OPTIM_STEP_ARCH", "gfx950")
 
 

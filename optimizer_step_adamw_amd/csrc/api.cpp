@@ -96,6 +96,7 @@ struct Built {
     int64_t nunits = 0;
     int64_t tile = 0;
     int32_t grid = 0;        // requested persistent workgroups
+    bool states16 = false;   // AdamW moments stored in 16 bits with scales
     int64_t npartials = 0;   // capacity of the partials region
     int32_t nblocks = 0;
     Layout L{};
@@ -152,14 +153,24 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     if (opts && opts->grid < 0) return fail(OPTIM_EINVAL, "negative grid");
     B.grid = opts ? opts->grid : 0;
     if (opts && opts->tile < 0) return fail(OPTIM_EINVAL, "negative tile");
+    const int32_t sdt = opts ? opts->state_dtype : OPTIM_F32;
+    if (sdt != OPTIM_F32 && sdt != OPTIM_F16 && sdt != OPTIM_BF16)
+        return fail(OPTIM_EDTYPE, "state_dtype must be OPTIM_F32, OPTIM_F16 or OPTIM_BF16");
+    const bool states16 = sdt != OPTIM_F32;
+    if (states16 && algo != OPTIM_ALGO_ADAMW) return fail(OPTIM_EUNSUPPORTED, "16-bit states are for AdamW plans");
+    if (states16 && masterw) return fail(OPTIM_EUNSUPPORTED, "16-bit states take fp32 or bf16 + remainder params");
+    if (n > 0 && states16 && (!list->scale_m || !list->scale_v))
+        return fail(OPTIM_EINVAL, "16-bit states need scale_m and scale_v arrays");
+    B.states16 = states16;
     // measured on MI355X: 2048 elements per workgroup (two groups of 4 per
-    // lane, loaded at once) stream best for AdamW / AdEMAMix, Adam-mini
-    // prefers 4096, and the blockwise step amortises its LDS tables and
-    // prologue over larger units
+    // lane, loaded at once) stream best for AdamW / AdEMAMix, Adam-mini and
+    // the two-pass fp16-state step prefer 4096 (per-unit reductions), and
+    // the blockwise step amortises its LDS tables and prologue over larger
+    // units
     const int64_t tile = (opts && opts->tile > 0) ? opts->tile
                          : is_blockwise(algo) ? kBlockwiseTile
-                         : algo == OPTIM_ALGO_ADAM_MINI ? kAdamMiniTile
-                                                        : kDefaultTile;
+                         : algo == OPTIM_ALGO_ADAM_MINI || sdt == OPTIM_F16 ? kAdamMiniTile
+                                                                            : kDefaultTile;
     if (tile < kMinTile || tile > (1 << 24) || (tile & (tile - 1)))
         return fail(OPTIM_EINVAL, "tile must be a power of two in [1024, 2^24]");
     if (is_blockwise(algo) && tile < kMinBlockwiseTile)
@@ -256,10 +267,20 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
             T.m = static_cast<float *>(list->m[i]);
             T.v = static_cast<float *>(list->v[i]);
             if (numel > 0 && (!T.m || !T.v)) return fail(OPTIM_EINVAL, ti + "NULL m or v");
-            if (!aligned(T.m, 4) || !aligned(T.v, 4)) return fail(OPTIM_EALIGN, ti + "m/v misaligned");
+            const size_t ssz = states16 ? 2 : 4;  // bytes per stored moment
+            if (!aligned(T.m, ssz) || !aligned(T.v, ssz)) return fail(OPTIM_EALIGN, ti + "m/v misaligned");
             vec = vec && aligned(T.m, 16) && (kind != OPTIM_MINI_FULL_V || aligned(T.v, 16));
-            add(T.m, numel * 4, true, "m");
-            add(T.v, vlen * 4, true, "v");
+            add(T.m, numel * ssz, true, "m");
+            add(T.v, vlen * ssz, true, "v");
+            if (states16) {
+                T.scale_m = list->scale_m[i];
+                T.scale_v = list->scale_v[i];
+                if (numel > 0 && (!T.scale_m || !T.scale_v)) return fail(OPTIM_EINVAL, ti + "NULL state scale");
+                if (!aligned(T.scale_m, 4) || !aligned(T.scale_v, 4))
+                    return fail(OPTIM_EALIGN, ti + "state scale misaligned");
+                add(T.scale_m, 4, true, "scale_m");
+                add(T.scale_v, 4, true, "scale_v");
+            }
         }
         if (algo == OPTIM_ALGO_LION) {
             T.m = static_cast<float *>(list->m[i]);
@@ -312,8 +333,8 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
                 if (B.nblocks == INT32_MAX) return fail(OPTIM_EUNSUPPORTED, "too many blocks");
                 ++B.nblocks;
             }
-        } else if (algo == OPTIM_ALGO_LAMB) {
-            // one block per tensor: its trust ratio
+        } else if (algo == OPTIM_ALGO_LAMB || states16) {
+            // one block per tensor: its trust ratio, or its state scales
             B.blockspan.push_back((int32_t)B.spans.size());
             B.spans.push_back(SpanDesc{B.nunits, 0, numel, i, B.nblocks});
             B.nunits += (numel + tile - 1) / tile;
@@ -360,7 +381,11 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
                                                                  : 0,
                                     norm_partials(B.nunits, B.tile, B.grid));
     off += align256(std::max<int64_t>(1, B.npartials) * sizeof(double));
-    L.blockfac = off; off += align256(std::max<int32_t>(1, B.nblocks) * sizeof(float));
+    // per-block factors; 16-bit states: the maxima slots of each tensor
+    // (zero in the uploaded image)
+    L.blockfac = off;
+    off += align256(B.states16 ? std::max<int32_t>(1, B.nblocks) * kAmaxBytesPerBlock
+                               : std::max<int32_t>(1, 2 * B.nblocks) * sizeof(float));
     L.total = off;
     return OPTIM_OK;
 }
@@ -377,6 +402,7 @@ struct optim_plan {
     int64_t nunits;
     int64_t tile;
     int64_t npartials;
+    int32_t state_dtype;
     char *ws;
     Layout L;
     int32_t sched;
@@ -418,8 +444,9 @@ int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_p
     if (workspace_bytes < B.L.total)
         return fail(OPTIM_EWORKSPACE, "workspace too small: need " + std::to_string(B.L.total) +
                                           " bytes, got " + std::to_string(workspace_bytes));
-    // host image of the table region [0, partials)
-    std::vector<char> img(B.L.partials, 0);
+    // host image of the table region [0, partials); with 16-bit states the
+    // whole workspace, so the maxima slots start at zero
+    std::vector<char> img(B.states16 ? B.L.total : B.L.partials, 0);
     std::memcpy(img.data() + B.L.group_wd, B.group_wd.data(), B.group_wd.size() * sizeof(double));
     std::memcpy(img.data() + B.L.tensors, B.tensors.data(), B.tensors.size() * sizeof(TensorDesc));
     std::memcpy(img.data() + B.L.spans, B.spans.data(), B.spans.size() * sizeof(SpanDesc));
@@ -454,6 +481,7 @@ int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_p
     P->nunits = B.nunits;
     P->tile = B.tile;
     P->npartials = B.npartials;
+    P->state_dtype = opts ? opts->state_dtype : OPTIM_F32;
     P->ws = static_cast<char *>(workspace);
     P->L = B.L;
     P->sched = OPTIM_SCHED_NONE;
@@ -586,7 +614,11 @@ int optim_step_adamw(optim_plan *plan, const optim_adamw_hp *hp, float *lr_dev, 
     rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
                      step_dev, a);
     if (rc) return rc;
-    HIP_OK(launch_adamw(a, plan->pk, plan->gk, static_cast<hipStream_t>(stream)));
+    if (plan->state_dtype != OPTIM_F32)
+        HIP_OK(launch_adamw_scaled(a, plan->pk, plan->gk, plan->state_dtype == OPTIM_F16 ? S_F16 : S_BF16,
+                                   static_cast<hipStream_t>(stream)));
+    else
+        HIP_OK(launch_adamw(a, plan->pk, plan->gk, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
 

@@ -382,23 +382,33 @@ __device__ __forceinline__ uint32_t arrive(uint32_t *c) {
     return __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void step_end(const StepArgs &a, const Scalars &S) {
-    if (!a.commit || threadIdx.x != 0) return;
+// Called by thread 0 of every workgroup; true in the last one to arrive
+// (the counters are rearmed by then).
+__device__ __forceinline__ bool last_arrival(const StepArgs &a) {
     const uint32_t G = gridDim.x, b = blockIdx.x;
     const uint32_t nsub = G < (uint32_t)kSubCounters ? G : (uint32_t)kSubCounters;
     const uint32_t j = b % nsub;
     const uint32_t members = G / nsub + (j < G % nsub ? 1u : 0u);
     uint32_t *sub = a.done + (1 + j) * kCounterStride;
-    if (arrive(sub) != members - 1) return;
+    if (arrive(sub) != members - 1) return false;
     __hip_atomic_store(sub, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (arrive(a.done) != nsub - 1) return;
+    if (arrive(a.done) != nsub - 1) return false;
     __hip_atomic_store(a.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
+__device__ __forceinline__ void publish_step(const StepArgs &a, const Scalars &S) {
     const PrepArgs &p = a.prep;
     if (p.sched == 1) {
         *p.lr_dev = S.lr;
         *p.iter_dev = S.k + 1;
     }
     if (!S.skip) *p.step_dev = S.t;
+}
+
+__device__ __forceinline__ void step_end(const StepArgs &a, const Scalars &S) {
+    if (!a.commit || threadIdx.x != 0) return;
+    if (last_arrival(a)) publish_step(a, S);
 }
 
 // Runs the commit on every exit path of a step kernel (skipped steps too).

@@ -15,7 +15,7 @@ namespace optim {
 // persistent grid whose workgroups walk the units grid-stride.
 constexpr int kThreads = 256;        // workgroup size (4 wavefronts of 64)
 constexpr int64_t kDefaultTile = 2048;
-constexpr int64_t kAdamMiniTile = 4096;
+constexpr int64_t kAdamMiniTile = 4096;   // also the fp16 scaled-state step
 constexpr int64_t kBlockwiseTile = 16384;
 constexpr int64_t kFiniteCheckElems = 8192;  // read-only scan: elements per workgroup
 constexpr int64_t kMinTile = 1024;   // one group of 4 elements per lane
@@ -25,8 +25,10 @@ constexpr int kMaxGroups = 64;    // distinct weight-decay values per plan
 // fp32; bf16 + int16 remainder; fp32 master + bf16 or fp16 model copy
 enum ParamKind { P_F32 = 0, P_BF16R = 1, P_MBF16 = 2, P_MF16 = 3 };
 enum GradKind { G_F32 = 0, G_BF16 = 1 };
+// 16-bit scaled moments (same codes as the public state_dtype values)
+enum StateKind { S_BF16 = 1, S_F16 = 2 };
 
-struct TensorDesc {       // 136 bytes
+struct TensorDesc {       // 152 bytes
     void *p;              // param (fp32 or bf16 patterns)
     const void *g;        // gradient
     float *m;             // first moment
@@ -44,8 +46,10 @@ struct TensorDesc {       // 136 bytes
     uint8_t *qm2;         // blockwise AdEMAMix: codes of m2
     float *am2;           // blockwise AdEMAMix: absmax of m2
     float *master;        // fp32 master of a bf16 / fp16 model param (p)
+    float *scale_m;       // 16-bit states: device scale of the stored m
+    float *scale_v;       // 16-bit states: device scale of the stored v
 };
-static_assert(sizeof(TensorDesc) == 136, "TensorDesc layout");
+static_assert(sizeof(TensorDesc) == 152, "TensorDesc layout");
 
 struct SpanDesc {         // 32 bytes
     int64_t unit_begin;   // first global unit number of this span
@@ -82,6 +86,11 @@ struct Scalars {
 constexpr int kSubCounters = 32;
 constexpr int kCounterStride = 32;  // uint32 words between counters
 constexpr size_t kCounterBytes = (1 + kSubCounters) * kCounterStride * sizeof(uint32_t);
+// fp16 scaled moments: per tensor and moment, the running maximum |x| of
+// the step as fp32 bits, kept in kAmaxSlots words on separate lines (a
+// workgroup's atomic max goes to one of them); 0 between steps.
+constexpr int kAmaxSlots = 16;
+constexpr size_t kAmaxBytesPerBlock = 2 * kAmaxSlots * kCounterStride * sizeof(uint32_t);
 
 // Workspace layout (byte offsets from the workspace base, 256-aligned).
 // `counters` holds the arrival counters of the step kernels' commit.
@@ -157,6 +166,8 @@ hipError_t launch_adamw(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_ademamix(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_adam_mini(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_lion(const StepArgs &a, int pk, int gk, hipStream_t s);
+// AdamW with 16-bit moments and per-tensor scales (sk: S_F16 / S_BF16)
+hipError_t launch_adamw_scaled(const StepArgs &a, int pk, int gk, int sk, hipStream_t s);
 hipError_t launch_lamb(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_blockwise(const StepArgs &a, int gk, bool ademamix, hipStream_t s);
 hipError_t launch_check_finite(const StepArgs &a, int gk, hipStream_t s);

@@ -208,6 +208,36 @@ def test_master_weight_validation(L):
     expect_error(osa.OPTIM_EDTYPE, lambda: ws(fake_list([n], fake=f, param_dtype=3), osa.OPTIM_ALGO_ADAMW))
 
 
+def test_scaled_state_validation(L):
+    f = Fake()
+    n = 1000
+    opts = lambda sdt: osa.optim_plan_opts(0, 0, 0, 0, sdt)
+    s16 = lambda **kw: fake_list([n], fake=f, **{**dict(m=[f(2 * n)], v=[f(2 * n)], scale_m=[f(4)],
+                                                    scale_v=[f(4)]), **kw})
+    for sdt in (osa.OPTIM_F16, osa.OPTIM_BF16):
+        assert ws(s16(), osa.OPTIM_ALGO_ADAMW, opts(sdt)) > 0
+        assert ws(s16(param_dtype=osa.OPTIM_BF16, params=[f(2 * n)], remainders=[f(2 * n)]),
+                  osa.OPTIM_ALGO_ADAMW, opts(sdt)) > 0
+        # a 16-bit moment needs 2-byte alignment only
+        assert ws(s16(m=[f(2 * n, misalign=2)]), osa.OPTIM_ALGO_ADAMW, opts(sdt)) > 0
+        expect_error(osa.OPTIM_EALIGN, lambda: ws(s16(m=[f(2 * n, misalign=1)]), osa.OPTIM_ALGO_ADAMW, opts(sdt)))
+        expect_error(osa.OPTIM_EALIGN, lambda: ws(s16(scale_v=[f(4, misalign=2)]), osa.OPTIM_ALGO_ADAMW,
+                                                  opts(sdt)))
+        expect_error(osa.OPTIM_EINVAL, lambda: ws(  # the scales are required
+            fake_list([n], fake=f, m=[f(2 * n)], v=[f(2 * n)]), osa.OPTIM_ALGO_ADAMW, opts(sdt)))
+        expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(
+            s16(m2=[f(4 * n)]), osa.OPTIM_ALGO_ADEMAMIX, opts(sdt)))
+        expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(
+            s16(param_dtype=osa.OPTIM_BF16, params=[f(2 * n)], master=[f(4 * n)]), osa.OPTIM_ALGO_ADAMW, opts(sdt)))
+        sm = f(4)
+        expect_error(osa.OPTIM_EINVAL, lambda: ws(  # a scale shared by two tensors
+            fake_list([n, n], fake=f, m=[f(2 * n), f(2 * n)], v=[f(2 * n), f(2 * n)], scale_m=[sm, sm],
+                      scale_v=[f(4), f(4)]), osa.OPTIM_ALGO_ADAMW, opts(sdt)))
+    expect_error(osa.OPTIM_EDTYPE, lambda: ws(s16(), osa.OPTIM_ALGO_ADAMW, opts(3)))
+    # the 16-bit moments halve the state footprint, the scales are per tensor
+    assert ws(s16(), osa.OPTIM_ALGO_ADAMW, opts(osa.OPTIM_F16)) >= ws(fake_list([n]), osa.OPTIM_ALGO_ADAMW)
+
+
 def test_null_plan_is_rejected_without_device(L):
     expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_step_adamw(
         None, osa.optim_adamw_hp(0.9, 0.999, 1e-8), 1 << 40, None, None, 1 << 41, 0))
