@@ -10,6 +10,8 @@ namespace {
 // flattened gradient, updated with the block mean of g^2.  Three kernels:
 // per-unit partial sums of g^2 -> per-block finalize (fixed-order fp64 sum,
 // v update, step factor) -> elementwise m/p update.
+constexpr int32_t kMiniSumUnitsPerWg = 4;
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
@@ -120,10 +122,15 @@ hipError_t launch_adam_mini(const StepArgs &args, int pk, int gk, hipStream_t s)
     // block sums and finalize read the step's inputs; the update publishes it
     StepArgs a = args;
     a.commit = 0;
+    // the read-only sum pass streams better with 4 consecutive units per
+    // workgroup (measured on MI355X: 2.8% off a whole step of a
+    // 536M-element list against one unit; 2 and 8 in between)
+    if (a.grid_request == 0) a.units_per_wg = kMiniSumUnitsPerWg;
     if (gk == G_F32)
         LAUNCH_PERSISTENT((mini_sumsq_kernel<G_F32>), a, s);
     else
         LAUNCH_PERSISTENT((mini_sumsq_kernel<G_BF16>), a, s);
+    a.units_per_wg = args.units_per_wg;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.nblocks > 0) {
