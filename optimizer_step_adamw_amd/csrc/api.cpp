@@ -163,14 +163,15 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
         return fail(OPTIM_EINVAL, "16-bit states need scale_m and scale_v arrays");
     B.states16 = states16;
     // measured on MI355X: 2048 elements per workgroup (two groups of 4 per
-    // lane, loaded at once) stream best for AdamW / AdEMAMix, Adam-mini and
-    // the two-pass fp16-state step prefer 4096 (per-unit reductions), and
-    // the blockwise step amortises its LDS tables and prologue over larger
-    // units
+    // lane, loaded at once) stream best for AdamW / AdEMAMix / Lion;
+    // Adam-mini, LAMB and the two-pass fp16-state step prefer 4096 (per-unit
+    // reductions), and the blockwise step amortises its LDS tables and
+    // prologue over larger units
+    const bool unit_sums = algo == OPTIM_ALGO_ADAM_MINI || algo == OPTIM_ALGO_LAMB || sdt == OPTIM_F16;
     const int64_t tile = (opts && opts->tile > 0) ? opts->tile
                          : is_blockwise(algo) ? kBlockwiseTile
-                         : algo == OPTIM_ALGO_ADAM_MINI || sdt == OPTIM_F16 ? kAdamMiniTile
-                                                                            : kDefaultTile;
+                         : unit_sums          ? kAdamMiniTile
+                                              : kDefaultTile;
     if (tile < kMinTile || tile > (1 << 24) || (tile & (tile - 1)))
         return fail(OPTIM_EINVAL, "tile must be a power of two in [1024, 2^24]");
     if (is_blockwise(algo) && tile < kMinBlockwiseTile)

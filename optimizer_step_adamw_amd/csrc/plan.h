@@ -15,9 +15,12 @@ namespace optim {
 // persistent grid whose workgroups walk the units grid-stride.
 constexpr int kThreads = 256;        // workgroup size (4 wavefronts of 64)
 constexpr int64_t kDefaultTile = 2048;
-constexpr int64_t kAdamMiniTile = 4096;   // also the fp16 scaled-state step
+constexpr int64_t kAdamMiniTile = 4096;   // also LAMB and the fp16 scaled-state step
 constexpr int64_t kBlockwiseTile = 16384;
-constexpr int64_t kFiniteCheckElems = 8192;  // read-only scan: elements per workgroup
+// read-only scans (finite check, gradient norm): elements per workgroup;
+// measured on MI355X over a 1.1B bf16 gradient list: 8192 -> 5.3 TB/s,
+// 32768 -> 6.2 (check) / 6.4 (check + norm), 65536 no better
+constexpr int64_t kFiniteCheckElems = 32768;
 constexpr int64_t kMinTile = 1024;   // one group of 4 elements per lane
 constexpr int64_t kMinBlockwiseTile = 2048;  // one quantizer row: 256 lanes x 8 elements
 constexpr int kMaxGroups = 64;    // distinct weight-decay values per plan
