@@ -130,10 +130,16 @@ __device__ __forceinline__ void dequantize_lane(uint64_t codes, float A,
 }
 
 // Packed codes of elements [e, e + E) (e a multiple of E, so this lane owns
-// whole bytes).  Full: one access of E*BITS bits (64, 32 or 16).
+// whole bytes).  Full: one access of E*BITS bits (64, 32 or 16).  A 16-bit
+// run per lane (4-bit codes, E = 4) makes 128-byte wave accesses, which
+// measured faster with ordinary than with non-temporal loads and stores on
+// MI355X (4-bit step -4%); 32-bit runs keep the row's access kind.
+template <int BITS, int E>
+constexpr int code_layout() { return E * BITS >= 32 ? row_layout<E>() : kRun; }
+
 template <int BITS, int E>
 __device__ __forceinline__ uint64_t load_codes_full(const uint8_t *q, int64_t e) {
-    constexpr int LAY = row_layout<E>();
+    constexpr int LAY = code_layout<BITS, E>();
     const int64_t byte0 = e * BITS / 8;
     if constexpr (E * BITS == 64) {
         const u32x2 w = vload<LAY>((const GMEM u32x2 *)gp(q + byte0));
@@ -148,7 +154,7 @@ __device__ __forceinline__ uint64_t load_codes_full(const uint8_t *q, int64_t e)
 
 template <int BITS, int E>
 __device__ __forceinline__ void store_codes_full(uint8_t *q, int64_t e, uint64_t c) {
-    constexpr int LAY = row_layout<E>();
+    constexpr int LAY = code_layout<BITS, E>();
     const int64_t byte0 = e * BITS / 8;
     if constexpr (E * BITS == 64)
         vstore<LAY>((GMEM u32x2 *)gp(q + byte0), u32x2{(uint32_t)c, (uint32_t)(c >> 32)});
@@ -342,20 +348,42 @@ __global__ __launch_bounds__(kThreads) void blockwise_kernel(StepArgs a) {
         const UnitPtrs u = unit_ptrs<GK, BITS, BLOCK, ADE>(T, start, uniform(S.decay[T.group]));
         const uint32_t len = (uint32_t)len64;  // <= tile <= 2^24
         const uint32_t lane0 = threadIdx.x * E;
-        // full rows, software-pipelined: the next row's loads are in flight
-        // while this row computes
+        // full rows, software-pipelined: the loads of the next rows are in
+        // flight while a row computes -- two rows ahead for the 2-state step
+        // with 4 elements per lane (measured on MI355X: 4-bit -2%), one with
+        // AdEMAMix's third state or 8 elements per lane, whose extra
+        // registers would cost occupancy
         const uint32_t nfull = T.vec_ok ? len / kRow : 0;
-        if (nfull > 0) {
+        const auto load_at = [&](uint32_t r, RowIn<E> &in) {
+            load_row<GK, BITS, BLOCK, ADE, true>(u, k, lane0 + r * kRow, E, in);
+        };
+        const auto step_at = [&](uint32_t r, RowIn<E> &in) {
+            step_row<GK, BITS, BLOCK, ADE, true>(u, k, lane0 + r * kRow, E, in, Mm, Mv);
+        };
+        uint32_t r = 0;
+        if (!ADE && E == 4 && nfull > 1) {
+            RowIn<E> cur, nxt;
+            load_at(0, cur);
+            load_at(1, nxt);
+            for (; r + 2 < nfull; ++r) {
+                RowIn<E> nn;
+                load_at(r + 2, nn);
+                step_at(r, cur);
+                cur = nxt;
+                nxt = nn;
+            }
+            step_at(r, cur);
+            step_at(r + 1, nxt);
+        } else if (nfull > 0) {
             RowIn<E> cur;
-            load_row<GK, BITS, BLOCK, ADE, true>(u, k, lane0, E, cur);
-            uint32_t r = 0;
+            load_at(0, cur);
             for (; r + 1 < nfull; ++r) {
                 RowIn<E> nxt;
-                load_row<GK, BITS, BLOCK, ADE, true>(u, k, lane0 + (r + 1) * kRow, E, nxt);
-                step_row<GK, BITS, BLOCK, ADE, true>(u, k, lane0 + r * kRow, E, cur, Mm, Mv);
+                load_at(r + 1, nxt);
+                step_at(r, cur);
                 cur = nxt;
             }
-            step_row<GK, BITS, BLOCK, ADE, true>(u, k, lane0 + r * kRow, E, cur, Mm, Mv);
+            step_at(r, cur);
         }
         for (uint32_t r0 = nfull * kRow; r0 < len; r0 += kRow) {
             const uint32_t rel = r0 + lane0;
