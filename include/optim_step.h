@@ -64,7 +64,7 @@ enum { OPTIM_SCHED_NONE = 0, OPTIM_SCHED_COSINE = 1 };
  * n tensors; every array below is a host array of length n (or NULL where
  * the algorithm does not use it) whose entries are device pointers.
  *
- *  numel        elements per tensor (> 0)
+ *  numel        elements per tensor, 0 .. 2^48 (0: an empty tensor, skipped)
  *  param        F32: float[numel]; BF16: uint16 bf16 patterns[numel];
  *               F16 (with master only): uint16 fp16 patterns[numel]
  *  grad         F32 float[numel] or BF16 uint16[numel] (grad_dtype)

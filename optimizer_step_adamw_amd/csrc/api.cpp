@@ -206,6 +206,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
         TensorDesc &T = B.tensors[i];
         const int64_t numel = list->numel[i];
         if (numel < 0) return fail(OPTIM_EINVAL, ti + "negative numel");
+        if (numel > kMaxNumel) return fail(OPTIM_EINVAL, ti + "numel above 2^48");
         const double wd = list->weight_decay[i];
         if (!(wd >= 0.0) || !std::isfinite(wd)) return fail(OPTIM_EINVAL, ti + "invalid weight_decay");
         auto git = std::find(B.group_wd.begin(), B.group_wd.end(), wd);

@@ -24,6 +24,7 @@ constexpr int64_t kFiniteCheckElems = 32768;
 constexpr int64_t kMinTile = 1024;   // one group of 4 elements per lane
 constexpr int64_t kMinBlockwiseTile = 2048;  // one quantizer row: 256 lanes x 8 elements
 constexpr int kMaxGroups = 64;    // distinct weight-decay values per plan
+constexpr int64_t kMaxNumel = int64_t(1) << 48;  // per tensor (byte sizes stay far from overflow)
 
 // fp32; bf16 + int16 remainder; fp32 master + bf16 or fp16 model copy
 enum ParamKind { P_F32 = 0, P_BF16R = 1, P_MBF16 = 2, P_MF16 = 3 };

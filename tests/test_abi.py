@@ -88,6 +88,8 @@ def test_workspace_size_grows_with_units(L):
 def test_validation_codes(L):
     f = Fake()
     expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([-1]), osa.OPTIM_ALGO_ADAMW))
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([(1 << 48) + 1]), osa.OPTIM_ALGO_ADAMW))
+    assert ws(fake_list([(1 << 33) + 5]), osa.OPTIM_ALGO_ADAMW) > 0  # beyond 32-bit element counts
     expect_error(osa.OPTIM_EALIGN, lambda: ws(
         fake_list([8], params=[f(32, misalign=2)]), osa.OPTIM_ALGO_ADAMW))
     # a gradient that aliases another tensor's moment buffer
