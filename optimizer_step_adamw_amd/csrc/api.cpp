@@ -169,7 +169,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     // prologue over larger units
     const bool unit_sums = algo == OPTIM_ALGO_ADAM_MINI || algo == OPTIM_ALGO_LAMB || sdt == OPTIM_F16;
     const int64_t tile = (opts && opts->tile > 0) ? opts->tile
-                         : is_blockwise(algo) ? kBlockwiseTile
+                         : is_blockwise(algo) ? blockwise_tile(algo == OPTIM_ALGO_BLOCKWISE_ADEMAMIX, bits)
                          : unit_sums          ? kAdamMiniTile
                                               : kDefaultTile;
     if (tile < kMinTile || tile > (1 << 24) || (tile & (tile - 1)))

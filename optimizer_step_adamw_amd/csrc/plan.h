@@ -16,7 +16,11 @@ namespace optim {
 constexpr int kThreads = 256;        // workgroup size (4 wavefronts of 64)
 constexpr int64_t kDefaultTile = 2048;
 constexpr int64_t kAdamMiniTile = 4096;   // also LAMB and the fp16 scaled-state step
-constexpr int64_t kBlockwiseTile = 16384;
+// blockwise units, measured best on MI355X over 2^28 elements (4096-65536):
+// 2-state 8-bit 4096, 2-state 4-bit 8192, AdEMAMix 8-bit 8192, 4-bit 16384
+constexpr int64_t blockwise_tile(bool ademamix, int bits) {
+    return ademamix ? (bits == 8 ? 8192 : 16384) : (bits == 8 ? 4096 : 8192);
+}
 // read-only scans (finite check, gradient norm): elements per workgroup;
 // measured on MI355X over a 1.1B bf16 gradient list: 8192 -> 5.3 TB/s,
 // 32768 -> 6.2 (check) / 6.4 (check + norm), 65536 no better
