@@ -232,6 +232,19 @@ MUTANTS = [
      "oracle_thresholds(1 << bv, Mv, Tv);\n\n    double b1 = F32(beta1), c1 = F32(1.0 - beta1);\n    double b2 = F32(beta2), c2 = F32(1.0 - beta2);\n    double bc1",
      "oracle_thresholds(1 << bv, Mv, Tv);\n\n    double c1 = F32(beta1), b1 = F32(1.0 - beta1);\n    double b2 = F32(beta2), c2 = F32(1.0 - beta2);\n    double bc1",
      ["test_blockwise_fresh_step"]),
+    # invisible on a fresh step (zero states): only the multi-step pins see them
+    ("blockwise_v_dequantized_with_m_absmax",
+     "    oracle_dequantize(n, block, bv, 0, qv, Mv, av, scratch_v);\n    for (int64_t i = 0; i < n; ++i) {\n"
+     "        double gi = (double)g[i];\n        double mi = F32(F32(b1 * (double)scratch_m[i]) + F32(c1 * gi));\n"
+     "        double vi",
+     "    oracle_dequantize(n, block, bv, 0, qv, Mv, am, scratch_v);\n    for (int64_t i = 0; i < n; ++i) {\n"
+     "        double gi = (double)g[i];\n        double mi = F32(F32(b1 * (double)scratch_m[i]) + F32(c1 * gi));\n"
+     "        double vi",
+     ["test_blockwise_constant_magnitude_blocks_track_adamw"]),
+    ("blockwise_ademamix_m2_dequantized_with_m1_absmax",
+     "oracle_dequantize(n, block, bm, 1, qm2, Mm, am2, scratch_m2);",
+     "oracle_dequantize(n, block, bm, 1, qm2, Mm, am, scratch_m2);",
+     ["test_blockwise_ademamix_constant_magnitude_blocks_track_ademamix"]),
 ]
 
 

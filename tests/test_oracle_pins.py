@@ -549,6 +549,57 @@ def test_blockwise_ademamix_fresh_step(orc, bits, block):
         assert np.array_equal(c, code) and np.array_equal(A, am)
 
 
+def _constant_magnitude_grads(nblk, block, steps, seed):
+    """g[t] = mag[t, block] * sign: each element keeps its sign over time and
+    every element of a block has the same magnitude at every step."""
+    rng = np.random.default_rng(seed)
+    sign = rng.choice([-1.0, 1.0], nblk * block)
+    for _ in range(steps):
+        yield (np.repeat(rng.uniform(1e-4, 1e-2, nblk), block) * sign).astype(np.float32)
+
+
+@pytest.mark.parametrize("bits,block", [(8, 256), (4, 128)])
+def test_blockwise_constant_magnitude_blocks_track_adamw(orc, bits, block):
+    """With the gradients above every element of a block has the same |m|
+    and the same v at every step, so each normalised magnitude is the map's
+    largest value, 1, held exactly: the quantized states carry no error and
+    the blockwise step follows AdamW (pinned to torch in float64 above) over
+    30 steps, up to the fp32 state recipe.  A block boundary off by one
+    element, a wrong bias correction after step 1 or a dropped state update
+    breaks it."""
+    nblk, lr, wd, steps = 12, 1e-3, 0.1, 30
+    n = nblk * block
+    p = host_normal(n, 0.02, 907, bits, 0, 0).astype(np.float64)
+    q, m, v = p.copy(), np.zeros(n), np.zeros(n)
+    qm, qv = np.zeros(n, np.uint8), np.zeros(n, np.uint8)
+    am, av = np.zeros(nblk, np.float32), np.zeros(nblk, np.float32)
+    for t, g in enumerate(_constant_magnitude_grads(nblk, block, steps, 907 + bits), start=1):
+        orc.adamw_step(p, m, v, g.astype(np.float64), lr, 0.9, 0.999, 1e-8, wd, t)
+        orc.blockwise_step(q, g, qm, qv, am, av, bits, block, lr, 0.9, 0.999, 1e-8, wd, t)
+        assert rel_tau(q, p, lr) < 1e-5, t
+    top = (1 << (bits - 1)) - 1  # the signed map's largest magnitude code
+    assert set(np.unique(qm & top).tolist()) == {top} and set(np.unique(qv).tolist()) == {(1 << bits) - 1}
+
+
+@pytest.mark.parametrize("bits,block", [(8, 256), (4, 128)])
+def test_blockwise_ademamix_constant_magnitude_blocks_track_ademamix(orc, bits, block):
+    """The same construction for the three AdEMAMix states (m1, m2, nu all
+    exact): the blockwise AdEMAMix step follows the fp64 AdEMAMix step
+    (pinned by its fresh-step and constant-gradient closed forms and by
+    alpha = 0 being AdamW) over 30 steps."""
+    nblk, lr, wd, b3, a, steps = 12, 1e-3, 0.1, 0.9999, 5.0, 30
+    n = nblk * block
+    p = host_normal(n, 0.02, 908, bits, 0, 0).astype(np.float64)
+    r, m1, m2, nu = p.copy(), np.zeros(n), np.zeros(n), np.zeros(n)
+    q = [np.zeros(n, np.uint8) for _ in range(3)]
+    ab = [np.zeros(nblk, np.float32) for _ in range(3)]
+    for t, g in enumerate(_constant_magnitude_grads(nblk, block, steps, 909 + bits), start=1):
+        orc.ademamix_step(p, m1, m2, nu, g.astype(np.float64), lr, 0.9, 0.999, b3, a, 1e-8, wd, t)
+        orc.blockwise_ademamix_step(r, g, q[0], q[1], q[2], ab[0], ab[1], ab[2], bits, block, lr, 0.9, 0.999,
+                                    b3, a, 1e-8, wd, t)
+        assert rel_tau(r, p, lr) < 1e-5, t
+
+
 def test_blockwise_ademamix_alpha_zero_is_blockwise_adamw(orc):
     """alpha = 0 takes m2 out of the update: the m and nu codes and absmax
     equal the 2-state blockwise AdamW step's bit for bit over several steps,
