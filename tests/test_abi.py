@@ -257,3 +257,19 @@ def test_product_partition_by_name():
     assert wds == [0.1, 0.1, 0.1, 0.1, 0.0, 0.1]
     with pytest.raises(ValueError):
         osa.adam_mini_partition(names, numels, dim=10, n_heads=3, weight_decay=0.1)
+
+
+def test_missing_library_raises_without_fallback():
+    """With the built library absent every entry point raises: there is no
+    CPU or torch fallback (checked in a fresh interpreter)."""
+    import subprocess
+    import sys
+    code = ("import optimizer_step_adamw_amd as osa\n"
+            "osa.LIB_PATH = '/nonexistent/liboptim_step.so'\n"
+            "osa._lib = None\n"
+            "try:\n"
+            "    osa.optim_plan_workspace_size(osa.TensorList([], [], weight_decay=[], numel=[]), osa.OPTIM_ALGO_ADAMW)\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', 'no fallback' in str(e))\n")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
+    assert "raised: True" in out.stdout, (out.stdout, out.stderr)
