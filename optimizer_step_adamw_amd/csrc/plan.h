@@ -1,5 +1,5 @@
 // plan.h -- device-visible plan tables shared by the C-ABI host layer
-// (api.cpp) and the gfx950 kernels (kernels.hip).  Internal; not installed.
+// (api.cpp) and the gfx950 kernels (kernels_*.hip).  Internal; not installed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -152,11 +152,13 @@ struct StepArgs {
     int32_t nspans;
     int64_t nunits;
     int64_t tile;             // elements per unit
-    double *partials;         // Adam-mini: one per unit; gradient norm:
-                              // one per workgroup
+    double *partials;         // Adam-mini: one per unit; LAMB: two per unit;
+                              // gradient norm: one per workgroup (+ stage 2)
     int64_t npartials;        // capacity of partials
-    float *blockfac;          // Adam-mini: per block lr/bc1/h
-    const int32_t *blockspan; // Adam-mini: span index of each block
+    float *blockfac;          // per block: Adam-mini lr/bc1/h, LAMB lr*trust;
+                              // fp16 scaled moments: the maxima slots
+    const int32_t *blockspan; // span index of each block (Adam-mini shared-v
+                              // block; LAMB or scaled-moment tensor)
     int32_t nblocks;
     const Codebook *codebook;
     int32_t bits, block;
@@ -167,7 +169,7 @@ struct StepArgs {
                               // per workgroup (set by the launcher)
 };
 
-// Launchers (kernels.hip).  Return the hipError_t of the launch.  Step
+// Launchers (kernels_*.hip).  Return the hipError_t of the launch.  Step
 // launchers always start at least one workgroup (the commit must run even
 // for an empty plan).
 hipError_t launch_adamw(const StepArgs &a, int pk, int gk, hipStream_t s);
