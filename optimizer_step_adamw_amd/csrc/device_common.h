@@ -72,6 +72,13 @@ __device__ __forceinline__ void rem_split(float x, uint32_t &b, uint32_t &r) {
 //  kRun (blockwise quantizer rows): N consecutive elements from e, ordinary
 //    loads and stores; the per-block DPP reductions want each lane's
 //    elements adjacent.
+//  kStridedKeep: kStrided's addresses with ordinary accesses, for arrays a
+//    second pass of the same step reads again (LAMB, fp16 scaled moments):
+//    ordinary accesses in both passes leave them in the Infinity Cache, and
+//    the second pass, walking the units backwards, meets the most recent
+//    ones first (measured on MI355X: LAMB and fp16-moment steps 6-11% faster
+//    up to a few hundred MB re-read; slower past that, so the launchers
+//    choose by size).
 // N = 1 is one element, ordinary access, in either layout.
 #define GMEM __attribute__((address_space(1)))
 typedef float __attribute__((ext_vector_type(4))) f32x4;
@@ -80,7 +87,7 @@ typedef uint32_t __attribute__((ext_vector_type(2))) u32x2;
 
 constexpr int kVec = 4;                             // elements per lane per group
 constexpr int64_t kSub = (int64_t)kVec * kThreads;  // elements per workgroup per group
-enum Layout { kStrided = 0, kRun = 1 };
+enum Layout { kStrided = 0, kRun = 1, kStridedKeep = 2 };
 // groups of 4 elements per lane the AdamW / AdEMAMix / Adam-mini update
 // loads before computing (one 1 KiB run per array per wave and group)
 constexpr int kAdamGroups = 2;
@@ -103,7 +110,7 @@ __device__ __forceinline__ void vstore(GMEM V *q, V x) {
 // element offset of group j of a lane's elements
 template <int LAY>
 __device__ __forceinline__ constexpr int64_t group_off(int j) {
-    return LAY == kStrided ? j * kSub : (int64_t)j * kVec;
+    return LAY == kRun ? (int64_t)j * kVec : j * kSub;
 }
 
 template <int N, int LAY = kStrided>
@@ -186,18 +193,18 @@ __device__ __forceinline__ uint32_t f32_to_f16_rne(float x) {
 // Parameters: fp32 (P_F32); bf16 + int16 remainder rebuilding the fp32
 // master (P_BF16R); or an fp32 master with a bf16 / fp16 model copy in p
 // (P_MBF16 / P_MF16), rewritten from the updated master.
-template <int PK, int N>
+template <int PK, int N, int LAY = kStrided>
 __device__ __forceinline__ void load_p(const TensorDesc &T, int64_t e, float (&p)[N]) {
     if constexpr (PK == P_F32) {
-        ldf<N>(static_cast<const float *>(T.p), e, p);
+        ldf<N, LAY>(static_cast<const float *>(T.p), e, p);
     } else if constexpr (PK == P_BF16R) {
         uint32_t b[N], r[N];
-        ldh<N>(static_cast<const uint16_t *>(T.p), e, b);
-        ldh<N>(T.rem, e, r);
+        ldh<N, LAY>(static_cast<const uint16_t *>(T.p), e, b);
+        ldh<N, LAY>(T.rem, e, r);
 #pragma unroll
         for (int k = 0; k < N; ++k) p[k] = rem_reconstruct(b[k], r[k]);
     } else {
-        ldf<N>(T.master, e, p);
+        ldf<N, LAY>(T.master, e, p);
     }
 }
 
@@ -253,7 +260,10 @@ __device__ __forceinline__ int span_of(const StepArgs &a, int64_t u) {
     return lo;
 }
 
-template <class Body>
+// REV: the default grid walks the units backwards (workgroup b takes the
+// units of workgroup G-1-b), for a second pass that should meet the lines
+// its first pass touched last.
+template <bool REV = false, class Body>
 __device__ __forceinline__ void for_units(const StepArgs &a, Body &&body) {
     int64_t u, u1, stride;
     if (a.grid_request > 0) {
@@ -261,7 +271,8 @@ __device__ __forceinline__ void for_units(const StepArgs &a, Body &&body) {
         u1 = a.nunits;
         stride = gridDim.x;
     } else {
-        u = (int64_t)blockIdx.x * a.units_per_wg;
+        const int64_t wb = REV ? (int64_t)gridDim.x - 1 - blockIdx.x : (int64_t)blockIdx.x;
+        u = wb * a.units_per_wg;
         u1 = u + a.units_per_wg < a.nunits ? u + a.units_per_wg : a.nunits;
         stride = 1;
     }
@@ -502,6 +513,15 @@ int persistent_grid(K, const StepArgs &a) {
     else
         g = (units + a.units_per_wg - 1) / a.units_per_wg;
     return (int)(g < INT32_MAX ? g : INT32_MAX);
+}
+
+// Whether a two-pass step keeps the arrays its second pass reads again in
+// the Infinity Cache (kStridedKeep accesses in both passes, the second pass
+// walking backwards): only on the default grid and while those bytes stay
+// under `limit`; past it, ordinary accesses stream slower than non-temporal
+// ones.  The limits are measured per step on MI355X.
+inline bool keep_for_second_pass(const StepArgs &a, int64_t reread_bytes_per_elem, int64_t limit) {
+    return a.grid_request == 0 && a.nunits * a.tile * reread_bytes_per_elem <= limit;
 }
 
 #define LAUNCH_PERSISTENT(K, a, s)                                                     \
