@@ -466,31 +466,53 @@ __device__ __forceinline__ AdamK adam_consts(const Scalars &S) {
 //   m <- b1 m + c1 g;  v <- b2 v + c2 g^2;  h = sqrt(v)/sqrt(bc2) + eps
 //   p <- p (1 - lr wd) - (lr/bc1) m / h          (decay from the old p)
 // AdEMAMix adds m2 <- b3 m2 + c3 g and uses lr (m/bc1 + alpha m2) / h.
+// A lane's N elements of every array of the update.
+template <int N>
+struct AdamRegs {
+    float p[N], g[N], m[N], v[N], m2[N];
+};
+
+// Loads; the gradient is multiplied by gscale (1 to defer the unscale).
+template <int PK, int GK, bool ADE, int N>
+__device__ __forceinline__ void adam_load(const TensorDesc &T, int64_t e, float gscale, AdamRegs<N> &r) {
+    load_p<PK, N>(T, e, r.p);
+    load_g<GK, N>(T.g, e, gscale, r.g);
+    ldf<N>(T.m, e, r.m);
+    ldf<N>(T.v, e, r.v);
+    if constexpr (ADE) ldf<N>(T.m2, e, r.m2);
+}
+
+template <bool ADE, int N>
+__device__ __forceinline__ void adam_math(AdamRegs<N> &r, const AdamK &k, float decay) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        r.m[i] = k.b1 * r.m[i] + k.c1 * r.g[i];
+        r.v[i] = k.b2 * r.v[i] + k.c2 * (r.g[i] * r.g[i]);
+        const float h = sqrtf(r.v[i]) * k.isb2 + k.eps;
+        if constexpr (ADE) {
+            r.m2[i] = k.b3 * r.m2[i] + k.c3 * r.g[i];
+            r.p[i] = r.p[i] * decay - k.lr * ((r.m[i] * k.ibc1 + k.alpha * r.m2[i]) / h);
+        } else {
+            r.p[i] = r.p[i] * decay - k.ss * (r.m[i] / h);
+        }
+    }
+}
+
+template <int PK, bool ADE, int N>
+__device__ __forceinline__ void adam_store(const TensorDesc &T, int64_t e, const AdamRegs<N> &r) {
+    store_p<PK, N>(T, e, r.p);
+    stf<N>(T.m, e, r.m);
+    stf<N>(T.v, e, r.v);
+    if constexpr (ADE) stf<N>(T.m2, e, r.m2);
+}
+
 template <int PK, int GK, bool ADE, int N>
 __device__ __forceinline__ void adam_elems(const TensorDesc &T, int64_t e, const AdamK &k,
                                            float decay) {
-    float p[N], g[N], m[N], v[N], m2[N];
-    load_p<PK, N>(T, e, p);
-    load_g<GK, N>(T.g, e, k.inv_scale, g);
-    ldf<N>(T.m, e, m);
-    ldf<N>(T.v, e, v);
-    if constexpr (ADE) ldf<N>(T.m2, e, m2);
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-        m[i] = k.b1 * m[i] + k.c1 * g[i];
-        v[i] = k.b2 * v[i] + k.c2 * (g[i] * g[i]);
-        const float h = sqrtf(v[i]) * k.isb2 + k.eps;
-        if constexpr (ADE) {
-            m2[i] = k.b3 * m2[i] + k.c3 * g[i];
-            p[i] = p[i] * decay - k.lr * ((m[i] * k.ibc1 + k.alpha * m2[i]) / h);
-        } else {
-            p[i] = p[i] * decay - k.ss * (m[i] / h);
-        }
-    }
-    store_p<PK, N>(T, e, p);
-    stf<N>(T.m, e, m);
-    stf<N>(T.v, e, v);
-    if constexpr (ADE) stf<N>(T.m2, e, m2);
+    AdamRegs<N> r;
+    adam_load<PK, GK, ADE, N>(T, e, k.inv_scale, r);
+    adam_math<ADE, N>(r, k, decay);
+    adam_store<PK, ADE, N>(T, e, r);
 }
 
 template <int PK, int GK, bool ADE>
