@@ -481,6 +481,37 @@ def test_empty_and_zero_size_lists():
     _run_adam(osa.OPTIM_ALGO_ADAMW, [0, 5, 0], 3, lr=1e-3, key=19)
 
 
+def test_empty_plans_of_every_step_commit():
+    """A plan with no tensors still launches one workgroup per kernel, which
+    has no unit to walk: every step form publishes its step counter and
+    nothing else."""
+    hp = osa.optim_adamw_hp(0.9, 0.999, 1e-8)
+    hpe = osa.optim_ademamix_hp(0.9, 0.999, 0.9999, 5.0, 1e-8)
+    e = lambda **kw: osa.TensorList([], [], weight_decay=[], numel=[], **kw)
+    cases = [
+        (osa.OPTIM_ALGO_ADEMAMIX, {}, lambda pl, sc: osa.optim_step_ademamix(pl.handle, hpe, sc.lr, None, None, sc.step)),
+        (osa.OPTIM_ALGO_ADAM_MINI, {}, lambda pl, sc: osa.optim_step_adam_mini(pl.handle, hp, sc.lr, None, None, sc.step)),
+        (osa.OPTIM_ALGO_LION, {}, lambda pl, sc: osa.optim_step_lion(pl.handle, osa.optim_lion_hp(0.9, 0.99), sc.lr,
+                                                                    None, None, sc.step)),
+        (osa.OPTIM_ALGO_LAMB, {}, lambda pl, sc: osa.optim_step_lamb(pl.handle, hp, sc.lr, None, None, sc.step)),
+        (osa.OPTIM_ALGO_BLOCKWISE, dict(bits=8, block=256),
+         lambda pl, sc: osa.optim_step_8bit_blockwise(pl.handle, hp, 8, 256, sc.lr, None, None, sc.step)),
+        (osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX, dict(bits=4, block=128),
+         lambda pl, sc: osa.optim_step_8bit_blockwise_ademamix(pl.handle, hpe, 4, 128, sc.lr, None, None, sc.step)),
+        (osa.OPTIM_ALGO_ADAMW, dict(state_dtype=osa.OPTIM_F16),
+         lambda pl, sc: osa.optim_step_adamw(pl.handle, hp, sc.lr, None, None, sc.step)),
+        (osa.OPTIM_ALGO_ADAMW, dict(state_dtype=osa.OPTIM_BF16),
+         lambda pl, sc: osa.optim_step_adamw(pl.handle, hp, sc.lr, None, None, sc.step)),
+    ]
+    for algo, opts, step in cases:
+        plan = osa.Plan(e(), algo, **opts)
+        sc = DevScalars(1e-3)
+        step(plan, sc)
+        step(plan, sc)
+        assert int(sc.step.item()) == 2, (algo, opts)
+        plan.close()
+
+
 def test_checkpoint_resume_is_bitwise():
     """State is raw caller-owned buffers plus the step counter: restoring them
     into fresh buffers under a new plan continues bit for bit."""
