@@ -83,9 +83,17 @@ class Timer:
         return [a.elapsed_time(b) for a, b in zip(self.marks[:-1], self.marks[1:])]
 
 
-def run_timed(torch, calls, steps, warmup):
+def dist(xs):
+    """Median and 10th / 90th percentiles (ms) of per-call event intervals."""
+    a = sorted(xs)
+    q = lambda f: a[min(len(a) - 1, int(round(f * (len(a) - 1))))]
+    return dict(median_ms=q(0.5), p10_ms=q(0.1), p90_ms=q(0.9))
+
+
+def run_timed(torch, calls, steps, warmup, stats=None):
     """calls: list of zero-arg functions forming one step.  Returns total ms
-    per step and the mean ms of each call."""
+    per step and the mean ms of each call; if `stats` is a list, appends each
+    call's median / p10 / p90 to it."""
     for _ in range(warmup):
         for c in calls:
             c()
@@ -100,7 +108,37 @@ def run_timed(torch, calls, steps, warmup):
     d = tm.durations_ms()
     wall = (time.perf_counter() - t0) * 1e3
     per_call = [sum(d[i::len(calls)]) / steps for i in range(len(calls))]
+    if stats is not None:
+        stats.extend(dist(d[i::len(calls)]) for i in range(len(calls)))
     return sum(d) / steps, per_call, wall / steps
+
+
+def run_timed_cold(torch, call, steps, warmup, flush_bytes=1 << 30):
+    """One call per step with a 1 GiB device write between steps, outside the
+    events, so the step's inputs come from HBM rather than the 256 MB
+    Infinity Cache.  Returns the per-call event intervals (ms)."""
+    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        call()
+    out = []
+    for i in range(steps):
+        scratch.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    del scratch
+    return out
+
+
+def environment(torch):
+    """Device and software the numbers were taken on."""
+    pr = torch.cuda.get_device_properties(0)
+    return dict(device=pr.name, arch=getattr(pr, "gcnArchName", None), compute_units=pr.multi_processor_count,
+                hbm_gib=round(pr.total_memory / 2 ** 30, 1), torch=torch.__version__,
+                hip=getattr(torch.version, "hip", None), host_cpus=os.cpu_count())
 
 
 def gbs(bytes_per_step, ms):
@@ -160,14 +198,15 @@ def bench_headline(torch, osa, synth, steps, warmup):
     def call_b():
         osa.optim_step_ademamix(pb.handle, hpb, sb["lr"], None, None, sb["step"])
 
-    ms, per_call, wall = run_timed(torch, [call_a, call_b], steps, warmup)
+    stats = []
+    ms, per_call, wall = run_timed(torch, [call_a, call_b], steps, warmup, stats)
     res = dict(workload=wl.name, elements=n, ms_per_step=ms, wall_ms_per_step=wall,
                elements_per_s=2 * n / (ms * 1e-3),
                kernels={
                    "adamw_fp32": dict(ms=per_call[0], bytes=B_ADAMW_F32 * n,
-                                      gbs=gbs(B_ADAMW_F32 * n, per_call[0])),
+                                      gbs=gbs(B_ADAMW_F32 * n, per_call[0]), **stats[0]),
                    "ademamix_fp32": dict(ms=per_call[1], bytes=B_ADEMAMIX_F32 * n,
-                                         gbs=gbs(B_ADEMAMIX_F32 * n, per_call[1])),
+                                         gbs=gbs(B_ADEMAMIX_F32 * n, per_call[1]), **stats[1]),
                })
     for k in res["kernels"].values():
         k["frac"] = k["gbs"] / PEAK_HBM_GBS
@@ -277,12 +316,16 @@ def bench_c1(torch, osa, synth, steps, warmup):
                     osa.OPTIM_ALGO_ADAMW)
     s = scalars(torch, hp.lr)
     h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
-    ms, _, _ = run_timed(torch, [lambda: osa.optim_step_adamw(plan.handle, h, s["lr"], None, None,
-                                                               s["step"])], steps, warmup)
+    step = lambda: osa.optim_step_adamw(plan.handle, h, s["lr"], None, None, s["step"])
+    stats = []
+    ms, _, _ = run_timed(torch, [step], steps, warmup, stats)
+    cold = dist(run_timed_cold(torch, step, steps, warmup))
     plan.close()
     return dict(workload=wl.name, elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
-                gbs=gbs(B_ADAMW_F32 * n, ms), frac=gbs(B_ADAMW_F32 * n, ms) / PEAK_HBM_GBS,
-                note="29 MB of state: cache-resident and launch-bound")
+                gbs=gbs(B_ADAMW_F32 * n, ms), frac=gbs(B_ADAMW_F32 * n, ms) / PEAK_HBM_GBS, warm=stats[0],
+                cold=dict(cold, gbs=gbs(B_ADAMW_F32 * n, cold["median_ms"])),
+                note="29 MB of state: cache-resident and launch-bound when warm; cold = after a 1 GiB "
+                     "write between steps, inputs from HBM")
 
 
 def bench_c3(torch, osa, synth, steps, warmup):
@@ -556,6 +599,7 @@ def main():
         "kernels": head["kernels"],
         "copy_ceiling": copy,
         "secondary": secondary,
+        "environment": environment(torch),
     }
     print(json.dumps(out), flush=True)
 
