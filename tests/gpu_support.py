@@ -28,6 +28,17 @@ def relerr_tau(x, ref, tau):
     return float(np.max(np.abs(x - ref) / np.maximum(np.abs(ref), tau))) if x.size else 0.0
 
 
+def err_report(x, ref, tau):
+    """relerr_tau, the largest plain relative error (over ref != 0) and the
+    share of elements where the floor tau engaged (|ref| < tau)."""
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    nz = ref != 0
+    plain = float(np.max(np.abs(x[nz] - ref[nz]) / np.abs(ref[nz]))) if nz.any() else 0.0
+    share = float(np.mean(np.abs(ref) < tau)) if ref.size else 0.0
+    return f"relerr_tau {relerr_tau(x, ref, tau):.3e}, max plain rel {plain:.3e}, tau engaged on {100 * share:.2f}%"
+
+
 class DevScalars:
     """lr / step / found_inf / iter / inv_scale device scalars of one run."""
 

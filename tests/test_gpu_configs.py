@@ -13,7 +13,7 @@ import torch
 import oracle as orc
 import optimizer_step_adamw_amd as osa
 import synth
-from gpu_support import (DEV, TOL_RUN, TOL_STEP1, AdamState, DevScalars, QuantState, all_equal,
+from gpu_support import (DEV, TOL_RUN, TOL_STEP1, AdamState, DevScalars, QuantState, all_equal, err_report,
                          relerr_tau, say, snapshot, to_np_u16)
 
 pytestmark = pytest.mark.gpu
@@ -52,7 +52,7 @@ def test_c1_single_tensor_full_oracle():
             gd = g.astype(np.float64)
             closed = p0 * (1 - lr32 * wl.hp.wd) - lr32 * gd / (np.abs(gd) + wl.hp.eps)
             assert relerr_tau(st.p[0].cpu().numpy(), closed, lr32) <= TOL_STEP1
-    say(f"C1 ok: {wl.steps} steps, final relerr_tau {err:.3e}")
+    say(f"C1 ok: {wl.steps} steps, final {err_report(st.p[0].cpu().numpy(), p, lr32)}")
 
 
 # ------------------------------------------------------------------ C2
@@ -91,7 +91,7 @@ def test_c2_decay_stress_sampled(algo):
         if t in (1, 10, 50, wl.steps):
             got = st.p[0][di].cpu().numpy()
             err = relerr_tau(got, p, lr32)
-            say(f"C2 {algo} step {t}: relerr_tau {err:.3e}")
+            say(f"C2 {algo} step {t}: {err_report(got, p, lr32)}")
             assert err <= (TOL_STEP1 if t == 1 else TOL_RUN), (t, err)
             if t == 1 and not ade:
                 # the decay-after ordering is ~lr^2*wd = 1e-3 away: far outside the bound
