@@ -209,7 +209,10 @@ int optim_plan_set_schedule(optim_plan *plan, int32_t kind, double lr_max,
  * the decay taken from the previous p, in Loshchilov & Hutter Algorithm 2
  * order ([BNB] PR description; [MINI] AdamWMini for bias correction and
  * eps placement).  Bias corrections are evaluated in fp64 on the device and
- * rounded once to fp32; the element math is fp32.  With BF16 params the
+ * rounded once to fp32; the element math is fp32, with the decay and the
+ * update applied as p - (fl32(lr wd) p + update), so each step rounds once
+ * at the parameter's scale (no fl32(1 - lr wd) factor whose rounding would
+ * bias every step the same way).  With BF16 params the
  * fp32 master is rebuilt from (param, remainder), updated, and split back
  * ([TE] description).
  *

@@ -374,7 +374,7 @@ __device__ __forceinline__ void step_begin(const StepArgs &a, Scalars &S) {
     }
     __syncthreads();
     if ((int)threadIdx.x < p.ngroups)
-        S.decay[threadIdx.x] = (float)(1.0 - S.lr64 * p.group_wd[threadIdx.x]);
+        S.lrwd[threadIdx.x] = (float)(S.lr64 * p.group_wd[threadIdx.x]);
     __syncthreads();
 }
 
@@ -482,8 +482,16 @@ __device__ __forceinline__ void adam_load(const TensorDesc &T, int64_t e, float 
     if constexpr (ADE) ldf<N>(T.m2, e, r.m2);
 }
 
+// Decoupled decay and update with one rounding at the parameter's scale:
+// p - (lw p + d), lw = fl32(lr wd), d the update term.  Multiplying by
+// fl32(1 - lr wd) instead carries that factor's rounding (up to 2^-25
+// relative, the same sign every step) into every step: over 100 steps a
+// parameter decaying toward zero drifts by several times the fp32 rounding
+// of its own value (measured: 1.4e-4 against 4.1e-5 relerr_tau, lr 3e-4).
+__device__ __forceinline__ float decayed(float p, float lw, float d) { return p - (lw * p + d); }
+
 template <bool ADE, int N>
-__device__ __forceinline__ void adam_math(AdamRegs<N> &r, const AdamK &k, float decay) {
+__device__ __forceinline__ void adam_math(AdamRegs<N> &r, const AdamK &k, float lw) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         r.m[i] = k.b1 * r.m[i] + k.c1 * r.g[i];
@@ -491,9 +499,9 @@ __device__ __forceinline__ void adam_math(AdamRegs<N> &r, const AdamK &k, float 
         const float h = sqrtf(r.v[i]) * k.isb2 + k.eps;
         if constexpr (ADE) {
             r.m2[i] = k.b3 * r.m2[i] + k.c3 * r.g[i];
-            r.p[i] = r.p[i] * decay - k.lr * ((r.m[i] * k.ibc1 + k.alpha * r.m2[i]) / h);
+            r.p[i] = decayed(r.p[i], lw, k.lr * ((r.m[i] * k.ibc1 + k.alpha * r.m2[i]) / h));
         } else {
-            r.p[i] = r.p[i] * decay - k.ss * (r.m[i] / h);
+            r.p[i] = decayed(r.p[i], lw, k.ss * (r.m[i] / h));
         }
     }
 }
@@ -508,18 +516,18 @@ __device__ __forceinline__ void adam_store(const TensorDesc &T, int64_t e, const
 
 template <int PK, int GK, bool ADE, int N>
 __device__ __forceinline__ void adam_elems(const TensorDesc &T, int64_t e, const AdamK &k,
-                                           float decay) {
+                                           float lw) {
     AdamRegs<N> r;
     adam_load<PK, GK, ADE, N>(T, e, k.inv_scale, r);
-    adam_math<ADE, N>(r, k, decay);
+    adam_math<ADE, N>(r, k, lw);
     adam_store<PK, ADE, N>(T, e, r);
 }
 
 template <int PK, int GK, bool ADE>
 __device__ __forceinline__ void adam_unit(const TensorDesc &T, int64_t start, int64_t len,
-                                          const AdamK &k, float decay) {
+                                          const AdamK &k, float lw) {
     lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
-        adam_elems<PK, GK, ADE, decltype(n)::value>(T, e, k, decay);
+        adam_elems<PK, GK, ADE, decltype(n)::value>(T, e, k, lw);
     });
 }
 

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
             const AdamK k = adam_consts(S);
 #pragma unroll
             for (int i = 0; i < N; ++i) r.g[i] = r.g[i] * k.inv_scale;  // g * 1 * s == g * s
-            adam_math<ADE, N>(r, k, uniform(S.decay[T.group]));
+            adam_math<ADE, N>(r, k, uniform(S.lrwd[T.group]));
             adam_store<PK, ADE, N>(T, e, r);
             return;
         }
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
     const AdamK k = adam_consts(S);
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
         const TensorDesc &T = a.tensors[sp.tensor];
-        adam_unit<PK, GK, ADE>(T, start, len, k, uniform(S.decay[T.group]));
+        adam_unit<PK, GK, ADE>(T, start, len, k, uniform(S.lrwd[T.group]));
     });
 }
 

@@ -201,12 +201,12 @@ struct UnitPtrs {
     const void *g;
     uint8_t *qm, *qv, *qm2;
     float *am, *av, *am2;
-    float decay;
+    float lw;  // fl32(lr wd)
     int lane;
 };
 
 template <int GK, int BITS, int BLOCK, bool ADE>
-__device__ __forceinline__ UnitPtrs unit_ptrs(const TensorDesc &T, int64_t start, float decay) {
+__device__ __forceinline__ UnitPtrs unit_ptrs(const TensorDesc &T, int64_t start, float lw) {
     UnitPtrs u;
     u.p = uniform_ptr(static_cast<float *>(T.p) + start);
     u.g = uniform_ptr(static_cast<const char *>(T.g) + start * (GK == G_F32 ? 4 : 2));
@@ -218,7 +218,7 @@ __device__ __forceinline__ UnitPtrs unit_ptrs(const TensorDesc &T, int64_t start
         u.qm2 = uniform_ptr(T.qm2 + start * BITS / 8);
         u.am2 = uniform_ptr(T.am2 + start / BLOCK);
     }
-    u.decay = decay;
+    u.lw = lw;
     u.lane = threadIdx.x & 63;
     return u;
 }
@@ -273,7 +273,7 @@ __device__ __forceinline__ void load_row(const UnitPtrs &u, const AdamK &k, uint
 }
 
 // ADE: AdEMAMix's third state m2 (signed map) and update
-// p <- p decay - lr (m/bc1 + alpha m2) / h.
+// p <- p (1 - lr wd) - lr (m/bc1 + alpha m2) / h.
 template <int GK, int BITS, int BLOCK, bool ADE, bool FULL>
 __device__ __forceinline__ void step_row(const UnitPtrs &u, const AdamK &k, uint32_t e, int nv,
                                          RowIn<lane_elems(BLOCK)> &in, const LdsMap<BITS - 1> &Mm,
@@ -295,9 +295,9 @@ __device__ __forceinline__ void step_row(const UnitPtrs &u, const AdamK &k, uint
         const float h = __builtin_amdgcn_sqrtf(vn[j]) * k.isb2 + k.eps;
         if (ADE) {
             m2n[j] = k.b3 * m2t[j] + k.c3 * in.g[j];
-            in.p[j] = in.p[j] * u.decay - k.lr * ((mn[j] * k.ibc1 + k.alpha * m2n[j]) * __builtin_amdgcn_rcpf(h));
+            in.p[j] = decayed(in.p[j], u.lw, k.lr * ((mn[j] * k.ibc1 + k.alpha * m2n[j]) * __builtin_amdgcn_rcpf(h)));
         } else {
-            in.p[j] = in.p[j] * u.decay - k.ss * (mn[j] * __builtin_amdgcn_rcpf(h));
+            in.p[j] = decayed(in.p[j], u.lw, k.ss * (mn[j] * __builtin_amdgcn_rcpf(h)));
         }
     }
     float am2, av2, am22 = 0.0f;
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void blockwise_kernel(StepArgs a) {
     const AdamK k = adam_consts(S);
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len64) {
         const TensorDesc &T = a.tensors[sp.tensor];
-        const UnitPtrs u = unit_ptrs<GK, BITS, BLOCK, ADE>(T, start, uniform(S.decay[T.group]));
+        const UnitPtrs u = unit_ptrs<GK, BITS, BLOCK, ADE>(T, start, uniform(S.lrwd[T.group]));
         const uint32_t len = (uint32_t)len64;  // <= tile <= 2^24
         const uint32_t lane0 = threadIdx.x * E;
         // full rows, software-pipelined: the loads of the next rows are in

@@ -11,7 +11,7 @@ namespace {
 // contraction:
 //   c = b1 m + c1 g;  p <- p (1 - lr wd) - lr sign(c);  m <- b2 m + c2 g
 template <int PK, int GK, int N>
-__device__ __forceinline__ void lion_elems(const TensorDesc &T, int64_t e, const AdamK &k, float decay) {
+__device__ __forceinline__ void lion_elems(const TensorDesc &T, int64_t e, const AdamK &k, float lw) {
     float p[N], g[N], m[N];
     load_p<PK, N>(T, e, p);
     load_g<GK, N>(T.g, e, k.inv_scale, g);
@@ -20,7 +20,7 @@ __device__ __forceinline__ void lion_elems(const TensorDesc &T, int64_t e, const
     for (int i = 0; i < N; ++i) {
         const float c = k.b1 * m[i] + k.c1 * g[i];
         const float s = c > 0.0f ? 1.0f : (c < 0.0f ? -1.0f : 0.0f);
-        p[i] = p[i] * decay - k.lr * s;
+        p[i] = decayed(p[i], lw, k.lr * s);
         m[i] = k.b2 * m[i] + k.c2 * g[i];
     }
     store_p<PK, N>(T, e, p);
@@ -36,9 +36,9 @@ __global__ __launch_bounds__(kThreads) void lion_kernel(StepArgs a) {
     const AdamK k = adam_consts(S);
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
         const TensorDesc &T = a.tensors[sp.tensor];
-        const float decay = uniform(S.decay[T.group]);
+        const float lw = uniform(S.lrwd[T.group]);
         lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
-            lion_elems<PK, GK, decltype(n)::value>(T, e, k, decay);
+            lion_elems<PK, GK, decltype(n)::value>(T, e, k, lw);
         });
     });
 }

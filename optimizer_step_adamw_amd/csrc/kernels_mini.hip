@@ -81,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void mini_finalize_kernel(StepArgs a) {
 
 template <int PK, int GK, int N>
 __device__ __forceinline__ void mini_elems(const TensorDesc &T, int64_t e, const AdamK &k,
-                                           float decay, float f) {
+                                           float lw, float f) {
     float p[N], g[N], m[N];
     load_p<PK, N>(T, e, p);
     load_g<GK, N>(T.g, e, k.inv_scale, g);
@@ -89,7 +89,7 @@ __device__ __forceinline__ void mini_elems(const TensorDesc &T, int64_t e, const
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         m[i] = k.b1 * m[i] + k.c1 * g[i];
-        p[i] = p[i] * decay - f * m[i];
+        p[i] = decayed(p[i], lw, f * m[i]);
     }
     store_p<PK, N>(T, e, p);
     stf<N>(T.m, e, m);
@@ -104,14 +104,14 @@ __global__ __launch_bounds__(kThreads) void mini_update_kernel(StepArgs a) {
     const AdamK k = adam_consts(S);
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
         const TensorDesc &T = a.tensors[sp.tensor];
-        const float decay = uniform(S.decay[T.group]);
+        const float lw = uniform(S.lrwd[T.group]);
         if (sp.block < 0) {
-            adam_unit<PK, GK, false>(T, start, len, k, decay);
+            adam_unit<PK, GK, false>(T, start, len, k, lw);
             return;
         }
         const float f = a.blockfac[sp.block];
         lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
-            mini_elems<PK, GK, decltype(n)::value>(T, e, k, decay, f);
+            mini_elems<PK, GK, decltype(n)::value>(T, e, k, lw, f);
         });
     });
 }

@@ -58,11 +58,11 @@ __device__ __forceinline__ void scaled_moments(const TensorDesc &T, int64_t e, c
 
 template <int N>
 __device__ __forceinline__ void adamw_update(float (&p)[N], const float (&m)[N], const float (&v)[N],
-                                             const AdamK &k, float decay) {
+                                             const AdamK &k, float lw) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         const float h = sqrtf(v[i]) * k.isb2 + k.eps;
-        p[i] = p[i] * decay - k.ss * (m[i] / h);
+        p[i] = decayed(p[i], lw, k.ss * (m[i] / h));
     }
 }
 
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void scaled_bf16_kernel(StepArgs a) {
         const AdamK k = adam_consts(S);
         for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
             const TensorDesc &T = a.tensors[sp.tensor];
-            const float decay = uniform(S.decay[T.group]);
+            const float lw = uniform(S.lrwd[T.group]);
             const float sm = uniform(*T.scale_m), sv = uniform(*T.scale_v);
             lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
                 constexpr int N = decltype(n)::value;
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kThreads) void scaled_bf16_kernel(StepArgs a) {
                 load_p<PK, N>(T, e, p);
                 load_g<GK, N>(T.g, e, k.inv_scale, g);
                 scaled_moments<S_BF16, N>(T, e, k, sm, sv, g, m, v);
-                adamw_update<N>(p, m, v, k, decay);
+                adamw_update<N>(p, m, v, k, lw);
                 uint32_t qm[N], qv[N];
 #pragma unroll
                 for (int i = 0; i < N; ++i) {  // scale 1: x * 1 is x
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void scaled_f16_pass1_kernel(StepArgs a) 
     const int slot = (int)((blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) % kAmaxSlots);
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
         const TensorDesc &T = a.tensors[sp.tensor];
-        const float decay = uniform(S.decay[T.group]);
+        const float lw = uniform(S.lrwd[T.group]);
         const float sm = uniform(*T.scale_m), sv = uniform(*T.scale_v);
         float mx = 0.0f, vx = 0.0f;
         lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void scaled_f16_pass1_kernel(StepArgs a) 
             load_p<PK, N>(T, e, p);
             load_g<GK, N, RL>(T.g, e, k.inv_scale, g);
             scaled_moments<S_F16, N, RL>(T, e, k, sm, sv, g, m, v);
-            adamw_update<N>(p, m, v, k, decay);
+            adamw_update<N>(p, m, v, k, lw);
 #pragma unroll
             for (int i = 0; i < N; ++i) {
                 mx = fmaxf(mx, fabsf(m[i]));

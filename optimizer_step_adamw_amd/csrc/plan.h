@@ -86,7 +86,7 @@ struct Scalars {
     float inv_scale;      // gradient multiplier (AMP unscale), 1 if none
     int32_t k;            // schedule iteration read by this step
     double lr64, step_size64, inv_sqrt_bc2_64, eps64, beta2_64, c2_64;
-    float decay[kMaxGroups];  // fl32(1 - lr * wd_group)
+    float lrwd[kMaxGroups];   // fl32(lr * wd_group)
 };
 
 // Commit counters: one top counter and kSubCounters sub-counters, each on its

@@ -202,6 +202,20 @@ def test_adam_mini_small_units():
     _mini_run(5, 9, dim=128, heads=2, items=items, tile=1024)
 
 
+def test_adam_mini_100_steps_two_layer_slice():
+    """100 steps on a two-layer Llama-shaped slice with all three kinds: the
+    embedding and output with full v, q/k with one v per head block, every
+    other tensor (v/o projections, MLP, norms) with one v."""
+    dim, heads, ffn, vocab = 256, 4, 688, 1000
+    items = [("tok_embeddings.weight", vocab * dim)]
+    for layer in range(2):
+        items += [(f"layers.{layer}.attention.{w}.weight", dim * dim) for w in ("wq", "wk", "wv", "wo")]
+        items += [(f"layers.{layer}.feed_forward.{w}.weight", ffn * dim) for w in ("w1", "w2", "w3")]
+        items += [(f"layers.{layer}.attention_norm.weight", dim), (f"layers.{layer}.ffn_norm.weight", dim)]
+    items += [("norm.weight", dim), ("output.weight", vocab * dim)]
+    _mini_run(100, 11, dim=dim, heads=heads, items=items)
+
+
 def test_adam_mini_deterministic():
     a = _mini_run(4, 7)
     b = _mini_run(4, 7)
