@@ -210,7 +210,7 @@ int optim_plan_set_schedule(optim_plan *plan, int32_t kind, double lr_max,
  * order ([BNB] PR description; [MINI] AdamWMini for bias correction and
  * eps placement).  Bias corrections are evaluated in fp64 on the device and
  * rounded once to fp32; the element math is fp32, with the decay and the
- * update applied as p - (fl32(lr wd) p + update), so each step rounds once
+ * update applied as p - fma(fl32(lr wd), p, update), so each step rounds once
  * at the parameter's scale (no fl32(1 - lr wd) factor whose rounding would
  * bias every step the same way).  With BF16 params the
  * fp32 master is rebuilt from (param, remainder), updated, and split back

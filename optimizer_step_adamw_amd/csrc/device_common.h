@@ -483,12 +483,14 @@ __device__ __forceinline__ void adam_load(const TensorDesc &T, int64_t e, float 
 }
 
 // Decoupled decay and update with one rounding at the parameter's scale:
-// p - (lw p + d), lw = fl32(lr wd), d the update term.  Multiplying by
+// p - fma(lw, p, d), lw = fl32(lr wd), d the update term (the fused inner
+// term also keeps the register footprint of the bf16-remainder kernels at
+// that of a plain multiply by a factor).  Multiplying by
 // fl32(1 - lr wd) instead carries that factor's rounding (up to 2^-25
 // relative, the same sign every step) into every step: over 100 steps a
 // parameter decaying toward zero drifts by several times the fp32 rounding
 // of its own value (measured: 1.4e-4 against 4.1e-5 relerr_tau, lr 3e-4).
-__device__ __forceinline__ float decayed(float p, float lw, float d) { return p - (lw * p + d); }
+__device__ __forceinline__ float decayed(float p, float lw, float d) { return p - __builtin_fmaf(lw, p, d); }
 
 template <bool ADE, int N>
 __device__ __forceinline__ void adam_math(AdamRegs<N> &r, const AdamK &k, float lw) {
