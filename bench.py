@@ -91,26 +91,55 @@ def dist(xs):
 
 
 def run_timed(torch, calls, steps, warmup, stats=None):
-    """calls: list of zero-arg functions forming one step.  Returns total ms
-    per step and the mean ms of each call; if `stats` is a list, appends each
-    call's median / p10 / p90 to it."""
+    """calls: list of zero-arg functions forming one step.  The timed region
+    is `steps` steps between two events, with nothing recorded between the
+    calls: its mean is the step time.  A second pass of `steps` steps records
+    an event after every call, for each call's mean and (into `stats`, if a
+    list) its median / p10 / p90; an event between two kernels adds a few
+    microseconds to the interval, so these per-call figures sit slightly
+    above the kernels' own durations.  Returns (ms per step, per-call mean
+    ms from the second pass, host wall ms per step of the timed region)."""
     for _ in range(warmup):
         for c in calls:
             c()
     torch.cuda.synchronize()
-    tm = Timer(torch)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        for c in calls:
+            c()
+    b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    ms = a.elapsed_time(b) / steps
+    tm = Timer(torch)
     tm.mark()
     for _ in range(steps):
         for c in calls:
             c()
             tm.mark()
     d = tm.durations_ms()
-    wall = (time.perf_counter() - t0) * 1e3
     per_call = [sum(d[i::len(calls)]) / steps for i in range(len(calls))]
     if stats is not None:
         stats.extend(dist(d[i::len(calls)]) for i in range(len(calls)))
-    return sum(d) / steps, per_call, wall / steps
+    return ms, per_call, wall / steps
+
+
+def run_each(torch, call, steps, warmup=2):
+    """Mean duration (ms) of one call run `steps` times back to back between
+    two events: the kernel's launch duration as a training loop sees it, with
+    no event between launches."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
 
 
 def run_timed_cold(torch, call, steps, warmup, flush_bytes=1 << 30):
@@ -200,14 +229,19 @@ def bench_headline(torch, osa, synth, steps, warmup):
 
     stats = []
     ms, per_call, wall = run_timed(torch, [call_a, call_b], steps, warmup, stats)
+    each = [run_each(torch, call_a, steps), run_each(torch, call_b, steps)]
+    ev = lambda i: dict(events_mean_ms=per_call[i], events=stats[i])
     res = dict(workload=wl.name, elements=n, ms_per_step=ms, wall_ms_per_step=wall,
                elements_per_s=2 * n / (ms * 1e-3),
                kernels={
-                   "adamw_fp32": dict(ms=per_call[0], bytes=B_ADAMW_F32 * n,
-                                      gbs=gbs(B_ADAMW_F32 * n, per_call[0]), **stats[0]),
-                   "ademamix_fp32": dict(ms=per_call[1], bytes=B_ADEMAMIX_F32 * n,
-                                         gbs=gbs(B_ADEMAMIX_F32 * n, per_call[1]), **stats[1]),
-               })
+                   "adamw_fp32": dict(ms=each[0], bytes=B_ADAMW_F32 * n,
+                                      gbs=gbs(B_ADAMW_F32 * n, each[0]), **ev(0)),
+                   "ademamix_fp32": dict(ms=each[1], bytes=B_ADEMAMIX_F32 * n,
+                                         gbs=gbs(B_ADEMAMIX_F32 * n, each[1]), **ev(1)),
+               },
+               note="step time: the timed steps between two events; kernel ms: the same call run "
+                    "`steps` times back to back between two events; events_*: an event after every "
+                    "call (each adds a few microseconds)")
     for k in res["kernels"].values():
         k["frac"] = k["gbs"] / PEAK_HBM_GBS
     pa.close()
@@ -230,9 +264,10 @@ def bench_lion_lamb(torch, osa, synth, steps, warmup):
     sl, sm = scalars(torch, 1e-4), scalars(torch, 1e-3)
     hl = osa.optim_lion_hp(0.9, 0.99)
     hm = osa.optim_adamw_hp(hp.beta1, hp.beta2, 1e-6)
-    ms, per_call, _ = run_timed(torch, [
-        lambda: osa.optim_step_lion(pl.handle, hl, sl["lr"], None, None, sl["step"]),
-        lambda: osa.optim_step_lamb(pm.handle, hm, sm["lr"], None, None, sm["step"])], steps, warmup)
+    calls = [lambda: osa.optim_step_lion(pl.handle, hl, sl["lr"], None, None, sl["step"]),
+             lambda: osa.optim_step_lamb(pm.handle, hm, sm["lr"], None, None, sm["step"])]
+    ms, _, _ = run_timed(torch, calls, steps, warmup)
+    per_call = [run_each(torch, c, steps) for c in calls]
     pl.close()
     pm.close()
     del A, B, g
