@@ -130,13 +130,21 @@ typedef struct optim_tensor_list {
  *              blockwise AdEMAMix 8-bit 8192, 4-bit 16384)
  *  state_dtype AdamW only: OPTIM_F32 (0, default) fp32 moments; OPTIM_F16
  *              or OPTIM_BF16 16-bit moments with a per-tensor scale
- *              ([TE] review: state scaling), see optim_step_adamw         */
+ *              ([TE] review: state scaling), see optim_step_adamw
+ *  segment_bytes  Adam-mini only: the step runs its block-sum, finalize
+ *              and update kernels once per segment, a run of consecutive
+ *              whole tensors with shared v holding at most this many
+ *              gradient bytes (a larger tensor forms a segment alone), or a
+ *              run of full-v tensors; 0 = 384 MiB (the gradients are read
+ *              twice, the second time mostly from the Infinity Cache).  Results
+ *              do not depend on it.  Negative: OPTIM_EINVAL.              */
 typedef struct optim_plan_opts {
     int32_t bits;
     int32_t block;
     int32_t grid;
     int32_t tile;
     int32_t state_dtype;
+    int64_t segment_bytes;
 } optim_plan_opts;
 
 /* Hyperparameters, validated as in [MINI] AdamWMini's constructor:

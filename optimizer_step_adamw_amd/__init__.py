@@ -60,7 +60,7 @@ class optim_tensor_list(ctypes.Structure):
 
 class optim_plan_opts(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("block", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("tile", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
+                ("tile", ctypes.c_int32), ("state_dtype", ctypes.c_int32), ("segment_bytes", ctypes.c_int64)]
 
 
 class optim_adamw_hp(ctypes.Structure):
@@ -315,11 +315,12 @@ class Plan:
     """Plan + workspace.  ``tl`` must hold device tensors that outlive it."""
 
     def __init__(self, tl: TensorList, algo: int, *, bits: int = 0, block: int = 0, grid: int = 0,
-                 tile: int = 0, state_dtype: int = OPTIM_F32, device=None, stream=None):
+                 tile: int = 0, state_dtype: int = OPTIM_F32, segment_bytes: int = 0, device=None,
+                 stream=None):
         import torch
         self.algo = algo
         self.tl = tl
-        self.opts = optim_plan_opts(bits, block, grid, tile, state_dtype)
+        self.opts = optim_plan_opts(bits, block, grid, tile, state_dtype, segment_bytes)
         nbytes = optim_plan_workspace_size(tl, algo, self.opts)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
         self.handle = optim_plan_create(tl, algo, self.opts, self.workspace, nbytes, stream)

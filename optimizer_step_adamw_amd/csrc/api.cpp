@@ -99,6 +99,7 @@ struct Built {
     bool states16 = false;   // AdamW moments stored in 16 bits with scales
     int64_t npartials = 0;   // capacity of the partials region
     int32_t nblocks = 0;
+    std::vector<MiniSegment> segs;  // Adam-mini launch segments
     Layout L{};
 };
 
@@ -153,6 +154,10 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     if (opts && opts->grid < 0) return fail(OPTIM_EINVAL, "negative grid");
     B.grid = opts ? opts->grid : 0;
     if (opts && opts->tile < 0) return fail(OPTIM_EINVAL, "negative tile");
+    if (opts && opts->segment_bytes < 0) return fail(OPTIM_EINVAL, "negative segment_bytes");
+    const int64_t seg_cap = (opts && opts->segment_bytes > 0) ? opts->segment_bytes : kMiniSegmentBytes;
+    bool seg_shared = false;
+    int64_t seg_gbytes = 0;
     const int32_t sdt = opts ? opts->state_dtype : OPTIM_F32;
     if (sdt != OPTIM_F32 && sdt != OPTIM_F16 && sdt != OPTIM_BF16)
         return fail(OPTIM_EDTYPE, "state_dtype must be OPTIM_F32, OPTIM_F16 or OPTIM_BF16");
@@ -201,6 +206,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     B.group_wd.clear();
     B.nunits = 0;
     B.nblocks = 0;
+    B.segs.clear();
     for (int i = 0; i < n; ++i) {
         const std::string ti = "tensor " + std::to_string(i) + ": ";
         TensorDesc &T = B.tensors[i];
@@ -325,6 +331,8 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
         }
         T.vec_ok = vec ? 1 : 0;
         if (numel == 0) continue;
+        const int64_t units_before = B.nunits;
+        const int32_t blocks_before = B.nblocks;
         // spans
         if (algo == OPTIM_ALGO_ADAM_MINI && kind != OPTIM_MINI_FULL_V) {
             for (int64_t s = 0; s < numel; s += T.block_len) {
@@ -344,6 +352,22 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
         } else {
             B.spans.push_back(SpanDesc{B.nunits, 0, numel, i, -1});
             B.nunits += (numel + tile - 1) / tile;
+        }
+        // Adam-mini segments: runs of whole tensors, all with shared v and
+        // at most seg_cap gradient bytes (a larger tensor alone), or all
+        // with full v
+        if (algo == OPTIM_ALGO_ADAM_MINI) {
+            const bool shared = kind != OPTIM_MINI_FULL_V;
+            const int64_t gb = numel * (int64_t)gsz;
+            if (B.segs.empty() || shared != seg_shared || (shared && seg_gbytes + gb > seg_cap)) {
+                B.segs.push_back(MiniSegment{units_before, B.nunits, blocks_before, B.nblocks});
+                seg_shared = shared;
+                seg_gbytes = gb;
+            } else {
+                B.segs.back().unit_end = B.nunits;
+                B.segs.back().block_end = B.nblocks;
+                seg_gbytes += gb;
+            }
         }
     }
     if (B.spans.size() >= (size_t)INT32_MAX) return fail(OPTIM_EUNSUPPORTED, "too many spans");
@@ -407,6 +431,7 @@ struct optim_plan {
     int32_t state_dtype;
     char *ws;
     Layout L;
+    std::vector<MiniSegment> segs;  // Adam-mini launch segments
     int32_t sched;
     double lr_max, lr_min;
     int32_t K;
@@ -486,6 +511,7 @@ int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_p
     P->state_dtype = opts ? opts->state_dtype : OPTIM_F32;
     P->ws = static_cast<char *>(workspace);
     P->L = B.L;
+    P->segs = std::move(B.segs);
     P->sched = OPTIM_SCHED_NONE;
     *out = P;
     return OPTIM_OK;
@@ -647,7 +673,8 @@ int optim_step_adam_mini(optim_plan *plan, const optim_adamw_hp *hp, float *lr_d
     rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
                      step_dev, a);
     if (rc) return rc;
-    HIP_OK(launch_adam_mini(a, plan->pk, plan->gk, static_cast<hipStream_t>(stream)));
+    HIP_OK(launch_adam_mini(a, plan->pk, plan->gk, plan->segs.data(), (int32_t)plan->segs.size(),
+                            static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
 

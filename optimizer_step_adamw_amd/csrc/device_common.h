@@ -245,6 +245,7 @@ __device__ __forceinline__ void load_g(const void *g, int64_t e, float s, float 
 // ---------------------------------------------------------------- traversal
 // Calls body(u, span, first element, element count) for every unit u this
 // workgroup owns.  All arguments are uniform across the workgroup.
+// A launch covers units [unit0, nunits).
 // Default grid: workgroup b owns units_per_wg consecutive units (usually
 // one), and the hardware dispatcher keeps the resident workgroups on one
 // narrow, advancing window of every array.  Persistent grid: workgroup b
@@ -267,12 +268,12 @@ template <bool REV = false, class Body>
 __device__ __forceinline__ void for_units(const StepArgs &a, Body &&body) {
     int64_t u, u1, stride;
     if (a.grid_request > 0) {
-        u = blockIdx.x;
+        u = a.unit0 + blockIdx.x;
         u1 = a.nunits;
         stride = gridDim.x;
     } else {
         const int64_t wb = REV ? (int64_t)gridDim.x - 1 - blockIdx.x : (int64_t)blockIdx.x;
-        u = wb * a.units_per_wg;
+        u = a.unit0 + wb * a.units_per_wg;
         u1 = u + a.units_per_wg < a.nunits ? u + a.units_per_wg : a.nunits;
         stride = 1;
     }
@@ -538,7 +539,7 @@ __device__ __forceinline__ void adam_unit(const TensorDesc &T, int64_t start, in
 // units).  At least one workgroup: the commit must run for an empty plan.
 template <class K>
 int persistent_grid(K, const StepArgs &a) {
-    const int64_t units = a.nunits > 0 ? a.nunits : 1;
+    const int64_t units = a.nunits > a.unit0 ? a.nunits - a.unit0 : 1;
     int64_t g;
     if (a.grid_request > 0)
         g = a.grid_request < units ? a.grid_request : units;
@@ -553,7 +554,7 @@ int persistent_grid(K, const StepArgs &a) {
 // under `limit`; past it, ordinary accesses stream slower than non-temporal
 // ones.  The limits are measured per step on MI355X.
 inline bool keep_for_second_pass(const StepArgs &a, int64_t reread_bytes_per_elem, int64_t limit) {
-    return a.grid_request == 0 && a.nunits * a.tile * reread_bytes_per_elem <= limit;
+    return a.grid_request == 0 && (a.nunits - a.unit0) * a.tile * reread_bytes_per_elem <= limit;
 }
 
 #define LAUNCH_PERSISTENT(K, a, s)                                                     \

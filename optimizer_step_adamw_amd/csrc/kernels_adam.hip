@@ -17,8 +17,8 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
     __shared__ Scalars S;
     constexpr int N = kAdamGroups * kVec;
     // (an empty plan still launches one workgroup, which has no unit)
-    if (EARLY && (int64_t)blockIdx.x < a.nunits) {
-        const int64_t u = blockIdx.x;
+    if (EARLY && a.unit0 + (int64_t)blockIdx.x < a.nunits) {
+        const int64_t u = a.unit0 + blockIdx.x;
         int si = span_of(a, u);
         while (a.spans[si + 1].unit_begin <= u) ++si;
         const SpanDesc sp = a.spans[si];

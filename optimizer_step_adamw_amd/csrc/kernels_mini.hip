@@ -10,6 +10,16 @@ namespace {
 // flattened gradient, updated with the block mean of g^2.  Three kernels:
 // per-unit partial sums of g^2 -> per-block finalize (fixed-order fp64 sum,
 // v update, step factor) -> elementwise m/p update.
+//
+// The three run once per segment of the list (whole tensors holding at most
+// a bounded number of gradient bytes, 384 MiB by default), not once over the
+// whole list.  The sum pass reads g with ordinary loads, so much of a
+// segment's g is still in the 256 MB Infinity Cache when its update pass
+// reads it again right after; the update then takes mostly p, m (and v)
+// from HBM.  Measured on MI355X for one 180 MB-gradient tensor after
+// non-temporal traffic: the ordinary-load sum costs what a non-temporal one
+// does (28.8 vs 27.6 us) and the update drops from 150.5 to 124.6 us; on the
+// Llama-7B-shaped list the step drops from 28.1 to 25.8 ms.
 constexpr int32_t kMiniSumUnitsPerWg = 4;
 
 __device__ __forceinline__ float wave_sum(float x) {
@@ -20,6 +30,8 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 template <int GK>
 __global__ __launch_bounds__(kThreads) void mini_sumsq_kernel(StepArgs a) {
+    // g stays in the Infinity Cache for the update pass that follows
+    constexpr int LAY = kStridedKeep;
     __shared__ Scalars S;
     step_begin(a, S);
     const StepCommit commit{a, S};
@@ -33,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void mini_sumsq_kernel(StepArgs a) {
         lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
             constexpr int N = decltype(n)::value;
             float g[N];
-            load_g<GK, N>(T.g, e, s, g);
+            load_g<GK, N, LAY>(T.g, e, s, g);
 #pragma unroll
             for (int i = 0; i < N; ++i) acc += g[i] * g[i];
         });
@@ -56,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void mini_finalize_kernel(StepArgs a) {
     const StepCommit commit{a, S};
     if (S.skip) return;
     __shared__ double red[kThreads];
-    for (int b = blockIdx.x; b < a.nblocks; b += gridDim.x) {
+    for (int b = a.block0 + blockIdx.x; b < a.nblocks; b += gridDim.x) {
         const int si = a.blockspan[b];
         const SpanDesc sp = a.spans[si];
         const int64_t u0 = sp.unit_begin, u1 = a.spans[si + 1].unit_begin;
@@ -118,37 +130,61 @@ __global__ __launch_bounds__(kThreads) void mini_update_kernel(StepArgs a) {
 
 }  // namespace
 
-hipError_t launch_adam_mini(const StepArgs &args, int pk, int gk, hipStream_t s) {
-    // block sums and finalize read the step's inputs; the update publishes it
+template <int PK, int GK>
+static void launch_mini_update(const StepArgs &a, hipStream_t s) {
+    LAUNCH_PERSISTENT((mini_update_kernel<PK, GK>), a, s);
+}
+
+static hipError_t launch_mini_update_kind(const StepArgs &a, int pk, int gk, hipStream_t s) {
+    if (pk == P_F32 && gk == G_F32)
+        launch_mini_update<P_F32, G_F32>(a, s);
+    else if (pk == P_F32 && gk == G_BF16)
+        launch_mini_update<P_F32, G_BF16>(a, s);
+    else if (pk == P_BF16R && gk == G_F32)
+        launch_mini_update<P_BF16R, G_F32>(a, s);
+    else
+        launch_mini_update<P_BF16R, G_BF16>(a, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_adam_mini(const StepArgs &args, int pk, int gk, const MiniSegment *segs, int32_t nsegs,
+                            hipStream_t s) {
+    // every launch reads the step's inputs; the last update publishes it
     StepArgs a = args;
     a.commit = 0;
-    // the read-only sum pass streams better with 4 consecutive units per
-    // workgroup (measured on MI355X: 2.8% off a whole step of a
-    // 536M-element list against one unit; 2 and 8 in between)
-    if (a.grid_request == 0) a.units_per_wg = kMiniSumUnitsPerWg;
-    if (gk == G_F32)
-        LAUNCH_PERSISTENT((mini_sumsq_kernel<G_F32>), a, s);
-    else
-        LAUNCH_PERSISTENT((mini_sumsq_kernel<G_BF16>), a, s);
-    a.units_per_wg = args.units_per_wg;
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.nblocks > 0) {
-        const int fg = a.nblocks < 2048 ? a.nblocks : 2048;
-        hipLaunchKernelGGL(mini_finalize_kernel, dim3(fg), dim3(kThreads), 0, s, a);
-        e = hipGetLastError();
+    if (nsegs == 0) {  // empty plan: one workgroup commits
+        a.unit0 = a.nunits = 0;
+        a.commit = 1;
+        return launch_mini_update_kind(a, pk, gk, s);
+    }
+    for (int32_t i = 0; i < nsegs; ++i) {
+        const MiniSegment &sg = segs[i];
+        a.unit0 = sg.unit_begin;
+        a.nunits = sg.unit_end;
+        if (sg.block_end > sg.block_begin) {
+            // the read-only sum pass streams better with 4 consecutive units
+            // per workgroup (measured on MI355X: 2.8% off a whole step of a
+            // 536M-element list against one unit; 2 and 8 in between)
+            if (a.grid_request == 0) a.units_per_wg = kMiniSumUnitsPerWg;
+            if (gk == G_F32)
+                LAUNCH_PERSISTENT((mini_sumsq_kernel<G_F32>), a, s);
+            else
+                LAUNCH_PERSISTENT((mini_sumsq_kernel<G_BF16>), a, s);
+            a.units_per_wg = args.units_per_wg;
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            a.block0 = sg.block_begin;
+            a.nblocks = sg.block_end;
+            const int nb = sg.block_end - sg.block_begin;
+            hipLaunchKernelGGL(mini_finalize_kernel, dim3(nb < 2048 ? nb : 2048), dim3(kThreads), 0, s, a);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        a.commit = i == nsegs - 1 ? 1 : 0;
+        const hipError_t e = launch_mini_update_kind(a, pk, gk, s);
         if (e != hipSuccess) return e;
     }
-    a.commit = 1;
-    if (pk == P_F32 && gk == G_F32)
-        LAUNCH_PERSISTENT((mini_update_kernel<P_F32, G_F32>), a, s);
-    else if (pk == P_F32 && gk == G_BF16)
-        LAUNCH_PERSISTENT((mini_update_kernel<P_F32, G_BF16>), a, s);
-    else if (pk == P_BF16R && gk == G_F32)
-        LAUNCH_PERSISTENT((mini_update_kernel<P_BF16R, G_F32>), a, s);
-    else
-        LAUNCH_PERSISTENT((mini_update_kernel<P_BF16R, G_BF16>), a, s);
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 }  // namespace optim

@@ -16,6 +16,13 @@ namespace optim {
 constexpr int kThreads = 256;        // workgroup size (4 wavefronts of 64)
 constexpr int64_t kDefaultTile = 2048;
 constexpr int64_t kAdamMiniTile = 4096;   // also LAMB and the fp16 scaled-state step
+// Adam-mini: gradient bytes per segment (a segment's g is read twice, the
+// second time mostly from the 256 MB Infinity Cache).  Measured on MI355X,
+// Llama-7B-shaped list: 28.1 ms per step in one pass over the list; with
+// segments of 160 / 256 / 384 / 512 / 1024 MiB 27.3 / 26.5 / 25.8 / 26.0 /
+// 26.8 ms (fewer, larger segments launch less often; past the cache's size
+// less of g is found there).
+constexpr int64_t kMiniSegmentBytes = (int64_t)384 << 20;
 // blockwise units, measured best on MI355X over 2^28 elements (4096-65536):
 // 2-state 8-bit 4096, 2-state 4-bit 8192, AdEMAMix 8-bit 8192, 4-bit 16384
 constexpr int64_t blockwise_tile(bool ademamix, int bits) {
@@ -150,6 +157,7 @@ struct StepArgs {
     const TensorDesc *tensors;
     const SpanDesc *spans;    // nspans + 1 entries (sentinel at the end)
     int32_t nspans;
+    int64_t unit0;            // this launch covers units [unit0, nunits)
     int64_t nunits;
     int64_t tile;             // elements per unit
     double *partials;         // Adam-mini: one per unit; LAMB: two per unit;
@@ -159,6 +167,7 @@ struct StepArgs {
                               // fp16 scaled moments: the maxima slots
     const int32_t *blockspan; // span index of each block (Adam-mini shared-v
                               // block; LAMB or scaled-moment tensor)
+    int32_t block0;           // Adam-mini finalize: blocks [block0, nblocks)
     int32_t nblocks;
     const Codebook *codebook;
     int32_t bits, block;
@@ -174,7 +183,16 @@ struct StepArgs {
 // for an empty plan).
 hipError_t launch_adamw(const StepArgs &a, int pk, int gk, hipStream_t s);
 hipError_t launch_ademamix(const StepArgs &a, int pk, int gk, hipStream_t s);
-hipError_t launch_adam_mini(const StepArgs &a, int pk, int gk, hipStream_t s);
+// Adam-mini runs its three kernels segment by segment: a segment is a run of
+// whole tensors (units [unit_begin, unit_end), shared-v blocks
+// [block_begin, block_end)), either all with shared v and at most a bounded
+// number of gradient bytes, or all with full v (no block sums).
+struct MiniSegment {
+    int64_t unit_begin, unit_end;
+    int32_t block_begin, block_end;
+};
+hipError_t launch_adam_mini(const StepArgs &a, int pk, int gk, const MiniSegment *segs, int32_t nsegs,
+                            hipStream_t s);
 hipError_t launch_lion(const StepArgs &a, int pk, int gk, hipStream_t s);
 // AdamW with 16-bit moments and per-tensor scales (sk: S_F16 / S_BF16)
 hipError_t launch_adamw_scaled(const StepArgs &a, int pk, int gk, int sk, hipStream_t s);

@@ -116,6 +116,11 @@ def test_adam_mini_validation(L):
         fake_list([4096], mini_kind=kinds, head_numel=[500]), osa.OPTIM_ALGO_ADAM_MINI))
     expect_error(osa.OPTIM_EINVAL, lambda: ws(
         fake_list([4096], mini_kind=[7], head_numel=[0]), osa.OPTIM_ALGO_ADAM_MINI))
+    # launch segments: any positive gradient-byte bound (0 = default), never negative
+    seg = lambda b: osa.optim_plan_opts(0, 0, 0, 0, 0, b)
+    for b in (0, 1, 1 << 40):
+        assert ws(ok, osa.OPTIM_ALGO_ADAM_MINI, seg(b)) == ws(ok, osa.OPTIM_ALGO_ADAM_MINI)
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(ok, osa.OPTIM_ALGO_ADAM_MINI, seg(-1)))
 
 
 def test_blockwise_validation(L):
