@@ -162,12 +162,26 @@ def run_timed_cold(torch, call, steps, warmup, flush_bytes=1 << 30):
     return out
 
 
+def library_sources_sha256():
+    """sha256 over the library's sources and header, naming the build the
+    numbers were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "optimizer_step_adamw_amd", "csrc")
+    files = [os.path.join(csrc, f) for f in sorted(os.listdir(csrc))]
+    files.append(os.path.join(ROOT, "include", "optim_step.h"))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def environment(torch):
     """Device and software the numbers were taken on."""
     pr = torch.cuda.get_device_properties(0)
     return dict(device=pr.name, arch=getattr(pr, "gcnArchName", None), compute_units=pr.multi_processor_count,
                 hbm_gib=round(pr.total_memory / 2 ** 30, 1), torch=torch.__version__,
-                hip=getattr(torch.version, "hip", None), host_cpus=os.cpu_count())
+                hip=getattr(torch.version, "hip", None), host_cpus=os.cpu_count(),
+                library_sources_sha256=library_sources_sha256())
 
 
 def gbs(bytes_per_step, ms):
