@@ -512,7 +512,8 @@ def bench_c5(torch, osa, synth, steps, warmup):
     return dict(workload=wl.name, elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
                 gbs=gbs(alg, ms), frac=gbs(alg, ms) / PEAK_HBM_GBS,
                 note="algorithmic bytes 28 B/elem for full-v tensors, 20 B/elem for shared-v tensors; "
-                     "the kernels read g twice (block sums, then update)")
+                     "the kernels read g twice (block sums, then update), segment by segment, so the "
+                     "second read comes mostly from the Infinity Cache")
 
 
 # --------------------------------------------------------------------------
