@@ -91,6 +91,9 @@ enum Layout { kStrided = 0, kRun = 1, kStridedKeep = 2 };
 // groups of 4 elements per lane the AdamW / AdEMAMix / Adam-mini update
 // loads before computing (one 1 KiB run per array per wave and group)
 constexpr int kAdamGroups = 2;
+// the same for the early-load AdamW / AdEMAMix kernel on 4096-element units
+// (lists of more than 2^20 and at most 2^24 elements)
+constexpr int kAdamGroupsEarly = 4;
 
 template <class T>
 __device__ __forceinline__ GMEM T *gp(T *p) { return (GMEM T *)p; }
@@ -526,10 +529,10 @@ __device__ __forceinline__ void adam_elems(const TensorDesc &T, int64_t e, const
     adam_store<PK, ADE, N>(T, e, r);
 }
 
-template <int PK, int GK, bool ADE>
+template <int PK, int GK, bool ADE, int G = kAdamGroups>
 __device__ __forceinline__ void adam_unit(const TensorDesc &T, int64_t start, int64_t len,
                                           const AdamK &k, float lw) {
-    lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+    lane_walk<G>(start, len, T.vec_ok, [&](auto n, int64_t e) {
         adam_elems<PK, GK, ADE, decltype(n)::value>(T, e, k, lw);
     });
 }

@@ -5,19 +5,27 @@
 namespace optim {
 namespace {
 
-// EARLY: a workgroup whose unit is one whole, aligned tile (one group of
-// loads per lane) issues the unit's loads before the per-step prologue, so
-// their latency overlaps the scalar loads and fp64 arithmetic.  Measured on
-// MI355X: 5-10% faster up to ~2 resident waves of workgroups (8M elements:
-// AdamW 41.9 -> 39.1 us, AdEMAMix 54.3 -> 51.4 us), 1-6% slower from 12M
-// elements on, where the early loads of new workgroups crowd the stores of
-// the finishing ones -- so the launcher chooses by size.
-template <int PK, int GK, bool ADE, bool EARLY>
+// EG > 0 (early form): a workgroup whose unit is one whole, aligned tile of
+// EG groups per lane (EG * 1024 elements) issues all of the unit's loads
+// before the per-step prologue, so their latency overlaps the scalar loads
+// and fp64 arithmetic.  Plans up to ~2 resident waves of workgroups take it
+// (see kEarlyLoadUnits): 2048-element units of 2 groups for lists up to
+// 2^20 elements, 4096-element units of 4 groups above that up to 2^24.
+// Measured on MI355X with two state sets alternating (nothing cached),
+// against 2048-element units of two groups without early loads: AdamW 2^22
+// elements 22.5 -> 20.9 us, 2^23 42.1 -> 40.6 us, 2^24 80.8 -> 79.3 us;
+// AdEMAMix 28.8 -> 26.3, 54.9 -> 51.9, 104.2 -> 103.6 us.  From 2^25
+// elements on early loads of new workgroups crowd the stores of the
+// finishing ones (2^26: AdamW 311.7 -> 317.5 us), so larger plans take
+// 2048-element units of 2 groups without them (EG = 0).  The plan picks the
+// unit size by its element count and the launcher the form by the units.
+template <int PK, int GK, bool ADE, int EG>
 __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
     __shared__ Scalars S;
-    constexpr int N = kAdamGroups * kVec;
+    constexpr int G = EG > 0 ? EG : kAdamGroups;
+    constexpr int N = G * kVec;
     // (an empty plan still launches one workgroup, which has no unit)
-    if (EARLY && a.unit0 + (int64_t)blockIdx.x < a.nunits) {
+    if (EG > 0 && a.unit0 + (int64_t)blockIdx.x < a.nunits) {
         const int64_t u = a.unit0 + blockIdx.x;
         int si = span_of(a, u);
         while (a.spans[si + 1].unit_begin <= u) ++si;
@@ -46,25 +54,26 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
     const AdamK k = adam_consts(S);
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
         const TensorDesc &T = a.tensors[sp.tensor];
-        adam_unit<PK, GK, ADE>(T, start, len, k, uniform(S.lrwd[T.group]));
+        adam_unit<PK, GK, ADE, G>(T, start, len, k, uniform(S.lrwd[T.group]));
     });
 }
 
-// Up to this many units (2048 elements each) the early-load form is used.
+// Up to this many units the early-load form is used.
 constexpr int64_t kEarlyLoadUnits = 4096;
 
 }  // namespace
 
 template <bool ADE, int PK, int GK>
 static void launch_adam_g(const StepArgs &a, hipStream_t s) {
-    // the early form needs one whole tile of one group per lane per
-    // workgroup: the default grid over 2048-element units
-    const bool early = a.grid_request == 0 && a.units_per_wg == 1 && a.tile == (int64_t)kAdamGroups * kSub &&
-                       a.nunits <= kEarlyLoadUnits;
-    if (early)
-        LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, true>), a, s);
+    // the early form needs one whole tile of its groups per lane per
+    // workgroup: the default grid over 2048- or 4096-element units
+    const bool early = a.grid_request == 0 && a.units_per_wg == 1 && a.nunits - a.unit0 <= kEarlyLoadUnits;
+    if (early && a.tile == (int64_t)kAdamGroups * kSub)
+        LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, kAdamGroups>), a, s);
+    else if (early && a.tile == (int64_t)kAdamGroupsEarly * kSub)
+        LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, kAdamGroupsEarly>), a, s);
     else
-        LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, false>), a, s);
+        LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, 0>), a, s);
 }
 
 template <bool ADE, int PK>

@@ -124,6 +124,28 @@ def test_launch_shapes(algo, tile, grid):
               key=5, tile=tile, grid=grid)
 
 
+# More than 2^20 elements: the default plan takes 4096-element units and the
+# step its early-load form with 4 groups per lane; ragged tensors mix whole
+# units (early form) and partial ones.
+MID = [1 << 20, 4096 * 100 + 37, 3000]
+
+
+@pytest.mark.parametrize("algo,bf16", [(osa.OPTIM_ALGO_ADAMW, True), (osa.OPTIM_ALGO_ADEMAMIX, False)])
+def test_mid_size_list_early_units(algo, bf16):
+    _run_adam(algo, MID, 3, lr=3e-4, betas=(0.9, 0.95), grad_bf16=bf16, param_bf16=bf16, g_std=1e-3, key=21)
+
+
+@pytest.mark.parametrize("algo", [osa.OPTIM_ALGO_ADAMW, osa.OPTIM_ALGO_ADEMAMIX])
+def test_launch_forms_give_the_same_bits(algo):
+    """4096-element units (early form, 4 groups), 2048-element units (early
+    form, 2 groups), 8192-element units and a persistent grid (no early
+    loads) compute the same elementwise step: identical bits."""
+    runs = [_run_adam(algo, MID, 2, lr=1e-3, key=22, tile=t, grid=g)[0]
+            for t, g in ((0, 0), (2048, 0), (8192, 0), (4096, 11))]
+    for st in runs[1:]:
+        assert all_equal(runs[0].buffers(), st.buffers())
+
+
 def test_ademamix_fp32_ragged():
     _run_adam(osa.OPTIM_ALGO_ADEMAMIX, RAGGED, 12, lr=0.1, wd_of=lambda i: 0.1, key=3)
 
