@@ -125,9 +125,9 @@ typedef struct optim_tensor_list {
  *  grid        0 (default): one workgroup per work unit; > 0: a persistent
  *              grid of that many workgroups walking the units grid-stride
  *  tile        elements per work unit, a power of two in [1024, 2^24]
- *              (blockwise: at least 2048); 0 = 2048 (AdamW and AdEMAMix
- *              with fp32 moments on lists of more than 2^20 and at most
- *              2^24 elements 4096; Adam-mini, LAMB and fp16 states 4096;
+ *              (blockwise: at least 2048); 0 = 2048 (AdamW, AdEMAMix
+ *              with fp32 moments and Lion on lists of more than 2^20 and at
+ *              most 2^24 elements 4096; Adam-mini, LAMB and fp16 states 4096;
  *              blockwise 8-bit 4096, 4-bit 8192, and blockwise AdEMAMix
  *              8-bit 8192, 4-bit 16384)
  *  state_dtype AdamW only: OPTIM_F32 (0, default) fp32 moments; OPTIM_F16

@@ -173,13 +173,14 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     // reductions), and the blockwise step amortises its LDS tables and
     // prologue over larger units
     const bool unit_sums = algo == OPTIM_ALGO_ADAM_MINI || algo == OPTIM_ALGO_LAMB || sdt == OPTIM_F16;
-    // AdamW / AdEMAMix (fp32 moments) plans of (2^20, 2^24] elements take
-    // the units of the early-load kernel form
+    // AdamW / AdEMAMix (fp32 moments) and Lion plans of (2^20, 2^24]
+    // elements take the units of the early-load kernel form
     int64_t total = 0;  // elements, counted only up to past the bound
     if (n > 0 && list->numel)
         for (int i = 0; i < n && total <= kEarlyTileMaxElems; ++i)
             total += std::min<int64_t>(std::max<int64_t>(list->numel[i], 0), kMaxNumel);
-    const bool early_units = (algo == OPTIM_ALGO_ADAMW || algo == OPTIM_ALGO_ADEMAMIX) && !states16 &&
+    const bool early_units = (algo == OPTIM_ALGO_ADAMW || algo == OPTIM_ALGO_ADEMAMIX || algo == OPTIM_ALGO_LION) &&
+                             !states16 &&
                              total > kEarlyTileMinElems && total <= kEarlyTileMaxElems;
     const int64_t tile = (opts && opts->tile > 0) ? opts->tile
                          : is_blockwise(algo) ? blockwise_tile(algo == OPTIM_ALGO_BLOCKWISE_ADEMAMIX, bits)

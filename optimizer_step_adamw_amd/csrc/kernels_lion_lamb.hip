@@ -10,12 +10,9 @@ namespace {
 // sign update.  Per element (Chen et al., arXiv:2302.06675), fp32, no
 // contraction:
 //   c = b1 m + c1 g;  p <- p (1 - lr wd) - lr sign(c);  m <- b2 m + c2 g
-template <int PK, int GK, int N>
-__device__ __forceinline__ void lion_elems(const TensorDesc &T, int64_t e, const AdamK &k, float lw) {
-    float p[N], g[N], m[N];
-    load_p<PK, N>(T, e, p);
-    load_g<GK, N>(T.g, e, k.inv_scale, g);
-    ldf<N>(T.m, e, m);
+template <int N>
+__device__ __forceinline__ void lion_math(float (&p)[N], const float (&g)[N], float (&m)[N], const AdamK &k,
+                                          float lw) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
         const float c = k.b1 * m[i] + k.c1 * g[i];
@@ -23,13 +20,54 @@ __device__ __forceinline__ void lion_elems(const TensorDesc &T, int64_t e, const
         p[i] = decayed(p[i], lw, k.lr * s);
         m[i] = k.b2 * m[i] + k.c2 * g[i];
     }
+}
+
+template <int PK, int GK, int N>
+__device__ __forceinline__ void lion_elems(const TensorDesc &T, int64_t e, const AdamK &k, float lw) {
+    float p[N], g[N], m[N];
+    load_p<PK, N>(T, e, p);
+    load_g<GK, N>(T.g, e, k.inv_scale, g);
+    ldf<N>(T.m, e, m);
+    lion_math<N>(p, g, m, k, lw);
     store_p<PK, N>(T, e, p);
     stf<N>(T.m, e, m);
 }
 
-template <int PK, int GK>
+// EG > 0: the early-load form of the AdamW kernel (a whole unit of EG groups
+// per lane loaded before the per-step prologue), for plans of at most
+// kLionEarlyUnits units; the plan's unit size (2048 or 4096 elements) fixes
+// EG.
+template <int PK, int GK, int EG>
 __global__ __launch_bounds__(kThreads) void lion_kernel(StepArgs a) {
     __shared__ Scalars S;
+    constexpr int G = EG > 0 ? EG : kAdamGroups;
+    constexpr int N = G * kVec;
+    if (EG > 0 && a.unit0 + (int64_t)blockIdx.x < a.nunits) {
+        const int64_t u = a.unit0 + blockIdx.x;
+        int si = span_of(a, u);
+        while (a.spans[si + 1].unit_begin <= u) ++si;
+        const SpanDesc sp = a.spans[si];
+        const int64_t off = (u - sp.unit_begin) * a.tile;
+        const TensorDesc &T = a.tensors[sp.tensor];
+        const int64_t start = sp.elem_begin + off;
+        if (sp.len - off >= a.tile && T.vec_ok && start % kVec == 0) {
+            const int64_t e = start + threadIdx.x * kVec;
+            float p[N], g[N], m[N];
+            load_p<PK, N>(T, e, p);
+            load_g<GK, N>(T.g, e, 1.0f, g);
+            ldf<N>(T.m, e, m);
+            step_begin(a, S);
+            const StepCommit commit{a, S};
+            if (S.skip) return;
+            const AdamK k = adam_consts(S);
+#pragma unroll
+            for (int i = 0; i < N; ++i) g[i] = g[i] * k.inv_scale;  // g * 1 * s == g * s
+            lion_math<N>(p, g, m, k, uniform(S.lrwd[T.group]));
+            store_p<PK, N>(T, e, p);
+            stf<N>(T.m, e, m);
+            return;
+        }
+    }
     step_begin(a, S);
     const StepCommit commit{a, S};
     if (S.skip) return;
@@ -37,11 +75,13 @@ __global__ __launch_bounds__(kThreads) void lion_kernel(StepArgs a) {
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
         const TensorDesc &T = a.tensors[sp.tensor];
         const float lw = uniform(S.lrwd[T.group]);
-        lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+        lane_walk<G>(start, len, T.vec_ok, [&](auto n, int64_t e) {
             lion_elems<PK, GK, decltype(n)::value>(T, e, k, lw);
         });
     });
 }
+
+constexpr int64_t kLionEarlyUnits = 4096;
 
 // ---------------------------------------------------------------- LAMB
 // You et al., arXiv:1904.00962, Algorithm 2, with Adam's direction as in the
@@ -173,15 +213,26 @@ __global__ __launch_bounds__(kThreads) void lamb_update_kernel(StepArgs a) {
 
 }  // namespace
 
+template <int PK, int GK>
+static void launch_lion_t(const StepArgs &a, hipStream_t s) {
+    const bool early = a.grid_request == 0 && a.units_per_wg == 1 && a.nunits - a.unit0 <= kLionEarlyUnits;
+    if (early && a.tile == (int64_t)kAdamGroups * kSub)
+        LAUNCH_PERSISTENT((lion_kernel<PK, GK, kAdamGroups>), a, s);
+    else if (early && a.tile == (int64_t)kAdamGroupsEarly * kSub)
+        LAUNCH_PERSISTENT((lion_kernel<PK, GK, kAdamGroupsEarly>), a, s);
+    else
+        LAUNCH_PERSISTENT((lion_kernel<PK, GK, 0>), a, s);
+}
+
 hipError_t launch_lion(const StepArgs &a, int pk, int gk, hipStream_t s) {
     if (pk == P_F32 && gk == G_F32)
-        LAUNCH_PERSISTENT((lion_kernel<P_F32, G_F32>), a, s);
+        launch_lion_t<P_F32, G_F32>(a, s);
     else if (pk == P_F32 && gk == G_BF16)
-        LAUNCH_PERSISTENT((lion_kernel<P_F32, G_BF16>), a, s);
+        launch_lion_t<P_F32, G_BF16>(a, s);
     else if (pk == P_BF16R && gk == G_F32)
-        LAUNCH_PERSISTENT((lion_kernel<P_BF16R, G_F32>), a, s);
+        launch_lion_t<P_BF16R, G_F32>(a, s);
     else
-        LAUNCH_PERSISTENT((lion_kernel<P_BF16R, G_BF16>), a, s);
+        launch_lion_t<P_BF16R, G_BF16>(a, s);
     return hipGetLastError();
 }
 

@@ -15,8 +15,9 @@ namespace optim {
 // persistent grid whose workgroups walk the units grid-stride.
 constexpr int kThreads = 256;        // workgroup size (4 wavefronts of 64)
 constexpr int64_t kDefaultTile = 2048;
-// AdamW / AdEMAMix plans of more than 2^20 and at most 2^24 elements: units
-// of 4096, which the step runs in its early-load form (see kernels_adam.hip)
+// AdamW / AdEMAMix / Lion plans of more than 2^20 and at most 2^24 elements:
+// units of 4096, which the step runs in its early-load form (see
+// kernels_adam.hip)
 constexpr int64_t kEarlyTile = 4096;
 constexpr int64_t kEarlyTileMinElems = int64_t(1) << 20;
 constexpr int64_t kEarlyTileMaxElems = int64_t(1) << 24;

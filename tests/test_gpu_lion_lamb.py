@@ -37,11 +37,17 @@ def _load(state, sizes, key, t, scale):
     return out
 
 
-@pytest.mark.parametrize("bf16,tile,grid", [(False, 0, 0), (True, 0, 0), (False, 1024, 0), (True, 2048, 7)])
-def test_lion_matches_oracle(bf16, tile, grid):
+# more than 2^20 elements: 4096-element units, early-load form with 4 groups
+MID = [1 << 20, 4096 * 100 + 37, 3000]
+
+
+@pytest.mark.parametrize("bf16,tile,grid,sizes", [(False, 0, 0, RAGGED), (True, 0, 0, RAGGED), (False, 1024, 0, RAGGED),
+                                                  (True, 2048, 7, RAGGED), (False, 0, 0, MID), (True, 0, 0, MID)])
+def test_lion_matches_oracle(bf16, tile, grid, sizes):
     """m bit for bit (the fp32 recipe is fixed, so every sign decision is the
-    oracle's); p within the step bounds over 12 steps."""
-    sizes = RAGGED
+    oracle's); p within the step bounds over 12 steps.  The default plans take
+    the early-load form (2048-element units for the ragged list, 4096 for the
+    list above 2^20 elements)."""
     lr, wd = 1e-3, 0.1
     wds = [wd * (i % 2) for i in range(len(sizes))]
     p0 = _p0(sizes, 1 + bf16)
@@ -62,7 +68,7 @@ def test_lion_matches_oracle(bf16, tile, grid):
             err = relerr_tau(st.master(i).cpu().numpy(), op[i], lr32)
             assert err <= (TOL_STEP1 if t == 1 else TOL_RUN), (t, i, err)
     assert int(sc.step.item()) == 12
-    say(f"lion bf16={bf16} tile={tile} grid={grid}: m bit-exact, p within bounds")
+    say(f"lion bf16={bf16} tile={tile} grid={grid} n={sum(sizes)}: m bit-exact, p within bounds")
 
 
 @pytest.mark.parametrize("bf16,tile,grid", [(False, 0, 0), (True, 0, 0), (False, 1024, 0), (False, 2048, 5)])
