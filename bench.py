@@ -464,6 +464,28 @@ def bench_c4(torch, osa, synth, steps, warmup):
         out[f"blockwise_{bits}bit_block{block}"] = dict(
             elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3), bytes_per_element=bpe,
             gbs=gbs(bpe * n, ms), frac=gbs(bpe * n, ms) / PEAK_HBM_GBS)
+        # the same states in the interleaved layout (m and v codes side by side
+        # in one array, the two absmax values of a block in another)
+        del qm, qv, am, av
+        torch.cuda.empty_cache()
+        qmv = torch.zeros(2 * nb, dtype=torch.uint8, device="cuda")
+        amv = torch.zeros(2 * (n // block), dtype=torch.float32, device="cuda")
+        tl = osa.TensorList([p], [g], qm=[qmv], absmax_m=[amv], weight_decay=[hp.wd])
+        plan = osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE, bits=bits, block=block,
+                        state_layout=osa.OPTIM_LAYOUT_INTERLEAVED)
+        s = scalars(torch, hp.lr)
+        ms, _, _ = run_timed(torch, [lambda: osa.optim_step_8bit_blockwise(
+            plan.handle, h, bits, block, s["lr"], None, None, s["step"])], steps, warmup)
+        plan.close()
+        out[f"blockwise_{bits}bit_block{block}_interleaved"] = dict(
+            elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3), bytes_per_element=bpe,
+            gbs=gbs(bpe * n, ms), frac=gbs(bpe * n, ms) / PEAK_HBM_GBS)
+        del qmv, amv
+        torch.cuda.empty_cache()
+        qm = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+        qv = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+        am = torch.zeros(n // block, dtype=torch.float32, device="cuda")
+        av = torch.zeros(n // block, dtype=torch.float32, device="cuda")
         # the same list with AdEMAMix's third state (slow EMA m2, signed codes)
         qm2 = torch.zeros(nb, dtype=torch.uint8, device="cuda")
         am2 = torch.zeros(n // block, dtype=torch.float32, device="cuda")

@@ -47,6 +47,8 @@ extern "C" {
 
 /* ---- enumerations ------------------------------------------------------ */
 enum { OPTIM_F32 = 0, OPTIM_BF16 = 1, OPTIM_F16 = 2 };
+/* blockwise state layouts (optim_plan_opts.state_layout)                  */
+enum { OPTIM_LAYOUT_SEPARATE = 0, OPTIM_LAYOUT_INTERLEAVED = 1 };
 enum {
     OPTIM_ALGO_ADAMW = 0,
     OPTIM_ALGO_ADEMAMIX = 1,
@@ -128,7 +130,7 @@ typedef struct optim_tensor_list {
  *              (blockwise: at least 2048); 0 = 2048 (AdamW, AdEMAMix
  *              with fp32 moments and Lion on lists of more than 2^20 and at
  *              most 2^24 elements 4096; Adam-mini, LAMB and fp16 states 4096;
- *              blockwise 8-bit 4096, 4-bit 8192, and blockwise AdEMAMix
+ *              blockwise 8-bit and 4-bit 8192, and blockwise AdEMAMix
  *              8-bit 8192, 4-bit 16384)
  *  state_dtype AdamW only: OPTIM_F32 (0, default) fp32 moments; OPTIM_F16
  *              or OPTIM_BF16 16-bit moments with a per-tensor scale
@@ -139,7 +141,17 @@ typedef struct optim_tensor_list {
  *              gradient bytes (a larger tensor forms a segment alone), or a
  *              run of full-v tensors; 0 = 384 MiB (the gradients are read
  *              twice, the second time mostly from the Infinity Cache).  Results
- *              do not depend on it.  Negative: OPTIM_EINVAL.              */
+ *              do not depend on it.  Negative: OPTIM_EINVAL.
+ *  state_layout  OPTIM_ALGO_BLOCKWISE only.  OPTIM_LAYOUT_SEPARATE (0,
+ *              default): qm / qv and absmax_m / absmax_v are four arrays.
+ *              OPTIM_LAYOUT_INTERLEAVED (1): each element's m and v codes
+ *              sit side by side in qm -- 8-bit: 2 bytes per element, m
+ *              first; 4-bit: 1 byte per element, m in the low nibble, v in
+ *              the high one -- and absmax_m holds (absmax of m, absmax of v)
+ *              per block (8-byte aligned); qv and absmax_v must be NULL.
+ *              The values are those of the separate layout, bit for bit; the
+ *              step streams two arrays fewer.  The quantize / dequantize
+ *              helpers below work on separate arrays.                     */
 typedef struct optim_plan_opts {
     int32_t bits;
     int32_t block;
@@ -147,6 +159,7 @@ typedef struct optim_plan_opts {
     int32_t tile;
     int32_t state_dtype;
     int64_t segment_bytes;
+    int32_t state_layout;
 } optim_plan_opts;
 
 /* Hyperparameters, validated as in [MINI] AdamWMini's constructor:

@@ -18,6 +18,7 @@ from .build import LIB_PATH, build as build_library
 OPTIM_OK = 0
 OPTIM_EINVAL, OPTIM_EALIGN, OPTIM_EDTYPE, OPTIM_EWORKSPACE, OPTIM_EUNSUPPORTED, OPTIM_EHIP = range(1, 7)
 OPTIM_F32, OPTIM_BF16, OPTIM_F16 = 0, 1, 2
+OPTIM_LAYOUT_SEPARATE, OPTIM_LAYOUT_INTERLEAVED = 0, 1
 (OPTIM_ALGO_ADAMW, OPTIM_ALGO_ADEMAMIX, OPTIM_ALGO_ADAM_MINI, OPTIM_ALGO_BLOCKWISE,
  OPTIM_ALGO_BLOCKWISE_ADEMAMIX, OPTIM_ALGO_LION, OPTIM_ALGO_LAMB) = range(7)
 OPTIM_MINI_FULL_V, OPTIM_MINI_HEAD, OPTIM_MINI_SCALAR = range(3)
@@ -60,7 +61,8 @@ class optim_tensor_list(ctypes.Structure):
 
 class optim_plan_opts(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("block", ctypes.c_int32), ("grid", ctypes.c_int32),
-                ("tile", ctypes.c_int32), ("state_dtype", ctypes.c_int32), ("segment_bytes", ctypes.c_int64)]
+                ("tile", ctypes.c_int32), ("state_dtype", ctypes.c_int32), ("segment_bytes", ctypes.c_int64),
+                ("state_layout", ctypes.c_int32)]
 
 
 class optim_adamw_hp(ctypes.Structure):
@@ -315,12 +317,12 @@ class Plan:
     """Plan + workspace.  ``tl`` must hold device tensors that outlive it."""
 
     def __init__(self, tl: TensorList, algo: int, *, bits: int = 0, block: int = 0, grid: int = 0,
-                 tile: int = 0, state_dtype: int = OPTIM_F32, segment_bytes: int = 0, device=None,
-                 stream=None):
+                 tile: int = 0, state_dtype: int = OPTIM_F32, segment_bytes: int = 0,
+                 state_layout: int = 0, device=None, stream=None):
         import torch
         self.algo = algo
         self.tl = tl
-        self.opts = optim_plan_opts(bits, block, grid, tile, state_dtype, segment_bytes)
+        self.opts = optim_plan_opts(bits, block, grid, tile, state_dtype, segment_bytes, state_layout)
         nbytes = optim_plan_workspace_size(tl, algo, self.opts)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
         self.handle = optim_plan_create(tl, algo, self.opts, self.workspace, nbytes, stream)

@@ -100,6 +100,7 @@ struct Built {
     int64_t npartials = 0;   // capacity of the partials region
     int32_t nblocks = 0;
     std::vector<MiniSegment> segs;  // Adam-mini launch segments
+    bool interleaved = false;       // blockwise: interleaved state layout
     Layout L{};
 };
 
@@ -151,6 +152,13 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
             return fail(OPTIM_EINVAL, bits == 8 ? "8-bit block must be 64, 128 or 256"
                                                 : "4-bit block must be 128, 256 or 512");
     }
+    const int32_t layout = opts ? opts->state_layout : OPTIM_LAYOUT_SEPARATE;
+    if (layout != OPTIM_LAYOUT_SEPARATE && layout != OPTIM_LAYOUT_INTERLEAVED)
+        return fail(OPTIM_EINVAL, "unknown state_layout");
+    if (layout == OPTIM_LAYOUT_INTERLEAVED && algo != OPTIM_ALGO_BLOCKWISE)
+        return fail(OPTIM_EUNSUPPORTED, "the interleaved state layout is for the 2-state blockwise step");
+    const bool il = layout == OPTIM_LAYOUT_INTERLEAVED;
+    B.interleaved = il;
     if (opts && opts->grid < 0) return fail(OPTIM_EINVAL, "negative grid");
     B.grid = opts ? opts->grid : 0;
     if (opts && opts->tile < 0) return fail(OPTIM_EINVAL, "negative tile");
@@ -199,8 +207,9 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     if (n > 0 && algo == OPTIM_ALGO_LION && !list->m) return fail(OPTIM_EINVAL, "Lion needs the m array");
     if (n > 0 && algo == OPTIM_ALGO_ADEMAMIX && !list->m2)
         return fail(OPTIM_EINVAL, "AdEMAMix needs the m2 array");
-    if (n > 0 && is_blockwise(algo) && (!list->qm || !list->qv || !list->absmax_m || !list->absmax_v))
-        return fail(OPTIM_EINVAL, "blockwise plans need qm, qv, absmax_m and absmax_v");
+    if (n > 0 && is_blockwise(algo) && (!list->qm || (!il && !list->qv) || !list->absmax_m || (!il && !list->absmax_v)))
+        return fail(OPTIM_EINVAL, il ? "interleaved blockwise plans need qm and absmax_m"
+                                     : "blockwise plans need qm, qv, absmax_m and absmax_v");
     if (n > 0 && algo == OPTIM_ALGO_BLOCKWISE_ADEMAMIX && (!list->qm2 || !list->absmax_m2))
         return fail(OPTIM_EINVAL, "blockwise AdEMAMix plans need qm2 and absmax_m2");
     if (n > 0 && algo == OPTIM_ALGO_ADAM_MINI && (!list->mini_kind || !list->head_numel))
@@ -314,7 +323,18 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
             vec = vec && aligned(T.m2, 16);
             add(T.m2, numel * 4, true, "m2");
         }
-        if (is_blockwise(algo)) {
+        if (is_blockwise(algo) && il) {
+            // m and v codes side by side in qm, (absmax m, absmax v) pairs in am
+            if ((list->qv && list->qv[i]) || (list->absmax_v && list->absmax_v[i]))
+                return fail(OPTIM_EINVAL, ti + "interleaved layout: qv and absmax_v must be NULL");
+            T.qm = static_cast<uint8_t *>(list->qm[i]);
+            T.am = list->absmax_m[i];
+            if (numel > 0 && (!T.qm || !T.am)) return fail(OPTIM_EINVAL, ti + "NULL code or absmax buffer");
+            if (!aligned(T.am, 8)) return fail(OPTIM_EALIGN, ti + "interleaved absmax must be 8-byte aligned");
+            vec = vec && aligned(T.qm, 16);
+            add(T.qm, numel * 2 * bits / 8, true, "qm");
+            add(T.am, (numel + block - 1) / block * 8, true, "absmax_m");
+        } else if (is_blockwise(algo)) {
             T.qm = static_cast<uint8_t *>(list->qm[i]);
             T.qv = static_cast<uint8_t *>(list->qv[i]);
             T.am = list->absmax_m[i];
@@ -442,6 +462,7 @@ struct optim_plan {
     char *ws;
     Layout L;
     std::vector<MiniSegment> segs;  // Adam-mini launch segments
+    int32_t interleaved;            // blockwise: interleaved state layout
     int32_t sched;
     double lr_max, lr_min;
     int32_t K;
@@ -522,6 +543,7 @@ int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_p
     P->ws = static_cast<char *>(workspace);
     P->L = B.L;
     P->segs = std::move(B.segs);
+    P->interleaved = B.interleaved ? 1 : 0;
     P->sched = OPTIM_SCHED_NONE;
     *out = P;
     return OPTIM_OK;
@@ -574,6 +596,7 @@ StepArgs step_args(optim_plan *P) {
     a.codebook = reinterpret_cast<const Codebook *>(P->ws + P->L.codebook);
     a.bits = P->bits;
     a.block = P->block;
+    a.interleaved = P->interleaved;
     a.cus = P->cus;
     a.grid_request = P->grid;
     a.units_per_wg = 1;

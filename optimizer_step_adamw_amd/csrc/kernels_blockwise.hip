@@ -182,6 +182,76 @@ __device__ __forceinline__ void store_codes_part(uint8_t *q, int64_t e, int nv, 
     for (int b = 0; b < nbytes; ++b) gp(q)[byte0 + b] = (uint8_t)(c >> (8 * b));
 }
 
+// Interleaved layout: element j's m and v codes are one field of 2*BITS
+// bits (m in the low BITS), fields in element order; a lane's E elements
+// are E*BITS/4 bytes.  split / join convert to and from the per-state
+// packing above (element j in bits [j*BITS, (j+1)*BITS) of cm and cv).
+template <int BITS, int E>
+__device__ __forceinline__ void split_il(uint64_t raw, uint64_t &cm, uint64_t &cv) {
+    constexpr uint64_t mask = (1ull << BITS) - 1ull;
+    cm = 0;
+    cv = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        const uint64_t f = raw >> (j * 2 * BITS);
+        cm |= (f & mask) << (j * BITS);
+        cv |= ((f >> BITS) & mask) << (j * BITS);
+    }
+}
+
+template <int BITS, int E>
+__device__ __forceinline__ uint64_t join_il(uint64_t cm, uint64_t cv) {
+    constexpr uint64_t mask = (1ull << BITS) - 1ull;
+    uint64_t raw = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+        raw |= (((cm >> (j * BITS)) & mask) | (((cv >> (j * BITS)) & mask) << BITS)) << (j * 2 * BITS);
+    return raw;
+}
+
+// Whole lanes: one 32- or 64-bit access of the lane's fields, in the row's
+// access kind.
+template <int BITS, int E>
+__device__ __forceinline__ uint64_t load_il_full(const uint8_t *q, int64_t e) {
+    constexpr int NB = E * BITS / 4;
+    constexpr int LAY = row_layout<E>();
+    const int64_t byte0 = e * BITS / 4;
+    if constexpr (NB == 8) {
+        const u32x2 w = vload<LAY>((const GMEM u32x2 *)gp(q + byte0));
+        return (uint64_t)w.x | ((uint64_t)w.y << 32);
+    } else {
+        static_assert(NB == 4, "interleaved run");
+        return vload<LAY>((const GMEM uint32_t *)gp(q + byte0));
+    }
+}
+
+template <int BITS, int E>
+__device__ __forceinline__ void store_il_full(uint8_t *q, int64_t e, uint64_t raw) {
+    constexpr int NB = E * BITS / 4;
+    constexpr int LAY = row_layout<E>();
+    const int64_t byte0 = e * BITS / 4;
+    if constexpr (NB == 8)
+        vstore<LAY>((GMEM u32x2 *)gp(q + byte0), u32x2{(uint32_t)raw, (uint32_t)(raw >> 32)});
+    else
+        vstore<LAY>((GMEM uint32_t *)gp(q + byte0), (uint32_t)raw);
+}
+
+// Tail: the fields of nv < E valid elements, byte by byte (a field is whole
+// bytes: 2 for 8-bit codes, 1 for 4-bit).
+template <int BITS>
+__device__ __forceinline__ uint64_t load_il_part(const uint8_t *q, int64_t e, int nv) {
+    const int64_t byte0 = e * BITS / 4;
+    uint64_t out = 0;
+    for (int b = 0; b < nv * BITS / 4; ++b) out |= (uint64_t)gp(q)[byte0 + b] << (8 * b);
+    return out;
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_il_part(uint8_t *q, int64_t e, int nv, uint64_t raw) {
+    const int64_t byte0 = e * BITS / 4;
+    for (int b = 0; b < nv * BITS / 4; ++b) gp(q)[byte0 + b] = (uint8_t)(raw >> (8 * b));
+}
+
 // A 64-bit pointer that is the same in every lane, moved to scalar registers.
 // readfirstlane returns int: each half goes back through uint32_t, so a low
 // half with bit 31 set is not sign-extended into the high half.
@@ -205,15 +275,23 @@ struct UnitPtrs {
     int lane;
 };
 
-template <int GK, int BITS, int BLOCK, bool ADE>
+// IL: interleaved layout, qm / am hold both states (qv, av unused).
+template <int GK, int BITS, int BLOCK, bool ADE, bool IL>
 __device__ __forceinline__ UnitPtrs unit_ptrs(const TensorDesc &T, int64_t start, float lw) {
     UnitPtrs u;
     u.p = uniform_ptr(static_cast<float *>(T.p) + start);
     u.g = uniform_ptr(static_cast<const char *>(T.g) + start * (GK == G_F32 ? 4 : 2));
-    u.qm = uniform_ptr(T.qm + start * BITS / 8);
-    u.qv = uniform_ptr(T.qv + start * BITS / 8);
-    u.am = uniform_ptr(T.am + start / BLOCK);
-    u.av = uniform_ptr(T.av + start / BLOCK);
+    if (IL) {
+        u.qm = uniform_ptr(T.qm + start * BITS / 4);
+        u.am = uniform_ptr(T.am + 2 * (start / BLOCK));
+        u.qv = nullptr;
+        u.av = nullptr;
+    } else {
+        u.qm = uniform_ptr(T.qm + start * BITS / 8);
+        u.qv = uniform_ptr(T.qv + start * BITS / 8);
+        u.am = uniform_ptr(T.am + start / BLOCK);
+        u.av = uniform_ptr(T.av + start / BLOCK);
+    }
     if (ADE) {
         u.qm2 = uniform_ptr(T.qm2 + start * BITS / 8);
         u.am2 = uniform_ptr(T.am2 + start / BLOCK);
@@ -234,7 +312,7 @@ struct RowIn {
 
 // FULL: the whole row is inside the tensor and every pointer is aligned;
 // otherwise nv (0..E) of the lane's elements are valid and the rest read 0.
-template <int GK, int BITS, int BLOCK, bool ADE, bool FULL>
+template <int GK, int BITS, int BLOCK, bool ADE, bool FULL, bool IL>
 __device__ __forceinline__ void load_row(const UnitPtrs &u, const AdamK &k, uint32_t e, int nv,
                                          RowIn<lane_elems(BLOCK)> &in) {
     constexpr int E = lane_elems(BLOCK);
@@ -243,16 +321,26 @@ __device__ __forceinline__ void load_row(const UnitPtrs &u, const AdamK &k, uint
     in.am = in.av = in.am2 = 0.0f;
     in.cm = in.cv = in.cm2 = 0;
     if (FULL || nv > 0) {
-        in.am = gp(u.am)[blk];
-        in.av = gp(u.av)[blk];
-        if (ADE) in.am2 = gp(u.am2)[blk];
+        if constexpr (IL) {
+            const u32x2 w = gp(reinterpret_cast<const u32x2 *>(u.am))[blk];
+            in.am = __uint_as_float(w.x);
+            in.av = __uint_as_float(w.y);
+        } else {
+            in.am = gp(u.am)[blk];
+            in.av = gp(u.av)[blk];
+            if (ADE) in.am2 = gp(u.am2)[blk];
+        }
     }
     if (FULL) {
         ldf<E, LAY>(u.p, e, in.p);
         load_g<GK, E, LAY>(u.g, e, k.inv_scale, in.g);
-        in.cm = load_codes_full<BITS, E>(u.qm, e);
-        in.cv = load_codes_full<BITS, E>(u.qv, e);
-        if (ADE) in.cm2 = load_codes_full<BITS, E>(u.qm2, e);
+        if constexpr (IL) {
+            split_il<BITS, E>(load_il_full<BITS, E>(u.qm, e), in.cm, in.cv);
+        } else {
+            in.cm = load_codes_full<BITS, E>(u.qm, e);
+            in.cv = load_codes_full<BITS, E>(u.qv, e);
+            if (ADE) in.cm2 = load_codes_full<BITS, E>(u.qm2, e);
+        }
     } else {
 #pragma unroll
         for (int j = 0; j < E; ++j) {
@@ -265,16 +353,20 @@ __device__ __forceinline__ void load_row(const UnitPtrs &u, const AdamK &k, uint
             in.g[j] = gj[0];
         }
         if (nv > 0) {
-            in.cm = load_codes_part<BITS>(u.qm, e, nv);
-            in.cv = load_codes_part<BITS>(u.qv, e, nv);
-            if (ADE) in.cm2 = load_codes_part<BITS>(u.qm2, e, nv);
+            if constexpr (IL) {
+                split_il<BITS, E>(load_il_part<BITS>(u.qm, e, nv), in.cm, in.cv);
+            } else {
+                in.cm = load_codes_part<BITS>(u.qm, e, nv);
+                in.cv = load_codes_part<BITS>(u.qv, e, nv);
+                if (ADE) in.cm2 = load_codes_part<BITS>(u.qm2, e, nv);
+            }
         }
     }
 }
 
 // ADE: AdEMAMix's third state m2 (signed map) and update
 // p <- p (1 - lr wd) - lr (m/bc1 + alpha m2) / h.
-template <int GK, int BITS, int BLOCK, bool ADE, bool FULL>
+template <int GK, int BITS, int BLOCK, bool ADE, bool FULL, bool IL>
 __device__ __forceinline__ void step_row(const UnitPtrs &u, const AdamK &k, uint32_t e, int nv,
                                          RowIn<lane_elems(BLOCK)> &in, const LdsMap<BITS - 1> &Mm,
                                          const LdsMap<BITS> &Mv) {
@@ -307,31 +399,44 @@ __device__ __forceinline__ void step_row(const UnitPtrs &u, const AdamK &k, uint
     if (ADE) om2 = quantize_lane<BITS, true, E, L>(m2n, Mm, am22);
     if (FULL) {
         stf<E, LAY>(u.p, e, in.p);
-        store_codes_full<BITS, E>(u.qm, e, om);
-        store_codes_full<BITS, E>(u.qv, e, ov);
-        if (ADE) store_codes_full<BITS, E>(u.qm2, e, om2);
+        if constexpr (IL) {
+            store_il_full<BITS, E>(u.qm, e, join_il<BITS, E>(om, ov));
+        } else {
+            store_codes_full<BITS, E>(u.qm, e, om);
+            store_codes_full<BITS, E>(u.qv, e, ov);
+            if (ADE) store_codes_full<BITS, E>(u.qm2, e, om2);
+        }
     } else if (nv > 0) {
 #pragma unroll
         for (int j = 0; j < E; ++j) {
             const float pj[1] = {in.p[j]};
             if (j < nv) stf<1>(u.p, e + j, pj);
         }
-        store_codes_part<BITS>(u.qm, e, nv, om);
-        store_codes_part<BITS>(u.qv, e, nv, ov);
-        if (ADE) store_codes_part<BITS>(u.qm2, e, nv, om2);
+        if constexpr (IL) {
+            store_il_part<BITS>(u.qm, e, nv, join_il<BITS, E>(om, ov));
+        } else {
+            store_codes_part<BITS>(u.qm, e, nv, om);
+            store_codes_part<BITS>(u.qv, e, nv, ov);
+            if (ADE) store_codes_part<BITS>(u.qm2, e, nv, om2);
+        }
     }
     // every lane of a block holds the block's absmax: all of them store it
     // (one line per wave instruction, no branch around the store)
     if (FULL || nv > 0) {
         const uint32_t blk = e / BLOCK;
-        gp(u.am)[blk] = am2;
-        gp(u.av)[blk] = av2;
-        if (ADE) gp(u.am2)[blk] = am22;
+        if constexpr (IL) {
+            gp(reinterpret_cast<u32x2 *>(u.am))[blk] = u32x2{__float_as_uint(am2), __float_as_uint(av2)};
+        } else {
+            gp(u.am)[blk] = am2;
+            gp(u.av)[blk] = av2;
+            if (ADE) gp(u.am2)[blk] = am22;
+        }
     }
 }
 
-template <int GK, int BITS, int BLOCK, bool ADE>
+template <int GK, int BITS, int BLOCK, bool ADE, bool IL>
 __global__ __launch_bounds__(kThreads) void blockwise_kernel(StepArgs a) {
+    static_assert(!(ADE && IL), "the interleaved layout holds two states");
     constexpr int E = lane_elems(BLOCK);
     constexpr uint32_t kRow = (uint32_t)kThreads * E;
     __shared__ LdsMap<BITS - 1> Mm;
@@ -345,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void blockwise_kernel(StepArgs a) {
     const AdamK k = adam_consts(S);
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len64) {
         const TensorDesc &T = a.tensors[sp.tensor];
-        const UnitPtrs u = unit_ptrs<GK, BITS, BLOCK, ADE>(T, start, uniform(S.lrwd[T.group]));
+        const UnitPtrs u = unit_ptrs<GK, BITS, BLOCK, ADE, IL>(T, start, uniform(S.lrwd[T.group]));
         const uint32_t len = (uint32_t)len64;  // <= tile <= 2^24
         const uint32_t lane0 = threadIdx.x * E;
         // full rows, software-pipelined: the loads of the next rows are in
@@ -355,10 +460,10 @@ __global__ __launch_bounds__(kThreads) void blockwise_kernel(StepArgs a) {
         // registers would cost occupancy
         const uint32_t nfull = T.vec_ok ? len / kRow : 0;
         const auto load_at = [&](uint32_t r, RowIn<E> &in) {
-            load_row<GK, BITS, BLOCK, ADE, true>(u, k, lane0 + r * kRow, E, in);
+            load_row<GK, BITS, BLOCK, ADE, true, IL>(u, k, lane0 + r * kRow, E, in);
         };
         const auto step_at = [&](uint32_t r, RowIn<E> &in) {
-            step_row<GK, BITS, BLOCK, ADE, true>(u, k, lane0 + r * kRow, E, in, Mm, Mv);
+            step_row<GK, BITS, BLOCK, ADE, true, IL>(u, k, lane0 + r * kRow, E, in, Mm, Mv);
         };
         uint32_t r = 0;
         if (!ADE && E == 4 && nfull > 1) {
@@ -389,8 +494,8 @@ __global__ __launch_bounds__(kThreads) void blockwise_kernel(StepArgs a) {
             const uint32_t rel = r0 + lane0;
             const int nv = rel + E <= len ? E : (rel < len ? (int)(len - rel) : 0);
             RowIn<E> in;
-            load_row<GK, BITS, BLOCK, ADE, false>(u, k, rel, nv, in);
-            step_row<GK, BITS, BLOCK, ADE, false>(u, k, rel, nv, in, Mm, Mv);
+            load_row<GK, BITS, BLOCK, ADE, false, IL>(u, k, rel, nv, in);
+            step_row<GK, BITS, BLOCK, ADE, false, IL>(u, k, rel, nv, in, Mm, Mv);
         }
     });
 }
@@ -491,14 +596,20 @@ int quant_grid(int64_t n, int E) {
 hipError_t launch_blockwise(const StepArgs &a, int gk, bool ademamix, hipStream_t s) {
     return with_block(a.bits, a.block, [&](auto bits, auto block) {
         constexpr int B = decltype(bits)::value, K = decltype(block)::value;
-        if (gk == G_F32 && !ademamix)
-            LAUNCH_PERSISTENT((blockwise_kernel<G_F32, B, K, false>), a, s);
+        const bool il = a.interleaved != 0;
+        if (ademamix && il) return hipErrorInvalidValue;
+        if (gk == G_F32 && !ademamix && il)
+            LAUNCH_PERSISTENT((blockwise_kernel<G_F32, B, K, false, true>), a, s);
+        else if (!ademamix && il)
+            LAUNCH_PERSISTENT((blockwise_kernel<G_BF16, B, K, false, true>), a, s);
+        else if (gk == G_F32 && !ademamix)
+            LAUNCH_PERSISTENT((blockwise_kernel<G_F32, B, K, false, false>), a, s);
         else if (!ademamix)
-            LAUNCH_PERSISTENT((blockwise_kernel<G_BF16, B, K, false>), a, s);
+            LAUNCH_PERSISTENT((blockwise_kernel<G_BF16, B, K, false, false>), a, s);
         else if (gk == G_F32)
-            LAUNCH_PERSISTENT((blockwise_kernel<G_F32, B, K, true>), a, s);
+            LAUNCH_PERSISTENT((blockwise_kernel<G_F32, B, K, true, false>), a, s);
         else
-            LAUNCH_PERSISTENT((blockwise_kernel<G_BF16, B, K, true>), a, s);
+            LAUNCH_PERSISTENT((blockwise_kernel<G_BF16, B, K, true, false>), a, s);
         return hipGetLastError();
     });
 }

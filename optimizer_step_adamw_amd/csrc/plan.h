@@ -30,9 +30,11 @@ constexpr int64_t kAdamMiniTile = 4096;   // also LAMB and the fp16 scaled-state
 // less of g is found there).
 constexpr int64_t kMiniSegmentBytes = (int64_t)384 << 20;
 // blockwise units, measured best on MI355X over 2^28 elements (4096-65536):
-// 2-state 8-bit 4096, 2-state 4-bit 8192, AdEMAMix 8-bit 8192, 4-bit 16384
+// 2-state 8192 (8-bit separate layout 770.9 us against 789.0 at 4096,
+// interleaved 738.9 against 766.3; 4-bit 641.5 / 638.4 us), AdEMAMix
+// 8-bit 8192, 4-bit 16384
 constexpr int64_t blockwise_tile(bool ademamix, int bits) {
-    return ademamix ? (bits == 8 ? 8192 : 16384) : (bits == 8 ? 4096 : 8192);
+    return ademamix ? (bits == 8 ? 8192 : 16384) : 8192;
 }
 // read-only scans (finite check, gradient norm): elements per workgroup;
 // measured on MI355X over a 1.1B bf16 gradient list: 8192 -> 5.3 TB/s,
@@ -177,6 +179,8 @@ struct StepArgs {
     int32_t nblocks;
     const Codebook *codebook;
     int32_t bits, block;
+    int32_t interleaved;      // blockwise 2-state: m and v codes (and absmax)
+                              // side by side in qm (absmax_m)
     float *found_inf;         // finite check output
     int32_t cus;              // compute units of the device
     int32_t grid_request;     // persistent workgroups (0 = see units_per_wg)

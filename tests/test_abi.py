@@ -139,6 +139,38 @@ def test_blockwise_validation(L):
         fake_list([n], **kw), osa.OPTIM_ALGO_BLOCKWISE, osa.optim_plan_opts(8, 256, 0, 0)))
 
 
+def test_blockwise_interleaved_layout_validation(L):
+    """Interleaved state: codes of m and v in qm (2 bytes an element at 8
+    bits, 1 at 4), (absmax m, absmax v) pairs in absmax_m; qv and absmax_v
+    absent; the 2-state blockwise step only."""
+    f = Fake()
+    n = 1000
+    il = lambda bits, block: osa.optim_plan_opts(bits, block, 0, 0, 0, 0, osa.OPTIM_LAYOUT_INTERLEAVED)
+    kw = lambda **o: {**dict(m=None, v=None, qm=[f(2 * n)], absmax_m=[f(64)]), **o}
+    for bits, block in ((8, 256), (8, 64), (4, 128), (4, 512)):
+        assert ws(fake_list([n], fake=f, **kw()), osa.OPTIM_ALGO_BLOCKWISE, il(bits, block)) > 0
+    # qv / absmax_v given, absmax only 4-byte aligned, codes overlapping the next tensor's
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, **kw(qv=[f(n)])), osa.OPTIM_ALGO_BLOCKWISE,
+                                              il(8, 256)))
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, **kw(absmax_v=[f(64)])),
+                                              osa.OPTIM_ALGO_BLOCKWISE, il(8, 256)))
+    expect_error(osa.OPTIM_EALIGN, lambda: ws(fake_list([n], fake=f, **kw(absmax_m=[f(64, misalign=4)])),
+                                              osa.OPTIM_ALGO_BLOCKWISE, il(8, 256)))
+    q = f(4 * n)
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(  # 8-bit codes take 2n bytes: q + n overlaps
+        fake_list([n, n], fake=f, m=None, v=None, qm=[q, q + n], absmax_m=[f(64), f(64)]),
+        osa.OPTIM_ALGO_BLOCKWISE, il(8, 256)))
+    assert ws(fake_list([n, n], fake=f, m=None, v=None, qm=[q, q + 2 * n], absmax_m=[f(64), f(64)]),
+              osa.OPTIM_ALGO_BLOCKWISE, il(8, 256)) > 0
+    # other algorithms, unknown layouts
+    expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(
+        fake_list([n], fake=f, **kw(qm2=[f(n)], absmax_m2=[f(64)])), osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX, il(8, 256)))
+    expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(fake_list([n], fake=f), osa.OPTIM_ALGO_ADAMW,
+                                                    osa.optim_plan_opts(0, 0, 0, 0, 0, 0, 1)))
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, **kw()), osa.OPTIM_ALGO_BLOCKWISE,
+                                              osa.optim_plan_opts(8, 256, 0, 0, 0, 0, 2)))
+
+
 def test_tile_bounds(L):
     """Work units are a power of two of at least one group of 4 elements per
     lane (1024); blockwise rows need 2048."""
