@@ -601,7 +601,9 @@ KERNEL_SOURCES = {  # kernel -> sources its device code comes from
     "adamw_fp32": ("device_common.h", "kernels_adam.hip"),
     "ademamix_fp32": ("device_common.h", "kernels_adam.hip"),
     "blockwise_8bit": ("device_common.h", "kernels_blockwise.hip"),
+    "blockwise_8bit_interleaved": ("device_common.h", "kernels_blockwise.hip"),
     "blockwise_4bit": ("device_common.h", "kernels_blockwise.hip"),
+    "blockwise_4bit_interleaved": ("device_common.h", "kernels_blockwise.hip"),
     "blockwise_ademamix_8bit": ("device_common.h", "kernels_blockwise.hip"),
     "blockwise_ademamix_4bit": ("device_common.h", "kernels_blockwise.hip"),
 }
