@@ -47,14 +47,24 @@ def _adam_like(algo, key):
     sizes = SIZES
     tw = []
     for _ in range(2):
-        if algo == "mini":
+        if algo in ("mini", "mini_segments"):
             names = [n for n, _ in MINI]
             msz = [s for _, s in MINI]
             kinds, hn, wds = osa.adam_mini_partition(names, msz, dim=64, n_heads=4, weight_decay=0.1)
             vlen = [s if k == osa.OPTIM_MINI_FULL_V else s // h for k, s, h in zip(kinds, msz, hn)]
             st = AdamState(_p0(msz, key), v_len=vlen)
-            plan = osa.Plan(st.tensor_list(wds, mini_kind=kinds, head_numel=hn), osa.OPTIM_ALGO_ADAM_MINI)
+            # mini_segments: every tensor its own segment (three launches each)
+            plan = osa.Plan(st.tensor_list(wds, mini_kind=kinds, head_numel=hn), osa.OPTIM_ALGO_ADAM_MINI,
+                            segment_bytes=1 if algo == "mini_segments" else 0)
             sizes = msz
+        elif algo == "blockwise8_interleaved":
+            st = QuantState(_p0(sizes, key), 8, 256)
+            st.qm = [torch.zeros(2 * n, dtype=torch.uint8, device=DEV) for n in sizes]
+            st.am = [torch.zeros(2 * ((n + 255) // 256), dtype=torch.float32, device=DEV) for n in sizes]
+            st.qv = st.av = None
+            tl = osa.TensorList(st.p, st.g, qm=st.qm, absmax_m=st.am, weight_decay=[0.01] * len(sizes))
+            plan = osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE, bits=8, block=256,
+                            state_layout=osa.OPTIM_LAYOUT_INTERLEAVED)
         elif algo in ("blockwise8", "blockwise4", "blockwise_ademamix8"):
             bits = 4 if algo == "blockwise4" else 8
             block = 128 if bits == 4 else 256
@@ -85,9 +95,9 @@ def _adam_like(algo, key):
     def step(st, plan, sc):
         hp = osa.optim_adamw_hp(0.9, 0.999, 1e-8)
         hpe = osa.optim_ademamix_hp(0.9, 0.999, 0.9999, 5.0, 1e-8)
-        if algo == "mini":
+        if algo in ("mini", "mini_segments"):
             osa.optim_step_adam_mini(plan.handle, hp, sc.lr, None, None, sc.step)
-        elif algo == "blockwise8":
+        elif algo in ("blockwise8", "blockwise8_interleaved"):
             osa.optim_step_8bit_blockwise(plan.handle, hp, 8, 256, sc.lr, None, None, sc.step)
         elif algo == "blockwise4":
             osa.optim_step_8bit_blockwise(plan.handle, hp, 4, 128, sc.lr, None, None, sc.step)
@@ -112,8 +122,8 @@ def _buffers(st):
     return out
 
 
-@pytest.mark.parametrize("algo", ["ademamix", "mini", "lion", "lamb", "blockwise8", "blockwise4",
-                                  "blockwise_ademamix8", "states16"])
+@pytest.mark.parametrize("algo", ["ademamix", "mini", "mini_segments", "lion", "lamb", "blockwise8", "blockwise4",
+                                  "blockwise_ademamix8", "blockwise8_interleaved", "states16"])
 def test_step_graph_replays_match_eager(algo):
     (eager, graph), sizes, step = _adam_like(algo, sum(map(ord, algo)))
     g = _capture(lambda: step(*graph))
