@@ -20,7 +20,7 @@ namespace {
 // non-temporal traffic: the ordinary-load sum costs what a non-temporal one
 // does (28.8 vs 27.6 us) and the update drops from 150.5 to 124.6 us; on the
 // Llama-7B-shaped list the step drops from 28.1 to 25.8 ms.
-constexpr int32_t kMiniSumUnitsPerWg = 4;
+constexpr int32_t kMiniSumUnitsPerWg = 2;
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -162,9 +162,9 @@ hipError_t launch_adam_mini(const StepArgs &args, int pk, int gk, const MiniSegm
         a.unit0 = sg.unit_begin;
         a.nunits = sg.unit_end;
         if (sg.block_end > sg.block_begin) {
-            // the read-only sum pass streams better with 4 consecutive units
-            // per workgroup (measured on MI355X: 2.8% off a whole step of a
-            // 536M-element list against one unit; 2 and 8 in between)
+            // the read-only sum pass streams better with 2 consecutive units
+            // per workgroup (measured on MI355X, segmented 7B list: 25.5 ms
+            // per step against 26.0 with 1, 25.8 with 4, 26.3 with 8 or 16)
             if (a.grid_request == 0) a.units_per_wg = kMiniSumUnitsPerWg;
             if (gk == G_F32)
                 LAUNCH_PERSISTENT((mini_sumsq_kernel<G_F32>), a, s);
