@@ -21,6 +21,10 @@ namespace {
 // does (28.8 vs 27.6 us) and the update drops from 150.5 to 124.6 us; on the
 // Llama-7B-shaped list the step drops from 28.1 to 25.8 ms.
 constexpr int32_t kMiniSumUnitsPerWg = 2;
+// groups of 4 elements per lane the block sums and the update load at once:
+// a whole 4096-element unit (measured on MI355X, segmented 7B list: 25.0 ms
+// per step against 25.4 with two groups at a time)
+constexpr int kMiniGroups = 4;
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -42,7 +46,7 @@ __global__ __launch_bounds__(kThreads) void mini_sumsq_kernel(StepArgs a) {
         if (sp.block < 0) return;  // full-v tensor: no shared block
         const TensorDesc &T = a.tensors[sp.tensor];
         float acc = 0.0f;
-        lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+        lane_walk<kMiniGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
             constexpr int N = decltype(n)::value;
             float g[N];
             load_g<GK, N, LAY>(T.g, e, s, g);
@@ -118,11 +122,11 @@ __global__ __launch_bounds__(kThreads) void mini_update_kernel(StepArgs a) {
         const TensorDesc &T = a.tensors[sp.tensor];
         const float lw = uniform(S.lrwd[T.group]);
         if (sp.block < 0) {
-            adam_unit<PK, GK, false>(T, start, len, k, lw);
+            adam_unit<PK, GK, false, kMiniGroups>(T, start, len, k, lw);
             return;
         }
         const float f = a.blockfac[sp.block];
-        lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+        lane_walk<kMiniGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
             mini_elems<PK, GK, decltype(n)::value>(T, e, k, lw, f);
         });
     });
