@@ -92,6 +92,11 @@ constexpr int64_t kLionEarlyUnits = 4096;
 // p) -> per-tensor factor lr |p|/|u| (fixed-order fp64 sums) -> update,
 // which recomputes u from the stored m, v and the untouched p with the same
 // fp32 operations.
+// groups of 4 elements per lane both passes load at once: a whole
+// 4096-element unit (measured on MI355X, 4096^2: 113.4 us per step against
+// 115.4 with two groups at a time)
+constexpr int kLambGroups = 4;
+
 __device__ __forceinline__ float lamb_u(float p, float m, float v, const AdamK &k, float wd) {
     const float h = sqrtf(v) * k.isb2 + k.eps;
     return (m * k.ibc1) / h + wd * p;
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void lamb_moments_kernel(StepArgs a) {
         const TensorDesc &T = a.tensors[sp.tensor];
         const float wd = uniform((float)a.prep.group_wd[T.group]);
         float sp2 = 0.0f, su2 = 0.0f;
-        lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+        lane_walk<kLambGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
             constexpr int N = decltype(n)::value;
             float p[N], g[N], m[N], v[N];
             load_p<PK, N, RL>(T, e, p);
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void lamb_update_kernel(StepArgs a) {
         const TensorDesc &T = a.tensors[sp.tensor];
         const float wd = uniform((float)a.prep.group_wd[T.group]);
         const float f = a.blockfac[sp.block];
-        lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
+        lane_walk<kLambGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
             constexpr int N = decltype(n)::value;
             float p[N], m[N], v[N];
             load_p<PK, N, RL>(T, e, p);
