@@ -184,11 +184,13 @@ def test_c3_llama1b_bf16_remainder_amp_cosine():
 
 
 # ------------------------------------------------------------------ C4
-@pytest.mark.parametrize("bits", [8, 4])
-def test_c4_blockwise_268M(bits):
+@pytest.mark.parametrize("bits,interleaved", [(8, False), (4, False), (8, True), (4, True)])
+def test_c4_blockwise_268M(bits, interleaved):
     """Fresh step: codes and absmax bit-exact on sampled blocks, p at the closed
     form; then 10 steps with codes still bit-exact; plus the discriminating
-    fresh step at lr=0.1, wd=0.1."""
+    fresh step at lr=0.1, wd=0.1.  Both state layouts (the interleaved one
+    keeps each element's m and v codes side by side, and each block's two
+    absmax values)."""
     wl = synth.c4_blockwise()
     n, hpw = wl.numel, wl.hp
     block = wl.extra["block8"] if bits == 8 else wl.extra["block4"]
@@ -200,7 +202,16 @@ def test_c4_blockwise_268M(bits):
     for lr, wd, steps in ((hpw.lr, hpw.wd, wl.steps), (0.1, 0.1, 1)):
         p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, DEV)
         qs = QuantState([p0], bits, block)
-        plan = osa.Plan(qs.tensor_list([wd]), osa.OPTIM_ALGO_BLOCKWISE, bits=bits, block=block)
+        if interleaved:
+            qs.qm = [torch.zeros(2 * n * bits // 8, dtype=torch.uint8, device=DEV)]
+            qs.am = [torch.zeros(2 * nblk, dtype=torch.float32, device=DEV)]
+            qs.qv = qs.av = None
+            _free()
+            tl = osa.TensorList(qs.p, qs.g, qm=qs.qm, absmax_m=qs.am, weight_decay=[wd])
+            plan = osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE, bits=bits, block=block,
+                            state_layout=osa.OPTIM_LAYOUT_INTERLEAVED)
+        else:
+            plan = osa.Plan(qs.tensor_list([wd]), osa.OPTIM_ALGO_BLOCKWISE, bits=bits, block=block)
         sc = DevScalars(lr)
         lr32 = float(np.float32(lr))
         p = p0[di].double().cpu().numpy()
@@ -216,9 +227,18 @@ def test_c4_blockwise_268M(bits):
             osa.optim_step_8bit_blockwise(plan.handle, hp, bits, block, sc.lr, None, None, sc.step)
             orc.blockwise_step(p, g, qm, qv, am, av, bits, block, lr32, hpw.beta1, hpw.beta2, hpw.eps, wd, t)
             bi = torch.from_numpy(blocks).to(DEV)
-            assert np.array_equal(qs.am[0][bi].cpu().numpy().view(np.uint32), am.view(np.uint32)), t
-            assert np.array_equal(qs.av[0][bi].cpu().numpy().view(np.uint32), av.view(np.uint32)), t
-            if bits == 8:
+            if interleaved:
+                gam, gav = qs.am[0][2 * bi].cpu().numpy(), qs.am[0][2 * bi + 1].cpu().numpy()
+            else:
+                gam, gav = qs.am[0][bi].cpu().numpy(), qs.av[0][bi].cpu().numpy()
+            assert np.array_equal(gam.view(np.uint32), am.view(np.uint32)), t
+            assert np.array_equal(gav.view(np.uint32), av.view(np.uint32)), t
+            if interleaved and bits == 8:
+                gm, gv = qs.qm[0][2 * di].cpu().numpy(), qs.qm[0][2 * di + 1].cpu().numpy()
+            elif interleaved:
+                b = qs.qm[0][di].cpu().numpy()
+                gm, gv = b & 0xF, b >> 4
+            elif bits == 8:
                 gm, gv = qs.qm[0][di].cpu().numpy(), qs.qv[0][di].cpu().numpy()
             else:
                 bytes_idx = torch.from_numpy(np.unique(eidx // 2)).to(DEV)
@@ -236,7 +256,8 @@ def test_c4_blockwise_268M(bits):
                 if lr == 0.1:
                     mutant = (p_init - lr32 * gd / (np.abs(gd) + hpw.eps)) * (1 - lr32 * wd)
                     assert np.max(np.abs(got - mutant)) > 0.9e-3
-        say(f"C4 {bits}-bit block {block} lr={lr}: {steps} steps, codes bit-exact, relerr_tau {err:.3e}")
+        say(f"C4 {bits}-bit block {block} interleaved={interleaved} lr={lr}: {steps} steps, codes bit-exact, "
+            f"relerr_tau {err:.3e}")
         del qs, plan
         _free()
 
