@@ -11,9 +11,11 @@ Secondary workloads (same JSON line, "secondary"): the 1M-element tensor,
 the Llama-shaped 1.1B bf16+remainder AMP list with device cosine lr (also
 timed as the full AMP loop with global-norm clipping folded into the step
 and the dynamic loss-scale update), the 268M-element blockwise 8-bit and
-4-bit states (2-state AdamW and 3-state AdEMAMix), Adam-mini over the 7B
-list, and Lion, LAMB and AdamW with an fp32 master and a bf16 / fp16 model
-copy on the 4096 x 4096 tensor.  Gradients are drawn once per workload, outside the timed region.
+4-bit states (2-state AdamW in both state layouts and 3-state AdEMAMix),
+Adam-mini over the 7B list, Lion, LAMB and AdamW with an fp32 master and a
+bf16 / fp16 model copy or with scaled 16-bit moments on the 4096 x 4096
+tensor, and the headline's AdamW elements as lists of 4096 and 65536
+tensors.  Gradients are drawn once per workload, outside the timed region.
 
 Timing: HIP events on the stream the library launches on (torch's current
 stream), one pair around every optimizer call inside the timed region; the
@@ -59,8 +61,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--secondary", default="c1,c3,c4,c5,lion_lamb,master,states16",
-                    help="comma list of secondary workloads (c1,c3,c4,c5,lion_lamb,master,states16) or 'none'")
+    ap.add_argument("--secondary", default="c1,c3,c4,c5,lion_lamb,master,states16,many",
+                    help="comma list of secondary workloads (c1,c3,c4,c5,lion_lamb,master,states16,many) "
+                         "or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
@@ -261,6 +264,35 @@ def bench_headline(torch, osa, synth, steps, warmup):
     pa.close()
     pb.close()
     return res
+
+
+def bench_many(torch, osa, synth, steps, warmup):
+    """The headline's 16,777,216 AdamW fp32 elements as one list of many
+    tensors (views of one allocation per array): 4096 tensors of 4096
+    elements, and 65536 tensors of 256 (each shorter than a work unit), next
+    to the single tensor -- the cost of the multi-tensor traversal."""
+    n = 1 << 24
+    out = {}
+    for count in (1, 4096, 65536):
+        size = n // count
+        P = torch.randn(n, device="cuda") * 0.02
+        G = torch.randn(n, device="cuda") * 1e-3
+        M = torch.zeros(n, device="cuda")
+        V = torch.zeros(n, device="cuda")
+        views = lambda x: [x[i * size:(i + 1) * size] for i in range(count)]
+        plan = osa.Plan(osa.TensorList(views(P), views(G), m=views(M), v=views(V),
+                                       weight_decay=[0.1] * count), osa.OPTIM_ALGO_ADAMW)
+        s = scalars(torch, 1e-3)
+        h = osa.optim_adamw_hp(0.9, 0.999, 1e-8)
+        ms = run_each(torch, lambda: osa.optim_step_adamw(plan.handle, h, s["lr"], None, None, s["step"]), steps)
+        plan.close()
+        out[f"tensors_{count}x{size}"] = dict(ms=ms, gbs=gbs(B_ADAMW_F32 * n, ms),
+                                              frac=gbs(B_ADAMW_F32 * n, ms) / PEAK_HBM_GBS)
+        del P, G, M, V
+        torch.cuda.empty_cache()
+    return dict(workload="adamw_fp32_16M_as_many_tensors", elements=n, lists=out,
+                note="kernel ms: the same call run back to back on one state (a 448 MB working set "
+                     "partly held by the Infinity Cache between calls)")
 
 
 def bench_lion_lamb(torch, osa, synth, steps, warmup):
@@ -673,7 +705,7 @@ def main():
     secondary = {}
     todo = [] if args.secondary == "none" else args.secondary.split(",")
     fns = dict(c1=bench_c1, c3=bench_c3, c4=bench_c4, c5=bench_c5, lion_lamb=bench_lion_lamb,
-               master=bench_master, states16=bench_states16)
+               master=bench_master, states16=bench_states16, many=bench_many)
     for key in todo:
         t0 = time.perf_counter()
         secondary[key] = fns[key](torch, osa, synth, args.steps, args.warmup)
