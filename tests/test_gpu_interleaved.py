@@ -28,10 +28,13 @@ def interleave(qm, qv, bits):
 
 
 class ILState:
-    def __init__(self, p0, bits, block):
+    def __init__(self, p0, bits, block, code_offset=0):
         self.p = [torch.from_numpy(x).to(DEV) for x in p0]
         self.g = [torch.zeros_like(x) for x in self.p]
-        self.q = [torch.zeros(x.size * 2 * bits // 8, dtype=torch.uint8, device=DEV) for x in p0]
+        # code_offset > 0: codes start that many bytes past a 16-byte boundary,
+        # so every row takes the byte-wise path
+        self.q = [torch.zeros(x.size * 2 * bits // 8 + code_offset, dtype=torch.uint8, device=DEV)[code_offset:]
+                  for x in p0]
         self.a = [torch.zeros(2 * ((x.size + block - 1) // block), dtype=torch.float32, device=DEV) for x in p0]
 
     def plan(self, bits, block, wd, grad_bf16=False, tile=0):
@@ -41,12 +44,13 @@ class ILState:
                         state_layout=osa.OPTIM_LAYOUT_INTERLEAVED)
 
 
-@pytest.mark.parametrize("bits,block,tile", [(8, 256, 0), (4, 128, 0), (8, 64, 0), (4, 512, 0), (8, 256, 2048),
-                                             (4, 128, 16384)])
-def test_interleaved_codes_bit_exact(bits, block, tile):
+@pytest.mark.parametrize("bits,block,tile,code_offset", [(8, 256, 0, 0), (4, 128, 0, 0), (8, 64, 0, 0),
+                                                         (4, 512, 0, 0), (8, 256, 2048, 0), (4, 128, 16384, 0),
+                                                         (8, 256, 0, 3), (4, 512, 0, 5)])
+def test_interleaved_codes_bit_exact(bits, block, tile, code_offset):
     lr, wd = 1e-3, 0.01
     p0 = [host_normal(n, 0.02, 940, bits, block, i) for i, n in enumerate(SIZES)]
-    st = ILState(p0, bits, block)
+    st = ILState(p0, bits, block, code_offset)
     plan = st.plan(bits, block, [wd] * len(SIZES), tile=tile)
     sc = DevScalars(lr)
     lr32 = float(np.float32(lr))
@@ -73,7 +77,8 @@ def test_interleaved_codes_bit_exact(bits, block, tile):
             err = relerr_tau(st.p[i].cpu().numpy(), op[i], lr32)
             assert err <= (TOL_STEP1 if t == 1 else TOL_RUN), (t, i, err)
     assert int(sc.step.item()) == 8
-    say(f"interleaved bits={bits} block={block} tile={tile}: codes and absmax bit-exact over 8 steps")
+    say(f"interleaved bits={bits} block={block} tile={tile} code_offset={code_offset}: codes and absmax "
+        "bit-exact over 8 steps")
 
 
 @pytest.mark.parametrize("bits,block", [(8, 256), (4, 128)])
