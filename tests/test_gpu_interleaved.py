@@ -37,21 +37,22 @@ class ILState:
                   for x in p0]
         self.a = [torch.zeros(2 * ((x.size + block - 1) // block), dtype=torch.float32, device=DEV) for x in p0]
 
-    def plan(self, bits, block, wd, grad_bf16=False, tile=0):
+    def plan(self, bits, block, wd, grad_bf16=False, tile=0, grid=0):
         tl = osa.TensorList(self.p, self.g, qm=self.q, absmax_m=self.a, weight_decay=wd,
                             grad_dtype=osa.OPTIM_BF16 if grad_bf16 else osa.OPTIM_F32)
-        return osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE, bits=bits, block=block, tile=tile,
+        return osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE, bits=bits, block=block, tile=tile, grid=grid,
                         state_layout=osa.OPTIM_LAYOUT_INTERLEAVED)
 
 
-@pytest.mark.parametrize("bits,block,tile,code_offset", [(8, 256, 0, 0), (4, 128, 0, 0), (8, 64, 0, 0),
-                                                         (4, 512, 0, 0), (8, 256, 2048, 0), (4, 128, 16384, 0),
-                                                         (8, 256, 0, 3), (4, 512, 0, 5)])
-def test_interleaved_codes_bit_exact(bits, block, tile, code_offset):
+@pytest.mark.parametrize("bits,block,tile,code_offset,grid", [(8, 256, 0, 0, 0), (4, 128, 0, 0, 0), (8, 64, 0, 0, 0),
+                                                              (4, 512, 0, 0, 0), (8, 256, 2048, 0, 0),
+                                                              (4, 128, 16384, 0, 0), (8, 256, 0, 3, 0),
+                                                              (4, 512, 0, 5, 0), (8, 256, 2048, 0, 7)])
+def test_interleaved_codes_bit_exact(bits, block, tile, code_offset, grid):
     lr, wd = 1e-3, 0.01
     p0 = [host_normal(n, 0.02, 940, bits, block, i) for i, n in enumerate(SIZES)]
     st = ILState(p0, bits, block, code_offset)
-    plan = st.plan(bits, block, [wd] * len(SIZES), tile=tile)
+    plan = st.plan(bits, block, [wd] * len(SIZES), tile=tile, grid=grid)
     sc = DevScalars(lr)
     lr32 = float(np.float32(lr))
     op = [x.astype(np.float64) for x in p0]

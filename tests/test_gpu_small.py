@@ -175,7 +175,7 @@ MINI_LIST = [("tok_embeddings.weight", 37 * 64), ("layers.0.attention.wq.weight"
 
 
 def _mini_run(steps, key, grad_bf16=False, lr=3e-4, wd=0.1, dim=64, heads=4, items=MINI_LIST, tile=0,
-              segment_bytes=0):
+              segment_bytes=0, grid=0):
     names = [n for n, _ in items]
     sizes = [s for _, s in items]
     kinds, hn, wds = osa.adam_mini_partition(names, sizes, dim=dim, n_heads=heads, weight_decay=wd)
@@ -183,7 +183,7 @@ def _mini_run(steps, key, grad_bf16=False, lr=3e-4, wd=0.1, dim=64, heads=4, ite
     p0 = _p0(sizes, key)
     st = AdamState(_to_dev(p0), grad_bf16=grad_bf16, v_len=vlen)
     plan = osa.Plan(st.tensor_list(wds, mini_kind=kinds, head_numel=hn), osa.OPTIM_ALGO_ADAM_MINI, tile=tile,
-                    segment_bytes=segment_bytes)
+                    segment_bytes=segment_bytes, grid=grid)
     sc = DevScalars(lr)
     lr32 = float(np.float32(lr))
     # oracle side: its own partition by name
@@ -246,15 +246,16 @@ def test_adam_mini_deterministic():
     assert all_equal(a.buffers(), b.buffers())
 
 
-@pytest.mark.parametrize("segment_bytes", [1, 20000])
-def test_adam_mini_segments_match_one_segment(segment_bytes):
+@pytest.mark.parametrize("segment_bytes,grid", [(1, 0), (20000, 0), (20000, 5)])
+def test_adam_mini_segments_match_one_segment(segment_bytes, grid):
     """The step runs its block-sum, finalize and update kernels per segment
     (consecutive shared-v tensors up to segment_bytes of gradient, a larger
     tensor alone; full-v tensors apart).  Every tensor alone (1 byte) and
     1-2 tensors per segment (20000 bytes: the norm joins the next q block)
     give the bits of a single segment over the list, and the oracle's
-    values within the bounds."""
-    a = _mini_run(4, 7, segment_bytes=segment_bytes)
+    values within the bounds; also with a persistent grid of 5 workgroups
+    walking each segment's units."""
+    a = _mini_run(4, 7, segment_bytes=segment_bytes, grid=grid)
     b = _mini_run(4, 7, segment_bytes=1 << 40)
     assert all_equal(a.buffers(), b.buffers())
 
