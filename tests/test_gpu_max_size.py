@@ -142,3 +142,59 @@ def test_blockwise_past_2g(bits, n):
     say(f"blockwise {bits}-bit n={n}: {blocks.size} sampled blocks bit-exact, relerr_tau {err:.2e}")
     del qs, plan
     _free()
+
+
+@pytest.mark.parametrize("bits,n", [(8, (1 << 30) + 512 + 100), (4, (1 << 31) + 300)])
+def test_blockwise_interleaved_past_2g(bits, n):
+    """Interleaved layout (each element's m and v codes side by side, the two
+    absmax values of a block side by side): 8-bit takes 2 code bytes per
+    element and 4-bit 1, so both tensors put code byte offsets past 2^31.
+    Codes and absmax bit-exact on the windows (whole blocks), p within the
+    step bounds, over two steps."""
+    block = 256 if bits == 8 else 128
+    nblk = (n + block - 1) // block
+    p = synth.device_normal(n, 0.02, DEV, 993, bits)
+    g = torch.empty_like(p)
+    q = torch.zeros(n * bits // 4, dtype=torch.uint8, device=DEV)
+    a = torch.zeros(2 * nblk, dtype=torch.float32, device=DEV)
+    plan = osa.Plan(osa.TensorList([p], [g], qm=[q], absmax_m=[a], weight_decay=[0.01]), osa.OPTIM_ALGO_BLOCKWISE,
+                    bits=bits, block=block, state_layout=osa.OPTIM_LAYOUT_INTERLEAVED)
+    sc = DevScalars(1e-3)
+    lr32 = float(np.float32(1e-3))
+    idx = _windows(n, block, 20 + bits, w=2048)
+    blocks = np.unique(idx // block)
+    idx = np.concatenate([np.arange(b * block, min((b + 1) * block, n)) for b in blocks])
+    di = torch.from_numpy(idx).to(DEV)
+    op = p[di].double().cpu().numpy()
+    k = idx.size
+    qm, qv = np.zeros(k, np.uint8), np.zeros(k, np.uint8)
+    am, av = np.zeros(blocks.size, np.float32), np.zeros(blocks.size, np.float32)
+    pad = (-k) % block
+    if bits == 8:
+        code_idx = torch.from_numpy(np.stack([2 * idx, 2 * idx + 1], axis=1).ravel()).to(DEV)
+    else:
+        code_idx = di
+    amax_idx = torch.from_numpy(np.stack([2 * blocks, 2 * blocks + 1], axis=1).ravel()).to(DEV)
+    for t in (1, 2):
+        g.copy_(synth.device_normal(n, 1e-3, DEV, 993, 10 + bits, t))
+        osa.optim_step_8bit_blockwise(plan.handle, HP, bits, block, sc.lr, None, None, sc.step)
+        gw = g[di].cpu().numpy()
+        pp = np.concatenate([op, np.zeros(pad)])
+        gg = np.concatenate([gw, np.zeros(pad, np.float32)])
+        qmp, qvp = np.concatenate([qm, np.zeros(pad, np.uint8)]), np.concatenate([qv, np.zeros(pad, np.uint8)])
+        orc.blockwise_step(pp, gg, qmp, qvp, am, av, bits, block, lr32, 0.9, 0.999, 1e-8, 0.01, t)
+        op, qm, qv = pp[:k], qmp[:k], qvp[:k]
+        want_a = np.stack([am, av], axis=1).ravel().view(np.uint32)
+        assert np.array_equal(a[amax_idx].cpu().numpy().view(np.uint32), want_a), t
+        got = q[code_idx].cpu().numpy()
+        if bits == 8:
+            gm, gv = got[0::2], got[1::2]
+        else:
+            gm, gv = got & 0xF, got >> 4
+        assert np.array_equal(gm, qm), (t, int(np.sum(gm != qm)))
+        assert np.array_equal(gv, qv), (t, int(np.sum(gv != qv)))
+        err = relerr_tau(p[di].cpu().numpy(), op, lr32)
+        assert err <= (TOL_STEP1 if t == 1 else TOL_RUN), (t, err)
+    say(f"blockwise {bits}-bit interleaved n={n}: {blocks.size} sampled blocks bit-exact, relerr_tau {err:.2e}")
+    del p, g, q, a, plan
+    _free()
