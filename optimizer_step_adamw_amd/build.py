@@ -27,19 +27,36 @@ def hipcc() -> str:
     return "hipcc"
 
 
+def _flags():
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+            "-fno-gpu-flush-denormals-to-zero",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wall", "-Wno-unused-command-line-argument",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+
+
 def build(verbose: bool = False) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
-           "-fno-gpu-flush-denormals-to-zero",
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-Wno-unused-command-line-argument",
-           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           "-o", tmp] + SOURCES
+    """Compiles every source to an object (in parallel), then links the
+    shared library; always recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
+    obj_dir = os.path.join(LIB_DIR, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    objs = [os.path.join(obj_dir, os.path.basename(src) + ".o") for src in SOURCES]
+    cmds = [[hipcc()] + _flags() + ["-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    jobs = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(jobs) as ex:
+        for c, rc in zip(cmds, ex.map(lambda c: subprocess.call(c), cmds)):
+            if rc != 0:
+                raise subprocess.CalledProcessError(rc, c)
+    tmp = LIB_PATH + ".tmp"
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(link), flush=True)
+    subprocess.check_call(link)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 
