@@ -341,14 +341,16 @@ int optim_check_finite(optim_plan *plan, float *found_inf_dev, void *stream);
  * that unscales inside must not receive already-unscaled gradients).  One
  * read of every gradient of the plan: as optim_check_finite it ORs 1.0f
  * into *found_inf_dev on a NaN / +-Inf, and it sums G^2 (the stored, scaled
- * gradients; fp32 per lane, fp64 per workgroup and across workgroups in a
- * fixed order).  Then, with s = *inv_scale_dev (NULL: 1):
+ * gradients; each square exact in fp64, summed in fp64 per lane, per
+ * workgroup and across workgroups in a fixed order, so a finite gradient
+ * list always has a finite norm).  Then, with s = *inv_scale_dev (NULL: 1):
  *   *norm_dev           = sqrt(sum G^2) * s, the global L2 norm of the
  *                         unscaled gradients (norm_dev may be NULL);
  *   *clip_inv_scale_dev = s * min(1, max_norm / (norm + 1e-6)),
  * to be passed as the inv_scale of the step that follows.  max_norm <= 0
- * or +inf means no clipping (clip = s); NaN is EINVAL.  When the norm is
- * not finite, clip = s (found_inf is set and the step skips).  Uses the
+ * or +inf means no clipping (clip = s); NaN is EINVAL.  The norm is not
+ * finite only when an element is NaN / +-Inf: then clip = s, found_inf is
+ * set and the step skips.  Uses the
  * plan's workspace (partial sums): do not overlap it with a step of the
  * same plan on another stream.                                             */
 int optim_grad_norm(optim_plan *plan, const float *inv_scale_dev,

@@ -11,10 +11,14 @@ namespace {
 // consecutive units, merged into one walk where they are contiguous).
 // Measured on MI355X: bf16 gradients stream best with 8 groups of 4 per lane
 // in flight (7.4 TB/s), fp32 with one group at a time (7.0 TB/s).
-// NORM: the same pass also sums the squares of the (scaled) gradients, per
-// lane in fp32 and per workgroup in fp64, into partials[workgroup].
+// NORM: the same pass also sums the squares of the (scaled) gradients in
+// fp64, per lane and per workgroup, into partials[workgroup].  The square of
+// an fp32 or bf16 value is exact in fp64 and cannot overflow there, so a
+// large but finite loss-scaled gradient (|G| above ~1.8e19, whose fp32 square
+// is +inf) still gives a finite norm and is clipped; only a NaN / Inf
+// element, which sets found_inf, makes the norm non-finite.
 template <int GK, bool NORM>
-__device__ __forceinline__ bool scan_grads(const TensorDesc &T, int64_t start, int64_t len, float &acc) {
+__device__ __forceinline__ bool scan_grads(const TensorDesc &T, int64_t start, int64_t len, double &acc) {
     constexpr int G = GK == G_F32 ? 1 : 8;
     bool bad = false;
     lane_walk<G>(start, len, T.vec_ok, [&](auto n, int64_t e) {
@@ -35,7 +39,7 @@ __device__ __forceinline__ bool scan_grads(const TensorDesc &T, int64_t start, i
         }
         if constexpr (NORM) {
 #pragma unroll
-            for (int i = 0; i < N; ++i) acc += x[i] * x[i];
+            for (int i = 0; i < N; ++i) acc = __builtin_fma((double)x[i], (double)x[i], acc);
         }
     });
     return bad;
@@ -44,7 +48,7 @@ __device__ __forceinline__ bool scan_grads(const TensorDesc &T, int64_t start, i
 template <int GK, bool NORM>
 __global__ __launch_bounds__(kThreads) void finite_kernel(StepArgs a) {
     bool bad = false;
-    float acc = 0.0f;
+    double acc = 0.0;
     int tensor = -1;
     int64_t start = 0, len = 0;
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t s, int64_t l) {
@@ -63,7 +67,7 @@ __global__ __launch_bounds__(kThreads) void finite_kernel(StepArgs a) {
         __shared__ double red[kThreads / 64];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = (double)acc;
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
         __syncthreads();
         if (threadIdx.x == 0) {
             double t = 0.0;

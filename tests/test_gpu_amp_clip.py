@@ -14,7 +14,7 @@ from synth import host_normal
 pytestmark = pytest.mark.gpu
 
 RAGGED = [1, 7, 8, 9, 4095, 4096, 4097, 10007, 65539]
-NORM_RTOL = 1e-6  # fp32 sums of squares per lane, fp64 beyond: ~1e-7 relative
+NORM_RTOL = 1e-6  # fp64 sums of exact squares, rounded once to fp32: ~6e-8 relative
 
 
 def _scalars():
@@ -71,6 +71,49 @@ def test_grad_norm_and_clip_match_oracle(bf16, grid):
     assert abs(norm.item() - orc.grad_norm(G)) <= NORM_RTOL * orc.grad_norm(G)
     assert clip.item() == 1.0
     say(f"bf16={bf16} grid={grid}: norm {norm_o:.6e} matches")
+
+
+@pytest.mark.parametrize("bf16", [True, False])
+def test_grad_norm_large_finite_gradients_clip(bf16):
+    """Loss-scaled gradients whose squares overflow fp32 (|G| ~ 1e25, every
+    element finite): the norm stays finite and matches the oracle's fp64
+    norm, found_inf stays 0 and the clip factor follows oracle_clip_coef, as
+    unscale-then-clip would ([LTN] analysis: clipping is why unscale_ runs
+    before step).  Then the clipped step runs (it is not skipped)."""
+    sizes = [4097, 65539, 9]
+    p0 = [host_normal(n, 0.02, 921, 0, i, 0) for i, n in enumerate(sizes)]
+    st = AdamState([torch.from_numpy(x).to(DEV) for x in p0], grad_bf16=bf16)
+    plan = osa.Plan(st.tensor_list([0.1] * len(sizes)), osa.OPTIM_ALGO_ADAMW)
+    scale = 2.0 ** 100  # stored |G| ~ 1e-3 * 2^100 ~ 1.3e27: G^2 ~ 1e54 > fp32 max
+    inv = torch.tensor([2.0 ** -100], device=DEV)
+    G = _scaled_grads(st, sizes, 7, 1, scale)
+    assert all(np.all(np.isfinite(g)) for g in G) and max(np.max(np.abs(g)) for g in G) > 1.9e19
+    norm_o = orc.grad_norm(G, 2.0 ** -100)
+    fi, norm, clip = _scalars()
+    max_norm = 0.25 * norm_o
+    osa.optim_grad_norm(plan.handle, inv, max_norm, fi, norm, clip)
+    assert fi.item() == 0.0
+    assert np.isfinite(norm.item()) and abs(norm.item() - norm_o) <= NORM_RTOL * norm_o, (norm.item(), norm_o)
+    want = 2.0 ** -100 * orc.clip_coef(norm_o, max_norm)
+    assert abs(clip.item() - want) <= NORM_RTOL * want, (clip.item(), want)
+    # the clipped step: found_inf 0, the step counter advances, p moves as
+    # the oracle's step on the clipped, unscaled gradient
+    lr = torch.tensor([1e-3], device=DEV)
+    step = torch.zeros(1, dtype=torch.int32, device=DEV)
+    hp = osa.optim_adamw_hp(0.9, 0.999, 1e-8)
+    osa.optim_step_adamw(plan.handle, hp, lr, clip, fi, step)
+    torch.cuda.synchronize()
+    assert int(step.item()) == 1
+    c = float(clip.item())
+    lr32 = float(np.float32(1e-3))
+    for i, n in enumerate(sizes):
+        po, mo, vo = p0[i].astype(np.float64), np.zeros(n), np.zeros(n)
+        # the step multiplies G by the fp32 clip factor, rounding g to fp32
+        g = (G[i].astype(np.float32) * np.float32(c)).astype(np.float64)
+        orc.adamw_step(po, mo, vo, g, lr32, 0.9, 0.999, 1e-8, 0.1, 1)
+        assert relerr_tau(st.p[i].cpu().numpy(), po, lr32) <= TOL_STEP1
+    say(f"bf16={bf16}: norm {norm_o:.6e} of gradients up to {max(np.max(np.abs(g)) for g in G):.3e} "
+        f"clipped by {orc.clip_coef(norm_o, max_norm):.3f}")
 
 
 def test_grad_norm_agrees_with_finite_check():
