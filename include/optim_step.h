@@ -18,8 +18,9 @@
  *  - "dev" pointers are device (HBM) pointers owned by the caller; "host"
  *    pointers are host memory owned by the caller.  The library allocates no
  *    device memory: plan metadata, per-step scalars and reduction partials
- *    live in a caller-owned workspace.  The only host allocation is the plan
- *    object itself.
+ *    live in a caller-owned workspace (or, for optim_plan_create_static, in
+ *    the library's static device workspace).  The only host allocation is
+ *    the plan object itself.
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
  *    device-side effect is enqueued on it, in order; nothing reads device
  *    memory back to the host, so a whole step can be captured in a HIP graph.
@@ -203,6 +204,31 @@ int optim_plan_create(const optim_tensor_list *list, int32_t algo,
 
 /* Frees the host plan object.  Work already enqueued is unaffected.      */
 int optim_plan_destroy(optim_plan *plan);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * plan as optim_plan_create, built on a workspace the library holds in
+ * static device memory -- OPTIM_STATIC_WORKSPACE_BYTES per device, held by
+ * every device the library runs on until the process ends -- instead of a
+ * caller buffer.  It calls no device allocator (the host plan object is
+ * malloc'd as with optim_plan_create; free it with optim_plan_destroy).
+ * A plan needing more workspace than that (Adam-mini lists of more than
+ * ~8.5 billion elements, LAMB lists of more than ~4.2 billion, lists of more
+ * than ~90,000 tensors) is refused with OPTIM_EWORKSPACE before anything is
+ * touched.
+ * One static workspace per device, shared by every call on that device: a
+ * call overwrites the tables of the previous static plan of the current
+ * device, which from then on fails (OPTIM_EINVAL) in every entry point.
+ * Creating a static plan while a step of the previous one may still run on
+ * the device (another stream, not yet synchronised) races with that step;
+ * so do steps of one static plan that overlap each other.  The commit
+ * counters (and the maxima slots of fp16 states) are cleared by the call.
+ * Validation, stream semantics and errors as optim_plan_create; the device
+ * is the current one.                                                      */
+#define OPTIM_STATIC_WORKSPACE_BYTES ((size_t)16 << 20)
+int optim_plan_create_static(const optim_tensor_list *list, int32_t algo,
+                             const optim_plan_opts *opts, void *stream,
+                             optim_plan **out);
 
 /* Device learning-rate schedule ([AO]: the lr changes every step and must
  * stay a device scalar updated in place, with no per-step allocation).

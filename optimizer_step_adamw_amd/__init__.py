@@ -31,7 +31,10 @@ EXPORTED = (
     "optim_remainder_reconstruct", "optim_quant_codebook", "optim_quantize_blockwise",
     "optim_dequantize_blockwise", "optim_grad_norm", "optim_scaler_update",
     "optim_step_8bit_blockwise_ademamix", "optim_step_lion", "optim_step_lamb",
+    "optim_plan_create_static",
 )
+# bytes of the library's static per-device workspace (optim_plan_create_static)
+OPTIM_STATIC_WORKSPACE_BYTES = 16 << 20
 
 
 class OptimError(RuntimeError):
@@ -98,6 +101,7 @@ def lib() -> ctypes.CDLL:
             "optim_plan_workspace_size": ([tl, i32, opts, ctypes.POINTER(sz)], i32),
             "optim_plan_create": ([tl, i32, opts, _P, sz, _P, ctypes.POINTER(_P)], i32),
             "optim_plan_destroy": ([_P], i32),
+            "optim_plan_create_static": ([tl, i32, opts, _P, ctypes.POINTER(_P)], i32),
             "optim_plan_set_schedule": ([_P, i32, f64, f64, i32, _P], i32),
             "optim_step_adamw": ([_P, ctypes.POINTER(optim_adamw_hp), _P, _P, _P, _P, _P], i32),
             "optim_step_ademamix": ([_P, ctypes.POINTER(optim_ademamix_hp), _P, _P, _P, _P, _P], i32),
@@ -203,6 +207,14 @@ def optim_plan_create(tl: TensorList, algo: int, opts, workspace, nbytes: int, s
     _check(lib().optim_plan_create(ctypes.byref(tl.struct), algo, ctypes.byref(opts) if opts else None,
                                    _ptr(workspace), nbytes, _stream(stream), ctypes.byref(h)),
            "optim_plan_create")
+    return h.value
+
+
+def optim_plan_create_static(tl: TensorList, algo: int, opts, stream=None) -> int:
+    h = ctypes.c_void_p(0)
+    _check(lib().optim_plan_create_static(ctypes.byref(tl.struct), algo, ctypes.byref(opts) if opts else None,
+                                          _stream(stream), ctypes.byref(h)),
+           "optim_plan_create_static")
     return h.value
 
 

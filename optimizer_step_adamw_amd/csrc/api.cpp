@@ -6,8 +6,10 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -467,6 +469,10 @@ struct optim_plan {
     double lr_max, lr_min;
     int32_t K;
     int32_t *iter_dev;
+    // plans on the static workspace: the device and the creation number
+    // (0 for a plan on a caller's workspace)
+    int32_t static_dev;
+    uint64_t static_gen;
 };
 
 extern "C" {
@@ -490,18 +496,53 @@ int optim_plan_workspace_size(const optim_tensor_list *list, int32_t algo,
     return OPTIM_OK;
 }
 
-int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *opts,
-                      void *workspace, size_t workspace_bytes, void *stream, optim_plan **out) {
-    if (!out) return fail(OPTIM_EINVAL, "out is NULL");
-    *out = nullptr;
-    Built B;
-    int rc = build(list, algo, opts, B);
-    if (rc) return rc;
-    if (!workspace || !aligned(workspace, 256))
-        return fail(OPTIM_EWORKSPACE, "workspace must be a 256-byte aligned device pointer");
-    if (workspace_bytes < B.L.total)
-        return fail(OPTIM_EWORKSPACE, "workspace too small: need " + std::to_string(B.L.total) +
-                                          " bytes, got " + std::to_string(workspace_bytes));
+}  // extern "C"
+
+namespace {
+
+// ---------------------------------------------------------------- static workspace
+// The workspace of plans made by optim_plan_create_static, for callers that
+// cannot allocate device memory.  One array per device (each device that
+// loads the library holds its own copy at its own address until the process
+// ends).  In host code `scratch` is only a stand-in for the symbol: its
+// device address is looked up once per device with hipGetSymbolAddress and
+// kept in g_scratch_ptr, and only that address is ever handed to the device.
+__device__ __align__(256) unsigned char scratch[OPTIM_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+// creation number of the live static plan of each device; a plan made
+// earlier on the same device has been overwritten and is refused
+std::atomic<uint64_t> g_static_gen[kMaxDevices];
+
+int scratch_of_device(int dev, void **ptr) {
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(OPTIM_EUNSUPPORTED, "static workspace: device index " + std::to_string(dev) + " above 63");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        HIP_OK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p || !aligned(p, 256)) return fail(OPTIM_EHIP, "static workspace: no 256-byte aligned device address");
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return OPTIM_OK;
+}
+
+// Refuses a static plan whose tables a later optim_plan_create_static on the
+// same device has overwritten (its kernels would walk another plan's tables).
+int check_live(const optim_plan *P, const char *fn) {
+    if (P->static_gen && P->static_gen != g_static_gen[P->static_dev].load(std::memory_order_acquire))
+        return fail(OPTIM_EINVAL, std::string(fn) +
+                                      ": this static plan was superseded by a later optim_plan_create_static "
+                                      "on its device (the static workspace holds one plan at a time)");
+    return OPTIM_OK;
+}
+
+// Plan creation on a given workspace (the caller's, or the static one).
+int create_on(const Built &B, const optim_tensor_list *list, int32_t algo, const optim_plan_opts *opts,
+              void *workspace, hipStream_t s, int dev, optim_plan **out) {
     // host image of the table region [0, partials); with 16-bit states the
     // whole workspace, so the maxima slots start at zero
     std::vector<char> img(B.states16 ? B.L.total : B.L.partials, 0);
@@ -514,10 +555,8 @@ int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_p
         if (!build_map(7, cb->m8) || !build_map(8, cb->v8) || !build_map(3, cb->m4) || !build_map(4, cb->v4))
             return fail(OPTIM_EUNSUPPORTED, "quantization map does not fit the bucket table");
     }
-    int dev = 0, cus = 0;
-    HIP_OK(hipGetDevice(&dev));
+    int cus = 0;
     HIP_OK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-    hipStream_t s = static_cast<hipStream_t>(stream);
     HIP_OK(hipMemcpyAsync(workspace, img.data(), img.size(), hipMemcpyHostToDevice, s));
     HIP_OK(hipStreamSynchronize(s));
 
@@ -542,9 +581,58 @@ int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_p
     P->state_dtype = opts ? opts->state_dtype : OPTIM_F32;
     P->ws = static_cast<char *>(workspace);
     P->L = B.L;
-    P->segs = std::move(B.segs);
+    P->segs = B.segs;
     P->interleaved = B.interleaved ? 1 : 0;
     P->sched = OPTIM_SCHED_NONE;
+    P->static_dev = dev;
+    P->static_gen = 0;
+    *out = P;
+    return OPTIM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int optim_plan_create(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *opts,
+                      void *workspace, size_t workspace_bytes, void *stream, optim_plan **out) {
+    if (!out) return fail(OPTIM_EINVAL, "out is NULL");
+    *out = nullptr;
+    Built B;
+    int rc = build(list, algo, opts, B);
+    if (rc) return rc;
+    if (!workspace || !aligned(workspace, 256))
+        return fail(OPTIM_EWORKSPACE, "workspace must be a 256-byte aligned device pointer");
+    if (workspace_bytes < B.L.total)
+        return fail(OPTIM_EWORKSPACE, "workspace too small: need " + std::to_string(B.L.total) +
+                                          " bytes, got " + std::to_string(workspace_bytes));
+    int dev = 0;
+    HIP_OK(hipGetDevice(&dev));
+    return create_on(B, list, algo, opts, workspace, static_cast<hipStream_t>(stream), dev, out);
+}
+
+int optim_plan_create_static(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *opts,
+                             void *stream, optim_plan **out) {
+    if (!out) return fail(OPTIM_EINVAL, "out is NULL");
+    *out = nullptr;
+    Built B;
+    int rc = build(list, algo, opts, B);
+    if (rc) return rc;
+    if (B.L.total > (size_t)OPTIM_STATIC_WORKSPACE_BYTES)
+        return fail(OPTIM_EWORKSPACE, "optim_plan_create_static: the plan needs " + std::to_string(B.L.total) +
+                                          " bytes of workspace; the static workspace holds " +
+                                          std::to_string((size_t)OPTIM_STATIC_WORKSPACE_BYTES) +
+                                          " (use optim_plan_create with a caller workspace)");
+    int dev = 0;
+    HIP_OK(hipGetDevice(&dev));
+    void *ws = nullptr;
+    if ((rc = scratch_of_device(dev, &ws))) return rc;
+    // every earlier static plan of this device is superseded from here on,
+    // also if this creation fails after overwriting part of the tables
+    const uint64_t gen = g_static_gen[dev].fetch_add(1, std::memory_order_acq_rel) + 1;
+    optim_plan *P = nullptr;
+    if ((rc = create_on(B, list, algo, opts, ws, static_cast<hipStream_t>(stream), dev, &P))) return rc;
+    P->static_gen = gen;
     *out = P;
     return OPTIM_OK;
 }
@@ -635,14 +723,14 @@ int step_inputs(optim_plan *P, double b1, double b2, double b3, double alpha, do
 int check_plan(optim_plan *P, int32_t algo, const char *fn) {
     if (!P) return fail(OPTIM_EINVAL, std::string(fn) + ": plan is NULL");
     if (P->algo != algo) return fail(OPTIM_EINVAL, std::string(fn) + ": plan was built for another algorithm");
-    return OPTIM_OK;
+    return check_live(P, fn);
 }
 
 // the quantize / dequantize helpers take either blockwise plan
 int check_blockwise_plan(optim_plan *P, const char *fn) {
     if (!P) return fail(OPTIM_EINVAL, std::string(fn) + ": plan is NULL");
     if (!is_blockwise(P->algo)) return fail(OPTIM_EINVAL, std::string(fn) + ": plan is not blockwise");
-    return OPTIM_OK;
+    return check_live(P, fn);
 }
 
 int check_ademamix_hp(const optim_ademamix_hp *hp) {
@@ -771,6 +859,7 @@ int optim_step_8bit_blockwise_ademamix(optim_plan *plan, const optim_ademamix_hp
 
 int optim_check_finite(optim_plan *plan, float *found_inf_dev, void *stream) {
     if (!plan) return fail(OPTIM_EINVAL, "plan is NULL");
+    if (int rc = check_live(plan, "optim_check_finite")) return rc;
     if (!found_inf_dev || !aligned(found_inf_dev, 4))
         return fail(OPTIM_EINVAL, "found_inf_dev must be an aligned device float");
     if (plan->nunits == 0) return OPTIM_OK;
@@ -784,6 +873,7 @@ int optim_check_finite(optim_plan *plan, float *found_inf_dev, void *stream) {
 int optim_grad_norm(optim_plan *plan, const float *inv_scale_dev, double max_norm, float *found_inf_dev,
                     float *norm_dev, float *clip_inv_scale_dev, void *stream) {
     if (!plan) return fail(OPTIM_EINVAL, "plan is NULL");
+    if (int rc = check_live(plan, "optim_grad_norm")) return rc;
     if (!found_inf_dev || !aligned(found_inf_dev, 4))
         return fail(OPTIM_EINVAL, "found_inf_dev must be an aligned device float");
     if (!clip_inv_scale_dev || !aligned(clip_inv_scale_dev, 4))

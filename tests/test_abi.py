@@ -27,7 +27,7 @@ def header_functions():
 
 def test_exports_every_declared_function(L):
     declared = header_functions()
-    assert len(declared) == 20, declared
+    assert len(declared) == 21, declared
     assert sorted(osa.EXPORTED) == declared
     for name in declared:
         assert hasattr(L, name), name
@@ -310,3 +310,37 @@ def test_missing_library_raises_without_fallback():
             "    print('raised:', 'no fallback' in str(e))\n")
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120)
     assert "raised: True" in out.stdout, (out.stdout, out.stderr)
+
+
+def test_static_plan_refuses_oversize_and_invalid_lists_on_the_host(L):
+    """optim_plan_create_static validates and sizes the plan before it
+    touches any device: an invalid list and a plan larger than the static
+    workspace are refused with no device call (fake pointers, no GPU)."""
+    big = [1 << 34]  # Adam-mini SCALAR: one partial sum per 4096-element unit
+    tl = fake_list(big, mini_kind=[osa.OPTIM_MINI_SCALAR], head_numel=big)
+    need = ws(tl, osa.OPTIM_ALGO_ADAM_MINI)
+    assert need > osa.OPTIM_STATIC_WORKSPACE_BYTES
+    with pytest.raises(osa.OptimError) as ei:
+        osa.optim_plan_create_static(tl, osa.OPTIM_ALGO_ADAM_MINI, None, stream=0)
+    assert ei.value.code == osa.OPTIM_EWORKSPACE
+    assert str(need) in str(ei.value) and str(osa.OPTIM_STATIC_WORKSPACE_BYTES) in str(ei.value)
+    expect_error(osa.OPTIM_EINVAL, lambda: osa.optim_plan_create_static(
+        fake_list([4096], weight_decay=[-1.0]), osa.OPTIM_ALGO_ADAMW, None, stream=0))
+
+
+def test_static_workspace_holds_the_7b_adam_mini_plan(L):
+    """The static workspace is sized for the largest list of the benchmark
+    workloads: the Llama-7B-shaped Adam-mini plan (one partial sum per
+    4096-element unit) fits it."""
+    import synth
+    wl = synth.c5_adam_mini_7b()
+    names = [t.name for t in wl.tensors]
+    sizes = [t.numel for t in wl.tensors]
+    kinds, heads, wds = osa.adam_mini_partition(names, sizes, dim=4096, n_heads=32, weight_decay=0.1)
+    fake = Fake()
+    vlen = [n if k == osa.OPTIM_MINI_FULL_V else n // h for n, k, h in zip(sizes, kinds, heads)]
+    tl = osa.TensorList([fake(4 * n) for n in sizes], [fake(4 * n) for n in sizes],
+                        m=[fake(4 * n) for n in sizes], v=[fake(4 * k) for k in vlen], weight_decay=wds,
+                        mini_kind=kinds, head_numel=heads, numel=sizes)
+    need = ws(tl, osa.OPTIM_ALGO_ADAM_MINI)
+    assert 8 << 20 < need <= osa.OPTIM_STATIC_WORKSPACE_BYTES, need
