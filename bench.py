@@ -1,26 +1,35 @@
 """Benchmark of the fused AdamW-family optimizer step on one MI355X.
 
-Headline workload: one fp32 tensor of 4096 x 4096 elements stepped by AdamW
-(lr 0.1, wd 0.1) and by AdEMAMix (beta3 0.9999, alpha 5) on the same
-gradients, each optimizer with its own state.  One benchmark step = one
-AdamW step + one AdEMAMix step through the C ABI (every kernel of the path:
-per-step scalars, moments, bias correction, decay, update).  `value` is
-optimizer element-updates per second with all inputs resident in HBM.
+Headline workload: Adam-mini over the Llama-7B-shaped list (32 layers,
+d 4096, 32 heads, ffn 11008, vocab 32000, untied output: 291 fp32 tensors,
+6,738,415,616 parameters), the largest workload that fits one GPU.  One
+benchmark step = one optim_step_adam_mini call through the C ABI (per-step
+scalars, block sums of g^2, per-block finalize, m / p update, segment by
+segment).  `value` is optimizer element-updates per second with every input
+resident in HBM.
 
-Secondary workloads (same JSON line, "secondary"): the 1M-element tensor,
-the Llama-shaped 1.1B bf16+remainder AMP list with device cosine lr (also
-timed as the full AMP loop with global-norm clipping folded into the step
-and the dynamic loss-scale update), the 268M-element blockwise 8-bit and
-4-bit states (2-state AdamW in both state layouts and 3-state AdEMAMix),
-Adam-mini over the 7B list, Lion, LAMB and AdamW with an fp32 master and a
-bf16 / fp16 model copy or with scaled 16-bit moments on the 4096 x 4096
-tensor, and the headline's AdamW elements as lists of 4096 and 65536
-tensors.  Gradients are drawn once per workload, outside the timed region.
+Rooflines (`rooflines`, one entry per kernel; the headline's is `roofline`):
+the device duration of every launch, from the library's kernel trace (each
+launch's own start and end, recorded inside the timed region, on the stream
+the library launches on), against the kernel's algorithmic bytes per launch
+and MI355X's 8 TB/s:
+  - the Adam-mini update kernel (7B list);
+  - AdamW and AdEMAMix fp32 on 4096 x 4096 (four state sets taken in turn,
+    1.1 / 1.3 GB together, so no set is still in the 256 MB Infinity Cache
+    when its turn comes);
+  - the bf16 + int16-remainder AdamW kernel and the non-finite check on the
+    Llama-1.1B-shaped list;
+  - blockwise 8-bit (block 256) and 4-bit (block 128) on 268M elements.
+Each entry also carries `ceiling`: the bandwidth of the same access pattern
+streamed without arithmetic by a probe kernel (probes/stream_probe.hip; same
+arrays, lane layout, unit size and access kind), and `frac_of_ceiling`.
 
-Timing: HIP events on the stream the library launches on (torch's current
-stream), one pair around every optimizer call inside the timed region; the
-region itself is bracketed by device synchronisation.  Achieved bandwidth
-counts algorithmic bytes (what the method must read and write once).
+Secondary workloads (`secondary`): the 1M-element tensor, the 1.1B AMP loop
+with global-norm clipping and the dynamic loss scale, blockwise states in the
+interleaved layout and with AdEMAMix's third state, Lion, LAMB, fp32 masters
+with 16-bit model copies, scaled 16-bit moments, and 16M AdamW elements as
+lists of 4096 and 65536 tensors.  Gradients are drawn once per workload,
+outside the timed region.
 """
 from __future__ import annotations
 
@@ -45,11 +54,16 @@ B_LION_F32 = 20.0             # R p g m (12) + W p m (8)
 B_ADAMW_MASTER = 30.0         # R master g m v (16) + W master, 16-bit copy, m, v (14)
 B_ADAMW_STATES16 = 20.0       # R p g (8) + 16-bit m v (4); W p (4) + 16-bit m v (4)
 T_ADAMW_STATES16 = 28.0       # fp16: two passes, the second re-reads g, m, v (8)
-B_BF16R_AMP = 26.0 + 2.0      # R bf16 p, int16 r, bf16 g, m, v (14) + W (12); + finite check g
+B_BF16R = 26.0                # R bf16 p, int16 r, bf16 g, m, v (14) + W (12)
+B_FINITE_BF16 = 2.0           # R bf16 g
+B_MINI_SHARED = 20.0          # Adam-mini shared v: R p g m (12) + W p m (8)
+B_MINI_FULL = 28.0            # Adam-mini full v: as AdamW
+B_MINI_SUMS = 4.0             # block sums: R g
 B_8BIT = 4 + 4 + 1 + 1 + 8 / 256 + 4 + 1 + 1 + 8 / 256
 B_4BIT = 4 + 4 + 0.5 + 0.5 + 8 / 128 + 4 + 0.5 + 0.5 + 8 / 128
 CLIP_MAX_NORM = 1.0           # global-norm clip of the Llama 1.1B AMP loop
 C4_BETA3, C4_ALPHA = 0.9999, 5.0   # AdEMAMix on the blockwise list: the 4096^2 run's values
+ROTATE = 4                    # state sets taken in turn for the 4096^2 rooflines
 
 
 def log(*a):
@@ -61,50 +75,29 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--secondary", default="c1,c3,c4,c5,lion_lamb,master,states16,many",
-                    help="comma list of secondary workloads (c1,c3,c4,c5,lion_lamb,master,states16,many) "
-                         "or 'none'")
+    ap.add_argument("--secondary", default="c2,c3,c4,probes,c1,amp,c4x,lion_lamb,master,states16,many",
+                    help="comma list of further workloads (c2,c3,c4,probes: the rooflines and ceilings; "
+                         "c1,amp,c4x,lion_lamb,master,states16,many) or 'none'")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     return ap.parse_args()
 
 
-class Timer:
-    """Events around each call on the current stream; total from first to last."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.marks = []
-
-    def mark(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        self.marks.append(e)
-
-    def durations_ms(self):
-        self.torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in zip(self.marks[:-1], self.marks[1:])]
-
-
 def dist(xs):
-    """Median and 10th / 90th percentiles (ms) of per-call event intervals."""
+    """Median and 10th / 90th percentiles (ms)."""
     a = sorted(xs)
     q = lambda f: a[min(len(a) - 1, int(round(f * (len(a) - 1))))]
     return dict(median_ms=q(0.5), p10_ms=q(0.1), p90_ms=q(0.9))
 
 
-def run_timed(torch, calls, steps, warmup, stats=None):
-    """calls: list of zero-arg functions forming one step.  The timed region
-    is `steps` steps between two events, with nothing recorded between the
-    calls: its mean is the step time.  A second pass of `steps` steps records
-    an event after every call, for each call's mean and (into `stats`, if a
-    list) its median / p10 / p90; an event between two kernels adds a few
-    microseconds to the interval, so these per-call figures sit slightly
-    above the kernels' own durations.  Returns (ms per step, per-call mean
-    ms from the second pass, host wall ms per step of the timed region)."""
-    for _ in range(warmup):
-        for c in calls:
-            c()
+def gbs(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def timed_region(torch, calls, steps):
+    """`steps` steps between two events on the current stream (the stream
+    the library launches on), bracketed by device synchronisation; returns
+    (ms per step, host wall ms per step)."""
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -114,55 +107,58 @@ def run_timed(torch, calls, steps, warmup, stats=None):
             c()
     b.record()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) * 1e3
-    ms = a.elapsed_time(b) / steps
-    tm = Timer(torch)
-    tm.mark()
-    for _ in range(steps):
+    return a.elapsed_time(b) / steps, (time.perf_counter() - t0) * 1e3 / steps
+
+
+def run_timed(torch, calls, steps, warmup, plans=(), trace_cap=0):
+    """calls: zero-arg functions forming one step.  `warmup` untimed steps,
+    then a timed region of `steps` steps (the step time).  If `plans` are
+    given, a second timed region of `steps` steps follows with their kernel
+    traces on (each launch's start and end stamped by its own dispatch): the
+    per-kernel durations.  The trace adds a few microseconds between
+    launches but nothing to a kernel's own duration, so the step time comes
+    from the untraced region.  Returns (ms per step, host wall ms per step,
+    {plan: trace records}, ms per step of the traced region)."""
+    import optimizer_step_adamw_amd as osa
+    for _ in range(warmup):
         for c in calls:
             c()
-            tm.mark()
-    d = tm.durations_ms()
-    per_call = [sum(d[i::len(calls)]) / steps for i in range(len(calls))]
-    if stats is not None:
-        stats.extend(dist(d[i::len(calls)]) for i in range(len(calls)))
-    return ms, per_call, wall / steps
+    ms, wall = timed_region(torch, calls, steps)
+    recs, ms_traced = {}, None
+    if plans:
+        for p in plans:
+            osa.optim_plan_trace(p, trace_cap)
+        ms_traced, _ = timed_region(torch, calls, steps)
+        for p in plans:
+            r, dropped = osa.optim_plan_trace_read(p, trace_cap)
+            if dropped:
+                raise RuntimeError(f"kernel trace full: {dropped} launches untraced")
+            osa.optim_plan_trace(p, 0)
+            recs[p] = r
+    return ms, wall, recs, ms_traced
 
 
-def run_each(torch, call, steps, warmup=2):
-    """Mean duration (ms) of one call run `steps` times back to back between
-    two events: the kernel's launch duration as a training loop sees it, with
-    no event between launches."""
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(steps):
-        call()
-    b.record()
-    torch.cuda.synchronize()
-    return a.elapsed_time(b) / steps
+def kernel_stats(records, name=None):
+    """Launch count, total / mean ms and per-launch spread of the records of
+    one kernel (all records if name is None)."""
+    ms = [r[2] for r in records if name is None or r[0] == name]
+    if not ms:
+        return None
+    return dict(launches=len(ms), total_ms=sum(ms), mean_ms=sum(ms) / len(ms), **dist(ms))
 
 
-def run_timed_cold(torch, call, steps, warmup, flush_bytes=1 << 30):
-    """One call per step with a 1 GiB device write between steps, outside the
-    events, so the step's inputs come from HBM rather than the 256 MB
-    Infinity Cache.  Returns the per-call event intervals (ms)."""
-    scratch = torch.empty(flush_bytes // 4, dtype=torch.float32, device="cuda")
-    for _ in range(warmup):
-        call()
-    out = []
-    for i in range(steps):
-        scratch.fill_(float(i))
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        call()
-        b.record()
-        torch.cuda.synchronize()
-        out.append(a.elapsed_time(b))
-    del scratch
-    return out
+def roofline_entry(kernel, workload, bytes_per_launch, stats, ceiling=None, traffic=None, note=None):
+    achieved = gbs(bytes_per_launch, stats["mean_ms"])
+    e = dict(kernel=kernel, workload=workload, bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
+             frac=achieved / PEAK_HBM_GBS, traffic=traffic, bytes_per_launch=bytes_per_launch,
+             launch_ms=stats["mean_ms"], launches=stats["launches"],
+             launch_spread_ms=dict(p10=stats["p10_ms"], median=stats["median_ms"], p90=stats["p90_ms"]))
+    if ceiling:
+        e["ceiling"] = ceiling
+        e["frac_of_ceiling"] = achieved / ceiling["gbs"]
+    if note:
+        e["note"] = note
+    return e
 
 
 def library_sources_sha256():
@@ -187,12 +183,47 @@ def environment(torch):
                 library_sources_sha256=library_sources_sha256())
 
 
-def gbs(bytes_per_step, ms):
-    return bytes_per_step / (ms * 1e-3) / 1e9
+KERNEL_SOURCES = {  # traffic summary name -> sources its device code comes from
+    "adamw_fp32": ("device_common.h", "kernels_adam.hip"),
+    "ademamix_fp32": ("device_common.h", "kernels_adam.hip"),
+    "adamw_bf16_remainder": ("device_common.h", "kernels_adam.hip"),
+    "check_finite_bf16": ("device_common.h", "kernels_util.hip"),
+    "mini_update": ("device_common.h", "kernels_mini.hip"),
+    "mini_sumsq": ("device_common.h", "kernels_mini.hip"),
+    "blockwise_8bit": ("device_common.h", "kernels_blockwise.hip"),
+    "blockwise_8bit_interleaved": ("device_common.h", "kernels_blockwise.hip"),
+    "blockwise_4bit": ("device_common.h", "kernels_blockwise.hip"),
+    "blockwise_4bit_interleaved": ("device_common.h", "kernels_blockwise.hip"),
+    "blockwise_ademamix_8bit": ("device_common.h", "kernels_blockwise.hip"),
+    "blockwise_ademamix_4bit": ("device_common.h", "kernels_blockwise.hip"),
+}
+
+
+def kernel_sources_sha256(key):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[key]:
+        with open(os.path.join(ROOT, "optimizer_step_adamw_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_from_profile(key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size), valid
+    only while the kernel's sources are the ones the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", f"counters_{key}.txt")
+    if not os.path.exists(path) or key not in KERNEL_SOURCES:
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != kernel_sources_sha256(key):
+        return None
+    return float(t.group(1))
 
 
 # --------------------------------------------------------------------------
-def adam_buffers(torch, p0_list, grad_dtype, param_bf16=False, ademamix=False, v_len=None):
+def adam_buffers(torch, p0_list, param_bf16=False, ademamix=False, v_len=None):
     dev = "cuda"
     import optimizer_step_adamw_amd as osa
     bufs = {}
@@ -222,202 +253,110 @@ def scalars(torch, lr, inv_scale=None):
                 torch.tensor([inv_scale], dtype=torch.float32, device=dev))
 
 
-def bench_headline(torch, osa, synth, steps, warmup):
-    wl = synth.c2_decay_stress()
-    n, hp = wl.numel, wl.hp
-    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
-    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
-    A = adam_buffers(torch, [p0], osa.OPTIM_F32)
-    B = adam_buffers(torch, [p0], osa.OPTIM_F32, ademamix=True)
-    del p0
-    tla = osa.TensorList(A["p"], [g], m=A["m"], v=A["v"], weight_decay=[hp.wd])
-    tlb = osa.TensorList(B["p"], [g], m=B["m"], v=B["v"], m2=B["m2"], weight_decay=[hp.wd])
-    pa = osa.Plan(tla, osa.OPTIM_ALGO_ADAMW)
-    pb = osa.Plan(tlb, osa.OPTIM_ALGO_ADEMAMIX)
-    sa, sb = scalars(torch, hp.lr), scalars(torch, hp.lr)
-    hpa = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
-    hpb = osa.optim_ademamix_hp(hp.beta1, hp.beta2, wl.extra["beta3"], wl.extra["alpha"], hp.eps)
-
-    def call_a():
-        osa.optim_step_adamw(pa.handle, hpa, sa["lr"], None, None, sa["step"])
-
-    def call_b():
-        osa.optim_step_ademamix(pb.handle, hpb, sb["lr"], None, None, sb["step"])
-
-    stats = []
-    ms, per_call, wall = run_timed(torch, [call_a, call_b], steps, warmup, stats)
-    each = [run_each(torch, call_a, steps), run_each(torch, call_b, steps)]
-    ev = lambda i: dict(events_mean_ms=per_call[i], events=stats[i])
-    res = dict(workload=wl.name, elements=n, ms_per_step=ms, wall_ms_per_step=wall,
-               elements_per_s=2 * n / (ms * 1e-3),
-               kernels={
-                   "adamw_fp32": dict(ms=each[0], bytes=B_ADAMW_F32 * n,
-                                      gbs=gbs(B_ADAMW_F32 * n, each[0]), **ev(0)),
-                   "ademamix_fp32": dict(ms=each[1], bytes=B_ADEMAMIX_F32 * n,
-                                         gbs=gbs(B_ADEMAMIX_F32 * n, each[1]), **ev(1)),
-               },
-               note="step time: the timed steps between two events; kernel ms: the same call run "
-                    "`steps` times back to back between two events; events_*: an event after every "
-                    "call (each adds a few microseconds)")
-    for k in res["kernels"].values():
-        k["frac"] = k["gbs"] / PEAK_HBM_GBS
-    pa.close()
-    pb.close()
-    return res
-
-
-def bench_many(torch, osa, synth, steps, warmup):
-    """The headline's 16,777,216 AdamW fp32 elements as one list of many
-    tensors (views of one allocation per array): 4096 tensors of 4096
-    elements, and 65536 tensors of 256 (each shorter than a work unit), next
-    to the single tensor -- the cost of the multi-tensor traversal."""
-    n = 1 << 24
-    out = {}
-    for count in (1, 4096, 65536):
-        size = n // count
-        P = torch.randn(n, device="cuda") * 0.02
-        G = torch.randn(n, device="cuda") * 1e-3
-        M = torch.zeros(n, device="cuda")
-        V = torch.zeros(n, device="cuda")
-        views = lambda x: [x[i * size:(i + 1) * size] for i in range(count)]
-        plan = osa.Plan(osa.TensorList(views(P), views(G), m=views(M), v=views(V),
-                                       weight_decay=[0.1] * count), osa.OPTIM_ALGO_ADAMW)
-        s = scalars(torch, 1e-3)
-        h = osa.optim_adamw_hp(0.9, 0.999, 1e-8)
-        ms = run_each(torch, lambda: osa.optim_step_adamw(plan.handle, h, s["lr"], None, None, s["step"]), steps)
-        plan.close()
-        out[f"tensors_{count}x{size}"] = dict(ms=ms, gbs=gbs(B_ADAMW_F32 * n, ms),
-                                              frac=gbs(B_ADAMW_F32 * n, ms) / PEAK_HBM_GBS)
-        del P, G, M, V
-        torch.cuda.empty_cache()
-    return dict(workload="adamw_fp32_16M_as_many_tensors", elements=n, lists=out,
-                note="kernel ms: the same call run back to back on one state (a 448 MB working set "
-                     "partly held by the Infinity Cache between calls)")
-
-
-def bench_lion_lamb(torch, osa, synth, steps, warmup):
-    """Lion and LAMB on the 4096 x 4096 tensor and gradients of the headline,
-    each with its own state (beta (0.9, 0.99) for Lion; LAMB eps 1e-6)."""
-    wl = synth.c2_decay_stress()
-    n, hp = wl.numel, wl.hp
-    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
-    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
-    A = adam_buffers(torch, [p0], osa.OPTIM_F32)
-    B = adam_buffers(torch, [p0], osa.OPTIM_F32)
-    del p0
-    pl = osa.Plan(osa.TensorList(A["p"], [g], m=A["m"], weight_decay=[hp.wd]), osa.OPTIM_ALGO_LION)
-    pm = osa.Plan(osa.TensorList(B["p"], [g], m=B["m"], v=B["v"], weight_decay=[hp.wd]), osa.OPTIM_ALGO_LAMB)
-    sl, sm = scalars(torch, 1e-4), scalars(torch, 1e-3)
-    hl = osa.optim_lion_hp(0.9, 0.99)
-    hm = osa.optim_adamw_hp(hp.beta1, hp.beta2, 1e-6)
-    calls = [lambda: osa.optim_step_lion(pl.handle, hl, sl["lr"], None, None, sl["step"]),
-             lambda: osa.optim_step_lamb(pm.handle, hm, sm["lr"], None, None, sm["step"])]
-    ms, _, _ = run_timed(torch, calls, steps, warmup)
-    per_call = [run_each(torch, c, steps) for c in calls]
-    pl.close()
-    pm.close()
-    del A, B, g
+def free(torch):
+    torch.cuda.synchronize()
     torch.cuda.empty_cache()
-    return dict(workload="lion_lamb_fp32_4096x4096", elements=n, ms_per_step=ms,
-                kernels={"lion_fp32": dict(ms=per_call[0], bytes_per_element=B_LION_F32,
-                                           gbs=gbs(B_LION_F32 * n, per_call[0]),
-                                           frac=gbs(B_LION_F32 * n, per_call[0]) / PEAK_HBM_GBS),
-                         "lamb_fp32": dict(ms=per_call[1], bytes_per_element=B_ADAMW_F32,
-                                           gbs=gbs(B_ADAMW_F32 * n, per_call[1]),
-                                           frac=gbs(B_ADAMW_F32 * n, per_call[1]) / PEAK_HBM_GBS,
-                                           note="algorithmic 28 B/elem; the two passes move 40 B/elem "
-                                                "(p, m, v read again for the per-tensor trust ratio)")})
 
 
-def bench_master(torch, osa, synth, steps, warmup):
-    """AdamW with an fp32 master and a bf16 or fp16 model copy on the
-    4096 x 4096 tensor and gradients of the headline."""
-    wl = synth.c2_decay_stress()
-    n, hp = wl.numel, wl.hp
-    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
-    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
-    out = {}
-    for name, dt in (("adamw_master_bf16", osa.OPTIM_BF16), ("adamw_master_f16", osa.OPTIM_F16)):
-        master = p0.clone()
-        model = torch.zeros(n, dtype=torch.int16, device="cuda")
-        m = torch.zeros(n, device="cuda")
-        v = torch.zeros(n, device="cuda")
-        plan = osa.Plan(osa.TensorList([model], [g], m=[m], v=[v], master=[master], weight_decay=[hp.wd],
-                                       param_dtype=dt), osa.OPTIM_ALGO_ADAMW)
-        sc = scalars(torch, hp.lr)
-        h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
-        ms, _, _ = run_timed(torch, [lambda: osa.optim_step_adamw(plan.handle, h, sc["lr"], None, None,
-                                                                  sc["step"])], steps, warmup)
-        plan.close()
-        out[name] = dict(ms=ms, bytes_per_element=B_ADAMW_MASTER, gbs=gbs(B_ADAMW_MASTER * n, ms),
-                         frac=gbs(B_ADAMW_MASTER * n, ms) / PEAK_HBM_GBS)
-        del master, model, m, v
-    del p0, g
-    torch.cuda.empty_cache()
-    return dict(workload="adamw_master_copy_4096x4096", elements=n, kernels=out)
-
-
-def bench_states16(torch, osa, synth, steps, warmup):
-    """AdamW with fp16 or bf16 moments and per-tensor scales on the
-    4096 x 4096 fp32 tensor and gradients of the headline.  frac is priced on
-    the algorithmic 20 B/element; the two-pass fp16 step moves 28."""
-    wl = synth.c2_decay_stress()
-    n, hp = wl.numel, wl.hp
-    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
-    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
-    out = {}
-    for name, sdt in (("adamw_states_f16", osa.OPTIM_F16), ("adamw_states_bf16", osa.OPTIM_BF16)):
-        p = p0.clone()
-        m = torch.zeros(n, dtype=torch.int16, device="cuda")
-        v = torch.zeros(n, dtype=torch.int16, device="cuda")
-        sm, sv = torch.ones(1, device="cuda"), torch.ones(1, device="cuda")
-        plan = osa.Plan(osa.TensorList([p], [g], m=[m], v=[v], scale_m=[sm], scale_v=[sv], weight_decay=[hp.wd]),
-                        osa.OPTIM_ALGO_ADAMW, state_dtype=sdt)
-        sc = scalars(torch, hp.lr)
-        h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
-        ms, _, _ = run_timed(torch, [lambda: osa.optim_step_adamw(plan.handle, h, sc["lr"], None, None,
-                                                                  sc["step"])], steps, warmup)
-        plan.close()
-        moved = T_ADAMW_STATES16 if sdt == osa.OPTIM_F16 else B_ADAMW_STATES16  # bf16: one pass
-        out[name] = dict(ms=ms, bytes_per_element=B_ADAMW_STATES16, moved_per_element=moved,
-                         gbs=gbs(B_ADAMW_STATES16 * n, ms), frac=gbs(B_ADAMW_STATES16 * n, ms) / PEAK_HBM_GBS)
-        del p, m, v
-    del p0, g
-    torch.cuda.empty_cache()
-    return dict(workload="adamw_scaled_states_fp32_4096x4096", elements=n, kernels=out)
-
-
-def bench_c1(torch, osa, synth, steps, warmup):
-    wl = synth.c1_single_tensor()
-    n, hp = wl.numel, wl.hp
-    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
-    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
-    A = adam_buffers(torch, [p0], osa.OPTIM_F32)
-    plan = osa.Plan(osa.TensorList(A["p"], [g], m=A["m"], v=A["v"], weight_decay=[hp.wd]),
-                    osa.OPTIM_ALGO_ADAMW)
+# --------------------------------------------------------------------------
+# headline: Adam-mini, Llama-7B-shaped list
+def bench_c5(torch, osa, synth, steps, warmup):
+    wl = synth.c5_adam_mini_7b()
+    hp = wl.hp
+    specs = wl.tensors
+    names = [s.name for s in specs]
+    sizes = [s.numel for s in specs]
+    kinds, hn, wds = osa.adam_mini_partition(names, sizes, dim=wl.extra["dim"], n_heads=wl.extra["n_heads"],
+                                             weight_decay=hp.wd)
+    vlen = [s if k == osa.OPTIM_MINI_FULL_V else s // h for k, s, h in zip(kinds, sizes, hn)]
+    P = [synth.initial_param_device(s, wl.p_std, wl.index, i, "cuda") for i, s in enumerate(specs)]
+    G = [synth.device_normal(s.numel, wl.g_std, "cuda", wl.index, i, 1, synth.GRAD) for i, s in enumerate(specs)]
+    M = [torch.zeros(k, dtype=torch.float32, device="cuda") for k in sizes]
+    V = [torch.zeros(k, dtype=torch.float32, device="cuda") for k in vlen]
+    plan = osa.Plan(osa.TensorList(P, G, m=M, v=V, weight_decay=wds, mini_kind=kinds, head_numel=hn),
+                    osa.OPTIM_ALGO_ADAM_MINI)
     s = scalars(torch, hp.lr)
     h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
-    step = lambda: osa.optim_step_adamw(plan.handle, h, s["lr"], None, None, s["step"])
-    stats = []
-    ms, _, _ = run_timed(torch, [step], steps, warmup, stats)
-    cold = dist(run_timed_cold(torch, step, steps, warmup))
+    step = lambda: osa.optim_step_adam_mini(plan.handle, h, s["lr"], None, None, s["step"])
+    ms, wall, recs, ms_traced = run_timed(torch, [step], steps, warmup, plans=[plan.handle], trace_cap=300 * steps)
+    rec = recs[plan.handle]
+    n = wl.numel
+    full = sum(sz for sz, k in zip(sizes, kinds) if k == osa.OPTIM_MINI_FULL_V)
+    shared = n - full
+    alg = B_MINI_FULL * full + B_MINI_SHARED * shared
+    upd, sums, fin = (kernel_stats(rec, k) for k in ("mini_update_kernel", "mini_sumsq_kernel",
+                                                    "mini_finalize_kernel"))
+    per_step = lambda st: st["launches"] // steps
+    kern = dict(
+        mini_update=dict(launches_per_step=per_step(upd), ms_per_step=upd["total_ms"] / steps,
+                         bytes_per_step=alg, gbs=gbs(alg, upd["total_ms"] / steps)),
+        mini_sumsq=dict(launches_per_step=per_step(sums), ms_per_step=sums["total_ms"] / steps,
+                        bytes_per_step=B_MINI_SUMS * shared, gbs=gbs(B_MINI_SUMS * shared, sums["total_ms"] / steps)),
+        mini_finalize=dict(launches_per_step=per_step(fin), ms_per_step=fin["total_ms"] / steps))
+    kernel_ms = kernel_stats(rec)["total_ms"] / steps
+    roof = roofline_entry("mini_update_kernel", wl.name, alg / per_step(upd), upd,
+                          traffic=traffic_from_profile("mini_update"),
+                          note="bytes per launch: the update's algorithmic bytes per step (28 B/elem full v, "
+                               "20 B/elem shared v: R p g m, W p m) over its launches per step (one per "
+                               "segment); g was read by the segment's block sums just before, so part of the "
+                               "update's g comes from the Infinity Cache")
     plan.close()
-    return dict(workload=wl.name, elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
-                gbs=gbs(B_ADAMW_F32 * n, ms), frac=gbs(B_ADAMW_F32 * n, ms) / PEAK_HBM_GBS, warm=stats[0],
-                cold=dict(cold, gbs=gbs(B_ADAMW_F32 * n, cold["median_ms"])),
-                note="29 MB of state: cache-resident and launch-bound when warm; cold = after a 1 GiB "
-                     "write between steps, inputs from HBM")
+    del P, G, M, V
+    free(torch)
+    return dict(workload=wl.name, elements=n, ms_per_step=ms, wall_ms_per_step=wall,
+                traced_ms_per_step=ms_traced, elements_per_s=n / (ms * 1e-3), algorithmic_bytes_per_step=alg,
+                gbs=gbs(alg, ms), frac=gbs(alg, ms) / PEAK_HBM_GBS,
+                kernel_ms_per_step=kernel_ms, kernels=kern, roofline=roof,
+                note="step bytes: 28 B/elem for the 2 full-v tensors, 20 B/elem for the 289 shared-v tensors "
+                     "(the block-sum pass's read of g is not counted)")
 
 
-def bench_c3(torch, osa, synth, steps, warmup):
+# --------------------------------------------------------------------------
+# 4096 x 4096: AdamW and AdEMAMix, four state sets in turn
+def bench_c2(torch, osa, synth, steps, warmup):
+    wl = synth.c2_decay_stress()
+    n, hp = wl.numel, wl.hp
+    out = {}
+    for ade in (False, True):
+        sets = []
+        for k in range(ROTATE):
+            p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
+            g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1 + k, synth.GRAD)
+            B = adam_buffers(torch, [p0], ademamix=ade)
+            del p0
+            tl = osa.TensorList(B["p"], [g], m=B["m"], v=B["v"], m2=B["m2"], weight_decay=[hp.wd])
+            plan = osa.Plan(tl, osa.OPTIM_ALGO_ADEMAMIX if ade else osa.OPTIM_ALGO_ADAMW)
+            sets.append((plan, scalars(torch, hp.lr), B, g))
+        if ade:
+            h = osa.optim_ademamix_hp(hp.beta1, hp.beta2, wl.extra["beta3"], wl.extra["alpha"], hp.eps)
+            fn = osa.optim_step_ademamix
+        else:
+            h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
+            fn = osa.optim_step_adamw
+        calls = [(lambda pl=pl, sc=sc: fn(pl.handle, h, sc["lr"], None, None, sc["step"]))
+                 for pl, sc, _, _ in sets]
+        ms, _, recs, _ = run_timed(torch, calls, steps, warmup, plans=[x[0].handle for x in sets], trace_cap=4 * steps)
+        rec = [r for v in recs.values() for r in v]
+        name = "ademamix_fp32" if ade else "adamw_fp32"
+        bpe = B_ADEMAMIX_F32 if ade else B_ADAMW_F32
+        out[name] = dict(stats=kernel_stats(rec), bytes=bpe * n, ms_per_call=ms / ROTATE)
+        for pl, _, _, _ in sets:
+            pl.close()
+        del sets
+        free(torch)
+    return dict(workload=wl.name, elements=n, rotate=ROTATE, kernels=out)
+
+
+# --------------------------------------------------------------------------
+# Llama 1.1B: bf16 params + int16 remainders, bf16 grads x 65536, AMP, cosine lr
+def c3_state(torch, osa, synth):
     wl = synth.c3_llama_1b()
     hp, scale = wl.hp, wl.extra["loss_scale"]
     specs = wl.tensors
-    n = wl.numel
     p0 = [synth.initial_param_device(s, wl.p_std, wl.index, i, "cuda") for i, s in enumerate(specs)]
-    A = adam_buffers(torch, p0, osa.OPTIM_BF16, param_bf16=True)
+    A = adam_buffers(torch, p0, param_bf16=True)
     del p0
-    torch.cuda.empty_cache()
+    free(torch)
     G = []
     for i, s in enumerate(specs):
         x = synth.device_normal(s.numel, wl.g_std, "cuda", wl.index, i, 0, synth.GRAD)
@@ -430,6 +369,12 @@ def bench_c3(torch, osa, synth, steps, warmup):
     s = scalars(torch, 0.0, inv_scale=1.0 / scale)
     osa.optim_plan_set_schedule(plan.handle, osa.OPTIM_SCHED_COSINE, hp.lr, 0.0, wl.steps, s["iter"])
     h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
+    return wl, plan, s, h, (A, G)
+
+
+def bench_c3(torch, osa, synth, steps, warmup):
+    wl, plan, s, h, keep = c3_state(torch, osa, synth)
+    n = wl.numel
 
     def finite():
         s["found_inf"].zero_()
@@ -438,11 +383,25 @@ def bench_c3(torch, osa, synth, steps, warmup):
     def step():
         osa.optim_step_adamw(plan.handle, h, s["lr"], s["inv_scale"], s["found_inf"], s["step"])
 
-    ms, per_call, _ = run_timed(torch, [finite, step], steps, warmup)
+    ms, _, recs, _ = run_timed(torch, [finite, step], steps, warmup, plans=[plan.handle], trace_cap=4 * steps)
+    rec = recs[plan.handle]
+    plan.close()
+    del keep
+    free(torch)
+    b = (B_BF16R + B_FINITE_BF16) * n
+    return dict(workload=wl.name, elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
+                gbs=gbs(b, ms), frac=gbs(b, ms) / PEAK_HBM_GBS,
+                kernels=dict(adamw_bf16_remainder=dict(stats=kernel_stats(rec, "adam_kernel"), bytes=B_BF16R * n),
+                             check_finite_bf16=dict(stats=kernel_stats(rec, "finite_kernel"),
+                                                    bytes=B_FINITE_BF16 * n)))
 
-    # the same list in the full AMP loop with clipping folded into the step:
-    # check + global norm (one read of the grads), clipped step, scale update
-    scale_dev = torch.tensor([scale], dtype=torch.float32, device="cuda")
+
+def bench_amp(torch, osa, synth, steps, warmup):
+    """The 1.1B list in the full AMP loop with clipping folded into the step:
+    check + global norm (one read of the grads), clipped step, scale update."""
+    wl, plan, s, h, keep = c3_state(torch, osa, synth)
+    n = wl.numel
+    scale_dev = torch.tensor([wl.extra["loss_scale"]], dtype=torch.float32, device="cuda")
     tracker = torch.zeros(1, dtype=torch.int32, device="cuda")
     norm = torch.zeros(1, dtype=torch.float32, device="cuda")
     clip = torch.zeros(1, dtype=torch.float32, device="cuda")
@@ -457,24 +416,24 @@ def bench_c3(torch, osa, synth, steps, warmup):
     def scaler():
         osa.optim_scaler_update(scale_dev, s["inv_scale"], tracker, s["found_inf"], 2.0, 0.5, 2000)
 
-    ms_c, per_c, _ = run_timed(torch, [check_norm, clipped_step, scaler], steps, warmup)
+    ms, _, recs, _ = run_timed(torch, [check_norm, clipped_step, scaler], steps, warmup, plans=[plan.handle],
+                            trace_cap=8 * steps)
+    rec = recs[plan.handle]
     plan.close()
-    del A, G
-    torch.cuda.empty_cache()
-    b = B_BF16R_AMP * n
-    return dict(workload=wl.name, elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
-                gbs=gbs(b, ms), frac=gbs(b, ms) / PEAK_HBM_GBS,
-                kernels={"check_finite_bf16": dict(ms=per_call[0], gbs=gbs(2.0 * n, per_call[0])),
-                         "adamw_bf16_remainder": dict(ms=per_call[1], gbs=gbs(26.0 * n, per_call[1]))},
-                amp_clip_loop=dict(
-                    ms_per_step=ms_c, elements_per_s=n / (ms_c * 1e-3), gbs=gbs(b, ms_c),
-                    frac=gbs(b, ms_c) / PEAK_HBM_GBS, max_norm=CLIP_MAX_NORM,
-                    kernels={"check_and_norm_bf16": dict(ms=per_c[0], gbs=gbs(2.0 * n, per_c[0])),
-                             "adamw_bf16_remainder_clipped": dict(ms=per_c[1], gbs=gbs(26.0 * n, per_c[1])),
-                             "scaler_update": dict(ms=per_c[2])}))
+    del keep
+    free(torch)
+    b = (B_BF16R + B_FINITE_BF16) * n
+    ks = {k: kernel_stats(rec, k) for k in ("finite_kernel", "norm_stage1_kernel", "norm_finalize_kernel",
+                                            "adam_kernel")}
+    return dict(workload=wl.name + "_clip_loop", elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
+                gbs=gbs(b, ms), frac=gbs(b, ms) / PEAK_HBM_GBS, max_norm=CLIP_MAX_NORM,
+                kernels={k: dict(mean_ms=v["mean_ms"], launches=v["launches"]) for k, v in ks.items() if v},
+                check_and_norm_gbs=gbs(B_FINITE_BF16 * n, ks["finite_kernel"]["mean_ms"]))
 
 
-def bench_c4(torch, osa, synth, steps, warmup):
+# --------------------------------------------------------------------------
+# blockwise 8-bit / 4-bit states, 268M elements
+def bench_blockwise(torch, osa, synth, steps, warmup, interleaved=False, ademamix=False):
     wl = synth.c4_blockwise()
     n, hp = wl.numel, wl.hp
     out = {}
@@ -482,123 +441,322 @@ def bench_c4(torch, osa, synth, steps, warmup):
         p = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
         g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
         nb = (n * bits + 7) // 8
-        qm = torch.zeros(nb, dtype=torch.uint8, device="cuda")
-        qv = torch.zeros(nb, dtype=torch.uint8, device="cuda")
-        am = torch.zeros(n // block, dtype=torch.float32, device="cuda")
-        av = torch.zeros(n // block, dtype=torch.float32, device="cuda")
-        tl = osa.TensorList([p], [g], qm=[qm], qv=[qv], absmax_m=[am], absmax_v=[av], weight_decay=[hp.wd])
-        plan = osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE, bits=bits, block=block)
+        keep = []
+        if interleaved:
+            qmv = torch.zeros(2 * nb, dtype=torch.uint8, device="cuda")
+            amv = torch.zeros(2 * (n // block), dtype=torch.float32, device="cuda")
+            keep += [qmv, amv]
+            tl = osa.TensorList([p], [g], qm=[qmv], absmax_m=[amv], weight_decay=[hp.wd])
+            plan = osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE, bits=bits, block=block,
+                            state_layout=osa.OPTIM_LAYOUT_INTERLEAVED)
+        else:
+            mk = lambda: torch.zeros(nb, dtype=torch.uint8, device="cuda")
+            ak = lambda: torch.zeros(n // block, dtype=torch.float32, device="cuda")
+            qm, qv, am, av = mk(), mk(), ak(), ak()
+            keep += [qm, qv, am, av]
+            kw = {}
+            if ademamix:
+                qm2, am2 = mk(), ak()
+                keep += [qm2, am2]
+                kw = dict(qm2=[qm2], absmax_m2=[am2])
+            tl = osa.TensorList([p], [g], qm=[qm], qv=[qv], absmax_m=[am], absmax_v=[av], weight_decay=[hp.wd], **kw)
+            plan = osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX if ademamix else osa.OPTIM_ALGO_BLOCKWISE,
+                            bits=bits, block=block)
         s = scalars(torch, hp.lr)
-        h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
-        ms, _, _ = run_timed(torch, [lambda: osa.optim_step_8bit_blockwise(
-            plan.handle, h, bits, block, s["lr"], None, None, s["step"])], steps, warmup)
+        if ademamix:
+            he = osa.optim_ademamix_hp(hp.beta1, hp.beta2, C4_BETA3, C4_ALPHA, hp.eps)
+            call = lambda: osa.optim_step_8bit_blockwise_ademamix(plan.handle, he, bits, block, s["lr"], None, None,
+                                                                  s["step"])
+            bpe = bpe + bits / 4 + 8 / block  # + m2 codes and absmax, read and written
+        else:
+            h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
+            call = lambda: osa.optim_step_8bit_blockwise(plan.handle, h, bits, block, s["lr"], None, None, s["step"])
+        ms, _, recs, _ = run_timed(torch, [call], steps, warmup, plans=[plan.handle], trace_cap=2 * steps)
+        st = kernel_stats(recs[plan.handle])
         plan.close()
-        out[f"blockwise_{bits}bit_block{block}"] = dict(
-            elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3), bytes_per_element=bpe,
-            gbs=gbs(bpe * n, ms), frac=gbs(bpe * n, ms) / PEAK_HBM_GBS)
-        # the same states in the interleaved layout (m and v codes side by side
-        # in one array, the two absmax values of a block in another)
-        del qm, qv, am, av
-        torch.cuda.empty_cache()
-        qmv = torch.zeros(2 * nb, dtype=torch.uint8, device="cuda")
-        amv = torch.zeros(2 * (n // block), dtype=torch.float32, device="cuda")
-        tl = osa.TensorList([p], [g], qm=[qmv], absmax_m=[amv], weight_decay=[hp.wd])
-        plan = osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE, bits=bits, block=block,
-                        state_layout=osa.OPTIM_LAYOUT_INTERLEAVED)
-        s = scalars(torch, hp.lr)
-        ms, _, _ = run_timed(torch, [lambda: osa.optim_step_8bit_blockwise(
-            plan.handle, h, bits, block, s["lr"], None, None, s["step"])], steps, warmup)
-        plan.close()
-        out[f"blockwise_{bits}bit_block{block}_interleaved"] = dict(
-            elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3), bytes_per_element=bpe,
-            gbs=gbs(bpe * n, ms), frac=gbs(bpe * n, ms) / PEAK_HBM_GBS)
-        del qmv, amv
-        torch.cuda.empty_cache()
-        qm = torch.zeros(nb, dtype=torch.uint8, device="cuda")
-        qv = torch.zeros(nb, dtype=torch.uint8, device="cuda")
-        am = torch.zeros(n // block, dtype=torch.float32, device="cuda")
-        av = torch.zeros(n // block, dtype=torch.float32, device="cuda")
-        # the same list with AdEMAMix's third state (slow EMA m2, signed codes)
-        qm2 = torch.zeros(nb, dtype=torch.uint8, device="cuda")
-        am2 = torch.zeros(n // block, dtype=torch.float32, device="cuda")
-        tl = osa.TensorList([p], [g], qm=[qm], qv=[qv], absmax_m=[am], absmax_v=[av], qm2=[qm2],
-                            absmax_m2=[am2], weight_decay=[hp.wd])
-        plan = osa.Plan(tl, osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX, bits=bits, block=block)
-        s = scalars(torch, hp.lr)
-        he = osa.optim_ademamix_hp(hp.beta1, hp.beta2, C4_BETA3, C4_ALPHA, hp.eps)
-        ms, _, _ = run_timed(torch, [lambda: osa.optim_step_8bit_blockwise_ademamix(
-            plan.handle, he, bits, block, s["lr"], None, None, s["step"])], steps, warmup)
-        plan.close()
-        bpe3 = bpe + bits / 4 + 8 / block  # + m2 codes and absmax, read and written
-        out[f"blockwise_ademamix_{bits}bit_block{block}"] = dict(
-            elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3), bytes_per_element=bpe3,
-            gbs=gbs(bpe3 * n, ms), frac=gbs(bpe3 * n, ms) / PEAK_HBM_GBS, beta3=C4_BETA3, alpha=C4_ALPHA)
-        del p, g, qm, qv, am, av, qm2, am2
-        torch.cuda.empty_cache()
-    return dict(workload=wl.name, **out)
+        name = ("blockwise_ademamix_" if ademamix else "blockwise_") + f"{bits}bit" + \
+               ("_interleaved" if interleaved else "")
+        out[name] = dict(elements=n, block=block, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
+                         bytes_per_element=bpe, stats=st, bytes=bpe * n,
+                         gbs=gbs(bpe * n, st["mean_ms"]), frac=gbs(bpe * n, st["mean_ms"]) / PEAK_HBM_GBS)
+        del p, g, keep, tl
+        free(torch)
+    return dict(workload=wl.name, kernels=out)
 
 
-def bench_c5(torch, osa, synth, steps, warmup):
-    wl = synth.c5_adam_mini_7b()
-    hp = wl.hp
-    specs = wl.tensors
-    names = [s.name for s in specs]
-    sizes = [s.numel for s in specs]
-    kinds, hn, wds = osa.adam_mini_partition(names, sizes, dim=wl.extra["dim"], n_heads=wl.extra["n_heads"],
-                                             weight_decay=hp.wd)
-    vlen = [s if k == osa.OPTIM_MINI_FULL_V else s // h for k, s, h in zip(kinds, sizes, hn)]
-    P = [synth.initial_param_device(s, wl.p_std, wl.index, i, "cuda") for i, s in enumerate(specs)]
-    G = [synth.device_normal(s.numel, wl.g_std, "cuda", wl.index, i, 1, synth.GRAD) for i, s in enumerate(specs)]
-    M = [torch.zeros(k, dtype=torch.float32, device="cuda") for k in sizes]
-    V = [torch.zeros(k, dtype=torch.float32, device="cuda") for k in vlen]
-    tl = osa.TensorList(P, G, m=M, v=V, weight_decay=wds, mini_kind=kinds, head_numel=hn)
-    plan = osa.Plan(tl, osa.OPTIM_ALGO_ADAM_MINI)
+# --------------------------------------------------------------------------
+# access-pattern ceilings
+def probe_time(torch, fn, reps, warmup=2):
+    """Mean ms of one probe launch (events around each launch on the current
+    stream; each probe is one kernel)."""
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    ev = []
+    for i in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i)
+        b.record()
+        ev.append((a, b))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / reps
+
+
+def bench_probes(torch, reps):
+    import probes
+    out = {}
+    f32 = lambda k: torch.empty(k, dtype=torch.float32, device="cuda").normal_()
+    # 4096^2 AdamW / AdEMAMix patterns: four array sets in turn, units of 4096
+    # (the kernels' form at this size)
+    n = 1 << 24
+    for name, arrays, bpe in (("adamw_4096x4096", 4, B_ADAMW_F32), ("ademamix_4096x4096", 5, B_ADEMAMIX_F32)):
+        sets = [[f32(n) for _ in range(arrays)] for _ in range(ROTATE)]
+        if arrays == 4:
+            fn = lambda i: probes.call("probe_adamw", *sets[i % ROTATE], n, 4)
+        else:
+            fn = lambda i: probes.call("probe_ademamix", *sets[i % ROTATE], n, 4)
+        ms = probe_time(torch, fn, 4 * reps)
+        out[name] = dict(ms=ms, bytes=bpe * n, gbs=gbs(bpe * n, ms))
+        del sets
+        free(torch)
+    n = 1 << 28
+    # Llama-1.1B bf16 + remainder pattern (2048-element units)
+    h16 = lambda: torch.empty(n, dtype=torch.int16, device="cuda").random_(-30000, 30000)
+    arr = [h16(), h16(), h16(), f32(n), f32(n)]
+    ms = probe_time(torch, lambda i: probes.call("probe_bf16r", *arr, n), reps)
+    out["bf16r_268M"] = dict(ms=ms, bytes=B_BF16R * n, gbs=gbs(B_BF16R * n, ms))
+    sink = torch.zeros(n // 32768, dtype=torch.int32, device="cuda")
+    ms = probe_time(torch, lambda i: probes.call("probe_read", arr[2], n, 2, sink), reps)
+    out["read_bf16_268M"] = dict(ms=ms, bytes=2.0 * n, gbs=gbs(2.0 * n, ms))
+    ms = probe_time(torch, lambda i: probes.call("probe_read", arr[3], n, 4, sink), reps)
+    out["read_fp32_268M"] = dict(ms=ms, bytes=4.0 * n, gbs=gbs(4.0 * n, ms))
+    del arr
+    free(torch)
+    # Adam-mini update pattern with g from HBM (R p g m, W p m; units of 4096)
+    arr = [f32(n), f32(n), f32(n)]
+    ms = probe_time(torch, lambda i: probes.call("probe_mini", *arr, n), reps)
+    out["mini_3r2w_268M"] = dict(ms=ms, bytes=B_MINI_SHARED * n, gbs=gbs(B_MINI_SHARED * n, ms))
+    ms = probe_time(torch, lambda i: probes.call("probe_copy", arr[0], arr[1], n), reps)
+    out["copy_268M"] = dict(ms=ms, bytes=8.0 * n, gbs=gbs(8.0 * n, ms))
+    del arr
+    free(torch)
+    # blockwise separate layout: 8-bit block 256, 4-bit block 128 (8192-element
+    # units, 2 or 8 rows of loads in flight; the better one is the ceiling)
+    for bits, block, bpe in ((8, 256, B_8BIT), (4, 128, B_4BIT)):
+        nb = n * bits // 8
+        arr = [f32(n), f32(n), torch.zeros(nb, dtype=torch.uint8, device="cuda"),
+               torch.zeros(nb, dtype=torch.uint8, device="cuda"),
+               torch.zeros(n // block, device="cuda"), torch.zeros(n // block, device="cuda")]
+        best = None
+        for rows in (2, 8):
+            ms = probe_time(torch, lambda i: probes.call("probe_blockwise", *arr, n, bits, rows), reps)
+            e = dict(ms=ms, bytes=bpe * n, gbs=gbs(bpe * n, ms), rows_in_flight=rows)
+            best = e if best is None or e["gbs"] > best["gbs"] else best
+        out[f"blockwise_{bits}bit_268M"] = best
+        del arr
+        free(torch)
+    return out
+
+
+# --------------------------------------------------------------------------
+# secondary workloads
+def bench_c1(torch, osa, synth, steps, warmup):
+    """The 1M-element tensor (29 MB of state): warm (cache-resident, launch
+    bound) and cold (a 1 GiB device write between steps, outside the events)."""
+    wl = synth.c1_single_tensor()
+    n, hp = wl.numel, wl.hp
+    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
+    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
+    A = adam_buffers(torch, [p0])
+    plan = osa.Plan(osa.TensorList(A["p"], [g], m=A["m"], v=A["v"], weight_decay=[hp.wd]), osa.OPTIM_ALGO_ADAMW)
     s = scalars(torch, hp.lr)
     h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
-    ms, _, _ = run_timed(torch, [lambda: osa.optim_step_adam_mini(plan.handle, h, s["lr"], None, None,
-                                                                   s["step"])], max(3, steps // 2), 2)
+    step = lambda: osa.optim_step_adamw(plan.handle, h, s["lr"], None, None, s["step"])
+    ms, _, recs, _ = run_timed(torch, [step], steps, warmup, plans=[plan.handle], trace_cap=2 * steps)
+    warm = kernel_stats(recs[plan.handle])
+    scratch = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda")
+    osa.optim_plan_trace(plan.handle, 2 * steps)
+    for i in range(steps):
+        scratch.fill_(float(i))
+        step()
+    cold = kernel_stats(osa.optim_plan_trace_read(plan.handle)[0])
+    osa.optim_plan_trace(plan.handle, 0)
     plan.close()
-    n = wl.numel
-    full = sum(sz for sz, k in zip(sizes, kinds) if k == osa.OPTIM_MINI_FULL_V)
-    alg = 28.0 * full + 20.0 * (n - full)
-    del P, G, M, V
-    torch.cuda.empty_cache()
+    del scratch
+    free(torch)
     return dict(workload=wl.name, elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
-                gbs=gbs(alg, ms), frac=gbs(alg, ms) / PEAK_HBM_GBS,
-                note="algorithmic bytes 28 B/elem for full-v tensors, 20 B/elem for shared-v tensors; "
-                     "the kernels read g twice (block sums, then update), segment by segment, so the "
-                     "second read comes mostly from the Infinity Cache")
+                warm=dict(warm, gbs=gbs(B_ADAMW_F32 * n, warm["mean_ms"])),
+                cold=dict(cold, gbs=gbs(B_ADAMW_F32 * n, cold["mean_ms"])),
+                note="kernel durations from the trace; warm = back to back (29 MB in the Infinity Cache), "
+                     "cold = after a 1 GiB write")
+
+
+def bench_lion_lamb(torch, osa, synth, steps, warmup):
+    """Lion and LAMB on the 4096 x 4096 tensor (beta (0.9, 0.99) for Lion;
+    LAMB eps 1e-6), each kernel timed from the trace."""
+    wl = synth.c2_decay_stress()
+    n, hp = wl.numel, wl.hp
+    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
+    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
+    A = adam_buffers(torch, [p0])
+    B = adam_buffers(torch, [p0])
+    del p0
+    pl = osa.Plan(osa.TensorList(A["p"], [g], m=A["m"], weight_decay=[hp.wd]), osa.OPTIM_ALGO_LION)
+    pm = osa.Plan(osa.TensorList(B["p"], [g], m=B["m"], v=B["v"], weight_decay=[hp.wd]), osa.OPTIM_ALGO_LAMB)
+    sl, sm = scalars(torch, 1e-4), scalars(torch, 1e-3)
+    hl = osa.optim_lion_hp(0.9, 0.99)
+    hm = osa.optim_adamw_hp(hp.beta1, hp.beta2, 1e-6)
+    calls = [lambda: osa.optim_step_lion(pl.handle, hl, sl["lr"], None, None, sl["step"]),
+             lambda: osa.optim_step_lamb(pm.handle, hm, sm["lr"], None, None, sm["step"])]
+    ms, _, recs, _ = run_timed(torch, calls, steps, warmup, plans=[pl.handle, pm.handle], trace_cap=4 * steps)
+    lion = kernel_stats(recs[pl.handle])
+    lamb = {k: kernel_stats(recs[pm.handle], k) for k in ("lamb_moments_kernel", "lamb_trust_kernel",
+                                                         "lamb_update_kernel")}
+    lamb_ms = sum(v["mean_ms"] for v in lamb.values())
+    pl.close()
+    pm.close()
+    del A, B, g
+    free(torch)
+    return dict(workload="lion_lamb_fp32_4096x4096", elements=n, ms_per_step=ms,
+                kernels={"lion_fp32": dict(mean_ms=lion["mean_ms"], gbs=gbs(B_LION_F32 * n, lion["mean_ms"]),
+                                           frac=gbs(B_LION_F32 * n, lion["mean_ms"]) / PEAK_HBM_GBS),
+                         "lamb_fp32": dict(ms=lamb_ms, passes={k: v["mean_ms"] for k, v in lamb.items()},
+                                           gbs=gbs(B_ADAMW_F32 * n, lamb_ms),
+                                           frac=gbs(B_ADAMW_F32 * n, lamb_ms) / PEAK_HBM_GBS,
+                                           note="algorithmic 28 B/elem; the two passes move 40 B/elem")},
+                note="back to back on one state each (the state partly stays in the Infinity Cache)")
+
+
+def bench_master(torch, osa, synth, steps, warmup):
+    """AdamW with an fp32 master and a bf16 or fp16 model copy, 4096 x 4096."""
+    wl = synth.c2_decay_stress()
+    n, hp = wl.numel, wl.hp
+    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
+    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
+    out = {}
+    for name, dt in (("adamw_master_bf16", osa.OPTIM_BF16), ("adamw_master_f16", osa.OPTIM_F16)):
+        master = p0.clone()
+        model = torch.zeros(n, dtype=torch.int16, device="cuda")
+        m = torch.zeros(n, device="cuda")
+        v = torch.zeros(n, device="cuda")
+        plan = osa.Plan(osa.TensorList([model], [g], m=[m], v=[v], master=[master], weight_decay=[hp.wd],
+                                       param_dtype=dt), osa.OPTIM_ALGO_ADAMW)
+        sc = scalars(torch, hp.lr)
+        h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
+        _, _, recs, _ = run_timed(torch, [lambda: osa.optim_step_adamw(plan.handle, h, sc["lr"], None, None, sc["step"])],
+                               steps, warmup, plans=[plan.handle], trace_cap=2 * steps)
+        st = kernel_stats(recs[plan.handle])
+        plan.close()
+        out[name] = dict(mean_ms=st["mean_ms"], bytes_per_element=B_ADAMW_MASTER,
+                         gbs=gbs(B_ADAMW_MASTER * n, st["mean_ms"]),
+                         frac=gbs(B_ADAMW_MASTER * n, st["mean_ms"]) / PEAK_HBM_GBS)
+        del master, model, m, v
+    del p0, g
+    free(torch)
+    return dict(workload="adamw_master_copy_4096x4096", elements=n, kernels=out)
+
+
+def bench_states16(torch, osa, synth, steps, warmup):
+    """AdamW with fp16 or bf16 moments and per-tensor scales, 4096 x 4096;
+    frac on the algorithmic 20 B/element (the two-pass fp16 step moves 28)."""
+    wl = synth.c2_decay_stress()
+    n, hp = wl.numel, wl.hp
+    p0 = synth.initial_param_device(wl.tensors[0], wl.p_std, wl.index, 0, "cuda")
+    g = synth.device_normal(n, wl.g_std, "cuda", wl.index, 0, 1, synth.GRAD)
+    out = {}
+    for name, sdt in (("adamw_states_f16", osa.OPTIM_F16), ("adamw_states_bf16", osa.OPTIM_BF16)):
+        p = p0.clone()
+        m = torch.zeros(n, dtype=torch.int16, device="cuda")
+        v = torch.zeros(n, dtype=torch.int16, device="cuda")
+        sm, sv = torch.ones(1, device="cuda"), torch.ones(1, device="cuda")
+        plan = osa.Plan(osa.TensorList([p], [g], m=[m], v=[v], scale_m=[sm], scale_v=[sv], weight_decay=[hp.wd]),
+                        osa.OPTIM_ALGO_ADAMW, state_dtype=sdt)
+        sc = scalars(torch, hp.lr)
+        h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
+        ms, _, recs, _ = run_timed(torch, [lambda: osa.optim_step_adamw(plan.handle, h, sc["lr"], None, None,
+                                                                     sc["step"])],
+                                steps, warmup, plans=[plan.handle], trace_cap=4 * steps)
+        kt = kernel_stats(recs[plan.handle])["total_ms"] / steps
+        plan.close()
+        moved = T_ADAMW_STATES16 if sdt == osa.OPTIM_F16 else B_ADAMW_STATES16
+        out[name] = dict(kernel_ms_per_step=kt, bytes_per_element=B_ADAMW_STATES16, moved_per_element=moved,
+                         gbs=gbs(B_ADAMW_STATES16 * n, kt), frac=gbs(B_ADAMW_STATES16 * n, kt) / PEAK_HBM_GBS)
+        del p, m, v
+    del p0, g
+    free(torch)
+    return dict(workload="adamw_scaled_states_fp32_4096x4096", elements=n, kernels=out)
+
+
+def bench_many(torch, osa, synth, steps, warmup):
+    """16,777,216 AdamW fp32 elements as one tensor, as 4096 tensors of 4096
+    and as 65536 of 256 (views of one allocation per array), four state sets
+    in turn: the cost of the multi-tensor traversal."""
+    n = 1 << 24
+    out = {}
+    for count in (1, 4096, 65536):
+        size = n // count
+        sets = []
+        for k in range(ROTATE):
+            P = torch.randn(n, device="cuda") * 0.02
+            G = torch.randn(n, device="cuda") * 1e-3
+            M = torch.zeros(n, device="cuda")
+            V = torch.zeros(n, device="cuda")
+            views = lambda x: [x[i * size:(i + 1) * size] for i in range(count)]
+            plan = osa.Plan(osa.TensorList(views(P), views(G), m=views(M), v=views(V),
+                                           weight_decay=[0.1] * count), osa.OPTIM_ALGO_ADAMW)
+            sets.append((plan, scalars(torch, 1e-3), (P, G, M, V)))
+        h = osa.optim_adamw_hp(0.9, 0.999, 1e-8)
+        calls = [(lambda pl=pl, s=s: osa.optim_step_adamw(pl.handle, h, s["lr"], None, None, s["step"]))
+                 for pl, s, _ in sets]
+        _, _, recs, _ = run_timed(torch, calls, steps, warmup, plans=[x[0].handle for x in sets], trace_cap=2 * steps)
+        st = kernel_stats([r for v in recs.values() for r in v])
+        out[f"tensors_{count}x{size}"] = dict(mean_ms=st["mean_ms"], gbs=gbs(B_ADAMW_F32 * n, st["mean_ms"]),
+                                              frac=gbs(B_ADAMW_F32 * n, st["mean_ms"]) / PEAK_HBM_GBS)
+        for pl, _, _ in sets:
+            pl.close()
+        del sets
+        free(torch)
+    return dict(workload="adamw_fp32_16M_as_many_tensors", elements=n, rotate=ROTATE, lists=out)
 
 
 # --------------------------------------------------------------------------
 def cpu_baseline(synth, target_s):
-    """The CPU oracle (scalar C, fp64, as it stands) on row slices of the
-    headline tensor: AdamW + AdEMAMix, same hyperparameters.  First one
-    thread on 256 rows for about half the time budget, then one thread per
-    host core, each on its own 256 rows (the oracle's calls release the
-    interpreter lock), for the same number of steps.  `value` is the
-    all-cores rate; the single-thread rate is reported beside it."""
+    """The CPU oracle (scalar C, fp64, as it stands) on a sample of the 7B
+    Adam-mini list, per thread: two q-projection head blocks (2 x 524,288
+    elements, shared v per block), a 1,048,576-element slice of a w1 matrix
+    as one shared-v block, one norm (4096, no decay) and a 1,048,576-element
+    slice of the embedding (full v), same hyperparameters and distributions.
+    First one thread for about half the time budget, then one thread per
+    host core (each on its own sample) for the same number of steps; `value`
+    is the all-cores rate in element updates per second."""
     import threading
 
     import numpy as np
     import oracle
-    wl = synth.c2_decay_stress()
+    wl = synth.c5_adam_mini_7b()
     hp = wl.hp
-    rows = 256
-    n = rows * 4096
+    head = wl.extra["dim"] * wl.extra["dim"] // wl.extra["n_heads"]
+    parts = [("head", 2 * head, head, hp.wd, False), ("scalar", 1 << 20, 1 << 20, hp.wd, False),
+             ("norm", 4096, 4096, 0.0, True), ("full", 1 << 20, 1, hp.wd, False)]
+    per_step = sum(p[1] for p in parts)
 
     def state(chunk):
-        p0 = synth.host_normal(n, wl.p_std, wl.index, 0, chunk, synth.P0).astype(np.float64)
-        g = synth.host_normal(n, wl.g_std, wl.index, 0, chunk, synth.GRAD).astype(np.float64)
-        return dict(g=g, a=(p0.copy(), np.zeros(n), np.zeros(n)),
-                    b=(p0.copy(), np.zeros(n), np.zeros(n), np.zeros(n)))
+        st = []
+        for j, (_, n, block, wd, is_norm) in enumerate(parts):
+            p0 = (np.ones(n) if is_norm else
+                  synth.host_normal(n, wl.p_std, wl.index, 100 + chunk, j, synth.P0).astype(np.float64))
+            g = synth.host_normal(n, wl.g_std, wl.index, 100 + chunk, j, synth.GRAD).astype(np.float64)
+            v = np.zeros(n if block == 1 else n // block)
+            st.append((p0, np.zeros(n), v, g, block, wd))
+        return st
 
     def one_step(st, t):
-        pa, ma, va = st["a"]
-        pb, m1, m2, nu = st["b"]
-        oracle.adamw_step(pa, ma, va, st["g"], hp.lr, hp.beta1, hp.beta2, hp.eps, hp.wd, t)
-        oracle.ademamix_step(pb, m1, m2, nu, st["g"], hp.lr, hp.beta1, hp.beta2, wl.extra["beta3"],
-                             wl.extra["alpha"], hp.eps, hp.wd, t)
+        for p, m, v, g, block, wd in st:
+            if block == 1:
+                oracle.adamw_step(p, m, v, g, hp.lr, hp.beta1, hp.beta2, hp.eps, wd, t)
+            else:
+                oracle.adam_mini_step(p, m, v, g, block, hp.lr, hp.beta1, hp.beta2, hp.eps, wd, t)
 
     st0 = state(0)
     steps, spent = 0, 0.0
@@ -607,7 +765,7 @@ def cpu_baseline(synth, target_s):
         one_step(st0, steps + 1)
         spent += time.perf_counter() - t0
         steps += 1
-    single = 2 * n * steps / spent
+    single = per_step * steps / spent
     cores = max(1, min(os.cpu_count() or 1, 16))
     states = [state(1 + c) for c in range(cores)]
 
@@ -622,65 +780,12 @@ def cpu_baseline(synth, target_s):
     for th in threads:
         th.join()
     wall = time.perf_counter() - t0
-    return dict(value=2 * n * steps * cores / wall, unit="elements/s", cores=cores, kind="oracle",
+    return dict(value=per_step * steps * cores / wall, unit="elements/s", cores=cores, kind="oracle",
                 single_thread_value=single,
-                sample=f"{rows}x4096 rows of the 4096x4096 tensor per thread, AdamW + AdEMAMix, {steps} steps: "
-                       f"1 thread {spent:.1f} s, then {cores} threads {wall:.1f} s "
+                sample=f"per thread {per_step} elements of the 7B Adam-mini list (2 q head blocks of {head}, "
+                       f"a 1M slice of w1 as one shared-v block, a 4096 norm, a 1M embedding slice with full v), "
+                       f"{steps} steps: 1 thread {spent:.1f} s, then {cores} threads {wall:.1f} s "
                        f"({os.cpu_count()} host cores visible)")
-
-
-KERNEL_SOURCES = {  # kernel -> sources its device code comes from
-    "adamw_fp32": ("device_common.h", "kernels_adam.hip"),
-    "ademamix_fp32": ("device_common.h", "kernels_adam.hip"),
-    "blockwise_8bit": ("device_common.h", "kernels_blockwise.hip"),
-    "blockwise_8bit_interleaved": ("device_common.h", "kernels_blockwise.hip"),
-    "blockwise_4bit": ("device_common.h", "kernels_blockwise.hip"),
-    "blockwise_4bit_interleaved": ("device_common.h", "kernels_blockwise.hip"),
-    "blockwise_ademamix_8bit": ("device_common.h", "kernels_blockwise.hip"),
-    "blockwise_ademamix_4bit": ("device_common.h", "kernels_blockwise.hip"),
-}
-
-
-def kernel_sources_sha256(kernel_key):
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel_key]:
-        with open(os.path.join(ROOT, "optimizer_step_adamw_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
-
-
-def traffic_from_profile(kernel_key):
-    """HBM bytes per launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE scaled by a plain copy of known size), valid
-    only while the kernel's sources are the ones the counters were taken on."""
-    path = os.path.join(ROOT, "profiles", f"counters_{kernel_key}.txt")
-    if not os.path.exists(path) or kernel_key not in KERNEL_SOURCES:
-        return None
-    text = open(path).read()
-    m = re.search(r"kernel_sources_sha256:\s*([0-9a-f]{64})", text)
-    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m or not t or m.group(1) != kernel_sources_sha256(kernel_key):
-        return None
-    return float(t.group(1))
-
-
-def copy_probe(torch, nbytes=256 << 20, reps=5):
-    """Plain device-to-device copy of a known size: the streaming ceiling for
-    context, and the known-size kernel that scales the traffic counters."""
-    x = torch.randn(nbytes // 4, device="cuda")
-    y = torch.empty_like(x)
-    y.copy_(x)
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
-        y.copy_(x)
-    b.record()
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
-    del x, y
-    return dict(bytes=2 * nbytes, ms=ms, gbs=2 * nbytes / (ms * 1e-3) / 1e9)
 
 
 def main():
@@ -697,25 +802,48 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     log(f"device: {torch.cuda.get_device_name(0)}")
-    copy = copy_probe(torch)
-    log(f"copy probe: {json.dumps(copy)}")
-    head = bench_headline(torch, osa, synth, args.steps, args.warmup)
-    log(f"headline: {head['ms_per_step']:.4f} ms/step, {head['elements_per_s']:.4e} elem/s, "
-        f"{json.dumps(head['kernels'])}")
-    secondary = {}
-    todo = [] if args.secondary == "none" else args.secondary.split(",")
-    fns = dict(c1=bench_c1, c3=bench_c3, c4=bench_c4, c5=bench_c5, lion_lamb=bench_lion_lamb,
-               master=bench_master, states16=bench_states16, many=bench_many)
+    head = bench_c5(torch, osa, synth, args.steps, args.warmup)
+    log(f"headline c5: {head['ms_per_step']:.3f} ms/step, {head['elements_per_s']:.4e} elem/s, "
+        f"update {head['roofline']['achieved']:.0f} GB/s")
+    todo = [] if args.secondary == "none" else [k for k in args.secondary.split(",") if k]
+    res = {}
+    fns = dict(c2=bench_c2, c3=bench_c3, c4=bench_blockwise, c1=bench_c1, amp=bench_amp,
+               c4x=lambda *a: dict(interleaved=bench_blockwise(*a, interleaved=True),
+                                   ademamix=bench_blockwise(*a, ademamix=True)),
+               lion_lamb=bench_lion_lamb, master=bench_master, states16=bench_states16, many=bench_many)
     for key in todo:
         t0 = time.perf_counter()
-        secondary[key] = fns[key](torch, osa, synth, args.steps, args.warmup)
-        log(f"{key}: {json.dumps(secondary[key])} ({time.perf_counter() - t0:.1f} s)")
-    dom_name = max(head["kernels"], key=lambda k: head["kernels"][k]["ms"])
-    dom = head["kernels"][dom_name]
-    roof = dict(bound="hbm", kernel=dom_name, achieved=dom["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
-                frac=dom["gbs"] / PEAK_HBM_GBS, traffic=traffic_from_profile(dom_name),
-                bytes_per_launch=dom["bytes"], launch_ms=dom["ms"])
+        if key == "probes":
+            res[key] = bench_probes(torch, max(5, args.steps // 2))
+        else:
+            res[key] = fns[key](torch, osa, synth, args.steps, args.warmup)
+        log(f"{key}: {json.dumps(res[key])} ({time.perf_counter() - t0:.1f} s)")
+    ceil = res.get("probes", {})
+    # per-kernel rooflines, each against its access pattern's ceiling
+    roofs = [dict(head["roofline"], ceiling=ceil.get("mini_3r2w_268M"),
+                  frac_of_ceiling=(head["roofline"]["achieved"] / ceil["mini_3r2w_268M"]["gbs"]
+                                   if "mini_3r2w_268M" in ceil else None))]
+    if "c2" in res:
+        c2 = res["c2"]
+        for k, pk in (("adamw_fp32", "adamw_4096x4096"), ("ademamix_fp32", "ademamix_4096x4096")):
+            e = c2["kernels"][k]
+            roofs.append(roofline_entry("adam_kernel", f"{k}_4096x4096", e["bytes"], e["stats"], ceil.get(pk),
+                                        traffic_from_profile(k),
+                                        note=f"{ROTATE} state sets taken in turn (none stays in the Infinity Cache)"))
+    if "c3" in res:
+        for k, pk in (("adamw_bf16_remainder", "bf16r_268M"), ("check_finite_bf16", "read_bf16_268M")):
+            e = res["c3"]["kernels"][k]
+            roofs.append(roofline_entry("adam_kernel" if k.startswith("adamw") else "finite_kernel",
+                                        f"{k}_llama1b", e["bytes"], e["stats"], ceil.get(pk),
+                                        traffic_from_profile(k)))
+    if "c4" in res:
+        for k, pk in (("blockwise_8bit", "blockwise_8bit_268M"), ("blockwise_4bit", "blockwise_4bit_268M")):
+            e = res["c4"]["kernels"][k]
+            roofs.append(roofline_entry("blockwise_kernel", f"{k}_268M", e["bytes"], e["stats"], ceil.get(pk),
+                                        traffic_from_profile(k)))
+    roof = roofs[0]
     cpu = cpu_baseline(synth, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    wl_c5 = synth.c5_adam_mini_7b()
     out = {
         "metric": METRIC,
         "value": head["elements_per_s"],
@@ -729,14 +857,16 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": head["workload"], "elements": head["elements"],
-                   "optimizers": ["adamw", "ademamix"], "lr": 0.1, "weight_decay": 0.1,
-                   "betas": [0.9, 0.999], "beta3": 0.9999, "alpha": 5.0},
+        "config": {"workload": head["workload"], "elements": head["elements"], "tensors": len(wl_c5.tensors),
+                   "optimizer": "adam_mini", "lr": wl_c5.hp.lr, "betas": [wl_c5.hp.beta1, wl_c5.hp.beta2],
+                   "eps": wl_c5.hp.eps, "weight_decay": wl_c5.hp.wd, "layers": 32, "dim": 4096, "n_heads": 32,
+                   "ffn": 11008, "vocab": 32000},
         "roofline": roof,
+        "rooflines": roofs,
         "cpu_baseline": cpu,
-        "kernels": head["kernels"],
-        "copy_ceiling": copy,
-        "secondary": secondary,
+        "headline": head,
+        "ceilings": ceil,
+        "secondary": {k: v for k, v in res.items() if k != "probes"},
         "environment": environment(torch),
     }
     print(json.dumps(out), flush=True)

@@ -230,6 +230,35 @@ int optim_plan_create_static(const optim_tensor_list *list, int32_t algo,
                              const optim_plan_opts *opts, void *stream,
                              optim_plan **out);
 
+/* ---- kernel trace (measurement) -----------------------------------------
+ * The device duration of every kernel a plan's calls launch, for measuring
+ * a step kernel by kernel (the multi-kernel steps -- Adam-mini's block sums,
+ * finalize and update per segment, LAMB's passes, the gradient norm's
+ * stages -- are otherwise timed only as a whole).
+ * optim_plan_trace(plan, capacity > 0): from now on each of the next
+ * `capacity` kernel launches of the plan's step, check and norm calls
+ * carries a pair of HIP events that the kernel's own dispatch stamps at its
+ * start and end (hipExtLaunchKernel); nothing else is added to the stream.
+ * Launches beyond the capacity run untraced and are counted.  Creates
+ * 2*capacity HIP events (host resources, no device memory); not meant for
+ * graph capture.  capacity 0 ends the trace and frees the events (also done
+ * by optim_plan_destroy); a new call restarts it.
+ * optim_plan_trace_read: blocks the host until the traced launches have
+ * finished (the one other blocking call, with optim_plan_create), writes
+ * min(count, max) records in launch order to out[], the number of traced
+ * launches to *count and of untraced ones to *dropped (may be NULL), and
+ * empties the trace for the next launches.  kernel names are the kernels'
+ * function names, valid until the trace is freed.                          */
+typedef struct optim_kernel_time {
+    const char *kernel;   /* e.g. "mini_update_kernel"                      */
+    int64_t workgroups;   /* grid size of the launch                        */
+    double ms;            /* from the kernel's start to its end             */
+} optim_kernel_time;
+
+int optim_plan_trace(optim_plan *plan, int32_t capacity);
+int optim_plan_trace_read(optim_plan *plan, optim_kernel_time *out,
+                          int32_t max, int32_t *count, int64_t *dropped);
+
 /* Device learning-rate schedule ([AO]: the lr changes every step and must
  * stay a device scalar updated in place, with no per-step allocation).
  * OPTIM_SCHED_COSINE: at each step call the library reads k = *iter_dev,

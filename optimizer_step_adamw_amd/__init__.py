@@ -31,7 +31,7 @@ EXPORTED = (
     "optim_remainder_reconstruct", "optim_quant_codebook", "optim_quantize_blockwise",
     "optim_dequantize_blockwise", "optim_grad_norm", "optim_scaler_update",
     "optim_step_8bit_blockwise_ademamix", "optim_step_lion", "optim_step_lamb",
-    "optim_plan_create_static",
+    "optim_plan_create_static", "optim_plan_trace", "optim_plan_trace_read",
 )
 # bytes of the library's static per-device workspace (optim_plan_create_static)
 OPTIM_STATIC_WORKSPACE_BYTES = 16 << 20
@@ -68,6 +68,10 @@ class optim_plan_opts(ctypes.Structure):
                 ("state_layout", ctypes.c_int32)]
 
 
+class optim_kernel_time(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p), ("workgroups", ctypes.c_int64), ("ms", ctypes.c_double)]
+
+
 class optim_adamw_hp(ctypes.Structure):
     _fields_ = [("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("eps", ctypes.c_double)]
 
@@ -102,6 +106,9 @@ def lib() -> ctypes.CDLL:
             "optim_plan_create": ([tl, i32, opts, _P, sz, _P, ctypes.POINTER(_P)], i32),
             "optim_plan_destroy": ([_P], i32),
             "optim_plan_create_static": ([tl, i32, opts, _P, ctypes.POINTER(_P)], i32),
+            "optim_plan_trace": ([_P, i32], i32),
+            "optim_plan_trace_read": ([_P, ctypes.POINTER(optim_kernel_time), i32, ctypes.POINTER(i32),
+                                       ctypes.POINTER(i64)], i32),
             "optim_plan_set_schedule": ([_P, i32, f64, f64, i32, _P], i32),
             "optim_step_adamw": ([_P, ctypes.POINTER(optim_adamw_hp), _P, _P, _P, _P, _P], i32),
             "optim_step_ademamix": ([_P, ctypes.POINTER(optim_ademamix_hp), _P, _P, _P, _P, _P], i32),
@@ -216,6 +223,22 @@ def optim_plan_create_static(tl: TensorList, algo: int, opts, stream=None) -> in
                                           _stream(stream), ctypes.byref(h)),
            "optim_plan_create_static")
     return h.value
+
+
+def optim_plan_trace(plan: int, capacity: int) -> None:
+    _check(lib().optim_plan_trace(plan, int(capacity)), "optim_plan_trace")
+
+
+def optim_plan_trace_read(plan: int, max_records: int = 1 << 16):
+    """(records, dropped): records are (kernel name, workgroups, ms) in launch
+    order; waits for the traced launches to finish and empties the trace."""
+    buf = (optim_kernel_time * max(1, max_records))()
+    n = ctypes.c_int32(0)
+    dropped = ctypes.c_int64(0)
+    _check(lib().optim_plan_trace_read(plan, buf, max_records, ctypes.byref(n), ctypes.byref(dropped)),
+           "optim_plan_trace_read")
+    recs = [(buf[i].kernel.decode(), int(buf[i].workgroups), float(buf[i].ms)) for i in range(min(n.value, max_records))]
+    return recs, int(dropped.value)
 
 
 def optim_plan_destroy(plan: int) -> None:

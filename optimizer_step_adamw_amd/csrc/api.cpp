@@ -16,6 +16,23 @@
 
 using namespace optim;
 
+namespace optim {
+thread_local Trace *g_trace = nullptr;
+
+TraceRec *trace_slot(const char *name, int64_t grid) {
+    Trace *t = g_trace;
+    if (!t) return nullptr;
+    if (t->used >= t->recs.size()) {
+        ++t->dropped;
+        return nullptr;
+    }
+    TraceRec &r = t->recs[t->used++];
+    r.name = name;
+    r.grid = grid;
+    return &r;
+}
+}  // namespace optim
+
 namespace {
 
 thread_local std::string g_err;
@@ -473,6 +490,7 @@ struct optim_plan {
     // (0 for a plan on a caller's workspace)
     int32_t static_dev;
     uint64_t static_gen;
+    Trace *trace;  // kernel trace (optim_plan_trace), or NULL
 };
 
 extern "C" {
@@ -539,6 +557,37 @@ int check_live(const optim_plan *P, const char *fn) {
                                       "on its device (the static workspace holds one plan at a time)");
     return OPTIM_OK;
 }
+
+// ---------------------------------------------------------------- kernel trace
+void free_trace(optim_plan *P) {
+    if (!P->trace) return;
+    for (TraceRec &r : P->trace->recs) {
+        if (r.start) (void)hipEventDestroy(r.start);
+        if (r.stop) (void)hipEventDestroy(r.stop);
+    }
+    delete P->trace;
+    P->trace = nullptr;
+}
+
+// "(mini_update_kernel<PK, GK>)" -> "mini_update_kernel"; kept in the trace
+// so the returned pointers live until the trace is freed.
+const char *clean_name(Trace *t, const char *raw) {
+    for (const auto &kv : t->names)
+        if (kv.first == raw) return kv.second.c_str();
+    std::string s(raw ? raw : "");
+    s.erase(std::remove(s.begin(), s.end(), '('), s.end());
+    const size_t lt = s.find('<');
+    if (lt != std::string::npos) s.resize(lt);
+    while (!s.empty() && (s.back() == ')' || s.back() == ' ')) s.pop_back();
+    t->names.emplace_back(raw, s);
+    return t->names.back().second.c_str();
+}
+
+// Points the launches of one entry point at its plan's trace.
+struct TraceScope {
+    explicit TraceScope(const optim_plan *P) { g_trace = P ? P->trace : nullptr; }
+    ~TraceScope() { g_trace = nullptr; }
+};
 
 // Plan creation on a given workspace (the caller's, or the static one).
 int create_on(const Built &B, const optim_tensor_list *list, int32_t algo, const optim_plan_opts *opts,
@@ -638,7 +687,56 @@ int optim_plan_create_static(const optim_tensor_list *list, int32_t algo, const 
 }
 
 int optim_plan_destroy(optim_plan *plan) {
+    if (plan) free_trace(plan);
     delete plan;
+    return OPTIM_OK;
+}
+
+int optim_plan_trace(optim_plan *plan, int32_t capacity) {
+    if (!plan) return fail(OPTIM_EINVAL, "plan is NULL");
+    if (capacity < 0) return fail(OPTIM_EINVAL, "negative trace capacity");
+    free_trace(plan);
+    if (capacity == 0) return OPTIM_OK;
+    Trace *t = new (std::nothrow) Trace{};
+    if (!t) return fail(OPTIM_EINVAL, "out of host memory");
+    t->recs.reserve((size_t)capacity);
+    for (int32_t i = 0; i < capacity; ++i) {
+        TraceRec r{nullptr, 0, nullptr, nullptr};
+        hipError_t e = hipEventCreate(&r.start);
+        if (e == hipSuccess) {
+            e = hipEventCreate(&r.stop);
+            if (e != hipSuccess) (void)hipEventDestroy(r.start);
+        }
+        if (e != hipSuccess) {
+            plan->trace = t;
+            free_trace(plan);
+            return fail(OPTIM_EHIP, std::string("hipEventCreate: ") + hipGetErrorString(e));
+        }
+        t->recs.push_back(r);
+    }
+    plan->trace = t;
+    return OPTIM_OK;
+}
+
+int optim_plan_trace_read(optim_plan *plan, optim_kernel_time *out, int32_t max, int32_t *count,
+                          int64_t *dropped) {
+    if (!plan || !count) return fail(OPTIM_EINVAL, "plan and count are required");
+    if (max < 0 || (max > 0 && !out)) return fail(OPTIM_EINVAL, "need out[max], max >= 0");
+    Trace *t = plan->trace;
+    if (!t) return fail(OPTIM_EINVAL, "the plan has no trace (optim_plan_trace)");
+    const size_t n = t->used;
+    t->used = 0;
+    const int64_t lost = t->dropped;
+    t->dropped = 0;
+    for (size_t i = 0; i < n; ++i) {
+        const TraceRec &r = t->recs[i];
+        HIP_OK(hipEventSynchronize(r.stop));
+        float ms = 0.0f;
+        HIP_OK(hipEventElapsedTime(&ms, r.start, r.stop));
+        if ((int64_t)i < (int64_t)max) out[i] = optim_kernel_time{clean_name(t, r.name), r.grid, (double)ms};
+    }
+    *count = (int32_t)n;
+    if (dropped) *dropped = lost;
     return OPTIM_OK;
 }
 
@@ -763,6 +861,7 @@ int optim_step_adamw(optim_plan *plan, const optim_adamw_hp *hp, float *lr_dev, 
     rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
                      step_dev, a);
     if (rc) return rc;
+    const TraceScope ts(plan);
     if (plan->state_dtype != OPTIM_F32)
         HIP_OK(launch_adamw_scaled(a, plan->pk, plan->gk, plan->state_dtype == OPTIM_F16 ? S_F16 : S_BF16,
                                    static_cast<hipStream_t>(stream)));
@@ -781,6 +880,7 @@ int optim_step_ademamix(optim_plan *plan, const optim_ademamix_hp *hp, float *lr
     rc = step_inputs(plan, hp->beta1, hp->beta2, hp->beta3, hp->alpha, hp->eps, lr_dev, inv_scale_dev,
                      found_inf_dev, step_dev, a);
     if (rc) return rc;
+    const TraceScope ts(plan);
     HIP_OK(launch_ademamix(a, plan->pk, plan->gk, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
@@ -794,6 +894,7 @@ int optim_step_adam_mini(optim_plan *plan, const optim_adamw_hp *hp, float *lr_d
     rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
                      step_dev, a);
     if (rc) return rc;
+    const TraceScope ts(plan);
     HIP_OK(launch_adam_mini(a, plan->pk, plan->gk, plan->segs.data(), (int32_t)plan->segs.size(),
                             static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
@@ -808,6 +909,7 @@ int optim_step_lion(optim_plan *plan, const optim_lion_hp *hp, float *lr_dev, co
     StepArgs a;
     rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, 0.0, lr_dev, inv_scale_dev, found_inf_dev, step_dev, a);
     if (rc) return rc;
+    const TraceScope ts(plan);
     HIP_OK(launch_lion(a, plan->pk, plan->gk, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
@@ -821,6 +923,7 @@ int optim_step_lamb(optim_plan *plan, const optim_adamw_hp *hp, float *lr_dev, c
     rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
                      step_dev, a);
     if (rc) return rc;
+    const TraceScope ts(plan);
     HIP_OK(launch_lamb(a, plan->pk, plan->gk, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
@@ -837,6 +940,7 @@ int optim_step_8bit_blockwise(optim_plan *plan, const optim_adamw_hp *hp, int32_
     rc = step_inputs(plan, hp->beta1, hp->beta2, 0.0, 0.0, hp->eps, lr_dev, inv_scale_dev, found_inf_dev,
                      step_dev, a);
     if (rc) return rc;
+    const TraceScope ts(plan);
     HIP_OK(launch_blockwise(a, plan->gk, false, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
@@ -853,6 +957,7 @@ int optim_step_8bit_blockwise_ademamix(optim_plan *plan, const optim_ademamix_hp
     rc = step_inputs(plan, hp->beta1, hp->beta2, hp->beta3, hp->alpha, hp->eps, lr_dev, inv_scale_dev,
                      found_inf_dev, step_dev, a);
     if (rc) return rc;
+    const TraceScope ts(plan);
     HIP_OK(launch_blockwise(a, plan->gk, true, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
@@ -866,6 +971,7 @@ int optim_check_finite(optim_plan *plan, float *found_inf_dev, void *stream) {
     StepArgs a = step_args(plan);
     a.commit = 0;
     a.found_inf = found_inf_dev;
+    const TraceScope ts(plan);
     HIP_OK(launch_check_finite(a, plan->gk, static_cast<hipStream_t>(stream)));
     return OPTIM_OK;
 }
@@ -883,6 +989,7 @@ int optim_grad_norm(optim_plan *plan, const float *inv_scale_dev, double max_nor
     StepArgs a = step_args(plan);
     a.commit = 0;
     a.found_inf = found_inf_dev;
+    const TraceScope ts(plan);
     HIP_OK(launch_grad_norm(a, plan->gk, inv_scale_dev, max_norm, norm_dev, clip_inv_scale_dev,
                             static_cast<hipStream_t>(stream)));
     return OPTIM_OK;

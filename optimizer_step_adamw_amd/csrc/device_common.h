@@ -29,6 +29,7 @@
 
 #include "plan.h"
 
+#include <hip/hip_ext.h>
 #include <hip/hip_fp16.h>
 #include <math.h>
 
@@ -560,8 +561,18 @@ inline bool keep_for_second_pass(const StepArgs &a, int64_t reread_bytes_per_ele
     return a.grid_request == 0 && (a.nunits - a.unit0) * a.tile * reread_bytes_per_elem <= limit;
 }
 
-#define LAUNCH_PERSISTENT(K, a, s)                                                     \
-    hipLaunchKernelGGL(K, dim3(persistent_grid(K, a)), dim3(kThreads), 0, s, a)
+// Launch of kernel K over `grid` workgroups of `block` lanes; under a plan
+// trace the kernel's own start and end stamp the trace's next event pair.
+#define LAUNCH_TRACED(K, grid, block, s, ...)                                                      \
+    do {                                                                                           \
+        TraceRec *tr_ = trace_slot(#K, (int64_t)(grid));                                           \
+        if (tr_)                                                                                   \
+            hipExtLaunchKernelGGL(K, dim3(grid), dim3(block), 0, s, tr_->start, tr_->stop, 0, __VA_ARGS__); \
+        else                                                                                       \
+            hipLaunchKernelGGL(K, dim3(grid), dim3(block), 0, s, __VA_ARGS__);                    \
+    } while (0)
+
+#define LAUNCH_PERSISTENT(K, a, s) LAUNCH_TRACED(K, persistent_grid(K, a), kThreads, s, a)
 
 }  // namespace
 }  // namespace optim

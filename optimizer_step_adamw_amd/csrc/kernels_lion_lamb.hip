@@ -251,7 +251,7 @@ hipError_t launch_lamb_t(const StepArgs &args, hipStream_t s) {
     if (e != hipSuccess) return e;
     if (a.nblocks > 0) {
         const int fg = a.nblocks < 2048 ? a.nblocks : 2048;
-        hipLaunchKernelGGL(lamb_trust_kernel, dim3(fg), dim3(kThreads), 0, s, a);
+        LAUNCH_TRACED(lamb_trust_kernel, fg, kThreads, s, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

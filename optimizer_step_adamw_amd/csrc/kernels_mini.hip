@@ -180,7 +180,7 @@ hipError_t launch_adam_mini(const StepArgs &args, int pk, int gk, const MiniSegm
             a.block0 = sg.block_begin;
             a.nblocks = sg.block_end;
             const int nb = sg.block_end - sg.block_begin;
-            hipLaunchKernelGGL(mini_finalize_kernel, dim3(nb < 2048 ? nb : 2048), dim3(kThreads), 0, s, a);
+            LAUNCH_TRACED(mini_finalize_kernel, nb < 2048 ? nb : 2048, kThreads, s, a);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

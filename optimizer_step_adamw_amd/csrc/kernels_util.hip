@@ -227,10 +227,10 @@ hipError_t launch_grad_norm(const StepArgs &args, int gk, const float *inv_scale
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     double *partials2 = a.partials + grid;
-    hipLaunchKernelGGL(norm_stage1_kernel, dim3((unsigned)grid1), dim3(kThreads), 0, s, a.partials, grid, partials2);
+    LAUNCH_TRACED(norm_stage1_kernel, (unsigned)grid1, kThreads, s, a.partials, grid, partials2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(norm_finalize_kernel, dim3(1), dim3(kThreads), 0, s, partials2, grid1, inv_scale, max_norm,
+    LAUNCH_TRACED(norm_finalize_kernel, 1, kThreads, s, partials2, grid1, inv_scale, max_norm,
                        norm_out, clip_out);
     return hipGetLastError();
 }

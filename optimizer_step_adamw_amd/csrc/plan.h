@@ -5,6 +5,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <deque>
+#include <string>
+#include <utility>
+#include <vector>
+
 namespace optim {
 
 // Work decomposition: every tensor (Adam-mini: every shared-v block) is a
@@ -187,6 +192,26 @@ struct StepArgs {
     int32_t units_per_wg;     // without a persistent grid: consecutive units
                               // per workgroup (set by the launcher)
 };
+
+// Kernel trace of a plan (optim_plan_trace): while one of a traced plan's
+// entry points runs, g_trace points at its trace and every launch takes the
+// next start / stop event pair, which the kernel's dispatch stamps itself
+// (hipExtLaunchKernel); nothing is added to the stream.
+struct TraceRec {
+    const char *name;  // the launch site's kernel expression (a literal)
+    int64_t grid;      // workgroups
+    hipEvent_t start, stop;
+};
+struct Trace {
+    std::vector<TraceRec> recs;  // capacity: one pair per launch
+    size_t used = 0;
+    int64_t dropped = 0;         // launches after the trace was full
+    std::deque<std::pair<const char *, std::string>> names;  // cleaned names (stable addresses)
+};
+extern thread_local Trace *g_trace;
+// The event pair for the next launch of `name` over `grid` workgroups, or
+// nullptr (no trace, or the trace is full).
+TraceRec *trace_slot(const char *name, int64_t grid);
 
 // Launchers (kernels_*.hip).  Return the hipError_t of the launch.  Step
 // launchers always start at least one workgroup (the commit must run even

@@ -1,0 +1,66 @@
+"""Access-pattern ceiling probes for the benchmark (stream_probe.hip).
+
+Benchmark-only: a separate library, not part of liboptim_step.so's C ABI.
+Each probe streams one step kernel's exact access pattern (arrays, lane
+layout, unit size, access kind) with no arithmetic; bench.py reports each
+kernel's bandwidth as a fraction of its pattern's measured ceiling.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "stream_probe.hip")
+LIB_PATH = os.path.join(HERE, "libstream_probe.so")
+ARCH = os.environ.get("OPTIM_STEP_ARCH", "gfx950")
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc",
+           f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Wall", "-Wno-unused-command-line-argument", "-o", tmp, SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with probes.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        sigs = {
+            "probe_adamw": [P, P, P, P, i64, i32, P],
+            "probe_ademamix": [P, P, P, P, P, i64, i32, P],
+            "probe_mini": [P, P, P, i64, P],
+            "probe_bf16r": [P, P, P, P, P, i64, P],
+            "probe_blockwise": [P, P, P, P, P, P, i64, i32, i32, P],
+            "probe_read": [P, i64, i32, P, P],
+            "probe_copy": [P, P, i64, P],
+        }
+        for name, args in sigs.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def call(name: str, *args) -> None:
+    """Calls a probe (tensors become device pointers; the stream is torch's
+    current one) and raises on a launch error."""
+    import torch
+    conv = [a.data_ptr() if hasattr(a, "data_ptr") else a for a in args]
+    rc = getattr(lib(), name)(*conv, torch.cuda.current_stream().cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"{name}: hipError {rc}")
