@@ -120,6 +120,10 @@ struct Built {
     int32_t nblocks = 0;
     std::vector<MiniSegment> segs;  // Adam-mini launch segments
     bool interleaved = false;       // blockwise: interleaved state layout
+    std::vector<PackDesc> packs;    // packs of small tensors
+    std::vector<int32_t> pack_off;
+    std::vector<TensorDesc> pack_td;
+    int64_t pack_unit0 = 0;         // first pack unit (packs come last)
     Layout L{};
 };
 
@@ -245,6 +249,38 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     B.nunits = 0;
     B.nblocks = 0;
     B.segs.clear();
+    B.packs.clear();
+    B.pack_off.clear();
+    B.pack_td.clear();
+    // Packs: AdamW / AdEMAMix (fp32 moments) and Lion plans lay runs of
+    // tensors of at most half a unit end to end in shared units, so a
+    // workgroup serves many small tensors (one prologue, every lane busy)
+    // instead of one each.
+    const bool packable = (algo == OPTIM_ALGO_ADAMW || algo == OPTIM_ALGO_ADEMAMIX || algo == OPTIM_ALGO_LION) &&
+                          !states16;
+    std::vector<int32_t> open_pack;  // members of the pack being filled
+    int64_t open_len = 0;
+    auto close_pack = [&]() {
+        if (open_pack.empty()) return;
+        if (open_pack.size() == 1) {  // a lone member: an ordinary span
+            const int32_t t = open_pack[0];
+            B.spans.push_back(SpanDesc{B.nunits, 0, B.tensors[t].numel, t, -1});
+        } else {
+            PackDesc P{(int32_t)B.pack_td.size(), (int32_t)B.pack_off.size(), (int32_t)open_pack.size(),
+                       (int32_t)open_len};
+            int32_t off = 0;
+            for (int32_t t : open_pack) {
+                B.pack_td.push_back(B.tensors[t]);
+                B.pack_off.push_back(off);
+                off += (int32_t)((B.tensors[t].numel + 3) / 4 * 4);
+            }
+            B.pack_off.push_back(off);
+            B.packs.push_back(P);  // its span is laid after all single-tensor units
+        }
+        if (open_pack.size() == 1) B.nunits += 1;
+        open_pack.clear();
+        open_len = 0;
+    };
     for (int i = 0; i < n; ++i) {
         const std::string ti = "tensor " + std::to_string(i) + ": ";
         TensorDesc &T = B.tensors[i];
@@ -398,7 +434,13 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
             B.spans.push_back(SpanDesc{B.nunits, 0, numel, i, B.nblocks});
             B.nunits += (numel + tile - 1) / tile;
             ++B.nblocks;
+        } else if (packable && numel <= tile / 2) {
+            const int64_t r = (numel + 3) / 4 * 4;
+            if (open_len + r > tile || (int32_t)open_pack.size() >= kMaxPackTensors) close_pack();
+            open_pack.push_back(i);
+            open_len += r;
         } else {
+            close_pack();
             B.spans.push_back(SpanDesc{B.nunits, 0, numel, i, -1});
             B.nunits += (numel + tile - 1) / tile;
         }
@@ -419,7 +461,14 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
             }
         }
     }
-    if (B.spans.size() >= (size_t)INT32_MAX) return fail(OPTIM_EUNSUPPORTED, "too many spans");
+    close_pack();
+    B.pack_unit0 = B.nunits;
+    for (size_t k = 0; k < B.packs.size(); ++k) {
+        B.spans.push_back(SpanDesc{B.nunits, (int64_t)k, B.packs[k].len, kPackTensor, -1});
+        B.nunits += 1;
+    }
+    if (B.spans.size() >= (size_t)INT32_MAX || B.pack_off.size() >= (size_t)INT32_MAX)
+        return fail(OPTIM_EUNSUPPORTED, "too many spans");
     B.spans.push_back(SpanDesc{B.nunits, 0, 0, -1, -1});  // sentinel
 
     // no written buffer may overlap any other buffer of the plan
@@ -446,6 +495,9 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     L.spans = off; off += align256(B.spans.size() * sizeof(SpanDesc));
     L.codebook = off; off += is_blockwise(algo) ? align256(sizeof(Codebook)) : 0;
     L.blockspan = off; off += align256(std::max<size_t>(1, B.blockspan.size()) * sizeof(int32_t));
+    L.packs = off; off += align256(B.packs.size() * sizeof(PackDesc));
+    L.pack_off = off; off += align256(B.pack_off.size() * sizeof(int32_t));
+    L.pack_td = off; off += align256(B.pack_td.size() * sizeof(TensorDesc));
     // partial sums: Adam-mini's block sums (one per unit) and the gradient
     // norm pass (one per workgroup) share the region; they never overlap in
     // stream order
@@ -491,6 +543,7 @@ struct optim_plan {
     int32_t static_dev;
     uint64_t static_gen;
     Trace *trace;  // kernel trace (optim_plan_trace), or NULL
+    int64_t pack_unit0;  // first pack unit
 };
 
 extern "C" {
@@ -599,6 +652,9 @@ int create_on(const Built &B, const optim_tensor_list *list, int32_t algo, const
     std::memcpy(img.data() + B.L.tensors, B.tensors.data(), B.tensors.size() * sizeof(TensorDesc));
     std::memcpy(img.data() + B.L.spans, B.spans.data(), B.spans.size() * sizeof(SpanDesc));
     std::memcpy(img.data() + B.L.blockspan, B.blockspan.data(), B.blockspan.size() * sizeof(int32_t));
+    std::memcpy(img.data() + B.L.packs, B.packs.data(), B.packs.size() * sizeof(PackDesc));
+    std::memcpy(img.data() + B.L.pack_off, B.pack_off.data(), B.pack_off.size() * sizeof(int32_t));
+    std::memcpy(img.data() + B.L.pack_td, B.pack_td.data(), B.pack_td.size() * sizeof(TensorDesc));
     if (is_blockwise(algo)) {
         Codebook *cb = reinterpret_cast<Codebook *>(img.data() + B.L.codebook);
         if (!build_map(7, cb->m8) || !build_map(8, cb->v8) || !build_map(3, cb->m4) || !build_map(4, cb->v4))
@@ -635,6 +691,7 @@ int create_on(const Built &B, const optim_tensor_list *list, int32_t algo, const
     P->sched = OPTIM_SCHED_NONE;
     P->static_dev = dev;
     P->static_gen = 0;
+    P->pack_unit0 = B.pack_unit0;
     *out = P;
     return OPTIM_OK;
 }
@@ -778,6 +835,10 @@ StepArgs step_args(optim_plan *P) {
     a.npartials = P->npartials;
     a.blockfac = reinterpret_cast<float *>(P->ws + P->L.blockfac);
     a.blockspan = reinterpret_cast<const int32_t *>(P->ws + P->L.blockspan);
+    a.packs = reinterpret_cast<const PackDesc *>(P->ws + P->L.packs);
+    a.pack_off = reinterpret_cast<const int32_t *>(P->ws + P->L.pack_off);
+    a.pack_td = reinterpret_cast<const TensorDesc *>(P->ws + P->L.pack_td);
+    a.pack_unit0 = P->pack_unit0;
     a.nblocks = P->nblocks;
     a.codebook = reinterpret_cast<const Codebook *>(P->ws + P->L.codebook);
     a.bits = P->bits;

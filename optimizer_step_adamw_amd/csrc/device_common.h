@@ -316,6 +316,62 @@ __device__ __forceinline__ void lane_walk(int64_t start, int64_t len, bool vec_o
     }
 }
 
+// ---------------------------------------------------------------- packs
+// A pack span (tensor == kPackTensor) holds several small tensors end to end
+// (see PackDesc).  A workgroup copies the pack's offsets and its members'
+// tensor descriptors into LDS (one contiguous copy), then lane t takes the
+// pack's groups of 4 elements at 4t + q kSub, as in a unit of one tensor,
+// and finds the member holding each group by a binary search of the
+// offsets (every member starts at a multiple of 4, so a group never crosses
+// two members).  Member descriptors are then read from LDS.
+struct PackLds {
+    TensorDesc td[kMaxPackTensors];
+    int32_t off[kMaxPackTensors + 1];
+};
+
+// Copies pack P's tables into L; ends with a barrier.
+__device__ __forceinline__ void pack_fill(const StepArgs &a, const PackDesc &P, PackLds &L) {
+    constexpr int kWords = (int)(sizeof(TensorDesc) / 4);
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(a.pack_td + P.td_base);
+    uint32_t *dst = reinterpret_cast<uint32_t *>(L.td);
+    for (int i = threadIdx.x; i < P.k * kWords; i += kThreads) dst[i] = src[i];
+    for (int i = threadIdx.x; i <= P.k; i += kThreads) L.off[i] = a.pack_off[P.off_base + i];
+    __syncthreads();
+}
+
+// This lane's G groups from pack element v0 on (v0 + q kSub): member j[q],
+// first element e[q] of that member, count n[q] (1..4; 0 past the pack's
+// end); whole: every group is 4 elements of a member whose arrays are
+// 16-byte aligned.
+template <int G>
+struct PackSlots {
+    int32_t j[G];
+    int32_t e[G];
+    int32_t n[G];
+    bool whole;
+};
+
+template <int G>
+__device__ __forceinline__ PackSlots<G> pack_slots(const PackLds &L, const PackDesc &P, int32_t v0) {
+    PackSlots<G> sl;
+    sl.whole = true;
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        const int32_t v = v0 + q * (int32_t)kSub;
+        int lo = 0, hi = P.k;  // off[lo] <= v < off[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (L.off[mid] <= v) lo = mid; else hi = mid;
+        }
+        sl.j[q] = lo;
+        sl.e[q] = v - L.off[lo];
+        const int64_t left = v < P.len ? L.td[lo].numel - sl.e[q] : 0;
+        sl.n[q] = left < kVec ? (int32_t)left : kVec;
+        sl.whole = sl.whole && sl.n[q] == kVec && L.td[lo].vec_ok;
+    }
+    return sl;
+}
+
 // ---------------------------------------------------------------- per-step scalars
 // Bias corrections and step sizes in fp64, rounded once to fp32: in fp32,
 // 1 - beta2^t cancels badly at small t, and fast power/divide intrinsics put
@@ -528,6 +584,60 @@ __device__ __forceinline__ void adam_elems(const TensorDesc &T, int64_t e, const
     adam_load<PK, GK, ADE, N>(T, e, k.inv_scale, r);
     adam_math<ADE, N>(r, k, lw);
     adam_store<PK, ADE, N>(T, e, r);
+}
+
+// AdamW / AdEMAMix over a lane's G groups of a pack.  Whole slots: all
+// loads (adam_pack_load, gradient times gscale) issue before the
+// arithmetic and the stores (adam_pack_finish, which applies the remaining
+// gradient scale rs); otherwise adam_pack_finish goes group by group,
+// element by element where a group is partial.
+template <int PK, int GK, bool ADE, int G>
+__device__ __forceinline__ void adam_pack_load(const PackLds &L, const PackSlots<G> &sl, float gscale,
+                                               AdamRegs<kVec> (&r)[G]) {
+    if (!sl.whole) return;
+#pragma unroll
+    for (int q = 0; q < G; ++q) adam_load<PK, GK, ADE, kVec>(L.td[sl.j[q]], sl.e[q], gscale, r[q]);
+}
+
+template <int PK, int GK, bool ADE, int G>
+__device__ __forceinline__ void adam_pack_finish(const PackLds &L, const PackSlots<G> &sl, const Scalars &S,
+                                                 const AdamK &k, float rs, AdamRegs<kVec> (&r)[G]) {
+    if (sl.whole) {
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+#pragma unroll
+            for (int i = 0; i < kVec; ++i) r[q].g[i] = r[q].g[i] * rs;
+            adam_math<ADE, kVec>(r[q], k, S.lrwd[L.td[sl.j[q]].group]);
+        }
+#pragma unroll
+        for (int q = 0; q < G; ++q) adam_store<PK, ADE, kVec>(L.td[sl.j[q]], sl.e[q], r[q]);
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        if (sl.n[q] == 0) continue;
+        const TensorDesc &T = L.td[sl.j[q]];
+        const float lw = S.lrwd[T.group];
+        if (sl.n[q] == kVec && T.vec_ok)
+            adam_elems<PK, GK, ADE, kVec>(T, sl.e[q], k, lw);
+        else
+            for (int i = 0; i < sl.n[q]; ++i) adam_elems<PK, GK, ADE, 1>(T, sl.e[q] + i, k, lw);
+    }
+}
+
+// A whole pack after the prologue: G groups per lane at a time.
+template <int PK, int GK, bool ADE, int G>
+__device__ __forceinline__ void adam_pack_unit(const StepArgs &a, const SpanDesc &sp, PackLds &L, const Scalars &S,
+                                               const AdamK &k) {
+    const PackDesc P = a.packs[sp.elem_begin];
+    pack_fill(a, P, L);
+    for (int32_t v0 = (int32_t)threadIdx.x * kVec; v0 < P.len; v0 += G * (int32_t)kSub) {
+        const PackSlots<G> sl = pack_slots<G>(L, P, v0);
+        AdamRegs<kVec> r[G];
+        adam_pack_load<PK, GK, ADE, G>(L, sl, k.inv_scale, r);
+        adam_pack_finish<PK, GK, ADE, G>(L, sl, S, k, 1.0f, r);
+    }
+    __syncthreads();  // L is refilled for the next pack
 }
 
 template <int PK, int GK, bool ADE, int G = kAdamGroups>

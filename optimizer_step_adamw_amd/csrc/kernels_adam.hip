@@ -61,19 +61,78 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
 // Up to this many units the early-load form is used.
 constexpr int64_t kEarlyLoadUnits = 4096;
 
+// Packs of small tensors (the plan's units from pack_unit0 on; see
+// PackDesc), G groups of 4 elements per lane and pass.  On the default grid
+// a workgroup takes one pack and, when the pack fits one pass (always with
+// the plan's own unit size, G * 1024 elements), copies its tables to LDS and
+// issues the lanes' loads before the per-step prologue, as the early form
+// above; otherwise (persistent grid, larger units) it walks its packs after
+// the prologue.  Measured on MI355X, 2^24 AdamW elements as 65536 tensors of
+// 256 (four state sets in turn): one workgroup per tensor 285.7 us; packs
+// of 16 tensors (4096-element units) in the step kernel itself 115.7 us;
+// in kernels of their own, with the member descriptors in LDS and the loads
+// before the prologue, see the benchmark's many-tensor lists.
+template <int PK, int GK, bool ADE, int G>
+__global__ __launch_bounds__(kThreads) void adam_pack_kernel(StepArgs a) {
+    __shared__ Scalars S;
+    __shared__ PackLds PL;
+    if (a.grid_request == 0 && a.units_per_wg == 1 && a.unit0 + (int64_t)blockIdx.x < a.nunits) {
+        const PackDesc P = a.packs[a.unit0 + blockIdx.x - a.pack_unit0];
+        if (P.len <= G * kSub) {
+            pack_fill(a, P, PL);
+            const int32_t v0 = (int32_t)threadIdx.x * kVec;
+            const bool mine = v0 < P.len;
+            PackSlots<G> sl;
+            AdamRegs<kVec> r[G];
+            if (mine) {
+                sl = pack_slots<G>(PL, P, v0);
+                adam_pack_load<PK, GK, ADE, G>(PL, sl, 1.0f, r);
+            }
+            step_begin(a, S);
+            const StepCommit commit{a, S};
+            if (S.skip) return;
+            const AdamK k = adam_consts(S);
+            if (mine) adam_pack_finish<PK, GK, ADE, G>(PL, sl, S, k, k.inv_scale, r);  // g * 1 * s == g * s
+            return;
+        }
+    }
+    step_begin(a, S);
+    const StepCommit commit{a, S};
+    if (S.skip) return;
+    const AdamK k = adam_consts(S);
+    for_units(a, [&](int64_t, const SpanDesc &sp, int64_t, int64_t) { adam_pack_unit<PK, GK, ADE, G>(a, sp, PL, S, k); });
+}
+
 }  // namespace
 
 template <bool ADE, int PK, int GK>
-static void launch_adam_g(const StepArgs &a, hipStream_t s) {
-    // the early form needs one whole tile of its groups per lane per
-    // workgroup: the default grid over 2048- or 4096-element units
-    const bool early = a.grid_request == 0 && a.units_per_wg == 1 && a.nunits - a.unit0 <= kEarlyLoadUnits;
-    if (early && a.tile == (int64_t)kAdamGroups * kSub)
-        LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, kAdamGroups>), a, s);
-    else if (early && a.tile == (int64_t)kAdamGroupsEarly * kSub)
-        LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, kAdamGroupsEarly>), a, s);
-    else
-        LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, 0>), a, s);
+static void launch_adam_g(const StepArgs &args, hipStream_t s) {
+    // units of single tensors [unit0, pack_unit0), then the packs
+    StepArgs a = args;
+    const bool packs = a.pack_unit0 < a.nunits;
+    if (packs) {
+        a.nunits = a.pack_unit0;
+        a.commit = 0;  // the pack launch publishes the step
+    }
+    if (!packs || a.nunits > a.unit0) {
+        // the early form needs one whole tile of its groups per lane per
+        // workgroup: the default grid over 2048- or 4096-element units
+        const bool early = a.grid_request == 0 && a.units_per_wg == 1 && a.nunits - a.unit0 <= kEarlyLoadUnits;
+        if (early && a.tile == (int64_t)kAdamGroups * kSub)
+            LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, kAdamGroups>), a, s);
+        else if (early && a.tile == (int64_t)kAdamGroupsEarly * kSub)
+            LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, kAdamGroupsEarly>), a, s);
+        else
+            LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, 0>), a, s);
+    }
+    if (packs) {
+        StepArgs b = args;
+        b.unit0 = args.pack_unit0;
+        if (b.tile == (int64_t)kAdamGroupsEarly * kSub)
+            LAUNCH_PERSISTENT((adam_pack_kernel<PK, GK, ADE, kAdamGroupsEarly>), b, s);
+        else
+            LAUNCH_PERSISTENT((adam_pack_kernel<PK, GK, ADE, kAdamGroups>), b, s);
+    }
 }
 
 template <bool ADE, int PK>

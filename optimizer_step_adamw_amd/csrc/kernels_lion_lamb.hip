@@ -33,6 +33,55 @@ __device__ __forceinline__ void lion_elems(const TensorDesc &T, int64_t e, const
     stf<N>(T.m, e, m);
 }
 
+// A lane's G groups of a pack (as adam_pack_load / adam_pack_finish).
+template <int G>
+struct LionRegs {
+    float p[G][kVec], g[G][kVec], m[G][kVec];
+};
+
+template <int PK, int GK, int G>
+__device__ __forceinline__ void lion_pack_load(const PackLds &L, const PackSlots<G> &sl, float gscale,
+                                               LionRegs<G> &r) {
+    if (!sl.whole) return;
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        const TensorDesc &T = L.td[sl.j[q]];
+        load_p<PK, kVec>(T, sl.e[q], r.p[q]);
+        load_g<GK, kVec>(T.g, sl.e[q], gscale, r.g[q]);
+        ldf<kVec>(T.m, sl.e[q], r.m[q]);
+    }
+}
+
+template <int PK, int GK, int G>
+__device__ __forceinline__ void lion_pack_finish(const PackLds &L, const PackSlots<G> &sl, const Scalars &S,
+                                                 const AdamK &k, float rs, LionRegs<G> &r) {
+    if (sl.whole) {
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+#pragma unroll
+            for (int i = 0; i < kVec; ++i) r.g[q][i] = r.g[q][i] * rs;
+            lion_math<kVec>(r.p[q], r.g[q], r.m[q], k, S.lrwd[L.td[sl.j[q]].group]);
+        }
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            const TensorDesc &T = L.td[sl.j[q]];
+            store_p<PK, kVec>(T, sl.e[q], r.p[q]);
+            stf<kVec>(T.m, sl.e[q], r.m[q]);
+        }
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        if (sl.n[q] == 0) continue;
+        const TensorDesc &T = L.td[sl.j[q]];
+        const float lw = S.lrwd[T.group];
+        if (sl.n[q] == kVec && T.vec_ok)
+            lion_elems<PK, GK, kVec>(T, sl.e[q], k, lw);
+        else
+            for (int i = 0; i < sl.n[q]; ++i) lion_elems<PK, GK, 1>(T, sl.e[q] + i, k, lw);
+    }
+}
+
 // EG > 0: the early-load form of the AdamW kernel (a whole unit of EG groups
 // per lane loaded before the per-step prologue), for plans of at most
 // kLionEarlyUnits units; the plan's unit size (2048 or 4096 elements) fixes
@@ -82,6 +131,48 @@ __global__ __launch_bounds__(kThreads) void lion_kernel(StepArgs a) {
 }
 
 constexpr int64_t kLionEarlyUnits = 4096;
+
+// Packs of small tensors (as adam_pack_kernel).
+template <int PK, int GK, int G>
+__global__ __launch_bounds__(kThreads) void lion_pack_kernel(StepArgs a) {
+    __shared__ Scalars S;
+    __shared__ PackLds PL;
+    if (a.grid_request == 0 && a.units_per_wg == 1 && a.unit0 + (int64_t)blockIdx.x < a.nunits) {
+        const PackDesc P = a.packs[a.unit0 + blockIdx.x - a.pack_unit0];
+        if (P.len <= G * kSub) {
+            pack_fill(a, P, PL);
+            const int32_t v0 = (int32_t)threadIdx.x * kVec;
+            const bool mine = v0 < P.len;
+            PackSlots<G> sl;
+            LionRegs<G> r;
+            if (mine) {
+                sl = pack_slots<G>(PL, P, v0);
+                lion_pack_load<PK, GK, G>(PL, sl, 1.0f, r);
+            }
+            step_begin(a, S);
+            const StepCommit commit{a, S};
+            if (S.skip) return;
+            const AdamK k = adam_consts(S);
+            if (mine) lion_pack_finish<PK, GK, G>(PL, sl, S, k, k.inv_scale, r);  // g * 1 * s == g * s
+            return;
+        }
+    }
+    step_begin(a, S);
+    const StepCommit commit{a, S};
+    if (S.skip) return;
+    const AdamK k = adam_consts(S);
+    for_units(a, [&](int64_t, const SpanDesc &sp, int64_t, int64_t) {
+        const PackDesc P = a.packs[sp.elem_begin];
+        pack_fill(a, P, PL);
+        for (int32_t v0 = (int32_t)threadIdx.x * kVec; v0 < P.len; v0 += G * (int32_t)kSub) {
+            const PackSlots<G> sl = pack_slots<G>(PL, P, v0);
+            LionRegs<G> r;
+            lion_pack_load<PK, GK, G>(PL, sl, k.inv_scale, r);
+            lion_pack_finish<PK, GK, G>(PL, sl, S, k, 1.0f, r);
+        }
+        __syncthreads();  // PL is refilled for the next pack
+    });
+}
 
 // ---------------------------------------------------------------- LAMB
 // You et al., arXiv:1904.00962, Algorithm 2, with Adam's direction as in the
@@ -219,14 +310,31 @@ __global__ __launch_bounds__(kThreads) void lamb_update_kernel(StepArgs a) {
 }  // namespace
 
 template <int PK, int GK>
-static void launch_lion_t(const StepArgs &a, hipStream_t s) {
-    const bool early = a.grid_request == 0 && a.units_per_wg == 1 && a.nunits - a.unit0 <= kLionEarlyUnits;
-    if (early && a.tile == (int64_t)kAdamGroups * kSub)
-        LAUNCH_PERSISTENT((lion_kernel<PK, GK, kAdamGroups>), a, s);
-    else if (early && a.tile == (int64_t)kAdamGroupsEarly * kSub)
-        LAUNCH_PERSISTENT((lion_kernel<PK, GK, kAdamGroupsEarly>), a, s);
-    else
-        LAUNCH_PERSISTENT((lion_kernel<PK, GK, 0>), a, s);
+static void launch_lion_t(const StepArgs &args, hipStream_t s) {
+    // units of single tensors [unit0, pack_unit0), then the packs
+    StepArgs a = args;
+    const bool packs = a.pack_unit0 < a.nunits;
+    if (packs) {
+        a.nunits = a.pack_unit0;
+        a.commit = 0;  // the pack launch publishes the step
+    }
+    if (!packs || a.nunits > a.unit0) {
+        const bool early = a.grid_request == 0 && a.units_per_wg == 1 && a.nunits - a.unit0 <= kLionEarlyUnits;
+        if (early && a.tile == (int64_t)kAdamGroups * kSub)
+            LAUNCH_PERSISTENT((lion_kernel<PK, GK, kAdamGroups>), a, s);
+        else if (early && a.tile == (int64_t)kAdamGroupsEarly * kSub)
+            LAUNCH_PERSISTENT((lion_kernel<PK, GK, kAdamGroupsEarly>), a, s);
+        else
+            LAUNCH_PERSISTENT((lion_kernel<PK, GK, 0>), a, s);
+    }
+    if (packs) {
+        StepArgs b = args;
+        b.unit0 = args.pack_unit0;
+        if (b.tile == (int64_t)kAdamGroupsEarly * kSub)
+            LAUNCH_PERSISTENT((lion_pack_kernel<PK, GK, kAdamGroupsEarly>), b, s);
+        else
+            LAUNCH_PERSISTENT((lion_pack_kernel<PK, GK, kAdamGroups>), b, s);
+    }
 }
 
 hipError_t launch_lion(const StepArgs &a, int pk, int gk, hipStream_t s) {

@@ -8,50 +8,88 @@ namespace {
 // ---------------------------------------------------------------- finite check
 // [LTN] analysis: found_inf marks a NaN or +-Inf anywhere in the gradients.
 // A read-only scan: each workgroup takes kFiniteCheckElems elements (several
-// consecutive units, merged into one walk where they are contiguous).
+// consecutive units, merged into one walk where they are contiguous; packs
+// of small tensors member by member).
 // Measured on MI355X: bf16 gradients stream best with 8 groups of 4 per lane
 // in flight (7.4 TB/s), fp32 with one group at a time (7.0 TB/s).
-// NORM: the same pass also sums the squares of the (scaled) gradients in
-// fp64, per lane and per workgroup, into partials[workgroup].  The square of
-// an fp32 or bf16 value is exact in fp64 and cannot overflow there, so a
-// large but finite loss-scaled gradient (|G| above ~1.8e19, whose fp32 square
-// is +inf) still gives a finite norm and is clipped; only a NaN / Inf
-// element, which sets found_inf, makes the norm non-finite.
-template <int GK, bool NORM>
-__device__ __forceinline__ bool scan_grads(const TensorDesc &T, int64_t start, int64_t len, double &acc) {
-    constexpr int G = GK == G_F32 ? 1 : 8;
+// NORM: the same pass also sums the squares of the (scaled) gradients into
+// partials[workgroup]: per lane in fp32 (Acc = float), then across lanes and
+// workgroups in fp64.  A loss-scaled gradient can be finite and still have
+// an fp32 square of +inf (|G| above ~1.8e19): if any lane's fp32 sum
+// overflows without the lane having met a NaN / Inf, the workgroup walks its
+// range again summing exact fp64 squares (Acc = double), so finite gradients
+// always give a finite norm and are clipped; only a NaN / Inf element, which
+// sets found_inf, makes the norm non-finite.  (Squares in fp64 on every
+// pass measured 13% slower on the 1.1B bf16 list: 373 against 330 us.)
+
+// This lane's N gradient elements of T from element e (N = 1, or whole
+// groups of 4 in the step layout).
+template <int GK, bool NORM, int N, class Acc>
+__device__ __forceinline__ bool scan_elems(const TensorDesc &T, int64_t e, Acc &acc) {
+    bool bad = false;
+    float x[N];
+    if constexpr (GK == G_F32) {
+        ldf<N>(static_cast<const float *>(T.g), e, x);
+#pragma unroll
+        for (int i = 0; i < N; ++i) bad |= (__float_as_uint(x[i]) & 0x7F800000u) == 0x7F800000u;
+    } else {
+        uint32_t w[N];
+        ldh<N>(static_cast<const uint16_t *>(T.g), e, w);
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            bad |= (w[i] & 0x7F80u) == 0x7F80u;
+            x[i] = bf16_to_f32(w[i]);
+        }
+    }
+    if constexpr (NORM) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            if constexpr (sizeof(Acc) == 8)
+                acc = __builtin_fma((double)x[i], (double)x[i], acc);
+            else
+                acc += x[i] * x[i];
+        }
+    }
+    return bad;
+}
+
+template <int GK, bool NORM, class Acc>
+__device__ __forceinline__ bool scan_grads(const TensorDesc &T, int64_t start, int64_t len, Acc &acc) {
+    // (the rare fp64 pass takes one group at a time: it must not raise the
+    // kernel's register count)
+    constexpr int G = (GK == G_F32 || sizeof(Acc) == 8) ? 1 : 8;
     bool bad = false;
     lane_walk<G>(start, len, T.vec_ok, [&](auto n, int64_t e) {
-        constexpr int N = decltype(n)::value;
-        float x[N];
-        if constexpr (GK == G_F32) {
-            ldf<N>(static_cast<const float *>(T.g), e, x);
-#pragma unroll
-            for (int i = 0; i < N; ++i) bad |= (__float_as_uint(x[i]) & 0x7F800000u) == 0x7F800000u;
-        } else {
-            uint32_t w[N];
-            ldh<N>(static_cast<const uint16_t *>(T.g), e, w);
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                bad |= (w[i] & 0x7F80u) == 0x7F80u;
-                x[i] = bf16_to_f32(w[i]);
-            }
-        }
-        if constexpr (NORM) {
-#pragma unroll
-            for (int i = 0; i < N; ++i) acc = __builtin_fma((double)x[i], (double)x[i], acc);
-        }
+        bad |= scan_elems<GK, NORM, decltype(n)::value>(T, e, acc);
     });
     return bad;
 }
 
-template <int GK, bool NORM>
-__global__ __launch_bounds__(kThreads) void finite_kernel(StepArgs a) {
+// The workgroup's whole range; true if this lane met a NaN / Inf.
+template <int GK, bool NORM, class Acc>
+__device__ __forceinline__ bool scan_workgroup(const StepArgs &a, PackLds &PL, Acc &acc) {
     bool bad = false;
-    double acc = 0.0;
     int tensor = -1;
     int64_t start = 0, len = 0;
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t s, int64_t l) {
+        if (sp.tensor == kPackTensor) {  // small tensors laid end to end
+            const PackDesc P = a.packs[sp.elem_begin];
+            pack_fill(a, P, PL);
+            for (int32_t v0 = (int32_t)threadIdx.x * kVec; v0 < P.len; v0 += 2 * (int32_t)kSub) {
+                const PackSlots<2> sl = pack_slots<2>(PL, P, v0);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const TensorDesc &T = PL.td[sl.j[q]];
+                    if (sl.n[q] == kVec && T.vec_ok) {
+                        bad |= scan_elems<GK, NORM, kVec>(T, sl.e[q], acc);
+                    } else {
+                        for (int j = 0; j < sl.n[q]; ++j) bad |= scan_elems<GK, NORM, 1>(T, sl.e[q] + j, acc);
+                    }
+                }
+            }
+            __syncthreads();  // PL is refilled for the next pack
+            return;
+        }
         if (sp.tensor == tensor && s == start + len) {
             len += l;
             return;
@@ -62,8 +100,22 @@ __global__ __launch_bounds__(kThreads) void finite_kernel(StepArgs a) {
         len = l;
     });
     if (len > 0) bad |= scan_grads<GK, NORM>(a.tensors[tensor], start, len, acc);
+    return bad;
+}
+
+template <int GK, bool NORM>
+__global__ __launch_bounds__(kThreads) void finite_kernel(StepArgs a) {
+    __shared__ PackLds PL;
+    float acc32 = 0.0f;
+    const bool bad = scan_workgroup<GK, NORM>(a, PL, acc32);
     if (bad) *a.found_inf = 1.0f;
     if constexpr (NORM) {
+        double acc = (double)acc32;
+        // a finite-gradient overflow of the fp32 sums: again in fp64
+        if (__syncthreads_or(!bad && !(acc32 <= 3.4028234663852886e38f))) {
+            acc = 0.0;
+            scan_workgroup<GK, NORM>(a, PL, acc);
+        }
         __shared__ double red[kThreads / 64];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);

@@ -79,6 +79,27 @@ struct TensorDesc {       // 152 bytes
 };
 static_assert(sizeof(TensorDesc) == 152, "TensorDesc layout");
 
+// Packs (AdamW, AdEMAMix and Lion plans): a run of whole tensors of at most
+// half a unit each (in list order, empty tensors left out), laid end to end
+// as one unit with each tensor's length rounded up to a multiple of 4.  A
+// pack is one span whose tensor field is kPackTensor and whose elem_begin is
+// the pack's index; its len is the rounded total.  Packs take the plan's
+// last units, after every unit of a single tensor, and have kernels of
+// their own (the step kernels of single tensors stay free of their registers
+// and LDS).  Member j holds the pack's
+// elements [off[j], off[j + 1]), off[j] = pack_off[off_base + j], off[0] = 0,
+// off[k] = len; pack_td[td_base + j] is a copy of its tensor descriptor, so
+// a workgroup loads a pack's tables with one contiguous copy into LDS.
+constexpr int32_t kPackTensor = -2;
+constexpr int32_t kMaxPackTensors = 64;  // members per pack (LDS: 64 descriptors, ~10 KB)
+struct PackDesc {         // 16 bytes
+    int32_t td_base;      // index of member 0 in pack_td
+    int32_t off_base;     // index of off[0] in pack_off
+    int32_t k;            // members
+    int32_t len;          // elements including the rounding
+};
+static_assert(sizeof(PackDesc) == 16, "PackDesc layout");
+
 struct SpanDesc {         // 32 bytes
     int64_t unit_begin;   // first global unit number of this span
     int64_t elem_begin;   // first element, relative to the tensor
@@ -124,7 +145,7 @@ constexpr size_t kAmaxBytesPerBlock = 2 * kAmaxSlots * kCounterStride * sizeof(u
 // `counters` holds the arrival counters of the step kernels' commit.
 struct Layout {
     size_t counters, group_wd, tensors, spans, codebook, partials, blockfac,
-        blockspan, total;
+        blockspan, packs, pack_off, pack_td, total;
 };
 
 // Quantization maps.  A normalised magnitude a in [0, 1] maps to the largest
@@ -188,6 +209,10 @@ struct StepArgs {
                               // side by side in qm (absmax_m)
     float *found_inf;         // finite check output
     int32_t cus;              // compute units of the device
+    const PackDesc *packs;    // packs of small tensors (elementwise plans)
+    const int32_t *pack_off;
+    const TensorDesc *pack_td;
+    int64_t pack_unit0;       // units [pack_unit0, nunits) of the plan are packs
     int32_t grid_request;     // persistent workgroups (0 = see units_per_wg)
     int32_t units_per_wg;     // without a persistent grid: consecutive units
                               // per workgroup (set by the launcher)
