@@ -139,19 +139,21 @@ def run_timed(torch, calls, steps, warmup, plans=(), trace_cap=0):
 
 
 def kernel_stats(records, name=None):
-    """Launch count, total / mean ms and per-launch spread of the records of
-    one kernel (all records if name is None)."""
-    ms = [r[2] for r in records if name is None or r[0] == name]
-    if not ms:
+    """Launch count, total / mean ms, per-launch spread and grid sizes of the
+    records of one kernel (all records if name is None)."""
+    sel = [r for r in records if name is None or r[0] == name]
+    if not sel:
         return None
-    return dict(launches=len(ms), total_ms=sum(ms), mean_ms=sum(ms) / len(ms), **dist(ms))
+    ms = [r[2] for r in sel]
+    return dict(launches=len(ms), total_ms=sum(ms), mean_ms=sum(ms) / len(ms),
+                workgroups=sorted(set(r[1] for r in sel)), **dist(ms))
 
 
 def roofline_entry(kernel, workload, bytes_per_launch, stats, ceiling=None, traffic=None, note=None):
     achieved = gbs(bytes_per_launch, stats["mean_ms"])
     e = dict(kernel=kernel, workload=workload, bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
              frac=achieved / PEAK_HBM_GBS, traffic=traffic, bytes_per_launch=bytes_per_launch,
-             launch_ms=stats["mean_ms"], launches=stats["launches"],
+             launch_ms=stats["mean_ms"], launches=stats["launches"], workgroups=stats["workgroups"],
              launch_spread_ms=dict(p10=stats["p10_ms"], median=stats["median_ms"], p90=stats["p90_ms"]))
     if ceiling:
         e["ceiling"] = ceiling
@@ -188,8 +190,15 @@ KERNEL_SOURCES = {  # traffic summary name -> sources its device code comes from
     "ademamix_fp32": ("device_common.h", "kernels_adam.hip"),
     "adamw_bf16_remainder": ("device_common.h", "kernels_adam.hip"),
     "check_finite_bf16": ("device_common.h", "kernels_util.hip"),
+    "check_norm_bf16": ("device_common.h", "kernels_util.hip"),
     "mini_update": ("device_common.h", "kernels_mini.hip"),
     "mini_sumsq": ("device_common.h", "kernels_mini.hip"),
+    "lion_fp32": ("device_common.h", "kernels_lion_lamb.hip"),
+    "lamb_moments": ("device_common.h", "kernels_lion_lamb.hip"),
+    "lamb_update": ("device_common.h", "kernels_lion_lamb.hip"),
+    "scaled_bf16": ("device_common.h", "kernels_scaled.hip"),
+    "scaled_f16_pass1": ("device_common.h", "kernels_scaled.hip"),
+    "scaled_f16_pass2": ("device_common.h", "kernels_scaled.hip"),
     "blockwise_8bit": ("device_common.h", "kernels_blockwise.hip"),
     "blockwise_8bit_interleaved": ("device_common.h", "kernels_blockwise.hip"),
     "blockwise_4bit": ("device_common.h", "kernels_blockwise.hip"),
