@@ -252,7 +252,12 @@ def test_c4_blockwise_268M(bits, interleaved):
             if t == 1:
                 gd = g.astype(np.float64)
                 closed = p_init * (1 - lr32 * wd) - lr32 * gd / (np.abs(gd) + hpw.eps)
-                assert relerr_tau(got, closed, lr32) <= TOL_STEP1
+                err_closed = relerr_tau(got, closed, lr32)
+                # the margin of the hardware sqrt / reciprocal in the update
+                # direction against the 2e-6 bound
+                say(f"C4 {bits}-bit interleaved={interleaved} lr={lr} fresh step: relerr_tau vs oracle {err:.3e}, "
+                    f"vs closed form {err_closed:.3e}; {err_report(got, p, lr32)}")
+                assert err_closed <= TOL_STEP1
                 if lr == 0.1:
                     mutant = (p_init - lr32 * gd / (np.abs(gd) + hpw.eps)) * (1 - lr32 * wd)
                     assert np.max(np.abs(got - mutant)) > 0.9e-3
