@@ -129,35 +129,51 @@ __global__ __launch_bounds__(kThreads) void mini_sumsq_kernel(StepArgs a) {
 }
 
 // Per block b of [block0, nblocks): V_b <- beta2 V_b + (1 - beta2) mean(g^2)
-// (fixed-order fp64 sum of the unit partials), step factor lr/bc1 / h_b.
-// The first block's partial sums are loaded before the per-step prologue
-// (if the step turns out skipped they are not used).
+// (fixed-order fp64 sum of the unit partials: per lane, then across each
+// wave, then over the four waves), step factor lr/bc1 / h_b.  The first
+// block's partial sums, and in thread 0 the chain block -> span -> tensor ->
+// V_b, are loaded before the per-step prologue (if the step turns out
+// skipped they are not used).
 __global__ __launch_bounds__(kThreads) void mini_finalize_kernel(StepArgs a) {
     __shared__ Scalars S;
-    __shared__ double red[kThreads];
+    static_assert(kThreads == 256, "the cross-wave sum below adds four waves");
+    __shared__ double red[kThreads / 64];
     int b = a.block0 + blockIdx.x;
     const auto block_sum = [&](int blk) {
         const int si = a.blockspan[blk];
         return lane_sum(a.partials, 1, a.spans[si].unit_begin, a.spans[si + 1].unit_begin);
     };
-    double part = b < a.nblocks ? block_sum(b) : 0.0;
+    struct BlockV {
+        float *v;
+        float old;
+        int64_t len;
+    };
+    const auto block_v = [&](int blk) {
+        const SpanDesc sp = a.spans[a.blockspan[blk]];
+        const TensorDesc &T = a.tensors[sp.tensor];
+        float *v = T.v + sp.elem_begin / T.block_len;
+        return BlockV{v, *v, sp.len};
+    };
+    double part = 0.0;
+    BlockV bv{nullptr, 0.0f, 1};
+    if (b < a.nblocks) {
+        part = block_sum(b);
+        if (threadIdx.x == 0) bv = block_v(b);
+    }
     step_begin(a, S);
     const StepCommit commit{a, S};
     if (S.skip) return;
     for (bool first = true; b < a.nblocks; b += gridDim.x, first = false) {
-        red[threadIdx.x] = first ? part : block_sum(b);
+        double x = first ? part : block_sum(b);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
         __syncthreads();
-        for (int st = kThreads / 2; st > 0; st >>= 1) {
-            if (threadIdx.x < st) red[threadIdx.x] += red[threadIdx.x + st];
-            __syncthreads();
-        }
         if (threadIdx.x == 0) {
-            const SpanDesc sp = a.spans[a.blockspan[b]];
-            const TensorDesc &T = a.tensors[sp.tensor];
-            const int64_t j = sp.elem_begin / T.block_len;
-            const double mean = red[0] / (double)sp.len;
-            const double V = S.beta2_64 * (double)T.v[j] + S.c2_64 * mean;
-            T.v[j] = (float)V;
+            if (!first) bv = block_v(b);
+            const double mean = ((red[0] + red[1]) + (red[2] + red[3])) / (double)bv.len;
+            const double V = S.beta2_64 * (double)bv.old + S.c2_64 * mean;
+            *bv.v = (float)V;
             const double h = sqrt(V) * S.inv_sqrt_bc2_64 + S.eps64;
             a.blockfac[b] = (float)(S.step_size64 / h);
         }
