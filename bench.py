@@ -550,17 +550,18 @@ def bench_probes(torch, reps):
     out["copy_268M"] = dict(ms=ms, bytes=8.0 * n, gbs=gbs(8.0 * n, ms))
     del arr
     free(torch)
-    # blockwise separate layout: 8-bit block 256, 4-bit block 128 (8192-element
-    # units, 2 or 8 rows of loads in flight; the better one is the ceiling)
-    for bits, block, bpe in ((8, 256, B_8BIT), (4, 128, B_4BIT)):
+    # blockwise separate layout: 8-bit block 256 on 4096-element units, 4-bit
+    # block 128 on 8192 (the step's units), 2 rows of loads in flight or the
+    # whole unit; the better one is the ceiling
+    for bits, block, bpe, unit_rows in ((8, 256, B_8BIT, 4), (4, 128, B_4BIT, 8)):
         nb = n * bits // 8
         arr = [f32(n), f32(n), torch.zeros(nb, dtype=torch.uint8, device="cuda"),
                torch.zeros(nb, dtype=torch.uint8, device="cuda"),
                torch.zeros(n // block, device="cuda"), torch.zeros(n // block, device="cuda")]
         best = None
-        for rows in (2, 8):
-            ms = probe_time(torch, lambda i: probes.call("probe_blockwise", *arr, n, bits, rows), reps)
-            e = dict(ms=ms, bytes=bpe * n, gbs=gbs(bpe * n, ms), rows_in_flight=rows)
+        for rows in (2, unit_rows):
+            ms = probe_time(torch, lambda i: probes.call("probe_blockwise", *arr, n, bits, unit_rows, rows), reps)
+            e = dict(ms=ms, bytes=bpe * n, gbs=gbs(bpe * n, ms), unit=unit_rows * 1024, rows_in_flight=rows)
             best = e if best is None or e["gbs"] > best["gbs"] else best
         out[f"blockwise_{bits}bit_268M"] = best
         del arr

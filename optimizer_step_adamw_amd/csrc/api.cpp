@@ -214,7 +214,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
                              !states16 &&
                              total > kEarlyTileMinElems && total <= kEarlyTileMaxElems;
     const int64_t tile = (opts && opts->tile > 0) ? opts->tile
-                         : is_blockwise(algo) ? blockwise_tile(algo == OPTIM_ALGO_BLOCKWISE_ADEMAMIX, bits)
+                         : is_blockwise(algo) ? blockwise_tile(algo == OPTIM_ALGO_BLOCKWISE_ADEMAMIX, bits, il)
                          : unit_sums          ? kAdamMiniTile
                          : early_units        ? kEarlyTile
                                               : kDefaultTile;

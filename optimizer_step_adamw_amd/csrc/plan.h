@@ -34,12 +34,15 @@ constexpr int64_t kAdamMiniTile = 4096;   // also LAMB and the fp16 scaled-state
 // 26.8 ms (fewer, larger segments launch less often; past the cache's size
 // less of g is found there).
 constexpr int64_t kMiniSegmentBytes = (int64_t)384 << 20;
-// blockwise units, measured best on MI355X over 2^28 elements (4096-65536):
-// 2-state 8192 (8-bit separate layout 770.9 us against 789.0 at 4096,
-// interleaved 738.9 against 766.3; 4-bit 641.5 / 638.4 us), AdEMAMix
-// 8-bit 8192, 4-bit 16384
-constexpr int64_t blockwise_tile(bool ademamix, int bits) {
-    return ademamix ? (bits == 8 ? 8192 : 16384) : 8192;
+// blockwise units, measured best on MI355X over 2^28 elements (4096-16384,
+// every size timed in one process on the same arrays, since where the
+// driver places a fresh set of arrays moves the step by up to several
+// percent): 8-bit separate layout 4096 (757 us against 766 at 8192),
+// interleaved 8192 (729 against 751 at 4096), 4-bit 8192 either layout
+// (632-634 against 678-684 at 4096 and 653-684 at 16384), AdEMAMix 8-bit
+// 8192 (874 against 935 / 895), 4-bit 16384
+constexpr int64_t blockwise_tile(bool ademamix, int bits, bool interleaved) {
+    return ademamix ? (bits == 8 ? 8192 : 16384) : (bits == 8 && !interleaved) ? 4096 : 8192;
 }
 // read-only scans (finite check, gradient norm): elements per workgroup;
 // measured on MI355X over a 1.1B bf16 gradient list: 8192 -> 5.3 TB/s,

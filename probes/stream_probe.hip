@@ -95,11 +95,13 @@ __global__ __launch_bounds__(kThreads) void bf16r_pattern(uint16_t *p, uint16_t 
 }
 
 // blockwise 2-state step, separate layout, 4 elements a lane per row of
-// 1024; one workgroup per 8 rows (8192 elements); R rows in flight
-template <int BITS, int BLOCK, int R>
+// 1024; one workgroup per unit of ROWS rows (the step's unit: 4096 elements
+// for 8-bit codes, 8192 for 4-bit); R rows in flight
+template <int BITS, int BLOCK, int R, int ROWS>
 __global__ __launch_bounds__(kThreads) void blockwise_pattern(float *p, const float *g, uint8_t *qm, uint8_t *qv,
                                                               float *am, float *av) {
-    constexpr int kRows = 8;
+    constexpr int kRows = ROWS;
+    static_assert(kRows % R == 0, "whole batches of rows");
     const int64_t base = (int64_t)blockIdx.x * (kRows * 1024);
 #pragma unroll
     for (int r0 = 0; r0 < kRows; r0 += R) {
@@ -208,17 +210,20 @@ int probe_bf16r(uint16_t *p, uint16_t *r, const uint16_t *g, float *m, float *v,
 }
 
 int probe_blockwise(float *p, const float *g, uint8_t *qm, uint8_t *qv, float *am, float *av, int64_t n, int bits,
-                    int rows_in_flight, void *stream) {
+                    int unit_rows, int rows_in_flight, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 grid(grid_of(n, 8192));
-    if (bits == 8 && rows_in_flight == 2)
-        hipLaunchKernelGGL((blockwise_pattern<8, 256, 2>), grid, dim3(kThreads), 0, s, p, g, qm, qv, am, av);
-    else if (bits == 8)
-        hipLaunchKernelGGL((blockwise_pattern<8, 256, 8>), grid, dim3(kThreads), 0, s, p, g, qm, qv, am, av);
-    else if (rows_in_flight == 2)
-        hipLaunchKernelGGL((blockwise_pattern<4, 128, 2>), grid, dim3(kThreads), 0, s, p, g, qm, qv, am, av);
+    if (n <= 0 || n % ((int64_t)unit_rows * 1024) != 0) return -1;  // whole units only
+    const dim3 grid(grid_of(n, (int64_t)unit_rows * 1024));
+    if (bits == 8 && unit_rows == 4 && rows_in_flight == 2)
+        hipLaunchKernelGGL((blockwise_pattern<8, 256, 2, 4>), grid, dim3(kThreads), 0, s, p, g, qm, qv, am, av);
+    else if (bits == 8 && unit_rows == 4 && rows_in_flight == 4)
+        hipLaunchKernelGGL((blockwise_pattern<8, 256, 4, 4>), grid, dim3(kThreads), 0, s, p, g, qm, qv, am, av);
+    else if (bits == 4 && unit_rows == 8 && rows_in_flight == 2)
+        hipLaunchKernelGGL((blockwise_pattern<4, 128, 2, 8>), grid, dim3(kThreads), 0, s, p, g, qm, qv, am, av);
+    else if (bits == 4 && unit_rows == 8 && rows_in_flight == 8)
+        hipLaunchKernelGGL((blockwise_pattern<4, 128, 8, 8>), grid, dim3(kThreads), 0, s, p, g, qm, qv, am, av);
     else
-        hipLaunchKernelGGL((blockwise_pattern<4, 128, 8>), grid, dim3(kThreads), 0, s, p, g, qm, qv, am, av);
+        return -1;
     return (int)hipGetLastError();
 }
 
