@@ -253,11 +253,12 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     B.pack_off.clear();
     B.pack_td.clear();
     // Packs: AdamW / AdEMAMix (fp32 moments) and Lion plans lay runs of
-    // tensors of at most half a unit end to end in shared units, so a
-    // workgroup serves many small tensors (one prologue, every lane busy)
-    // instead of one each.
+    // tensors of at most half a pack end to end in shared units of up to
+    // pack_cap elements, so a workgroup serves many small tensors (one
+    // prologue, every lane busy) instead of one each.
     const bool packable = (algo == OPTIM_ALGO_ADAMW || algo == OPTIM_ALGO_ADEMAMIX || algo == OPTIM_ALGO_LION) &&
                           !states16;
+    const int64_t pack_cap = std::min<int64_t>(tile, kPackElems);
     std::vector<int32_t> open_pack;  // members of the pack being filled
     int64_t open_len = 0;
     auto close_pack = [&]() {
@@ -434,9 +435,9 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
             B.spans.push_back(SpanDesc{B.nunits, 0, numel, i, B.nblocks});
             B.nunits += (numel + tile - 1) / tile;
             ++B.nblocks;
-        } else if (packable && numel <= tile / 2) {
+        } else if (packable && numel <= pack_cap / 2) {
             const int64_t r = (numel + 3) / 4 * 4;
-            if (open_len + r > tile || (int32_t)open_pack.size() >= kMaxPackTensors) close_pack();
+            if (open_len + r > pack_cap || (int32_t)open_pack.size() >= kMaxPackTensors) close_pack();
             open_pack.push_back(i);
             open_len += r;
         } else {

@@ -63,15 +63,16 @@ constexpr int64_t kEarlyLoadUnits = 4096;
 
 // Packs of small tensors (the plan's units from pack_unit0 on; see
 // PackDesc), G groups of 4 elements per lane and pass.  On the default grid
-// a workgroup takes one pack and, when the pack fits one pass (always with
-// the plan's own unit size, G * 1024 elements), copies its tables to LDS and
-// issues the lanes' loads before the per-step prologue, as the early form
-// above; otherwise (persistent grid, larger units) it walks its packs after
-// the prologue.  Measured on MI355X, 2^24 AdamW elements as 65536 tensors of
+// a workgroup takes one pack and, when the pack fits one pass (always: a
+// pack holds at most kPackElems = G * 1024 elements), copies its tables to
+// LDS and issues the lanes' loads before the per-step prologue, as the early
+// form above; otherwise (persistent grid) it walks its packs after the
+// prologue.  Measured on MI355X, 2^24 AdamW elements as 65536 tensors of
 // 256 (four state sets in turn): one workgroup per tensor 285.7 us; packs
 // of 16 tensors (4096-element units) in the step kernel itself 115.7 us;
 // in kernels of their own, with the member descriptors in LDS and the loads
-// before the prologue, see the benchmark's many-tensor lists.
+// before the prologue, 89.6 us with 4096-element packs and 84.5 us with
+// 2048-element packs (see kPackElems).
 template <int PK, int GK, bool ADE, int G>
 __global__ __launch_bounds__(kThreads) void adam_pack_kernel(StepArgs a) {
     __shared__ Scalars S;
@@ -128,10 +129,8 @@ static void launch_adam_g(const StepArgs &args, hipStream_t s) {
     if (packs) {
         StepArgs b = args;
         b.unit0 = args.pack_unit0;
-        if (b.tile == (int64_t)kAdamGroupsEarly * kSub)
-            LAUNCH_PERSISTENT((adam_pack_kernel<PK, GK, ADE, kAdamGroupsEarly>), b, s);
-        else
-            LAUNCH_PERSISTENT((adam_pack_kernel<PK, GK, ADE, kAdamGroups>), b, s);
+        static_assert(kPackElems == (int64_t)kAdamGroups * kSub, "a pack is one pass of the pack kernel");
+        LAUNCH_PERSISTENT((adam_pack_kernel<PK, GK, ADE, kAdamGroups>), b, s);
     }
 }
 

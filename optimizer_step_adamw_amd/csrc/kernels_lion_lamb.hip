@@ -330,10 +330,8 @@ static void launch_lion_t(const StepArgs &args, hipStream_t s) {
     if (packs) {
         StepArgs b = args;
         b.unit0 = args.pack_unit0;
-        if (b.tile == (int64_t)kAdamGroupsEarly * kSub)
-            LAUNCH_PERSISTENT((lion_pack_kernel<PK, GK, kAdamGroupsEarly>), b, s);
-        else
-            LAUNCH_PERSISTENT((lion_pack_kernel<PK, GK, kAdamGroups>), b, s);
+        static_assert(kPackElems == (int64_t)kAdamGroups * kSub, "a pack is one pass of the pack kernel");
+        LAUNCH_PERSISTENT((lion_pack_kernel<PK, GK, kAdamGroups>), b, s);
     }
 }
 
