@@ -214,10 +214,11 @@ __device__ __forceinline__ void mini_update_unit(const StepArgs &a, const Scalar
     });
 }
 
-// The update walks its units backwards: a segment's block sums read g in
-// unit order just before, so the last units' g is the likeliest to be still
-// in the Infinity Cache (measured on MI355X, 7B list: update 19.84 -> 19.50
-// ms per step).
+// The update walks its units backwards, meeting first the g lines the block
+// sums read last.  Timed in one process on the same arrays (7B list) this
+// is no faster than the forward walk (24.88 against 24.86 ms per step): how
+// much of a segment's g the Infinity Cache still holds does not depend on
+// the order here.
 template <int PK, int GK>
 __global__ __launch_bounds__(kThreads) void mini_update_kernel(StepArgs a) {
     __shared__ Scalars S;
@@ -271,7 +272,9 @@ hipError_t launch_adam_mini(const StepArgs &args, int pk, int gk, const MiniSegm
         if (sg.block_end > sg.block_begin) {
             // the read-only sum pass streams better with 2 consecutive units
             // per workgroup (measured on MI355X, segmented 7B list: 25.5 ms
-            // per step against 26.0 with 1, 25.8 with 4, 26.3 with 8 or 16)
+            // per step against 26.0 with 1, 25.8 with 4, 26.3 with 8 or 16;
+            // in one process on the same arrays, with the early form, 24.88
+            // against 25.31 ms with 4)
             if (a.grid_request == 0) a.units_per_wg = kMiniSumUnitsPerWg;
             if (gk == G_F32)
                 LAUNCH_PERSISTENT((mini_sumsq_kernel<G_F32>), a, s);

@@ -32,7 +32,9 @@ constexpr int64_t kAdamMiniTile = 4096;   // also LAMB and the fp16 scaled-state
 // Llama-7B-shaped list: 28.1 ms per step in one pass over the list; with
 // segments of 160 / 256 / 384 / 512 / 1024 MiB 27.3 / 26.5 / 25.8 / 26.0 /
 // 26.8 ms (fewer, larger segments launch less often; past the cache's size
-// less of g is found there).
+// less of g is found there).  With today's kernels, every size timed in one
+// process on the same arrays: 256 / 320 / 384 / 448 / 512 MiB 25.18 /
+// 24.95 / 24.88 / 24.99 / 25.06 ms.
 constexpr int64_t kMiniSegmentBytes = (int64_t)384 << 20;
 // blockwise units, measured best on MI355X over 2^28 elements (4096-16384,
 // every size timed in one process on the same arrays, since where the
