@@ -189,6 +189,7 @@ KERNEL_SOURCES = {  # traffic summary name -> sources its device code comes from
     "adamw_fp32": ("device_common.h", "kernels_adam.hip"),
     "ademamix_fp32": ("device_common.h", "kernels_adam.hip"),
     "adamw_bf16_remainder": ("device_common.h", "kernels_adam.hip"),
+    "adamw_fp32_packs": ("device_common.h", "kernels_adam.hip"),
     "check_finite_bf16": ("device_common.h", "kernels_util.hip"),
     "check_norm_bf16": ("device_common.h", "kernels_util.hip"),
     "mini_update": ("device_common.h", "kernels_mini.hip"),
@@ -722,7 +723,10 @@ def bench_many(torch, osa, synth, steps, warmup):
         _, _, recs, _ = run_timed(torch, calls, steps, warmup, plans=[x[0].handle for x in sets], trace_cap=2 * steps)
         st = kernel_stats([r for v in recs.values() for r in v])
         out[f"tensors_{count}x{size}"] = dict(mean_ms=st["mean_ms"], gbs=gbs(B_ADAMW_F32 * n, st["mean_ms"]),
-                                              frac=gbs(B_ADAMW_F32 * n, st["mean_ms"]) / PEAK_HBM_GBS)
+                                              frac=gbs(B_ADAMW_F32 * n, st["mean_ms"]) / PEAK_HBM_GBS,
+                                              workgroups=st["workgroups"])
+        if count == 65536:  # packs of small tensors: the pack kernel's own counters
+            out[f"tensors_{count}x{size}"]["traffic"] = traffic_from_profile("adamw_fp32_packs")
         for pl, _, _ in sets:
             pl.close()
         del sets
