@@ -210,3 +210,61 @@ def test_tiny_tensors_adam_mini_scalar():
         assert np.allclose(vb[members], oV[k], rtol=1e-6, atol=0)
     say(f"Adam-mini: {N_T} one-block tensors, 3 steps, max relerr_tau {worst:.2e}")
     plan.close()
+
+
+# Launch shapes of the pack kernels: the default grid (a pack per workgroup,
+# loads before the prologue), smaller and larger units (pack capacity
+# follows min(unit, 2048)) and persistent grids (packs walked after the
+# prologue).  The step is elementwise, so every shape gives the same bits.
+FORMS = ((0, 0), (1024, 0), (8192, 0), (0, 13), (4096, 5))
+
+
+def _forms_layout():
+    rng = synth.host_rng(992, 0)
+    sizes = [int(x) for x in rng.integers(1, 701, 2000)] + [100003]
+    offs, pos = [], 0
+    for i, n in enumerate(sizes):
+        pos = (pos + 7) // 8 * 8 + (1 if rng.random() < 0.1 else 0)
+        offs.append(pos)
+        pos += n
+    return sizes, offs, pos
+
+
+@pytest.mark.parametrize("algo", ["adamw", "ademamix", "lion"])
+def test_pack_launch_forms_give_the_same_bits(algo):
+    print(f"case: pack launch forms, {algo}", flush=True)
+    sizes, offs, total = _forms_layout()
+    vw = lambda buf: [buf[o:o + n] for o, n in zip(offs, sizes)]
+    p0 = synth.host_normal(total, 0.02, 993, 0)
+    gs = [synth.host_normal(total, 1e-3, 993, t) for t in (1, 2)]
+    wd = [WD[i % 3] for i in range(len(sizes))]
+    algo_id = dict(adamw=osa.OPTIM_ALGO_ADAMW, ademamix=osa.OPTIM_ALGO_ADEMAMIX, lion=osa.OPTIM_ALGO_LION)[algo]
+    results = []
+    for tile, grid in FORMS:
+        P = torch.from_numpy(p0.copy()).to(DEV)
+        G = torch.zeros(total, device=DEV)
+        M, V, M2 = (torch.zeros(total, device=DEV) for _ in range(3))
+        kw = dict(m=vw(M), weight_decay=wd)
+        if algo != "lion":
+            kw["v"] = vw(V)
+        if algo == "ademamix":
+            kw["m2"] = vw(M2)
+        plan = osa.Plan(osa.TensorList(vw(P), vw(G), **kw), algo_id, tile=tile, grid=grid)
+        lr_d = torch.tensor([1e-3], device=DEV)
+        step = torch.zeros(1, dtype=torch.int32, device=DEV)
+        for g in gs:
+            G.copy_(torch.from_numpy(g))
+            if algo == "adamw":
+                osa.optim_step_adamw(plan.handle, osa.optim_adamw_hp(0.9, 0.999, 1e-8), lr_d, None, None, step)
+            elif algo == "ademamix":
+                osa.optim_step_ademamix(plan.handle, osa.optim_ademamix_hp(0.9, 0.999, 0.9999, 5.0, 1e-8), lr_d,
+                                        None, None, step)
+            else:
+                osa.optim_step_lion(plan.handle, osa.optim_lion_hp(0.9, 0.99), lr_d, None, None, step)
+        assert int(step.item()) == 2
+        results.append([x.cpu().numpy().view(np.uint32) for x in (P, M, V, M2)])
+        plan.close()
+    for (tile, grid), r in zip(FORMS[1:], results[1:]):
+        for a, b in zip(results[0], r):
+            assert np.array_equal(a, b), (algo, tile, grid, np.flatnonzero(a != b)[:8])
+    say(f"{algo}: {len(sizes)} tensors, {len(FORMS)} launch shapes, identical bits")
