@@ -16,8 +16,12 @@ namespace {
 // elements 22.5 -> 20.9 us, 2^23 42.1 -> 40.6 us, 2^24 80.8 -> 79.3 us;
 // AdEMAMix 28.8 -> 26.3, 54.9 -> 51.9, 104.2 -> 103.6 us.  From 2^25
 // elements on early loads of new workgroups crowd the stores of the
-// finishing ones (2^26: AdamW 311.7 -> 317.5 us), so larger plans take
-// 2048-element units of 2 groups without them (EG = 0).  The plan picks the
+// finishing ones (2^26: AdamW 311.7 -> 317.5 us; re-timed in one process
+// on the same arrays, early loads on 2048- / 4096-element units against
+// none: fp32 2^26 320.9 / 309.9 against 304.7 us, 2^28 1305.9 / 1275.0
+// against 1235.8 us, bf16 + remainder 2^28 1264.0 / 1234.1 against 1143.6
+// us, the 1.1B-element bf16 + remainder list 5179 / 5301 against 5070 us),
+// so larger plans take 2048-element units of 2 groups without them (EG = 0).  The plan picks the
 // unit size by its element count and the launcher the form by the units.
 template <int PK, int GK, bool ADE, int EG>
 __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
