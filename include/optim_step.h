@@ -214,8 +214,8 @@ int optim_plan_destroy(optim_plan *plan);
  * malloc'd as with optim_plan_create; free it with optim_plan_destroy).
  * A plan needing more workspace than that (Adam-mini lists of more than
  * ~8.5 billion elements, LAMB lists of more than ~4.2 billion, lists of more
- * than ~90,000 tensors) is refused with OPTIM_EWORKSPACE before anything is
- * touched.
+ * than ~90,000 tensors, or ~71,000 tensors small enough to share packs) is
+ * refused with OPTIM_EWORKSPACE before anything is touched.
  * One static workspace per device, shared by every call on that device: a
  * call overwrites the tables of the previous static plan of the current
  * device, which from then on fails (OPTIM_EINVAL) in every entry point.

@@ -122,7 +122,7 @@ struct Built {
     bool interleaved = false;       // blockwise: interleaved state layout
     std::vector<PackDesc> packs;    // packs of small tensors
     std::vector<int32_t> pack_off;
-    std::vector<TensorDesc> pack_td;
+    std::vector<PackMember> pack_td;
     int64_t pack_unit0 = 0;         // first pack unit (packs come last)
     Layout L{};
 };
@@ -271,7 +271,9 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
                        (int32_t)open_len};
             int32_t off = 0;
             for (int32_t t : open_pack) {
-                B.pack_td.push_back(B.tensors[t]);
+                const TensorDesc &T = B.tensors[t];
+                B.pack_td.push_back(PackMember{T.p, T.g, T.m, T.v, T.m2, T.rem, T.master, (int32_t)T.numel, T.group,
+                                               T.vec_ok, 0});
                 B.pack_off.push_back(off);
                 off += (int32_t)((B.tensors[t].numel + 3) / 4 * 4);
             }
@@ -498,7 +500,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     L.blockspan = off; off += align256(std::max<size_t>(1, B.blockspan.size()) * sizeof(int32_t));
     L.packs = off; off += align256(B.packs.size() * sizeof(PackDesc));
     L.pack_off = off; off += align256(B.pack_off.size() * sizeof(int32_t));
-    L.pack_td = off; off += align256(B.pack_td.size() * sizeof(TensorDesc));
+    L.pack_td = off; off += align256(B.pack_td.size() * sizeof(PackMember));
     // partial sums: Adam-mini's block sums (one per unit) and the gradient
     // norm pass (one per workgroup) share the region; they never overlap in
     // stream order
@@ -655,7 +657,7 @@ int create_on(const Built &B, const optim_tensor_list *list, int32_t algo, const
     std::memcpy(img.data() + B.L.blockspan, B.blockspan.data(), B.blockspan.size() * sizeof(int32_t));
     std::memcpy(img.data() + B.L.packs, B.packs.data(), B.packs.size() * sizeof(PackDesc));
     std::memcpy(img.data() + B.L.pack_off, B.pack_off.data(), B.pack_off.size() * sizeof(int32_t));
-    std::memcpy(img.data() + B.L.pack_td, B.pack_td.data(), B.pack_td.size() * sizeof(TensorDesc));
+    std::memcpy(img.data() + B.L.pack_td, B.pack_td.data(), B.pack_td.size() * sizeof(PackMember));
     if (is_blockwise(algo)) {
         Codebook *cb = reinterpret_cast<Codebook *>(img.data() + B.L.codebook);
         if (!build_map(7, cb->m8) || !build_map(8, cb->v8) || !build_map(3, cb->m4) || !build_map(4, cb->v4))
@@ -838,7 +840,7 @@ StepArgs step_args(optim_plan *P) {
     a.blockspan = reinterpret_cast<const int32_t *>(P->ws + P->L.blockspan);
     a.packs = reinterpret_cast<const PackDesc *>(P->ws + P->L.packs);
     a.pack_off = reinterpret_cast<const int32_t *>(P->ws + P->L.pack_off);
-    a.pack_td = reinterpret_cast<const TensorDesc *>(P->ws + P->L.pack_td);
+    a.pack_td = reinterpret_cast<const PackMember *>(P->ws + P->L.pack_td);
     a.pack_unit0 = P->pack_unit0;
     a.nblocks = P->nblocks;
     a.codebook = reinterpret_cast<const Codebook *>(P->ws + P->L.codebook);

@@ -197,8 +197,9 @@ __device__ __forceinline__ uint32_t f32_to_f16_rne(float x) {
 // Parameters: fp32 (P_F32); bf16 + int16 remainder rebuilding the fp32
 // master (P_BF16R); or an fp32 master with a bf16 / fp16 model copy in p
 // (P_MBF16 / P_MF16), rewritten from the updated master.
-template <int PK, int N, int LAY = kStrided>
-__device__ __forceinline__ void load_p(const TensorDesc &T, int64_t e, float (&p)[N]) {
+// (D: a TensorDesc, or a pack's PackMember record.)
+template <int PK, int N, int LAY = kStrided, class D>
+__device__ __forceinline__ void load_p(const D &T, int64_t e, float (&p)[N]) {
     if constexpr (PK == P_F32) {
         ldf<N, LAY>(static_cast<const float *>(T.p), e, p);
     } else if constexpr (PK == P_BF16R) {
@@ -212,8 +213,8 @@ __device__ __forceinline__ void load_p(const TensorDesc &T, int64_t e, float (&p
     }
 }
 
-template <int PK, int N>
-__device__ __forceinline__ void store_p(const TensorDesc &T, int64_t e, const float (&p)[N]) {
+template <int PK, int N, class D>
+__device__ __forceinline__ void store_p(const D &T, int64_t e, const float (&p)[N]) {
     if constexpr (PK == P_F32) {
         stf<N>(static_cast<float *>(T.p), e, p);
     } else if constexpr (PK == P_BF16R) {
@@ -319,19 +320,19 @@ __device__ __forceinline__ void lane_walk(int64_t start, int64_t len, bool vec_o
 // ---------------------------------------------------------------- packs
 // A pack span (tensor == kPackTensor) holds several small tensors end to end
 // (see PackDesc).  A workgroup copies the pack's offsets and its members'
-// tensor descriptors into LDS (one contiguous copy), then lane t takes the
+// PackMember records into LDS (one contiguous copy), then lane t takes the
 // pack's groups of 4 elements at 4t + q kSub, as in a unit of one tensor,
 // and finds the member holding each group by a binary search of the
 // offsets (every member starts at a multiple of 4, so a group never crosses
-// two members).  Member descriptors are then read from LDS.
+// two members).  Member records are then read from LDS.
 struct PackLds {
-    TensorDesc td[kMaxPackTensors];
+    PackMember td[kMaxPackTensors];
     int32_t off[kMaxPackTensors + 1];
 };
 
 // Copies pack P's tables into L; ends with a barrier.
 __device__ __forceinline__ void pack_fill(const StepArgs &a, const PackDesc &P, PackLds &L) {
-    constexpr int kWords = (int)(sizeof(TensorDesc) / 4);
+    constexpr int kWords = (int)(sizeof(PackMember) / 4);
     const uint32_t *src = reinterpret_cast<const uint32_t *>(a.pack_td + P.td_base);
     uint32_t *dst = reinterpret_cast<uint32_t *>(L.td);
     for (int i = threadIdx.x; i < P.k * kWords; i += kThreads) dst[i] = src[i];
@@ -534,8 +535,8 @@ struct AdamRegs {
 };
 
 // Loads; the gradient is multiplied by gscale (1 to defer the unscale).
-template <int PK, int GK, bool ADE, int N>
-__device__ __forceinline__ void adam_load(const TensorDesc &T, int64_t e, float gscale, AdamRegs<N> &r) {
+template <int PK, int GK, bool ADE, int N, class D>
+__device__ __forceinline__ void adam_load(const D &T, int64_t e, float gscale, AdamRegs<N> &r) {
     load_p<PK, N>(T, e, r.p);
     load_g<GK, N>(T.g, e, gscale, r.g);
     ldf<N>(T.m, e, r.m);
@@ -569,17 +570,16 @@ __device__ __forceinline__ void adam_math(AdamRegs<N> &r, const AdamK &k, float 
     }
 }
 
-template <int PK, bool ADE, int N>
-__device__ __forceinline__ void adam_store(const TensorDesc &T, int64_t e, const AdamRegs<N> &r) {
+template <int PK, bool ADE, int N, class D>
+__device__ __forceinline__ void adam_store(const D &T, int64_t e, const AdamRegs<N> &r) {
     store_p<PK, N>(T, e, r.p);
     stf<N>(T.m, e, r.m);
     stf<N>(T.v, e, r.v);
     if constexpr (ADE) stf<N>(T.m2, e, r.m2);
 }
 
-template <int PK, int GK, bool ADE, int N>
-__device__ __forceinline__ void adam_elems(const TensorDesc &T, int64_t e, const AdamK &k,
-                                           float lw) {
+template <int PK, int GK, bool ADE, int N, class D>
+__device__ __forceinline__ void adam_elems(const D &T, int64_t e, const AdamK &k, float lw) {
     AdamRegs<N> r;
     adam_load<PK, GK, ADE, N>(T, e, k.inv_scale, r);
     adam_math<ADE, N>(r, k, lw);
@@ -616,7 +616,7 @@ __device__ __forceinline__ void adam_pack_finish(const PackLds &L, const PackSlo
 #pragma unroll
     for (int q = 0; q < G; ++q) {
         if (sl.n[q] == 0) continue;
-        const TensorDesc &T = L.td[sl.j[q]];
+        const PackMember &T = L.td[sl.j[q]];
         const float lw = S.lrwd[T.group];
         if (sl.n[q] == kVec && T.vec_ok)
             adam_elems<PK, GK, ADE, kVec>(T, sl.e[q], k, lw);

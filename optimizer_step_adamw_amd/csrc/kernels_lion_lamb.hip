@@ -22,8 +22,8 @@ __device__ __forceinline__ void lion_math(float (&p)[N], const float (&g)[N], fl
     }
 }
 
-template <int PK, int GK, int N>
-__device__ __forceinline__ void lion_elems(const TensorDesc &T, int64_t e, const AdamK &k, float lw) {
+template <int PK, int GK, int N, class D>
+__device__ __forceinline__ void lion_elems(const D &T, int64_t e, const AdamK &k, float lw) {
     float p[N], g[N], m[N];
     load_p<PK, N>(T, e, p);
     load_g<GK, N>(T.g, e, k.inv_scale, g);
@@ -45,7 +45,7 @@ __device__ __forceinline__ void lion_pack_load(const PackLds &L, const PackSlots
     if (!sl.whole) return;
 #pragma unroll
     for (int q = 0; q < G; ++q) {
-        const TensorDesc &T = L.td[sl.j[q]];
+        const PackMember &T = L.td[sl.j[q]];
         load_p<PK, kVec>(T, sl.e[q], r.p[q]);
         load_g<GK, kVec>(T.g, sl.e[q], gscale, r.g[q]);
         ldf<kVec>(T.m, sl.e[q], r.m[q]);
@@ -64,7 +64,7 @@ __device__ __forceinline__ void lion_pack_finish(const PackLds &L, const PackSlo
         }
 #pragma unroll
         for (int q = 0; q < G; ++q) {
-            const TensorDesc &T = L.td[sl.j[q]];
+            const PackMember &T = L.td[sl.j[q]];
             store_p<PK, kVec>(T, sl.e[q], r.p[q]);
             stf<kVec>(T.m, sl.e[q], r.m[q]);
         }
@@ -73,7 +73,7 @@ __device__ __forceinline__ void lion_pack_finish(const PackLds &L, const PackSlo
 #pragma unroll
     for (int q = 0; q < G; ++q) {
         if (sl.n[q] == 0) continue;
-        const TensorDesc &T = L.td[sl.j[q]];
+        const PackMember &T = L.td[sl.j[q]];
         const float lw = S.lrwd[T.group];
         if (sl.n[q] == kVec && T.vec_ok)
             lion_elems<PK, GK, kVec>(T, sl.e[q], k, lw);

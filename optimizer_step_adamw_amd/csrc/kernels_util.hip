@@ -22,10 +22,10 @@ namespace {
 // sets found_inf, makes the norm non-finite.  (Squares in fp64 on every
 // pass measured 13% slower on the 1.1B bf16 list: 373 against 330 us.)
 
-// This lane's N gradient elements of T from element e (N = 1, or whole
-// groups of 4 in the step layout).
-template <int GK, bool NORM, int N, class Acc>
-__device__ __forceinline__ bool scan_elems(const TensorDesc &T, int64_t e, Acc &acc) {
+// This lane's N gradient elements of T (a TensorDesc or a pack's PackMember)
+// from element e (N = 1, or whole groups of 4 in the step layout).
+template <int GK, bool NORM, int N, class Acc, class D>
+__device__ __forceinline__ bool scan_elems(const D &T, int64_t e, Acc &acc) {
     bool bad = false;
     float x[N];
     if constexpr (GK == G_F32) {
@@ -79,7 +79,7 @@ __device__ __forceinline__ bool scan_workgroup(const StepArgs &a, PackLds &PL, A
                 const PackSlots<2> sl = pack_slots<2>(PL, P, v0);
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
-                    const TensorDesc &T = PL.td[sl.j[q]];
+                    const PackMember &T = PL.td[sl.j[q]];
                     if (sl.n[q] == kVec && T.vec_ok) {
                         bad |= scan_elems<GK, NORM, kVec>(T, sl.e[q], acc);
                     } else {

@@ -94,8 +94,9 @@ static_assert(sizeof(TensorDesc) == 152, "TensorDesc layout");
 // their own (the step kernels of single tensors stay free of their registers
 // and LDS).  Member j holds the pack's
 // elements [off[j], off[j + 1]), off[j] = pack_off[off_base + j], off[0] = 0,
-// off[k] = len; pack_td[td_base + j] is a copy of its tensor descriptor, so
-// a workgroup loads a pack's tables with one contiguous copy into LDS.
+// off[k] = len; pack_td[td_base + j] is its PackMember record (the fields of
+// its tensor descriptor the pack kernels read), so a workgroup loads a
+// pack's tables with one contiguous copy into LDS.
 constexpr int32_t kPackTensor = -2;
 constexpr int32_t kMaxPackTensors = 64;  // members per pack (LDS: 64 descriptors, ~10 KB)
 // Pack capacity: 2048 elements, two groups of 4 per lane.  A pack kernel's
@@ -107,6 +108,23 @@ constexpr int32_t kMaxPackTensors = 64;  // members per pack (LDS: 64 descriptor
 // 1024-element packs: 65536 tensors of 256 89.6 / 84.5 / 84.5 us, 32768 of
 // 512 87.7 / 83.1 / 82.8 us, 262144 of 64 98.5 / 88.4 / 90.6 us.
 constexpr int64_t kPackElems = 2048;
+// A pack member as the pack kernels see it: its arrays, length, weight-decay
+// group and alignment (72 bytes, against 152 for the full TensorDesc; the
+// tables are read from HBM once per step, so their size is traffic).
+struct PackMember {
+    void *p;
+    const void *g;
+    float *m;
+    float *v;
+    float *m2;
+    uint16_t *rem;
+    float *master;
+    int32_t numel;        // at most kPackElems / 2
+    int32_t group;
+    int32_t vec_ok;
+    int32_t pad_;
+};
+static_assert(sizeof(PackMember) == 72, "PackMember layout");
 struct PackDesc {         // 16 bytes
     int32_t td_base;      // index of member 0 in pack_td
     int32_t off_base;     // index of off[0] in pack_off
@@ -226,7 +244,7 @@ struct StepArgs {
     int32_t cus;              // compute units of the device
     const PackDesc *packs;    // packs of small tensors (elementwise plans)
     const int32_t *pack_off;
-    const TensorDesc *pack_td;
+    const PackMember *pack_td;
     int64_t pack_unit0;       // units [pack_unit0, nunits) of the plan are packs
     int32_t grid_request;     // persistent workgroups (0 = see units_per_wg)
     int32_t units_per_wg;     // without a persistent grid: consecutive units
