@@ -232,6 +232,22 @@ __device__ __forceinline__ void store_p(const D &T, int64_t e, const float (&p)[
     }
 }
 
+// fl32(1/a), correctly rounded, for a > 0.  Inside [2^-126, 2^126] (normal a
+// with a normal reciprocal) Markstein's correction of the hardware
+// reciprocal -- y = rcp(a), e = fma(-a, y, 1), y + e y as one fma (P.
+// Markstein, "Computation of elementary functions on the IBM RISC
+// System/6000 processor", IBM J. Res. Dev. 34(1), 1990) -- gives the IEEE
+// quotient for every such a on gfx950 (a GPU test checks all 2^32 inputs);
+// elsewhere (denormal a, or a denormal quotient) the IEEE division.  Three
+// VALU instructions instead of the division's ten.
+__device__ __forceinline__ float recip_rn(float a) {
+    if (a >= 0x1p-126f && a <= 0x1p126f) {
+        const float y = __builtin_amdgcn_rcpf(a);
+        return __builtin_fmaf(__builtin_fmaf(-a, y, 1.0f), y, y);
+    }
+    return 1.0f / a;
+}
+
 // Gradient load with the AMP unscale applied exactly once ([LTN] analysis).
 template <int GK, int N, int LAY = kStrided>
 __device__ __forceinline__ void load_g(const void *g, int64_t e, float s, float (&x)[N]) {

@@ -106,7 +106,7 @@ __device__ __forceinline__ uint64_t quantize_lane(const float (&x)[E],
     for (int j = 1; j < E; ++j) lm = fmaxf(lm, fabsf(x[j]));
     const float mx = __uint_as_float(group_max<L>(lm == lm ? __float_as_uint(lm) : 0u));
     A = mx;
-    const float r = mx > 0.0f ? 1.0f / mx : 0.0f;
+    const float r = mx > 0.0f ? recip_rn(mx) : 0.0f;
     uint64_t out = 0;
 #pragma unroll
     for (int j = 0; j < E; ++j) {

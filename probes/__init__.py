@@ -1,9 +1,11 @@
-"""Access-pattern ceiling probes for the benchmark (stream_probe.hip).
+"""Access-pattern ceiling probes for the benchmark (stream_probe.hip), and
+device checks of the step library's numeric helpers for the test suite
+(numerics_check.hip).
 
-Benchmark-only: a separate library, not part of liboptim_step.so's C ABI.
-Each probe streams one step kernel's exact access pattern (arrays, lane
-layout, unit size, access kind) with no arithmetic; bench.py reports each
-kernel's bandwidth as a fraction of its pattern's measured ceiling.
+A separate library, not part of liboptim_step.so's C ABI.  Each probe
+streams one step kernel's exact access pattern (arrays, lane layout, unit
+size, access kind) with no arithmetic; bench.py reports each kernel's
+bandwidth as a fraction of its pattern's measured ceiling.
 """
 from __future__ import annotations
 
@@ -12,7 +14,8 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "stream_probe.hip")
+ROOT = os.path.dirname(HERE)
+SRCS = [os.path.join(HERE, "stream_probe.hip"), os.path.join(HERE, "numerics_check.hip")]
 LIB_PATH = os.path.join(HERE, "libstream_probe.so")
 ARCH = os.environ.get("OPTIM_STEP_ARCH", "gfx950")
 
@@ -23,8 +26,11 @@ def build(verbose: bool = False) -> str:
     tmp = LIB_PATH + ".tmp"
     cmd = ["/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc",
            f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           # the step library's floating-point flags, for the numerics checks
+           "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-Wall", "-Wno-unused-command-line-argument", "-o", tmp, SRC]
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "optimizer_step_adamw_amd", "csrc"),
+           "-Wall", "-Wno-unused-command-line-argument", "-o", tmp] + SRCS
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
@@ -47,6 +53,7 @@ def lib() -> ctypes.CDLL:
             "probe_blockwise": [P, P, P, P, P, P, i64, i32, i32, i32, P],
             "probe_read": [P, i64, i32, P, P],
             "probe_copy": [P, P, i64, P],
+            "check_recip_rn": [ctypes.c_uint32, ctypes.c_uint32, P, P, P],
         }
         for name, args in sigs.items():
             fn = getattr(L, name)
