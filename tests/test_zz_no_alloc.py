@@ -94,3 +94,34 @@ def test_static_plans_match_workspace_plans_twice():
     osa.optim_plan_destroy(h2)
     ref.close()
     ref2.close()
+
+
+@pytest.mark.parametrize("ademamix", [False, True])
+def test_static_plan_with_packs_matches_workspace_plan(ademamix):
+    """A list of small tensors, laid end to end in packs (their member
+    records in the static workspace), then a larger tensor: the static plan
+    steps bit for bit as the workspace plan, with bf16 params + remainders."""
+    print(f"case: static plan with packs, ademamix={ademamix}", flush=True)
+    sizes = [300, 7, 1000, 4, 65, 513, 9000, 1, 2047, 12]
+    p0 = [host_normal(n, 0.02, 963, 0, i, 0) for i, n in enumerate(sizes)]
+    A, B = _twin(p0, param_bf16=True, ademamix=ademamix)
+    wd = [0.1 if i % 3 else 0.0 for i in range(len(sizes))]
+    algo = osa.OPTIM_ALGO_ADEMAMIX if ademamix else osa.OPTIM_ALGO_ADAMW
+    ref = osa.Plan(A.tensor_list(wd), algo)
+    h = osa.optim_plan_create_static(B.tensor_list(wd), algo, None)
+    sa, sb = DevScalars(1e-3), DevScalars(1e-3)
+    for t in (1, 2, 3):
+        _grads(A, sizes, 3, t)
+        for x, y in zip(B.g, A.g):
+            x.copy_(y)
+        for plan, s in ((ref.handle, sa), (h, sb)):
+            if ademamix:
+                osa.optim_step_ademamix(plan, osa.optim_ademamix_hp(0.9, 0.999, 0.9999, 5.0, 1e-8), s.lr, None,
+                                        None, s.step)
+            else:
+                osa.optim_step_adamw(plan, osa.optim_adamw_hp(0.9, 0.999, 1e-8), s.lr, None, None, s.step)
+    torch.cuda.synchronize()
+    assert all_equal(A.buffers(), B.buffers()) and int(sb.step.item()) == 3
+    say(f"{'AdEMAMix' if ademamix else 'AdamW'} with packs: static plan equals the workspace plan over 3 steps")
+    osa.optim_plan_destroy(h)
+    ref.close()
