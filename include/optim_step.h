@@ -131,8 +131,11 @@ typedef struct optim_tensor_list {
  *              (blockwise: at least 2048); 0 = 2048 (AdamW, AdEMAMix
  *              with fp32 moments and Lion on lists of more than 2^20 and at
  *              most 2^24 elements 4096; Adam-mini, LAMB and fp16 states 4096;
- *              blockwise 8-bit and 4-bit 8192, and blockwise AdEMAMix
- *              8-bit 8192, 4-bit 16384)
+ *              blockwise 8-bit 4096 in the separate state layout, 8192 in
+ *              the interleaved one, 4-bit 8192, and blockwise AdEMAMix
+ *              8-bit 8192, 4-bit 16384).  AdamW, AdEMAMix and Lion lay
+ *              runs of tensors of at most min(tile, 2048) / 2 elements end
+ *              to end in shared units of up to min(tile, 2048) elements
  *  state_dtype AdamW only: OPTIM_F32 (0, default) fp32 moments; OPTIM_F16
  *              or OPTIM_BF16 16-bit moments with a per-tensor scale
  *              ([TE] review: state scaling), see optim_step_adamw
