@@ -513,11 +513,21 @@ __device__ __forceinline__ float uniform(float x) {
 
 // ---------------------------------------------------------------- partial sums
 // Sum of x[i * stride] over i in [i0, i1), this lane taking i0 + lane,
-// i0 + lane + kThreads, ...: eight independent accumulators (loads in
-// flight together), combined in a fixed order -- deterministic.
+// i0 + lane + kThreads, ...: eight independent accumulators, combined in a
+// fixed order -- deterministic.  Loads go out 32 at a time (a whole-matrix
+// Adam-mini block has up to ~11,000 unit partials, 43 a lane), each
+// accumulator still adding its elements in ascending order, so the sum is
+// the same as with 8 at a time.
 __device__ __forceinline__ double lane_sum(const double *x, int64_t stride, int64_t i0, int64_t i1) {
     double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     int64_t i = i0 + threadIdx.x;
+    for (; i + 31 * kThreads < i1; i += 32 * kThreads) {
+        double y[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) y[j] = x[(i + j * kThreads) * stride];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) acc[j & 7] += y[j];
+    }
     for (; i + 7 * kThreads < i1; i += 8 * kThreads) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] += x[(i + j * kThreads) * stride];
