@@ -142,10 +142,18 @@ def _check(rc: int, fn: str) -> None:
 
 
 def _ptr(t) -> Optional[int]:
+    """Device address of a tensor argument (None and plain integers pass
+    through).  The kernels walk numel() elements from data_ptr(), so a torch
+    tensor must be on the GPU and contiguous: anything else is refused here,
+    before the library sees it."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if hasattr(t, "is_cuda") and not t.is_cuda:
+        raise ValueError(f"expected a GPU tensor, got one on {t.device}")
+    if hasattr(t, "is_contiguous") and not t.is_contiguous():
+        raise ValueError(f"expected a contiguous tensor, got shape {tuple(t.shape)} with strides {t.stride()}")
     return t.data_ptr()
 
 

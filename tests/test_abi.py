@@ -344,3 +344,33 @@ def test_static_workspace_holds_the_7b_adam_mini_plan(L):
                         mini_kind=kinds, head_numel=heads, numel=sizes)
     need = ws(tl, osa.OPTIM_ALGO_ADAM_MINI)
     assert 8 << 20 < need <= osa.OPTIM_STATIC_WORKSPACE_BYTES, need
+
+
+def test_binding_refuses_host_and_strided_tensors():
+    """The kernels walk numel() elements from each tensor's address, so the
+    binding refuses a tensor that is not on the GPU, or not contiguous,
+    before the library sees it."""
+    import torch
+    host = torch.zeros(16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        osa.TensorList([host], [host], m=[host], v=[host], weight_decay=[0.0])
+    strided = torch.zeros(4, 4).t()
+
+    class Cuda:  # a stand-in that claims the GPU but is a transposed view
+        is_cuda = True
+
+        def __init__(self, t):
+            self.t = t
+            self.shape = t.shape
+
+        def is_contiguous(self):
+            return self.t.is_contiguous()
+
+        def stride(self):
+            return self.t.stride()
+
+        def data_ptr(self):
+            return self.t.data_ptr()
+
+    with pytest.raises(ValueError, match="contiguous"):
+        osa.optim_step_adamw(None, osa.optim_adamw_hp(0.9, 0.999, 1e-8), Cuda(strided), None, None, None)
