@@ -374,3 +374,15 @@ def test_binding_refuses_host_and_strided_tensors():
 
     with pytest.raises(ValueError, match="contiguous"):
         osa.optim_step_adamw(None, osa.optim_adamw_hp(0.9, 0.999, 1e-8), Cuda(strided), None, None, None)
+
+
+def test_trace_calls_refuse_bad_arguments_on_the_host(L):
+    """The kernel-trace entry points validate before touching a device."""
+    import ctypes
+    count, dropped = ctypes.c_int32(-1), ctypes.c_int64(-1)
+    recs = (osa.optim_kernel_time * 4)()
+    assert L.optim_plan_trace(None, 16) == osa.OPTIM_EINVAL
+    assert b"plan" in L.optim_last_error()
+    assert L.optim_plan_trace_read(None, recs, 4, ctypes.byref(count), ctypes.byref(dropped)) == osa.OPTIM_EINVAL
+    assert count.value == -1  # nothing written on an error
+    assert L.optim_plan_destroy(None) == osa.OPTIM_OK  # destroying NULL is a no-op
