@@ -175,13 +175,13 @@ MINI_LIST = [("tok_embeddings.weight", 37 * 64), ("layers.0.attention.wq.weight"
 
 
 def _mini_run(steps, key, grad_bf16=False, lr=3e-4, wd=0.1, dim=64, heads=4, items=MINI_LIST, tile=0,
-              segment_bytes=0, grid=0):
+              segment_bytes=0, grid=0, param_bf16=False):
     names = [n for n, _ in items]
     sizes = [s for _, s in items]
     kinds, hn, wds = osa.adam_mini_partition(names, sizes, dim=dim, n_heads=heads, weight_decay=wd)
     vlen = [s if k == osa.OPTIM_MINI_FULL_V else s // h for k, s, h in zip(kinds, sizes, hn)]
     p0 = _p0(sizes, key)
-    st = AdamState(_to_dev(p0), grad_bf16=grad_bf16, v_len=vlen)
+    st = AdamState(_to_dev(p0), grad_bf16=grad_bf16, param_bf16=param_bf16, v_len=vlen)
     plan = osa.Plan(st.tensor_list(wds, mini_kind=kinds, head_numel=hn), osa.OPTIM_ALGO_ADAM_MINI, tile=tile,
                     segment_bytes=segment_bytes, grid=grid)
     sc = DevScalars(lr)
@@ -201,13 +201,22 @@ def _mini_run(steps, key, grad_bf16=False, lr=3e-4, wd=0.1, dim=64, heads=4, ite
                 orc.adamw_step(op[i], om[i], ov[i], g[i], lr32, 0.9, 0.95, 1e-8, owd[i], t)
             else:
                 orc.adam_mini_step(op[i], om[i], ov[i], g[i], oblock[i], lr32, 0.9, 0.95, 1e-8, owd[i], t)
-        err = max(relerr_tau(st.p[i].cpu().numpy(), op[i], lr32) for i in range(len(sizes)))
+        err = max(relerr_tau((st.master(i) if param_bf16 else st.p[i]).cpu().numpy(), op[i], lr32)
+                  for i in range(len(sizes)))
         assert err <= (TOL_STEP1 if t == 1 else TOL_RUN), (t, err)
     return st
 
 
 def test_adam_mini_small_list():
     _mini_run(10, 5)
+
+
+@pytest.mark.parametrize("grad_bf16,grid,segment_bytes", [(True, 0, 0), (False, 7, 20000)])
+def test_adam_mini_bf16_params_with_remainders(grad_bf16, grid, segment_bytes):
+    """bf16 params + int16 remainders ([TE]: the fp32 master rebuilt
+    bit-exactly) under Adam-mini's shared-v update, against the oracle on
+    the reconstructed master."""
+    _mini_run(6, 8, grad_bf16=grad_bf16, param_bf16=True, grid=grid, segment_bytes=segment_bytes)
 
 
 def test_adam_mini_bf16_grads_and_unaligned_blocks():
