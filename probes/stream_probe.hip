@@ -44,29 +44,42 @@ __device__ __forceinline__ void nts(V *p, V x) { __builtin_nontemporal_store(x, 
 __device__ __forceinline__ u32x4 bits(f32x4 x) { return __builtin_bit_cast(u32x4, x); }
 __device__ __forceinline__ f32x4 flt(u32x4 x) { return __builtin_bit_cast(f32x4, x); }
 
-// lane t owns elements 4t..4t+3 of each group of 1024; group j at +j*1024
+// lane t owns elements 4t..4t+3 of each group of 1024; group j at +j*1024.
+// Accesses go array by array (all G groups of p, then of g, ...), in the
+// order the step kernels issue them (one array's groups 4 KiB apart, back
+// to back; measured on MI355X 1-2% faster than group by group).
 template <int G, int NS>
 __global__ __launch_bounds__(kThreads) void fp32_pattern(float *p, const float *g, float *m, float *v, float *m2) {
     const int64_t e = (int64_t)blockIdx.x * (G * 1024) + threadIdx.x * 4;
     u32x4 P[G], Gr[G], M[G], V[G], M2[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        P[j] = bits(ntl((const f32x4 *)(p + e + j * 1024)));
-        Gr[j] = bits(ntl((const f32x4 *)(g + e + j * 1024)));
-        M[j] = bits(ntl((const f32x4 *)(m + e + j * 1024)));
-        if (NS >= 4) V[j] = bits(ntl((const f32x4 *)(v + e + j * 1024)));
-        if (NS >= 5) M2[j] = bits(ntl((const f32x4 *)(m2 + e + j * 1024)));
+    for (int j = 0; j < G; ++j) P[j] = bits(ntl((const f32x4 *)(p + e + j * 1024)));
+#pragma unroll
+    for (int j = 0; j < G; ++j) Gr[j] = bits(ntl((const f32x4 *)(g + e + j * 1024)));
+#pragma unroll
+    for (int j = 0; j < G; ++j) M[j] = bits(ntl((const f32x4 *)(m + e + j * 1024)));
+    if (NS >= 4) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) V[j] = bits(ntl((const f32x4 *)(v + e + j * 1024)));
+    }
+    if (NS >= 5) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) M2[j] = bits(ntl((const f32x4 *)(m2 + e + j * 1024)));
     }
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        nts((f32x4 *)(p + e + j * 1024), flt(P[j] ^ Gr[j]));
-        if (NS >= 4) {
-            nts((f32x4 *)(m + e + j * 1024), flt(V[j]));
-            nts((f32x4 *)(v + e + j * 1024), flt(M[j]));
-        } else {
-            nts((f32x4 *)(m + e + j * 1024), flt(M[j] ^ Gr[j]));
-        }
-        if (NS >= 5) nts((f32x4 *)(m2 + e + j * 1024), flt(M2[j] ^ Gr[j]));
+    for (int j = 0; j < G; ++j) nts((f32x4 *)(p + e + j * 1024), flt(P[j] ^ Gr[j]));
+    if (NS >= 4) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) nts((f32x4 *)(m + e + j * 1024), flt(V[j]));
+#pragma unroll
+        for (int j = 0; j < G; ++j) nts((f32x4 *)(v + e + j * 1024), flt(M[j]));
+    } else {
+#pragma unroll
+        for (int j = 0; j < G; ++j) nts((f32x4 *)(m + e + j * 1024), flt(M[j] ^ Gr[j]));
+    }
+    if (NS >= 5) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) nts((f32x4 *)(m2 + e + j * 1024), flt(M2[j] ^ Gr[j]));
     }
 }
 
@@ -77,21 +90,25 @@ __global__ __launch_bounds__(kThreads) void bf16r_pattern(uint16_t *p, uint16_t 
     const int64_t e = (int64_t)blockIdx.x * (G * 1024) + threadIdx.x * 4;
     u32x2 P[G], R[G], Gr[G];
     u32x4 M[G], V[G];
+    // array by array, as fp32_pattern
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        P[j] = ntl((const u32x2 *)(p + e + j * 1024));
-        R[j] = ntl((const u32x2 *)(r + e + j * 1024));
-        Gr[j] = ntl((const u32x2 *)(g + e + j * 1024));
-        M[j] = bits(ntl((const f32x4 *)(m + e + j * 1024)));
-        V[j] = bits(ntl((const f32x4 *)(v + e + j * 1024)));
-    }
+    for (int j = 0; j < G; ++j) P[j] = ntl((const u32x2 *)(p + e + j * 1024));
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-        nts((u32x2 *)(p + e + j * 1024), R[j] ^ Gr[j]);
-        nts((u32x2 *)(r + e + j * 1024), P[j]);
-        nts((f32x4 *)(m + e + j * 1024), flt(V[j]));
-        nts((f32x4 *)(v + e + j * 1024), flt(M[j]));
-    }
+    for (int j = 0; j < G; ++j) R[j] = ntl((const u32x2 *)(r + e + j * 1024));
+#pragma unroll
+    for (int j = 0; j < G; ++j) Gr[j] = ntl((const u32x2 *)(g + e + j * 1024));
+#pragma unroll
+    for (int j = 0; j < G; ++j) M[j] = bits(ntl((const f32x4 *)(m + e + j * 1024)));
+#pragma unroll
+    for (int j = 0; j < G; ++j) V[j] = bits(ntl((const f32x4 *)(v + e + j * 1024)));
+#pragma unroll
+    for (int j = 0; j < G; ++j) nts((u32x2 *)(p + e + j * 1024), R[j] ^ Gr[j]);
+#pragma unroll
+    for (int j = 0; j < G; ++j) nts((u32x2 *)(r + e + j * 1024), P[j]);
+#pragma unroll
+    for (int j = 0; j < G; ++j) nts((f32x4 *)(m + e + j * 1024), flt(V[j]));
+#pragma unroll
+    for (int j = 0; j < G; ++j) nts((f32x4 *)(v + e + j * 1024), flt(M[j]));
 }
 
 // blockwise 2-state step, separate layout, 4 elements a lane per row of
