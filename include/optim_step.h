@@ -48,7 +48,7 @@ extern "C" {
 
 /* ---- enumerations ------------------------------------------------------ */
 enum { OPTIM_F32 = 0, OPTIM_BF16 = 1, OPTIM_F16 = 2 };
-/* blockwise state layouts (optim_plan_opts.state_layout)                  */
+/* state layouts (optim_plan_opts.state_layout)                            */
 enum { OPTIM_LAYOUT_SEPARATE = 0, OPTIM_LAYOUT_INTERLEAVED = 1 };
 enum {
     OPTIM_ALGO_ADAMW = 0,
@@ -74,7 +74,9 @@ enum { OPTIM_SCHED_NONE = 0, OPTIM_SCHED_COSINE = 1 };
  *  m, v         float[numel] first / second moment (AdamW, AdEMAMix, LAMB,
  *               Adam-mini FULL_V).  Adam-mini HEAD/SCALAR: m float[numel]
  *               and v float[numel/head_numel] (one shared v per block).
- *               Lion: m only (v NULL).
+ *               Lion: m only (v NULL).  AdamW / AdEMAMix in the
+ *               interleaved moment layout (opts->state_layout): m holds all
+ *               of a tensor's moments, v and m2 are NULL.
  *  m2           float[numel] AdEMAMix slow EMA; NULL otherwise
  *  remainder    int16[numel] low halves of the fp32 master ([TE]); required
  *               when param_dtype is BF16, NULL otherwise
@@ -146,8 +148,20 @@ typedef struct optim_tensor_list {
  *              run of full-v tensors; 0 = 384 MiB (the gradients are read
  *              twice, the second time mostly from the Infinity Cache).  Results
  *              do not depend on it.  Negative: OPTIM_EINVAL.
- *  state_layout  OPTIM_ALGO_BLOCKWISE only.  OPTIM_LAYOUT_SEPARATE (0,
- *              default): qm / qv and absmax_m / absmax_v are four arrays.
+ *  state_layout  OPTIM_LAYOUT_SEPARATE (0, default): every state is an
+ *              array of its own.  OPTIM_LAYOUT_INTERLEAVED (1), for
+ *              OPTIM_ALGO_ADAMW and OPTIM_ALGO_ADEMAMIX with fp32 moments:
+ *              the moments of a tensor share its m array, in blocks of 1024
+ *              elements -- block b holds m, then v (then AdEMAMix's m2) of
+ *              elements [1024 b, 1024 b + 1024), 1024 floats each, the last
+ *              block whole too -- so m holds K * 1024 * ceil(numel / 1024)
+ *              floats (K = 2 AdamW, 3 AdEMAMix); v and m2 must be NULL.
+ *              Element e's m sits at m[K * 1024 * (e / 1024) + e % 1024], its
+ *              v 1024 floats further, its m2 2048.  The values are those of
+ *              separate arrays, bit for bit; the step streams one (AdamW) or
+ *              two (AdEMAMix) arrays fewer.
+ *              For OPTIM_ALGO_BLOCKWISE, OPTIM_LAYOUT_SEPARATE: qm / qv and
+ *              absmax_m / absmax_v are four arrays.
  *              OPTIM_LAYOUT_INTERLEAVED (1): each element's m and v codes
  *              sit side by side in qm -- 8-bit: 2 bytes per element, m
  *              first; 4-bit: 1 byte per element, m in the low nibble, v in

@@ -178,10 +178,15 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     const int32_t layout = opts ? opts->state_layout : OPTIM_LAYOUT_SEPARATE;
     if (layout != OPTIM_LAYOUT_SEPARATE && layout != OPTIM_LAYOUT_INTERLEAVED)
         return fail(OPTIM_EINVAL, "unknown state_layout");
-    if (layout == OPTIM_LAYOUT_INTERLEAVED && algo != OPTIM_ALGO_BLOCKWISE)
-        return fail(OPTIM_EUNSUPPORTED, "the interleaved state layout is for the 2-state blockwise step");
-    const bool il = layout == OPTIM_LAYOUT_INTERLEAVED;
-    B.interleaved = il;
+    const bool adam_like = algo == OPTIM_ALGO_ADAMW || algo == OPTIM_ALGO_ADEMAMIX;
+    if (layout == OPTIM_LAYOUT_INTERLEAVED && algo != OPTIM_ALGO_BLOCKWISE && !adam_like)
+        return fail(OPTIM_EUNSUPPORTED,
+                    "the interleaved state layout is for AdamW, AdEMAMix and the 2-state blockwise step");
+    // blockwise: m and v codes side by side; AdamW / AdEMAMix: the moments
+    // of each tensor in one array, in blocks of kMomentBlock elements
+    const bool il = layout == OPTIM_LAYOUT_INTERLEAVED && algo == OPTIM_ALGO_BLOCKWISE;
+    const bool mom_il = layout == OPTIM_LAYOUT_INTERLEAVED && adam_like;
+    B.interleaved = il || mom_il;
     if (opts && opts->grid < 0) return fail(OPTIM_EINVAL, "negative grid");
     B.grid = opts ? opts->grid : 0;
     if (opts && opts->tile < 0) return fail(OPTIM_EINVAL, "negative tile");
@@ -195,6 +200,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     const bool states16 = sdt != OPTIM_F32;
     if (states16 && algo != OPTIM_ALGO_ADAMW) return fail(OPTIM_EUNSUPPORTED, "16-bit states are for AdamW plans");
     if (states16 && masterw) return fail(OPTIM_EUNSUPPORTED, "16-bit states take fp32 or bf16 + remainder params");
+    if (states16 && mom_il) return fail(OPTIM_EUNSUPPORTED, "the interleaved moment layout holds fp32 moments");
     if (n > 0 && states16 && (!list->scale_m || !list->scale_v))
         return fail(OPTIM_EINVAL, "16-bit states need scale_m and scale_v arrays");
     B.states16 = states16;
@@ -226,9 +232,10 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
     if (n > 0 && (!list->numel || !list->param || !list->grad || !list->weight_decay))
         return fail(OPTIM_EINVAL, "numel, param, grad and weight_decay arrays are required");
     const bool need_mv = !is_blockwise(algo) && algo != OPTIM_ALGO_LION;
-    if (n > 0 && need_mv && (!list->m || !list->v)) return fail(OPTIM_EINVAL, "m and v arrays are required");
+    if (n > 0 && need_mv && (!list->m || (!mom_il && !list->v)))
+        return fail(OPTIM_EINVAL, mom_il ? "the m array is required" : "m and v arrays are required");
     if (n > 0 && algo == OPTIM_ALGO_LION && !list->m) return fail(OPTIM_EINVAL, "Lion needs the m array");
-    if (n > 0 && algo == OPTIM_ALGO_ADEMAMIX && !list->m2)
+    if (n > 0 && algo == OPTIM_ALGO_ADEMAMIX && !mom_il && !list->m2)
         return fail(OPTIM_EINVAL, "AdEMAMix needs the m2 array");
     if (n > 0 && is_blockwise(algo) && (!list->qm || (!il && !list->qv) || !list->absmax_m || (!il && !list->absmax_v)))
         return fail(OPTIM_EINVAL, il ? "interleaved blockwise plans need qm and absmax_m"
@@ -348,7 +355,20 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
             }
         }
         T.kind = kind;
-        if (need_mv) {
+        if (mom_il) {
+            // m, v (, m2) of each block of kMomentBlock elements side by side
+            // in m: K kMomentBlock floats per block, the last block whole
+            const int K = algo == OPTIM_ALGO_ADEMAMIX ? 3 : 2;
+            if ((list->v && list->v[i]) || (list->m2 && list->m2[i]))
+                return fail(OPTIM_EINVAL, ti + "interleaved moments: v and m2 must be NULL (they live in m)");
+            T.m = static_cast<float *>(list->m[i]);
+            if (numel > 0 && !T.m) return fail(OPTIM_EINVAL, ti + "NULL m");
+            if (!aligned(T.m, 4)) return fail(OPTIM_EALIGN, ti + "m misaligned");
+            T.v = T.m ? T.m + kMomentBlock : nullptr;
+            T.m2 = T.m && K == 3 ? T.m + 2 * kMomentBlock : nullptr;
+            vec = vec && aligned(T.m, 16);
+            add(T.m, (numel + kMomentBlock - 1) / kMomentBlock * K * kMomentBlock * 4, true, "m");
+        } else if (need_mv) {
             T.m = static_cast<float *>(list->m[i]);
             T.v = static_cast<float *>(list->v[i]);
             if (numel > 0 && (!T.m || !T.v)) return fail(OPTIM_EINVAL, ti + "NULL m or v");
@@ -374,7 +394,7 @@ int build(const optim_tensor_list *list, int32_t algo, const optim_plan_opts *op
             vec = vec && aligned(T.m, 16);
             add(T.m, numel * 4, true, "m");
         }
-        if (algo == OPTIM_ALGO_ADEMAMIX) {
+        if (algo == OPTIM_ALGO_ADEMAMIX && !mom_il) {
             T.m2 = static_cast<float *>(list->m2[i]);
             if (numel > 0 && !T.m2) return fail(OPTIM_EINVAL, ti + "NULL m2");
             if (!aligned(T.m2, 4)) return fail(OPTIM_EALIGN, ti + "m2 misaligned");

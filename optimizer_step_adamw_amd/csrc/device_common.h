@@ -117,29 +117,31 @@ __device__ __forceinline__ constexpr int64_t group_off(int j) {
     return LAY == kRun ? (int64_t)j * kVec : j * kSub;
 }
 
+// gs: the distance between a lane's groups in the strided layouts (kSub,
+// or more in an interleaved moment array).
 template <int N, int LAY = kStrided>
-__device__ __forceinline__ void ldf(const float *a, int64_t e, float (&x)[N]) {
+__device__ __forceinline__ void ldf(const float *a, int64_t e, float (&x)[N], int64_t gs = kSub) {
     if constexpr (N == 1) {
         x[0] = gp(a)[e];
     } else {
         static_assert(N % kVec == 0, "groups of 4");
 #pragma unroll
         for (int j = 0; j < N / kVec; ++j) {
-            const f32x4 u = vload<LAY>((const GMEM f32x4 *)gp(a + e + group_off<LAY>(j)));
+            const f32x4 u = vload<LAY>((const GMEM f32x4 *)gp(a + e + (LAY == kRun ? group_off<LAY>(j) : j * gs)));
             x[4 * j] = u.x; x[4 * j + 1] = u.y; x[4 * j + 2] = u.z; x[4 * j + 3] = u.w;
         }
     }
 }
 
 template <int N, int LAY = kStrided>
-__device__ __forceinline__ void stf(float *a, int64_t e, const float (&x)[N]) {
+__device__ __forceinline__ void stf(float *a, int64_t e, const float (&x)[N], int64_t gs = kSub) {
     if constexpr (N == 1) {
         gp(a)[e] = x[0];
     } else {
         static_assert(N % kVec == 0, "groups of 4");
 #pragma unroll
         for (int j = 0; j < N / kVec; ++j)
-            vstore<LAY>((GMEM f32x4 *)gp(a + e + group_off<LAY>(j)),
+            vstore<LAY>((GMEM f32x4 *)gp(a + e + (LAY == kRun ? group_off<LAY>(j) : j * gs)),
                         f32x4{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]});
     }
 }
@@ -511,6 +513,37 @@ __device__ __forceinline__ float uniform(float x) {
     return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
 }
 
+// A 64-bit pointer that is the same in every lane, moved to scalar registers.
+// readfirstlane returns int: each half goes back through uint32_t, so a low
+// half with bit 31 set is not sign-extended into the high half.
+template <class T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (T *)((hi << 32) | lo);
+}
+
+// The descriptor of the tensor a workgroup works on, copied into scalar
+// registers.  Through a reference into the plan's table, the compiler must
+// assume that the step's own stores may have changed the table, and reloads
+// each array's pointer after the previous array's stores, waiting for all of
+// them to complete (s_waitcnt vmcnt(0)) before the next array's stores can
+// go out; a register copy lets every store of a unit issue back to back.
+__device__ __forceinline__ TensorDesc uniform_desc(const TensorDesc &src) {
+    TensorDesc T = src;
+    T.p = uniform_ptr(T.p);
+    T.g = uniform_ptr(T.g);
+    T.m = uniform_ptr(T.m);
+    T.v = uniform_ptr(T.v);
+    T.m2 = uniform_ptr(T.m2);
+    T.rem = uniform_ptr(T.rem);
+    T.master = uniform_ptr(T.master);
+    T.group = __builtin_amdgcn_readfirstlane(T.group);
+    T.vec_ok = __builtin_amdgcn_readfirstlane(T.vec_ok);
+    return T;
+}
+
 // ---------------------------------------------------------------- partial sums
 // Sum of x[i * stride] over i in [i0, i1), this lane taking i0 + lane,
 // i0 + lane + kThreads, ...: eight independent accumulators, combined in a
@@ -560,14 +593,39 @@ struct AdamRegs {
     float p[N], g[N], m[N], v[N], m2[N];
 };
 
+// Where element e's moments sit.  Separate arrays (MI false): m[e], v[e],
+// m2[e].  Interleaved (MI, the plan's moment layout): one array per tensor
+// in blocks of kMomentBlock elements, block b holding m, then v (then m2)
+// of elements [b kMomentBlock, (b + 1) kMomentBlock); the descriptor's v and
+// m2 point kMomentBlock and 2 kMomentBlock floats past m, so every moment of
+// e sits at the same index e + X (e - e mod kMomentBlock), X the number of
+// moments after m, and a lane's groups (kSub = kMomentBlock elements apart)
+// are (X + 1) kSub apart.  A pack member (at most kMomentBlock elements, one
+// block) needs no remapping.
+template <bool MI, bool ADE>
+__device__ __forceinline__ int64_t moment_at(int64_t e) {
+    if constexpr (MI) return e + (ADE ? 2 : 1) * (e & ~(kMomentBlock - 1));
+    else return e;
+}
+template <bool MI, bool ADE>
+constexpr int64_t moment_gs() { return MI ? (ADE ? 3 : 2) * kSub : kSub; }
+// v and m2 of the interleaved layout taken from m, so the compiler sees
+// that the moments of a group are one run (one address for m and v)
+template <bool MI, class D>
+__device__ __forceinline__ float *moment_v(const D &T) { return MI ? T.m + kMomentBlock : T.v; }
+template <bool MI, class D>
+__device__ __forceinline__ float *moment_m2(const D &T) { return MI ? T.m + 2 * kMomentBlock : T.m2; }
+static_assert(kSub == kMomentBlock, "a lane's groups step whole moment blocks");
+
 // Loads; the gradient is multiplied by gscale (1 to defer the unscale).
-template <int PK, int GK, bool ADE, int N, class D>
+template <int PK, int GK, bool ADE, int N, bool MI = false, class D>
 __device__ __forceinline__ void adam_load(const D &T, int64_t e, float gscale, AdamRegs<N> &r) {
     load_p<PK, N>(T, e, r.p);
     load_g<GK, N>(T.g, e, gscale, r.g);
-    ldf<N>(T.m, e, r.m);
-    ldf<N>(T.v, e, r.v);
-    if constexpr (ADE) ldf<N>(T.m2, e, r.m2);
+    const int64_t i = moment_at<MI, ADE>(e), gs = moment_gs<MI, ADE>();
+    ldf<N>(T.m, i, r.m, gs);
+    ldf<N>(moment_v<MI>(T), i, r.v, gs);
+    if constexpr (ADE) ldf<N>(moment_m2<MI>(T), i, r.m2, gs);
 }
 
 // Decoupled decay and update with one rounding at the parameter's scale:
@@ -596,20 +654,21 @@ __device__ __forceinline__ void adam_math(AdamRegs<N> &r, const AdamK &k, float 
     }
 }
 
-template <int PK, bool ADE, int N, class D>
+template <int PK, bool ADE, int N, bool MI = false, class D>
 __device__ __forceinline__ void adam_store(const D &T, int64_t e, const AdamRegs<N> &r) {
     store_p<PK, N>(T, e, r.p);
-    stf<N>(T.m, e, r.m);
-    stf<N>(T.v, e, r.v);
-    if constexpr (ADE) stf<N>(T.m2, e, r.m2);
+    const int64_t i = moment_at<MI, ADE>(e), gs = moment_gs<MI, ADE>();
+    stf<N>(T.m, i, r.m, gs);
+    stf<N>(moment_v<MI>(T), i, r.v, gs);
+    if constexpr (ADE) stf<N>(moment_m2<MI>(T), i, r.m2, gs);
 }
 
-template <int PK, int GK, bool ADE, int N, class D>
+template <int PK, int GK, bool ADE, int N, bool MI = false, class D>
 __device__ __forceinline__ void adam_elems(const D &T, int64_t e, const AdamK &k, float lw) {
     AdamRegs<N> r;
-    adam_load<PK, GK, ADE, N>(T, e, k.inv_scale, r);
+    adam_load<PK, GK, ADE, N, MI>(T, e, k.inv_scale, r);
     adam_math<ADE, N>(r, k, lw);
-    adam_store<PK, ADE, N>(T, e, r);
+    adam_store<PK, ADE, N, MI>(T, e, r);
 }
 
 // AdamW / AdEMAMix over a lane's G groups of a pack.  Whole slots: all
@@ -666,11 +725,11 @@ __device__ __forceinline__ void adam_pack_unit(const StepArgs &a, const SpanDesc
     __syncthreads();  // L is refilled for the next pack
 }
 
-template <int PK, int GK, bool ADE, int G = kAdamGroups>
+template <int PK, int GK, bool ADE, int G = kAdamGroups, bool MI = false>
 __device__ __forceinline__ void adam_unit(const TensorDesc &T, int64_t start, int64_t len,
                                           const AdamK &k, float lw) {
     lane_walk<G>(start, len, T.vec_ok, [&](auto n, int64_t e) {
-        adam_elems<PK, GK, ADE, decltype(n)::value>(T, e, k, lw);
+        adam_elems<PK, GK, ADE, decltype(n)::value, MI>(T, e, k, lw);
     });
 }
 

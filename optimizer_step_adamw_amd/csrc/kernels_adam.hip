@@ -23,7 +23,24 @@ namespace {
 // us, the 1.1B-element bf16 + remainder list 5179 / 5301 against 5070 us),
 // so larger plans take 2048-element units of 2 groups without them (EG = 0).  The plan picks the
 // unit size by its element count and the launcher the form by the units.
-template <int PK, int GK, bool ADE, int EG>
+// The tensor descriptor a unit works with: for bf16 + remainder params a
+// copy in scalar registers (uniform_desc: the unit's stores issue back to
+// back), otherwise a reference into the plan's table, which the compiler
+// re-reads after each array's stores and waits for them first.  Measured on
+// MI355X in one process on the same arrays, table reference against
+// register copy: bf16 + remainder 2^28 elements 1174.7 / 1163.6 us, the
+// Llama-1.1B list 5352 / 5223 us, with interleaved moments 1228.9 / 1136.6
+// and 5484 / 4830 us; fp32 4096^2 78.4 / 82.1 us, fp32 2^28 1252.5 /
+// 1283.2 us (with interleaved moments 1224.3 / 1253.7 us) -- the fp32 step
+// streams faster with its stores spaced out by those waits.
+template <int PK, class F>
+__device__ __forceinline__ void with_desc(const TensorDesc &T, F &&f) {
+    if constexpr (PK == P_BF16R) f(uniform_desc(T));
+    else f(T);
+}
+
+// MI: the plan's interleaved moment layout (moment_at).
+template <int PK, int GK, bool ADE, int EG, bool MI>
 __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
     __shared__ Scalars S;
     constexpr int G = EG > 0 ? EG : kAdamGroups;
@@ -35,20 +52,22 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
         while (a.spans[si + 1].unit_begin <= u) ++si;
         const SpanDesc sp = a.spans[si];
         const int64_t off = (u - sp.unit_begin) * a.tile;
-        const TensorDesc &T = a.tensors[sp.tensor];
+        const TensorDesc &Tt = a.tensors[sp.tensor];
         const int64_t start = sp.elem_begin + off;
-        if (sp.len - off >= a.tile && T.vec_ok && start % kVec == 0) {
-            const int64_t e = start + threadIdx.x * kVec;
-            AdamRegs<N> r;
-            adam_load<PK, GK, ADE, N>(T, e, 1.0f, r);
-            step_begin(a, S);
-            const StepCommit commit{a, S};
-            if (S.skip) return;
-            const AdamK k = adam_consts(S);
+        if (sp.len - off >= a.tile && Tt.vec_ok && start % kVec == 0) {
+            with_desc<PK>(Tt, [&](const TensorDesc &T) {
+                const int64_t e = start + threadIdx.x * kVec;
+                AdamRegs<N> r;
+                adam_load<PK, GK, ADE, N, MI>(T, e, 1.0f, r);
+                step_begin(a, S);
+                const StepCommit commit{a, S};
+                if (S.skip) return;
+                const AdamK k = adam_consts(S);
 #pragma unroll
-            for (int i = 0; i < N; ++i) r.g[i] = r.g[i] * k.inv_scale;  // g * 1 * s == g * s
-            adam_math<ADE, N>(r, k, uniform(S.lrwd[T.group]));
-            adam_store<PK, ADE, N>(T, e, r);
+                for (int i = 0; i < N; ++i) r.g[i] = r.g[i] * k.inv_scale;  // g * 1 * s == g * s
+                adam_math<ADE, N>(r, k, uniform(S.lrwd[T.group]));
+                adam_store<PK, ADE, N, MI>(T, e, r);
+            });
             return;
         }
     }
@@ -57,8 +76,9 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
     if (S.skip) return;
     const AdamK k = adam_consts(S);
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
-        const TensorDesc &T = a.tensors[sp.tensor];
-        adam_unit<PK, GK, ADE, G>(T, start, len, k, uniform(S.lrwd[T.group]));
+        with_desc<PK>(a.tensors[sp.tensor], [&](const TensorDesc &T) {
+            adam_unit<PK, GK, ADE, G, MI>(T, start, len, k, uniform(S.lrwd[T.group]));
+        });
     });
 }
 
@@ -110,8 +130,10 @@ __global__ __launch_bounds__(kThreads) void adam_pack_kernel(StepArgs a) {
 
 }  // namespace
 
-template <bool ADE, int PK, int GK>
-static void launch_adam_g(const StepArgs &args, hipStream_t s) {
+// MI: the plan's interleaved moment layout (pack members are one moment
+// block each, so the pack kernel needs no variant)
+template <bool ADE, int PK, int GK, bool MI>
+static void launch_adam_mi(const StepArgs &args, hipStream_t s) {
     // units of single tensors [unit0, pack_unit0), then the packs
     StepArgs a = args;
     const bool packs = a.pack_unit0 < a.nunits;
@@ -124,11 +146,11 @@ static void launch_adam_g(const StepArgs &args, hipStream_t s) {
         // workgroup: the default grid over 2048- or 4096-element units
         const bool early = a.grid_request == 0 && a.units_per_wg == 1 && a.nunits - a.unit0 <= kEarlyLoadUnits;
         if (early && a.tile == (int64_t)kAdamGroups * kSub)
-            LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, kAdamGroups>), a, s);
+            LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, kAdamGroups, MI>), a, s);
         else if (early && a.tile == (int64_t)kAdamGroupsEarly * kSub)
-            LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, kAdamGroupsEarly>), a, s);
+            LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, kAdamGroupsEarly, MI>), a, s);
         else
-            LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, 0>), a, s);
+            LAUNCH_PERSISTENT((adam_kernel<PK, GK, ADE, 0, MI>), a, s);
     }
     if (packs) {
         StepArgs b = args;
@@ -136,6 +158,14 @@ static void launch_adam_g(const StepArgs &args, hipStream_t s) {
         static_assert(kPackElems == (int64_t)kAdamGroups * kSub, "a pack is one pass of the pack kernel");
         LAUNCH_PERSISTENT((adam_pack_kernel<PK, GK, ADE, kAdamGroups>), b, s);
     }
+}
+
+template <bool ADE, int PK, int GK>
+static void launch_adam_g(const StepArgs &a, hipStream_t s) {
+    if (a.interleaved)
+        launch_adam_mi<ADE, PK, GK, true>(a, s);
+    else
+        launch_adam_mi<ADE, PK, GK, false>(a, s);
 }
 
 template <bool ADE, int PK>

@@ -252,17 +252,6 @@ __device__ __forceinline__ void store_il_part(uint8_t *q, int64_t e, int nv, uin
     for (int b = 0; b < nv * BITS / 4; ++b) gp(q)[byte0 + b] = (uint8_t)(raw >> (8 * b));
 }
 
-// A 64-bit pointer that is the same in every lane, moved to scalar registers.
-// readfirstlane returns int: each half goes back through uint32_t, so a low
-// half with bit 31 set is not sign-extended into the high half.
-template <class T>
-__device__ __forceinline__ T *uniform_ptr(T *p) {
-    const uint64_t v = (uint64_t)p;
-    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
-    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
-    return (T *)((hi << 32) | lo);
-}
-
 // One unit's arrays, offset to the unit's first element (a multiple of the
 // tile, hence of the quantization block and of 8 elements) and kept in scalar
 // registers: the tensor descriptor is read once per unit, not once per row.

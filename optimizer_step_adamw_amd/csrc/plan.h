@@ -52,6 +52,9 @@ constexpr int64_t blockwise_tile(bool ademamix, int bits, bool interleaved) {
 constexpr int64_t kFiniteCheckElems = 32768;
 constexpr int64_t kMinTile = 1024;   // one group of 4 elements per lane
 constexpr int64_t kMinBlockwiseTile = 2048;  // one quantizer row: 256 lanes x 8 elements
+// AdamW / AdEMAMix interleaved moment layout: blocks of this many elements
+// (one group of 4 per lane of a workgroup), m then v (then m2) per block
+constexpr int64_t kMomentBlock = 1024;
 constexpr int kMaxGroups = 64;    // distinct weight-decay values per plan
 constexpr int64_t kMaxNumel = int64_t(1) << 48;  // per tensor (byte sizes stay far from overflow)
 
@@ -239,7 +242,9 @@ struct StepArgs {
     const Codebook *codebook;
     int32_t bits, block;
     int32_t interleaved;      // blockwise 2-state: m and v codes (and absmax)
-                              // side by side in qm (absmax_m)
+                              // side by side in qm (absmax_m); AdamW /
+                              // AdEMAMix: the moments of a tensor in one
+                              // array, in blocks of kMomentBlock elements
     float *found_inf;         // finite check output
     int32_t cus;              // compute units of the device
     const PackDesc *packs;    // packs of small tensors (elementwise plans)

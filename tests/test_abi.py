@@ -165,10 +165,42 @@ def test_blockwise_interleaved_layout_validation(L):
     # other algorithms, unknown layouts
     expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(
         fake_list([n], fake=f, **kw(qm2=[f(n)], absmax_m2=[f(64)])), osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX, il(8, 256)))
-    expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(fake_list([n], fake=f), osa.OPTIM_ALGO_ADAMW,
+    expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(fake_list([n], fake=f, v=None), osa.OPTIM_ALGO_LION,
                                                     osa.optim_plan_opts(0, 0, 0, 0, 0, 0, 1)))
     expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, **kw()), osa.OPTIM_ALGO_BLOCKWISE,
                                               osa.optim_plan_opts(8, 256, 0, 0, 0, 0, 2)))
+
+
+def test_interleaved_moment_layout_validation(L):
+    """AdamW / AdEMAMix with interleaved moments: m holds K * 1024 *
+    ceil(numel / 1024) floats (K = 2, or 3 with m2), v and m2 absent; the
+    other algorithms and 16-bit moments refuse the layout."""
+    f = Fake()
+    il = lambda sdt=0: osa.optim_plan_opts(0, 0, 0, 0, sdt, 0, osa.OPTIM_LAYOUT_INTERLEAVED)
+    n = 1000  # one block: the buffer is K * 1024 floats
+    assert ws(fake_list([n], fake=f, v=None, m=[f(2 * 4096)]), osa.OPTIM_ALGO_ADAMW, il()) > 0
+    assert ws(fake_list([n], fake=f, v=None, m=[f(3 * 4096)]), osa.OPTIM_ALGO_ADEMAMIX, il()) > 0
+    # v or m2 given, m misaligned
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f), osa.OPTIM_ALGO_ADAMW, il()))
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([n], fake=f, v=None, m2=[f(4 * n)]),
+                                              osa.OPTIM_ALGO_ADEMAMIX, il()))
+    expect_error(osa.OPTIM_EALIGN, lambda: ws(fake_list([n], fake=f, v=None, m=[f(8192, misalign=2)]),
+                                              osa.OPTIM_ALGO_ADAMW, il()))
+    # two tensors of 1500 elements: each buffer spans 2 * 2048 floats, so
+    # buffers 2 * 1500 floats apart overlap and 2 * 2048 apart do not
+    k = 1500
+    base = f(4 * 2 * 2048 * 2)
+    expect_error(osa.OPTIM_EINVAL, lambda: ws(fake_list([k, k], fake=f, v=None, m=[base, base + 4 * 2 * k]),
+                                              osa.OPTIM_ALGO_ADAMW, il()))
+    assert ws(fake_list([k, k], fake=f, v=None, m=[base, base + 4 * 2 * 2048]), osa.OPTIM_ALGO_ADAMW, il()) > 0
+    # not for Lion, LAMB, Adam-mini or 16-bit moments
+    for algo in (osa.OPTIM_ALGO_LION, osa.OPTIM_ALGO_LAMB):
+        expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(fake_list([n], fake=f, v=None), algo, il()))
+    expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(
+        fake_list([4096], fake=f, v=None, mini_kind=[osa.OPTIM_MINI_FULL_V], head_numel=[0]),
+        osa.OPTIM_ALGO_ADAM_MINI, il()))
+    expect_error(osa.OPTIM_EUNSUPPORTED, lambda: ws(
+        fake_list([n], fake=f, v=None, scale_m=[f(4)], scale_v=[f(4)]), osa.OPTIM_ALGO_ADAMW, il(osa.OPTIM_F16)))
 
 
 def test_tile_bounds(L):
