@@ -17,7 +17,8 @@ and MI355X's 8 TB/s:
   - AdamW and AdEMAMix fp32 on 4096 x 4096 (four state sets taken in turn,
     1.1 / 1.3 GB together, so no set is still in the 256 MB Infinity Cache
     when its turn comes);
-  - the bf16 + int16-remainder AdamW kernel and the non-finite check on the
+  - the bf16 + int16-remainder AdamW kernel (moments in separate arrays, and
+    interleaved in one array per tensor) and the non-finite check on the
     Llama-1.1B-shaped list;
   - blockwise 8-bit (block 256) and 4-bit (block 128) on 268M elements.
 Each entry also carries `ceiling`: the bandwidth of the same access pattern
@@ -189,6 +190,7 @@ KERNEL_SOURCES = {  # traffic summary name -> sources its device code comes from
     "adamw_fp32": ("device_common.h", "kernels_adam.hip"),
     "ademamix_fp32": ("device_common.h", "kernels_adam.hip"),
     "adamw_bf16_remainder": ("device_common.h", "kernels_adam.hip"),
+    "adamw_bf16_remainder_interleaved": ("device_common.h", "kernels_adam.hip"),
     "adamw_fp32_packs": ("device_common.h", "kernels_adam.hip"),
     "check_finite_bf16": ("device_common.h", "kernels_util.hip"),
     "check_norm_bf16": ("device_common.h", "kernels_util.hip"),
@@ -359,13 +361,18 @@ def bench_c2(torch, osa, synth, steps, warmup):
 
 # --------------------------------------------------------------------------
 # Llama 1.1B: bf16 params + int16 remainders, bf16 grads x 65536, AMP, cosine lr
-def c3_state(torch, osa, synth):
+def c3_state(torch, osa, synth, interleaved=False):
+    """interleaved: the moments of each tensor in one array, in blocks of 1024
+    elements (the plan's interleaved moment layout)."""
     wl = synth.c3_llama_1b()
     hp, scale = wl.hp, wl.extra["loss_scale"]
     specs = wl.tensors
     p0 = [synth.initial_param_device(s, wl.p_std, wl.index, i, "cuda") for i, s in enumerate(specs)]
     A = adam_buffers(torch, p0, param_bf16=True)
     del p0
+    if interleaved:
+        A["m"] = [torch.zeros(2 * ((x.numel() + 1023) // 1024 * 1024), device="cuda") for x in A["p"]]
+        A["v"] = None
     free(torch)
     G = []
     for i, s in enumerate(specs):
@@ -375,7 +382,8 @@ def c3_state(torch, osa, synth):
     wd = [0.0 if s.is_norm else hp.wd for s in specs]
     tl = osa.TensorList(A["p"], G, m=A["m"], v=A["v"], remainders=A["r"], weight_decay=wd,
                         param_dtype=osa.OPTIM_BF16, grad_dtype=osa.OPTIM_BF16)
-    plan = osa.Plan(tl, osa.OPTIM_ALGO_ADAMW)
+    plan = osa.Plan(tl, osa.OPTIM_ALGO_ADAMW,
+                    state_layout=osa.OPTIM_LAYOUT_INTERLEAVED if interleaved else osa.OPTIM_LAYOUT_SEPARATE)
     s = scalars(torch, 0.0, inv_scale=1.0 / scale)
     osa.optim_plan_set_schedule(plan.handle, osa.OPTIM_SCHED_COSINE, hp.lr, 0.0, wl.steps, s["iter"])
     h = osa.optim_adamw_hp(hp.beta1, hp.beta2, hp.eps)
@@ -398,10 +406,20 @@ def bench_c3(torch, osa, synth, steps, warmup):
     plan.close()
     del keep
     free(torch)
+    # the same step with the moments interleaved (one array per tensor)
+    _, plan, s, h, keep = c3_state(torch, osa, synth, interleaved=True)
+    ms_il, _, recs, _ = run_timed(torch, [finite, step], steps, warmup, plans=[plan.handle], trace_cap=4 * steps)
+    rec_il = recs[plan.handle]
+    plan.close()
+    del keep
+    free(torch)
     b = (B_BF16R + B_FINITE_BF16) * n
     return dict(workload=wl.name, elements=n, ms_per_step=ms, elements_per_s=n / (ms * 1e-3),
                 gbs=gbs(b, ms), frac=gbs(b, ms) / PEAK_HBM_GBS,
+                interleaved_moments=dict(ms_per_step=ms_il, elements_per_s=n / (ms_il * 1e-3)),
                 kernels=dict(adamw_bf16_remainder=dict(stats=kernel_stats(rec, "adam_kernel"), bytes=B_BF16R * n),
+                             adamw_bf16_remainder_interleaved=dict(stats=kernel_stats(rec_il, "adam_kernel"),
+                                                                   bytes=B_BF16R * n),
                              check_finite_bf16=dict(stats=kernel_stats(rec, "finite_kernel"),
                                                     bytes=B_FINITE_BF16 * n)))
 
@@ -534,8 +552,13 @@ def bench_probes(torch, reps):
     # Llama-1.1B bf16 + remainder pattern (2048-element units)
     h16 = lambda: torch.empty(n, dtype=torch.int16, device="cuda").random_(-30000, 30000)
     arr = [h16(), h16(), h16(), f32(n), f32(n)]
-    ms = probe_time(torch, lambda i: probes.call("probe_bf16r", *arr, n), reps)
+    ms = probe_time(torch, lambda i: probes.call("probe_bf16r", *arr, n, 0), reps)
     out["bf16r_268M"] = dict(ms=ms, bytes=B_BF16R * n, gbs=gbs(B_BF16R * n, ms))
+    # the same with m and v interleaved in one array of 2n floats
+    mv = f32(2 * n)
+    ms = probe_time(torch, lambda i: probes.call("probe_bf16r", arr[0], arr[1], arr[2], mv, None, n, 1), reps)
+    out["bf16r_il_268M"] = dict(ms=ms, bytes=B_BF16R * n, gbs=gbs(B_BF16R * n, ms))
+    del mv
     sink = torch.zeros(n // 32768, dtype=torch.int32, device="cuda")
     ms = probe_time(torch, lambda i: probes.call("probe_read", arr[2], n, 2, sink), reps)
     out["read_bf16_268M"] = dict(ms=ms, bytes=2.0 * n, gbs=gbs(2.0 * n, ms))
@@ -845,7 +868,8 @@ def main():
                                         traffic_from_profile(k),
                                         note=f"{ROTATE} state sets taken in turn (none stays in the Infinity Cache)"))
     if "c3" in res:
-        for k, pk in (("adamw_bf16_remainder", "bf16r_268M"), ("check_finite_bf16", "read_bf16_268M")):
+        for k, pk in (("adamw_bf16_remainder", "bf16r_268M"), ("adamw_bf16_remainder_interleaved", "bf16r_il_268M"),
+                      ("check_finite_bf16", "read_bf16_268M")):
             e = res["c3"]["kernels"][k]
             roofs.append(roofline_entry("adam_kernel" if k.startswith("adamw") else "finite_kernel",
                                         f"{k}_llama1b", e["bytes"], e["stats"], ceil.get(pk),

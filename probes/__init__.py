@@ -49,7 +49,7 @@ def lib() -> ctypes.CDLL:
             "probe_adamw": [P, P, P, P, i64, i32, P],
             "probe_ademamix": [P, P, P, P, P, i64, i32, P],
             "probe_mini": [P, P, P, i64, P],
-            "probe_bf16r": [P, P, P, P, P, i64, P],
+            "probe_bf16r": [P, P, P, P, P, i64, i32, P],
             "probe_blockwise": [P, P, P, P, P, P, i64, i32, i32, i32, P],
             "probe_read": [P, i64, i32, P, P],
             "probe_copy": [P, P, i64, P],

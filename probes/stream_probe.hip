@@ -14,7 +14,8 @@
 //                                     per lane, one workgroup per G*1024
 //                                     elements, non-temporal accesses
 //  ademamix   R p g m v m2, W p m v m2  as adamw
-//  bf16r      R p r g (16-bit) m v, W p r (16-bit) m v   as adamw
+//  bf16r      R p r g (16-bit) m v, W p r (16-bit) m v   as adamw; or with
+//             m and v in one array, in blocks of 1024 elements (m, then v)
 //  mini       R p g m,  W p m         as adamw (the Adam-mini update's
 //                                     HBM pattern when g comes from HBM)
 //  blockwise  rows of 1024 elements, 4 per lane: R p g (16 B a lane),
@@ -83,11 +84,18 @@ __global__ __launch_bounds__(kThreads) void fp32_pattern(float *p, const float *
     }
 }
 
-// bf16 param + int16 remainder + bf16 grad (4 x 16 bits a lane per group) and fp32 m, v
-template <int G>
-__global__ __launch_bounds__(kThreads) void bf16r_pattern(uint16_t *p, uint16_t *r, const uint16_t *g, float *m,
-                                                          float *v) {
+// bf16 param + int16 remainder + bf16 grad (4 x 16 bits a lane per group) and fp32 m, v;
+// IL: m and v interleaved in m, block b (1024 elements) holding m then v
+template <int G, bool IL>
+__global__ __launch_bounds__(kThreads) void bf16r_pattern(uint16_t *p, uint16_t *r, const uint16_t *g, float *mm,
+                                                          float *vv) {
     const int64_t e = (int64_t)blockIdx.x * (G * 1024) + threadIdx.x * 4;
+    // IL: element e's m at 2e - e mod 1024, its v 1024 further; a lane's
+    // groups (1024 elements apart) are two blocks apart
+    float *m = IL ? mm + (2 * e - (e & 1023)) : mm;
+    float *v = IL ? m + 1024 : vv;
+    const int64_t ms = IL ? 2048 : 1024;  // distance between a lane's groups in m and v
+    const int64_t me = IL ? 0 : e;
     u32x2 P[G], R[G], Gr[G];
     u32x4 M[G], V[G];
     // array by array, as fp32_pattern
@@ -98,17 +106,17 @@ __global__ __launch_bounds__(kThreads) void bf16r_pattern(uint16_t *p, uint16_t 
 #pragma unroll
     for (int j = 0; j < G; ++j) Gr[j] = ntl((const u32x2 *)(g + e + j * 1024));
 #pragma unroll
-    for (int j = 0; j < G; ++j) M[j] = bits(ntl((const f32x4 *)(m + e + j * 1024)));
+    for (int j = 0; j < G; ++j) M[j] = bits(ntl((const f32x4 *)(m + me + j * ms)));
 #pragma unroll
-    for (int j = 0; j < G; ++j) V[j] = bits(ntl((const f32x4 *)(v + e + j * 1024)));
+    for (int j = 0; j < G; ++j) V[j] = bits(ntl((const f32x4 *)(v + me + j * ms)));
 #pragma unroll
     for (int j = 0; j < G; ++j) nts((u32x2 *)(p + e + j * 1024), R[j] ^ Gr[j]);
 #pragma unroll
     for (int j = 0; j < G; ++j) nts((u32x2 *)(r + e + j * 1024), P[j]);
 #pragma unroll
-    for (int j = 0; j < G; ++j) nts((f32x4 *)(m + e + j * 1024), flt(V[j]));
+    for (int j = 0; j < G; ++j) nts((f32x4 *)(m + me + j * ms), flt(V[j]));
 #pragma unroll
-    for (int j = 0; j < G; ++j) nts((f32x4 *)(v + e + j * 1024), flt(M[j]));
+    for (int j = 0; j < G; ++j) nts((f32x4 *)(v + me + j * ms), flt(M[j]));
 }
 
 // blockwise 2-state step, separate layout, 4 elements a lane per row of
@@ -220,9 +228,16 @@ int probe_mini(float *p, const float *g, float *m, int64_t n, void *stream) {
     return (int)hipGetLastError();
 }
 
-int probe_bf16r(uint16_t *p, uint16_t *r, const uint16_t *g, float *m, float *v, int64_t n, void *stream) {
-    hipLaunchKernelGGL((bf16r_pattern<2>), dim3(grid_of(n, 2048)), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), p, r, g, m, v);
+// interleaved != 0: m holds 2n floats (m and v blocks), v is unused
+int probe_bf16r(uint16_t *p, uint16_t *r, const uint16_t *g, float *m, float *v, int64_t n, int interleaved,
+                void *stream) {
+    if (n <= 0 || n % 2048 != 0) return -1;  // whole units only
+    if (interleaved)
+        hipLaunchKernelGGL((bf16r_pattern<2, true>), dim3(grid_of(n, 2048)), dim3(kThreads), 0,
+                           static_cast<hipStream_t>(stream), p, r, g, m, v);
+    else
+        hipLaunchKernelGGL((bf16r_pattern<2, false>), dim3(grid_of(n, 2048)), dim3(kThreads), 0,
+                           static_cast<hipStream_t>(stream), p, r, g, m, v);
     return (int)hipGetLastError();
 }
 
