@@ -23,19 +23,24 @@ namespace {
 // us, the 1.1B-element bf16 + remainder list 5179 / 5301 against 5070 us),
 // so larger plans take 2048-element units of 2 groups without them (EG = 0).  The plan picks the
 // unit size by its element count and the launcher the form by the units.
-// The tensor descriptor a unit works with: for bf16 + remainder params a
-// copy in scalar registers (uniform_desc: the unit's stores issue back to
-// back), otherwise a reference into the plan's table, which the compiler
+// The tensor descriptor a unit works with: a copy in scalar registers
+// (uniform_desc: the unit's stores issue back to back) for bf16 + remainder
+// params, and for fp32 masters with a 16-bit model copy in the early-load
+// form; otherwise a reference into the plan's table, which the compiler
 // re-reads after each array's stores and waits for them first.  Measured on
 // MI355X in one process on the same arrays, table reference against
 // register copy: bf16 + remainder 2^28 elements 1174.7 / 1163.6 us, the
 // Llama-1.1B list 5352 / 5223 us, with interleaved moments 1228.9 / 1136.6
-// and 5484 / 4830 us; fp32 4096^2 78.4 / 82.1 us, fp32 2^28 1252.5 /
-// 1283.2 us (with interleaved moments 1224.3 / 1253.7 us) -- the fp32 step
-// streams faster with its stores spaced out by those waits.
-template <int PK, class F>
+// and 5484 / 4830 us; fp32 master + bf16 copy 4096^2 (early form) 82.6 /
+// 80.7 us, 2^28 1288.5 / 1355.1 us; fp32 4096^2 78.4 / 82.1 us, fp32 2^28
+// 1252.5 / 1283.2 us (with interleaved moments 1224.3 / 1253.7 us) -- the
+// fp32 steps stream faster with their stores spaced out by those waits.
+template <int PK, int EG>
+constexpr bool kDescInRegs = PK == P_BF16R || (EG > 0 && (PK == P_MBF16 || PK == P_MF16));
+
+template <int PK, int EG, class F>
 __device__ __forceinline__ void with_desc(const TensorDesc &T, F &&f) {
-    if constexpr (PK == P_BF16R) f(uniform_desc(T));
+    if constexpr (kDescInRegs<PK, EG>) f(uniform_desc(T));
     else f(T);
 }
 
@@ -55,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
         const TensorDesc &Tt = a.tensors[sp.tensor];
         const int64_t start = sp.elem_begin + off;
         if (sp.len - off >= a.tile && Tt.vec_ok && start % kVec == 0) {
-            with_desc<PK>(Tt, [&](const TensorDesc &T) {
+            with_desc<PK, EG>(Tt, [&](const TensorDesc &T) {
                 const int64_t e = start + threadIdx.x * kVec;
                 AdamRegs<N> r;
                 adam_load<PK, GK, ADE, N, MI>(T, e, 1.0f, r);
@@ -76,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
     if (S.skip) return;
     const AdamK k = adam_consts(S);
     for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
-        with_desc<PK>(a.tensors[sp.tensor], [&](const TensorDesc &T) {
+        with_desc<PK, EG>(a.tensors[sp.tensor], [&](const TensorDesc &T) {
             adam_unit<PK, GK, ADE, G, MI>(T, start, len, k, uniform(S.lrwd[T.group]));
         });
     });
