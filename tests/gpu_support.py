@@ -64,7 +64,7 @@ class AdamState:
     """Device buffers for AdamW / AdEMAMix / Adam-mini over a tensor list."""
 
     def __init__(self, p0: list, *, grad_bf16=False, param_bf16=False, ademamix=False,
-                 v_len=None):
+                 v_len=None, moments_interleaved=False):
         n = len(p0)
         self.param_bf16 = param_bf16
         self.grad_bf16 = grad_bf16
@@ -78,10 +78,18 @@ class AdamState:
             self.r = None
         gdt = torch.int16 if grad_bf16 else torch.float32
         self.g = [torch.zeros(x.numel(), dtype=gdt, device=DEV) for x in p0]
-        self.m = [torch.zeros(x.numel(), dtype=torch.float32, device=DEV) for x in p0]
-        vl = v_len or [x.numel() for x in p0]
-        self.v = [torch.zeros(k, dtype=torch.float32, device=DEV) for k in vl]
-        self.m2 = [torch.zeros(x.numel(), dtype=torch.float32, device=DEV) for x in p0] if ademamix else None
+        if moments_interleaved:
+            # the plan's interleaved moment layout: m, v (, m2) of each block of
+            # 1024 elements side by side in one array per tensor
+            k = 3 if ademamix else 2
+            self.m = [torch.zeros(k * ((x.numel() + 1023) // 1024 * 1024), dtype=torch.float32, device=DEV)
+                      for x in p0]
+            self.v = self.m2 = None
+        else:
+            self.m = [torch.zeros(x.numel(), dtype=torch.float32, device=DEV) for x in p0]
+            vl = v_len or [x.numel() for x in p0]
+            self.v = [torch.zeros(k, dtype=torch.float32, device=DEV) for k in vl]
+            self.m2 = [torch.zeros(x.numel(), dtype=torch.float32, device=DEV) for x in p0] if ademamix else None
         self.n = n
 
     def tensor_list(self, wd, mini_kind=None, head_numel=None):
@@ -100,7 +108,7 @@ class AdamState:
         return out
 
     def buffers(self):
-        out = list(self.p) + list(self.m) + list(self.v)
+        out = list(self.p) + list(self.m) + list(self.v or [])
         if self.r:
             out += list(self.r)
         if self.m2:

@@ -104,11 +104,14 @@ def test_c2_decay_stress_sampled(algo):
 
 
 # ------------------------------------------------------------------ C3
-def test_c3_llama1b_bf16_remainder_amp_cosine():
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_c3_llama1b_bf16_remainder_amp_cosine(interleaved):
     """Llama-shaped 1.1B list: bf16 params + int16 remainders, bf16 grads x
     65536 with inv_scale 2^-16 on the device, +Inf injected at iterations 49
     and 99, cosine lr written by the step.  Skips are bit-exact no-ops; the
-    sampled fp32 masters follow the oracle; the lr values are equal."""
+    sampled fp32 masters follow the oracle; the lr values are equal.  Both
+    moment layouts (separate arrays, and interleaved in one array per
+    tensor), each in the launch configuration the benchmark times."""
     wl = synth.c3_llama_1b()
     hpw, K = wl.hp, wl.steps
     scale = wl.extra["loss_scale"]
@@ -118,7 +121,7 @@ def test_c3_llama1b_bf16_remainder_amp_cosine():
     p0 = []
     for i, s in enumerate(specs):
         p0.append(synth.initial_param_device(s, wl.p_std, wl.index, i, DEV))
-    st = AdamState(p0, grad_bf16=True, param_bf16=True)
+    st = AdamState(p0, grad_bf16=True, param_bf16=True, moments_interleaved=interleaved)
     # sample: 64 elements per tensor (+ ends) and the injection sites
     inject = {}
     for k in range(wl.extra["inf_every"] - 1, K, wl.extra["inf_every"]):
@@ -137,7 +140,8 @@ def test_c3_llama1b_bf16_remainder_amp_cosine():
     _free()
     om = [np.zeros(x.size) for x in op]
     ov = [np.zeros(x.size) for x in op]
-    plan = osa.Plan(st.tensor_list(wd), osa.OPTIM_ALGO_ADAMW)
+    plan = osa.Plan(st.tensor_list(wd), osa.OPTIM_ALGO_ADAMW,
+                    state_layout=osa.OPTIM_LAYOUT_INTERLEAVED if interleaved else osa.OPTIM_LAYOUT_SEPARATE)
     sc = DevScalars(0.0, inv_scale=1.0 / scale)
     osa.optim_plan_set_schedule(plan.handle, osa.OPTIM_SCHED_COSINE, hpw.lr, wl.extra["lr_min"], K, sc.iter)
     hp = osa.optim_adamw_hp(hpw.beta1, hpw.beta2, hpw.eps)
@@ -172,7 +176,7 @@ def test_c3_llama1b_bf16_remainder_amp_cosine():
         if k in (0, 9, 48, K - 2):
             err = max(relerr_tau(st.master(i)[d].cpu().numpy(), op[i], hpw.lr)
                       for i, (d, _) in enumerate(samp))
-            say(f"C3 iteration {k}: applied {t_or}, sampled master relerr_tau {err:.3e}")
+            say(f"C3 (interleaved={interleaved}) iteration {k}: applied {t_or}, sampled master relerr_tau {err:.3e}")
             assert err <= (TOL_STEP1 if t_or == 1 else TOL_RUN), (k, err)
     # stored bf16 == split(stored master), on the samples
     for i, (d, _) in enumerate(samp):
