@@ -23,7 +23,9 @@ and MI355X's 8 TB/s:
   - blockwise 8-bit (block 256) and 4-bit (block 128) on 268M elements.
 Each entry also carries `ceiling`: the bandwidth of the same access pattern
 streamed without arithmetic by a probe kernel (probes/stream_probe.hip; same
-arrays, lane layout, unit size and access kind), and `frac_of_ceiling`.
+arrays, lane layout, unit size and access kind), and `frac_of_ceiling`; and
+`rw_bound`: the bandwidth its read and written bytes would reach at the
+read-only and write-only probes' rates, one after the other.
 
 Secondary workloads (`secondary`): the 1M-element tensor, the 1.1B AMP loop
 with global-norm clipping and the dynamic loss scale, blockwise states in the
@@ -514,6 +516,34 @@ def bench_blockwise(torch, osa, synth, steps, warmup, interleaved=False, ademami
 
 # --------------------------------------------------------------------------
 # access-pattern ceilings
+# read / written bytes per element of each roofline workload (the
+# Adam-mini update: per element of the 7B list, full-v and shared-v mixed)
+_C5_N, _C5_FULL = 6738415616, 2 * 32000 * 4096
+RW_SPLIT = {
+    "adam_mini_llama7b": ((16.0 * _C5_FULL + 12.0 * (_C5_N - _C5_FULL)) / _C5_N,
+                          (12.0 * _C5_FULL + 8.0 * (_C5_N - _C5_FULL)) / _C5_N),
+    "adamw_fp32_4096x4096": (16.0, 12.0),
+    "ademamix_fp32_4096x4096": (20.0, 16.0),
+    "adamw_bf16_remainder_llama1b": (14.0, 12.0),
+    "adamw_bf16_remainder_interleaved_llama1b": (14.0, 12.0),
+    "check_finite_bf16_llama1b": (2.0, 0.0),
+    "blockwise_8bit_268M": (4 + 4 + 1 + 1 + 8 / 256, 4 + 1 + 1 + 8 / 256),
+    "blockwise_4bit_268M": (4 + 4 + 0.5 + 0.5 + 8 / 128, 4 + 0.5 + 0.5 + 8 / 128),
+}
+
+
+def rw_bound(ceil, split):
+    """The bandwidth a kernel reading R and writing W bytes per element would
+    reach if its reads ran at the read-only probe's rate and its writes at the
+    write-only probe's, one after the other: (R + W) / (R / read + W / write)."""
+    if not split or "read_fp32_268M" not in ceil or "write_fp32_268M" not in ceil:
+        return None
+    r, w = split
+    rd = ceil["read_fp32_268M"]["gbs"]
+    wr = max(ceil["write_fp32_268M"]["gbs"], ceil.get("write_fp32_ordinary_268M", {}).get("gbs", 0.0))
+    return dict(gbs=(r + w) / (r / rd + w / wr), read_gbs=rd, write_gbs=wr, read_bytes=r, write_bytes=w)
+
+
 def probe_time(torch, fn, reps, warmup=2):
     """Mean ms of one probe launch (events around each launch on the current
     stream; each probe is one kernel)."""
@@ -572,6 +602,10 @@ def bench_probes(torch, reps):
     out["mini_3r2w_268M"] = dict(ms=ms, bytes=B_MINI_SHARED * n, gbs=gbs(B_MINI_SHARED * n, ms))
     ms = probe_time(torch, lambda i: probes.call("probe_copy", arr[0], arr[1], n), reps)
     out["copy_268M"] = dict(ms=ms, bytes=8.0 * n, gbs=gbs(8.0 * n, ms))
+    # one write-only stream, non-temporal stores (as the step kernels) and ordinary ones
+    for nt, key in ((1, "write_fp32_268M"), (0, "write_fp32_ordinary_268M")):
+        ms = probe_time(torch, lambda i: probes.call("probe_write", arr[2], n, nt), reps)
+        out[key] = dict(ms=ms, bytes=4.0 * n, gbs=gbs(4.0 * n, ms))
     del arr
     free(torch)
     # blockwise separate layout: 8-bit block 256 on 4096-element units, 4-bit
@@ -879,6 +913,10 @@ def main():
             e = res["c4"]["kernels"][k]
             roofs.append(roofline_entry("blockwise_kernel", f"{k}_268M", e["bytes"], e["stats"], ceil.get(pk),
                                         traffic_from_profile(k)))
+    for e in roofs:
+        rw = rw_bound(ceil, RW_SPLIT.get(e["workload"]))
+        if rw:
+            e["rw_bound"] = dict(rw, frac=e["achieved"] / rw["gbs"])
     roof = roofs[0]
     cpu = cpu_baseline(synth, args.cpu_seconds) if args.cpu_seconds > 0 else None
     wl_c5 = synth.c5_adam_mini_7b()

@@ -52,6 +52,7 @@ def lib() -> ctypes.CDLL:
             "probe_bf16r": [P, P, P, P, P, i64, i32, P],
             "probe_blockwise": [P, P, P, P, P, P, i64, i32, i32, i32, P],
             "probe_read": [P, i64, i32, P, P],
+            "probe_write": [P, i64, i32, P],
             "probe_copy": [P, P, i64, P],
             "check_recip_rn": [ctypes.c_uint32, ctypes.c_uint32, P, P, P],
         }

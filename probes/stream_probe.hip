@@ -25,6 +25,7 @@
 //  read       R one fp32 or 16-bit stream, 8 groups of 4 per lane in flight,
 //             32768 elements per workgroup (the non-finite check, the
 //             block-sum pass)
+//  write      W one fp32 stream (8 groups of 4 per lane; non-temporal or ordinary)
 //  copy       R x, W y (ordinary accesses, 4 per lane, 1024 per workgroup)
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -190,6 +191,20 @@ __global__ __launch_bounds__(kThreads) void read_pattern(const uint8_t *x, uint3
     if (acc == 0x12345678u) sink[blockIdx.x] = acc;  // practically never taken, not provable
 }
 
+// W one fp32 stream, 8 groups of 4 per lane (8192 elements per workgroup),
+// non-temporal stores (as the step kernels store) or ordinary ones
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void write_pattern(float *y) {
+    const int64_t e0 = (int64_t)blockIdx.x * 8192 + threadIdx.x * 4;
+    const float b = (float)blockIdx.x;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const f32x4 x{b, b, b, (float)j};
+        if (NT) nts((f32x4 *)(y + e0 + j * 1024), x);
+        else *(GMEM f32x4 *)(y + e0 + j * 1024) = x;
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void copy_pattern(const float *x, float *y) {
     const int64_t e = (int64_t)blockIdx.x * 1024 + threadIdx.x * 4;
     *(GMEM f32x4 *)(y + e) = *(const GMEM f32x4 *)(x + e);
@@ -266,6 +281,17 @@ int probe_read(const void *x, int64_t n, int elem_bytes, uint32_t *sink, void *s
         hipLaunchKernelGGL((read_pattern<4>), grid, dim3(kThreads), 0, s, static_cast<const uint8_t *>(x), sink);
     else
         hipLaunchKernelGGL((read_pattern<2>), grid, dim3(kThreads), 0, s, static_cast<const uint8_t *>(x), sink);
+    return (int)hipGetLastError();
+}
+
+int probe_write(float *y, int64_t n, int nontemporal, void *stream) {
+    if (n <= 0 || n % 8192 != 0) return -1;
+    if (nontemporal)
+        hipLaunchKernelGGL(write_pattern<true>, dim3(grid_of(n, 8192)), dim3(kThreads), 0,
+                           static_cast<hipStream_t>(stream), y);
+    else
+        hipLaunchKernelGGL(write_pattern<false>, dim3(grid_of(n, 8192)), dim3(kThreads), 0,
+                           static_cast<hipStream_t>(stream), y);
     return (int)hipGetLastError();
 }
 

@@ -69,3 +69,23 @@ def test_kernel_stats_and_roofline_arithmetic():
     assert e["frac"] == pytest.approx(e["achieved"] / 8000.0)
     assert e["frac_of_ceiling"] == pytest.approx(e["achieved"] / 5800.0)
     assert e["bound"] == "hbm" and e["unit"] == "GB/s" and e["peak"] == 8000.0
+
+
+def test_read_write_bound_model():
+    """(R + W) / (R / read + W / write): a pure read stays at the read rate, a
+    pure write at the better of the two write probes, and a mix lies between
+    them, nearer the side that moves more bytes."""
+    ceil = {"read_fp32_268M": {"gbs": 6600.0}, "write_fp32_268M": {"gbs": 5400.0},
+            "write_fp32_ordinary_268M": {"gbs": 5500.0}}
+    assert bench.rw_bound(ceil, (4.0, 0.0))["gbs"] == pytest.approx(6600.0)
+    assert bench.rw_bound(ceil, (0.0, 4.0))["gbs"] == pytest.approx(5500.0)
+    adamw = bench.rw_bound(ceil, (16.0, 12.0))["gbs"]
+    assert adamw == pytest.approx(28.0 / (16.0 / 6600.0 + 12.0 / 5500.0))
+    assert 5500.0 < adamw < 6600.0
+    assert bench.rw_bound({}, (16.0, 12.0)) is None and bench.rw_bound(ceil, None) is None
+    # every roofline workload's split adds up to its algorithmic bytes per element
+    assert sum(bench.RW_SPLIT["adamw_fp32_4096x4096"]) == bench.B_ADAMW_F32
+    assert sum(bench.RW_SPLIT["ademamix_fp32_4096x4096"]) == bench.B_ADEMAMIX_F32
+    assert sum(bench.RW_SPLIT["adamw_bf16_remainder_llama1b"]) == bench.B_BF16R
+    assert sum(bench.RW_SPLIT["blockwise_8bit_268M"]) == pytest.approx(bench.B_8BIT)
+    assert sum(bench.RW_SPLIT["blockwise_4bit_268M"]) == pytest.approx(bench.B_4BIT)
