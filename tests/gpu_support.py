@@ -12,7 +12,7 @@ import optimizer_step_adamw_amd as osa
 
 DEV = "cuda"
 
-# spec bounds: relerr_tau after 1 step / at the end of <= 100 steps
+# parity bounds: relerr_tau after 1 step / at the end of <= 100 steps
 TOL_STEP1 = 2e-6
 TOL_RUN = 5e-5
 
