@@ -148,4 +148,8 @@ def snapshot(bufs):
 
 
 def all_equal(a, b) -> bool:
-    return all(torch.equal(x, y) for x, y in zip(a, b))
+    """Bit for bit (NaN patterns compare equal to themselves, -0.0 differs
+    from +0.0)."""
+    return len(a) == len(b) and all(
+        x.shape == y.shape and torch.equal(x.reshape(-1).view(torch.uint8), y.reshape(-1).view(torch.uint8))
+        for x, y in zip(a, b))
