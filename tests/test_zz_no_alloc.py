@@ -96,19 +96,21 @@ def test_static_plans_match_workspace_plans_twice():
     ref2.close()
 
 
-@pytest.mark.parametrize("ademamix", [False, True])
-def test_static_plan_with_packs_matches_workspace_plan(ademamix):
+@pytest.mark.parametrize("ademamix,interleaved", [(False, False), (True, False), (False, True), (True, True)])
+def test_static_plan_with_packs_matches_workspace_plan(ademamix, interleaved):
     """A list of small tensors, laid end to end in packs (their member
     records in the static workspace), then a larger tensor: the static plan
-    steps bit for bit as the workspace plan, with bf16 params + remainders."""
-    print(f"case: static plan with packs, ademamix={ademamix}", flush=True)
+    steps bit for bit as the workspace plan, with bf16 params + remainders,
+    moments in separate arrays or interleaved in one array per tensor."""
+    print(f"case: static plan with packs, ademamix={ademamix} interleaved={interleaved}", flush=True)
     sizes = [300, 7, 1000, 4, 65, 513, 9000, 1, 2047, 12]
     p0 = [host_normal(n, 0.02, 963, 0, i, 0) for i, n in enumerate(sizes)]
-    A, B = _twin(p0, param_bf16=True, ademamix=ademamix)
+    A, B = _twin(p0, param_bf16=True, ademamix=ademamix, moments_interleaved=interleaved)
     wd = [0.1 if i % 3 else 0.0 for i in range(len(sizes))]
     algo = osa.OPTIM_ALGO_ADEMAMIX if ademamix else osa.OPTIM_ALGO_ADAMW
-    ref = osa.Plan(A.tensor_list(wd), algo)
-    h = osa.optim_plan_create_static(B.tensor_list(wd), algo, None)
+    layout = osa.OPTIM_LAYOUT_INTERLEAVED if interleaved else osa.OPTIM_LAYOUT_SEPARATE
+    ref = osa.Plan(A.tensor_list(wd), algo, state_layout=layout)
+    h = osa.optim_plan_create_static(B.tensor_list(wd), algo, osa.optim_plan_opts(0, 0, 0, 0, 0, 0, layout))
     sa, sb = DevScalars(1e-3), DevScalars(1e-3)
     for t in (1, 2, 3):
         _grads(A, sizes, 3, t)
@@ -122,6 +124,7 @@ def test_static_plan_with_packs_matches_workspace_plan(ademamix):
                 osa.optim_step_adamw(plan, osa.optim_adamw_hp(0.9, 0.999, 1e-8), s.lr, None, None, s.step)
     torch.cuda.synchronize()
     assert all_equal(A.buffers(), B.buffers()) and int(sb.step.item()) == 3
-    say(f"{'AdEMAMix' if ademamix else 'AdamW'} with packs: static plan equals the workspace plan over 3 steps")
+    say(f"{'AdEMAMix' if ademamix else 'AdamW'} with packs (interleaved={interleaved}): static plan equals the "
+        "workspace plan over 3 steps")
     osa.optim_plan_destroy(h)
     ref.close()
