@@ -1,4 +1,5 @@
-"""Every multi-kernel step, and the AMP loop around the step, captured once
+"""Every multi-kernel step (and the bf16 + remainder AdamW step with
+interleaved moments), and the AMP loop around the step, captured once
 in a HIP graph and replayed: each replay, with eager work and host
 synchronisation between replays, must leave every buffer and device scalar
 bit for bit where the same step run eagerly on a twin state leaves them.
@@ -73,6 +74,10 @@ def _adam_like(algo, key):
             plan = osa.Plan(st.tensor_list([0.01] * len(sizes)),
                             osa.OPTIM_ALGO_BLOCKWISE_ADEMAMIX if ade else osa.OPTIM_ALGO_BLOCKWISE,
                             bits=bits, block=block)
+        elif algo == "adamw_bf16r_interleaved":
+            st = AdamState(_p0(sizes, key), param_bf16=True, moments_interleaved=True)
+            plan = osa.Plan(st.tensor_list([0.1] * len(sizes)), osa.OPTIM_ALGO_ADAMW,
+                            state_layout=osa.OPTIM_LAYOUT_INTERLEAVED)
         elif algo == "states16":
             st = AdamState(_p0(sizes, key))
             st.m = [torch.zeros(n, dtype=torch.int16, device=DEV) for n in sizes]
@@ -103,7 +108,7 @@ def _adam_like(algo, key):
             osa.optim_step_8bit_blockwise(plan.handle, hp, 4, 128, sc.lr, None, None, sc.step)
         elif algo == "blockwise_ademamix8":
             osa.optim_step_8bit_blockwise_ademamix(plan.handle, hpe, 8, 256, sc.lr, None, None, sc.step)
-        elif algo == "states16":
+        elif algo in ("states16", "adamw_bf16r_interleaved"):
             osa.optim_step_adamw(plan.handle, hp, sc.lr, None, None, sc.step)
         elif algo == "ademamix":
             osa.optim_step_ademamix(plan.handle, hpe, sc.lr, None, None, sc.step)
@@ -117,13 +122,14 @@ def _adam_like(algo, key):
 
 def _buffers(st):
     out = [x for x in (getattr(st, "p", []) or [])]
-    for name in ("m", "v", "m2", "qm", "qv", "am", "av", "qm2", "am2", "sm", "sv"):
+    for name in ("m", "v", "m2", "r", "qm", "qv", "am", "av", "qm2", "am2", "sm", "sv"):
         out += list(getattr(st, name, None) or [])
     return out
 
 
 @pytest.mark.parametrize("algo", ["ademamix", "mini", "mini_segments", "lion", "lamb", "blockwise8", "blockwise4",
-                                  "blockwise_ademamix8", "blockwise8_interleaved", "states16"])
+                                  "blockwise_ademamix8", "blockwise8_interleaved", "states16",
+                                  "adamw_bf16r_interleaved"])
 def test_step_graph_replays_match_eager(algo):
     (eager, graph), sizes, step = _adam_like(algo, sum(map(ord, algo)))
     g = _capture(lambda: step(*graph))
