@@ -5,24 +5,6 @@
 namespace optim {
 namespace {
 
-// EG > 0 (early form): a workgroup whose unit is one whole, aligned tile of
-// EG groups per lane (EG * 1024 elements) issues all of the unit's loads
-// before the per-step prologue, so their latency overlaps the scalar loads
-// and fp64 arithmetic.  Plans up to ~2 resident waves of workgroups take it
-// (see kEarlyLoadUnits): 2048-element units of 2 groups for lists up to
-// 2^20 elements, 4096-element units of 4 groups above that up to 2^24.
-// Measured on MI355X with two state sets alternating (nothing cached),
-// against 2048-element units of two groups without early loads: AdamW 2^22
-// elements 22.5 -> 20.9 us, 2^23 42.1 -> 40.6 us, 2^24 80.8 -> 79.3 us;
-// AdEMAMix 28.8 -> 26.3, 54.9 -> 51.9, 104.2 -> 103.6 us.  From 2^25
-// elements on early loads of new workgroups crowd the stores of the
-// finishing ones (2^26: AdamW 311.7 -> 317.5 us; re-timed in one process
-// on the same arrays, early loads on 2048- / 4096-element units against
-// none: fp32 2^26 320.9 / 309.9 against 304.7 us, 2^28 1305.9 / 1275.0
-// against 1235.8 us, bf16 + remainder 2^28 1264.0 / 1234.1 against 1143.6
-// us, the 1.1B-element bf16 + remainder list 5179 / 5301 against 5070 us),
-// so larger plans take 2048-element units of 2 groups without them (EG = 0).  The plan picks the
-// unit size by its element count and the launcher the form by the units.
 // The tensor descriptor a unit works with: a copy in scalar registers
 // (uniform_desc: the unit's stores issue back to back) for bf16 + remainder
 // params, and for fp32 masters with a 16-bit model copy in the early-load
@@ -44,6 +26,26 @@ __device__ __forceinline__ void with_desc(const TensorDesc &T, F &&f) {
     else f(T);
 }
 
+// EG > 0 (early form): a workgroup whose unit is one whole, aligned tile of
+// EG groups per lane (EG * 1024 elements) issues all of the unit's loads
+// before the per-step prologue, so their latency overlaps the scalar loads
+// and fp64 arithmetic.  Plans up to ~2 resident waves of workgroups take it
+// (see kEarlyLoadUnits): 2048-element units of 2 groups for lists up to
+// 2^20 elements, 4096-element units of 4 groups above that up to 2^24.
+// Measured on MI355X with two state sets alternating (nothing cached),
+// against 2048-element units of two groups without early loads: AdamW 2^22
+// elements 22.5 -> 20.9 us, 2^23 42.1 -> 40.6 us, 2^24 80.8 -> 79.3 us;
+// AdEMAMix 28.8 -> 26.3, 54.9 -> 51.9, 104.2 -> 103.6 us.  From 2^25
+// elements on early loads of new workgroups crowd the stores of the
+// finishing ones (2^26: AdamW 311.7 -> 317.5 us; re-timed in one process
+// on the same arrays, early loads on 2048- / 4096-element units against
+// none: fp32 2^26 320.9 / 309.9 against 304.7 us, 2^28 1305.9 / 1275.0
+// against 1235.8 us, bf16 + remainder 2^28 1264.0 / 1234.1 against 1143.6
+// us, the 1.1B-element bf16 + remainder list 5179 / 5301 against 5070 us),
+// so larger plans take 2048-element units of 2 groups without them
+// (EG = 0).  The plan picks the unit size by its element count and the
+// launcher the form by the units.
+//
 // MI: the plan's interleaved moment layout (moment_at).
 template <int PK, int GK, bool ADE, int EG, bool MI>
 __global__ __launch_bounds__(kThreads) void adam_kernel(StepArgs a) {
