@@ -120,7 +120,11 @@ __global__ __launch_bounds__(kThreads) void scaled_bf16_kernel(StepArgs a) {
     if (!S.skip) {
         const AdamK k = adam_consts(S);
         for_units(a, [&](int64_t, const SpanDesc &sp, int64_t start, int64_t len) {
-            const TensorDesc &T = a.tensors[sp.tensor];
+            // the descriptor in scalar registers, so p, m and v are stored
+            // back to back (measured on MI355X, 4096^2 fp32 p / g, in one
+            // process on the same arrays: 62.4 -> 61.3 us against a
+            // reference into the plan's table, see uniform_desc)
+            const TensorDesc T = uniform_desc(a.tensors[sp.tensor]);
             const float lw = uniform(S.lrwd[T.group]);
             const float sm = uniform(*T.scale_m), sv = uniform(*T.scale_v);
             lane_walk<kAdamGroups>(start, len, T.vec_ok, [&](auto n, int64_t e) {
