@@ -179,13 +179,38 @@ def library_sources_sha256():
     return h.hexdigest()
 
 
+def clocks():
+    """The GPU's clock levels as rocm-smi reports them (read only, after the
+    timed work, so the current levels are mostly idle ones): the supported
+    shader-clock levels and the current shader and memory clocks; None where
+    the tool is missing or says nothing."""
+    import subprocess
+
+    def smi(arg):
+        for exe in ("/opt/rocm/bin/rocm-smi", "rocm-smi"):
+            try:
+                r = subprocess.run([exe, arg, "--json"], capture_output=True, text=True, timeout=20)
+            except (OSError, subprocess.SubprocessError):
+                continue
+            try:
+                data = json.loads(r.stdout[r.stdout.find("{"):])
+            except ValueError:
+                return None
+            return next((v for k, v in sorted(data.items()) if k.startswith("card")), None)
+        return None
+    cur, lev = smi("--showclocks"), smi("--showclkfrq")
+    if not cur and not lev:
+        return None
+    return dict(levels=lev, after_run={k: v for k, v in (cur or {}).items() if "clock" in k.lower()})
+
+
 def environment(torch):
     """Device and software the numbers were taken on."""
     pr = torch.cuda.get_device_properties(0)
     return dict(device=pr.name, arch=getattr(pr, "gcnArchName", None), compute_units=pr.multi_processor_count,
                 hbm_gib=round(pr.total_memory / 2 ** 30, 1), torch=torch.__version__,
                 hip=getattr(torch.version, "hip", None), host_cpus=os.cpu_count(),
-                library_sources_sha256=library_sources_sha256())
+                clocks=clocks(), library_sources_sha256=library_sources_sha256())
 
 
 KERNEL_SOURCES = {  # traffic summary name -> sources its device code comes from
