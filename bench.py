@@ -20,7 +20,8 @@ and MI355X's 8 TB/s:
   - the bf16 + int16-remainder AdamW kernel (moments in separate arrays, and
     interleaved in one array per tensor) and the non-finite check on the
     Llama-1.1B-shaped list;
-  - blockwise 8-bit (block 256) and 4-bit (block 128) on 268M elements.
+  - blockwise 8-bit (block 256) and 4-bit (block 128) on 268M elements, in
+    the separate and the interleaved state layout.
 Each entry also carries `ceiling`: the bandwidth of the same access pattern
 streamed without arithmetic by a probe kernel (probes/stream_probe.hip; same
 arrays, lane layout, unit size and access kind), and `frac_of_ceiling`; and
@@ -554,6 +555,8 @@ RW_SPLIT = {
     "check_finite_bf16_llama1b": (2.0, 0.0),
     "blockwise_8bit_268M": (4 + 4 + 1 + 1 + 8 / 256, 4 + 1 + 1 + 8 / 256),
     "blockwise_4bit_268M": (4 + 4 + 0.5 + 0.5 + 8 / 128, 4 + 0.5 + 0.5 + 8 / 128),
+    "blockwise_8bit_interleaved_268M": (4 + 4 + 1 + 1 + 8 / 256, 4 + 1 + 1 + 8 / 256),
+    "blockwise_4bit_interleaved_268M": (4 + 4 + 0.5 + 0.5 + 8 / 128, 4 + 0.5 + 0.5 + 8 / 128),
 }
 
 
@@ -937,6 +940,11 @@ def main():
         for k, pk in (("blockwise_8bit", "blockwise_8bit_268M"), ("blockwise_4bit", "blockwise_4bit_268M")):
             e = res["c4"]["kernels"][k]
             roofs.append(roofline_entry("blockwise_kernel", f"{k}_268M", e["bytes"], e["stats"], ceil.get(pk),
+                                        traffic_from_profile(k)))
+    if "c4x" in res:  # the same steps with each element's m and v codes side by side
+        for k in ("blockwise_8bit_interleaved", "blockwise_4bit_interleaved"):
+            e = res["c4x"]["interleaved"]["kernels"][k]
+            roofs.append(roofline_entry("blockwise_kernel", f"{k}_268M", e["bytes"], e["stats"], None,
                                         traffic_from_profile(k)))
     for e in roofs:
         rw = rw_bound(ceil, RW_SPLIT.get(e["workload"]))
