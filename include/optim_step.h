@@ -159,7 +159,11 @@ typedef struct optim_tensor_list {
  *              Element e's m sits at m[K * 1024 * (e / 1024) + e % 1024], its
  *              v 1024 floats further, its m2 2048.  The values are those of
  *              separate arrays, bit for bit; the step streams one (AdamW) or
- *              two (AdEMAMix) arrays fewer.
+ *              two (AdEMAMix) arrays fewer.  (A storage choice of this
+ *              library, not of the pages, which keep each state a tensor of
+ *              its own.)  Lion, LAMB, Adam-mini, blockwise AdEMAMix and
+ *              16-bit moments refuse the interleaved layout
+ *              (OPTIM_EUNSUPPORTED).
  *              For OPTIM_ALGO_BLOCKWISE, OPTIM_LAYOUT_SEPARATE: qm / qv and
  *              absmax_m / absmax_v are four arrays.
  *              OPTIM_LAYOUT_INTERLEAVED (1): each element's m and v codes
